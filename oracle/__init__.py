@@ -1,0 +1,219 @@
+"""fp64 CPU oracle for the speculative verify / logit-fusion pass.
+
+TEST INFRASTRUCTURE ONLY: the test suite, ``__graft_entry__.smoke`` and the
+CPU-baseline leg of ``bench.py`` are the only callers.  The GPU library and
+its Python binding never import this package, and this package imports
+nothing from them.
+
+The arithmetic lives in ``vwl_oracle.c`` (plain C, double precision, one row
+at a time, plain sequential sums); this module builds it with gcc, loads it
+with ctypes and marshals numpy arrays.  Each entry point follows the pages:
+
+* ``asym`` -- AsymSpec reading notes, section 4.1 (context gain
+  ``delta = a - b`` and the delta-fusion token ``argmax(t + beta*delta)``)
+  and section 4.2 (``D = JSD(softmax(a) || softmax(b))``, the CDA threshold
+  ``gamma*exp(-D)``, the acceptance test and emission at the first rejection).
+* ``rapid`` -- RAPID notes, key design 2 (``zhat = z + eta*T*(q - p)``,
+  ``phat = softmax(zhat/T)``), key design 3 (tail protection below 10% of the
+  peak) and key design 4 (residual ``norm(max(p - phat, p - q, 0))``), with
+  rejection sampling against the augmented target (overall framework).
+* ``rapid_zhat`` / ``rapid_phat`` -- the same definitions for one row, used
+  by the pins.
+
+Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
+against library routines (scipy), closed forms, the pages' bounds and
+special cases, brute force and exact enumeration of the sampling law.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "vwl_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+TAIL_EPS = 1e-6
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ``vwl_oracle.c`` with gcc (OpenMP, no fast-math) into liboracle.so."""
+    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+        return _LIB
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math",
+           "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    build(force=False)
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    i = ctypes.c_int
+    d = ctypes.c_double
+    lib.vwl_oracle_asym.argtypes = [P, P, P, i, P, i, i, i, d, d, P, P, P, P, P, P, P, P, P, i]
+    lib.vwl_oracle_asym.restype = i
+    lib.vwl_oracle_rapid.argtypes = [P, P, i, P, P, P, i, i, i, d, d,
+                                     P, P, P, P, P, P, P, P, P, P, P, d, P, i]
+    lib.vwl_oracle_rapid.restype = i
+    lib.vwl_oracle_rapid_zhat.argtypes = [P, P, i, d, d, P]
+    lib.vwl_oracle_rapid_zhat.restype = i
+    lib.vwl_oracle_rapid_phat.argtypes = [P, P, i, d, d, P]
+    lib.vwl_oracle_rapid_phat.restype = i
+    lib.vwl_oracle_max_threads.argtypes = []
+    lib.vwl_oracle_max_threads.restype = i
+    _lib = lib
+    return lib
+
+
+def max_threads() -> int:
+    return int(_load().vwl_oracle_max_threads())
+
+
+def _ptr(x: np.ndarray):
+    return x.ctypes.data_as(ctypes.c_void_p)
+
+
+def _stored(x: np.ndarray, dtype: str) -> tuple[np.ndarray, int]:
+    """Accept float32 values (widened by the oracle) or uint16 bf16 bits."""
+    if dtype == "bf16":
+        if x.dtype == np.uint16:
+            return np.ascontiguousarray(x), 1
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        bits = x.view(np.uint32)
+        if np.any(bits & 0xFFFF):
+            raise ValueError("bf16 workload holds values that are not bf16-exact")
+        return np.ascontiguousarray((bits >> 16).astype(np.uint16)), 1
+    if dtype == "f32":
+        return np.ascontiguousarray(x, dtype=np.float32), 0
+    raise ValueError(dtype)
+
+
+@dataclass
+class AsymResult:
+    lse: np.ndarray        # [B, K+1, 3] log-sum-exp of a, b, t
+    D: np.ndarray          # [B, K+1]
+    gamma_eff: np.ndarray  # [B, K+1]
+    fused: np.ndarray      # [B, K+1] int32
+    gap: np.ndarray        # [B, K+1]
+    accept: np.ndarray     # [B, K] uint8
+    margin: np.ndarray     # [B, K]
+    accept_len: np.ndarray  # [B] int32
+    token: np.ndarray      # [B] int32
+
+
+def asym(a, b, t, draft, beta: float, gamma: float, dtype: str = "f32",
+         nthreads: int = 0) -> AsymResult:
+    """Oracle of the AsymSpec verify pass on [B, K+1, V] rows.
+
+    ``beta`` and ``gamma`` should be the float32 values the device receives
+    (they are widened exactly)."""
+    lib = _load()
+    sa, dt = _stored(a, dtype)
+    sb, _ = _stored(b, dtype)
+    st, _ = _stored(t, dtype)
+    B, P, V = sa.shape
+    K = P - 1
+    draft = np.ascontiguousarray(draft, dtype=np.int32).reshape(B, K)
+    R = B * P
+    lse = np.zeros((B, P, 3))
+    D = np.zeros((B, P))
+    ge = np.zeros((B, P))
+    fused = np.zeros((B, P), np.int32)
+    gap = np.zeros((B, P))
+    acc = np.zeros((B, max(K, 0)), np.uint8)
+    margin = np.zeros((B, max(K, 0)))
+    alen = np.zeros(B, np.int32)
+    tok = np.zeros(B, np.int32)
+    rc = lib.vwl_oracle_asym(_ptr(sa), _ptr(sb), _ptr(st), dt, _ptr(draft), B, K, V,
+                             float(np.float32(beta)), float(np.float32(gamma)),
+                             _ptr(lse), _ptr(D), _ptr(ge), _ptr(fused), _ptr(gap),
+                             _ptr(acc), _ptr(margin), _ptr(alen), _ptr(tok), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle asym failed with code %d" % rc)
+    del R
+    return AsymResult(lse, D, ge, fused, gap, acc, margin, alen, tok)
+
+
+@dataclass
+class RapidResult:
+    rowstat: np.ndarray     # [B, G+1, 4] L_z, L_y, Mhat, L_zhat
+    phat_draft: np.ndarray  # [B, G]
+    q_draft: np.ndarray     # [B, G]
+    accept: np.ndarray      # [B, G] uint8
+    acc_rel: np.ndarray     # [B, G]
+    tail_d_dist: np.ndarray  # [B, G]
+    accept_len: np.ndarray  # [B]
+    token: np.ndarray       # [B]
+    resid_S: np.ndarray     # [B] (-1: drawn from p)
+    draw_slack: np.ndarray  # [B]
+    tail_close: np.ndarray  # [B]
+    emit_dist: np.ndarray | None  # [B, V]
+
+
+def rapid(z, y, draft, u_accept, u_sample, eta: float, T: float, dtype: str = "f32",
+          want_dist: bool = False, tail_eps: float = TAIL_EPS, nthreads: int = 0) -> RapidResult:
+    """Oracle of the RAPID verify pass on [B, G+1, V] rows."""
+    lib = _load()
+    sz, dt = _stored(z, dtype)
+    sy, _ = _stored(y, dtype)
+    B, P, V = sz.shape
+    G = P - 1
+    draft = np.ascontiguousarray(draft, dtype=np.int32).reshape(B, G)
+    ua = np.ascontiguousarray(u_accept, dtype=np.float32).reshape(B, G)
+    us = np.ascontiguousarray(u_sample, dtype=np.float32).reshape(B, P)
+    rowstat = np.zeros((B, P, 4))
+    phd = np.zeros((B, G))
+    qd = np.zeros((B, G))
+    acc = np.zeros((B, G), np.uint8)
+    arel = np.zeros((B, G))
+    tdd = np.zeros((B, G))
+    alen = np.zeros(B, np.int32)
+    tok = np.zeros(B, np.int32)
+    rs = np.zeros(B)
+    slack = np.zeros(B)
+    close = np.zeros(B, np.int32)
+    dist = np.zeros((B, V)) if want_dist else None
+    rc = lib.vwl_oracle_rapid(_ptr(sz), _ptr(sy), dt, _ptr(draft), _ptr(ua), _ptr(us),
+                              B, G, V, float(np.float32(eta)), float(np.float32(T)),
+                              _ptr(rowstat), _ptr(phd), _ptr(qd), _ptr(acc), _ptr(arel), _ptr(tdd),
+                              _ptr(alen), _ptr(tok), _ptr(rs), _ptr(slack), _ptr(close),
+                              float(tail_eps), _ptr(dist) if dist is not None else None,
+                              int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle rapid failed with code %d" % rc)
+    return RapidResult(rowstat, phd, qd, acc, arel, tdd, alen, tok, rs, slack, close, dist)
+
+
+def rapid_zhat(z: np.ndarray, y: np.ndarray, eta: float, T: float) -> np.ndarray:
+    """zhat = z + eta*T*(softmax(y/T) - softmax(z/T)) for one row (float64)."""
+    lib = _load()
+    z = np.ascontiguousarray(z, dtype=np.float64)
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    out = np.zeros_like(z)
+    if lib.vwl_oracle_rapid_zhat(_ptr(z), _ptr(y), z.size, float(eta), float(T), _ptr(out)):
+        raise RuntimeError("oracle rapid_zhat failed")
+    return out
+
+
+def rapid_phat(z: np.ndarray, y: np.ndarray, eta: float, T: float) -> np.ndarray:
+    """Tail-protected augmented target of one row (float64)."""
+    lib = _load()
+    z = np.ascontiguousarray(z, dtype=np.float64)
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    out = np.zeros_like(z)
+    if lib.vwl_oracle_rapid_phat(_ptr(z), _ptr(y), z.size, float(eta), float(T), _ptr(out)):
+        raise RuntimeError("oracle rapid_phat failed")
+    return out

@@ -1,0 +1,521 @@
+"""Pins of the fp64 oracle to things other than itself.
+
+Each test ties one oracle output to an independent library routine (scipy),
+a closed form, a bound or special case stated on the pages, brute force on
+tiny inputs, or exact enumeration of a sampling law.  Chosen so that a dropped
+term, a wrong sign, a wrong index or a transposed operand in the oracle fails
+at least one of them.
+
+Citations: "AsymSpec notes 4.1/4.2/4.4" = the AsymSpec reading notes page,
+sections 4.1 (delta-fusion), 4.2 (CDA gate), 4.4 (engineering); "RAPID
+notes design N" = the RAPID notes page, key design N.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy.spatial.distance import jensenshannon
+from scipy.special import log_softmax, logsumexp, softmax
+
+import oracle
+import workloads as W
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_constants.json")))
+LN2 = math.log(2.0)
+
+
+def _rows(B, K, V, seed, scale=2.0, dyadic=False):
+    rng = np.random.default_rng(seed)
+    x = rng.normal(0, scale, size=(3, B, K + 1, V))
+    if dyadic:  # multiples of 2^-10: shifts by small integers stay exact
+        x = np.round(x * 1024) / 1024
+    x = x.astype(np.float32)
+    draft = rng.integers(0, V, size=(B, K)).astype(np.int32)
+    return x[0], x[1], x[2], draft
+
+
+def _asym(a, b, t, draft, beta=1.0, gamma=0.5, dtype="f32"):
+    return oracle.asym(a, b, t, draft, beta, gamma, dtype)
+
+
+# ---------------------------------------------------------------- softmax / LSE
+@pytest.mark.parametrize("V", [1, 2, 3, 17, 1024])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_lse_matches_scipy(oracle_lib, V, dtype):
+    """Row log-sum-exp (the softmax normaliser of AsymSpec notes 4.2) against scipy."""
+    a, b, t, d = _rows(2, 2, V, 11 + V)
+    if dtype == "bf16":
+        a, b, t = (W.round_to_bf16(x) for x in (a, b, t))
+    r = _asym(a, b, t, d, dtype=dtype)
+    for j, x in enumerate((a, b, t)):
+        ref = logsumexp(x.astype(np.float64), axis=2)
+        np.testing.assert_allclose(r.lse[..., j], ref, rtol=1e-13, atol=1e-13)
+
+
+def test_shift_invariance(oracle_lib):
+    """Adding a constant to a row leaves its softmax unchanged: D, the fused
+    token, the test and the scan are unchanged, the normaliser moves by c."""
+    a, b, t, d = _rows(3, 2, 64, 5, dyadic=True)
+    r0 = _asym(a, b, t, d)
+    for c in (3.0, -5.0):
+        r1 = _asym(a + np.float32(c), b + np.float32(c), t + np.float32(c), d)
+        np.testing.assert_allclose(r1.D, r0.D, rtol=1e-9, atol=1e-15)
+        np.testing.assert_array_equal(r1.fused, r0.fused)
+        np.testing.assert_array_equal(r1.accept, r0.accept)
+        np.testing.assert_array_equal(r1.accept_len, r0.accept_len)
+        np.testing.assert_allclose(r1.lse, r0.lse + c, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- JSD
+@pytest.mark.parametrize("V", [2, 5, 1024, 20000])
+def test_jsd_matches_scipy(oracle_lib, V):
+    """D = JSD(softmax(a) || softmax(b)) (AsymSpec notes 4.2) against scipy's
+    Jensen-Shannon distance squared (natural log)."""
+    a, b, t, d = _rows(2, 1, V, 100 + V)
+    r = _asym(a, b, t, d)
+    for bi in range(2):
+        for i in range(2):
+            p = softmax(a[bi, i].astype(np.float64))
+            q = softmax(b[bi, i].astype(np.float64))
+            ref = jensenshannon(p, q) ** 2
+            assert r.D[bi, i] == pytest.approx(ref, rel=1e-9, abs=1e-15)
+
+
+def test_jsd_two_token_closed_form(oracle_lib):
+    """V=2: JSD = H(m) - (H(p)+H(q))/2 with binary entropies in nats."""
+    def H(x):
+        return -(x * math.log(x) + (1 - x) * math.log(1 - x))
+    for xa, xb in [(0.3, -1.2), (2.0, 2.0), (-4.0, 3.5), (0.0, 0.25)]:
+        a = np.array([[[xa, 0.0]]], np.float32)
+        b = np.array([[[xb, 0.0]]], np.float32)
+        r = _asym(a, b, a, np.zeros((1, 0), np.int32))
+        pa = 1 / (1 + math.exp(-float(np.float32(xa))))
+        pb = 1 / (1 + math.exp(-float(np.float32(xb))))
+        ref = H(0.5 * (pa + pb)) - 0.5 * (H(pa) + H(pb))
+        assert r.D[0, 0] == pytest.approx(ref, rel=1e-12, abs=1e-16)
+
+
+def test_identical_rows_give_zero_gain(oracle_lib):
+    """a == b: delta = 0 (AsymSpec notes 4.1), so D = 0 exactly, gamma_eff =
+    gamma exactly, and the fused token is argmax t (lowest index)."""
+    a, _, t, d = _rows(4, 2, 300, 9)
+    r = _asym(a, a.copy(), t, d, beta=1.7, gamma=0.45)
+    assert np.all(r.D == 0.0)
+    assert np.all(r.gamma_eff == np.float64(np.float32(0.45)))
+    np.testing.assert_array_equal(r.fused, np.argmax(t, axis=2))
+
+
+def test_disjoint_spikes_reach_ln2(oracle_lib):
+    """Distributions with disjoint support reach the ln 2 bound (AsymSpec notes 4.2)."""
+    V = 8
+    a = np.zeros((1, 1, V), np.float32)
+    b = np.zeros((1, 1, V), np.float32)
+    a[0, 0, 1] = 1000.0
+    b[0, 0, 6] = 1000.0
+    r = _asym(a, b, a, np.zeros((1, 0), np.int32), gamma=0.5)
+    assert r.D[0, 0] == pytest.approx(LN2, abs=1e-12)
+    assert r.gamma_eff[0, 0] == pytest.approx(0.25, abs=1e-12)
+
+
+def test_bounds_on_workloads(oracle_lib):
+    """JSD in [0, ln 2] hence gamma_eff in [gamma/2, gamma] (AsymSpec notes 4.2)."""
+    ub = GOLDEN["jsd_upper_bound"]["value"]
+    lo, hi = GOLDEN["gamma_eff_range"]["value"]
+    x = W.tiny_asym()
+    r = _asym(x.a, x.b, x.t, x.draft, x.beta, x.gamma)
+    g = float(np.float32(x.gamma))
+    assert np.all(r.D >= 0) and np.all(r.D <= ub)
+    assert np.all(r.gamma_eff >= lo * g - 1e-15) and np.all(r.gamma_eff <= hi * g + 1e-15)
+
+
+# ---------------------------------------------------------------- fused token
+def test_fused_steering_sign(oracle_lib):
+    """delta-fusion argmax(t + beta*(a - b)) (AsymSpec notes 4.1): a context
+    gain at index 1 moves the token there for beta > 0; beta = 0 keeps argmax t
+    with the lowest index on the tie."""
+    t = np.array([[[1.0, 1.0, 0.0]]], np.float32)
+    a = np.array([[[0.0, 2.0, 0.0]]], np.float32)
+    b = np.array([[[0.0, 0.0, 0.0]]], np.float32)
+    nod = np.zeros((1, 0), np.int32)
+    assert _asym(a, b, t, nod, beta=1.0).fused[0, 0] == 1
+    assert _asym(a, b, t, nod, beta=0.0).fused[0, 0] == 0
+    # the gain is a - b, not b - a: the same column in b pushes away
+    assert _asym(b, a, t, nod, beta=1.0).fused[0, 0] == 0
+    # strong negative gain at index 0 moves the token to index 1
+    a2 = np.array([[[-3.0, 0.0, 0.0]]], np.float32)
+    assert _asym(a2, b, t, nod, beta=0.5).fused[0, 0] == 1
+    # beta weights the gain: t favours 2 by 1.0, gain favours 0 by 0.75
+    t3 = np.array([[[0.0, 0.0, 1.0]]], np.float32)
+    a3 = np.array([[[0.75, 0.0, 0.0]]], np.float32)
+    assert _asym(a3, b, t3, nod, beta=1.0).fused[0, 0] == 2
+    assert _asym(a3, b, t3, nod, beta=2.0).fused[0, 0] == 0
+
+
+@pytest.mark.parametrize("V", [1, 2, 3, 5, 8])
+def test_fused_brute_force_tiny(oracle_lib, V):
+    """Exhaustive check of the lowest-index argmax on small integer grids,
+    where ties are frequent."""
+    rng = np.random.default_rng(V)
+    for _ in range(40):
+        a = rng.integers(-2, 3, size=(1, 1, V)).astype(np.float32)
+        b = rng.integers(-2, 3, size=(1, 1, V)).astype(np.float32)
+        t = rng.integers(-2, 3, size=(1, 1, V)).astype(np.float32)
+        beta = float(rng.integers(0, 3))
+        r = _asym(a, b, t, np.zeros((1, 0), np.int32), beta=beta)
+        f = int(r.fused[0, 0])
+        score = [float(t[0, 0, v]) + beta * (float(a[0, 0, v]) - float(b[0, 0, v])) for v in range(V)]
+        best = max(score)
+        assert score[f] == best
+        assert all(score[v] < best for v in range(f))
+        n_best = sum(s == best for s in score)
+        assert (r.gap[0, 0] == 0.0) == (n_best > 1) or V == 1
+
+
+def test_planted_ties(oracle_lib):
+    """Tie rows of the workload generator: exact tie at the fused maximum for
+    every beta >= 0, and the lowest of the tied indices is chosen."""
+    x = W.gen_asym(8, 2, 512, "bf16", seed=77, tie_frac=0.5, identical_frac=0.0)
+    rows = np.argwhere(x.tie)
+    assert len(rows) == 12
+    for beta in (0.0, 1.0, 2.0):
+        r = _asym(x.a, x.b, x.t, x.draft, beta=beta, dtype="bf16")
+        for bi, i in rows:
+            score = x.t[bi, i].astype(np.float64) + beta * (x.a[bi, i].astype(np.float64) - x.b[bi, i])
+            tied = np.flatnonzero(score == score.max())
+            assert len(tied) >= 2
+            assert r.gap[bi, i] == 0.0
+            assert r.fused[bi, i] == tied.min()
+
+
+# ---------------------------------------------------------------- acceptance test
+def test_accept_closed_form_two_tokens(oracle_lib):
+    """Test of AsymSpec notes 4.2 on V=2 rows, where softmax is the logistic
+    function: accept iff sigma(x_t) > gamma*exp(-D)*sigma(x_b)."""
+    cases = [(1.0, 0.5, 0.0, 0.5), (0.0, 1.0, 1.0, 0.5), (0.0, 1.0, 1.0, 0.9),
+             (-1.0, 1.0, -0.5, 0.2), (2.0, -3.0, 0.5, 1.0)]
+    for xt, xb, xa, g in cases:
+        t = np.array([[[xt, 0.0], [0.0, 0.0]]], np.float32)
+        b = np.array([[[xb, 0.0], [0.0, 0.0]]], np.float32)
+        a = np.array([[[xa, 0.0], [0.0, 0.0]]], np.float32)
+        d = np.array([[0]], np.int32)
+        r = _asym(a, b, t, d, beta=1.0, gamma=g)
+        sig = lambda v: 1 / (1 + math.exp(-float(np.float32(v))))
+        pa, pb = sig(xa), sig(xb)
+        H = lambda x: -(x * math.log(x) + (1 - x) * math.log(1 - x))
+        D = H(0.5 * (pa + pb)) - 0.5 * (H(pa) + H(pb))
+        gf = float(np.float32(g))
+        expect = sig(xt) > gf * math.exp(-D) * pb
+        assert bool(r.accept[0, 0]) == expect
+        margin = math.log(sig(xt)) - math.log(pb) - math.log(gf) + D
+        assert r.margin[0, 0] == pytest.approx(margin, abs=1e-12)
+
+
+def test_accept_margin_matches_scipy(oracle_lib):
+    """The log-space margin of the test, rebuilt from scipy's log_softmax and
+    Jensen-Shannon distance, and the flag agrees with its sign."""
+    a, b, t, d = _rows(5, 3, 700, 42)
+    g = 0.55
+    r = _asym(a, b, t, d, beta=0.7, gamma=g)
+    gf = float(np.float32(g))
+    for bi in range(5):
+        for i in range(3):
+            D = jensenshannon(softmax(a[bi, i].astype(np.float64)), softmax(b[bi, i].astype(np.float64))) ** 2
+            lt = log_softmax(t[bi, i].astype(np.float64))[d[bi, i]]
+            lb = log_softmax(b[bi, i].astype(np.float64))[d[bi, i]]
+            m = lt - lb - math.log(gf) + D
+            assert r.margin[bi, i] == pytest.approx(m, abs=1e-9)
+            assert bool(r.accept[bi, i]) == (m > 0)
+
+
+def test_accept_is_strict(oracle_lib):
+    """The printed test is a strict inequality (AsymSpec notes 4.2): with
+    a = b = t and gamma = 1, D = 0 and p_t(d) equals gamma_eff * p_b(d)
+    exactly, which rejects."""
+    a, _, _, d = _rows(3, 2, 50, 77)
+    r = _asym(a, a.copy(), a.copy(), d, beta=1.0, gamma=1.0)
+    assert np.all(r.D == 0.0)
+    assert np.all(r.accept == 0) and np.all(r.accept_len == 0)
+    assert np.all(r.margin == 0.0)
+
+
+def test_gamma_monotone_and_extremes(oracle_lib):
+    """A smaller gamma accepts a superset; gamma = 0 accepts every in-range
+    draft (accept length K, bonus-row token); a huge gamma rejects the first
+    draft (accept length 0, token of row 0)."""
+    a, b, t, d = _rows(6, 3, 200, 3)
+    prev = None
+    for g in (4.0, 1.0, 0.5, 0.1):
+        r = _asym(a, b, t, d, gamma=g)
+        if prev is not None:
+            assert np.all(r.accept >= prev.accept)
+            assert np.all(r.accept_len >= prev.accept_len)
+        prev = r
+    r0 = _asym(a, b, t, d, gamma=0.0)
+    assert np.all(r0.accept == 1) and np.all(r0.accept_len == 3)
+    np.testing.assert_array_equal(r0.token, r0.fused[:, 3])
+    rh = _asym(a, b, t, d, gamma=1e30)
+    assert np.all(rh.accept == 0) and np.all(rh.accept_len == 0)
+    np.testing.assert_array_equal(rh.token, rh.fused[:, 0])
+
+
+def test_scan_first_rejection(oracle_lib):
+    """Emission at the first rejection (AsymSpec notes 4.2) on a constructed
+    pattern: rows 0 and 2 accept, row 1 rejects -> length 1, token of row 1."""
+    V = 4
+    t = np.zeros((1, 4, V), np.float32)
+    b = np.zeros((1, 4, V), np.float32)
+    a = np.zeros((1, 4, V), np.float32)
+    t[0, 0, 0] = 3.0           # draft 0 strongly favoured by the verifier
+    t[0, 1, 0] = -3.0          # draft 0 disfavoured
+    t[0, 2, 0] = 3.0
+    t[0, 1, 2] = 1.0           # row 1's fused token is 2
+    d = np.zeros((1, 3), np.int32)
+    r = _asym(a, b, t, d, beta=1.0, gamma=0.5)
+    np.testing.assert_array_equal(r.accept[0], [1, 0, 1])
+    assert r.accept_len[0] == 1 and r.token[0] == 2
+
+
+def test_beta_does_not_change_gate(oracle_lib):
+    """D, gamma_eff, accept and the accept length do not depend on beta
+    (beta only enters the fused token, AsymSpec notes 4.1-4.2)."""
+    x = W.gen_asym(4, 2, 2048, "bf16", seed=5)
+    rs = [_asym(x.a, x.b, x.t, x.draft, beta=bt, gamma=0.5, dtype="bf16") for bt in (0.0, 1.0, 2.0)]
+    for r in rs[1:]:
+        np.testing.assert_array_equal(r.D, rs[0].D)
+        np.testing.assert_array_equal(r.gamma_eff, rs[0].gamma_eff)
+        np.testing.assert_array_equal(r.accept, rs[0].accept)
+        np.testing.assert_array_equal(r.accept_len, rs[0].accept_len)
+
+
+def test_standard_verification_point(oracle_lib):
+    """beta=0, gamma=1 (AsymSpec notes 4.2): the emitted-token rule becomes
+    argmax t, the CDA test accepts a superset of the fixed test
+    p_t(d) > p_b(d), and the two agree wherever D = 0."""
+    pt = GOLDEN["standard_verification_point"]["value"]
+    x = W.gen_asym(16, 2, 1024, "bf16", seed=12, identical_frac=0.3)
+    r = _asym(x.a, x.b, x.t, x.draft, beta=pt["beta"], gamma=pt["gamma"], dtype="bf16")
+    np.testing.assert_array_equal(r.fused, np.argmax(x.t, axis=2))
+    for bi in range(x.B):
+        for i in range(x.K):
+            dd = x.draft[bi, i]
+            std = softmax(x.t[bi, i].astype(np.float64))[dd] > softmax(x.b[bi, i].astype(np.float64))[dd]
+            assert (not std) or r.accept[bi, i]
+            if x.identical[bi, i]:
+                assert bool(r.accept[bi, i]) == bool(std)
+
+
+def test_bad_draft_is_rejected(oracle_lib):
+    a, b, t, d = _rows(2, 2, 16, 1)
+    d[0, 0] = 16
+    d[1, 1] = -1
+    r = _asym(a, b, t, d, gamma=0.0)
+    assert r.accept[0, 0] == 0 and r.accept[1, 1] == 0
+    assert r.accept_len[0] == 0 and r.accept_len[1] == 1
+
+
+def test_page_defaults_in_workloads():
+    """The named workloads use the pages' hyperparameters (AsymSpec notes 4.4;
+    RAPID notes, hyperparameters)."""
+    x = W.tiny_asym()
+    assert x.K == GOLDEN["asym_K"]["value"]
+    assert x.beta == GOLDEN["asym_beta"]["value"] and x.gamma == GOLDEN["asym_gamma"]["value"]
+    assert W.C3_ETAS == tuple(float(e) for e in GOLDEN["rapid_eta_self"]["value"])
+    r = W.gen_rapid(2, GOLDEN["rapid_drafts"]["value"], 64, seed=1)
+    assert r.G == 10
+
+
+# ---------------------------------------------------------------- RAPID
+def _kd_loss(z, y, T):
+    """T^2 * KL(q || softmax(z/T)) with q = softmax(y/T)."""
+    q = softmax(y / T)
+    return T * T * float(np.sum(q * (np.log(q) - log_softmax(z / T))))
+
+
+@pytest.mark.parametrize("T", [1.0, 0.7, 2.0])
+def test_zhat_is_one_kd_gradient_step(oracle_lib, T):
+    """RAPID notes design 2: zhat = z - eta * dL/dz with L = T^2 KL(q||p),
+    checked by central finite differences of L built from scipy routines."""
+    rng = np.random.default_rng(int(T * 10))
+    V = 12
+    z = rng.normal(0, 2, V)
+    y = rng.normal(0, 2, V)
+    eta = 5.0
+    h = 1e-5
+    grad = np.zeros(V)
+    for v in range(V):
+        e = np.zeros(V)
+        e[v] = h
+        grad[v] = (_kd_loss(z + e, y, T) - _kd_loss(z - e, y, T)) / (2 * h)
+    zhat = oracle.rapid_zhat(z, y, eta, T)
+    np.testing.assert_allclose(zhat, z - eta * grad, rtol=0, atol=1e-7)
+
+
+def test_eta_zero_is_plain_target(oracle_lib):
+    """eta = 0: zhat = z, so phat = p and tail protection changes nothing."""
+    rng = np.random.default_rng(4)
+    z = rng.normal(0, 2, 50)
+    y = rng.normal(0, 2, 50)
+    np.testing.assert_array_equal(oracle.rapid_zhat(z, y, 0.0, 1.3), z)
+    np.testing.assert_allclose(oracle.rapid_phat(z, y, 0.0, 1.3), softmax(z / 1.3), rtol=1e-13)
+
+
+def test_tail_protection_constructed(oracle_lib):
+    """RAPID notes design 3: tokens whose augmented probability is below 10%
+    of the peak keep the original target probability; the others take the
+    augmented one.  Row built so that tokens 2..5 are far below the peak."""
+    z = np.array([0.0, -0.5, -6.0, -7.0, -8.0, -9.0])
+    y = np.array([-0.5, 0.0, -9.0, -6.0, -8.0, -7.0])
+    eta, T = 3.0, 1.0
+    zhat = oracle.rapid_zhat(z, y, eta, T)
+    raw = softmax(zhat / T)
+    assert np.all(raw[2:] < 0.1 * raw.max()) and np.all(raw[:2] >= 0.1 * raw.max())
+    ph = oracle.rapid_phat(z, y, eta, T)
+    np.testing.assert_allclose(ph[2:], softmax(z / T)[2:], rtol=1e-13)
+    np.testing.assert_allclose(ph[:2], raw[:2], rtol=1e-13)
+    # the protected target is not renormalised
+    assert abs(ph.sum() - 1.0) > 1e-6
+
+
+def test_equal_target_and_drafter_is_noop(oracle_lib):
+    """q = p: no knowledge to transfer, zhat = z and phat = p."""
+    rng = np.random.default_rng(8)
+    z = rng.normal(0, 2, 40)
+    np.testing.assert_allclose(oracle.rapid_zhat(z, z.copy(), 20.0, 1.0), z, atol=1e-13)
+    np.testing.assert_allclose(oracle.rapid_phat(z, z.copy(), 20.0, 1.0), softmax(z), rtol=1e-12)
+
+
+def _rapid_one(z_rows, y_rows, draft, ua, us, eta, T, want_dist=False):
+    z = np.asarray(z_rows, np.float32)[None]
+    y = np.asarray(y_rows, np.float32)[None]
+    return oracle.rapid(z, y, np.asarray(draft, np.int32)[None], np.asarray(ua, np.float32)[None],
+                        np.asarray(us, np.float32)[None], eta, T, want_dist=want_dist)
+
+
+def test_inverse_cdf_draw_constructed(oracle_lib):
+    """Residual draw on a hand-built row (eta = 0): p = (.1,.2,.3,.4),
+    q = (.4,.3,.2,.1), residual max(p - q, 0) = (0, 0, .1, .3), S = .4.
+    Vocabulary-order inverse CDF: u*S below .1 -> token 2, above -> token 3."""
+    p = np.log(np.array([0.1, 0.2, 0.3, 0.4]))
+    q = np.log(np.array([0.4, 0.3, 0.2, 0.1]))
+    rows_z = [p, p]
+    rows_y = [q, q]
+    for u, tok in [(0.0, 2), (0.2, 2), (0.24, 2), (0.26, 3), (0.9, 3)]:
+        r = _rapid_one(rows_z, rows_y, [9], [0.0], [u, 0.0], 0.0, 1.0, want_dist=True)
+        # draft id 9 is outside the vocabulary: rejected, draw from row 0's residual
+        assert r.accept_len[0] == 0
+        assert r.token[0] == tok
+        assert r.resid_S[0] == pytest.approx(0.4, rel=1e-6)
+        np.testing.assert_allclose(r.emit_dist[0], [0, 0, 0.25, 0.75], atol=1e-6)
+
+
+def test_bonus_row_draws_from_target(oracle_lib):
+    """All G drafts accepted: the extra token comes from p of the last row,
+    checked with numpy's searchsorted over scipy's softmax."""
+    rng = np.random.default_rng(21)
+    G, V = 3, 30
+    z = rng.normal(0, 1, (G + 1, V)).astype(np.float32)
+    y = rng.normal(0, 1, (G + 1, V)).astype(np.float32)
+    for u in (0.05, 0.5, 0.93):
+        r = _rapid_one(z, y, [1, 2, 3], [0.0] * G, [0.1] * G + [u], 7.0, 1.0)
+        assert r.accept_len[0] == G and r.resid_S[0] == -1.0
+        p = softmax(z[G].astype(np.float64))
+        assert r.token[0] == int(np.searchsorted(np.cumsum(p), u * p.sum(), side="right"))
+
+
+def test_zero_residual_falls_back_to_target(oracle_lib):
+    """p = q and eta = 0: the residual is identically 0, so the draw uses p."""
+    rng = np.random.default_rng(2)
+    z = rng.normal(0, 1, (2, 16)).astype(np.float32)
+    r = _rapid_one(z, z, [99], [0.0], [0.6, 0.1], 0.0, 1.0)
+    assert r.accept_len[0] == 0 and r.resid_S[0] == -1.0
+    p = softmax(z[0].astype(np.float64))
+    assert r.token[0] == int(np.searchsorted(np.cumsum(p), 0.6 * p.sum(), side="right"))
+
+
+def test_temperature_placement(oracle_lib):
+    """p = softmax(z/T), q = softmax(y/T) and phat = softmax(zhat/T): running
+    with (z, y, T=2) equals running with (z/2, y/2, T=1)."""
+    rng = np.random.default_rng(13)
+    G, V = 4, 64
+    z = (np.round(rng.normal(0, 2, (3, G + 1, V)) * 256) / 256).astype(np.float32)
+    y = (np.round(rng.normal(0, 2, (3, G + 1, V)) * 256) / 256).astype(np.float32)
+    d = rng.integers(0, V, (3, G)).astype(np.int32)
+    ua = W.uniforms_2p24(rng, (3, G))
+    us = W.uniforms_2p24(rng, (3, G + 1))
+    r2 = oracle.rapid(z, y, d, ua, us, 6.0, 2.0, want_dist=True)
+    r1 = oracle.rapid(z / 2, y / 2, d, ua, us, 6.0, 1.0, want_dist=True)
+    np.testing.assert_array_equal(r2.accept, r1.accept)
+    np.testing.assert_array_equal(r2.token, r1.token)
+    np.testing.assert_allclose(r2.emit_dist, r1.emit_dist, rtol=1e-10, atol=1e-14)
+    np.testing.assert_allclose(r2.phat_draft, r1.phat_draft, rtol=1e-12)
+
+
+def _law_by_enumeration(z0, y0, eta, T, N=4000):
+    """Emitted-token law at the first draft position, by exact enumeration over
+    the draft token (weighted by q) and midpoint grids of the two uniforms,
+    every decision taken by the oracle itself."""
+    V = z0.size
+    q = softmax(y0.astype(np.float64) / T)
+    grid = ((np.arange(N) + 0.5) / N).astype(np.float32)
+    z = np.stack([z0, z0]).astype(np.float32)
+    y = np.stack([y0, y0]).astype(np.float32)
+    # acceptance probability of each draft token
+    acc = np.zeros(V)
+    for x in range(V):
+        r = oracle.rapid(np.repeat(z[None], N, 0), np.repeat(y[None], N, 0),
+                         np.full((N, 1), x, np.int32), grid[:, None],
+                         np.zeros((N, 2), np.float32), eta, T)
+        acc[x] = r.accept[:, 0].mean()
+    # draw after a rejection (an out-of-range draft forces it)
+    r = oracle.rapid(np.repeat(z[None], N, 0), np.repeat(y[None], N, 0),
+                     np.full((N, 1), V, np.int32), np.zeros((N, 1), np.float32),
+                     np.stack([grid, np.zeros(N, np.float32)], 1), eta, T)
+    draw = np.bincount(r.token, minlength=V) / N
+    p_acc = float(np.sum(q * acc))
+    return q * acc + (1.0 - p_acc) * draw, q
+
+
+@pytest.mark.parametrize("case", range(4))
+def test_sampler_law_equals_target(oracle_lib, case):
+    """RAPID notes design 4 (and its key findings): with the adjusted residual
+    the emitted token is distributed as the original target p wherever
+    p >= min(q, phat) holds pointwise -- always at eta = 0 (textbook
+    speculative sampling), and on the constructed rows for eta > 0."""
+    rng = np.random.default_rng(100 + case)
+    V = 6
+    z0 = rng.normal(0, 1.5, V).astype(np.float32)
+    if case == 0:
+        eta, y0 = 0.0, rng.normal(0, 1.5, V).astype(np.float32)
+    else:
+        eta = [2.0, 5.0, 10.0][case - 1]
+        y0 = (z0 + rng.normal(0, 0.3, V)).astype(np.float32)
+    p = softmax(z0.astype(np.float64))
+    ph = oracle.rapid_phat(z0.astype(np.float64), y0.astype(np.float64), eta, 1.0)
+    q = softmax(y0.astype(np.float64))
+    law, _ = _law_by_enumeration(z0, y0, eta, 1.0)
+    if np.all(p >= np.minimum(q, ph) - 1e-15):
+        np.testing.assert_allclose(law, p, atol=3e-3)
+    else:
+        # general law: min(q, phat) + (1 - sum min(q, phat)) * r / S
+        m = np.minimum(q, ph)
+        r = np.maximum(p - m, 0)
+        np.testing.assert_allclose(law, m + (1 - m.sum()) * r / r.sum(), atol=3e-3)
+
+
+def test_sampler_law_general_case(oracle_lib):
+    """Where phat > p and q > p on some token the law is min(q, phat) +
+    (1 - sum min(q, phat)) * r/S, no longer p; enumeration agrees."""
+    z0 = np.array([0.0, 0.2, -0.4, 0.1, -1.0], np.float32)
+    y0 = np.array([1.5, 0.0, -0.2, 0.0, -1.0], np.float32)
+    eta = 8.0
+    p = softmax(z0.astype(np.float64))
+    ph = oracle.rapid_phat(z0.astype(np.float64), y0.astype(np.float64), eta, 1.0)
+    q = softmax(y0.astype(np.float64))
+    m = np.minimum(q, ph)
+    assert np.any(p < m)  # the equality condition fails on this row
+    law, _ = _law_by_enumeration(z0, y0, eta, 1.0)
+    r = np.maximum(p - m, 0)
+    np.testing.assert_allclose(law, m + (1 - m.sum()) * r / r.sum(), atol=3e-3)
+    assert np.max(np.abs(law - p)) > 1e-2

@@ -1,0 +1,401 @@
+"""Seeded synthetic inputs for the speculative verify / logit-fusion pass.
+
+This module is shared by the fp64 oracle side and the HIP side of every test,
+by ``bench.py`` and by ``__graft_entry__.smoke``.  It draws random logits and
+plants structure (displaced spikes, identical drafter rows, exact ties); it
+holds none of the verification arithmetic itself: no softmax, no divergence,
+no acceptance rule.  Random numbers that the method consumes (the RAPID
+acceptance and residual uniforms) are drawn here and handed to both sides as
+inputs.
+
+Recipe (one logit row = one draft position of one request):
+
+* ``z0 ~ N(0, 2^2)`` over the vocabulary and one spike index ``s``;
+  ``z = z0`` with ``z[s] += 8``.
+* AsymSpec: ``a = z + N(0, 0.5^2)``, ``t = z + N(0, 0.5^2)``; ``b = z +
+  N(0, 0.5^2)`` except in an exact fraction of rows (seeded permutation) where
+  the spike is removed from ``s`` and placed at ``s' != s`` before the noise is
+  added.  Rows are produced in float64, rounded to float32 (round to nearest
+  even) and, for bf16 workloads, rounded again to bf16 (round to nearest
+  even).  Drafts are the drafter's greedy tokens ``d_i = argmax a_i`` (lowest
+  index) on the stored values, for the first K positions of each request.
+* "identical" rows set ``b := a`` bit for bit after rounding, so the context
+  gain is exactly zero.
+* "tie" rows get one column ``c`` that holds the row maxima of ``t`` and ``a``
+  and the row minimum of ``b`` (values copied from the row, so nothing leaves
+  the stored grid), and that whole column is then copied to a second index
+  ``j``.  Any fused score that is non-decreasing in ``t`` and in ``a - b``
+  (every ``t + beta*(a - b)`` with ``beta >= 0``) then has an exact tie at its
+  maximum, and ``a`` has an exact tie at its maximum, whatever the evaluation
+  order or precision.
+* RAPID: ``base = z``; target ``z_t = base + N(0, 0.5^2)``; drafter ``y =
+  base + N(0, 1)`` except in an exact fraction of rows where the spike is
+  displaced as above.  Drafts ``x_i`` are samples from the drafter's
+  tempered softmax, drawn with the Gumbel-max construction (``argmax(y/T +
+  G)``, ``G`` standard Gumbel) from a separate seeded stream.  Acceptance
+  and residual uniforms are ``k * 2^-24`` with ``k`` uniform on
+  ``[0, 2^24)``: exact in float32 and never 1.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+SEED_BASE = 7000
+
+F32 = "f32"
+BF16 = "bf16"
+
+
+# --------------------------------------------------------------------------
+# storage helpers (rounding and bit views; no method arithmetic)
+# --------------------------------------------------------------------------
+def round_to_bf16(x32: np.ndarray) -> np.ndarray:
+    """Round a float32 array to the nearest bf16 value (ties to even).
+
+    Returns float32 values that are exactly representable in bf16.
+    Inputs must be finite.
+    """
+    x32 = np.ascontiguousarray(x32, dtype=np.float32)
+    bits = x32.view(np.uint32).astype(np.uint64)
+    lsb = (bits >> 16) & 1
+    rounded = ((bits + 0x7FFF + lsb) >> 16) << 16
+    return rounded.astype(np.uint32).view(np.float32)
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Upper 16 bits of bf16-exact float32 values, as uint16 (the stored bf16)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    bits = x.view(np.uint32)
+    if np.any(bits & 0xFFFF):
+        raise ValueError("values are not bf16-exact")
+    return (bits >> 16).astype(np.uint16)
+
+
+def stored(x: np.ndarray, dtype: str) -> np.ndarray:
+    """The array exactly as a device buffer stores it (float32 or uint16 bf16 bits)."""
+    if dtype == F32:
+        return np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == BF16:
+        return bf16_bits(x)
+    raise ValueError(dtype)
+
+
+def _to_dtype(x64: np.ndarray, dtype: str) -> np.ndarray:
+    x32 = x64.astype(np.float32)
+    return round_to_bf16(x32) if dtype == BF16 else x32
+
+
+def uniforms_2p24(rng: np.random.Generator, shape) -> np.ndarray:
+    """Uniforms k * 2^-24, k ~ U{0, ..., 2^24 - 1}; exact in float32, < 1."""
+    k = rng.integers(0, 1 << 24, size=shape, dtype=np.int64)
+    return (k.astype(np.float64) * 2.0 ** -24).astype(np.float32)
+
+
+def _choose_rows(rng: np.random.Generator, pool: np.ndarray, count: int) -> np.ndarray:
+    if count <= 0:
+        return np.zeros(0, dtype=np.int64)
+    return np.sort(rng.permutation(pool)[:count])
+
+
+def _parallel_rows(R: int, V: int, nbuf: int, fn) -> None:
+    """Run ``fn(r, scratch_buffers)`` for every row; rows are independent and
+    seeded one by one, so the result does not depend on the thread count."""
+    from concurrent.futures import ThreadPoolExecutor
+    import os
+    nthreads = max(1, min(8, os.cpu_count() or 1, R))
+    chunks = [range(i, R, nthreads) for i in range(nthreads)]
+
+    def work(rows):
+        bufs = [np.empty(V, np.float64) for _ in range(nbuf)]
+        for r in rows:
+            fn(r, bufs)
+
+    if nthreads == 1:
+        work(range(R))
+        return
+    with ThreadPoolExecutor(nthreads) as ex:
+        list(ex.map(work, chunks))
+
+
+# --------------------------------------------------------------------------
+# AsymSpec inputs
+# --------------------------------------------------------------------------
+@dataclass
+class AsymInputs:
+    """Logit rows a (drafter, full context), b (drafter, compressed context),
+    t (verifier), each [B, K+1, V] float32 holding values exact in ``dtype``;
+    greedy drafts [B, K] int32; and the fusion strength / threshold."""
+
+    a: np.ndarray
+    b: np.ndarray
+    t: np.ndarray
+    draft: np.ndarray
+    dtype: str
+    beta: float
+    gamma: float
+    seed: int
+    displaced: np.ndarray = field(default=None)   # bool [B, K+1]
+    identical: np.ndarray = field(default=None)   # bool [B, K+1]
+    tie: np.ndarray = field(default=None)         # bool [B, K+1]
+    name: str = ""
+
+    @property
+    def B(self):
+        return self.a.shape[0]
+
+    @property
+    def K(self):
+        return self.a.shape[1] - 1
+
+    @property
+    def V(self):
+        return self.a.shape[2]
+
+    def stored(self, which: str) -> np.ndarray:
+        return stored(getattr(self, which), self.dtype)
+
+    def algorithmic_bytes(self) -> int:
+        es = 2 if self.dtype == BF16 else 4
+        return 3 * self.a.shape[0] * self.a.shape[1] * self.V * es
+
+
+def gen_asym(B: int, K: int, V: int, dtype: str = F32, seed: int = SEED_BASE,
+             displaced_frac: float = 0.3, identical_frac: float = 0.0,
+             tie_frac: float = 0.0, beta: float = 1.0, gamma: float = 0.5,
+             base_std: float = 2.0, spike: float = 8.0, noise_std: float = 0.5,
+             name: str = "") -> AsymInputs:
+    """Generate one AsymSpec workload following the module recipe."""
+    if B < 1 or K < 0 or V < 1:
+        raise ValueError("need B >= 1, K >= 0, V >= 1")
+    R = B * (K + 1)
+    ss = np.random.SeedSequence(seed)
+    s_rows, s_sel, s_tie = ss.spawn(3)
+    sel = np.random.default_rng(s_sel)
+
+    all_rows = np.arange(R)
+    n_ident = int(round(identical_frac * R))
+    ident_rows = _choose_rows(sel, all_rows, n_ident)
+    rest = np.setdiff1d(all_rows, ident_rows)
+    n_tie = int(round(tie_frac * R))
+    tie_rows = _choose_rows(sel, rest, min(n_tie, rest.size))
+    n_disp = int(round(displaced_frac * R))
+    disp_pool = rest if V > 1 else np.zeros(0, dtype=np.int64)
+    disp_rows = _choose_rows(sel, disp_pool, min(n_disp, disp_pool.size))
+
+    displaced = np.zeros(R, bool)
+    displaced[disp_rows] = True
+    identical = np.zeros(R, bool)
+    identical[ident_rows] = True
+    tie = np.zeros(R, bool)
+    tie[tie_rows] = True
+
+    a = np.empty((R, V), np.float32)
+    b = np.empty((R, V), np.float32)
+    t = np.empty((R, V), np.float32)
+    row_seeds = s_rows.spawn(R)
+
+    def make_row(r, bufs):
+        z0, z, n, zb = bufs
+        g = np.random.default_rng(row_seeds[r])
+        g.standard_normal(out=z0)
+        z0 *= base_std
+        s = int(g.integers(0, V))
+        np.copyto(z, z0)
+        z[s] += spike
+        g.standard_normal(out=n)
+        n *= noise_std
+        n += z
+        a[r] = _to_dtype(n, dtype)
+        g.standard_normal(out=n)
+        n *= noise_std
+        n += z
+        t[r] = _to_dtype(n, dtype)
+        if displaced[r]:
+            s2 = int(g.integers(0, V - 1))
+            s2 = s2 + 1 if s2 >= s else s2
+            np.copyto(zb, z0)
+            zb[s2] += spike
+            src_b = zb
+        else:
+            src_b = z
+        g.standard_normal(out=n)
+        n *= noise_std
+        n += src_b
+        b[r] = _to_dtype(n, dtype)
+        if identical[r]:
+            b[r] = a[r]
+
+    _parallel_rows(R, V, 4, make_row)
+
+    gt = np.random.default_rng(s_tie)
+    for r in tie_rows:
+        if V < 2:
+            continue
+        c = int(gt.integers(0, V))
+        j = int(gt.integers(0, V - 1))
+        j = j + 1 if j >= c else j
+        a[r, c] = a[r].max()
+        t[r, c] = t[r].max()
+        b[r, c] = b[r].min()
+        a[r, j], b[r, j], t[r, j] = a[r, c], b[r, c], t[r, c]
+
+    a = a.reshape(B, K + 1, V)
+    b = b.reshape(B, K + 1, V)
+    t = t.reshape(B, K + 1, V)
+    draft = np.argmax(a[:, :K, :], axis=2).astype(np.int32) if K > 0 else np.zeros((B, 0), np.int32)
+    return AsymInputs(a=a, b=b, t=t, draft=np.ascontiguousarray(draft), dtype=dtype,
+                      beta=float(beta), gamma=float(gamma), seed=seed,
+                      displaced=displaced.reshape(B, K + 1),
+                      identical=identical.reshape(B, K + 1),
+                      tie=tie.reshape(B, K + 1), name=name)
+
+
+# --------------------------------------------------------------------------
+# RAPID inputs
+# --------------------------------------------------------------------------
+@dataclass
+class RapidInputs:
+    """Target logits z and RAG-drafter logits y, each [B, G+1, V] float32
+    holding values exact in ``dtype``; drafts [B, G] int32 sampled from the
+    drafter; uniforms u_accept [B, G] and u_sample [B, G+1] float32."""
+
+    z: np.ndarray
+    y: np.ndarray
+    draft: np.ndarray
+    u_accept: np.ndarray
+    u_sample: np.ndarray
+    dtype: str
+    eta: float
+    T: float
+    seed: int
+    displaced: np.ndarray = field(default=None)
+    name: str = ""
+
+    @property
+    def B(self):
+        return self.z.shape[0]
+
+    @property
+    def G(self):
+        return self.z.shape[1] - 1
+
+    @property
+    def V(self):
+        return self.z.shape[2]
+
+    def stored(self, which: str) -> np.ndarray:
+        return stored(getattr(self, which), self.dtype)
+
+    def algorithmic_bytes(self) -> int:
+        es = 2 if self.dtype == BF16 else 4
+        return 2 * self.z.shape[0] * self.z.shape[1] * self.V * es
+
+
+def gen_rapid(B: int, G: int, V: int, dtype: str = F32, seed: int = SEED_BASE + 3,
+              displaced_frac: float = 0.4, eta: float = 10.0, T: float = 1.0,
+              base_std: float = 2.0, spike: float = 8.0, target_std: float = 0.5,
+              drafter_std: float = 1.0, name: str = "") -> RapidInputs:
+    """Generate one RAPID workload following the module recipe."""
+    if B < 1 or G < 0 or V < 1:
+        raise ValueError("need B >= 1, G >= 0, V >= 1")
+    R = B * (G + 1)
+    ss = np.random.SeedSequence(seed)
+    s_rows, s_sel, s_draft, s_unif = ss.spawn(4)
+    sel = np.random.default_rng(s_sel)
+    n_disp = int(round(displaced_frac * R)) if V > 1 else 0
+    disp_rows = _choose_rows(sel, np.arange(R), n_disp)
+    displaced = np.zeros(R, bool)
+    displaced[disp_rows] = True
+
+    z = np.empty((R, V), np.float32)
+    y = np.empty((R, V), np.float32)
+    row_seeds = s_rows.spawn(R)
+
+    def make_row(r, bufs):
+        z0, base, n, yb = bufs
+        g = np.random.default_rng(row_seeds[r])
+        g.standard_normal(out=z0)
+        z0 *= base_std
+        s = int(g.integers(0, V))
+        np.copyto(base, z0)
+        base[s] += spike
+        g.standard_normal(out=n)
+        n *= target_std
+        n += base
+        z[r] = _to_dtype(n, dtype)
+        if displaced[r]:
+            s2 = int(g.integers(0, V - 1))
+            s2 = s2 + 1 if s2 >= s else s2
+            np.copyto(yb, z0)
+            yb[s2] += spike
+            src_y = yb
+        else:
+            src_y = base
+        g.standard_normal(out=n)
+        n *= drafter_std
+        n += src_y
+        y[r] = _to_dtype(n, dtype)
+
+    _parallel_rows(R, V, 4, make_row)
+    z = z.reshape(B, G + 1, V)
+    y = y.reshape(B, G + 1, V)
+
+    # Drafter sampling: Gumbel-max over the stored drafter logits.
+    gd = np.random.default_rng(s_draft)
+    draft = np.zeros((B, G), np.int32)
+    for bi in range(B):
+        for i in range(G):
+            u = gd.random(V)
+            u = np.where(u <= 0.0, np.finfo(np.float64).tiny, u)
+            gumbel = -np.log(-np.log(u))
+            draft[bi, i] = int(np.argmax(y[bi, i].astype(np.float64) / T + gumbel))
+    gu = np.random.default_rng(s_unif)
+    u_accept = uniforms_2p24(gu, (B, G))
+    u_sample = uniforms_2p24(gu, (B, G + 1))
+    return RapidInputs(z=z, y=y, draft=draft, u_accept=u_accept, u_sample=u_sample,
+                       dtype=dtype, eta=float(eta), T=float(T), seed=seed,
+                       displaced=displaced.reshape(B, G + 1), name=name)
+
+
+# --------------------------------------------------------------------------
+# The five named workloads
+# --------------------------------------------------------------------------
+VOCAB_QWEN3 = 151936     # vocabulary width of the drafter/verifier family in the AsymSpec setup
+VOCAB_LLAMA31 = 128256   # vocabulary width of the RAPID target family
+
+C2_BETAS = (0.0, 1.0, 2.0)
+C2_GAMMAS = (0.4, 0.5, 0.7, 1.0)
+C3_ETAS = (5.0, 10.0, 20.0)
+
+
+def tiny_asym(seed: int = SEED_BASE + 0) -> AsymInputs:
+    """B=4, K=2, V=1024, fp32; beta=1, gamma=0.5."""
+    return gen_asym(4, 2, 1024, F32, seed, displaced_frac=0.3, beta=1.0, gamma=0.5,
+                    name="asym_tiny_B4_K2_V1024_f32")
+
+
+def single_asym(seed: int = SEED_BASE + 1) -> AsymInputs:
+    """B=1, K=2, V=151936, fp32; beta=1, gamma=0.5."""
+    return gen_asym(1, 2, VOCAB_QWEN3, F32, seed, displaced_frac=0.3, beta=1.0, gamma=0.5,
+                    name="asym_single_B1_K2_V151936_f32")
+
+
+def batched_asym(seed: int = SEED_BASE + 2, beta: float = 1.0, gamma: float = 0.5) -> AsymInputs:
+    """B=64, K=2, V=151936, bf16; the (beta, gamma) grid is swept on these inputs."""
+    return gen_asym(64, 2, VOCAB_QWEN3, BF16, seed, displaced_frac=0.3, beta=beta,
+                    gamma=gamma, name="asym_batched_B64_K2_V151936_bf16")
+
+
+def rapid_c3(seed: int = SEED_BASE + 3, eta: float = 10.0) -> RapidInputs:
+    """B=16, G=10, V=128256, fp32, T=1; eta in {5, 10, 20}."""
+    return gen_rapid(16, 10, VOCAB_LLAMA31, F32, seed, displaced_frac=0.4, eta=eta, T=1.0,
+                     name="rapid_B16_G10_V128256_f32")
+
+
+def large_asym(seed: int = SEED_BASE + 4, beta: float = 1.0, gamma: float = 0.5) -> AsymInputs:
+    """B=256, K=4, V=151936, bf16; 20% identical drafter rows, 5% planted ties."""
+    return gen_asym(256, 4, VOCAB_QWEN3, BF16, seed, displaced_frac=0.3,
+                    identical_frac=0.2, tie_frac=0.05, beta=beta, gamma=gamma,
+                    name="asym_large_B256_K4_V151936_bf16")

@@ -1,0 +1,190 @@
+"""Benchmark of the verification / logit-fusion pass on one MI355X.
+
+One step = one ``asym_verify`` call over the large batched AsymSpec workload
+(B=256 requests, K=4 drafts -> 1280 rows of a, b, t, V=151936, bf16), with
+inputs resident in HBM.  Prints one JSON line: verified logit rows/s, the
+dominant kernel's roofline (HBM bytes per launch over its event-timed
+duration, against 8 TB/s), the B=64/K=2 workload and the RAPID pass as
+secondary figures, and the fp64 CPU oracle timed on the host as a reported
+baseline.
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "verified logit rows/s (B·(K+1)·V) and achieved HBM GB/s vs peak, 1 GPU"
+PEAK_HBM_GBS = 8000.0
+
+
+def _say(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def _device_inputs(vwl, x, copies=1):
+    import torch
+    sets = []
+    base = [vwl.to_device_logits(getattr(x, n), x.dtype) for n in ("a", "b", "t")]
+    draft = torch.from_numpy(x.draft).cuda()
+    for c in range(copies):
+        sets.append(([t.clone() for t in base] if c else base, draft))
+    return sets
+
+
+def time_asym(vwl, x, steps, warmup, copies=1):
+    """Event-timed asym_verify calls on torch's current stream (the stream the
+    library launches on).  Returns (total seconds, per-call ms list)."""
+    import torch
+    sets = _device_inputs(vwl, x, copies)
+    B, K = x.B, x.K
+    out = vwl.asym_out(B, K, "cuda")
+    stream = torch.cuda.current_stream()
+    ws = vwl._workspace(0, B, K, x.V, vwl.VWL_BF16 if x.dtype == "bf16" else vwl.VWL_F32,
+                        torch.device("cuda", torch.cuda.current_device()), stream)
+    for i in range(warmup):
+        (a, b, t), d = sets[i % copies]
+        vwl.asym_verify(a, b, t, d, x.beta, x.gamma, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        (a, b, t), d = sets[i % copies]
+        ev[i][0].record(stream)
+        vwl.asym_verify(a, b, t, d, x.beta, x.gamma, out=out, workspace=ws)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [s.elapsed_time(e) for s, e in ev]
+    if int(out.dev_err.cpu()[0]) != 0:
+        raise RuntimeError("device error bits set: %d" % int(out.dev_err.cpu()[0]))
+    return wall, per
+
+
+def time_rapid(vwl, x, steps, warmup):
+    import torch
+    z = vwl.to_device_logits(x.z, x.dtype)
+    y = vwl.to_device_logits(x.y, x.dtype)
+    d = torch.from_numpy(x.draft).cuda()
+    ua = torch.from_numpy(x.u_accept).cuda()
+    us = torch.from_numpy(x.u_sample).cuda()
+    out = vwl.rapid_out(x.B, x.G, x.V, "cuda")
+    for _ in range(warmup):
+        vwl.rapid_verify(z, y, d, ua, us, x.eta, x.T, out=out)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        vwl.rapid_verify(z, y, d, ua, us, x.eta, x.T, out=out)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return [s.elapsed_time(e) for s, e in ev]
+
+
+def _median(v):
+    v = sorted(v)
+    return v[len(v) // 2]
+
+
+def cpu_baseline(x, runs=3):
+    """The fp64 oracle as it stands, on all host cores, over the same call."""
+    import oracle
+    oracle.build(force=False)
+    times = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        oracle.asym(x.a, x.b, x.t, x.draft, x.beta, x.gamma, x.dtype)
+        times.append(time.perf_counter() - t0)
+    t = _median(times)
+    rows = x.B * (x.K + 1)
+    return {"value": rows / t, "unit": "rows/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": "the full B=%d, K=%d, V=%d %s call, median of %d runs (%.2f s each)" % (
+                x.B, x.K, x.V, x.dtype, runs, t)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the pass is independent per request; see DESIGN.md for how it shards). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import vocab_wide_logit_amd as vwl
+    import workloads as W
+
+    torch.cuda.set_device(0)
+    vwl.load_library()
+    _say("generating B=256 K=4 V=151936 bf16 inputs")
+    x = W.large_asym()
+    plan = vwl.plan_info("asym", x.B, x.K, x.V, torch.bfloat16)
+    _say("plan %s; timing %d steps after %d warmup" % (plan, args.steps, args.warmup))
+    wall, per = time_asym(vwl, x, args.steps, args.warmup)
+    rows = x.B * (x.K + 1)
+    bytes_per_call = x.algorithmic_bytes()
+    ms_step = wall * 1e3 / args.steps
+    ms_kernel = sum(per) / len(per)
+    achieved = bytes_per_call / (ms_kernel * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": rows * args.steps / wall,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": x.name, "B": x.B, "K": x.K, "V": x.V, "logits": "bf16",
+                   "beta": x.beta, "gamma": x.gamma, "rows_per_step": rows,
+                   "identical_rows": 0.2, "tie_rows": 0.05, "plan": plan},
+        "tokens_verified_per_s": x.B * x.K * args.steps / wall,
+        "hbm_gbs_per_step": bytes_per_call * args.steps / wall / 1e9,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                     "kernel": "asym_rows_kernel<bf16,%d>" % plan["vec_per_thread"],
+                     "bytes_per_launch": bytes_per_call, "avg_launch_ms": ms_kernel,
+                     "p10_ms": sorted(per)[len(per) // 10], "p90_ms": sorted(per)[(9 * len(per)) // 10]},
+    }
+    if not args.no_extra:
+        _say("secondary: B=64 K=2 bf16 (4 rotating copies) and RAPID B=16 G=10 fp32")
+        x2 = W.batched_asym()
+        _, per2 = time_asym(vwl, x2, args.steps, args.warmup, copies=4)
+        ms2 = _median(per2)
+        b2 = x2.algorithmic_bytes()
+        r3 = W.rapid_c3()
+        per3 = time_rapid(vwl, r3, args.steps, args.warmup)
+        ms3 = _median(per3)
+        b3 = r3.algorithmic_bytes()
+        result["secondary"] = {
+            x2.name: {"rows_per_s": x2.B * 3 / (ms2 * 1e-3), "median_call_ms": ms2,
+                      "gbs": b2 / (ms2 * 1e-3) / 1e9, "frac_of_peak": b2 / (ms2 * 1e-3) / 1e9 / PEAK_HBM_GBS},
+            r3.name: {"rows_per_s": r3.B * 11 / (ms3 * 1e-3), "median_call_ms": ms3,
+                      "gbs": b3 / (ms3 * 1e-3) / 1e9, "frac_of_peak": b3 / (ms3 * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                      "eta": r3.eta},
+        }
+    if not args.no_cpu_baseline:
+        _say("timing the fp64 oracle on the host")
+        result["cpu_baseline"] = cpu_baseline(x)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

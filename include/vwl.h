@@ -1,0 +1,203 @@
+/*
+ * vwl.h -- speculative verification and logit fusion over vocabulary-wide
+ * logit rows, on AMD Instinct MI355X (gfx950).
+ *
+ * Two entry points, one per method:
+ *
+ *   asym_verify   AsymSpec ("AsymSpec: Context-Asymmetric Speculative
+ *                 Decoding for Agentic LLMs" reading notes, section 4.1
+ *                 "contrastive delta-fusion" and section 4.2 "CDA gate").
+ *   rapid_verify  RAPID ("RAPID: Long-Context Inference with
+ *                 Retrieval-Augmented Speculative Decoding" notes, key
+ *                 designs 2 "retrieval-augmented target distribution",
+ *                 3 "tail protection" and 4 "adjusted residual sampling",
+ *                 with the rejection-sampling loop of its overall framework).
+ *
+ * Conventions shared by every call:
+ *   - Every data pointer is a DEVICE pointer on the current HIP device.  The
+ *     caller allocates and owns every buffer; the library never allocates,
+ *     frees or synchronises.  Every call is asynchronous on `stream`.
+ *   - Logit tensors are contiguous, row-major [B][P][V] (P positions per
+ *     request), in the dtype given, with 16-byte-aligned base pointers; any
+ *     V >= 1 is accepted (rows that do not start on a 16-byte boundary are
+ *     peeled).  Index arrays are int32 and uniforms fp32 (4-byte aligned),
+ *     flags uint8.  A misaligned pointer returns VWL_ERR_ALIGN.
+ *   - Host-side argument checks run synchronously and return a status; a
+ *     failed launch returns VWL_ERR_HIP (from hipGetLastError).
+ *   - Device-side data faults cannot be reported synchronously; they get
+ *     defined behaviour and set bits in *dev_err when dev_err is non-null
+ *     (the kernels OR bits in; the caller clears it):
+ *       VWL_DEVERR_DRAFT    a draft id outside [0, V): that draft is rejected
+ *       VWL_DEVERR_UNIFORM  a uniform outside [0, 1) or NaN: clamped into [0, 1)
+ *       VWL_DEVERR_TIMEOUT  a workgroup waited more than ~2 s for the others
+ *                           of its row (only possible when the device is
+ *                           starved); outputs of that call are undefined and
+ *                           the workspace must be reset with vwl_workspace_reset
+ *   - Workspace: 256-byte-aligned device memory of at least the size the
+ *     matching *_workspace_bytes query returns for the same shape (the size
+ *     depends on the shape and dtype only, not on the device).  It must be
+ *     zero-filled before its first use (vwl_workspace_reset does that); every
+ *     completed call leaves it zero-filled again.  Two calls that share one
+ *     workspace must be ordered (same stream, or synchronised).
+ *   - Results are bitwise deterministic for identical inputs, shape and device.
+ */
+#ifndef VWL_H
+#define VWL_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    VWL_OK = 0,
+    VWL_ERR_NULL = 1,      /* a required pointer is null */
+    VWL_ERR_SHAPE = 2,     /* B, K/G or V out of range, or sizes overflow */
+    VWL_ERR_DTYPE = 3,     /* unknown dtype */
+    VWL_ERR_PARAM = 4,     /* beta, gamma, eta or T out of range */
+    VWL_ERR_WORKSPACE = 5, /* workspace smaller than the query returns */
+    VWL_ERR_HIP = 6,       /* a HIP runtime call or kernel launch failed */
+    VWL_ERR_ALIGN = 7      /* a pointer is not aligned as documented */
+} vwl_status;
+
+typedef enum { VWL_F32 = 0, VWL_BF16 = 1 } vwl_dtype;
+
+#define VWL_DEVERR_DRAFT 1
+#define VWL_DEVERR_UNIFORM 2
+#define VWL_DEVERR_TIMEOUT 4
+
+#define VWL_MAX_K 63 /* drafts per request, both methods */
+
+/* Human-readable name of a status code (static storage). */
+const char *vwl_status_string(vwl_status s);
+
+/* Library version as an integer: major*10000 + minor*100 + patch. */
+int vwl_version(void);
+
+/* Zero-fill `bytes` of workspace on `stream` with a fill kernel (no memset
+ * node, so it may be captured into a graph).  Returns VWL_ERR_NULL for a null
+ * pointer with bytes > 0. */
+vwl_status vwl_workspace_reset(void *workspace, size_t bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * AsymSpec verification (AsymSpec notes, sections 4.1-4.2)
+ *
+ * For request b and position i in [0, K] (row r = b*(K+1) + i):
+ *   L_x      = log sum_v exp(x_v)           for x in {a_i, b_i, t_i}
+ *   D_i      = JSD(softmax(a_i) || softmax(b_i)), natural log, in [0, ln 2]
+ *   geff_i   = gamma * exp(-D_i)            (section 4.2, the CDA threshold)
+ *   fused_i  = lowest v maximising t_v + beta*(a_v - b_v)   (section 4.1)
+ *   for i < K, with d = draft[b][i]:
+ *   accept_i = softmax(t_i)[d] > geff_i * softmax(b_i)[d]   (section 4.2),
+ *              evaluated as (t_d - L_t) - (b_d - L_b) > log(gamma) - D_i
+ *   accept_len[b] = first i < K with accept_i == 0, else K
+ *   token[b]      = fused[b][accept_len[b]]  (the delta-fusion token at the
+ *                   first rejection; the bonus row K when all are accepted)
+ *
+ * Inputs:
+ *   a, b, t   [B][K+1][V] logits of dtype `dt`: drafter on the full context,
+ *             drafter on the compressed context, verifier on the compressed
+ *             context.  Row i of request b holds position i.
+ *   draft     [B][K] int32 draft ids (may be null when K == 0).
+ *   B >= 1, 0 <= K <= VWL_MAX_K, V >= 1; B*(K+1)*V must fit in int64.
+ *   beta      finite (any sign); gamma finite and >= 0.
+ * Outputs (all required; written in full by every successful call):
+ *   D, gamma_eff  [B][K+1] fp32
+ *   accept        [B][K]   uint8 (may be null when K == 0)
+ *   fused         [B][K+1] int32
+ *   accept_len, token  [B] int32
+ *   dev_err       [1] int32, nullable; bits are OR-ed in.
+ * Precision: per-lane fp32 arithmetic on the widened logits, fp64 for every
+ *   combine across lanes and workgroups and for the row scalars.
+ * --------------------------------------------------------------------------- */
+size_t vwl_asym_workspace_bytes(int B, int K, int V, vwl_dtype dt);
+
+vwl_status asym_verify(const void *a, const void *b, const void *t,
+                       const int32_t *draft,
+                       int B, int K, int V, vwl_dtype dt, float beta, float gamma,
+                       float *D, float *gamma_eff, uint8_t *accept, int32_t *fused,
+                       int32_t *accept_len, int32_t *token, int32_t *dev_err,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * RAPID verification (RAPID notes, key designs 2-4)
+ *
+ * For request b and position i in [0, G] (G drafts, the page's "gamma"):
+ *   p = softmax(z_i / T), q = softmax(y_i / T)
+ *   zhat = z_i + eta*T*(q - p)                       (design 2)
+ *   phat_raw = softmax(zhat / T)
+ *   phat_v = p_v where phat_raw_v < 0.1 * max phat_raw, else phat_raw_v
+ *            (design 3; no renormalisation afterwards)
+ *   for i < G, with x = draft[b][i] and u = u_accept[b][i]:
+ *   accept_i = u * q(x) < phat(x)     (rejection sampling against phat)
+ *   n = accept_len[b] = first i < G with accept_i == 0, else G
+ *   token[b]: if n < G, the residual r = max(p - phat, p - q, 0) of row n
+ *             (design 4), S = sum r, token = smallest k with
+ *             sum_{v<=k} r_v > u_sample[b][n] * S; when S == 0, or when
+ *             n == G (all drafts accepted), the same inverse-CDF rule on p
+ *             of row n with u_sample[b][n].
+ *
+ * Inputs:
+ *   z, y      [B][G+1][V] target and RAG-drafter logits of dtype `dt`.
+ *   draft     [B][G] int32 (may be null when G == 0).
+ *   u_accept  [B][G] fp32 in [0,1) (may be null when G == 0);
+ *   u_sample  [B][G+1] fp32 in [0,1).
+ *   B >= 1, 0 <= G <= VWL_MAX_K, V >= 1; eta finite and >= 0; T finite and > 0.
+ * Outputs:
+ *   accept     [B][G] uint8 (may be null when G == 0)
+ *   accept_len, token  [B] int32 (required)
+ *   p_hat_draft, q_draft  [B][G] fp32, nullable: phat(x_i) and q(x_i)
+ *   emit_dist  [B][V] fp32, nullable: the normalised distribution the token
+ *              was drawn from (r/S, or p of row n)
+ *   dev_err    [1] int32, nullable.
+ * Precision: fp32 element arithmetic with fp64 sums for the row statistics;
+ *   the emitting row's residual, its sums and the inverse CDF in fp64.
+ * --------------------------------------------------------------------------- */
+size_t vwl_rapid_workspace_bytes(int B, int G, int V, vwl_dtype dt);
+
+vwl_status rapid_verify(const void *z, const void *y, const int32_t *draft,
+                        const float *u_accept, const float *u_sample,
+                        int B, int G, int V, vwl_dtype dt, float eta, float T,
+                        uint8_t *accept, int32_t *accept_len, int32_t *token,
+                        float *p_hat_draft, float *q_draft, float *emit_dist,
+                        int32_t *dev_err, void *workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Launch-plan inspection (host only; no device memory is touched).
+ * Fills `out` with: [0] workgroups per row (team size), [1] 16-byte vectors
+ * per thread per tensor, [2] teams, [3] grid size, [4] threads per
+ * workgroup, [5] rows.  Returns VWL_OK or an argument status.
+ * mode 0 = AsymSpec, 1 = RAPID (G in place of K).
+ * --------------------------------------------------------------------------- */
+vwl_status vwl_plan_info(int mode, int B, int K, int V, vwl_dtype dt, int64_t out[6]);
+
+/* Host-only argument check of asym_verify / rapid_verify: the same checks,
+ * in the same order, without launching anything.  Lets a caller (or a test
+ * on a machine without a GPU) validate arguments; `workspace_bytes` is
+ * compared against `needed_bytes` instead of querying the device. */
+vwl_status vwl_asym_check(const void *a, const void *b, const void *t, const int32_t *draft,
+                          int B, int K, int V, int dt, float beta, float gamma,
+                          const void *D, const void *gamma_eff, const void *accept,
+                          const void *fused, const void *accept_len, const void *token,
+                          const void *workspace, size_t workspace_bytes, size_t needed_bytes);
+
+vwl_status vwl_rapid_check(const void *z, const void *y, const int32_t *draft,
+                           const float *u_accept, const float *u_sample,
+                           int B, int G, int V, int dt, float eta, float T,
+                           const void *accept, const void *accept_len, const void *token,
+                           const void *workspace, size_t workspace_bytes, size_t needed_bytes);
+
+/* Tuning hook: pin the vectors-per-thread choice (1, 2, 4 or 8; 0 = automatic)
+ * and cap the number of teams (0 = no cap) of one mode (0 = AsymSpec,
+ * 1 = RAPID) for later calls in this process.  Results do not depend on the
+ * plan except through the documented fp32 summation order of the partials. */
+vwl_status vwl_set_plan_override(int mode, int nv, int max_teams);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VWL_H */

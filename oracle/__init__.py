@@ -63,10 +63,10 @@ def _load():
     P = ctypes.c_void_p
     i = ctypes.c_int
     d = ctypes.c_double
-    lib.vwl_oracle_asym.argtypes = [P, P, P, i, P, i, i, i, d, d, P, P, P, P, P, P, P, P, P, i]
+    lib.vwl_oracle_asym.argtypes = [P, P, P, i, P, i, i, i, d, d, P, P, P, P, P, P, P, P, P, P, i]
     lib.vwl_oracle_asym.restype = i
     lib.vwl_oracle_rapid.argtypes = [P, P, i, P, P, P, i, i, i, d, d,
-                                     P, P, P, P, P, P, P, P, P, P, P, d, P, i]
+                                     P, P, P, P, P, P, P, P, P, P, P, d, P, P, i]
     lib.vwl_oracle_rapid.restype = i
     lib.vwl_oracle_rapid_zhat.argtypes = [P, P, i, d, d, P]
     lib.vwl_oracle_rapid_zhat.restype = i
@@ -108,6 +108,7 @@ class AsymResult:
     gamma_eff: np.ndarray  # [B, K+1]
     fused: np.ndarray      # [B, K+1] int32
     gap: np.ndarray        # [B, K+1]
+    top: np.ndarray        # [B, K+1] maximum fused score
     accept: np.ndarray     # [B, K] uint8
     margin: np.ndarray     # [B, K]
     accept_len: np.ndarray  # [B] int32
@@ -133,18 +134,19 @@ def asym(a, b, t, draft, beta: float, gamma: float, dtype: str = "f32",
     ge = np.zeros((B, P))
     fused = np.zeros((B, P), np.int32)
     gap = np.zeros((B, P))
+    top = np.zeros((B, P))
     acc = np.zeros((B, max(K, 0)), np.uint8)
     margin = np.zeros((B, max(K, 0)))
     alen = np.zeros(B, np.int32)
     tok = np.zeros(B, np.int32)
     rc = lib.vwl_oracle_asym(_ptr(sa), _ptr(sb), _ptr(st), dt, _ptr(draft), B, K, V,
                              float(np.float32(beta)), float(np.float32(gamma)),
-                             _ptr(lse), _ptr(D), _ptr(ge), _ptr(fused), _ptr(gap),
+                             _ptr(lse), _ptr(D), _ptr(ge), _ptr(fused), _ptr(gap), _ptr(top),
                              _ptr(acc), _ptr(margin), _ptr(alen), _ptr(tok), int(nthreads))
     if rc != 0:
         raise RuntimeError("oracle asym failed with code %d" % rc)
     del R
-    return AsymResult(lse, D, ge, fused, gap, acc, margin, alen, tok)
+    return AsymResult(lse, D, ge, fused, gap, top, acc, margin, alen, tok)
 
 
 @dataclass
@@ -161,6 +163,7 @@ class RapidResult:
     draw_slack: np.ndarray  # [B]
     tail_close: np.ndarray  # [B]
     emit_dist: np.ndarray | None  # [B, V]
+    emit_scale: np.ndarray | None  # [B, V] p + max(phat, q) on the emitting row
 
 
 def rapid(z, y, draft, u_accept, u_sample, eta: float, T: float, dtype: str = "f32",
@@ -186,15 +189,16 @@ def rapid(z, y, draft, u_accept, u_sample, eta: float, T: float, dtype: str = "f
     slack = np.zeros(B)
     close = np.zeros(B, np.int32)
     dist = np.zeros((B, V)) if want_dist else None
+    scale = np.zeros((B, V)) if want_dist else None
     rc = lib.vwl_oracle_rapid(_ptr(sz), _ptr(sy), dt, _ptr(draft), _ptr(ua), _ptr(us),
                               B, G, V, float(np.float32(eta)), float(np.float32(T)),
                               _ptr(rowstat), _ptr(phd), _ptr(qd), _ptr(acc), _ptr(arel), _ptr(tdd),
                               _ptr(alen), _ptr(tok), _ptr(rs), _ptr(slack), _ptr(close),
                               float(tail_eps), _ptr(dist) if dist is not None else None,
-                              int(nthreads))
+                              _ptr(scale) if scale is not None else None, int(nthreads))
     if rc != 0:
         raise RuntimeError("oracle rapid failed with code %d" % rc)
-    return RapidResult(rowstat, phd, qd, acc, arel, tdd, alen, tok, rs, slack, close, dist)
+    return RapidResult(rowstat, phd, qd, acc, arel, tdd, alen, tok, rs, slack, close, dist, scale)
 
 
 def rapid_zhat(z: np.ndarray, y: np.ndarray, eta: float, T: float) -> np.ndarray:

@@ -109,6 +109,7 @@ static double logsumexp(const double *x, int n)
  *   geff[R]        gamma * exp(-D)
  *   fused[R]       lowest index maximising t + beta*(a - b)
  *   gap[R]         top1 - top2 of that score (0 for an exact tie)
+ *   top[R]         top1, the maximum of that score
  *   accept[B][K]   acceptance flag of draft i at row i (0 for an id outside [0,V))
  *   margin[B][K]   log p_t(d) - log p_b(d) - log gamma + D  (NaN for a bad id)
  *   accept_len[B], token[B]
@@ -117,7 +118,7 @@ int vwl_oracle_asym(const void *a, const void *b, const void *t, int dtype,
                     const int32_t *draft, int B, int K, int V,
                     double beta, double gamma,
                     double *lse, double *D, double *geff, int32_t *fused, double *gap,
-                    uint8_t *accept, double *margin,
+                    double *top, uint8_t *accept, double *margin,
                     int32_t *accept_len, int32_t *token, int nthreads)
 {
     if (B < 1 || K < 0 || V < 1 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16))
@@ -184,6 +185,7 @@ int vwl_oracle_asym(const void *a, const void *b, const void *t, int dtype,
                 }
                 fused[r] = arg;
                 gap[r] = (V > 1) ? best - second : INFINITY;
+                top[r] = best;
 
                 /* acceptance of the draft tested at this row */
                 const long bi = r / P;
@@ -265,6 +267,9 @@ static int draw_inverse_cdf(const double *w, int V, double S, double u, double *
  *   draw_slack[B]  relative distance of u*S to the chosen interval's ends
  *   tail_close[B]  number of tokens of the emitting row with |zhat/T - Mhat - ln 0.1| <= tail_eps
  *   emit_dist[B][V] (nullable) the distribution the token was drawn from
+ *   emit_scale[B][V] (nullable) p + max(phat, q) per token of the emitting row
+ *                   (p alone for a draw from p): the magnitude the residual's
+ *                   subtractions start from, used for rounding allowances
  */
 int vwl_oracle_rapid(const void *z, const void *y, int dtype,
                      const int32_t *draft, const float *u_accept, const float *u_sample,
@@ -273,7 +278,7 @@ int vwl_oracle_rapid(const void *z, const void *y, int dtype,
                      double *acc_rel, double *tail_d_dist,
                      int32_t *accept_len, int32_t *token,
                      double *resid_S, double *draw_slack, int32_t *tail_close, double tail_eps,
-                     double *emit_dist, int nthreads)
+                     double *emit_dist, double *emit_scale, int nthreads)
 {
     if (B < 1 || G < 0 || V < 1 || !(T > 0.0) || (dtype != ORACLE_F32 && dtype != ORACLE_BF16))
         return 1;
@@ -401,6 +406,8 @@ int vwl_oracle_rapid(const void *z, const void *y, int dtype,
                             rv = 0.0;
                         w[v] = rv;
                         S += rv;
+                        if (emit_scale)
+                            emit_scale[(size_t)bi * V + v] = p + (ph > q ? ph : q);
                         if (fabs(h - Mh - tail_log) <= tail_eps)
                             ++close;
                     }
@@ -411,6 +418,8 @@ int vwl_oracle_rapid(const void *z, const void *y, int dtype,
                     for (int v = 0; v < V; ++v) {
                         w[v] = exp(widen(z, dtype, off + v) / T - Lz);
                         S += w[v];
+                        if (emit_scale)
+                            emit_scale[(size_t)bi * V + v] = w[v];
                     }
                 }
                 double u = (double)u_sample[(long)bi * P + n];

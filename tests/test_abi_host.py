@@ -1,0 +1,170 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function ``include/vwl.h`` declares, sizes workspaces from the shape
+alone, and its argument checks return the documented status codes."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vwl.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?(?:vwl_status|size_t|int|char|void)\s*\**\s*(\w+)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import vocab_wide_logit_amd as vwl
+    return vwl.load_library()
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for n in ("asym_verify", "rapid_verify", "vwl_asym_workspace_bytes",
+              "vwl_rapid_workspace_bytes", "vwl_status_string", "vwl_workspace_reset"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    import vocab_wide_logit_amd as vwl
+    out = subprocess.run(["nm", "-D", "--defined-only", vwl.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for n in _declared_functions():
+        assert n in exported, n
+        assert hasattr(lib, n)
+    assert set(vwl.SYMBOLS) <= exported
+
+
+def test_status_strings(lib):
+    for code in range(8):
+        s = lib.vwl_status_string(code).decode()
+        assert s.startswith("VWL_")
+    assert lib.vwl_version() >= 100
+
+
+def test_workspace_sizes(lib):
+    for (B, K, V, dt) in [(1, 0, 1, 0), (4, 2, 1024, 0), (64, 2, 151936, 1), (256, 4, 151936, 1)]:
+        n = lib.vwl_asym_workspace_bytes(B, K, V, dt)
+        assert n > 0 and n % 256 == 0
+        # grows with rows
+        assert lib.vwl_asym_workspace_bytes(B + 1, K, V, dt) >= n
+    assert lib.vwl_rapid_workspace_bytes(16, 10, 128256, 0) > 0
+    assert lib.vwl_asym_workspace_bytes(0, 2, 10, 0) == 0
+    assert lib.vwl_asym_workspace_bytes(1, 64, 10, 0) == 0
+    assert lib.vwl_asym_workspace_bytes(1, 2, 0, 0) == 0
+    assert lib.vwl_asym_workspace_bytes(1, 2, 10, 7) == 0
+    assert lib.vwl_rapid_workspace_bytes(1, -1, 10, 0) == 0
+
+
+def _p(addr):
+    return ctypes.c_void_p(addr)
+
+
+A = 0x10000  # 16-byte aligned fake device addresses (never dereferenced)
+
+
+def _asym_check(lib, **kw):
+    args = dict(a=A, b=A + 0x1000, t=A + 0x2000, draft=A + 0x3000, B=2, K=2, V=100, dt=0,
+                beta=1.0, gamma=0.5, D=A + 0x4000, ge=A + 0x5000, acc=A + 0x6000, fused=A + 0x7000,
+                alen=A + 0x8000, tok=A + 0x9000, ws=0x100000, wsb=4096, need=4096)
+    args.update(kw)
+    return lib.vwl_asym_check(_p(args["a"]), _p(args["b"]), _p(args["t"]), _p(args["draft"]),
+                              args["B"], args["K"], args["V"], args["dt"], args["beta"], args["gamma"],
+                              _p(args["D"]), _p(args["ge"]), _p(args["acc"]), _p(args["fused"]),
+                              _p(args["alen"]), _p(args["tok"]), _p(args["ws"]), args["wsb"], args["need"])
+
+
+def test_asym_check_codes(lib):
+    assert _asym_check(lib) == 0
+    assert _asym_check(lib, a=0) == 1
+    assert _asym_check(lib, D=0) == 1
+    assert _asym_check(lib, draft=0) == 1
+    assert _asym_check(lib, draft=0, acc=0, K=0) == 0        # no drafts: both may be null
+    assert _asym_check(lib, B=0) == 2
+    assert _asym_check(lib, K=-1) == 2
+    assert _asym_check(lib, K=64) == 2
+    assert _asym_check(lib, V=0) == 2
+    assert _asym_check(lib, dt=2) == 3
+    assert _asym_check(lib, beta=float("nan")) == 4
+    assert _asym_check(lib, beta=float("inf")) == 4
+    assert _asym_check(lib, gamma=-0.1) == 4
+    assert _asym_check(lib, gamma=float("inf")) == 4
+    assert _asym_check(lib, beta=-3.0, gamma=0.0) == 0
+    assert _asym_check(lib, a=A + 8) == 7
+    assert _asym_check(lib, fused=A + 0x7002) == 7
+    assert _asym_check(lib, ws=0x100010) == 7
+    assert _asym_check(lib, wsb=100, need=4096) == 5
+    assert _asym_check(lib, ws=0) == 5
+
+
+def _rapid_check(lib, **kw):
+    args = dict(z=A, y=A + 0x1000, draft=A + 0x3000, ua=A + 0x4000, us=A + 0x5000, B=2, G=3, V=100,
+                dt=0, eta=5.0, T=1.0, acc=A + 0x6000, alen=A + 0x8000, tok=A + 0x9000,
+                ws=0x100000, wsb=4096, need=4096)
+    args.update(kw)
+    return lib.vwl_rapid_check(_p(args["z"]), _p(args["y"]), _p(args["draft"]), _p(args["ua"]),
+                               _p(args["us"]), args["B"], args["G"], args["V"], args["dt"], args["eta"],
+                               args["T"], _p(args["acc"]), _p(args["alen"]), _p(args["tok"]),
+                               _p(args["ws"]), args["wsb"], args["need"])
+
+
+def test_rapid_check_codes(lib):
+    assert _rapid_check(lib) == 0
+    assert _rapid_check(lib, us=0) == 1
+    assert _rapid_check(lib, ua=0) == 1
+    assert _rapid_check(lib, ua=0, draft=0, acc=0, G=0) == 0
+    assert _rapid_check(lib, G=64) == 2
+    assert _rapid_check(lib, dt=9) == 3
+    assert _rapid_check(lib, eta=-1.0) == 4
+    assert _rapid_check(lib, T=0.0) == 4
+    assert _rapid_check(lib, T=float("nan")) == 4
+    assert _rapid_check(lib, z=A + 4) == 7
+    assert _rapid_check(lib, us=A + 0x5002) == 7
+    assert _rapid_check(lib, wsb=10) == 5
+
+
+def test_plan_override_validation(lib):
+    assert lib.vwl_set_plan_override(0, 3, 0) == 4
+    assert lib.vwl_set_plan_override(2, 0, 0) == 4
+    assert lib.vwl_set_plan_override(0, 0, -1) == 4
+    assert lib.vwl_set_plan_override(0, 0, 0) == 0
+
+
+def test_bf16_marshalling_is_exact():
+    """The binding's host->device bf16 conversion keeps the stored bits."""
+    import torch
+    x = W.round_to_bf16(np.random.default_rng(0).normal(0, 3, 4096).astype(np.float32))
+    t = torch.from_numpy(x).to(torch.bfloat16)
+    assert np.array_equal(t.view(torch.int16).numpy().view(np.uint16), W.bf16_bits(x))
+
+
+def test_generator_structure():
+    """Exact counts of the planted structure and drafts = argmax a."""
+    x = W.gen_asym(20, 4, 700, "bf16", seed=3, displaced_frac=0.3, identical_frac=0.2, tie_frac=0.05)
+    R = 100
+    assert x.identical.sum() == round(0.2 * R)
+    assert x.tie.sum() == round(0.05 * R)
+    assert x.displaced.sum() == round(0.3 * R)
+    assert not np.any(x.identical & x.tie)
+    assert np.array_equal(x.b[x.identical], x.a[x.identical])
+    np.testing.assert_array_equal(x.draft, np.argmax(x.a[:, :4], axis=2))
+    W.bf16_bits(x.a)  # bf16-exact
+    r = W.gen_rapid(3, 4, 500, seed=9)
+    assert r.displaced.sum() == round(0.4 * 15)
+    assert r.u_accept.dtype == np.float32 and np.all(r.u_accept < 1.0)
+    assert np.all((r.u_sample * 2 ** 24) == np.round(r.u_sample * 2 ** 24))
+    # same seed, same data; generation does not depend on the thread count
+    x2 = W.gen_asym(20, 4, 700, "bf16", seed=3, displaced_frac=0.3, identical_frac=0.2, tie_frac=0.05)
+    assert np.array_equal(x.a, x2.a) and np.array_equal(x.t, x2.t)

@@ -1,0 +1,285 @@
+"""Speculative verification and logit fusion over vocabulary-wide logit rows,
+on AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding of ``lib/libvwl.so`` (HIP kernels behind a C ABI,
+declared in ``include/vwl.h``).  This module only marshals arguments:
+it checks tensor placement and layout, allocates output tensors and a
+zero-filled workspace with torch, passes raw device pointers and torch's
+current HIP stream, and raises on a non-OK status.  Every step of the pass
+runs in the library's kernels; there is no other implementation to fall
+back to, and importing fails loudly when the library has not been built.
+
+Entry points (same names as the C ABI):
+
+* ``asym_verify`` -- AsymSpec verification (AsymSpec reading notes, sections
+  4.1-4.2): JSD of the two drafter views, CDA threshold gamma*exp(-D),
+  acceptance test, first-rejection scan, delta-fusion token.
+* ``rapid_verify`` -- RAPID verification (RAPID notes, key designs 2-4):
+  augmented target with tail protection, rejection test against it, and the
+  adjusted residual draw from caller-supplied uniforms.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import NamedTuple, Optional
+
+import torch  # loaded first so the library binds to torch's HIP runtime
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libvwl.so")
+
+VWL_F32 = 0
+VWL_BF16 = 1
+DEVERR_DRAFT = 1
+DEVERR_UNIFORM = 2
+DEVERR_TIMEOUT = 4
+MAX_K = 63
+
+_lib = None
+_lib_lock = threading.Lock()
+
+SYMBOLS = ("vwl_status_string", "vwl_version", "vwl_workspace_reset",
+           "vwl_asym_workspace_bytes", "asym_verify",
+           "vwl_rapid_workspace_bytes", "rapid_verify",
+           "vwl_plan_info", "vwl_asym_check", "vwl_rapid_check",
+           "vwl_set_plan_override")
+
+
+class VwlError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(msg)
+        self.code = code
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libvwl.so and declare its signatures; raises if it is not built."""
+    global _lib
+    with _lib_lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise ImportError("libvwl.so is not built (%s); run __graft_entry__.build()" % path)
+        lib = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        i = ctypes.c_int
+        f = ctypes.c_float
+        sz = ctypes.c_size_t
+        lib.vwl_status_string.argtypes = [i]
+        lib.vwl_status_string.restype = ctypes.c_char_p
+        lib.vwl_version.argtypes = []
+        lib.vwl_version.restype = i
+        lib.vwl_workspace_reset.argtypes = [P, sz, P]
+        lib.vwl_workspace_reset.restype = i
+        lib.vwl_asym_workspace_bytes.argtypes = [i, i, i, i]
+        lib.vwl_asym_workspace_bytes.restype = sz
+        lib.vwl_rapid_workspace_bytes.argtypes = [i, i, i, i]
+        lib.vwl_rapid_workspace_bytes.restype = sz
+        lib.asym_verify.argtypes = [P, P, P, P, i, i, i, i, f, f, P, P, P, P, P, P, P, P, sz, P]
+        lib.asym_verify.restype = i
+        lib.rapid_verify.argtypes = [P, P, P, P, P, i, i, i, i, f, f, P, P, P, P, P, P, P, P, sz, P]
+        lib.rapid_verify.restype = i
+        lib.vwl_plan_info.argtypes = [i, i, i, i, i, ctypes.POINTER(ctypes.c_int64)]
+        lib.vwl_plan_info.restype = i
+        lib.vwl_asym_check.argtypes = [P, P, P, P, i, i, i, i, f, f, P, P, P, P, P, P, P, sz, sz]
+        lib.vwl_asym_check.restype = i
+        lib.vwl_rapid_check.argtypes = [P, P, P, P, P, i, i, i, i, f, f, P, P, P, P, sz, sz]
+        lib.vwl_rapid_check.restype = i
+        lib.vwl_set_plan_override.argtypes = [i, i, i]
+        lib.vwl_set_plan_override.restype = i
+        _lib = lib
+        return lib
+
+
+def _check(code: int) -> None:
+    if code != 0:
+        msg = load_library().vwl_status_string(code).decode()
+        raise VwlError(code, msg)
+
+
+def _dt(x: torch.Tensor) -> int:
+    if x.dtype == torch.float32:
+        return VWL_F32
+    if x.dtype == torch.bfloat16:
+        return VWL_BF16
+    raise TypeError("logits must be float32 or bfloat16, got %s" % x.dtype)
+
+
+def _ptr(x: Optional[torch.Tensor]):
+    return None if x is None else ctypes.c_void_p(x.data_ptr())
+
+
+def _dev_tensor(x: torch.Tensor, name: str, dtype=None) -> torch.Tensor:
+    if not isinstance(x, torch.Tensor) or x.device.type != "cuda":
+        raise TypeError("%s must be a device tensor" % name)
+    if dtype is not None and x.dtype != dtype:
+        raise TypeError("%s must have dtype %s" % (name, dtype))
+    if not x.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return x
+
+
+# Workspace cache: one zero-filled buffer per (device, stream, mode, shape).
+# The kernels leave it zero-filled after every completed call.
+_ws_cache: dict = {}
+_ws_lock = threading.Lock()
+
+
+def _workspace(mode: int, B: int, K: int, V: int, dt: int, device, stream) -> torch.Tensor:
+    lib = load_library()
+    need = (lib.vwl_asym_workspace_bytes if mode == 0 else lib.vwl_rapid_workspace_bytes)(B, K, V, dt)
+    if need == 0:
+        _check(2)
+    key = (device.index, stream.cuda_stream, mode, B, K, V, dt)
+    with _ws_lock:
+        ws = _ws_cache.get(key)
+        if ws is None:
+            ws = torch.zeros(need, dtype=torch.uint8, device=device)
+            _ws_cache[key] = ws
+        return ws
+
+
+def workspace_bytes(mode: str, B: int, K: int, V: int, dtype: torch.dtype) -> int:
+    """Size of the workspace of one call ("asym" or "rapid")."""
+    lib = load_library()
+    dt = VWL_BF16 if dtype == torch.bfloat16 else VWL_F32
+    f = lib.vwl_asym_workspace_bytes if mode == "asym" else lib.vwl_rapid_workspace_bytes
+    return int(f(B, K, V, dt))
+
+
+def plan_info(mode: str, B: int, K: int, V: int, dtype: torch.dtype) -> dict:
+    """Launch plan the library picks on the current device."""
+    lib = load_library()
+    out = (ctypes.c_int64 * 6)()
+    dt = VWL_BF16 if dtype == torch.bfloat16 else VWL_F32
+    _check(lib.vwl_plan_info(0 if mode == "asym" else 1, B, K, V, dt, out))
+    return {"team": out[0], "vec_per_thread": out[1], "teams": out[2], "grid": out[3],
+            "threads": out[4], "rows": out[5]}
+
+
+def set_plan_override(mode: str, vec_per_thread: int = 0, max_teams: int = 0) -> None:
+    """Tuning hook: pin vectors per thread / cap teams (0 = automatic)."""
+    _check(load_library().vwl_set_plan_override(0 if mode == "asym" else 1, vec_per_thread, max_teams))
+
+
+class AsymOut(NamedTuple):
+    D: torch.Tensor           # [B, K+1] float32
+    gamma_eff: torch.Tensor   # [B, K+1] float32
+    accept: torch.Tensor      # [B, K] uint8
+    fused: torch.Tensor       # [B, K+1] int32
+    accept_len: torch.Tensor  # [B] int32
+    token: torch.Tensor       # [B] int32
+    dev_err: torch.Tensor     # [1] int32
+
+
+def asym_out(B: int, K: int, device) -> AsymOut:
+    """Preallocated outputs for ``asym_verify(..., out=...)``."""
+    kw = dict(device=device)
+    return AsymOut(torch.empty(B, K + 1, dtype=torch.float32, **kw),
+                   torch.empty(B, K + 1, dtype=torch.float32, **kw),
+                   torch.empty(B, K, dtype=torch.uint8, **kw),
+                   torch.empty(B, K + 1, dtype=torch.int32, **kw),
+                   torch.empty(B, dtype=torch.int32, **kw),
+                   torch.empty(B, dtype=torch.int32, **kw),
+                   torch.zeros(1, dtype=torch.int32, **kw))
+
+
+def asym_verify(a: torch.Tensor, b: torch.Tensor, t: torch.Tensor, draft: torch.Tensor,
+                beta: float, gamma: float, *, out: Optional[AsymOut] = None,
+                workspace: Optional[torch.Tensor] = None) -> AsymOut:
+    """AsymSpec verification of [B, K+1, V] logit rows on the current stream.
+
+    a: drafter logits on the full context; b: drafter logits on the
+    compressed context; t: verifier logits; draft: [B, K] int32 draft ids.
+    Returns D, gamma_eff, accept, fused, accept_len, token and dev_err."""
+    lib = load_library()
+    _dev_tensor(a, "a")
+    dt = _dt(a)
+    _dev_tensor(b, "b", a.dtype)
+    _dev_tensor(t, "t", a.dtype)
+    if a.dim() != 3 or b.shape != a.shape or t.shape != a.shape:
+        raise ValueError("a, b, t must share one [B, K+1, V] shape")
+    B, P, V = a.shape
+    K = P - 1
+    _dev_tensor(draft, "draft", torch.int32)
+    if tuple(draft.shape) != (B, K):
+        raise ValueError("draft must be [B, K]")
+    if out is None:
+        out = asym_out(B, K, a.device)
+    stream = torch.cuda.current_stream(a.device)
+    ws = workspace if workspace is not None else _workspace(0, B, K, V, dt, a.device, stream)
+    code = lib.asym_verify(_ptr(a), _ptr(b), _ptr(t), _ptr(draft) if K > 0 else None,
+                           B, K, V, dt, float(beta), float(gamma),
+                           _ptr(out.D), _ptr(out.gamma_eff), _ptr(out.accept) if K > 0 else None,
+                           _ptr(out.fused), _ptr(out.accept_len), _ptr(out.token), _ptr(out.dev_err),
+                           _ptr(ws), ws.numel(), ctypes.c_void_p(stream.cuda_stream))
+    _check(code)
+    return out
+
+
+class RapidOut(NamedTuple):
+    accept: torch.Tensor       # [B, G] uint8
+    accept_len: torch.Tensor   # [B] int32
+    token: torch.Tensor        # [B] int32
+    p_hat_draft: Optional[torch.Tensor]  # [B, G] float32
+    q_draft: Optional[torch.Tensor]      # [B, G] float32
+    emit_dist: Optional[torch.Tensor]    # [B, V] float32
+    dev_err: torch.Tensor      # [1] int32
+
+
+def rapid_out(B: int, G: int, V: int, device, want_probs: bool = False,
+              want_dist: bool = False) -> RapidOut:
+    """Preallocated outputs for ``rapid_verify(..., out=...)``."""
+    kw = dict(device=device)
+    return RapidOut(torch.empty(B, G, dtype=torch.uint8, **kw),
+                    torch.empty(B, dtype=torch.int32, **kw),
+                    torch.empty(B, dtype=torch.int32, **kw),
+                    torch.empty(B, G, dtype=torch.float32, **kw) if want_probs else None,
+                    torch.empty(B, G, dtype=torch.float32, **kw) if want_probs else None,
+                    torch.empty(B, V, dtype=torch.float32, **kw) if want_dist else None,
+                    torch.zeros(1, dtype=torch.int32, **kw))
+
+
+def rapid_verify(z: torch.Tensor, y: torch.Tensor, draft: torch.Tensor,
+                 u_accept: torch.Tensor, u_sample: torch.Tensor, eta: float, T: float,
+                 *, want_probs: bool = False, want_dist: bool = False,
+                 out: Optional[RapidOut] = None,
+                 workspace: Optional[torch.Tensor] = None) -> RapidOut:
+    """RAPID verification of [B, G+1, V] logit rows on the current stream.
+
+    z: target logits; y: RAG-drafter logits; draft: [B, G] int32;
+    u_accept: [B, G] and u_sample: [B, G+1] float32 uniforms in [0, 1)."""
+    lib = load_library()
+    _dev_tensor(z, "z")
+    dt = _dt(z)
+    _dev_tensor(y, "y", z.dtype)
+    if z.dim() != 3 or y.shape != z.shape:
+        raise ValueError("z, y must share one [B, G+1, V] shape")
+    B, P, V = z.shape
+    G = P - 1
+    _dev_tensor(draft, "draft", torch.int32)
+    _dev_tensor(u_accept, "u_accept", torch.float32)
+    _dev_tensor(u_sample, "u_sample", torch.float32)
+    if tuple(draft.shape) != (B, G) or tuple(u_accept.shape) != (B, G) or tuple(u_sample.shape) != (B, P):
+        raise ValueError("draft, u_accept must be [B, G] and u_sample [B, G+1]")
+    if out is None:
+        out = rapid_out(B, G, V, z.device, want_probs, want_dist)
+    stream = torch.cuda.current_stream(z.device)
+    ws = workspace if workspace is not None else _workspace(1, B, G, V, dt, z.device, stream)
+    code = lib.rapid_verify(_ptr(z), _ptr(y), _ptr(draft) if G > 0 else None,
+                            _ptr(u_accept) if G > 0 else None, _ptr(u_sample),
+                            B, G, V, dt, float(eta), float(T),
+                            _ptr(out.accept) if G > 0 else None, _ptr(out.accept_len), _ptr(out.token),
+                            _ptr(out.p_hat_draft), _ptr(out.q_draft), _ptr(out.emit_dist),
+                            _ptr(out.dev_err), _ptr(ws), ws.numel(), ctypes.c_void_p(stream.cuda_stream))
+    _check(code)
+    return out
+
+
+def to_device_logits(x_f32, dtype: str, device="cuda") -> torch.Tensor:
+    """Move float32 host values (exact in ``dtype``) to a device tensor of that dtype."""
+    t = torch.from_numpy(x_f32)
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)  # exact: the values are bf16-representable
+    return t.to(device).contiguous()

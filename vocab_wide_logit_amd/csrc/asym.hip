@@ -1,0 +1,549 @@
+// AsymSpec verification pass (AsymSpec reading notes, section 4.1
+// "contrastive delta-fusion" and section 4.2 "CDA gate").
+//
+// Launch 1, asym_rows_kernel: each logit row (one draft position of one
+// request: a_i, b_i, t_i) is split over a team of W workgroups; each
+// workgroup loads its chunk of the three rows once into registers and
+//   pass AB online softmax statistics (running max, sum of exp) of a, b, t,
+//           rescaled once per 16-byte group (fp32 within a group, fp64
+//           across groups and lanes), and the maximum of the fused score
+//           t + beta*(a - b); its lowest index is searched afterwards only
+//           by the threads that hold the workgroup maximum
+//           -> the chunk record is published
+//   pass C  once all W records of the row are in, the row log-sum-exps
+//           L_a, L_b (combined in one fixed order by every member) and the
+//           JSD terms of the chunk, from a and b still held in registers in
+//           their stored form; the row is read once.
+// Each workgroup keeps two rows in flight: after publishing row r's record
+// it runs passes A+B of row r+1 (already streamed from HBM straight into
+// LDS) before it waits for row r's team and runs row r's pass C from a and
+// b still held in registers.  The chunk of row r+2 streams into LDS
+// meanwhile, and several teams share each compute unit.
+//
+// Launch 2, asym_finalize_kernel: one wave per row combines the W records
+// (D, gamma*exp(-D), fused token, acceptance test of the draft); the wave
+// that completes a request runs the first-rejection scan.
+#include "vwl_device.hpp"
+#include "vwl_internal.hpp"
+
+namespace vwl {
+
+// Record words of one (row, member):
+//   0..2  sums of 2^(x*log2e - c) for a, b, t (double bits)
+//   3     references of the sums of a and b (two floats, log2 units)
+//   4     reference of the sum of t (log2 units), maximum of the fused score
+//   5     lowest index of the fused maximum (low 32 bits)
+//   6     JSD partial sum_v Mx_v * g_v over the chunk (double bits)
+__device__ __forceinline__ uint64_t pack2(float lo, float hi) {
+    return (uint64_t)__float_as_uint(lo) | ((uint64_t)__float_as_uint(hi) << 32);
+}
+__device__ __forceinline__ float unpack_lo(uint64_t w) { return __uint_as_float((uint32_t)w); }
+__device__ __forceinline__ float unpack_hi(uint64_t w) { return __uint_as_float((uint32_t)(w >> 32)); }
+__device__ __forceinline__ double as_f64(uint64_t w) { return __longlong_as_double((long long)w); }
+__device__ __forceinline__ uint64_t f64_bits(double x) { return (uint64_t)__double_as_longlong(x); }
+
+// The delta-fusion score t + beta*(a - b), evaluated the same way everywhere.
+__device__ __forceinline__ float fused_score(float a, float b, float t, float beta) {
+    return __fmaf_rn(beta, __fsub_rn(a, b), t);
+}
+
+// JSD term of one element in log2 units.  With la2 = log2 p, lb2 = log2 q,
+// d = |la2 - lb2|, rho = 2^-d (ratio of the smaller to the larger
+// probability) and Mx = max(p, q):
+//   p ln(2p/(p+q)) + q ln(2q/(p+q)) = -ln2 * Mx * [(1+rho)(log2(1+rho) - 1) + rho*d]
+// The bracket is returned times Mx (it is <= 0).  Symmetric in p and q, no
+// overflow for any finite or -inf log-probabilities (d is capped at 128,
+// where rho*d underflows to 0).
+__device__ __forceinline__ float jsd_term_neg(float la2, float lb2) {
+    const float mx = fmaxf(la2, lb2);
+    const float d = fminf(fabsf(la2 - lb2), 128.0f);
+    const float M = __builtin_amdgcn_exp2f(mx);
+    const float rho = __builtin_amdgcn_exp2f(-d);
+    const float opr = 1.0f + rho;
+    const float l2 = __builtin_amdgcn_logf(opr);
+    const float g = __fmaf_rn(opr, l2, __fmaf_rn(rho, d, -opr)); // opr*(l2 - 1) + rho*d
+    return M * g;
+}
+
+// Row log-sum-exps, in log2 units, of two tensors from the W records of a
+// row: log2 sum_w s_w 2^(c_w - C), C = max c_w, in fp64 and in one fixed
+// order (lane w handles members w, w+64, ...; butterfly sums), so every
+// caller gets the same bits.  Each lane loads its (first two) members' words
+// once.  Called by one whole wave.  Tensor k has its sums in word sk and its
+// reference in the low (hik = false) or high half of word ck.
+__device__ __forceinline__ void team_lse2x(const uint64_t *rec_row, int W, int s0, int c0w, bool hi0,
+                                           int s1, int c1w, bool hi1, double &L0, double &L1) {
+    const int lane = threadIdx.x & 63;
+    float C0 = -__builtin_inff(), C1 = -__builtin_inff();
+    double a0[2] = {0.0, 0.0}, a1[2] = {0.0, 0.0};
+    float r0[2] = {C0, C0}, r1[2] = {C1, C1};
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int w = lane + 64 * k;
+        if (w < W) {
+            const uint64_t *r = rec_row + (size_t)w * kRecWords;
+            const uint64_t x0 = ld_relaxed(r + c0w), x1 = ld_relaxed(r + c1w);
+            r0[k] = hi0 ? unpack_hi(x0) : unpack_lo(x0);
+            r1[k] = hi1 ? unpack_hi(x1) : unpack_lo(x1);
+            a0[k] = as_f64(ld_relaxed(r + s0));
+            a1[k] = as_f64(ld_relaxed(r + s1));
+        }
+    }
+    C0 = fmaxf(r0[0], r0[1]);
+    C1 = fmaxf(r1[0], r1[1]);
+    for (int w = lane + 128; w < W; w += 64) { // teams wider than 128 members
+        const uint64_t *r = rec_row + (size_t)w * kRecWords;
+        const uint64_t x0 = ld_relaxed(r + c0w), x1 = ld_relaxed(r + c1w);
+        C0 = fmaxf(C0, hi0 ? unpack_hi(x0) : unpack_lo(x0));
+        C1 = fmaxf(C1, hi1 ? unpack_hi(x1) : unpack_lo(x1));
+    }
+    C0 = wave_max(C0);
+    C1 = wave_max(C1);
+    double t0 = 0.0, t1 = 0.0;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        if (a0[k] > 0.0)
+            t0 += a0[k] * exp2((double)r0[k] - (double)C0);
+        if (a1[k] > 0.0)
+            t1 += a1[k] * exp2((double)r1[k] - (double)C1);
+    }
+    for (int w = lane + 128; w < W; w += 64) { // teams wider than 128 members
+        const uint64_t *r = rec_row + (size_t)w * kRecWords;
+        const uint64_t x0 = ld_relaxed(r + c0w), x1 = ld_relaxed(r + c1w);
+        const double v0 = as_f64(ld_relaxed(r + s0)), v1 = as_f64(ld_relaxed(r + s1));
+        if (v0 > 0.0)
+            t0 += v0 * exp2((double)(hi0 ? unpack_hi(x0) : unpack_lo(x0)) - (double)C0);
+        if (v1 > 0.0)
+            t1 += v1 * exp2((double)(hi1 ? unpack_hi(x1) : unpack_lo(x1)) - (double)C1);
+    }
+    t0 = wave_sum(t0);
+    t1 = wave_sum(t1);
+    L0 = (double)C0 + log2(t0);
+    L1 = (double)C1 + log2(t1);
+}
+
+// Online sum-of-exp state of one tensor over a thread's elements, fed one
+// 16-byte group at a time.  The reference c is kept in log2 units as the
+// exact fp32 value used in the exponent arguments, so the state means
+// s = sum_v 2^(x_v*log2e - c) without any rounding of the reference itself.
+// c tracks the running maximum, so the dominant terms have arguments near 0
+// (where the argument's own rounding is smallest); the running sum is
+// rescaled once per group.
+struct OnlineLse {
+    float c;   // reference, log2 units
+    double s;
+};
+
+__device__ __forceinline__ void online_init(OnlineLse &st) {
+    st.c = -__builtin_inff();
+    st.s = 0.0;
+}
+
+template <int EPV>
+__device__ __forceinline__ void online_group(OnlineLse &st, const float (&x)[EPV]) {
+    float g = x[0];
+#pragma unroll
+    for (int e = 1; e < EPV; ++e)
+        g = fmaxf(g, x[e]);
+    const float c_new = fmaxf(st.c, fmaxf(g, -1e30f) * kLog2e); // finite even for -inf rows
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e)
+        acc += __builtin_amdgcn_exp2f(__fmaf_rn(x[e], kLog2e, -c_new));
+    const float scale = __builtin_amdgcn_exp2f(st.c - c_new);
+    st.s = __fma_rn(st.s, (double)scale, (double)acc);
+    st.c = c_new;
+}
+
+// Rescale a thread's state to the workgroup reference C (fp64 result).
+__device__ __forceinline__ double rescale_to(const OnlineLse &st, float C) {
+    if (!(st.s > 0.0))
+        return 0.0;
+    return st.s * (double)__builtin_amdgcn_exp2f(st.c - C);
+}
+
+// LDS staging of one row's chunk: [tensor][vector slot][thread], 16 bytes
+// each.  Every lane later reads back exactly the vectors it issued itself,
+// so only its own wave's loads have to be complete.
+template <int NV>
+struct AsymStage {
+    uint4 v[3][NV][kThreads];
+};
+
+// Direct global -> LDS load of one 16-byte vector per lane (the LDS address
+// of the wave is uniform; lane L lands at base + 16*L).
+__device__ __forceinline__ void g2lds16(const uint4 *src, uint4 *lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(static_cast<const void *>(src),
+                                     (__attribute__((address_space(3))) void *)(lds_wave_base),
+                                     16, 0, 0);
+}
+
+// Stream row r's chunk into LDS (waves 1-3: wave x+1 issues all of tensor x).
+template <int DT, int NV>
+__device__ __forceinline__ void prefetch_bulk(AsymStage<NV> &stage, long long r, int V, int W, int member,
+                                              const uint4 *A4, const uint4 *B4, const uint4 *T4) {
+    const int lane = threadIdx.x & 63;
+    const RowSplit<DT> s = row_split<DT>(r, V, W, member);
+    const int x = (threadIdx.x >> 6) - 1;
+    const uint4 *base = T4;
+    if (x == 0)
+        base = A4;
+    else if (x == 1)
+        base = B4;
+    const uint4 *src = base + s.vec0 + lane;
+    uint4 *dst = &stage.v[x][0][0];
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) {
+            if (v * 64 + lane + j * kThreads < s.nv)
+                g2lds16(src + v * 64 + j * kThreads, dst + j * kThreads + v * 64);
+        }
+}
+
+// Head/tail scalars of row r (wave 0's first lanes), widened to fp32.
+template <int DT>
+__device__ __forceinline__ void prefetch_scalars(long long r, int V, int W, int member, const void *a,
+                                                 const void *b, const void *t, float &na, float &nb, float &nt) {
+    const RowSplit<DT> s = row_split<DT>(r, V, W, member);
+    if ((int)threadIdx.x < s.nsc) {
+        const size_t off = (size_t)r * (size_t)V + scalar_index<DT>(s, threadIdx.x);
+        na = load_scalar<DT>(a, off);
+        nb = load_scalar<DT>(b, off);
+        nt = load_scalar<DT>(t, off);
+    }
+}
+
+// Passes A+B over one row's chunk held in registers (raw a, b, t plus the
+// head/tail scalar): online softmax statistics, the fused maximum and its
+// lowest index, reduced over the workgroup; thread 0 publishes the record.
+template <int DT, int NV>
+__device__ __forceinline__ void asym_pass_ab(const AsymParams &P, long long row, int member, const RowSplit<DT> &sp,
+                                             const uint4 (&ra)[NV], const uint4 (&rb)[NV], const uint4 (&rt)[NV],
+                                             float sa, float sb, float st, float *lds_f, double *lds_d, int *lds_i) {
+    constexpr int EPV = Elem<DT>::kPerVec;
+    const int tid = threadIdx.x;
+    const float NEG_INF = -__builtin_inff();
+    const bool has_sc = tid < sp.nsc;
+    OnlineLse la, lb, lt;
+    online_init(la);
+    online_init(lb);
+    online_init(lt);
+    float fmax_t = NEG_INF;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        if (tid + j * kThreads < sp.nv) {
+            float xa[EPV], xb[EPV], xt[EPV];
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) {
+                xa[e] = widen<DT>(ra[j], e);
+                xb[e] = widen<DT>(rb[j], e);
+                xt[e] = widen<DT>(rt[j], e);
+                fmax_t = fmaxf(fmax_t, fused_score(xa[e], xb[e], xt[e], P.beta));
+            }
+            online_group<EPV>(la, xa);
+            online_group<EPV>(lb, xb);
+            online_group<EPV>(lt, xt);
+        }
+    }
+    float fs = NEG_INF;
+    if (has_sc) {
+        fs = fused_score(sa, sb, st, P.beta);
+        fmax_t = fmaxf(fmax_t, fs);
+        const float x1a[1] = {sa}, x1b[1] = {sb}, x1t[1] = {st};
+        online_group<1>(la, x1a);
+        online_group<1>(lb, x1b);
+        online_group<1>(lt, x1t);
+    }
+    float mx[4] = {la.c, lb.c, lt.c, fmax_t};
+    block_max<4>(mx, lds_f);
+    const float Ca = mx[0], Cb = mx[1], Ct = mx[2], Fm = mx[3];
+
+    // lowest index of the workgroup's fused maximum (only its holders search)
+    int fi = 0x7fffffff;
+    if (fmax_t == Fm) {
+        if (has_sc && fs == Fm)
+            fi = scalar_index<DT>(sp, tid);
+        bool found = false;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            if (!found && tid + j * kThreads < sp.nv) {
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) {
+                    if (!found && fused_score(widen<DT>(ra[j], e), widen<DT>(rb[j], e), widen<DT>(rt[j], e),
+                                              P.beta) == Fm) {
+                        fi = min(fi, sp.first_elem + (tid + j * kThreads) * EPV + e);
+                        found = true;
+                    }
+                }
+            }
+        }
+    }
+    double S[3] = {rescale_to(la, Ca), rescale_to(lb, Cb), rescale_to(lt, Ct)};
+    block_sum_min<3>(S, fi, lds_d, lds_i);
+    if (tid == 0) {
+        uint64_t *rec = P.rec + ((size_t)row * P.Wmax + member) * kRecWords;
+        st_relaxed(rec + 0, f64_bits(S[0]));
+        st_relaxed(rec + 1, f64_bits(S[1]));
+        st_relaxed(rec + 2, f64_bits(S[2]));
+        st_relaxed(rec + 3, pack2(Ca, Cb));
+        st_relaxed(rec + 4, pack2(Ct, Fm));
+        st_relaxed(rec + 5, (uint64_t)(uint32_t)fi);
+        publish_add(P.row_ctr + (size_t)row * 16, 1u);
+    }
+}
+
+template <int DT, int NV>
+__global__ __launch_bounds__(kThreads, (NV <= 1 ? 4 : NV == 2 ? 3 : 2)) void asym_rows_kernel(AsymParams P) {
+    constexpr int EPV = Elem<DT>::kPerVec;
+    __shared__ AsymStage<NV> stage;
+    __shared__ float lds_f[kWaves * 4];
+    __shared__ double lds_d[kWaves * 3];
+    __shared__ int lds_i[kWaves];
+    __shared__ double sh_row[2];
+    __shared__ uint32_t sh_u[2];
+
+    const int tid = threadIdx.x;
+    if (tid == 0)
+        sh_u[0] = __hip_atomic_fetch_add(&P.ctl[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const uint32_t ticket = sh_u[0];
+    const int team = (int)(ticket / (uint32_t)P.W);
+    const int member = (int)(ticket % (uint32_t)P.W);
+    if (team >= P.R)
+        return;
+    const uint4 *A4 = static_cast<const uint4 *>(P.a);
+    const uint4 *B4 = static_cast<const uint4 *>(P.b);
+    const uint4 *T4 = static_cast<const uint4 *>(P.t);
+    const float NEG_INF = -__builtin_inff();
+    const int V = P.V, W = P.W;
+    const bool wave0 = tid < 64;
+    float na = NEG_INF, nb = NEG_INF, nt = NEG_INF;
+
+    // Rows of this team: team, team + n_teams, ...  Two are in flight: the
+    // pending row waits for its team while the next row's passes A+B run.
+    auto issue = [&](long long r) {
+        if (!wave0)
+            prefetch_bulk<DT, NV>(stage, r, V, W, member, A4, B4, T4);
+        else
+            prefetch_scalars<DT>(r, V, W, member, P.a, P.b, P.t, na, nb, nt);
+    };
+    uint4 ra[NV], rb[NV], rt[NV];
+    float sa, sb, st;
+    auto take = [&]() { // the staged row: LDS -> registers
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads(); // every wave's pieces have landed
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            ra[j] = stage.v[0][j][tid];
+            rb[j] = stage.v[1][j][tid];
+            rt[j] = stage.v[2][j][tid];
+        }
+        sa = na;
+        sb = nb;
+        st = nt;
+        __syncthreads(); // every wave has read its vectors before the refill
+    };
+
+    long long row = team;
+    issue(row);
+    take();
+    if (row + P.n_teams < P.R)
+        issue(row + P.n_teams);
+    RowSplit<DT> sp = row_split<DT>(row, V, W, member);
+    asym_pass_ab<DT, NV>(P, row, member, sp, ra, rb, rt, sa, sb, st, lds_f, lds_d, lds_i);
+    for (;;) {
+        // the pending row's a, b (raw) and head/tail scalars
+        uint4 pa[NV], pb[NV];
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            pa[j] = ra[j];
+            pb[j] = rb[j];
+        }
+        const float psa = sa, psb = sb;
+        const RowSplit<DT> psp = sp;
+
+        const long long next = row + P.n_teams;
+        const bool has_next = next < P.R;
+        if (has_next) {
+            take();
+            if (next + P.n_teams < P.R)
+                issue(next + P.n_teams);
+            sp = row_split<DT>(next, V, W, member);
+            asym_pass_ab<DT, NV>(P, next, member, sp, ra, rb, rt, sa, sb, st, lds_f, lds_d, lds_i);
+        }
+
+        // ---- the pending row: wait for its team, then pass C ----
+        const uint64_t *rec_row = P.rec + (size_t)row * P.Wmax * kRecWords;
+        if (tid == 0)
+            sh_u[1] = wait_at_least(P.row_ctr + (size_t)row * 16, (uint32_t)W) ? 1u : 0u;
+        __syncthreads();
+        if (!sh_u[1]) {
+            if (tid == 0)
+                set_dev_err(P.dev_err, 4);
+            return;
+        }
+        if (wave0) {
+            double La2, Lb2;
+            team_lse2x(rec_row, W, 0, 3, false, 1, 3, true, La2, Lb2);
+            if (tid == 0) {
+                sh_row[0] = La2;
+                sh_row[1] = Lb2;
+            }
+        }
+        __syncthreads();
+        const float la_c = (float)sh_row[0]; // row log-sum-exps, log2 units
+        const float lb_c = (float)sh_row[1];
+        float J = 0.f;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            if (tid + j * kThreads < psp.nv) {
+#pragma unroll
+                for (int e = 0; e < EPV; ++e)
+                    J += jsd_term_neg(__fmaf_rn(widen<DT>(pa[j], e), kLog2e, -la_c),
+                                      __fmaf_rn(widen<DT>(pb[j], e), kLog2e, -lb_c));
+            }
+        }
+        if (tid < psp.nsc)
+            J += jsd_term_neg(__fmaf_rn(psa, kLog2e, -la_c), __fmaf_rn(psb, kLog2e, -lb_c));
+        double Jd[1] = {(double)J};
+        block_sum<1>(Jd, lds_d);
+        if (tid == 0)
+            P.rec[((size_t)row * P.Wmax + member) * kRecWords + 6] = f64_bits(Jd[0]);
+
+        if (!has_next)
+            break;
+        row = next;
+    }
+}
+
+// One wave per row: combine the W records, write the row outputs, and let
+// the wave that completes a request run its first-rejection scan.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void asym_finalize_kernel(AsymParams P) {
+    const int lane = threadIdx.x & 63;
+    const long long row = (long long)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        P.ctl[0] = 0u; // ticket counter of the row kernel, for the next call
+    if (row >= P.R)
+        return;
+    const uint64_t *rec_row = P.rec + (size_t)row * P.Wmax * kRecWords;
+    double Lb2, Lt2;
+    team_lse2x(rec_row, P.W, 1, 3, true, 2, 4, false, Lb2, Lt2);
+    const double Lb = Lb2 * kLn2d, Lt = Lt2 * kLn2d;
+    float fbest = -__builtin_inff();
+    for (int w = lane; w < P.W; w += 64)
+        fbest = fmaxf(fbest, unpack_hi(ld_relaxed(rec_row + (size_t)w * kRecWords + 4)));
+    fbest = wave_max(fbest);
+    double jsum = 0.0;
+    int fidx = 0x7fffffff;
+    for (int w = lane; w < P.W; w += 64) {
+        const uint64_t *r = rec_row + (size_t)w * kRecWords;
+        jsum += as_f64(ld_relaxed(r + 6));
+        if (unpack_hi(ld_relaxed(r + 4)) == fbest)
+            fidx = min(fidx, (int)(uint32_t)ld_relaxed(r + 5));
+    }
+    jsum = wave_sum(jsum);
+    fidx = wave_min_int(fidx);
+    if (lane != 0)
+        return;
+    const double Dr = -0.5 * kLn2d * jsum;
+    const double ge = (double)P.gamma * exp(-Dr);
+    P.D[row] = (float)Dr;
+    P.geff[row] = (float)ge;
+    P.fused[row] = fidx;
+    const int Pn = P.K + 1;
+    const long long bi = row / Pn;
+    const int i = (int)(row - bi * Pn);
+    const size_t row_off = (size_t)row * (size_t)P.V;
+    uint32_t acc = 0;
+    if (i < P.K) {
+        const int d = P.draft[bi * P.K + i];
+        if (d < 0 || d >= P.V) {
+            set_dev_err(P.dev_err, 1);
+        } else {
+            const double td = (double)load_scalar<DT>(P.t, row_off + d);
+            const double bd = (double)load_scalar<DT>(P.b, row_off + d);
+            const double margin = (td - Lt) - (bd - Lb) - P.log_gamma + Dr;
+            acc = margin > 0.0 ? 1u : 0u;
+        }
+        P.accept[bi * P.K + i] = (uint8_t)acc;
+    }
+    st_relaxed(P.row_info + (size_t)row * 2 + 0, (uint32_t)fidx);
+    st_relaxed(P.row_info + (size_t)row * 2 + 1, acc);
+    P.row_ctr[(size_t)row * 16] = 0u; // arrivals of the row kernel, for the next call
+    uint32_t *rq = P.req_ctr + (size_t)bi * 16;
+    const uint32_t done = publish_add(rq, 1u);
+    if (done == (uint32_t)P.K) {
+        const size_t r0 = (size_t)bi * Pn;
+        int n = P.K;
+        for (int k = 0; k < P.K; ++k) {
+            if (ld_relaxed(P.row_info + (r0 + k) * 2 + 1) == 0u) {
+                n = k;
+                break;
+            }
+        }
+        P.acc_len[bi] = n;
+        P.token[bi] = (int32_t)ld_relaxed(P.row_info + (r0 + n) * 2 + 0);
+        st_relaxed(rq, 0u);
+    }
+}
+
+template <int DT, int NV>
+static int blocks_per_cu() {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, asym_rows_kernel<DT, NV>, kThreads, 0) != hipSuccess)
+        return 0;
+    return n;
+}
+
+int asym_blocks_per_cu(int dt, int nv) {
+    if (dt == DT_BF16) {
+        switch (nv) {
+        case 1: return blocks_per_cu<DT_BF16, 1>();
+        case 2: return blocks_per_cu<DT_BF16, 2>();
+        case 4: return blocks_per_cu<DT_BF16, 4>();
+        case 8: return blocks_per_cu<DT_BF16, 8>();
+        }
+    } else {
+        switch (nv) {
+        case 1: return blocks_per_cu<DT_F32, 1>();
+        case 2: return blocks_per_cu<DT_F32, 2>();
+        case 4: return blocks_per_cu<DT_F32, 4>();
+        case 8: return blocks_per_cu<DT_F32, 8>();
+        }
+    }
+    return 0;
+}
+
+template <int DT, int NV>
+static hipError_t launch_t(const Plan &plan, const AsymParams &p, hipStream_t s) {
+    hipLaunchKernelGGL((asym_rows_kernel<DT, NV>), dim3(plan.grid), dim3(kThreads), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    const unsigned fin = (unsigned)((p.R + kWaves - 1) / kWaves);
+    hipLaunchKernelGGL((asym_finalize_kernel<DT>), dim3(fin), dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_asym(int dt, const Plan &plan, const AsymParams &p, hipStream_t s) {
+    if (dt == DT_BF16) {
+        switch (plan.nv) {
+        case 1: return launch_t<DT_BF16, 1>(plan, p, s);
+        case 2: return launch_t<DT_BF16, 2>(plan, p, s);
+        case 4: return launch_t<DT_BF16, 4>(plan, p, s);
+        case 8: return launch_t<DT_BF16, 8>(plan, p, s);
+        }
+    } else {
+        switch (plan.nv) {
+        case 1: return launch_t<DT_F32, 1>(plan, p, s);
+        case 2: return launch_t<DT_F32, 2>(plan, p, s);
+        case 4: return launch_t<DT_F32, 4>(plan, p, s);
+        case 8: return launch_t<DT_F32, 8>(plan, p, s);
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
+} // namespace vwl

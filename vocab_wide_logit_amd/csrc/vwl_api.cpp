@@ -1,0 +1,352 @@
+// C ABI of the verify / fusion library: argument checks, workspace sizing,
+// launch plans and dispatch.  No allocation, no synchronisation.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+
+#include "vwl.h"
+#include "vwl_internal.hpp"
+
+using namespace vwl;
+
+namespace {
+
+constexpr int kNvChoices[4] = {1, 2, 4, 8};
+
+int elem_bytes(int dt) { return dt == VWL_BF16 ? 2 : 4; }
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Per-device cache of the CU count and the resident workgroups per CU of
+// every kernel instance.
+struct DeviceInfo {
+    bool ready = false;
+    int cus = 0;
+    int asym_bpc[2][4] = {};
+    int rapid_bpc[2][4] = {};
+};
+constexpr int kMaxDevices = 64;
+DeviceInfo g_dev[kMaxDevices];
+std::mutex g_dev_mu;
+
+// Plan overrides for tuning sweeps (0 = automatic).
+int g_force_nv[2] = {0, 0};
+int g_force_teams[2] = {0, 0};
+
+const DeviceInfo *device_info() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return nullptr;
+    std::lock_guard<std::mutex> lock(g_dev_mu);
+    DeviceInfo &d = g_dev[dev];
+    if (!d.ready) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            return nullptr;
+        d.cus = cus;
+        for (int dt = 0; dt < 2; ++dt)
+            for (int k = 0; k < 4; ++k) {
+                d.asym_bpc[dt][k] = asym_blocks_per_cu(dt, kNvChoices[k]);
+                d.rapid_bpc[dt][k] = rapid_blocks_per_cu(dt, kNvChoices[k]);
+            }
+        d.ready = true;
+    }
+    return &d;
+}
+
+// Team size for `nv` vectors per thread: enough workgroups to hold the row.
+int team_size(int V, int dt, int nv) {
+    const long long per_vec = 16 / elem_bytes(dt);
+    const long long nb = (V + per_vec - 1) / per_vec + 1; // body vectors, upper bound
+    const long long cap = (long long)kThreads * nv;
+    long long w = (nb + cap - 1) / cap;
+    if (w < 1)
+        w = 1;
+    return (int)w;
+}
+
+// Launch plan: among the vector-per-thread choices, the one that needs the
+// fewest rounds of rows per team at full residency; ties go to the larger
+// chunk (fewer workgroups per row).  Teams are then evened out over rounds.
+bool make_plan(int mode, int dt, long long R, int V, Plan &plan) {
+    const DeviceInfo *d = device_info();
+    if (!d)
+        return false;
+    long long best_rounds = -1;
+    Plan best{};
+    for (int k = 0; k < 4; ++k) {
+        const int nv = kNvChoices[k];
+        if (g_force_nv[mode] && nv != g_force_nv[mode])
+            continue;
+        const int bpc = mode == 0 ? d->asym_bpc[dt][k] : d->rapid_bpc[dt][k];
+        if (bpc <= 0)
+            continue;
+        const int W = team_size(V, dt, nv);
+        const long long capacity = (long long)bpc * d->cus;
+        long long teams = capacity / W;
+        if (teams < 1)
+            continue;
+        if (teams > R)
+            teams = R;
+        if (g_force_teams[mode] > 0 && g_force_teams[mode] < teams)
+            teams = g_force_teams[mode];
+        const long long rounds = (R + teams - 1) / teams;
+        if (best_rounds < 0 || rounds < best_rounds || (rounds == best_rounds && nv > best.nv)) {
+            best_rounds = rounds;
+            best.nv = nv;
+            best.W = W;
+            best.n_teams = (int)((R + rounds - 1) / rounds);
+        }
+    }
+    if (best_rounds < 0)
+        return false;
+    best.grid = best.n_teams * best.W;
+    plan = best;
+    return true;
+}
+
+bool finite_f(float x) { return std::isfinite(x); }
+
+} // namespace
+
+extern "C" {
+
+const char *vwl_status_string(vwl_status s) {
+    switch (s) {
+    case VWL_OK: return "VWL_OK";
+    case VWL_ERR_NULL: return "VWL_ERR_NULL: a required pointer is null";
+    case VWL_ERR_SHAPE: return "VWL_ERR_SHAPE: B, K/G or V out of range";
+    case VWL_ERR_DTYPE: return "VWL_ERR_DTYPE: unknown dtype";
+    case VWL_ERR_PARAM: return "VWL_ERR_PARAM: beta, gamma, eta or T out of range";
+    case VWL_ERR_WORKSPACE: return "VWL_ERR_WORKSPACE: workspace too small";
+    case VWL_ERR_HIP: return "VWL_ERR_HIP: HIP runtime or launch failure";
+    case VWL_ERR_ALIGN: return "VWL_ERR_ALIGN: a pointer is not aligned as required";
+    }
+    return "unknown vwl_status";
+}
+
+int vwl_version(void) { return 100; }
+
+vwl_status vwl_workspace_reset(void *workspace, size_t bytes, hipStream_t stream) {
+    if (bytes == 0)
+        return VWL_OK;
+    if (!workspace)
+        return VWL_ERR_NULL;
+    if (!aligned(workspace, 4))
+        return VWL_ERR_ALIGN;
+    return launch_fill_zero(workspace, bytes, stream) == hipSuccess ? VWL_OK : VWL_ERR_HIP;
+}
+
+static bool shape_ok(int B, int K, int V) {
+    if (B < 1 || K < 0 || K > VWL_MAX_K || V < 1)
+        return false;
+    const long double n = (long double)B * (long double)(K + 1) * (long double)V;
+    return n < 9.0e18L && (long long)B * (K + 1) < (1LL << 31);
+}
+
+size_t vwl_asym_workspace_bytes(int B, int K, int V, vwl_dtype dt) {
+    if (!shape_ok(B, K, V) || (dt != VWL_F32 && dt != VWL_BF16))
+        return 0;
+    return ws_layout(B, K + 1, V, elem_bytes(dt), false).total;
+}
+
+size_t vwl_rapid_workspace_bytes(int B, int G, int V, vwl_dtype dt) {
+    if (!shape_ok(B, G, V) || (dt != VWL_F32 && dt != VWL_BF16))
+        return 0;
+    return ws_layout(B, G + 1, V, elem_bytes(dt), true).total;
+}
+
+vwl_status vwl_asym_check(const void *a, const void *b, const void *t, const int32_t *draft,
+                          int B, int K, int V, int dt, float beta, float gamma,
+                          const void *D, const void *gamma_eff, const void *accept,
+                          const void *fused, const void *accept_len, const void *token,
+                          const void *workspace, size_t workspace_bytes, size_t needed_bytes) {
+    if (!a || !b || !t || !D || !gamma_eff || !fused || !accept_len || !token)
+        return VWL_ERR_NULL;
+    if (K > 0 && (!draft || !accept))
+        return VWL_ERR_NULL;
+    if (!shape_ok(B, K, V))
+        return VWL_ERR_SHAPE;
+    if (dt != VWL_F32 && dt != VWL_BF16)
+        return VWL_ERR_DTYPE;
+    if (!finite_f(beta) || !finite_f(gamma) || gamma < 0.0f)
+        return VWL_ERR_PARAM;
+    if (!aligned(a, 16) || !aligned(b, 16) || !aligned(t, 16) || !aligned(D, 4) || !aligned(gamma_eff, 4) ||
+        !aligned(fused, 4) || !aligned(accept_len, 4) || !aligned(token, 4) || (draft && !aligned(draft, 4)))
+        return VWL_ERR_ALIGN;
+    if (!workspace || workspace_bytes < needed_bytes)
+        return VWL_ERR_WORKSPACE;
+    if (!aligned(workspace, 256))
+        return VWL_ERR_ALIGN;
+    return VWL_OK;
+}
+
+vwl_status vwl_rapid_check(const void *z, const void *y, const int32_t *draft,
+                           const float *u_accept, const float *u_sample,
+                           int B, int G, int V, int dt, float eta, float T,
+                           const void *accept, const void *accept_len, const void *token,
+                           const void *workspace, size_t workspace_bytes, size_t needed_bytes) {
+    if (!z || !y || !u_sample || !accept_len || !token)
+        return VWL_ERR_NULL;
+    if (G > 0 && (!draft || !u_accept || !accept))
+        return VWL_ERR_NULL;
+    if (!shape_ok(B, G, V))
+        return VWL_ERR_SHAPE;
+    if (dt != VWL_F32 && dt != VWL_BF16)
+        return VWL_ERR_DTYPE;
+    if (!finite_f(eta) || eta < 0.0f || !finite_f(T) || !(T > 0.0f))
+        return VWL_ERR_PARAM;
+    if (!aligned(z, 16) || !aligned(y, 16) || !aligned(u_sample, 4) || !aligned(accept_len, 4) ||
+        !aligned(token, 4) || (draft && !aligned(draft, 4)) || (u_accept && !aligned(u_accept, 4)))
+        return VWL_ERR_ALIGN;
+    if (!workspace || workspace_bytes < needed_bytes)
+        return VWL_ERR_WORKSPACE;
+    if (!aligned(workspace, 256))
+        return VWL_ERR_ALIGN;
+    return VWL_OK;
+}
+
+vwl_status vwl_plan_info(int mode, int B, int K, int V, vwl_dtype dt, int64_t out[6]) {
+    if (!out)
+        return VWL_ERR_NULL;
+    if (mode != 0 && mode != 1)
+        return VWL_ERR_PARAM;
+    if (!shape_ok(B, K, V))
+        return VWL_ERR_SHAPE;
+    if (dt != VWL_F32 && dt != VWL_BF16)
+        return VWL_ERR_DTYPE;
+    Plan plan;
+    const long long R = (long long)B * (K + 1);
+    if (!make_plan(mode, dt, R, V, plan))
+        return VWL_ERR_HIP;
+    out[0] = plan.W;
+    out[1] = plan.nv;
+    out[2] = plan.n_teams;
+    out[3] = plan.grid;
+    out[4] = kThreads;
+    out[5] = R;
+    return VWL_OK;
+}
+
+/* Tuning hook: pin the vectors-per-thread choice (1, 2, 4 or 8) and/or cap
+ * the number of teams of one mode; 0 restores the automatic plan. */
+vwl_status vwl_set_plan_override(int mode, int nv, int max_teams) {
+    if (mode != 0 && mode != 1)
+        return VWL_ERR_PARAM;
+    if (nv != 0 && nv != 1 && nv != 2 && nv != 4 && nv != 8)
+        return VWL_ERR_PARAM;
+    if (max_teams < 0)
+        return VWL_ERR_PARAM;
+    g_force_nv[mode] = nv;
+    g_force_teams[mode] = max_teams;
+    return VWL_OK;
+}
+
+vwl_status asym_verify(const void *a, const void *b, const void *t, const int32_t *draft,
+                       int B, int K, int V, vwl_dtype dt, float beta, float gamma,
+                       float *D, float *gamma_eff, uint8_t *accept, int32_t *fused,
+                       int32_t *accept_len, int32_t *token, int32_t *dev_err,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    const size_t need = vwl_asym_workspace_bytes(B, K, V, dt);
+    const vwl_status st = vwl_asym_check(a, b, t, draft, B, K, V, (int)dt, beta, gamma, D, gamma_eff,
+                                         accept, fused, accept_len, token, workspace, workspace_bytes, need);
+    if (st != VWL_OK)
+        return st;
+    if (dev_err && !aligned(dev_err, 4))
+        return VWL_ERR_ALIGN;
+    const long long R = (long long)B * (K + 1);
+    Plan plan;
+    if (!make_plan(0, (int)dt, R, V, plan))
+        return VWL_ERR_HIP;
+    const WsLayout L = ws_layout(B, K + 1, V, elem_bytes(dt), false);
+    char *ws = static_cast<char *>(workspace);
+    AsymParams p{};
+    p.a = a;
+    p.b = b;
+    p.t = t;
+    p.draft = draft;
+    p.R = R;
+    p.B = B;
+    p.K = K;
+    p.V = V;
+    p.W = plan.W;
+    p.n_teams = plan.n_teams;
+    p.Wmax = L.Wmax;
+    p.beta = beta;
+    p.gamma = gamma;
+    p.log_gamma = std::log((double)gamma);
+    p.D = D;
+    p.geff = gamma_eff;
+    p.accept = accept;
+    p.fused = fused;
+    p.acc_len = accept_len;
+    p.token = token;
+    p.dev_err = dev_err;
+    p.ctl = reinterpret_cast<uint32_t *>(ws + L.ctl);
+    p.row_ctr = reinterpret_cast<uint32_t *>(ws + L.row_ctr);
+    p.req_ctr = reinterpret_cast<uint32_t *>(ws + L.req_ctr);
+    p.row_info = reinterpret_cast<uint32_t *>(ws + L.row_info);
+    p.rec = reinterpret_cast<uint64_t *>(ws + L.rec);
+    return launch_asym((int)dt, plan, p, stream) == hipSuccess ? VWL_OK : VWL_ERR_HIP;
+}
+
+vwl_status rapid_verify(const void *z, const void *y, const int32_t *draft,
+                        const float *u_accept, const float *u_sample,
+                        int B, int G, int V, vwl_dtype dt, float eta, float T,
+                        uint8_t *accept, int32_t *accept_len, int32_t *token,
+                        float *p_hat_draft, float *q_draft, float *emit_dist,
+                        int32_t *dev_err, void *workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+    const size_t need = vwl_rapid_workspace_bytes(B, G, V, dt);
+    const vwl_status st = vwl_rapid_check(z, y, draft, u_accept, u_sample, B, G, V, (int)dt, eta, T, accept,
+                                          accept_len, token, workspace, workspace_bytes, need);
+    if (st != VWL_OK)
+        return st;
+    if ((dev_err && !aligned(dev_err, 4)) || (p_hat_draft && !aligned(p_hat_draft, 4)) ||
+        (q_draft && !aligned(q_draft, 4)) || (emit_dist && !aligned(emit_dist, 4)))
+        return VWL_ERR_ALIGN;
+    const long long R = (long long)B * (G + 1);
+    Plan plan;
+    if (!make_plan(1, (int)dt, R, V, plan))
+        return VWL_ERR_HIP;
+    const WsLayout L = ws_layout(B, G + 1, V, elem_bytes(dt), true);
+    char *ws = static_cast<char *>(workspace);
+    RapidParams p{};
+    p.z = z;
+    p.y = y;
+    p.draft = draft;
+    p.u_accept = u_accept;
+    p.u_sample = u_sample;
+    p.R = R;
+    p.B = B;
+    p.G = G;
+    p.V = V;
+    p.W = plan.W;
+    p.n_teams = plan.n_teams;
+    p.Wmax = L.Wmax;
+    p.We = L.We;
+    p.eta = eta;
+    p.invT = 1.0f / T;
+    p.T = (double)T;
+    p.eta_d = (double)eta;
+    p.accept = accept;
+    p.acc_len = accept_len;
+    p.token = token;
+    p.dev_err = dev_err;
+    p.p_hat_draft = p_hat_draft;
+    p.q_draft = q_draft;
+    p.emit_dist = emit_dist;
+    p.ctl = reinterpret_cast<uint32_t *>(ws + L.ctl);
+    p.row_ctr = reinterpret_cast<uint32_t *>(ws + L.row_ctr);
+    p.req_ctr = reinterpret_cast<uint32_t *>(ws + L.req_ctr);
+    p.row_info = reinterpret_cast<uint32_t *>(ws + L.row_info);
+    p.rec = reinterpret_cast<uint64_t *>(ws + L.rec);
+    p.rowstat = reinterpret_cast<double *>(ws + L.rowstat);
+    p.emit = reinterpret_cast<double *>(ws + L.emit);
+    return launch_rapid((int)dt, plan, p, stream) == hipSuccess ? VWL_OK : VWL_ERR_HIP;
+}
+
+} // extern "C"

@@ -1,0 +1,284 @@
+// Device-side building blocks shared by the AsymSpec and RAPID kernels:
+// element widening, wavefront/workgroup reductions, and the team protocol
+// that lets the W workgroups of one logit row exchange per-chunk partials.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "vwl_internal.hpp"
+
+namespace vwl {
+
+constexpr int kWaves = kThreads / 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr double kLn2d = 0.6931471805599453;
+
+enum { DT_F32 = 0, DT_BF16 = 1 };
+
+// Elements per 16-byte vector and bytes per element of each dtype.
+template <int DT> struct Elem;
+template <> struct Elem<DT_F32> {
+    static constexpr int kPerVec = 4;
+    static constexpr int kBytes = 4;
+};
+template <> struct Elem<DT_BF16> {
+    static constexpr int kPerVec = 8;
+    static constexpr int kBytes = 2;
+};
+
+// Widen element j of a 16-byte vector to fp32 (exact for both dtypes).
+template <int DT>
+__device__ __forceinline__ float widen(const uint4 &v, int j);
+
+template <>
+__device__ __forceinline__ float widen<DT_F32>(const uint4 &v, int j) {
+    const uint32_t w = j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
+    return __uint_as_float(w);
+}
+
+template <>
+__device__ __forceinline__ float widen<DT_BF16>(const uint4 &v, int j) {
+    const int k = j >> 1;
+    const uint32_t w = k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+    return (j & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+}
+
+// One element of a row, widened to fp32.
+template <int DT>
+__device__ __forceinline__ float load_scalar(const void *base, size_t idx) {
+    if (DT == DT_BF16) {
+        const uint16_t h = static_cast<const uint16_t *>(base)[idx];
+        return __uint_as_float(static_cast<uint32_t>(h) << 16);
+    }
+    return static_cast<const float *>(base)[idx];
+}
+
+// ---------------------------------------------------------------------------
+// Wavefront reductions (64 lanes, butterfly order: every lane ends with the
+// same value, computed in a fixed order, so results are deterministic).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        x = fmaxf(x, __shfl_xor(x, o, 64));
+    return x;
+}
+
+__device__ __forceinline__ double wave_sum(double x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+__device__ __forceinline__ int wave_min_int(int x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        x = min(x, __shfl_xor(x, o, 64));
+    return x;
+}
+
+// Workgroup reductions: wave results go through LDS and every thread combines
+// the kWaves values in the same order, so all threads hold the same result.
+template <int N>
+__device__ __forceinline__ void block_max(float (&x)[N], float *lds /* kWaves*N */) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const float m = wave_max(x[i]);
+        if (lane == 0)
+            lds[wave * N + i] = m;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        float m = lds[i];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w)
+            m = fmaxf(m, lds[w * N + i]);
+        x[i] = m;
+    }
+    __syncthreads();
+}
+
+template <int N>
+__device__ __forceinline__ void block_sum(double (&x)[N], double *lds /* kWaves*N */) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const double s = wave_sum(x[i]);
+        if (lane == 0)
+            lds[wave * N + i] = s;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        double s = lds[i];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w)
+            s += lds[w * N + i];
+        x[i] = s;
+    }
+    __syncthreads();
+}
+
+// Sums of N doubles and the minimum of one int in a single LDS round.
+template <int N>
+__device__ __forceinline__ void block_sum_min(double (&x)[N], int &imin, double *lds /* kWaves*N */,
+                                              int *ldsi /* kWaves */) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const double s = wave_sum(x[i]);
+        if (lane == 0)
+            lds[wave * N + i] = s;
+    }
+    const int m = wave_min_int(imin);
+    if (lane == 0)
+        ldsi[wave] = m;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        double s = lds[i];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w)
+            s += lds[w * N + i];
+        x[i] = s;
+    }
+    int r = ldsi[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w)
+        r = min(r, ldsi[w]);
+    imin = r;
+    __syncthreads();
+}
+
+__device__ __forceinline__ int block_min_int(int x, int *lds /* kWaves */) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int m = wave_min_int(x);
+    if (lane == 0)
+        lds[wave] = m;
+    __syncthreads();
+    int r = lds[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w)
+        r = min(r, lds[w]);
+    __syncthreads();
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// Data exchanged between workgroups of one launch.
+//
+// Every such word (records, counters, per-row results) is written and read
+// only through device-scope (agent) atomic loads and stores, which are
+// coherent across the XCDs by themselves.  The one ordering the protocol
+// needs -- a record's stores are complete before the counter increment that
+// announces it -- is a wait for the issuing thread's outstanding memory
+// operations.  This avoids acquire/release fences, which on this target
+// write back and invalidate the whole L2 on every call (and on every poll of
+// a wait loop).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void wait_stores_complete() {
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+__device__ __forceinline__ uint32_t ld_counter(const uint32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Publish: all earlier stores of this thread complete, then the increment.
+__device__ __forceinline__ uint32_t publish_add(uint32_t *p, uint32_t v) {
+    wait_stores_complete();
+    const uint32_t old = __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); // later loads issue after the result
+    return old;
+}
+__device__ __forceinline__ void st_relaxed(uint32_t *p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_relaxed(uint64_t *p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_relaxed(const uint32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_relaxed(const uint64_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_f64(double *p, double v) {
+    st_relaxed(reinterpret_cast<uint64_t *>(p), static_cast<uint64_t>(__double_as_longlong(v)));
+}
+__device__ __forceinline__ double ld_f64(const double *p) {
+    return __longlong_as_double(static_cast<long long>(ld_relaxed(reinterpret_cast<const uint64_t *>(p))));
+}
+
+// Wall clock (constant 100 MHz) used to bound every wait.
+constexpr uint64_t kWaitLimitTicks = 200000000ull; // ~2 s
+
+// Wait until *ctr >= target.  Called by one thread.  Returns false when the
+// bound expired (the caller records a timeout and abandons its remaining work).
+__device__ __forceinline__ bool wait_at_least(const uint32_t *ctr, uint32_t target) {
+    if (ld_counter(ctr) >= target)
+        return true;
+    const uint64_t t0 = wall_clock64();
+    while (ld_counter(ctr) < target) {
+        __builtin_amdgcn_s_sleep(1);
+        if (wall_clock64() - t0 > kWaitLimitTicks)
+            return false;
+    }
+    __asm__ volatile("" ::: "memory");
+    return true;
+}
+
+__device__ __forceinline__ void set_dev_err(int32_t *dev_err, int bits) {
+    if (dev_err)
+        __hip_atomic_fetch_or(dev_err, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
+// Geometry of one row split over W workgroups.
+//
+// A row of V elements starting at element offset `row_off` of a 16-byte
+// aligned tensor has `head` leading elements before its first 16-byte
+// boundary, `nb` whole vectors, then `tail` trailing elements.  Vectors are
+// split into W contiguous, balanced ranges; head and tail elements are
+// handled one per thread by the first and the last workgroup.
+// ---------------------------------------------------------------------------
+template <int DT>
+struct RowSplit {
+    long long vec0;   // first vector (index into the tensor viewed as uint4)
+    int nv;           // vectors of this workgroup
+    int first_elem;   // element index within the row of this workgroup's first vector
+    int nsc;          // scalar elements of this workgroup (<= 2*(kPerVec-1))
+    int sc_idx0;      // row element index of scalar 0 (head)
+    int n_head;       // how many of the scalars are head elements
+    int sc_idx1;      // row element index of the first tail scalar
+};
+
+template <int DT>
+__device__ __forceinline__ RowSplit<DT> row_split(long long row, int V, int W, int w) {
+    constexpr int EPV = Elem<DT>::kPerVec;
+    const long long off = row * (long long)V;                 // element offset of the row
+    int head = (int)((EPV - (off % EPV)) % EPV);
+    if (head > V)
+        head = V;
+    const long long nb = (V - head) / EPV;
+    const int tail = (int)(V - head - nb * EPV);
+    const long long v0 = (nb * w) / W, v1 = (nb * (w + 1)) / W;
+    RowSplit<DT> s;
+    s.vec0 = (off + head) / EPV + v0;
+    s.nv = (int)(v1 - v0);
+    s.first_elem = head + (int)(v0 * EPV);
+    s.n_head = (w == 0) ? head : 0;
+    s.sc_idx0 = 0;
+    s.sc_idx1 = head + (int)(nb * EPV);
+    s.nsc = s.n_head + ((w == W - 1) ? tail : 0);
+    return s;
+}
+
+template <int DT>
+__device__ __forceinline__ int scalar_index(const RowSplit<DT> &s, int k) {
+    return k < s.n_head ? s.sc_idx0 + k : s.sc_idx1 + (k - s.n_head);
+}
+
+} // namespace vwl

@@ -1,0 +1,110 @@
+// Internal host/device declarations: workspace layout, kernel parameter
+// blocks and the launchers of each kernel family.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace vwl {
+
+constexpr int kThreads = 256; // threads per workgroup (4 wave64)
+
+// Workspace layout (bytes, each block 256-byte aligned).  Sizes depend only on
+// the call's shape, never on the device, so they can be queried on any host.
+//
+//   ctl      64 x u32   [0] ticket counter, [16] exit counter
+//   row_ctr  R x 16 u32 per row: [0] phase-1 arrivals, [1] phase-2 arrivals
+//   req_ctr  B x 16 u32 per request: rows finished
+//   row_info R x 2 u32  per row: fused token, accept flag (request scan input)
+//   rec      R x Wmax x 8 u64  per (row, member) record (see the kernels)
+//   rowstat  R x 4 f64  RAPID only: L_z, L_y, Mhat, L_zhat
+//   emit     B x We x 4 f64  RAPID only: per-chunk residual, target and
+//                             augmented-target sums
+struct WsLayout {
+    size_t ctl, row_ctr, req_ctr, row_info, rec, rowstat, emit, total;
+    int Wmax;
+    int We;
+};
+
+constexpr int kRecWords = 8;
+constexpr int kEmitChunk = 4096; // elements of the emitting row per emit workgroup
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Largest team size any plan may use: one 16-byte vector per thread.
+inline int max_team(int V, int elem_bytes) {
+    const long long per_vec = 16 / elem_bytes;
+    const long long nb = (V + per_vec - 1) / per_vec + 1;
+    long long w = (nb + 255) / 256;
+    return (int)(w < 1 ? 1 : w);
+}
+
+inline WsLayout ws_layout(int B, int P, int V, int elem_bytes, bool rapid) {
+    WsLayout L{};
+    const size_t R = (size_t)B * (size_t)P;
+    L.Wmax = max_team(V, elem_bytes);
+    L.We = rapid ? (int)((V + kEmitChunk - 1) / kEmitChunk) : 0;
+    size_t off = 0;
+    L.ctl = off;      off = align256(off + 64 * 4);
+    L.row_ctr = off;  off = align256(off + R * 16 * 4);
+    L.req_ctr = off;  off = align256(off + (size_t)B * 16 * 4);
+    L.row_info = off; off = align256(off + R * 2 * 4);
+    L.rec = off;      off = align256(off + R * (size_t)L.Wmax * kRecWords * 8);
+    L.rowstat = off;  off = align256(off + (rapid ? R * 4 * 8 : 0));
+    L.emit = off;     off = align256(off + (rapid ? (size_t)B * (size_t)L.We * 4 * 8 : 0));
+    L.total = off;
+    return L;
+}
+
+struct AsymParams {
+    const void *a, *b, *t;
+    const int32_t *draft;
+    long long R;
+    int B, K, V;
+    int W, n_teams, Wmax;
+    float beta, gamma;
+    double log_gamma;
+    float *D, *geff;
+    uint8_t *accept;
+    int32_t *fused, *acc_len, *token, *dev_err;
+    uint32_t *ctl, *row_ctr, *req_ctr, *row_info;
+    uint64_t *rec;
+};
+
+struct RapidParams {
+    const void *z, *y;
+    const int32_t *draft;
+    const float *u_accept, *u_sample;
+    long long R;
+    int B, G, V;
+    int W, n_teams, Wmax, We;
+    float eta, invT;
+    double T, eta_d;
+    uint8_t *accept;
+    int32_t *acc_len, *token, *dev_err;
+    float *p_hat_draft, *q_draft, *emit_dist;
+    uint32_t *ctl, *row_ctr, *req_ctr, *row_info;
+    uint64_t *rec;
+    double *rowstat, *emit;
+};
+
+// A launch plan: vectors per thread per tensor (template choice), team size,
+// number of teams (grid = n_teams * W).
+struct Plan {
+    int nv;
+    int W;
+    int n_teams;
+    int grid;
+};
+
+// Launchers (return hipSuccess or the launch error).
+hipError_t launch_asym(int dt, const Plan &plan, const AsymParams &p, hipStream_t s);
+hipError_t launch_rapid(int dt, const Plan &plan, const RapidParams &p, hipStream_t s);
+hipError_t launch_fill_zero(void *ptr, size_t bytes, hipStream_t s);
+
+// Resident workgroups per CU of each kernel instance (0 when unknown).
+int asym_blocks_per_cu(int dt, int nv);
+int rapid_blocks_per_cu(int dt, int nv);
+
+} // namespace vwl

@@ -47,21 +47,46 @@ __device__ __forceinline__ float fused_score(float a, float b, float t, float be
     return __fmaf_rn(beta, __fsub_rn(a, b), t);
 }
 
-// JSD term of one element in log2 units.  With la2 = log2 p, lb2 = log2 q,
-// d = |la2 - lb2|, rho = 2^-d (ratio of the smaller to the larger
-// probability) and Mx = max(p, q):
-//   p ln(2p/(p+q)) + q ln(2q/(p+q)) = -ln2 * Mx * [(1+rho)(log2(1+rho) - 1) + rho*d]
-// The bracket is returned times Mx (it is <= 0).  Symmetric in p and q, no
-// overflow for any finite or -inf log-probabilities (d is capped at 128,
-// where rho*d underflows to 0).
-__device__ __forceinline__ float jsd_term_neg(float la2, float lb2) {
-    const float mx = fmaxf(la2, lb2);
-    const float d = fminf(fabsf(la2 - lb2), 128.0f);
-    const float M = __builtin_amdgcn_exp2f(mx);
+// JSD term of one element.  With x = ln p - ln q (nats), d = |x| log2e,
+// rho = 2^-d (ratio of the smaller to the larger probability) and
+// Mx = max(p, q), the element contributes
+//   p ln(2p/(p+q)) + q ln(2q/(p+q)) = -ln2 * Mx * g,
+//   g = (1+rho)(log2(1+rho) - 1) + rho*d                    (|x| >= 1.5)
+//     = (1+rho) * s * Q(s),  s = x^2                        (|x| <  1.5)
+// The closed form cancels to O(x^2) from O(x) pieces, so below 1.5 the
+// polynomial Q (fitted to the exact even function x tanh(x/2) - 2 ln
+// cosh(x/2) by jsd_poly_fit.py; 2.4e-7 relative in fp32) takes over; above it
+// the closed form is within 6e-7 relative.  Mx * g (<= 0) is returned.  x is
+// formed from a - b and the row log-sum-exp difference, so it carries no
+// rounding of the separate log-probabilities.  Finite for any finite or -inf
+// logits (d is capped at 128, where rho*d underflows to 0; x is NaN only when
+// both logits are -inf, and then Mx = 0).
+constexpr float kJsdQ0 = -0x1.715474p-3f;
+constexpr float kJsdQ1 = 0x1.715312p-6f;
+constexpr float kJsdQ2 = -0x1.48116ap-9f;
+constexpr float kJsdQ3 = 0x1.138e8ep-12f;
+constexpr float kJsdQ4 = -0x1.9e95e8p-16f;
+constexpr float kJsdQ5 = 0x1.9357fap-20f;
+
+__device__ __forceinline__ float jsd_term(float la2, float lb2, float x) {
+    const float M = __builtin_amdgcn_exp2f(fmaxf(la2, lb2));
+    const float ax = fabsf(x);
+    const float d = fminf(ax * kLog2e, 128.0f);
     const float rho = __builtin_amdgcn_exp2f(-d);
     const float opr = 1.0f + rho;
-    const float l2 = __builtin_amdgcn_logf(opr);
-    const float g = __fmaf_rn(opr, l2, __fmaf_rn(rho, d, -opr)); // opr*(l2 - 1) + rho*d
+    float g;
+    if (ax < 1.5f) {
+        const float s = x * x;
+        float q = __fmaf_rn(kJsdQ5, s, kJsdQ4);
+        q = __fmaf_rn(q, s, kJsdQ3);
+        q = __fmaf_rn(q, s, kJsdQ2);
+        q = __fmaf_rn(q, s, kJsdQ1);
+        q = __fmaf_rn(q, s, kJsdQ0);
+        g = opr * (s * q);
+    } else {
+        const float l2 = __builtin_amdgcn_logf(opr);
+        g = __fmaf_rn(opr, l2, __fmaf_rn(rho, d, -opr)); // opr*(l2 - 1) + rho*d
+    }
     return M * g;
 }
 
@@ -394,18 +419,24 @@ __global__ __launch_bounds__(kThreads, (NV <= 1 ? 4 : NV == 2 ? 3 : 2)) void asy
         __syncthreads();
         const float la_c = (float)sh_row[0]; // row log-sum-exps, log2 units
         const float lb_c = (float)sh_row[1];
+        // L_a - L_b in nats as an unevaluated float pair
+        const double dl = (sh_row[0] - sh_row[1]) * kLn2d;
+        const float dl_hi = (float)dl, dl_lo = (float)(dl - (double)dl_hi);
         float J = 0.f;
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
             if (tid + j * kThreads < psp.nv) {
 #pragma unroll
-                for (int e = 0; e < EPV; ++e)
-                    J += jsd_term_neg(__fmaf_rn(widen<DT>(pa[j], e), kLog2e, -la_c),
-                                      __fmaf_rn(widen<DT>(pb[j], e), kLog2e, -lb_c));
+                for (int e = 0; e < EPV; ++e) {
+                    const float xa = widen<DT>(pa[j], e), xb = widen<DT>(pb[j], e);
+                    J += jsd_term(__fmaf_rn(xa, kLog2e, -la_c), __fmaf_rn(xb, kLog2e, -lb_c),
+                                  ((xa - xb) - dl_hi) - dl_lo);
+                }
             }
         }
         if (tid < psp.nsc)
-            J += jsd_term_neg(__fmaf_rn(psa, kLog2e, -la_c), __fmaf_rn(psb, kLog2e, -lb_c));
+            J += jsd_term(__fmaf_rn(psa, kLog2e, -la_c), __fmaf_rn(psb, kLog2e, -lb_c),
+                          ((psa - psb) - dl_hi) - dl_lo);
         double Jd[1] = {(double)J};
         block_sum<1>(Jd, lds_d);
         if (tid == 0)

@@ -15,20 +15,20 @@
 // Launch 2 (finalise): one wave per row: Mhat (recomputed in fp64 at the
 // argmax), L_zhat, the draft's tail-protected phat and q, the acceptance
 // test; the wave that completes a request runs the first-rejection scan.
-// Launches 3-5 work on the emitting row of each request only, in fp64: the
-// augmented target's log-sum-exp, then per-chunk sums of the residual
-// max(p - phat, p - q, 0) (or of p), then the inverse-CDF crossing of u * S
-// in vocabulary order.
+// Launches 3-6 work on the emitting row of each request only, in fp64: the
+// row's normalisers refined in fp64, the augmented target's log-sum-exp, then
+// per-chunk sums of the residual max(p - phat, p - q, 0) (or of p), then the
+// inverse-CDF crossing of u * S in vocabulary order.
 #include "vwl_device.hpp"
 #include "vwl_internal.hpp"
 
 namespace vwl {
 
 // Record words of one (row, member):
-//   0, 1  sums of 2^(x*log2e - c) for x = z/T and y/T (double bits)
+//   0, 1  sums of 2^(x*log2e/T - c) for x = z and y (double bits)
 //   2     their references cz, cy (two floats, log2 units)
 //   3     sum of 2^(h*log2e - ch) for h = zhat/T (double bits)
-//   4     maximum of h (float), its lowest index (int)
+//   4     maximum of h*log2e (float), its lowest index (int)
 //   5     ch (float, log2 units)
 __device__ __forceinline__ uint64_t pack_fi(float f, int i) {
     return (uint64_t)__float_as_uint(f) | ((uint64_t)(uint32_t)i << 32);
@@ -69,26 +69,36 @@ __device__ __forceinline__ double team_lse2_r(const uint64_t *rec_row, int W, in
 }
 
 // Online sum-of-exp state of one tensor over a thread's elements, fed one
-// 16-byte group at a time.  The reference c is kept in log2 units as the
-// exact fp32 value used in the exponent arguments, so the state means
-// s = sum_v 2^(x_v*log2e - c) without any rounding of the reference itself;
-// the running sum is rescaled once per group.
+// 16-byte group of raw logits x at a time, for the exponent x*c (log2 units,
+// c = log2e/T).  The product is evaluated as an fma with the reference
+// subtracted before rounding, plus the low part of c, so no rounding of x/T
+// or of x*c at the logits' magnitude enters the exponent.  The reference is
+// kept as the exact fp32 value used, so the state means
+// s = sum_v 2^(x_v*c - ref); the running sum is rescaled once per group.
 struct OnlineLseR {
-    float c;   // reference, log2 units (>= max x * log2e up to rounding)
+    float c;   // reference, log2 units (>= max x*c up to rounding)
     double s;
 };
 
+struct ExpCoef {
+    float hi, lo; // c = hi + lo, hi <= c, lo > 0 (so -inf logits stay -inf)
+};
+
+__device__ __forceinline__ float scaled_arg(float x, ExpCoef k, float ref) {
+    return __fmaf_rn(x, k.lo, __fmaf_rn(x, k.hi, -ref));
+}
+
 template <int EPV>
-__device__ __forceinline__ void online_group_r(OnlineLseR &st, const float (&x)[EPV]) {
+__device__ __forceinline__ void online_group_r(OnlineLseR &st, const float (&x)[EPV], ExpCoef k) {
     float g = x[0];
 #pragma unroll
     for (int e = 1; e < EPV; ++e)
         g = fmaxf(g, x[e]);
-    const float c_new = fmaxf(st.c, fmaxf(g, -1e30f) * kLog2e); // finite even for -inf rows
+    const float c_new = fmaxf(st.c, fmaxf(g, -1e30f) * k.hi); // finite even for -inf rows
     float acc = 0.f;
 #pragma unroll
     for (int e = 0; e < EPV; ++e)
-        acc += __builtin_amdgcn_exp2f(__fmaf_rn(x[e], kLog2e, -c_new));
+        acc += __builtin_amdgcn_exp2f(scaled_arg(x[e], k, c_new));
     const float scale = __builtin_amdgcn_exp2f(st.c - c_new);
     st.s = __fma_rn(st.s, (double)scale, (double)acc);
     st.c = c_new;
@@ -99,6 +109,51 @@ __device__ __forceinline__ double rescale_to_r(const OnlineLseR &st, float C) {
     if (!(st.s > 0.0))
         return 0.0;
     return st.s * (double)__builtin_amdgcn_exp2f(st.c - C);
+}
+
+// The augmentation of one element in the second pass.  p = 2^(z*c - Lz2)
+// and q = 2^(y*c - Ly2) with the row log-sum-exps (log2 units) as float
+// pairs, so p and q carry only the exp2 rounding.  h = zhat/T in log2 units is
+// z*c + eta*log2e*(q - p); happ is its fp32 value (for the maximum and the
+// reference), and h_arg(ref) its exponent relative to a reference with the
+// same exact-product treatment as above.
+struct AugCoef {
+    ExpCoef c;
+    float lz_hi, lz_lo, ly_hi, ly_lo, eta2;
+};
+
+__device__ __forceinline__ float aug_dqp(const AugCoef &k, float z, float y) {
+    const float p = __builtin_amdgcn_exp2f(scaled_arg(z, k.c, k.lz_hi) - k.lz_lo);
+    const float q = __builtin_amdgcn_exp2f(scaled_arg(y, k.c, k.ly_hi) - k.ly_lo);
+    return q - p;
+}
+__device__ __forceinline__ float aug_happ(const AugCoef &k, float z, float dqp) {
+    return __fmaf_rn(k.eta2, dqp, z * k.c.hi);
+}
+__device__ __forceinline__ float aug_harg(const AugCoef &k, float z, float dqp, float ref) {
+    return __fmaf_rn(k.eta2, dqp, scaled_arg(z, k.c, ref));
+}
+
+template <int EPV>
+__device__ __forceinline__ void online_group_h(OnlineLseR &st, const AugCoef &k, const float (&z)[EPV],
+                                               const float (&dqp)[EPV], const float (&happ)[EPV]) {
+    float g = happ[0];
+#pragma unroll
+    for (int e = 1; e < EPV; ++e)
+        g = fmaxf(g, happ[e]);
+    const float c_new = fmaxf(st.c, fmaxf(g, -1e30f));
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e)
+        acc += __builtin_amdgcn_exp2f(aug_harg(k, z[e], dqp[e], c_new));
+    const float scale = __builtin_amdgcn_exp2f(st.c - c_new);
+    st.s = __fma_rn(st.s, (double)scale, (double)acc);
+    st.c = c_new;
+}
+
+__device__ __forceinline__ void split_f64(double x, float &hi, float &lo) {
+    hi = (float)x;
+    lo = (float)(x - (double)hi);
 }
 
 template <int DT, int NV>
@@ -120,8 +175,7 @@ __global__ __launch_bounds__(kThreads, (NV <= 2 ? 4 : 3)) void rapid_rows_kernel
     const uint4 *Z4 = static_cast<const uint4 *>(P.z);
     const uint4 *Y4 = static_cast<const uint4 *>(P.y);
     const float NEG_INF = -__builtin_inff();
-    const float invT = P.invT;
-    const float eta = P.eta;
+    const ExpCoef kc{P.c_hi, P.c_lo};
 
     for (long long row = team; row < P.R; row += P.n_teams) {
         const RowSplit<DT> sp = row_split<DT>(row, P.V, P.W, member);
@@ -140,8 +194,8 @@ __global__ __launch_bounds__(kThreads, (NV <= 2 ? 4 : 3)) void rapid_rows_kernel
         }
         float sz = NEG_INF, sy = NEG_INF;
         if (has_sc) {
-            sz = load_scalar<DT>(P.z, row_off + sidx) * invT;
-            sy = load_scalar<DT>(P.y, row_off + sidx) * invT;
+            sz = load_scalar<DT>(P.z, row_off + sidx);
+            sy = load_scalar<DT>(P.y, row_off + sidx);
         }
 
         // ---- first pass: online softmax statistics of z/T and y/T ----
@@ -152,16 +206,16 @@ __global__ __launch_bounds__(kThreads, (NV <= 2 ? 4 : 3)) void rapid_rows_kernel
                 float xz[EPV], xy[EPV];
 #pragma unroll
                 for (int e = 0; e < EPV; ++e) {
-                    xz[e] = widen<DT>(rz[j], e) * invT;
-                    xy[e] = widen<DT>(ry[j], e) * invT;
+                    xz[e] = widen<DT>(rz[j], e);
+                    xy[e] = widen<DT>(ry[j], e);
                 }
-                online_group_r<EPV>(lz, xz);
-                online_group_r<EPV>(ly, xy);
+                online_group_r<EPV>(lz, xz, kc);
+                online_group_r<EPV>(ly, xy, kc);
             }
         if (has_sc) {
             const float a1[1] = {sz}, b1[1] = {sy};
-            online_group_r<1>(lz, a1);
-            online_group_r<1>(ly, b1);
+            online_group_r<1>(lz, a1, kc);
+            online_group_r<1>(ly, b1, kc);
         }
         float mx[2] = {lz.c, ly.c};
         block_max<2>(mx, lds_f);
@@ -195,32 +249,33 @@ __global__ __launch_bounds__(kThreads, (NV <= 2 ? 4 : 3)) void rapid_rows_kernel
         __syncthreads();
 
         // ---- second pass: h = zhat/T = z/T + eta*(q - p); online statistics ----
-        const float lz_c = (float)sh_row[0]; // row log-sum-exps, log2 units
-        const float ly_c = (float)sh_row[1];
-        auto aug = [&](float zs, float ys) {
-            const float p = __builtin_amdgcn_exp2f(__fmaf_rn(zs, kLog2e, -lz_c));
-            const float q = __builtin_amdgcn_exp2f(__fmaf_rn(ys, kLog2e, -ly_c));
-            return __fmaf_rn(eta, q - p, zs);
-        };
+        AugCoef ak;
+        ak.c = kc;
+        split_f64(sh_row[0], ak.lz_hi, ak.lz_lo);
+        split_f64(sh_row[1], ak.ly_hi, ak.ly_lo);
+        ak.eta2 = P.eta2;
         OnlineLseR lh{NEG_INF, 0.0};
         float hmax_t = NEG_INF;
 #pragma unroll
         for (int j = 0; j < NV; ++j)
             if (tid + j * kThreads < sp.nv) {
-                float xh[EPV];
+                float xz[EPV], dq[EPV], ha[EPV];
 #pragma unroll
                 for (int e = 0; e < EPV; ++e) {
-                    xh[e] = aug(widen<DT>(rz[j], e) * invT, widen<DT>(ry[j], e) * invT);
-                    hmax_t = fmaxf(hmax_t, xh[e]);
+                    xz[e] = widen<DT>(rz[j], e);
+                    dq[e] = aug_dqp(ak, xz[e], widen<DT>(ry[j], e));
+                    ha[e] = aug_happ(ak, xz[e], dq[e]);
+                    hmax_t = fmaxf(hmax_t, ha[e]);
                 }
-                online_group_r<EPV>(lh, xh);
+                online_group_h<EPV>(lh, ak, xz, dq, ha);
             }
         float hs = NEG_INF;
         if (has_sc) {
-            hs = aug(sz, sy);
+            const float dq1[1] = {aug_dqp(ak, sz, sy)};
+            hs = aug_happ(ak, sz, dq1[0]);
             hmax_t = fmaxf(hmax_t, hs);
-            const float h1[1] = {hs};
-            online_group_r<1>(lh, h1);
+            const float z1[1] = {sz}, h1[1] = {hs};
+            online_group_h<1>(lh, ak, z1, dq1, h1);
         }
         float hm[2] = {lh.c, hmax_t};
         block_max<2>(hm, lds_f);
@@ -236,11 +291,13 @@ __global__ __launch_bounds__(kThreads, (NV <= 2 ? 4 : 3)) void rapid_rows_kernel
             for (int j = 0; j < NV; ++j)
                 if (!found && tid + j * kThreads < sp.nv)
 #pragma unroll
-                    for (int e = 0; e < EPV; ++e)
-                        if (!found && aug(widen<DT>(rz[j], e) * invT, widen<DT>(ry[j], e) * invT) == Hm) {
+                    for (int e = 0; e < EPV; ++e) {
+                        const float z1 = widen<DT>(rz[j], e);
+                        if (!found && aug_happ(ak, z1, aug_dqp(ak, z1, widen<DT>(ry[j], e))) == Hm) {
                             hi = min(hi, sp.first_elem + (tid + j * kThreads) * EPV + e);
                             found = true;
                         }
+                    }
         }
         hi = block_min_int(hi, lds_i);
         if (tid == 0) {
@@ -283,17 +340,20 @@ __global__ __launch_bounds__(kThreads) void rapid_finalize_kernel(RapidParams P)
     const double T = P.T, eta_d = P.eta_d;
     const size_t row_off = (size_t)row * (size_t)P.V;
     // Mhat: the augmented logit at the argmax, recomputed in fp64
-    double Mh = (double)mh;
+    double Mh = (double)mh * kLn2d;
     if (hidx >= 0 && hidx < P.V) {
         const double zx = (double)load_scalar<DT>(P.z, row_off + hidx) / T;
         const double yx = (double)load_scalar<DT>(P.y, row_off + hidx) / T;
         Mh = zx + eta_d * (exp(yx - Ly) - exp(zx - Lz));
+    } else {
+        hidx = -1;
     }
-    double *rs = P.rowstat + (size_t)row * 4;
+    double *rs = P.rowstat + (size_t)row * kRowStatWords;
     rs[0] = Lz;
     rs[1] = Ly;
     rs[2] = Mh;
     rs[3] = Lh;
+    rs[4] = (double)hidx;
     const int Pn = P.G + 1;
     const long long bi = row / Pn;
     const int i = (int)(row - bi * Pn);
@@ -341,12 +401,71 @@ __global__ __launch_bounds__(kThreads) void rapid_finalize_kernel(RapidParams P)
 
 // ---------------------------------------------------------------------------
 // Emitting row, all in fp64.  With n the accept length: n < G uses the
-// residual max(p - phat, p - q, 0) of row n; otherwise p.  The augmented
-// target's log-sum-exp of that row is recomputed in fp64 first (launch 3),
-// so the residual's three probabilities share fp64 normalisers.
-// Per-request partials in the workspace, [B][We][4]:
-//   0 residual sum, 1 target sum, 2 sum of exp(h - Mhat), 3 unused.
+// residual max(p - phat, p - q, 0) of row n; otherwise p.  The row's
+// normalisers are refined in fp64 before use, so the residual's three
+// probabilities share fp64-accurate normalisers:
+//   launch 3  per chunk: sum exp(z/T - L_z), sum exp(y/T - L_y) around the
+//             row pass's values          -> L_z, L_y (fp64), Mhat at the argmax
+//   launch 4  per chunk: sum exp(h - Mhat) -> L_zhat (fp64)
+//   launch 5  per chunk: residual and target sums
+//   launch 6  the inverse-CDF crossing of u * S in vocabulary order
+// Every workgroup combines the per-chunk partials in chunk order, so all of
+// them derive the same bits.  Per-request partials [B][We][8]:
+//   0 residual sum, 1 target sum, 2 sum of exp(h - Mhat), 3 sum of
+//   exp(z/T - L_z), 4 sum of exp(y/T - L_y).
 // ---------------------------------------------------------------------------
+struct EmitRow {
+    long long row;
+    size_t row_off;
+    int n;
+    bool resid; // n < G: the residual of row n
+};
+
+__device__ __forceinline__ EmitRow emit_row(const RapidParams &P, int bi) {
+    int n = P.acc_len[bi];
+    if (n < 0 || n > P.G) // only after an abandoned row pass; keeps the row index in range
+        n = P.G;
+    EmitRow e;
+    e.n = n;
+    e.resid = n < P.G;
+    e.row = (long long)bi * (P.G + 1) + n;
+    e.row_off = (size_t)e.row * (size_t)P.V;
+    return e;
+}
+
+// Refined statistics of the emitting row (st[0] L_z, st[1] L_y, st[2] Mhat,
+// st[3] L_zhat when with_lh), computed by thread 0 and shared through LDS.
+template <int DT>
+__device__ __forceinline__ void emit_stats(const RapidParams &P, int bi, const EmitRow &er, bool with_lh,
+                                           double *sh_st) {
+    if (threadIdx.x == 0) {
+        const double *rs = P.rowstat + (size_t)er.row * kRowStatWords;
+        const double *parts = P.emit + (size_t)bi * P.We * kEmitWords;
+        double sz = 0.0, sy = 0.0, shh = 0.0;
+        for (int k = 0; k < P.We; ++k) {
+            sz += parts[kEmitWords * k + 3];
+            sy += parts[kEmitWords * k + 4];
+        }
+        const double Lz = rs[0] + log(sz), Ly = rs[1] + log(sy);
+        double Mh = rs[2];
+        const int hidx = (int)rs[4];
+        if (hidx >= 0 && hidx < P.V) {
+            const double zx = (double)load_scalar<DT>(P.z, er.row_off + hidx) / P.T;
+            const double yx = (double)load_scalar<DT>(P.y, er.row_off + hidx) / P.T;
+            Mh = zx + P.eta_d * (exp(yx - Ly) - exp(zx - Lz));
+        }
+        sh_st[0] = Lz;
+        sh_st[1] = Ly;
+        sh_st[2] = Mh;
+        if (with_lh) {
+            for (int k = 0; k < P.We; ++k)
+                shh += parts[kEmitWords * k + 2];
+            sh_st[3] = Mh + log(shh);
+        }
+    }
+    __syncthreads();
+}
+
 template <int DT>
 __device__ __forceinline__ double emit_h(const RapidParams &P, size_t row_off, int v, const double *st,
                                          double &p, double &q) {
@@ -359,7 +478,7 @@ __device__ __forceinline__ double emit_h(const RapidParams &P, size_t row_off, i
 
 template <int DT>
 __device__ __forceinline__ void emit_weights(const RapidParams &P, size_t row_off, int v, const double *st,
-                                             double Lh, bool resid, double &r, double &p) {
+                                             bool resid, double &r, double &p) {
     if (!resid) {
         p = exp((double)load_scalar<DT>(P.z, row_off + v) / P.T - st[0]);
         r = 0.0;
@@ -367,79 +486,86 @@ __device__ __forceinline__ void emit_weights(const RapidParams &P, size_t row_of
     }
     double q;
     const double h = emit_h<DT>(P, row_off, v, st, p, q);
-    const double ph = (h - st[2] < -2.302585092994046) ? p : exp(h - Lh);
+    const double ph = (h - st[2] < -2.302585092994046) ? p : exp(h - st[3]);
     double x = p - ph;
     if (p - q > x)
         x = p - q;
     r = x > 0.0 ? x : 0.0;
 }
 
-// fp64 log-sum-exp of the emitting row's augmented logits from the partials
-// (every workgroup sums them in the same order).
-__device__ __forceinline__ double emit_lse(const RapidParams &P, int bi, const double *st) {
-    const double *parts = P.emit + (size_t)bi * P.We * 4;
-    double s = 0.0;
-    for (int k = 0; k < P.We; ++k)
-        s += parts[4 * k + 2];
-    return st[2] + log(s);
-}
+constexpr int kEmitPerThread = kEmitChunk / kThreads; // contiguous elements per thread
 
-constexpr int kEmitPerThread = kEmitChunk / kThreads; // 16 contiguous elements per thread
+template <int DT>
+__global__ __launch_bounds__(kThreads) void rapid_emit_norm_kernel(RapidParams P) {
+    __shared__ double lds_d[kWaves * 2];
+    const int w = (int)(blockIdx.x % (unsigned)P.We), bi = (int)(blockIdx.x / (unsigned)P.We);
+    const EmitRow er = emit_row(P, bi);
+    const double *rs = P.rowstat + (size_t)er.row * kRowStatWords;
+    const double Lz = rs[0], Ly = rs[1];
+    const int v0 = w * kEmitChunk + threadIdx.x * kEmitPerThread;
+    double s[2] = {0.0, 0.0};
+    for (int e = 0; e < kEmitPerThread; ++e) {
+        const int v = v0 + e;
+        if (v < P.V) {
+            s[0] += exp((double)load_scalar<DT>(P.z, er.row_off + v) / P.T - Lz);
+            if (er.resid)
+                s[1] += exp((double)load_scalar<DT>(P.y, er.row_off + v) / P.T - Ly);
+        }
+    }
+    block_sum<2>(s, lds_d);
+    if (threadIdx.x == 0) {
+        double *o = P.emit + ((size_t)bi * P.We + w) * kEmitWords;
+        o[3] = s[0];
+        o[4] = er.resid ? s[1] : 1.0;
+    }
+}
 
 template <int DT>
 __global__ __launch_bounds__(kThreads) void rapid_emit_lse_kernel(RapidParams P) {
     __shared__ double lds_d[kWaves];
+    __shared__ double sh_st[4];
     const int w = (int)(blockIdx.x % (unsigned)P.We), bi = (int)(blockIdx.x / (unsigned)P.We);
-    const int Pn = P.G + 1;
-    int n = P.acc_len[bi];
-    if (n < 0 || n > P.G) // only after an abandoned row pass; keeps the row index in range
-        n = P.G;
-    if (n == P.G)
+    const EmitRow er = emit_row(P, bi);
+    if (!er.resid)
         return; // no residual on this request
-    const long long row = (long long)bi * Pn + n;
-    const size_t row_off = (size_t)row * (size_t)P.V;
-    const double *st = P.rowstat + (size_t)row * 4;
+    emit_stats<DT>(P, bi, er, false, sh_st);
+    const double st[3] = {sh_st[0], sh_st[1], sh_st[2]};
     const int v0 = w * kEmitChunk + threadIdx.x * kEmitPerThread;
     double s[1] = {0.0};
     for (int e = 0; e < kEmitPerThread; ++e) {
         const int v = v0 + e;
         if (v < P.V) {
             double p, q;
-            s[0] += exp(emit_h<DT>(P, row_off, v, st, p, q) - st[2]);
+            s[0] += exp(emit_h<DT>(P, er.row_off, v, st, p, q) - st[2]);
         }
     }
     block_sum<1>(s, lds_d);
     if (threadIdx.x == 0)
-        P.emit[((size_t)bi * P.We + w) * 4 + 2] = s[0];
+        P.emit[((size_t)bi * P.We + w) * kEmitWords + 2] = s[0];
 }
 
 template <int DT>
 __global__ __launch_bounds__(kThreads) void rapid_emit_sum_kernel(RapidParams P) {
     __shared__ double lds_d[kWaves * 2];
+    __shared__ double sh_st[4];
     const int w = (int)(blockIdx.x % (unsigned)P.We), bi = (int)(blockIdx.x / (unsigned)P.We);
-    const int Pn = P.G + 1;
-    int n = P.acc_len[bi];
-    if (n < 0 || n > P.G) // only after an abandoned row pass; keeps the row index in range
-        n = P.G;
-    const long long row = (long long)bi * Pn + n;
-    const size_t row_off = (size_t)row * (size_t)P.V;
-    const double *st = P.rowstat + (size_t)row * 4;
-    const bool resid = n < P.G;
-    const double Lh = resid ? emit_lse(P, bi, st) : 0.0;
+    const EmitRow er = emit_row(P, bi);
+    emit_stats<DT>(P, bi, er, er.resid, sh_st);
+    const double st[4] = {sh_st[0], sh_st[1], sh_st[2], sh_st[3]};
     const int v0 = w * kEmitChunk + threadIdx.x * kEmitPerThread;
     double s[2] = {0.0, 0.0};
     for (int e = 0; e < kEmitPerThread; ++e) {
         const int v = v0 + e;
         if (v < P.V) {
             double r, p;
-            emit_weights<DT>(P, row_off, v, st, Lh, resid, r, p);
+            emit_weights<DT>(P, er.row_off, v, st, er.resid, r, p);
             s[0] += r;
             s[1] += p;
         }
     }
     block_sum<2>(s, lds_d);
     if (threadIdx.x == 0) {
-        double *o = P.emit + ((size_t)bi * P.We + w) * 4;
+        double *o = P.emit + ((size_t)bi * P.We + w) * kEmitWords;
         o[0] = s[0];
         o[1] = s[1];
     }
@@ -449,46 +575,42 @@ template <int DT>
 __global__ __launch_bounds__(kThreads) void rapid_emit_pick_kernel(RapidParams P) {
     __shared__ double sh_scan[kThreads + 1];
     __shared__ int lds_i[kWaves];
+    __shared__ double sh_st[4];
     const int w = (int)(blockIdx.x % (unsigned)P.We), bi = (int)(blockIdx.x / (unsigned)P.We);
     const int tid = threadIdx.x;
-    const int Pn = P.G + 1;
-    int n = P.acc_len[bi];
-    if (n < 0 || n > P.G) // only after an abandoned row pass; keeps the row index in range
-        n = P.G;
-    const long long row = (long long)bi * Pn + n;
-    const size_t row_off = (size_t)row * (size_t)P.V;
-    const double *st = P.rowstat + (size_t)row * 4;
-    const double *parts = P.emit + (size_t)bi * P.We * 4;
+    const EmitRow er = emit_row(P, bi);
+    const double *parts = P.emit + (size_t)bi * P.We * kEmitWords;
 
     // totals and this chunk's prefix, summed in chunk order by every thread
     double Sr = 0.0, Sp = 0.0;
     for (int k = 0; k < P.We; ++k) {
-        Sr += parts[4 * k];
-        Sp += parts[4 * k + 1];
+        Sr += parts[kEmitWords * k];
+        Sp += parts[kEmitWords * k + 1];
     }
-    const bool use_r = (n < P.G) && (Sr > 0.0);
+    const bool use_r = er.resid && (Sr > 0.0);
     const int sel = use_r ? 0 : 1;
     const double S = use_r ? Sr : Sp;
     double pre = 0.0;
     for (int k = 0; k < w; ++k)
-        pre += parts[4 * k + sel];
-    const double mine = parts[4 * w + sel];
-    const double u = clamp_uniform(P.u_sample[row], (w == 0 && tid == 0) ? P.dev_err : nullptr);
+        pre += parts[kEmitWords * k + sel];
+    const double mine = parts[kEmitWords * w + sel];
+    const double u = clamp_uniform(P.u_sample[er.row], (w == 0 && tid == 0) ? P.dev_err : nullptr);
     const double target = u * S;
     const bool crossing_here = (pre <= target) && (target < pre + mine);
     const bool write_dist = P.emit_dist != nullptr;
     if (!crossing_here && !write_dist)
         return;
 
+    emit_stats<DT>(P, bi, er, use_r, sh_st);
+    const double st[4] = {sh_st[0], sh_st[1], sh_st[2], sh_st[3]};
     const int v0 = w * kEmitChunk + tid * kEmitPerThread;
-    const double Lh = use_r ? emit_lse(P, bi, st) : 0.0;
     double wt[kEmitPerThread];
     double tsum = 0.0;
     for (int e = 0; e < kEmitPerThread; ++e) {
         const int v = v0 + e;
         double r = 0.0, p = 0.0;
         if (v < P.V)
-            emit_weights<DT>(P, row_off, v, st, Lh, use_r, r, p);
+            emit_weights<DT>(P, er.row_off, v, st, use_r, r, p);
         wt[e] = use_r ? r : p;
         tsum += wt[e];
     }
@@ -577,6 +699,10 @@ static hipError_t launch_t(const Plan &plan, const RapidParams &p, hipStream_t s
     if (e != hipSuccess)
         return e;
     const dim3 eg((unsigned)p.We * (unsigned)p.B);
+    hipLaunchKernelGGL((rapid_emit_norm_kernel<DT>), eg, dim3(kThreads), 0, s, p);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
     hipLaunchKernelGGL((rapid_emit_lse_kernel<DT>), eg, dim3(kThreads), 0, s, p);
     e = hipGetLastError();
     if (e != hipSuccess)

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <limits>
 #include <mutex>
 
 #include "vwl.h"
@@ -328,8 +329,20 @@ vwl_status rapid_verify(const void *z, const void *y, const int32_t *draft,
     p.n_teams = plan.n_teams;
     p.Wmax = L.Wmax;
     p.We = L.We;
-    p.eta = eta;
-    p.invT = 1.0f / T;
+    {
+        // log2e / T split into a high part not above it and a positive low
+        // part (a -inf logit times a positive low part stays -inf)
+        const double c = 1.4426950408889634 / (double)T;
+        float hi = (float)c;
+        if ((double)hi > c)
+            hi = std::nextafter(hi, 0.0f);
+        float lo = (float)(c - (double)hi);
+        if (!(lo > 0.0f))
+            lo = std::numeric_limits<float>::min();
+        p.c_hi = hi;
+        p.c_lo = lo;
+        p.eta2 = (float)((double)eta * 1.4426950408889634);
+    }
     p.T = (double)T;
     p.eta_d = (double)eta;
     p.accept = accept;

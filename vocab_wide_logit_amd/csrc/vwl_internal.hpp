@@ -18,9 +18,9 @@ constexpr int kThreads = 256; // threads per workgroup (4 wave64)
 //   req_ctr  B x 16 u32 per request: rows finished
 //   row_info R x 2 u32  per row: fused token, accept flag (request scan input)
 //   rec      R x Wmax x 8 u64  per (row, member) record (see the kernels)
-//   rowstat  R x 4 f64  RAPID only: L_z, L_y, Mhat, L_zhat
-//   emit     B x We x 4 f64  RAPID only: per-chunk residual, target and
-//                             augmented-target sums
+//   rowstat  R x 8 f64  RAPID only: L_z, L_y, Mhat, L_zhat, argmax of zhat
+//   emit     B x We x 8 f64  RAPID only: per-chunk residual, target,
+//                             augmented-target and normaliser sums
 struct WsLayout {
     size_t ctl, row_ctr, req_ctr, row_info, rec, rowstat, emit, total;
     int Wmax;
@@ -29,6 +29,8 @@ struct WsLayout {
 
 constexpr int kRecWords = 8;
 constexpr int kEmitChunk = 4096; // elements of the emitting row per emit workgroup
+constexpr int kRowStatWords = 8;
+constexpr int kEmitWords = 8;
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -51,8 +53,8 @@ inline WsLayout ws_layout(int B, int P, int V, int elem_bytes, bool rapid) {
     L.req_ctr = off;  off = align256(off + (size_t)B * 16 * 4);
     L.row_info = off; off = align256(off + R * 2 * 4);
     L.rec = off;      off = align256(off + R * (size_t)L.Wmax * kRecWords * 8);
-    L.rowstat = off;  off = align256(off + (rapid ? R * 4 * 8 : 0));
-    L.emit = off;     off = align256(off + (rapid ? (size_t)B * (size_t)L.We * 4 * 8 : 0));
+    L.rowstat = off;  off = align256(off + (rapid ? R * kRowStatWords * 8 : 0));
+    L.emit = off;     off = align256(off + (rapid ? (size_t)B * (size_t)L.We * kEmitWords * 8 : 0));
     L.total = off;
     return L;
 }
@@ -79,7 +81,8 @@ struct RapidParams {
     long long R;
     int B, G, V;
     int W, n_teams, Wmax, We;
-    float eta, invT;
+    float c_hi, c_lo; // log2e / T = c_hi + c_lo, c_hi <= log2e / T, c_lo > 0
+    float eta2;       // eta * log2e
     double T, eta_d;
     uint8_t *accept;
     int32_t *acc_len, *token, *dev_err;

@@ -2,13 +2,15 @@
 
 One step = one ``asym_verify`` call over the large batched AsymSpec workload
 (B=256 requests, K=4 drafts -> 1280 rows of a, b, t, V=151936, bf16), with
-inputs resident in HBM.  Prints one JSON line: verified logit rows/s, the
-dominant kernel's roofline (HBM bytes per launch over its event-timed
-duration, against 8 TB/s), the B=64/K=2 workload and the RAPID pass as
-secondary figures, and the fp64 CPU oracle timed on the host as a reported
-baseline.
+inputs resident in HBM.  Prints one JSON line: verified logit rows/s; the
+dominant kernel's roofline (algorithmic HBM bytes per launch over its
+event-timed duration, against 8 TB/s, with the measured traffic of the
+committed counter summary while the kernel sources still match it); the
+B=64/K=2 workload and the RAPID pass as secondary figures; and the fp64 CPU
+oracle timed on the host as a reported baseline.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu-baseline]
+                    [--no-extra] [--calib-copy]
 """
 import argparse
 import json
@@ -22,6 +24,7 @@ if ROOT not in sys.path:
 
 METRIC = "verified logit rows/s (B·(K+1)·V) and achieved HBM GB/s vs peak, 1 GPU"
 PEAK_HBM_GBS = 8000.0
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "asym_rows_kernel_bf16_B256_K4_V151936_traffic.txt")
 
 
 def _say(msg):
@@ -38,9 +41,16 @@ def _device_inputs(vwl, x, copies=1):
     return sets
 
 
+def _events(n):
+    import torch
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
 def time_asym(vwl, x, steps, warmup, copies=1):
-    """Event-timed asym_verify calls on torch's current stream (the stream the
-    library launches on).  Returns (total seconds, per-call ms list)."""
+    """asym_verify calls on torch's current stream (the stream the library
+    launches on), each bracketed by events, with the library recording a
+    third event right after the row kernel.  Returns (wall seconds, per-call
+    ms, per-call row-kernel ms)."""
     import torch
     sets = _device_inputs(vwl, x, copies)
     B, K = x.B, x.K
@@ -51,20 +61,25 @@ def time_asym(vwl, x, steps, warmup, copies=1):
     for i in range(warmup):
         (a, b, t), d = sets[i % copies]
         vwl.asym_verify(a, b, t, d, x.beta, x.gamma, out=out, workspace=ws)
+    start, mid, end = _events(steps), _events(steps), _events(steps)
+    for e in mid:
+        e.record(stream)  # creates the underlying HIP event
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
         (a, b, t), d = sets[i % copies]
-        ev[i][0].record(stream)
+        start[i].record(stream)
+        vwl.set_phase_event(mid[i])
         vwl.asym_verify(a, b, t, d, x.beta, x.gamma, out=out, workspace=ws)
-        ev[i][1].record(stream)
+        end[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = [s.elapsed_time(e) for s, e in ev]
+    vwl.set_phase_event(None)
+    per = [s.elapsed_time(e) for s, e in zip(start, end)]
+    rows = [s.elapsed_time(m) for s, m in zip(start, mid)]
     if int(out.dev_err.cpu()[0]) != 0:
         raise RuntimeError("device error bits set: %d" % int(out.dev_err.cpu()[0]))
-    return wall, per
+    return wall, per, rows
 
 
 def time_rapid(vwl, x, steps, warmup):
@@ -77,20 +92,62 @@ def time_rapid(vwl, x, steps, warmup):
     out = vwl.rapid_out(x.B, x.G, x.V, "cuda")
     for _ in range(warmup):
         vwl.rapid_verify(z, y, d, ua, us, x.eta, x.T, out=out)
-    torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for i in range(steps):
-        ev[i][0].record(stream)
-        vwl.rapid_verify(z, y, d, ua, us, x.eta, x.T, out=out)
-        ev[i][1].record(stream)
+    start, mid, end = _events(steps), _events(steps), _events(steps)
+    for e in mid:
+        e.record(stream)
     torch.cuda.synchronize()
-    return [s.elapsed_time(e) for s, e in ev]
+    for i in range(steps):
+        start[i].record(stream)
+        vwl.set_phase_event(mid[i])
+        vwl.rapid_verify(z, y, d, ua, us, x.eta, x.T, out=out)
+        end[i].record(stream)
+    torch.cuda.synchronize()
+    vwl.set_phase_event(None)
+    return ([s.elapsed_time(e) for s, e in zip(start, end)],
+            [s.elapsed_time(m) for s, m in zip(start, mid)])
+
+
+def stream_read_gbs(nbytes=1 << 30, reps=20):
+    """Read bandwidth of a plain torch reduction over nbytes (a measured
+    streaming reference on this GPU)."""
+    import torch
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        x.sum()
+    torch.cuda.synchronize()
+    s, e = _events(1)[0], _events(1)[0]
+    s.record()
+    for _ in range(reps):
+        x.sum()
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    del x
+    return nbytes / (ms * 1e-3) / 1e9
+
+
+def calib_copy():
+    """The plain copy of known size that the counter runs scale by."""
+    import torch
+    from vocab_wide_logit_amd import profiling
+    n = profiling.COPY_BYTES // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def _median(v):
     v = sorted(v)
     return v[len(v) // 2]
+
+
+def _pct(v, q):
+    v = sorted(v)
+    return v[min(len(v) - 1, int(q * len(v)))]
 
 
 def cpu_baseline(x, runs=3):
@@ -105,8 +162,8 @@ def cpu_baseline(x, runs=3):
     t = _median(times)
     rows = x.B * (x.K + 1)
     return {"value": rows / t, "unit": "rows/s", "cores": oracle.max_threads(), "kind": "oracle",
-            "sample": "the full B=%d, K=%d, V=%d %s call, median of %d runs (%.2f s each)" % (
-                x.B, x.K, x.V, x.dtype, runs, t)}
+            "sample": "the full B=%d, K=%d, V=%d %s call (%d rows), median of %d runs (%.2f s each)" % (
+                x.B, x.K, x.V, x.dtype, rows, runs, t)}
 
 
 def main():
@@ -116,29 +173,37 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run the 1 GiB copy that counter summaries are scaled by")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the pass is independent per request; see DESIGN.md for how it shards). "
-              "Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(requests are independent; sharding is by requests or by vocabulary "
+              "slices, described in the design notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
     import vocab_wide_logit_amd as vwl
     import workloads as W
+    from vocab_wide_logit_amd import profiling
 
     torch.cuda.set_device(0)
     vwl.load_library()
+    if args.calib_copy:
+        _say("calibration copy of %d bytes" % profiling.COPY_BYTES)
+        calib_copy()
     _say("generating B=256 K=4 V=151936 bf16 inputs")
     x = W.large_asym()
     plan = vwl.plan_info("asym", x.B, x.K, x.V, torch.bfloat16)
     _say("plan %s; timing %d steps after %d warmup" % (plan, args.steps, args.warmup))
-    wall, per = time_asym(vwl, x, args.steps, args.warmup)
+    wall, per, rows_ms = time_asym(vwl, x, args.steps, args.warmup)
     rows = x.B * (x.K + 1)
     bytes_per_call = x.algorithmic_bytes()
     ms_step = wall * 1e3 / args.steps
-    ms_kernel = sum(per) / len(per)
-    achieved = bytes_per_call / (ms_kernel * 1e-3) / 1e9
+    ms_rows = sum(rows_ms) / len(rows_ms)
+    ms_call = sum(per) / len(per)
+    achieved = bytes_per_call / (ms_rows * 1e-3) / 1e9
+    traffic = profiling.read_traffic(TRAFFIC_SUMMARY, "asym")
     result = {
         "metric": METRIC,
         "value": rows * args.steps / wall,
@@ -156,27 +221,33 @@ def main():
                    "beta": x.beta, "gamma": x.gamma, "rows_per_step": rows,
                    "identical_rows": 0.2, "tie_rows": 0.05, "plan": plan},
         "tokens_verified_per_s": x.B * x.K * args.steps / wall,
-        "hbm_gbs_per_step": bytes_per_call * args.steps / wall / 1e9,
+        "call_ms": {"mean": ms_call, "median": _median(per), "p10": _pct(per, 0.1), "p90": _pct(per, 0.9)},
+        "hbm_gbs_per_call": bytes_per_call / (ms_call * 1e-3) / 1e9,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "kernel": "asym_rows_kernel<bf16,%d>" % plan["vec_per_thread"],
-                     "bytes_per_launch": bytes_per_call, "avg_launch_ms": ms_kernel,
-                     "p10_ms": sorted(per)[len(per) // 10], "p90_ms": sorted(per)[(9 * len(per)) // 10]},
+                     "bytes_per_launch": bytes_per_call, "avg_launch_ms": ms_rows,
+                     "p10_ms": _pct(rows_ms, 0.1), "p90_ms": _pct(rows_ms, 0.9)},
     }
     if not args.no_extra:
-        _say("secondary: B=64 K=2 bf16 (4 rotating copies) and RAPID B=16 G=10 fp32")
+        _say("secondary: B=64 K=2 bf16 (4 rotating input sets), RAPID B=16 G=10 fp32, stream reference")
         x2 = W.batched_asym()
-        _, per2 = time_asym(vwl, x2, args.steps, args.warmup, copies=4)
+        _, per2, rows2 = time_asym(vwl, x2, args.steps, args.warmup, copies=4)
         ms2 = _median(per2)
         b2 = x2.algorithmic_bytes()
         r3 = W.rapid_c3()
-        per3 = time_rapid(vwl, r3, args.steps, args.warmup)
+        per3, rows3 = time_rapid(vwl, r3, args.steps, args.warmup)
         ms3 = _median(per3)
         b3 = r3.algorithmic_bytes()
+        sgbs = stream_read_gbs()
+        result["stream_read_gbs"] = sgbs
+        result["roofline"]["frac_of_stream"] = achieved / sgbs
         result["secondary"] = {
-            x2.name: {"rows_per_s": x2.B * 3 / (ms2 * 1e-3), "median_call_ms": ms2,
+            x2.name: {"rows_per_s": x2.B * (x2.K + 1) / (ms2 * 1e-3), "median_call_ms": ms2,
+                      "median_row_kernel_ms": _median(rows2),
                       "gbs": b2 / (ms2 * 1e-3) / 1e9, "frac_of_peak": b2 / (ms2 * 1e-3) / 1e9 / PEAK_HBM_GBS},
-            r3.name: {"rows_per_s": r3.B * 11 / (ms3 * 1e-3), "median_call_ms": ms3,
+            r3.name: {"rows_per_s": r3.B * (r3.G + 1) / (ms3 * 1e-3), "median_call_ms": ms3,
+                      "median_row_kernel_ms": _median(rows3),
                       "gbs": b3 / (ms3 * 1e-3) / 1e9, "frac_of_peak": b3 / (ms3 * 1e-3) / 1e9 / PEAK_HBM_GBS,
                       "eta": r3.eta},
         }

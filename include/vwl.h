@@ -197,6 +197,15 @@ vwl_status vwl_rapid_check(const void *z, const void *y, const int32_t *draft,
  * plan except through the documented fp32 summation order of the partials. */
 vwl_status vwl_set_plan_override(int mode, int nv, int max_teams);
 
+/* Profiling hook: while `hip_event` (a hipEvent_t) is non-null, every
+ * asym_verify / rapid_verify call records it on the call's stream right after
+ * enqueuing the row kernel and before the kernels that follow it, so a caller
+ * that records an event of its own just before the call can time the row
+ * kernel alone with hipEventElapsedTime.  Process-wide; pass NULL to stop.
+ * The event stays owned by the caller and must outlive the calls that use it.
+ * A failed record is returned by that call as VWL_ERR_HIP. */
+vwl_status vwl_set_phase_event(void *hip_event);
+
 #ifdef __cplusplus
 }
 #endif

@@ -168,3 +168,7 @@ def test_generator_structure():
     # same seed, same data; generation does not depend on the thread count
     x2 = W.gen_asym(20, 4, 700, "bf16", seed=3, displaced_frac=0.3, identical_frac=0.2, tie_frac=0.05)
     assert np.array_equal(x.a, x2.a) and np.array_equal(x.t, x2.t)
+
+
+def test_phase_event_hook_accepts_null(lib):
+    assert lib.vwl_set_phase_event(None) == 0

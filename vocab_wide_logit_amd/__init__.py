@@ -44,7 +44,7 @@ SYMBOLS = ("vwl_status_string", "vwl_version", "vwl_workspace_reset",
            "vwl_asym_workspace_bytes", "asym_verify",
            "vwl_rapid_workspace_bytes", "rapid_verify",
            "vwl_plan_info", "vwl_asym_check", "vwl_rapid_check",
-           "vwl_set_plan_override")
+           "vwl_set_plan_override", "vwl_set_phase_event")
 
 
 class VwlError(RuntimeError):
@@ -88,6 +88,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.vwl_rapid_check.restype = i
         lib.vwl_set_plan_override.argtypes = [i, i, i]
         lib.vwl_set_plan_override.restype = i
+        lib.vwl_set_phase_event.argtypes = [P]
+        lib.vwl_set_phase_event.restype = i
         _lib = lib
         return lib
 
@@ -161,6 +163,17 @@ def plan_info(mode: str, B: int, K: int, V: int, dtype: torch.dtype) -> dict:
 def set_plan_override(mode: str, vec_per_thread: int = 0, max_teams: int = 0) -> None:
     """Tuning hook: pin vectors per thread / cap teams (0 = automatic)."""
     _check(load_library().vwl_set_plan_override(0 if mode == "asym" else 1, vec_per_thread, max_teams))
+
+
+def set_phase_event(event) -> None:
+    """Profiling hook: record ``event`` (a torch.cuda.Event, or None to stop)
+    on the call's stream between the row kernel and the kernels after it."""
+    ptr = None
+    if event is not None:
+        if not event.cuda_event:
+            raise ValueError("record the event once before handing it to the library")
+        ptr = ctypes.c_void_p(event.cuda_event)
+    _check(load_library().vwl_set_phase_event(ptr))
 
 
 class AsymOut(NamedTuple):

@@ -548,30 +548,35 @@ int asym_blocks_per_cu(int dt, int nv) {
 }
 
 template <int DT, int NV>
-static hipError_t launch_t(const Plan &plan, const AsymParams &p, hipStream_t s) {
+static hipError_t launch_t(const Plan &plan, const AsymParams &p, hipStream_t s, hipEvent_t after_rows) {
     hipLaunchKernelGGL((asym_rows_kernel<DT, NV>), dim3(plan.grid), dim3(kThreads), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
+    if (after_rows) {
+        e = hipEventRecord(after_rows, s);
+        if (e != hipSuccess)
+            return e;
+    }
     const unsigned fin = (unsigned)((p.R + kWaves - 1) / kWaves);
     hipLaunchKernelGGL((asym_finalize_kernel<DT>), dim3(fin), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 
-hipError_t launch_asym(int dt, const Plan &plan, const AsymParams &p, hipStream_t s) {
+hipError_t launch_asym(int dt, const Plan &plan, const AsymParams &p, hipStream_t s, hipEvent_t after_rows) {
     if (dt == DT_BF16) {
         switch (plan.nv) {
-        case 1: return launch_t<DT_BF16, 1>(plan, p, s);
-        case 2: return launch_t<DT_BF16, 2>(plan, p, s);
-        case 4: return launch_t<DT_BF16, 4>(plan, p, s);
-        case 8: return launch_t<DT_BF16, 8>(plan, p, s);
+        case 1: return launch_t<DT_BF16, 1>(plan, p, s, after_rows);
+        case 2: return launch_t<DT_BF16, 2>(plan, p, s, after_rows);
+        case 4: return launch_t<DT_BF16, 4>(plan, p, s, after_rows);
+        case 8: return launch_t<DT_BF16, 8>(plan, p, s, after_rows);
         }
     } else {
         switch (plan.nv) {
-        case 1: return launch_t<DT_F32, 1>(plan, p, s);
-        case 2: return launch_t<DT_F32, 2>(plan, p, s);
-        case 4: return launch_t<DT_F32, 4>(plan, p, s);
-        case 8: return launch_t<DT_F32, 8>(plan, p, s);
+        case 1: return launch_t<DT_F32, 1>(plan, p, s, after_rows);
+        case 2: return launch_t<DT_F32, 2>(plan, p, s, after_rows);
+        case 4: return launch_t<DT_F32, 4>(plan, p, s, after_rows);
+        case 8: return launch_t<DT_F32, 8>(plan, p, s, after_rows);
         }
     }
     return hipErrorInvalidValue;

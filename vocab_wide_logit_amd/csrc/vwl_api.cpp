@@ -6,6 +6,7 @@
 #include <cstdint>
 #include <cstring>
 #include <limits>
+#include <atomic>
 #include <mutex>
 
 #include "vwl.h"
@@ -36,6 +37,7 @@ std::mutex g_dev_mu;
 // Plan overrides for tuning sweeps (0 = automatic).
 int g_force_nv[2] = {0, 0};
 int g_force_teams[2] = {0, 0};
+std::atomic<hipEvent_t> g_phase_event{nullptr};
 
 const DeviceInfo *device_info() {
     int dev = 0;
@@ -246,6 +248,11 @@ vwl_status vwl_set_plan_override(int mode, int nv, int max_teams) {
     return VWL_OK;
 }
 
+vwl_status vwl_set_phase_event(void *hip_event) {
+    g_phase_event.store(static_cast<hipEvent_t>(hip_event));
+    return VWL_OK;
+}
+
 vwl_status asym_verify(const void *a, const void *b, const void *t, const int32_t *draft,
                        int B, int K, int V, vwl_dtype dt, float beta, float gamma,
                        float *D, float *gamma_eff, uint8_t *accept, int32_t *fused,
@@ -291,7 +298,7 @@ vwl_status asym_verify(const void *a, const void *b, const void *t, const int32_
     p.req_ctr = reinterpret_cast<uint32_t *>(ws + L.req_ctr);
     p.row_info = reinterpret_cast<uint32_t *>(ws + L.row_info);
     p.rec = reinterpret_cast<uint64_t *>(ws + L.rec);
-    return launch_asym((int)dt, plan, p, stream) == hipSuccess ? VWL_OK : VWL_ERR_HIP;
+    return launch_asym((int)dt, plan, p, stream, g_phase_event.load()) == hipSuccess ? VWL_OK : VWL_ERR_HIP;
 }
 
 vwl_status rapid_verify(const void *z, const void *y, const int32_t *draft,
@@ -359,7 +366,7 @@ vwl_status rapid_verify(const void *z, const void *y, const int32_t *draft,
     p.rec = reinterpret_cast<uint64_t *>(ws + L.rec);
     p.rowstat = reinterpret_cast<double *>(ws + L.rowstat);
     p.emit = reinterpret_cast<double *>(ws + L.emit);
-    return launch_rapid((int)dt, plan, p, stream) == hipSuccess ? VWL_OK : VWL_ERR_HIP;
+    return launch_rapid((int)dt, plan, p, stream, g_phase_event.load()) == hipSuccess ? VWL_OK : VWL_ERR_HIP;
 }
 
 } // extern "C"

@@ -102,8 +102,10 @@ struct Plan {
 };
 
 // Launchers (return hipSuccess or the launch error).
-hipError_t launch_asym(int dt, const Plan &plan, const AsymParams &p, hipStream_t s);
-hipError_t launch_rapid(int dt, const Plan &plan, const RapidParams &p, hipStream_t s);
+// `after_rows`, when non-null, is recorded on `s` between the row kernel and
+// the kernels that follow it.
+hipError_t launch_asym(int dt, const Plan &plan, const AsymParams &p, hipStream_t s, hipEvent_t after_rows);
+hipError_t launch_rapid(int dt, const Plan &plan, const RapidParams &p, hipStream_t s, hipEvent_t after_rows);
 hipError_t launch_fill_zero(void *ptr, size_t bytes, hipStream_t s);
 
 // Resident workgroups per CU of each kernel instance (0 when unknown).

@@ -1,0 +1,148 @@
+"""Summaries of rocprofv3 runs of ``bench.py`` (kernel durations and HBM
+traffic counters), written as short text files, and the reader ``bench.py``
+uses to attach the measured traffic of the row kernel to its roofline figure.
+
+    python -m vocab_wide_logit_amd.profiling stats  <kernel_stats.csv> <out.txt> <command...>
+    python -m vocab_wide_logit_amd.profiling pmc    <fetch counter csv> <write counter csv> <out.txt> <command...>
+
+The traffic summary scales the row kernel's FETCH_SIZE and WRITE_SIZE (KiB per
+dispatch) by what the same counters read for a plain elementwise copy of a
+known size in the same process, so the figure is in bytes per launch.
+"""
+from __future__ import annotations
+
+import csv
+import hashlib
+import os
+import re
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+
+# sources whose change invalidates a recorded traffic figure, per mode
+KERNEL_SOURCES = {
+    "asym": ("asym.hip", "vwl_device.hpp", "vwl_internal.hpp"),
+    "rapid": ("rapid.hip", "vwl_device.hpp", "vwl_internal.hpp"),
+}
+ROW_KERNEL_RE = {"asym": r"asym_rows_kernel", "rapid": r"rapid_rows_kernel"}
+COPY_KERNEL_RE = r"neg_kernel"        # torch.neg(src, out=dst): reads and writes COPY_BYTES
+COPY_BYTES = 1 << 30
+
+
+def source_hash(mode: str = "asym") -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[mode]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def _rows(path):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _col(row, *names):
+    for n in names:
+        if n in row:
+            return row[n]
+    raise KeyError(names)
+
+
+def short_name(name: str) -> str:
+    name = name.strip()
+    m = re.match(r"^(?:void\s+)?([^(]*)", name)
+    base = m.group(1) if m else name
+    return base.strip()[:110]
+
+
+def summarize_stats(stats_csv: str, out_path: str, command: str) -> None:
+    rows = _rows(stats_csv)
+    lines = ["# rocprofv3 kernel statistics", "",
+             "command: " + command, "source hash (asym kernels): " + source_hash("asym"),
+             "source hash (rapid kernels): " + source_hash("rapid"), "",
+             "%-100s %7s %11s %11s %11s %12s" % ("kernel", "calls", "avg_us", "min_us", "max_us", "total_ms")]
+    for r in rows:
+        name = short_name(_col(r, "Name", "KernelName", "Kernel_Name"))
+        calls = int(_col(r, "Calls"))
+        avg = float(_col(r, "AverageNs")) / 1e3
+        mn = float(_col(r, "MinNs")) / 1e3
+        mx = float(_col(r, "MaxNs")) / 1e3
+        tot = float(_col(r, "TotalDurationNs")) / 1e6
+        lines.append("%-100s %7d %11.2f %11.2f %11.2f %12.3f" % (name, calls, avg, mn, mx, tot))
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def _per_dispatch(path: str, counter: str, kernel_re: str):
+    """Mean over dispatches of the kernels matching kernel_re of the counter
+    (summed over its instances within a dispatch), and the dispatch count."""
+    per = {}
+    for r in _rows(path):
+        if _col(r, "Counter_Name") != counter:
+            continue
+        if not re.search(kernel_re, _col(r, "Kernel_Name")):
+            continue
+        d = _col(r, "Dispatch_Id")
+        per[d] = per.get(d, 0.0) + float(_col(r, "Counter_Value"))
+    if not per:
+        raise ValueError("no %s dispatches of /%s/ in %s" % (counter, kernel_re, path))
+    return sum(per.values()) / len(per), len(per)
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str, out_path: str, command: str, mode: str = "asym") -> dict:
+    kre = ROW_KERNEL_RE[mode]
+    f_rows, n_f = _per_dispatch(fetch_csv, "FETCH_SIZE", kre)
+    w_rows, n_w = _per_dispatch(write_csv, "WRITE_SIZE", kre)
+    f_copy, _ = _per_dispatch(fetch_csv, "FETCH_SIZE", COPY_KERNEL_RE)
+    w_copy, _ = _per_dispatch(write_csv, "WRITE_SIZE", COPY_KERNEL_RE)
+    kib = 1024.0
+    fetch_factor = f_copy * kib / COPY_BYTES     # counter bytes per true byte read
+    write_factor = w_copy * kib / COPY_BYTES
+    fetch_b = f_rows * kib / fetch_factor
+    write_b = w_rows * kib / write_factor
+    res = {"mode": mode, "kernel_regex": kre, "source_hash": source_hash(mode),
+           "fetch_kib_per_dispatch": f_rows, "write_kib_per_dispatch": w_rows,
+           "dispatches_fetch": n_f, "dispatches_write": n_w,
+           "copy_bytes": COPY_BYTES, "copy_fetch_kib": f_copy, "copy_write_kib": w_copy,
+           "fetch_factor": fetch_factor, "write_factor": write_factor,
+           "fetch_bytes_per_launch": fetch_b, "write_bytes_per_launch": write_b,
+           "traffic_bytes_per_launch": fetch_b + write_b}
+    lines = ["# HBM traffic of the row kernel from rocprofv3 counters", "",
+             "command: " + command, ""]
+    lines += ["%s: %s" % (k, v) for k, v in res.items()]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return res
+
+
+def read_traffic(path: str, mode: str = "asym"):
+    """Traffic bytes per launch recorded in a summary, or None when the file
+    is missing or the kernel sources changed since it was taken."""
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ": " in line and not line.startswith("#"):
+                k, v = line.rstrip("\n").split(": ", 1)
+                kv[k] = v
+    if kv.get("source_hash") != source_hash(mode) or kv.get("mode") != mode:
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
+def main(argv):
+    if len(argv) >= 3 and argv[0] == "stats":
+        summarize_stats(argv[1], argv[2], " ".join(argv[3:]))
+    elif len(argv) >= 4 and argv[0] == "pmc":
+        print(summarize_pmc(argv[1], argv[2], argv[3], " ".join(argv[4:])))
+    else:
+        print(__doc__)
+        return 2
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1:]))

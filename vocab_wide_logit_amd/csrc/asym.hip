@@ -74,34 +74,39 @@ __device__ __forceinline__ float jsd_term(float la2, float lb2, float x) {
     const float d = fminf(ax * kLog2e, 128.0f);
     const float rho = __builtin_amdgcn_exp2f(-d);
     const float opr = 1.0f + rho;
-    float g;
-    if (ax < 1.5f) {
-        const float s = x * x;
-        float q = __fmaf_rn(kJsdQ5, s, kJsdQ4);
-        q = __fmaf_rn(q, s, kJsdQ3);
-        q = __fmaf_rn(q, s, kJsdQ2);
-        q = __fmaf_rn(q, s, kJsdQ1);
-        q = __fmaf_rn(q, s, kJsdQ0);
-        g = opr * (s * q);
-    } else {
-        const float l2 = __builtin_amdgcn_logf(opr);
-        g = __fmaf_rn(opr, l2, __fmaf_rn(rho, d, -opr)); // opr*(l2 - 1) + rho*d
-    }
-    return M * g;
+    // both forms, then a select: straight-line code across elements
+    const float l2 = __builtin_amdgcn_logf(opr);
+    const float g_closed = __fmaf_rn(opr, l2, __fmaf_rn(rho, d, -opr)); // opr*(l2 - 1) + rho*d
+    const float s = x * x;
+    float q = __fmaf_rn(kJsdQ5, s, kJsdQ4);
+    q = __fmaf_rn(q, s, kJsdQ3);
+    q = __fmaf_rn(q, s, kJsdQ2);
+    q = __fmaf_rn(q, s, kJsdQ1);
+    q = __fmaf_rn(q, s, kJsdQ0);
+    const float g_poly = opr * (s * q);
+    return M * (ax < 1.5f ? g_poly : g_closed);
+}
+
+// 2^k * x for an integer-valued float k <= 0 (references are integers, so
+// every change of reference is an exact power-of-two rescale).
+__device__ __forceinline__ double scale_pow2(double x, float k) {
+    return ldexp(x, (int)fmaxf(k, -1100.0f));
 }
 
 // Row log-sum-exps, in log2 units, of two tensors from the W records of a
 // row: log2 sum_w s_w 2^(c_w - C), C = max c_w, in fp64 and in one fixed
 // order (lane w handles members w, w+64, ...; butterfly sums), so every
-// caller gets the same bits.  Each lane loads its (first two) members' words
-// once.  Called by one whole wave.  Tensor k has its sums in word sk and its
-// reference in the low (hik = false) or high half of word ck.
+// caller gets the same bits.  The references are integers, so each term is
+// an exact power-of-two rescale.  Called by one whole wave.  Tensor k has its
+// sums in word sk and its reference in the low (hik = false) or high half of
+// word ck.
 __device__ __forceinline__ void team_lse2x(const uint64_t *rec_row, int W, int s0, int c0w, bool hi0,
                                            int s1, int c1w, bool hi1, double &L0, double &L1) {
     const int lane = threadIdx.x & 63;
-    float C0 = -__builtin_inff(), C1 = -__builtin_inff();
+    const float NEG = -3.0e38f;
+    float C0 = NEG, C1 = NEG;
     double a0[2] = {0.0, 0.0}, a1[2] = {0.0, 0.0};
-    float r0[2] = {C0, C0}, r1[2] = {C1, C1};
+    float r0[2] = {NEG, NEG}, r1[2] = {NEG, NEG};
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
         const int w = lane + 64 * k;
@@ -124,22 +129,13 @@ __device__ __forceinline__ void team_lse2x(const uint64_t *rec_row, int W, int s
     }
     C0 = wave_max(C0);
     C1 = wave_max(C1);
-    double t0 = 0.0, t1 = 0.0;
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        if (a0[k] > 0.0)
-            t0 += a0[k] * exp2((double)r0[k] - (double)C0);
-        if (a1[k] > 0.0)
-            t1 += a1[k] * exp2((double)r1[k] - (double)C1);
-    }
+    double t0 = scale_pow2(a0[0], r0[0] - C0) + scale_pow2(a0[1], r0[1] - C0);
+    double t1 = scale_pow2(a1[0], r1[0] - C1) + scale_pow2(a1[1], r1[1] - C1);
     for (int w = lane + 128; w < W; w += 64) { // teams wider than 128 members
         const uint64_t *r = rec_row + (size_t)w * kRecWords;
         const uint64_t x0 = ld_relaxed(r + c0w), x1 = ld_relaxed(r + c1w);
-        const double v0 = as_f64(ld_relaxed(r + s0)), v1 = as_f64(ld_relaxed(r + s1));
-        if (v0 > 0.0)
-            t0 += v0 * exp2((double)(hi0 ? unpack_hi(x0) : unpack_lo(x0)) - (double)C0);
-        if (v1 > 0.0)
-            t1 += v1 * exp2((double)(hi1 ? unpack_hi(x1) : unpack_lo(x1)) - (double)C1);
+        t0 += scale_pow2(as_f64(ld_relaxed(r + s0)), (hi0 ? unpack_hi(x0) : unpack_lo(x0)) - C0);
+        t1 += scale_pow2(as_f64(ld_relaxed(r + s1)), (hi1 ? unpack_hi(x1) : unpack_lo(x1)) - C1);
     }
     t0 = wave_sum(t0);
     t1 = wave_sum(t1);
@@ -148,19 +144,18 @@ __device__ __forceinline__ void team_lse2x(const uint64_t *rec_row, int W, int s
 }
 
 // Online sum-of-exp state of one tensor over a thread's elements, fed one
-// 16-byte group at a time.  The reference c is kept in log2 units as the
-// exact fp32 value used in the exponent arguments, so the state means
-// s = sum_v 2^(x_v*log2e - c) without any rounding of the reference itself.
-// c tracks the running maximum, so the dominant terms have arguments near 0
-// (where the argument's own rounding is smallest); the running sum is
-// rescaled once per group.
+// 16-byte group at a time.  The reference c (log2 units) is an integer at or
+// above the running maximum of x*log2e, so the state means
+// s = sum_v 2^(x_v*log2e - c) exactly as evaluated (the reference itself is
+// never rounded), every exponent argument lies in [-inf, 0], and a change of
+// reference rescales the running sum by an exact power of two.
 struct OnlineLse {
-    float c;   // reference, log2 units
+    float c;   // reference, log2 units, integer-valued
     double s;
 };
 
 __device__ __forceinline__ void online_init(OnlineLse &st) {
-    st.c = -__builtin_inff();
+    st.c = -3.0e38f;
     st.s = 0.0;
 }
 
@@ -170,21 +165,19 @@ __device__ __forceinline__ void online_group(OnlineLse &st, const float (&x)[EPV
 #pragma unroll
     for (int e = 1; e < EPV; ++e)
         g = fmaxf(g, x[e]);
-    const float c_new = fmaxf(st.c, fmaxf(g, -1e30f) * kLog2e); // finite even for -inf rows
-    float acc = 0.f;
+    // finite even for -inf rows
+    const float c_new = fmaxf(st.c, __builtin_ceilf(fmaxf(g, -1e30f) * kLog2e));
+    float acc = __builtin_amdgcn_exp2f(__fmaf_rn(x[0], kLog2e, -c_new));
 #pragma unroll
-    for (int e = 0; e < EPV; ++e)
+    for (int e = 1; e < EPV; ++e)
         acc += __builtin_amdgcn_exp2f(__fmaf_rn(x[e], kLog2e, -c_new));
-    const float scale = __builtin_amdgcn_exp2f(st.c - c_new);
-    st.s = __fma_rn(st.s, (double)scale, (double)acc);
+    st.s = scale_pow2(st.s, st.c - c_new) + (double)acc;
     st.c = c_new;
 }
 
-// Rescale a thread's state to the workgroup reference C (fp64 result).
+// Rescale a thread's state to the workgroup reference C (fp64, exact).
 __device__ __forceinline__ double rescale_to(const OnlineLse &st, float C) {
-    if (!(st.s > 0.0))
-        return 0.0;
-    return st.s * (double)__builtin_amdgcn_exp2f(st.c - C);
+    return scale_pow2(st.s, st.c - C);
 }
 
 // LDS staging of one row's chunk: [tensor][vector slot][thread], 16 bytes
@@ -205,11 +198,11 @@ __device__ __forceinline__ void g2lds16(const uint4 *src, uint4 *lds_wave_base) 
 
 // Stream row r's chunk into LDS (waves 1-3: wave x+1 issues all of tensor x).
 template <int DT, int NV>
-__device__ __forceinline__ void prefetch_bulk(AsymStage<NV> &stage, long long r, int V, int W, int member,
+__device__ __forceinline__ void prefetch_bulk(AsymStage<NV> &stage, long long r, int V, int W, int member, int chunk,
                                               const uint4 *A4, const uint4 *B4, const uint4 *T4) {
     const int lane = threadIdx.x & 63;
-    const RowSplit<DT> s = row_split<DT>(r, V, W, member);
-    const int x = (threadIdx.x >> 6) - 1;
+    const RowSplit<DT> s = row_split<DT>(r, V, W, member, chunk);
+    const int x = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) - 1;
     const uint4 *base = T4;
     if (x == 0)
         base = A4;
@@ -217,20 +210,28 @@ __device__ __forceinline__ void prefetch_bulk(AsymStage<NV> &stage, long long r,
         base = B4;
     const uint4 *src = base + s.vec0 + lane;
     uint4 *dst = &stage.v[x][0][0];
+    if (s.nv >= NV * kThreads) { // the whole slot (uniform)
 #pragma unroll
-    for (int j = 0; j < NV; ++j)
+        for (int j = 0; j < NV; ++j)
 #pragma unroll
-        for (int v = 0; v < kWaves; ++v) {
-            if (v * 64 + lane + j * kThreads < s.nv)
+            for (int v = 0; v < kWaves; ++v)
                 g2lds16(src + v * 64 + j * kThreads, dst + j * kThreads + v * 64);
-        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+#pragma unroll
+            for (int v = 0; v < kWaves; ++v) {
+                if (v * 64 + lane + j * kThreads < s.nv)
+                    g2lds16(src + v * 64 + j * kThreads, dst + j * kThreads + v * 64);
+            }
+    }
 }
 
 // Head/tail scalars of row r (wave 0's first lanes), widened to fp32.
 template <int DT>
-__device__ __forceinline__ void prefetch_scalars(long long r, int V, int W, int member, const void *a,
+__device__ __forceinline__ void prefetch_scalars(long long r, int V, int W, int member, int chunk, const void *a,
                                                  const void *b, const void *t, float &na, float &nb, float &nt) {
-    const RowSplit<DT> s = row_split<DT>(r, V, W, member);
+    const RowSplit<DT> s = row_split<DT>(r, V, W, member, chunk);
     if ((int)threadIdx.x < s.nsc) {
         const size_t off = (size_t)r * (size_t)V + scalar_index<DT>(s, threadIdx.x);
         na = load_scalar<DT>(a, off);
@@ -314,7 +315,7 @@ __device__ __forceinline__ void asym_pass_ab(const AsymParams &P, long long row,
         st_relaxed(rec + 3, pack2(Ca, Cb));
         st_relaxed(rec + 4, pack2(Ct, Fm));
         st_relaxed(rec + 5, (uint64_t)(uint32_t)fi);
-        publish_add(P.row_ctr + (size_t)row * 16, 1u);
+        publish_add_nr(P.row_ctr + (size_t)row * 16, 1u);
     }
 }
 
@@ -332,7 +333,7 @@ __global__ __launch_bounds__(kThreads, (NV <= 1 ? 4 : NV == 2 ? 3 : 2)) void asy
     if (tid == 0)
         sh_u[0] = __hip_atomic_fetch_add(&P.ctl[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    const uint32_t ticket = sh_u[0];
+    const uint32_t ticket = __builtin_amdgcn_readfirstlane(sh_u[0]);
     const int team = (int)(ticket / (uint32_t)P.W);
     const int member = (int)(ticket % (uint32_t)P.W);
     if (team >= P.R)
@@ -349,9 +350,9 @@ __global__ __launch_bounds__(kThreads, (NV <= 1 ? 4 : NV == 2 ? 3 : 2)) void asy
     // pending row waits for its team while the next row's passes A+B run.
     auto issue = [&](long long r) {
         if (!wave0)
-            prefetch_bulk<DT, NV>(stage, r, V, W, member, A4, B4, T4);
+            prefetch_bulk<DT, NV>(stage, r, V, W, member, P.chunk, A4, B4, T4);
         else
-            prefetch_scalars<DT>(r, V, W, member, P.a, P.b, P.t, na, nb, nt);
+            prefetch_scalars<DT>(r, V, W, member, P.chunk, P.a, P.b, P.t, na, nb, nt);
     };
     uint4 ra[NV], rb[NV], rt[NV];
     float sa, sb, st;
@@ -375,7 +376,7 @@ __global__ __launch_bounds__(kThreads, (NV <= 1 ? 4 : NV == 2 ? 3 : 2)) void asy
     take();
     if (row + P.n_teams < P.R)
         issue(row + P.n_teams);
-    RowSplit<DT> sp = row_split<DT>(row, V, W, member);
+    RowSplit<DT> sp = row_split<DT>(row, V, W, member, P.chunk);
     asym_pass_ab<DT, NV>(P, row, member, sp, ra, rb, rt, sa, sb, st, lds_f, lds_d, lds_i);
     for (;;) {
         // the pending row's a, b (raw) and head/tail scalars
@@ -394,7 +395,7 @@ __global__ __launch_bounds__(kThreads, (NV <= 1 ? 4 : NV == 2 ? 3 : 2)) void asy
             take();
             if (next + P.n_teams < P.R)
                 issue(next + P.n_teams);
-            sp = row_split<DT>(next, V, W, member);
+            sp = row_split<DT>(next, V, W, member, P.chunk);
             asym_pass_ab<DT, NV>(P, next, member, sp, ra, rb, rt, sa, sb, st, lds_f, lds_d, lds_i);
         }
 

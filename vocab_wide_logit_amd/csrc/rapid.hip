@@ -178,7 +178,7 @@ __global__ __launch_bounds__(kThreads, (NV <= 2 ? 4 : 3)) void rapid_rows_kernel
     const ExpCoef kc{P.c_hi, P.c_lo};
 
     for (long long row = team; row < P.R; row += P.n_teams) {
-        const RowSplit<DT> sp = row_split<DT>(row, P.V, P.W, member);
+        const RowSplit<DT> sp = row_split<DT>(row, P.V, P.W, member, P.chunk);
         const size_t row_off = (size_t)row * (size_t)P.V;
         const bool has_sc = tid < sp.nsc;
         const int sidx = has_sc ? scalar_index<DT>(sp, tid) : 0;

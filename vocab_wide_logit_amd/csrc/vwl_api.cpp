@@ -60,20 +60,23 @@ const DeviceInfo *device_info() {
     return &d;
 }
 
-// Team size for `nv` vectors per thread: enough workgroups to hold the row.
-int team_size(int V, int dt, int nv) {
+// Team size for `nv` vectors per lane: enough members (of `lanes` lanes
+// each) to hold the row.
+int team_size(int V, int dt, int nv, int lanes) {
     const long long per_vec = 16 / elem_bytes(dt);
     const long long nb = (V + per_vec - 1) / per_vec + 1; // body vectors, upper bound
-    const long long cap = (long long)kThreads * nv;
+    const long long cap = (long long)lanes * nv;
     long long w = (nb + cap - 1) / cap;
     if (w < 1)
         w = 1;
     return (int)w;
 }
 
-// Launch plan: among the vector-per-thread choices, the one that needs the
+// Launch plan: among the vector-per-lane choices, the one that needs the
 // fewest rounds of rows per team at full residency; ties go to the larger
-// chunk (fewer workgroups per row).  Teams are then evened out over rounds.
+// chunk (fewer members per row).  Teams are then evened out over rounds.
+// Every member of the grid is resident at once, so no team waits on a
+// member that cannot start.
 bool make_plan(int mode, int dt, long long R, int V, Plan &plan) {
     const DeviceInfo *d = device_info();
     if (!d)
@@ -87,8 +90,9 @@ bool make_plan(int mode, int dt, long long R, int V, Plan &plan) {
         const int bpc = mode == 0 ? d->asym_bpc[dt][k] : d->rapid_bpc[dt][k];
         if (bpc <= 0)
             continue;
-        const int W = team_size(V, dt, nv);
-        const long long capacity = (long long)bpc * d->cus;
+        const int lanes = mode == 0 ? kAsymLanes : kRapidLanes;
+        const int W = team_size(V, dt, nv, lanes);
+        const long long capacity = (long long)bpc * d->cus * (kThreads / lanes); // members
         long long teams = capacity / W;
         if (teams < 1)
             continue;
@@ -106,12 +110,22 @@ bool make_plan(int mode, int dt, long long R, int V, Plan &plan) {
     }
     if (best_rounds < 0)
         return false;
-    best.grid = best.n_teams * best.W;
+    const long long members = (long long)best.n_teams * best.W;
+    const int per_wg = kThreads / (mode == 0 ? kAsymLanes : kRapidLanes);
+    best.grid = (int)((members + per_wg - 1) / per_wg);
     plan = best;
     return true;
 }
 
 bool finite_f(float x) { return std::isfinite(x); }
+
+// Vectors per member: the widest row body (no head) split evenly over W.
+int member_chunk(int V, int dt, int W) {
+    const int per_vec = 16 / elem_bytes(dt);
+    const long long nb = V / per_vec;
+    const long long c = (nb + W - 1) / W;
+    return (int)(c < 1 ? 1 : c);
+}
 
 } // namespace
 
@@ -283,6 +297,7 @@ vwl_status asym_verify(const void *a, const void *b, const void *t, const int32_
     p.W = plan.W;
     p.n_teams = plan.n_teams;
     p.Wmax = L.Wmax;
+    p.chunk = member_chunk(V, (int)dt, plan.W);
     p.beta = beta;
     p.gamma = gamma;
     p.log_gamma = std::log((double)gamma);
@@ -298,6 +313,7 @@ vwl_status asym_verify(const void *a, const void *b, const void *t, const int32_
     p.req_ctr = reinterpret_cast<uint32_t *>(ws + L.req_ctr);
     p.row_info = reinterpret_cast<uint32_t *>(ws + L.row_info);
     p.rec = reinterpret_cast<uint64_t *>(ws + L.rec);
+    p.row_stat = reinterpret_cast<double *>(ws + L.rowstat);
     return launch_asym((int)dt, plan, p, stream, g_phase_event.load()) == hipSuccess ? VWL_OK : VWL_ERR_HIP;
 }
 
@@ -335,6 +351,7 @@ vwl_status rapid_verify(const void *z, const void *y, const int32_t *draft,
     p.W = plan.W;
     p.n_teams = plan.n_teams;
     p.Wmax = L.Wmax;
+    p.chunk = member_chunk(V, (int)dt, plan.W);
     p.We = L.We;
     {
         // log2e / T split into a high part not above it and a positive low

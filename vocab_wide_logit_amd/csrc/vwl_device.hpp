@@ -55,27 +55,87 @@ __device__ __forceinline__ float load_scalar(const void *base, size_t idx) {
 }
 
 // ---------------------------------------------------------------------------
-// Wavefront reductions (64 lanes, butterfly order: every lane ends with the
-// same value, computed in a fixed order, so results are deterministic).
+// Wavefront all-reductions (64 lanes) without LDS: two DPP steps within each
+// quad (lane ^ 1, lane ^ 2), the half-row and row mirrors (combining groups of
+// 4 and 8), then the gfx950 lane swaps across 16-lane rows and 32-lane
+// halves.  Every step combines two partial results with a commutative
+// operation, so all lanes end with the same bits, in a fixed order: the
+// results are deterministic.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-        x = fmaxf(x, __shfl_xor(x, o, 64));
-    return x;
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+    return __builtin_amdgcn_update_dpp(x, x, CTRL, 0xf, 0xf, false);
+}
+constexpr int kDppXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+// Partner values across 16-lane rows and across 32-lane halves: returns the
+// pair (own, partner) in some order; only commutative uses are made of it.
+__device__ __forceinline__ void swap16(int x, int &u, int &v) {
+    const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    u = p[0];
+    v = p[1];
+}
+__device__ __forceinline__ void swap32(int x, int &u, int &v) {
+    const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    u = p[0];
+    v = p[1];
 }
 
-__device__ __forceinline__ double wave_sum(double x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-        x += __shfl_xor(x, o, 64);
-    return x;
+__device__ __forceinline__ float wave_max(float x) {
+    x = fmaxf(x, __int_as_float(dpp_i<kDppXor1>(__float_as_int(x))));
+    x = fmaxf(x, __int_as_float(dpp_i<kDppXor2>(__float_as_int(x))));
+    x = fmaxf(x, __int_as_float(dpp_i<kDppHalfMirror>(__float_as_int(x))));
+    x = fmaxf(x, __int_as_float(dpp_i<kDppMirror>(__float_as_int(x))));
+    int u, v;
+    swap16(__float_as_int(x), u, v);
+    x = fmaxf(__int_as_float(u), __int_as_float(v));
+    swap32(__float_as_int(x), u, v);
+    return fmaxf(__int_as_float(u), __int_as_float(v));
 }
 
 __device__ __forceinline__ int wave_min_int(int x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-        x = min(x, __shfl_xor(x, o, 64));
+    x = min(x, dpp_i<kDppXor1>(x));
+    x = min(x, dpp_i<kDppXor2>(x));
+    x = min(x, dpp_i<kDppHalfMirror>(x));
+    x = min(x, dpp_i<kDppMirror>(x));
+    int u, v;
+    swap16(x, u, v);
+    x = min(u, v);
+    swap32(x, u, v);
+    return min(u, v);
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double x) {
+    const long long b = __double_as_longlong(x);
+    const int lo = dpp_i<CTRL>((int)b), hi = dpp_i<CTRL>((int)(b >> 32));
+    return __longlong_as_double(((long long)hi << 32) | (long long)(uint32_t)lo);
+}
+
+__device__ __forceinline__ double wave_sum(double x) {
+    x += dpp_d<kDppXor1>(x);
+    x += dpp_d<kDppXor2>(x);
+    x += dpp_d<kDppHalfMirror>(x);
+    x += dpp_d<kDppMirror>(x);
+    {
+        const long long b = __double_as_longlong(x);
+        int l0, l1, h0, h1;
+        swap16((int)b, l0, l1);
+        swap16((int)(b >> 32), h0, h1);
+        x = __longlong_as_double(((long long)h0 << 32) | (long long)(uint32_t)l0) +
+            __longlong_as_double(((long long)h1 << 32) | (long long)(uint32_t)l1);
+    }
+    {
+        const long long b = __double_as_longlong(x);
+        int l0, l1, h0, h1;
+        swap32((int)b, l0, l1);
+        swap32((int)(b >> 32), h0, h1);
+        x = __longlong_as_double(((long long)h0 << 32) | (long long)(uint32_t)l0) +
+            __longlong_as_double(((long long)h1 << 32) | (long long)(uint32_t)l1);
+    }
     return x;
 }
 
@@ -193,6 +253,11 @@ __device__ __forceinline__ uint32_t publish_add(uint32_t *p, uint32_t v) {
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); // later loads issue after the result
     return old;
 }
+// Publish without waiting for the counter's result.
+__device__ __forceinline__ void publish_add_nr(uint32_t *p, uint32_t v) {
+    wait_stores_complete();
+    (void)__hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ void st_relaxed(uint32_t *p, uint32_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -236,42 +301,44 @@ __device__ __forceinline__ void set_dev_err(int32_t *dev_err, int bits) {
 }
 
 // ---------------------------------------------------------------------------
-// Geometry of one row split over W workgroups.
+// Geometry of one row split over W members.
 //
 // A row of V elements starting at element offset `row_off` of a 16-byte
 // aligned tensor has `head` leading elements before its first 16-byte
-// boundary, `nb` whole vectors, then `tail` trailing elements.  Vectors are
-// split into W contiguous, balanced ranges; head and tail elements are
-// handled one per thread by the first and the last workgroup.
+// boundary, `nb` whole vectors, then `tail` trailing elements.  Member w
+// takes the `chunk` vectors starting at w * chunk (the last member of a row
+// may take fewer; `chunk` is fixed per launch, so no division is needed
+// here); head and tail elements are handled one per lane by the first and
+// the last member.
 // ---------------------------------------------------------------------------
 template <int DT>
 struct RowSplit {
     long long vec0;   // first vector (index into the tensor viewed as uint4)
-    int nv;           // vectors of this workgroup
-    int first_elem;   // element index within the row of this workgroup's first vector
-    int nsc;          // scalar elements of this workgroup (<= 2*(kPerVec-1))
+    int nv;           // vectors of this member
+    int first_elem;   // element index within the row of this member's first vector
+    int nsc;          // scalar elements of this member (<= 2*(kPerVec-1))
     int sc_idx0;      // row element index of scalar 0 (head)
     int n_head;       // how many of the scalars are head elements
     int sc_idx1;      // row element index of the first tail scalar
 };
 
 template <int DT>
-__device__ __forceinline__ RowSplit<DT> row_split(long long row, int V, int W, int w) {
+__device__ __forceinline__ RowSplit<DT> row_split(long long row, int V, int W, int w, int chunk) {
     constexpr int EPV = Elem<DT>::kPerVec;
     const long long off = row * (long long)V;                 // element offset of the row
-    int head = (int)((EPV - (off % EPV)) % EPV);
+    int head = (int)((EPV - (int)(off & (EPV - 1))) & (EPV - 1));
     if (head > V)
         head = V;
-    const long long nb = (V - head) / EPV;
-    const int tail = (int)(V - head - nb * EPV);
-    const long long v0 = (nb * w) / W, v1 = (nb * (w + 1)) / W;
+    const int nb = (V - head) / EPV;
+    const int tail = V - head - nb * EPV;
+    const int v0 = min(w * chunk, nb), v1 = min(v0 + chunk, nb);
     RowSplit<DT> s;
     s.vec0 = (off + head) / EPV + v0;
-    s.nv = (int)(v1 - v0);
-    s.first_elem = head + (int)(v0 * EPV);
+    s.nv = v1 - v0;
+    s.first_elem = head + v0 * EPV;
     s.n_head = (w == 0) ? head : 0;
     s.sc_idx0 = 0;
-    s.sc_idx1 = head + (int)(nb * EPV);
+    s.sc_idx1 = head + nb * EPV;
     s.nsc = s.n_head + ((w == W - 1) ? tail : 0);
     return s;
 }

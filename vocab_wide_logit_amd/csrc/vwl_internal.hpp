@@ -18,7 +18,8 @@ constexpr int kThreads = 256; // threads per workgroup (4 wave64)
 //   req_ctr  B x 16 u32 per request: rows finished
 //   row_info R x 2 u32  per row: fused token, accept flag (request scan input)
 //   rec      R x Wmax x 8 u64  per (row, member) record (see the kernels)
-//   rowstat  R x 8 f64  RAPID only: L_z, L_y, Mhat, L_zhat, argmax of zhat
+//   rowstat  R x 8 f64  RAPID: L_z, L_y, Mhat, L_zhat, argmax of zhat
+//            R x 4 f64  AsymSpec: L_a, L_b, L_t (log2 units), fused token
 //   emit     B x We x 8 f64  RAPID only: per-chunk residual, target,
 //                             augmented-target and normaliser sums
 struct WsLayout {
@@ -34,18 +35,22 @@ constexpr int kEmitWords = 8;
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Largest team size any plan may use: one 16-byte vector per thread.
-inline int max_team(int V, int elem_bytes) {
+// Lanes of one team member (a whole workgroup in both modes).
+constexpr int kAsymLanes = kThreads;
+constexpr int kRapidLanes = kThreads;
+
+// Largest team size any plan may use: one 16-byte vector per lane.
+inline int max_team(int V, int elem_bytes, int lanes) {
     const long long per_vec = 16 / elem_bytes;
     const long long nb = (V + per_vec - 1) / per_vec + 1;
-    long long w = (nb + 255) / 256;
+    long long w = (nb + lanes - 1) / lanes;
     return (int)(w < 1 ? 1 : w);
 }
 
 inline WsLayout ws_layout(int B, int P, int V, int elem_bytes, bool rapid) {
     WsLayout L{};
     const size_t R = (size_t)B * (size_t)P;
-    L.Wmax = max_team(V, elem_bytes);
+    L.Wmax = max_team(V, elem_bytes, rapid ? kRapidLanes : kAsymLanes);
     L.We = rapid ? (int)((V + kEmitChunk - 1) / kEmitChunk) : 0;
     size_t off = 0;
     L.ctl = off;      off = align256(off + 64 * 4);
@@ -53,7 +58,7 @@ inline WsLayout ws_layout(int B, int P, int V, int elem_bytes, bool rapid) {
     L.req_ctr = off;  off = align256(off + (size_t)B * 16 * 4);
     L.row_info = off; off = align256(off + R * 2 * 4);
     L.rec = off;      off = align256(off + R * (size_t)L.Wmax * kRecWords * 8);
-    L.rowstat = off;  off = align256(off + (rapid ? R * kRowStatWords * 8 : 0));
+    L.rowstat = off;  off = align256(off + R * (rapid ? kRowStatWords : 4) * 8);
     L.emit = off;     off = align256(off + (rapid ? (size_t)B * (size_t)L.We * kEmitWords * 8 : 0));
     L.total = off;
     return L;
@@ -65,6 +70,7 @@ struct AsymParams {
     long long R;
     int B, K, V;
     int W, n_teams, Wmax;
+    int chunk;          // vectors per member (fixed per launch)
     float beta, gamma;
     double log_gamma;
     float *D, *geff;
@@ -72,6 +78,8 @@ struct AsymParams {
     int32_t *fused, *acc_len, *token, *dev_err;
     uint32_t *ctl, *row_ctr, *req_ctr, *row_info;
     uint64_t *rec;
+    double *row_stat;
+    uint32_t n_waves; // waves in the launch (exit count)
 };
 
 struct RapidParams {
@@ -81,6 +89,7 @@ struct RapidParams {
     long long R;
     int B, G, V;
     int W, n_teams, Wmax, We;
+    int chunk;          // vectors per member (fixed per launch)
     float c_hi, c_lo; // log2e / T = c_hi + c_lo, c_hi <= log2e / T, c_lo > 0
     float eta2;       // eta * log2e
     double T, eta_d;

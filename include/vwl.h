@@ -122,6 +122,9 @@ vwl_status asym_verify(const void *a, const void *b, const void *t,
                        int32_t *accept_len, int32_t *token, int32_t *dev_err,
                        void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Largest vocabulary a RAPID call accepts (2^21 logits per row). */
+#define VWL_RAPID_MAX_V 2097152
+
 /* ---------------------------------------------------------------------------
  * RAPID verification (RAPID notes, key designs 2-4)
  *
@@ -145,7 +148,8 @@ vwl_status asym_verify(const void *a, const void *b, const void *t,
  *   draft     [B][G] int32 (may be null when G == 0).
  *   u_accept  [B][G] fp32 in [0,1) (may be null when G == 0);
  *   u_sample  [B][G+1] fp32 in [0,1).
- *   B >= 1, 0 <= G <= VWL_MAX_K, V >= 1; eta finite and >= 0; T finite and > 0.
+ *   B >= 1, 0 <= G <= VWL_MAX_K, 1 <= V <= VWL_RAPID_MAX_V; eta finite and
+ *   >= 0; T finite and > 0.  Otherwise VWL_ERR_SHAPE / VWL_ERR_PARAM.
  * Outputs:
  *   accept     [B][G] uint8 (may be null when G == 0)
  *   accept_len, token  [B] int32 (required)

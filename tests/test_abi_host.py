@@ -172,3 +172,16 @@ def test_generator_structure():
 
 def test_phase_event_hook_accepts_null(lib):
     assert lib.vwl_set_phase_event(None) == 0
+
+
+def test_rapid_vocabulary_limit(lib):
+    """RAPID rejects V above VWL_RAPID_MAX_V (the tail's geometry limit)."""
+    import re
+    hdr = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "vwl.h")).read()
+    vmax = int(re.search(r"#define VWL_RAPID_MAX_V (\d+)", hdr).group(1))
+    assert lib.vwl_rapid_workspace_bytes(1, 1, vmax, 0) > 0
+    p = ctypes.c_void_p(256)
+    args = lambda V: (p, p, p, p, p, 1, 1, V, 0, ctypes.c_float(1.0), ctypes.c_float(1.0), p, p, p, p,
+                      ctypes.c_size_t(1 << 40), ctypes.c_size_t(1))
+    assert lib.vwl_rapid_check(*args(vmax)) == 0
+    assert lib.vwl_rapid_check(*args(vmax + 1)) == 2

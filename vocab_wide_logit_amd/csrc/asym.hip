@@ -34,13 +34,6 @@ namespace vwl {
 //   4     reference of the sum of t (log2 units), maximum of the fused score
 //   5     lowest index of the fused maximum (low 32 bits)
 //   6     JSD partial sum_v Mx_v * g_v over the chunk (double bits)
-__device__ __forceinline__ uint64_t pack2(float lo, float hi) {
-    return (uint64_t)__float_as_uint(lo) | ((uint64_t)__float_as_uint(hi) << 32);
-}
-__device__ __forceinline__ float unpack_lo(uint64_t w) { return __uint_as_float((uint32_t)w); }
-__device__ __forceinline__ float unpack_hi(uint64_t w) { return __uint_as_float((uint32_t)(w >> 32)); }
-__device__ __forceinline__ double as_f64(uint64_t w) { return __longlong_as_double((long long)w); }
-__device__ __forceinline__ uint64_t f64_bits(double x) { return (uint64_t)__double_as_longlong(x); }
 
 // The delta-fusion score t + beta*(a - b), evaluated the same way everywhere.
 __device__ __forceinline__ float fused_score(float a, float b, float t, float beta) {
@@ -85,12 +78,6 @@ __device__ __forceinline__ float jsd_term(float la2, float lb2, float x) {
     q = __fmaf_rn(q, s, kJsdQ0);
     const float g_poly = opr * (s * q);
     return M * (ax < 1.5f ? g_poly : g_closed);
-}
-
-// 2^k * x for an integer-valued float k <= 0 (references are integers, so
-// every change of reference is an exact power-of-two rescale).
-__device__ __forceinline__ double scale_pow2(double x, float k) {
-    return ldexp(x, (int)fmaxf(k, -1100.0f));
 }
 
 // Row log-sum-exps, in log2 units, of two tensors from the W records of a

@@ -12,13 +12,11 @@
 //                maximum's lowest index -> record
 // Several teams share each compute unit, so one team's wait overlaps the
 // others' loads and arithmetic.
-// Launch 2 (finalise): one wave per row: Mhat (recomputed in fp64 at the
-// argmax), L_zhat, the draft's tail-protected phat and q, the acceptance
-// test; the wave that completes a request runs the first-rejection scan.
-// Launches 3-6 work on the emitting row of each request only, in fp64: the
-// row's normalisers refined in fp64, the augmented target's log-sum-exp, then
-// per-chunk sums of the residual max(p - phat, p - q, 0) (or of p), then the
-// inverse-CDF crossing of u * S in vocabulary order.
+// Launch 2 (the tail): per request, row statistics and the acceptance test
+// of each row, the first rejection, then the emitting row in fp64 (refined
+// normalisers, the augmented target's log-sum-exp, the residual
+// max(p - phat, p - q, 0) or p, and the inverse-CDF draw in vocabulary
+// order), phase by phase across the request's workgroups.
 #include "vwl_device.hpp"
 #include "vwl_internal.hpp"
 
@@ -43,14 +41,13 @@ __device__ __forceinline__ double clamp_uniform(float u, int32_t *dev_err) {
     return x;
 }
 
-__device__ __forceinline__ double as_f64(uint64_t w) { return __longlong_as_double((long long)w); }
-__device__ __forceinline__ uint64_t f64_bits(double x) { return (uint64_t)__double_as_longlong(x); }
 
 // Row log-sum-exp in log2 units from the W records (fixed order; same
-// scheme as the AsymSpec kernel).  Called by one whole wave.
+// scheme as the AsymSpec kernel: integer references, exact power-of-two
+// rescales, butterfly sums).  Called by one whole wave.
 __device__ __forceinline__ double team_lse2_r(const uint64_t *rec_row, int W, int word, int cword, bool hi) {
     const int lane = threadIdx.x & 63;
-    float C = -__builtin_inff();
+    float C = -3.0e38f;
     for (int w = lane; w < W; w += 64) {
         const uint64_t x = ld_relaxed(rec_row + (size_t)w * kRecWords + cword);
         C = fmaxf(C, __uint_as_float(hi ? (uint32_t)(x >> 32) : (uint32_t)x));
@@ -60,9 +57,7 @@ __device__ __forceinline__ double team_lse2_r(const uint64_t *rec_row, int W, in
     for (int w = lane; w < W; w += 64) {
         const uint64_t *r = rec_row + (size_t)w * kRecWords;
         const uint64_t x = ld_relaxed(r + cword);
-        const double sw = as_f64(ld_relaxed(r + word));
-        if (sw > 0.0)
-            s += sw * exp2((double)__uint_as_float(hi ? (uint32_t)(x >> 32) : (uint32_t)x) - (double)C);
+        s += scale_pow2(as_f64(ld_relaxed(r + word)), __uint_as_float(hi ? (uint32_t)(x >> 32) : (uint32_t)x) - C);
     }
     s = wave_sum(s);
     return (double)C + log2(s);
@@ -73,10 +68,11 @@ __device__ __forceinline__ double team_lse2_r(const uint64_t *rec_row, int W, in
 // c = log2e/T).  The product is evaluated as an fma with the reference
 // subtracted before rounding, plus the low part of c, so no rounding of x/T
 // or of x*c at the logits' magnitude enters the exponent.  The reference is
-// kept as the exact fp32 value used, so the state means
-// s = sum_v 2^(x_v*c - ref); the running sum is rescaled once per group.
+// an integer at or above the running maximum, so the state means
+// s = sum_v 2^(x_v*c - ref) exactly as evaluated, and a change of reference
+// is an exact power-of-two rescale.
 struct OnlineLseR {
-    float c;   // reference, log2 units (>= max x*c up to rounding)
+    float c;   // reference, log2 units, integer-valued
     double s;
 };
 
@@ -94,21 +90,19 @@ __device__ __forceinline__ void online_group_r(OnlineLseR &st, const float (&x)[
 #pragma unroll
     for (int e = 1; e < EPV; ++e)
         g = fmaxf(g, x[e]);
-    const float c_new = fmaxf(st.c, fmaxf(g, -1e30f) * k.hi); // finite even for -inf rows
-    float acc = 0.f;
+    // finite even for -inf rows (the high part of c is positive)
+    const float c_new = fmaxf(st.c, __builtin_ceilf(fmaxf(g, -1e30f) * k.hi));
+    float acc = __builtin_amdgcn_exp2f(scaled_arg(x[0], k, c_new));
 #pragma unroll
-    for (int e = 0; e < EPV; ++e)
+    for (int e = 1; e < EPV; ++e)
         acc += __builtin_amdgcn_exp2f(scaled_arg(x[e], k, c_new));
-    const float scale = __builtin_amdgcn_exp2f(st.c - c_new);
-    st.s = __fma_rn(st.s, (double)scale, (double)acc);
+    st.s = scale_pow2(st.s, st.c - c_new) + (double)acc;
     st.c = c_new;
 }
 
-// Rescale a thread's state to the workgroup reference C (fp64 result).
+// Rescale a thread's state to the workgroup reference C (fp64, exact).
 __device__ __forceinline__ double rescale_to_r(const OnlineLseR &st, float C) {
-    if (!(st.s > 0.0))
-        return 0.0;
-    return st.s * (double)__builtin_amdgcn_exp2f(st.c - C);
+    return scale_pow2(st.s, st.c - C);
 }
 
 // The augmentation of one element in the second pass.  p = 2^(z*c - Lz2)
@@ -141,13 +135,12 @@ __device__ __forceinline__ void online_group_h(OnlineLseR &st, const AugCoef &k,
 #pragma unroll
     for (int e = 1; e < EPV; ++e)
         g = fmaxf(g, happ[e]);
-    const float c_new = fmaxf(st.c, fmaxf(g, -1e30f));
-    float acc = 0.f;
+    const float c_new = fmaxf(st.c, __builtin_ceilf(fmaxf(g, -1e30f)));
+    float acc = __builtin_amdgcn_exp2f(aug_harg(k, z[0], dqp[0], c_new));
 #pragma unroll
-    for (int e = 0; e < EPV; ++e)
+    for (int e = 1; e < EPV; ++e)
         acc += __builtin_amdgcn_exp2f(aug_harg(k, z[e], dqp[e], c_new));
-    const float scale = __builtin_amdgcn_exp2f(st.c - c_new);
-    st.s = __fma_rn(st.s, (double)scale, (double)acc);
+    st.s = scale_pow2(st.s, st.c - c_new) + (double)acc;
     st.c = c_new;
 }
 
@@ -199,7 +192,7 @@ __global__ __launch_bounds__(kThreads, (NV <= 2 ? 4 : 3)) void rapid_rows_kernel
         }
 
         // ---- first pass: online softmax statistics of z/T and y/T ----
-        OnlineLseR lz{NEG_INF, 0.0}, ly{NEG_INF, 0.0};
+        OnlineLseR lz{-3.0e38f, 0.0}, ly{-3.0e38f, 0.0};
 #pragma unroll
         for (int j = 0; j < NV; ++j)
             if (tid + j * kThreads < sp.nv) {
@@ -254,7 +247,7 @@ __global__ __launch_bounds__(kThreads, (NV <= 2 ? 4 : 3)) void rapid_rows_kernel
         split_f64(sh_row[0], ak.lz_hi, ak.lz_lo);
         split_f64(sh_row[1], ak.ly_hi, ak.ly_lo);
         ak.eta2 = P.eta2;
-        OnlineLseR lh{NEG_INF, 0.0};
+        OnlineLseR lh{-3.0e38f, 0.0};
         float hmax_t = NEG_INF;
 #pragma unroll
         for (int j = 0; j < NV; ++j)
@@ -309,64 +302,149 @@ __global__ __launch_bounds__(kThreads, (NV <= 2 ? 4 : 3)) void rapid_rows_kernel
     }
 }
 
-// One wave per row: row statistics from the W records (Mhat recomputed in
-// fp64 at the argmax), the tail-protected acceptance test of the draft, and
-// the first-rejection scan by the wave that completes a request.
+// ---------------------------------------------------------------------------
+// Launch 2, the tail: one team of We workgroups per request; workgroup w
+// owns the EPT * 256 elements of the request's emitting row starting at
+// w * EPT * 256 (EPT contiguous elements per thread).  Phases, separated by
+// barriers of the request's team:
+//   0  one wave per row of the request: row statistics from the W records
+//      (Mhat recomputed in fp64 at the argmax), the draft's tail-protected
+//      phat and q and the acceptance test
+//   1  accept length n; per element p' = exp(z/T - L_z), q' = exp(y/T - L_y)
+//      around the row pass's values (kept in registers) -> chunk sums ->
+//      L_z, L_y refined in fp64, Mhat recomputed with them
+//   2  (residual rows) e = exp(h - Mhat), kept, and the tail-protection flag
+//      -> chunk sums -> L_zhat in fp64
+//   3  residual max(p - phat, p - q, 0) (or p) per element -> chunk sums
+//   4  the chunk that holds u * S walks its elements in vocabulary order;
+//      emit_dist when requested.
+// Chunk intervals come from one fixed-order running sum evaluated the same
+// way by every workgroup, so they tile [0, S) exactly.  Everything on the
+// emitting row is fp64, with three exponentials per element.
+// With n < G the residual of row n is drawn from (p of row n when the
+// residual is all zero); with n = G, p of the bonus row.
+// Per-request partials [B][We][8]: 0 residual/target weights, 1 target,
+// 2 exp(h - Mhat), 3 p', 4 q'.
+// ---------------------------------------------------------------------------
+
+// Row statistics and the acceptance test of one row (one whole wave): all
+// record words of the row are loaded in one round.
 template <int DT>
-__global__ __launch_bounds__(kThreads) void rapid_finalize_kernel(RapidParams P) {
+__device__ __forceinline__ void tail_row(const RapidParams &P, long long row) {
     const int lane = threadIdx.x & 63;
-    const long long row = (long long)blockIdx.x * kWaves + (threadIdx.x >> 6);
-    if (blockIdx.x == 0 && threadIdx.x == 0)
-        P.ctl[0] = 0u; // ticket counter of the row kernel, for the next call
-    if (row >= P.R)
-        return;
-    const uint64_t *rec_row = P.rec + (size_t)row * P.Wmax * kRecWords;
-    const double Lz = team_lse2_r(rec_row, P.W, 0, 2, false) * kLn2d;
-    const double Ly = team_lse2_r(rec_row, P.W, 1, 2, true) * kLn2d;
-    const double Lh = team_lse2_r(rec_row, P.W, 3, 5, false) * kLn2d;
-    float mh = -__builtin_inff();
-    for (int w = lane; w < P.W; w += 64)
-        mh = fmaxf(mh, __uint_as_float((uint32_t)ld_relaxed(rec_row + (size_t)w * kRecWords + 4)));
-    mh = wave_max(mh);
-    int hidx = 0x7fffffff;
-    for (int w = lane; w < P.W; w += 64) {
-        const uint64_t w4 = ld_relaxed(rec_row + (size_t)w * kRecWords + 4);
-        if (__uint_as_float((uint32_t)w4) == mh)
-            hidx = min(hidx, (int)(uint32_t)(w4 >> 32));
-    }
-    hidx = wave_min_int(hidx);
-    if (lane != 0)
-        return;
-    const double T = P.T, eta_d = P.eta_d;
-    const size_t row_off = (size_t)row * (size_t)P.V;
-    // Mhat: the augmented logit at the argmax, recomputed in fp64
-    double Mh = (double)mh * kLn2d;
-    if (hidx >= 0 && hidx < P.V) {
-        const double zx = (double)load_scalar<DT>(P.z, row_off + hidx) / T;
-        const double yx = (double)load_scalar<DT>(P.y, row_off + hidx) / T;
-        Mh = zx + eta_d * (exp(yx - Ly) - exp(zx - Lz));
-    } else {
-        hidx = -1;
-    }
-    double *rs = P.rowstat + (size_t)row * kRowStatWords;
-    rs[0] = Lz;
-    rs[1] = Ly;
-    rs[2] = Mh;
-    rs[3] = Lh;
-    rs[4] = (double)hidx;
     const int Pn = P.G + 1;
     const long long bi = row / Pn;
     const int i = (int)(row - bi * Pn);
+    const size_t row_off = (size_t)row * (size_t)P.V;
+    // the draft's logits, early (independent of the records)
+    int x = -1;
+    double zx = 0.0, yx = 0.0;
+    if (i < P.G) {
+        x = P.draft[bi * P.G + i];
+        if (lane == 0 && x >= 0 && x < P.V) {
+            zx = (double)load_scalar<DT>(P.z, row_off + x) * P.invT64;
+            yx = (double)load_scalar<DT>(P.y, row_off + x) * P.invT64;
+        }
+    }
+    const uint64_t *rec_row = P.rec + (size_t)row * P.Wmax * kRecWords;
+    const float NEG = -3.0e38f;
+    float cz = NEG, cy = NEG, ch = NEG, mh = -__builtin_inff();
+    double sz = 0.0, sy = 0.0, sh = 0.0;
+    int hidx = 0x7fffffff;
+    // first pass: references and the maximum (loads kept for the second)
+    uint64_t w0[2] = {0, 0}, w1[2] = {0, 0}, w2[2] = {0, 0}, w3[2] = {0, 0}, w4[2] = {0, 0}, w5[2] = {0, 0};
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int w = lane + 64 * k;
+        if (w < P.W) {
+            const uint64_t *r = rec_row + (size_t)w * kRecWords;
+            w0[k] = ld_relaxed(r + 0);
+            w1[k] = ld_relaxed(r + 1);
+            w2[k] = ld_relaxed(r + 2);
+            w3[k] = ld_relaxed(r + 3);
+            w4[k] = ld_relaxed(r + 4);
+            w5[k] = ld_relaxed(r + 5);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        if (lane + 64 * k < P.W) {
+            cz = fmaxf(cz, unpack_lo(w2[k]));
+            cy = fmaxf(cy, unpack_hi(w2[k]));
+            ch = fmaxf(ch, unpack_lo(w5[k]));
+            const float m = unpack_lo(w4[k]);
+            const int ix = (int)(uint32_t)(w4[k] >> 32);
+            if (m > mh || (m == mh && ix < hidx)) {
+                mh = m;
+                hidx = ix;
+            }
+        }
+    }
+    for (int w = lane + 128; w < P.W; w += 64) { // teams wider than 128 members
+        const uint64_t *r = rec_row + (size_t)w * kRecWords;
+        const uint64_t a2 = ld_relaxed(r + 2), a4 = ld_relaxed(r + 4), a5 = ld_relaxed(r + 5);
+        cz = fmaxf(cz, unpack_lo(a2));
+        cy = fmaxf(cy, unpack_hi(a2));
+        ch = fmaxf(ch, unpack_lo(a5));
+        const float m = unpack_lo(a4);
+        const int ix = (int)(uint32_t)(a4 >> 32);
+        if (m > mh || (m == mh && ix < hidx)) {
+            mh = m;
+            hidx = ix;
+        }
+    }
+    cz = wave_max(cz);
+    cy = wave_max(cy);
+    ch = wave_max(ch);
+    const float mh_all = wave_max(mh);
+    hidx = wave_min_int(mh == mh_all ? hidx : 0x7fffffff);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        if (lane + 64 * k < P.W) {
+            sz += scale_pow2(as_f64(w0[k]), unpack_lo(w2[k]) - cz);
+            sy += scale_pow2(as_f64(w1[k]), unpack_hi(w2[k]) - cy);
+            sh += scale_pow2(as_f64(w3[k]), unpack_lo(w5[k]) - ch);
+        }
+    }
+    for (int w = lane + 128; w < P.W; w += 64) {
+        const uint64_t *r = rec_row + (size_t)w * kRecWords;
+        const uint64_t a2 = ld_relaxed(r + 2), a5 = ld_relaxed(r + 5);
+        sz += scale_pow2(as_f64(ld_relaxed(r + 0)), unpack_lo(a2) - cz);
+        sy += scale_pow2(as_f64(ld_relaxed(r + 1)), unpack_hi(a2) - cy);
+        sh += scale_pow2(as_f64(ld_relaxed(r + 3)), unpack_lo(a5) - ch);
+    }
+    sz = wave_sum(sz);
+    sy = wave_sum(sy);
+    sh = wave_sum(sh);
+    if (lane != 0)
+        return;
+    const double Lz = ((double)cz + log2(sz)) * kLn2d;
+    const double Ly = ((double)cy + log2(sy)) * kLn2d;
+    const double Lh = ((double)ch + log2(sh)) * kLn2d;
+    const double eta_d = P.eta_d;
+    // Mhat: the augmented logit at the argmax, recomputed in fp64
+    double Mh = (double)mh_all * kLn2d;
+    if (hidx >= 0 && hidx < P.V) {
+        const double zm = (double)load_scalar<DT>(P.z, row_off + hidx) * P.invT64;
+        const double ym = (double)load_scalar<DT>(P.y, row_off + hidx) * P.invT64;
+        Mh = zm + eta_d * (exp(ym - Ly) - exp(zm - Lz));
+    } else {
+        hidx = -1;
+    }
+    // read by the other workgroups of this launch: device-scope stores
+    double *rs = P.rowstat + (size_t)row * kRowStatWords;
+    st_f64(rs + 0, Lz);
+    st_f64(rs + 1, Ly);
+    st_f64(rs + 2, Mh);
+    st_f64(rs + 3, Lh);
+    st_f64(rs + 4, (double)hidx);
     uint32_t acc = 0;
     if (i < P.G) {
         const long long k = bi * P.G + i;
-        const int x = P.draft[k];
         float phd = 0.f, qd = 0.f;
         if (x < 0 || x >= P.V) {
             set_dev_err(P.dev_err, 1);
         } else {
-            const double zx = (double)load_scalar<DT>(P.z, row_off + x) / T;
-            const double yx = (double)load_scalar<DT>(P.y, row_off + x) / T;
             const double p = exp(zx - Lz);
             const double q = exp(yx - Ly);
             const double h = zx + eta_d * (q - p);
@@ -384,280 +462,319 @@ __global__ __launch_bounds__(kThreads) void rapid_finalize_kernel(RapidParams P)
     }
     st_relaxed(P.row_info + (size_t)row * 2 + 1, acc);
     P.row_ctr[(size_t)row * 16] = 0u; // arrivals of the row kernel, for the next call
-    uint32_t *rq = P.req_ctr + (size_t)bi * 16;
-    const uint32_t done = publish_add(rq, 1u);
-    if (done == (uint32_t)P.G) {
-        const size_t r0 = (size_t)bi * Pn;
-        int n = P.G;
-        for (int k = 0; k < P.G; ++k)
-            if (ld_relaxed(P.row_info + (r0 + k) * 2 + 1) == 0u) {
-                n = k;
-                break;
-            }
-        P.acc_len[bi] = n;
-        st_relaxed(rq, 0u);
-    }
 }
 
-// ---------------------------------------------------------------------------
-// Emitting row, all in fp64.  With n the accept length: n < G uses the
-// residual max(p - phat, p - q, 0) of row n; otherwise p.  The row's
-// normalisers are refined in fp64 before use, so the residual's three
-// probabilities share fp64-accurate normalisers:
-//   launch 3  per chunk: sum exp(z/T - L_z), sum exp(y/T - L_y) around the
-//             row pass's values          -> L_z, L_y (fp64), Mhat at the argmax
-//   launch 4  per chunk: sum exp(h - Mhat) -> L_zhat (fp64)
-//   launch 5  per chunk: residual and target sums
-//   launch 6  the inverse-CDF crossing of u * S in vocabulary order
-// Every workgroup combines the per-chunk partials in chunk order, so all of
-// them derive the same bits.  Per-request partials [B][We][8]:
-//   0 residual sum, 1 target sum, 2 sum of exp(h - Mhat), 3 sum of
-//   exp(z/T - L_z), 4 sum of exp(y/T - L_y).
-// ---------------------------------------------------------------------------
-struct EmitRow {
-    long long row;
-    size_t row_off;
-    int n;
-    bool resid; // n < G: the residual of row n
-};
-
-__device__ __forceinline__ EmitRow emit_row(const RapidParams &P, int bi) {
-    int n = P.acc_len[bi];
-    if (n < 0 || n > P.G) // only after an abandoned row pass; keeps the row index in range
-        n = P.G;
-    EmitRow e;
-    e.n = n;
-    e.resid = n < P.G;
-    e.row = (long long)bi * (P.G + 1) + n;
-    e.row_off = (size_t)e.row * (size_t)P.V;
-    return e;
-}
-
-// Refined statistics of the emitting row (st[0] L_z, st[1] L_y, st[2] Mhat,
-// st[3] L_zhat when with_lh), computed by thread 0 and shared through LDS.
-template <int DT>
-__device__ __forceinline__ void emit_stats(const RapidParams &P, int bi, const EmitRow &er, bool with_lh,
-                                           double *sh_st) {
+// Barrier of a request's team: every wave's stores complete, one arrival
+// per workgroup, wait for `target` arrivals.  Returns false on timeout.
+__device__ __forceinline__ bool tail_sync(uint32_t *ctr, uint32_t target, uint32_t *sh_flag) {
+    wait_stores_complete();
+    __syncthreads();
     if (threadIdx.x == 0) {
-        const double *rs = P.rowstat + (size_t)er.row * kRowStatWords;
-        const double *parts = P.emit + (size_t)bi * P.We * kEmitWords;
-        double sz = 0.0, sy = 0.0, shh = 0.0;
-        for (int k = 0; k < P.We; ++k) {
-            sz += parts[kEmitWords * k + 3];
-            sy += parts[kEmitWords * k + 4];
+        publish_add_nr(ctr, 1u);
+        *sh_flag = wait_at_least(ctr, target) ? 1u : 0u;
+    }
+    __syncthreads();
+    return *sh_flag != 0u;
+}
+
+// Sums of word `word` of the request's We partials in one fixed order, the
+// same in every workgroup: lane l of wave 0 adds up the partials
+// [l*m, (l+1)*m) in index order (m = ceil(We/64)); the lane totals are then
+// added in lane order.  When w >= 0 also returns E(w) and E(w + 1), where
+// E(k) is the same fixed-order sum over the partials before chunk k, so the
+// intervals [E(k), E(k+1)) of all chunks tile [0, E(We)) exactly.
+__device__ __forceinline__ double tail_parts(const double *parts, int We, int word, double *sh_lane,
+                                             double *sh_out, int w, double *pre0, double *pre1) {
+    const int tid = threadIdx.x;
+    if (tid < 64) {
+        const int m = (We + 63) / 64;
+        const int k0 = tid * m, k1 = min(k0 + m, We);
+        double c = 0.0, e0 = 0.0, e1 = 0.0;
+        for (int k = k0; k < k1; ++k) {
+            if (k == w)
+                e0 = c;
+            c += ld_f64(parts + (size_t)k * kEmitWords + word);
+            if (k == w)
+                e1 = c;
         }
-        const double Lz = rs[0] + log(sz), Ly = rs[1] + log(sy);
-        double Mh = rs[2];
-        const int hidx = (int)rs[4];
-        if (hidx >= 0 && hidx < P.V) {
-            const double zx = (double)load_scalar<DT>(P.z, er.row_off + hidx) / P.T;
-            const double yx = (double)load_scalar<DT>(P.y, er.row_off + hidx) / P.T;
-            Mh = zx + P.eta_d * (exp(yx - Ly) - exp(zx - Lz));
-        }
-        sh_st[0] = Lz;
-        sh_st[1] = Ly;
-        sh_st[2] = Mh;
-        if (with_lh) {
-            for (int k = 0; k < P.We; ++k)
-                shh += parts[kEmitWords * k + 2];
-            sh_st[3] = Mh + log(shh);
+        sh_lane[tid] = c;
+        sh_lane[64 + tid] = e0;
+        sh_lane[128 + tid] = e1;
+        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (tid == 0) {
+            double t = 0.0, a0 = 0.0, a1 = 0.0;
+            const int lw = (w >= 0) ? w / m : -1;
+            for (int l = 0; l < 64; ++l) {
+                if (l == lw) {
+                    a0 = t + sh_lane[64 + l];
+                    a1 = t + sh_lane[128 + l];
+                }
+                t += sh_lane[l];
+            }
+            sh_out[0] = t;
+            sh_out[1] = a0;
+            sh_out[2] = a1;
         }
     }
     __syncthreads();
-}
-
-template <int DT>
-__device__ __forceinline__ double emit_h(const RapidParams &P, size_t row_off, int v, const double *st,
-                                         double &p, double &q) {
-    const double zs = (double)load_scalar<DT>(P.z, row_off + v) / P.T;
-    const double ys = (double)load_scalar<DT>(P.y, row_off + v) / P.T;
-    p = exp(zs - st[0]);
-    q = exp(ys - st[1]);
-    return zs + P.eta_d * (q - p);
-}
-
-template <int DT>
-__device__ __forceinline__ void emit_weights(const RapidParams &P, size_t row_off, int v, const double *st,
-                                             bool resid, double &r, double &p) {
-    if (!resid) {
-        p = exp((double)load_scalar<DT>(P.z, row_off + v) / P.T - st[0]);
-        r = 0.0;
-        return;
+    if (pre0) {
+        *pre0 = sh_out[1];
+        *pre1 = sh_out[2];
     }
-    double q;
-    const double h = emit_h<DT>(P, row_off, v, st, p, q);
-    const double ph = (h - st[2] < -2.302585092994046) ? p : exp(h - st[3]);
-    double x = p - ph;
-    if (p - q > x)
-        x = p - q;
-    r = x > 0.0 ? x : 0.0;
+    const double total = sh_out[0];
+    __syncthreads();
+    return total;
 }
 
-constexpr int kEmitPerThread = kEmitChunk / kThreads; // contiguous elements per thread
-
-template <int DT>
-__global__ __launch_bounds__(kThreads) void rapid_emit_norm_kernel(RapidParams P) {
+template <int DT, int EPT>
+__global__ __launch_bounds__(kThreads) void rapid_tail_kernel(RapidParams P) {
     __shared__ double lds_d[kWaves * 2];
-    const int w = (int)(blockIdx.x % (unsigned)P.We), bi = (int)(blockIdx.x / (unsigned)P.We);
-    const EmitRow er = emit_row(P, bi);
-    const double *rs = P.rowstat + (size_t)er.row * kRowStatWords;
-    const double Lz = rs[0], Ly = rs[1];
-    const int v0 = w * kEmitChunk + threadIdx.x * kEmitPerThread;
-    double s[2] = {0.0, 0.0};
-    for (int e = 0; e < kEmitPerThread; ++e) {
-        const int v = v0 + e;
-        if (v < P.V) {
-            s[0] += exp((double)load_scalar<DT>(P.z, er.row_off + v) / P.T - Lz);
-            if (er.resid)
-                s[1] += exp((double)load_scalar<DT>(P.y, er.row_off + v) / P.T - Ly);
-        }
-    }
-    block_sum<2>(s, lds_d);
-    if (threadIdx.x == 0) {
-        double *o = P.emit + ((size_t)bi * P.We + w) * kEmitWords;
-        o[3] = s[0];
-        o[4] = er.resid ? s[1] : 1.0;
-    }
-}
-
-template <int DT>
-__global__ __launch_bounds__(kThreads) void rapid_emit_lse_kernel(RapidParams P) {
-    __shared__ double lds_d[kWaves];
-    __shared__ double sh_st[4];
-    const int w = (int)(blockIdx.x % (unsigned)P.We), bi = (int)(blockIdx.x / (unsigned)P.We);
-    const EmitRow er = emit_row(P, bi);
-    if (!er.resid)
-        return; // no residual on this request
-    emit_stats<DT>(P, bi, er, false, sh_st);
-    const double st[3] = {sh_st[0], sh_st[1], sh_st[2]};
-    const int v0 = w * kEmitChunk + threadIdx.x * kEmitPerThread;
-    double s[1] = {0.0};
-    for (int e = 0; e < kEmitPerThread; ++e) {
-        const int v = v0 + e;
-        if (v < P.V) {
-            double p, q;
-            s[0] += exp(emit_h<DT>(P, er.row_off, v, st, p, q) - st[2]);
-        }
-    }
-    block_sum<1>(s, lds_d);
-    if (threadIdx.x == 0)
-        P.emit[((size_t)bi * P.We + w) * kEmitWords + 2] = s[0];
-}
-
-template <int DT>
-__global__ __launch_bounds__(kThreads) void rapid_emit_sum_kernel(RapidParams P) {
-    __shared__ double lds_d[kWaves * 2];
-    __shared__ double sh_st[4];
-    const int w = (int)(blockIdx.x % (unsigned)P.We), bi = (int)(blockIdx.x / (unsigned)P.We);
-    const EmitRow er = emit_row(P, bi);
-    emit_stats<DT>(P, bi, er, er.resid, sh_st);
-    const double st[4] = {sh_st[0], sh_st[1], sh_st[2], sh_st[3]};
-    const int v0 = w * kEmitChunk + threadIdx.x * kEmitPerThread;
-    double s[2] = {0.0, 0.0};
-    for (int e = 0; e < kEmitPerThread; ++e) {
-        const int v = v0 + e;
-        if (v < P.V) {
-            double r, p;
-            emit_weights<DT>(P, er.row_off, v, st, er.resid, r, p);
-            s[0] += r;
-            s[1] += p;
-        }
-    }
-    block_sum<2>(s, lds_d);
-    if (threadIdx.x == 0) {
-        double *o = P.emit + ((size_t)bi * P.We + w) * kEmitWords;
-        o[0] = s[0];
-        o[1] = s[1];
-    }
-}
-
-template <int DT>
-__global__ __launch_bounds__(kThreads) void rapid_emit_pick_kernel(RapidParams P) {
-    __shared__ double sh_scan[kThreads + 1];
     __shared__ int lds_i[kWaves];
+    __shared__ double sh_lane[192];
+    __shared__ double sh_out[4];
     __shared__ double sh_st[4];
-    const int w = (int)(blockIdx.x % (unsigned)P.We), bi = (int)(blockIdx.x / (unsigned)P.We);
+    __shared__ double sh_scan[kThreads];
+    __shared__ uint32_t sh_u[2];
     const int tid = threadIdx.x;
-    const EmitRow er = emit_row(P, bi);
-    const double *parts = P.emit + (size_t)bi * P.We * kEmitWords;
+    const int We = P.We;
+    const int bi = (int)(blockIdx.x / (unsigned)We), w = (int)(blockIdx.x % (unsigned)We);
+    const int Pn = P.G + 1;
+    if (blockIdx.x == 0 && tid == 0)
+        P.ctl[0] = 0u; // ticket counter of the row kernel, for the next call
+    uint32_t *bar = P.req_ctr + (size_t)bi * 16 + 4;
+    uint32_t *leave = P.req_ctr + (size_t)bi * 16 + 5;
+    double *parts = P.emit + (size_t)bi * We * kEmitWords;
+    double *mine = parts + (size_t)w * kEmitWords;
+    uint32_t nbar = 0;
+    bool ok = true;
 
-    // totals and this chunk's prefix, summed in chunk order by every thread
-    double Sr = 0.0, Sp = 0.0;
-    for (int k = 0; k < P.We; ++k) {
-        Sr += parts[kEmitWords * k];
-        Sp += parts[kEmitWords * k + 1];
-    }
-    const bool use_r = er.resid && (Sr > 0.0);
-    const int sel = use_r ? 0 : 1;
-    const double S = use_r ? Sr : Sp;
-    double pre = 0.0;
-    for (int k = 0; k < w; ++k)
-        pre += parts[kEmitWords * k + sel];
-    const double mine = parts[kEmitWords * w + sel];
-    const double u = clamp_uniform(P.u_sample[er.row], (w == 0 && tid == 0) ? P.dev_err : nullptr);
-    const double target = u * S;
-    const bool crossing_here = (pre <= target) && (target < pre + mine);
-    const bool write_dist = P.emit_dist != nullptr;
-    if (!crossing_here && !write_dist)
-        return;
+    // ---- phase 0: the request's rows ----
+    for (int r = w * kWaves + (tid >> 6); r < Pn; r += We * kWaves)
+        tail_row<DT>(P, (long long)bi * Pn + r);
+    ok = tail_sync(bar, ++nbar * (uint32_t)We, &sh_u[0]);
 
-    emit_stats<DT>(P, bi, er, use_r, sh_st);
-    const double st[4] = {sh_st[0], sh_st[1], sh_st[2], sh_st[3]};
-    const int v0 = w * kEmitChunk + tid * kEmitPerThread;
-    double wt[kEmitPerThread];
-    double tsum = 0.0;
-    for (int e = 0; e < kEmitPerThread; ++e) {
-        const int v = v0 + e;
-        double r = 0.0, p = 0.0;
-        if (v < P.V)
-            emit_weights<DT>(P, er.row_off, v, st, use_r, r, p);
-        wt[e] = use_r ? r : p;
-        tsum += wt[e];
+    // ---- accept length and the emitting row ----
+    int n = P.G;
+    if (ok) {
+        if (tid < 64) {
+            int first = P.G;
+            for (int k = tid; k < P.G; k += 64)
+                if (ld_relaxed(P.row_info + ((size_t)bi * Pn + k) * 2 + 1) == 0u) {
+                    first = k;
+                    break;
+                }
+            first = wave_min_int(first);
+            if (tid == 0)
+                sh_u[1] = (uint32_t)first;
+        }
+        __syncthreads();
+        n = (int)sh_u[1];
+        if (w == 0 && tid == 0)
+            P.acc_len[bi] = n;
     }
-    if (write_dist) {
-        const double invS = 1.0 / S;
-        for (int e = 0; e < kEmitPerThread; ++e) {
+    const long long row = (long long)bi * Pn + n;
+    const size_t row_off = (size_t)row * (size_t)P.V;
+    const bool resid = n < P.G;
+    const double *rs = P.rowstat + (size_t)row * kRowStatWords;
+    const int v0 = (w * kThreads + tid) * EPT;
+    const double invT = P.invT64, eta_d = P.eta_d;
+
+    // per element, kept across the phases: p', q', exp(h - Mhat)
+    double pc[EPT], qc[EPT], ec[EPT];
+    uint32_t prot = 0; // tail-protected elements (bit e)
+
+    // ---- phase 1: p', q' and the refined normalisers ----
+    if (ok) {
+        const double Lz = ld_f64(rs + 0), Ly = ld_f64(rs + 1);
+        double s2[2] = {0.0, 0.0};
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            pc[e] = 0.0;
+            qc[e] = 0.0;
+            ec[e] = 0.0;
             const int v = v0 + e;
-            if (v < P.V)
-                P.emit_dist[(size_t)bi * P.V + v] = (float)(wt[e] * invS);
+            if (v < P.V) {
+                pc[e] = exp((double)load_scalar<DT>(P.z, row_off + v) * invT - Lz);
+                s2[0] += pc[e];
+                if (resid) {
+                    qc[e] = exp((double)load_scalar<DT>(P.y, row_off + v) * invT - Ly);
+                    s2[1] += qc[e];
+                }
+            }
+        }
+        block_sum<2>(s2, lds_d);
+        if (tid == 0) {
+            st_f64(mine + 3, s2[0]);
+            st_f64(mine + 4, resid ? s2[1] : 1.0);
+        }
+        ok = tail_sync(bar, ++nbar * (uint32_t)We, &sh_u[0]);
+    }
+    // refined L_z, L_y (as factors on p', q') and Mhat
+    double fz = 1.0, fy = 1.0, Mh = 0.0, Lz = 0.0, Ly = 0.0;
+    if (ok) {
+        const double sz = tail_parts(parts, We, 3, sh_lane, sh_out, -1, nullptr, nullptr);
+        const double sy = tail_parts(parts, We, 4, sh_lane, sh_out, -1, nullptr, nullptr);
+        if (tid == 0) {
+            const double lz = ld_f64(rs + 0) + log(sz), ly = ld_f64(rs + 1) + log(sy);
+            double mh = ld_f64(rs + 2);
+            const int hidx = (int)ld_f64(rs + 4);
+            if (resid && hidx >= 0 && hidx < P.V) {
+                const double zx = (double)load_scalar<DT>(P.z, row_off + hidx) * invT;
+                const double yx = (double)load_scalar<DT>(P.y, row_off + hidx) * invT;
+                mh = zx + eta_d * (exp(yx - ly) - exp(zx - lz));
+            }
+            sh_st[0] = lz;
+            sh_st[1] = ly;
+            sh_st[2] = mh;
+            sh_st[3] = 1.0 / sz; // p = p' / sum p'  (exp(L_z,row - L_z) = 1/sz)
+        }
+        __syncthreads();
+        Lz = sh_st[0];
+        Ly = sh_st[1];
+        Mh = sh_st[2];
+        fz = sh_st[3];
+        fy = 1.0 / sy;
+    }
+
+    // ---- phase 2 (residual rows): e = exp(h - Mhat) -> L_zhat ----
+    double fh = 0.0; // exp(Mhat - L_zhat)
+    if (ok && resid) {
+        double s1[1] = {0.0};
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const int v = v0 + e;
+            if (v < P.V) {
+                const double p = pc[e] * fz, q = qc[e] * fy;
+                const double h = (double)load_scalar<DT>(P.z, row_off + v) * invT + eta_d * (q - p);
+                ec[e] = exp(h - Mh);
+                if (h - Mh < -2.302585092994046)
+                    prot |= 1u << e;
+                s1[0] += ec[e];
+            }
+        }
+        block_sum<1>(s1, lds_d);
+        if (tid == 0)
+            st_f64(mine + 2, s1[0]);
+        ok = tail_sync(bar, ++nbar * (uint32_t)We, &sh_u[0]);
+        if (ok)
+            fh = 1.0 / tail_parts(parts, We, 2, sh_lane, sh_out, -1, nullptr, nullptr);
+    }
+
+    // weights of element e: residual max(p - phat, p - q, 0), or p
+    auto weights = [&](int e, double &r, double &p) {
+        p = pc[e] * fz;
+        if (!resid) {
+            r = 0.0;
+            return;
+        }
+        const double q = qc[e] * fy;
+        const double ph = ((prot >> e) & 1u) ? p : ec[e] * fh;
+        double d = p - ph;
+        if (p - q > d)
+            d = p - q;
+        r = d > 0.0 ? d : 0.0;
+    };
+
+    // ---- phase 3: residual and target sums ----
+    if (ok) {
+        double s2[2] = {0.0, 0.0};
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            if (v0 + e < P.V) {
+                double r, p;
+                weights(e, r, p);
+                s2[0] += r;
+                s2[1] += p;
+            }
+        }
+        block_sum<2>(s2, lds_d);
+        if (tid == 0) {
+            st_f64(mine + 0, s2[0]);
+            st_f64(mine + 1, s2[1]);
+        }
+        ok = tail_sync(bar, ++nbar * (uint32_t)We, &sh_u[0]);
+    }
+
+    // ---- phase 4: the draw ----
+    if (ok) {
+        double pre0, pre1;
+        const double Sr = tail_parts(parts, We, 0, sh_lane, sh_out, w, &pre0, &pre1);
+        const bool use_r = resid && (Sr > 0.0);
+        double S = Sr;
+        if (!use_r)
+            S = tail_parts(parts, We, 1, sh_lane, sh_out, w, &pre0, &pre1);
+        const double u = clamp_uniform(P.u_sample[row], (w == 0 && tid == 0) ? P.dev_err : nullptr);
+        const double target = u * S;
+        const bool crossing_here = (pre0 <= target) && (target < pre1);
+        double wt[EPT];
+        double tsum = 0.0;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            double r = 0.0, p = 0.0;
+            if (v0 + e < P.V)
+                weights(e, r, p);
+            wt[e] = use_r ? r : p;
+            tsum += wt[e];
+        }
+        if (P.emit_dist) {
+            const double invS = 1.0 / S;
+#pragma unroll
+            for (int e = 0; e < EPT; ++e)
+                if (v0 + e < P.V)
+                    P.emit_dist[(size_t)bi * P.V + v0 + e] = (float)(wt[e] * invS);
+        }
+        if (crossing_here) {
+            // exclusive scan of the per-thread sums, in thread order
+            sh_scan[tid] = tsum;
+            __syncthreads();
+            if (tid == 0) {
+                double c = pre0;
+                for (int k = 0; k < kThreads; ++k) {
+                    const double xk = sh_scan[k];
+                    sh_scan[k] = c;
+                    c += xk;
+                }
+            }
+            __syncthreads();
+            int found = 0x7fffffff, last_pos = -1;
+            double c = sh_scan[tid];
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) {
+                const int v = v0 + e;
+                if (v < P.V) {
+                    c += wt[e];
+                    if (wt[e] > 0.0)
+                        last_pos = v;
+                    if (c > target && found == 0x7fffffff)
+                        found = v;
+                }
+            }
+            found = block_min_int(found, lds_i);
+            if (found == 0x7fffffff) {
+                // only reachable through rounding at the chunk's end: the last
+                // element of the chunk with positive weight
+                const int neg = block_min_int(-last_pos, lds_i);
+                found = -neg;
+            }
+            if (tid == 0 && found >= 0)
+                P.token[bi] = found;
         }
     }
-    if (!crossing_here)
-        return;
-    // exclusive scan of the per-thread sums, in thread order
-    sh_scan[tid] = tsum;
+    if (!ok && tid == 0)
+        set_dev_err(P.dev_err, 4);
+    (void)Lz;
+    (void)Ly;
+
+    // the request's last workgroup to leave returns its counters to zero
+    wait_stores_complete();
     __syncthreads();
     if (tid == 0) {
-        double c = pre;
-        for (int k = 0; k < kThreads; ++k) {
-            const double x = sh_scan[k];
-            sh_scan[k] = c;
-            c += x;
+        const uint32_t left = __hip_atomic_fetch_add(leave, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (left == (uint32_t)We - 1u) {
+            st_relaxed(bar, 0u);
+            st_relaxed(leave, 0u);
         }
-        sh_scan[kThreads] = c;
     }
-    __syncthreads();
-    int found = 0x7fffffff, last_pos = -1;
-    double c = sh_scan[tid];
-    for (int e = 0; e < kEmitPerThread; ++e) {
-        const int v = v0 + e;
-        if (v >= P.V)
-            break;
-        c += wt[e];
-        if (wt[e] > 0.0)
-            last_pos = v;
-        if (c > target && found == 0x7fffffff)
-            found = v;
-    }
-    found = block_min_int(found, lds_i);
-    if (found == 0x7fffffff) {
-        // only reachable through rounding at the chunk's end: the last
-        // element of the chunk with positive weight
-        const int neg = block_min_int(-last_pos, lds_i);
-        found = -neg;
-    }
-    if (tid == 0 && found >= 0)
-        P.token[bi] = found;
 }
 
 template <int DT, int NV>
@@ -698,25 +815,11 @@ static hipError_t launch_t(const Plan &plan, const RapidParams &p, hipStream_t s
         if (e != hipSuccess)
             return e;
     }
-    const unsigned fin = (unsigned)((p.R + kWaves - 1) / kWaves);
-    hipLaunchKernelGGL((rapid_finalize_kernel<DT>), dim3(fin), dim3(kThreads), 0, s, p);
-    e = hipGetLastError();
-    if (e != hipSuccess)
-        return e;
-    const dim3 eg((unsigned)p.We * (unsigned)p.B);
-    hipLaunchKernelGGL((rapid_emit_norm_kernel<DT>), eg, dim3(kThreads), 0, s, p);
-    e = hipGetLastError();
-    if (e != hipSuccess)
-        return e;
-    hipLaunchKernelGGL((rapid_emit_lse_kernel<DT>), eg, dim3(kThreads), 0, s, p);
-    e = hipGetLastError();
-    if (e != hipSuccess)
-        return e;
-    hipLaunchKernelGGL((rapid_emit_sum_kernel<DT>), eg, dim3(kThreads), 0, s, p);
-    e = hipGetLastError();
-    if (e != hipSuccess)
-        return e;
-    hipLaunchKernelGGL((rapid_emit_pick_kernel<DT>), eg, dim3(kThreads), 0, s, p);
+    const dim3 tg((unsigned)p.We * (unsigned)p.B);
+    if (p.ept <= 8)
+        hipLaunchKernelGGL((rapid_tail_kernel<DT, 8>), tg, dim3(kThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((rapid_tail_kernel<DT, 16>), tg, dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 

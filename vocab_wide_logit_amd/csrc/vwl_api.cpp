@@ -119,6 +119,8 @@ bool make_plan(int mode, int dt, long long R, int V, Plan &plan) {
 
 bool finite_f(float x) { return std::isfinite(x); }
 
+static_assert(VWL_RAPID_MAX_V == kRapidMaxV, "RAPID vocabulary limit out of step with the tail geometry");
+
 // Vectors per member: the widest row body (no head) split evenly over W.
 int member_chunk(int V, int dt, int W) {
     const int per_vec = 16 / elem_bytes(dt);
@@ -210,7 +212,7 @@ vwl_status vwl_rapid_check(const void *z, const void *y, const int32_t *draft,
         return VWL_ERR_NULL;
     if (G > 0 && (!draft || !u_accept || !accept))
         return VWL_ERR_NULL;
-    if (!shape_ok(B, G, V))
+    if (!shape_ok(B, G, V) || V > VWL_RAPID_MAX_V)
         return VWL_ERR_SHAPE;
     if (dt != VWL_F32 && dt != VWL_BF16)
         return VWL_ERR_DTYPE;
@@ -313,7 +315,6 @@ vwl_status asym_verify(const void *a, const void *b, const void *t, const int32_
     p.req_ctr = reinterpret_cast<uint32_t *>(ws + L.req_ctr);
     p.row_info = reinterpret_cast<uint32_t *>(ws + L.row_info);
     p.rec = reinterpret_cast<uint64_t *>(ws + L.rec);
-    p.row_stat = reinterpret_cast<double *>(ws + L.rowstat);
     return launch_asym((int)dt, plan, p, stream, g_phase_event.load()) == hipSuccess ? VWL_OK : VWL_ERR_HIP;
 }
 
@@ -353,6 +354,7 @@ vwl_status rapid_verify(const void *z, const void *y, const int32_t *draft,
     p.Wmax = L.Wmax;
     p.chunk = member_chunk(V, (int)dt, plan.W);
     p.We = L.We;
+    p.ept = L.ept;
     {
         // log2e / T split into a high part not above it and a positive low
         // part (a -inf logit times a positive low part stays -inf)
@@ -368,6 +370,7 @@ vwl_status rapid_verify(const void *z, const void *y, const int32_t *draft,
         p.eta2 = (float)((double)eta * 1.4426950408889634);
     }
     p.T = (double)T;
+    p.invT64 = 1.0 / (double)T;
     p.eta_d = (double)eta;
     p.accept = accept;
     p.acc_len = accept_len;

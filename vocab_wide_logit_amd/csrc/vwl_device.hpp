@@ -44,6 +44,22 @@ __device__ __forceinline__ float widen<DT_BF16>(const uint4 &v, int j) {
     return (j & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
 }
 
+// Record words: two floats in one 64-bit word, doubles as bit patterns.
+__device__ __forceinline__ uint64_t pack2(float lo, float hi) {
+    return (uint64_t)__float_as_uint(lo) | ((uint64_t)__float_as_uint(hi) << 32);
+}
+__device__ __forceinline__ float unpack_lo(uint64_t w) { return __uint_as_float((uint32_t)w); }
+__device__ __forceinline__ float unpack_hi(uint64_t w) { return __uint_as_float((uint32_t)(w >> 32)); }
+__device__ __forceinline__ double as_f64(uint64_t w) { return __longlong_as_double((long long)w); }
+__device__ __forceinline__ uint64_t f64_bits(double x) { return (uint64_t)__double_as_longlong(x); }
+
+// 2^k * x for an integer-valued float k <= 0.  Softmax references are kept
+// as integers, so every change of reference is this exact power-of-two
+// rescale (k below -1100 gives 0 for any finite sum).
+__device__ __forceinline__ double scale_pow2(double x, float k) {
+    return ldexp(x, (int)fmaxf(k, -1100.0f));
+}
+
 // One element of a row, widened to fp32.
 template <int DT>
 __device__ __forceinline__ float load_scalar(const void *base, size_t idx) {

@@ -15,7 +15,8 @@ constexpr int kThreads = 256; // threads per workgroup (4 wave64)
 //
 //   ctl      64 x u32   [0] ticket counter, [16] exit counter
 //   row_ctr  R x 16 u32 per row: [0] phase-1 arrivals, [1] phase-2 arrivals
-//   req_ctr  B x 16 u32 per request: rows finished
+//   req_ctr  B x 16 u32 per request: rows finished; RAPID tail [4] phase
+//            arrivals, [5] departures
 //   row_info R x 2 u32  per row: fused token, accept flag (request scan input)
 //   rec      R x Wmax x 8 u64  per (row, member) record (see the kernels)
 //   rowstat  R x 8 f64  RAPID: L_z, L_y, Mhat, L_zhat, argmax of zhat
@@ -25,11 +26,13 @@ constexpr int kThreads = 256; // threads per workgroup (4 wave64)
 struct WsLayout {
     size_t ctl, row_ctr, req_ctr, row_info, rec, rowstat, emit, total;
     int Wmax;
-    int We;
+    int We;  // RAPID: workgroups per request in the tail
+    int ept; // RAPID: emitting-row elements per thread in the tail
 };
 
 constexpr int kRecWords = 8;
-constexpr int kEmitChunk = 4096; // elements of the emitting row per emit workgroup
+constexpr int kEmitMaxChunks = 512; // tail workgroups per request (at most)
+constexpr int kRapidMaxV = kThreads * 16 * kEmitMaxChunks; // largest RAPID vocabulary
 constexpr int kRowStatWords = 8;
 constexpr int kEmitWords = 8;
 
@@ -51,7 +54,11 @@ inline WsLayout ws_layout(int B, int P, int V, int elem_bytes, bool rapid) {
     WsLayout L{};
     const size_t R = (size_t)B * (size_t)P;
     L.Wmax = max_team(V, elem_bytes, rapid ? kRapidLanes : kAsymLanes);
-    L.We = rapid ? (int)((V + kEmitChunk - 1) / kEmitChunk) : 0;
+    if (rapid) {
+        // 8 elements per tail thread, 16 past 8 * 256 * kEmitMaxChunks
+        L.ept = ((long long)V > (long long)kThreads * 8 * kEmitMaxChunks) ? 16 : 8;
+        L.We = (int)(((long long)V + kThreads * L.ept - 1) / ((long long)kThreads * L.ept));
+    }
     size_t off = 0;
     L.ctl = off;      off = align256(off + 64 * 4);
     L.row_ctr = off;  off = align256(off + R * 16 * 4);
@@ -78,8 +85,6 @@ struct AsymParams {
     int32_t *fused, *acc_len, *token, *dev_err;
     uint32_t *ctl, *row_ctr, *req_ctr, *row_info;
     uint64_t *rec;
-    double *row_stat;
-    uint32_t n_waves; // waves in the launch (exit count)
 };
 
 struct RapidParams {
@@ -88,11 +93,11 @@ struct RapidParams {
     const float *u_accept, *u_sample;
     long long R;
     int B, G, V;
-    int W, n_teams, Wmax, We;
+    int W, n_teams, Wmax, We, ept;
     int chunk;          // vectors per member (fixed per launch)
     float c_hi, c_lo; // log2e / T = c_hi + c_lo, c_hi <= log2e / T, c_lo > 0
     float eta2;       // eta * log2e
-    double T, eta_d;
+    double T, eta_d, invT64;
     uint8_t *accept;
     int32_t *acc_len, *token, *dev_err;
     float *p_hat_draft, *q_draft, *emit_dist;

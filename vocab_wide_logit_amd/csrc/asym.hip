@@ -307,7 +307,7 @@ __device__ __forceinline__ void asym_pass_ab(const AsymParams &P, long long row,
 }
 
 template <int DT, int NV>
-__global__ __launch_bounds__(kThreads, (NV <= 1 ? 4 : NV == 2 ? 3 : 2)) void asym_rows_kernel(AsymParams P) {
+__global__ __launch_bounds__(kThreads, (NV <= 1 ? 4 : NV <= 4 ? 3 : 2)) void asym_rows_kernel(AsymParams P) {
     constexpr int EPV = Elem<DT>::kPerVec;
     __shared__ AsymStage<NV> stage;
     __shared__ float lds_f[kWaves * 4];

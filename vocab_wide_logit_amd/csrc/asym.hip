@@ -198,11 +198,15 @@ __device__ __forceinline__ void prefetch_bulk(AsymStage<NV> &stage, long long r,
     const uint4 *src = base + s.vec0 + lane;
     uint4 *dst = &stage.v[x][0][0];
     if (s.nv >= NV * kThreads) { // the whole slot (uniform)
+        // uniform base per vector slot, lane offset plus an immediate per sub-block
+        const uint4 *ub = base + s.vec0;
 #pragma unroll
-        for (int j = 0; j < NV; ++j)
+        for (int j = 0; j < NV; ++j) {
+            const uint4 *jb = ub + j * kThreads;
 #pragma unroll
             for (int v = 0; v < kWaves; ++v)
-                g2lds16(src + v * 64 + j * kThreads, dst + j * kThreads + v * 64);
+                g2lds16(jb + (lane + v * 64), dst + j * kThreads + v * 64);
+        }
     } else {
 #pragma unroll
         for (int j = 0; j < NV; ++j)

@@ -150,7 +150,7 @@ __device__ __forceinline__ void split_f64(double x, float &hi, float &lo) {
 }
 
 template <int DT, int NV>
-__global__ __launch_bounds__(kThreads, (NV <= 2 ? 4 : 3)) void rapid_rows_kernel(RapidParams P) {
+__global__ __launch_bounds__(kThreads, (NV <= 4 ? 5 : 4)) void rapid_rows_kernel(RapidParams P) {
     constexpr int EPV = Elem<DT>::kPerVec;
     __shared__ float lds_f[kWaves * 2];
     __shared__ double lds_d[kWaves * 2];

@@ -2,7 +2,7 @@
 traffic counters), written as short text files, and the reader ``bench.py``
 uses to attach the measured traffic of the row kernel to its roofline figure.
 
-    python -m vocab_wide_logit_amd.profiling stats  <kernel_stats.csv> <out.txt> <command...>
+    python -m vocab_wide_logit_amd.profiling stats  <kernel_stats.csv> <kernel_trace.csv> <out.txt> <command...>
     python -m vocab_wide_logit_amd.profiling pmc    <fetch counter csv> <write counter csv> <out.txt> <command...>
 
 The traffic summary scales the row kernel's FETCH_SIZE and WRITE_SIZE (KiB per
@@ -57,7 +57,25 @@ def short_name(name: str) -> str:
     return base.strip()[:110]
 
 
-def summarize_stats(stats_csv: str, out_path: str, command: str) -> None:
+def _shape_table(trace_csv: str):
+    """Per (kernel, grid) launch shape: calls, mean, median, min and max
+    duration in microseconds, from the kernel trace.  Workloads that launch
+    the same kernel at different grids are told apart this way."""
+    groups = {}
+    for r in _rows(trace_csv):
+        key = (short_name(r["Kernel_Name"]), int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"])),
+               int(r["Workgroup_Size_X"]))
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        groups.setdefault(key, []).append(dur)
+    out = []
+    for (name, wgs, wgsize), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        ds = sorted(d)
+        out.append("%-70s %7d %5d %7d %11.2f %11.2f %11.2f %11.2f" % (
+            name[:70], wgs, wgsize, len(d), sum(d) / len(d), ds[len(ds) // 2], ds[0], ds[-1]))
+    return out
+
+
+def summarize_stats(stats_csv: str, out_path: str, command: str, trace_csv: str | None = None) -> None:
     rows = _rows(stats_csv)
     lines = ["# rocprofv3 kernel statistics", "",
              "command: " + command, "source hash (asym kernels): " + source_hash("asym"),
@@ -71,6 +89,11 @@ def summarize_stats(stats_csv: str, out_path: str, command: str) -> None:
         mx = float(_col(r, "MaxNs")) / 1e3
         tot = float(_col(r, "TotalDurationNs")) / 1e6
         lines.append("%-100s %7d %11.2f %11.2f %11.2f %12.3f" % (name, calls, avg, mn, mx, tot))
+    if trace_csv:
+        lines += ["", "per launch shape (kernel trace):", "",
+                  "%-70s %7s %5s %7s %11s %11s %11s %11s" % ("kernel", "wgs", "wgsz", "calls", "avg_us",
+                                                            "median_us", "min_us", "max_us")]
+        lines += _shape_table(trace_csv)
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -134,8 +157,8 @@ def read_traffic(path: str, mode: str = "asym"):
 
 
 def main(argv):
-    if len(argv) >= 3 and argv[0] == "stats":
-        summarize_stats(argv[1], argv[2], " ".join(argv[3:]))
+    if len(argv) >= 4 and argv[0] == "stats":
+        summarize_stats(argv[1], argv[3], " ".join(argv[4:]), trace_csv=argv[2])
     elif len(argv) >= 4 and argv[0] == "pmc":
         print(summarize_pmc(argv[1], argv[2], argv[3], " ".join(argv[4:])))
     else:

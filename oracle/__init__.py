@@ -12,7 +12,9 @@ with ctypes and marshals numpy arrays.  Each entry point follows the pages:
 * ``asym`` -- AsymSpec reading notes, section 4.1 (context gain
   ``delta = a - b`` and the delta-fusion token ``argmax(t + beta*delta)``)
   and section 4.2 (``D = JSD(softmax(a) || softmax(b))``, the CDA threshold
-  ``gamma*exp(-D)``, the acceptance test and emission at the first rejection).
+  ``gamma*exp(-D)``, the acceptance test and emission at the first rejection);
+  with the ablation variants of the same notes: ``delta = a`` or
+  ``delta = t - b`` and the fixed threshold ``gamma`` without CDA.
 * ``rapid`` -- RAPID notes, key design 2 (``zhat = z + eta*T*(q - p)``,
   ``phat = softmax(zhat/T)``), key design 3 (tail protection below 10% of the
   peak) and key design 4 (residual ``norm(max(p - phat, p - q, 0))``), with
@@ -63,7 +65,7 @@ def _load():
     P = ctypes.c_void_p
     i = ctypes.c_int
     d = ctypes.c_double
-    lib.vwl_oracle_asym.argtypes = [P, P, P, i, P, i, i, i, d, d, P, P, P, P, P, P, P, P, P, P, i]
+    lib.vwl_oracle_asym.argtypes = [P, P, P, i, P, i, i, i, d, d, i, i, P, P, P, P, P, P, P, P, P, P, i]
     lib.vwl_oracle_asym.restype = i
     lib.vwl_oracle_rapid.argtypes = [P, P, i, P, P, P, i, i, i, d, d,
                                      P, P, P, P, P, P, P, P, P, P, P, d, P, P, i]
@@ -101,11 +103,15 @@ def _stored(x: np.ndarray, dtype: str) -> tuple[np.ndarray, int]:
     raise ValueError(dtype)
 
 
+DELTA_SOURCES = {"a-b": 0, "a": 1, "t-b": 2}
+GATES = {"cda": 0, "fixed": 1}
+
+
 @dataclass
 class AsymResult:
     lse: np.ndarray        # [B, K+1, 3] log-sum-exp of a, b, t
     D: np.ndarray          # [B, K+1]
-    gamma_eff: np.ndarray  # [B, K+1]
+    gamma_eff: np.ndarray  # [B, K+1] the threshold in use (gamma under the fixed gate)
     fused: np.ndarray      # [B, K+1] int32
     gap: np.ndarray        # [B, K+1]
     top: np.ndarray        # [B, K+1] maximum fused score
@@ -116,11 +122,12 @@ class AsymResult:
 
 
 def asym(a, b, t, draft, beta: float, gamma: float, dtype: str = "f32",
-         nthreads: int = 0) -> AsymResult:
+         nthreads: int = 0, delta: str = "a-b", gate: str = "cda") -> AsymResult:
     """Oracle of the AsymSpec verify pass on [B, K+1, V] rows.
 
     ``beta`` and ``gamma`` should be the float32 values the device receives
-    (they are widened exactly)."""
+    (they are widened exactly).  ``delta`` picks the fusion source ("a-b",
+    "a", "t-b") and ``gate`` the threshold ("cda" or "fixed")."""
     lib = _load()
     sa, dt = _stored(a, dtype)
     sb, _ = _stored(b, dtype)
@@ -141,7 +148,7 @@ def asym(a, b, t, draft, beta: float, gamma: float, dtype: str = "f32",
     tok = np.zeros(B, np.int32)
     rc = lib.vwl_oracle_asym(_ptr(sa), _ptr(sb), _ptr(st), dt, _ptr(draft), B, K, V,
                              float(np.float32(beta)), float(np.float32(gamma)),
-                             _ptr(lse), _ptr(D), _ptr(ge), _ptr(fused), _ptr(gap), _ptr(top),
+                             DELTA_SOURCES[delta], GATES[gate], _ptr(lse), _ptr(D), _ptr(ge), _ptr(fused), _ptr(gap), _ptr(top),
                              _ptr(acc), _ptr(margin), _ptr(alen), _ptr(tok), int(nthreads))
     if rc != 0:
         raise RuntimeError("oracle asym failed with code %d" % rc)

@@ -18,6 +18,11 @@
  *     geff_i    = gamma * exp(-D_i)                        (4.2)
  *     accept_i  = softmax(t_i)[d_i] > geff_i * softmax(b_i)[d_i]   (4.2)
  *     the first rejection emits the delta-fusion token     (4.2)
+ *   and the variants of the same notes' mechanism ablation and
+ *   counterfactual discussion: delta_i = a_i (the raw full-context logits)
+ *   or delta_i = t_i - b_i (the two-model difference of contrastive /
+ *   speculative contrastive decoding), and the fixed threshold gamma in
+ *   place of the CDA threshold (section 4.2 contrasts the two).
  *
  *   RAPID ("RAPID: Long-Context Inference with Retrieval-Augmented
  *   Speculative Decoding" notes, key designs 2-4):
@@ -102,26 +107,31 @@ static double logsumexp(const double *x, int n)
 
 /*
  * Inputs: a, b, t stored rows [B][K+1][V] (dtype 0 = fp32, 1 = bf16 bits),
- * draft [B][K], beta, gamma (the float arguments, widened).
+ * draft [B][K], beta, gamma (the float arguments, widened),
+ * delta_src: 0 delta = a - b, 1 delta = a, 2 delta = t - b;
+ * gate: 0 the CDA threshold gamma*exp(-D), 1 the fixed threshold gamma.
  * Outputs (all required):
  *   lse[R][3]      log-sum-exp of a, b, t per row (R = B*(K+1))
  *   D[R]           Jensen-Shannon divergence of softmax(a) and softmax(b)
- *   geff[R]        gamma * exp(-D)
- *   fused[R]       lowest index maximising t + beta*(a - b)
+ *                  (reported under either gate)
+ *   geff[R]        the threshold in use: gamma * exp(-D), or gamma
+ *   fused[R]       lowest index maximising t + beta*delta
  *   gap[R]         top1 - top2 of that score (0 for an exact tie)
  *   top[R]         top1, the maximum of that score
  *   accept[B][K]   acceptance flag of draft i at row i (0 for an id outside [0,V))
- *   margin[B][K]   log p_t(d) - log p_b(d) - log gamma + D  (NaN for a bad id)
+ *   margin[B][K]   log p_t(d) - log p_b(d) - log geff  (NaN for a bad id)
  *   accept_len[B], token[B]
  */
 int vwl_oracle_asym(const void *a, const void *b, const void *t, int dtype,
                     const int32_t *draft, int B, int K, int V,
-                    double beta, double gamma,
+                    double beta, double gamma, int delta_src, int gate,
                     double *lse, double *D, double *geff, int32_t *fused, double *gap,
                     double *top, uint8_t *accept, double *margin,
                     int32_t *accept_len, int32_t *token, int nthreads)
 {
     if (B < 1 || K < 0 || V < 1 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16))
+        return 1;
+    if (delta_src < 0 || delta_src > 2 || gate < 0 || gate > 1)
         return 1;
     const int P = K + 1;
     const long R = (long)B * P;
@@ -167,14 +177,22 @@ int vwl_oracle_asym(const void *a, const void *b, const void *t, int dtype,
                 }
                 const double Dr = 0.5 * kl;
                 D[r] = Dr;
-                geff[r] = gamma * exp(-Dr);
+                /* the acceptance threshold: CDA relaxes gamma by exp(-D) */
+                geff[r] = (gate == 0) ? gamma * exp(-Dr) : gamma;
 
-                /* fused token: lowest index of the maximum of t + beta*(a - b);
+                /* fused token: lowest index of the maximum of t + beta*delta;
                  * gap = best - second best (counting multiplicity). */
                 double best = -INFINITY, second = -INFINITY;
                 int arg = 0;
                 for (int v = 0; v < V; ++v) {
-                    const double s = xt[v] + beta * (xa[v] - xb[v]);
+                    double delta;
+                    if (delta_src == 0)
+                        delta = xa[v] - xb[v];
+                    else if (delta_src == 1)
+                        delta = xa[v];
+                    else
+                        delta = xt[v] - xb[v];
+                    const double s = xt[v] + beta * delta;
                     if (s > best) {
                         second = best;
                         best = s;
@@ -199,7 +217,7 @@ int vwl_oracle_asym(const void *a, const void *b, const void *t, int dtype,
                         const double pt = exp(xt[d] - Lt);
                         const double pb = exp(xb[d] - Lb);
                         accept[bi * K + i] = (pt > geff[r] * pb) ? 1 : 0;
-                        margin[bi * K + i] = (xt[d] - Lt) - (xb[d] - Lb) - log(gamma) + Dr;
+                        margin[bi * K + i] = (xt[d] - Lt) - (xb[d] - Lb) - log(gamma) + (gate == 0 ? Dr : 0.0);
                     }
                 }
             }

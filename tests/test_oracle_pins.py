@@ -315,6 +315,106 @@ def test_bad_draft_is_rejected(oracle_lib):
     assert r.accept_len[0] == 0 and r.accept_len[1] == 1
 
 
+# ------------------------------------------------ AsymSpec ablation variants
+# The mechanism ablation of the AsymSpec notes (experiments; counterfactual
+# reasoning) swaps the fusion source for the raw full-context logits a or for
+# the two-model difference t - b, and replaces the CDA threshold by a fixed
+# gamma (the gate section 4.2 argues against).
+
+def test_delta_raw_a_follows_a_alone(oracle_lib):
+    """delta = a: with a flat verifier row the fused token is argmax a (beta
+    > 0) or argmin a (beta < 0), lowest index first; b never matters."""
+    a, b, t, d = _rows(4, 2, 257, 31)
+    flat = np.zeros_like(t)
+    r = oracle.asym(a, b, flat, d, 1.5, 0.5, "f32", delta="a")
+    np.testing.assert_array_equal(r.fused, np.argmax(a, axis=2))
+    r = oracle.asym(a, b, flat, d, -0.75, 0.5, "f32", delta="a")
+    np.testing.assert_array_equal(r.fused, np.argmin(a, axis=2))
+    r1 = oracle.asym(a, b, t, d, 1.0, 0.5, "f32", delta="a")
+    b2 = np.random.default_rng(5).normal(0, 3, size=b.shape).astype(np.float32)
+    r2 = oracle.asym(a, b2, t, d, 1.0, 0.5, "f32", delta="a")
+    np.testing.assert_array_equal(r1.fused, r2.fused)
+    np.testing.assert_array_equal(r1.top, r2.top)
+    # the default source does depend on b
+    r3 = oracle.asym(a, b, t, d, 1.0, 0.5, "f32")
+    r4 = oracle.asym(a, b2, t, d, 1.0, 0.5, "f32")
+    assert np.any(r3.fused != r4.fused)
+
+
+def test_delta_two_model_difference(oracle_lib):
+    """delta = t - b: at beta = -1 the score t - (t - b) is b, so the fused
+    token is argmax b; with b equal to t it is argmax t; a never matters."""
+    a, b, t, d = _rows(4, 2, 300, 32, dyadic=True)
+    r = oracle.asym(a, b, t, d, -1.0, 0.5, "f32", delta="t-b")
+    np.testing.assert_array_equal(r.fused, np.argmax(b, axis=2))
+    r = oracle.asym(a, t.copy(), t, d, 2.0, 0.5, "f32", delta="t-b")
+    np.testing.assert_array_equal(r.fused, np.argmax(t, axis=2))
+    r1 = oracle.asym(a, b, t, d, 1.0, 0.5, "f32", delta="t-b")
+    a2 = np.random.default_rng(6).normal(0, 3, size=a.shape).astype(np.float32)
+    r2 = oracle.asym(a2, b, t, d, 1.0, 0.5, "f32", delta="t-b")
+    np.testing.assert_array_equal(r1.fused, r2.fused)
+    np.testing.assert_array_equal(r1.gap, r2.gap)
+
+
+def test_delta_sources_coincide_where_they_must(oracle_lib):
+    """With a := t the context gain a - b is the two-model difference t - b;
+    with b := 0 it is the raw a.  Scores agree bit for bit there."""
+    a, b, t, d = _rows(3, 2, 500, 33)
+    r1 = oracle.asym(t.copy(), b, t, d, 1.3, 0.5, "f32", delta="a-b")
+    r2 = oracle.asym(a, b, t, d, 1.3, 0.5, "f32", delta="t-b")
+    np.testing.assert_array_equal(r1.fused, r2.fused)
+    np.testing.assert_array_equal(r1.top, r2.top)
+    np.testing.assert_array_equal(r1.gap, r2.gap)
+    zero = np.zeros_like(b)
+    r3 = oracle.asym(a, zero, t, d, 1.3, 0.5, "f32", delta="a-b")
+    r4 = oracle.asym(a, b, t, d, 1.3, 0.5, "f32", delta="a")
+    np.testing.assert_array_equal(r3.fused, r4.fused)
+    np.testing.assert_array_equal(r3.top, r4.top)
+
+
+def test_fixed_gate_matches_scipy(oracle_lib):
+    """The fixed gate accepts iff softmax(t)[d] > gamma * softmax(b)[d]; its
+    margin is the log-space difference against log gamma; the threshold it
+    reports is gamma itself; D is still the CDA divergence; a does not enter."""
+    a, b, t, d = _rows(6, 3, 700, 34)
+    gamma = 0.6
+    r = oracle.asym(a, b, t, d, 1.0, gamma, "f32", gate="fixed")
+    rc = oracle.asym(a, b, t, d, 1.0, gamma, "f32")
+    g32 = float(np.float32(gamma))
+    assert np.all(r.gamma_eff == g32)
+    np.testing.assert_array_equal(r.D, rc.D)
+    for bi in range(6):
+        for i in range(3):
+            dd = d[bi, i]
+            lt = log_softmax(t[bi, i].astype(np.float64))[dd]
+            lb = log_softmax(b[bi, i].astype(np.float64))[dd]
+            assert abs(r.margin[bi, i] - (lt - lb - math.log(g32))) < 1e-12
+            pt = softmax(t[bi, i].astype(np.float64))[dd]
+            pb = softmax(b[bi, i].astype(np.float64))[dd]
+            assert bool(r.accept[bi, i]) == bool(pt > g32 * pb)
+    a2 = np.random.default_rng(7).normal(0, 3, size=a.shape).astype(np.float32)
+    r2 = oracle.asym(a2, b, t, d, 1.0, gamma, "f32", gate="fixed")
+    np.testing.assert_array_equal(r2.accept, r.accept)
+    np.testing.assert_array_equal(r2.margin, r.margin)
+    assert np.any(r2.D != r.D)
+
+
+def test_fixed_gate_against_cda(oracle_lib):
+    """D >= 0 makes the CDA threshold gamma*exp(-D) no larger than gamma: every
+    draft the fixed gate accepts, CDA accepts too; they agree where D = 0; the
+    gate never moves the fused token."""
+    x = W.gen_asym(24, 3, 1024, "bf16", seed=35, identical_frac=0.3, displaced_frac=0.5)
+    x.draft = np.random.default_rng(8).integers(0, 1024, size=x.draft.shape).astype(np.int32)
+    for delta in ("a-b", "a", "t-b"):
+        rf = oracle.asym(x.a, x.b, x.t, x.draft, 1.0, 0.5, "bf16", delta=delta, gate="fixed")
+        rc = oracle.asym(x.a, x.b, x.t, x.draft, 1.0, 0.5, "bf16", delta=delta)
+        assert np.all(rc.accept >= rf.accept)
+        ident = x.identical[:, :x.K]
+        np.testing.assert_array_equal(rf.accept[ident], rc.accept[ident])
+        np.testing.assert_array_equal(rf.fused, rc.fused)
+    assert np.any(rc.accept > rf.accept)  # CDA does relax somewhere on these rows
+
+
 def test_page_defaults_in_workloads():
     """The named workloads use the pages' hyperparameters (AsymSpec notes 4.4;
     RAPID notes, hyperparameters)."""

@@ -122,6 +122,39 @@ vwl_status asym_verify(const void *a, const void *b, const void *t,
                        int32_t *accept_len, int32_t *token, int32_t *dev_err,
                        void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * AsymSpec variants: the mechanism ablation of the AsymSpec notes
+ * (experiments, and the counterfactual reasoning of its analysis) replaces
+ * the fusion source and drops the CDA gate.
+ *
+ *   delta  VWL_DELTA_A_MINUS_B  delta = a - b, the context gain (section 4.1;
+ *                               asym_verify)
+ *          VWL_DELTA_A          delta = a, the raw full-context logits
+ *          VWL_DELTA_T_MINUS_B  delta = t - b, the two-model difference of
+ *                               speculative contrastive decoding
+ *          fused_i = lowest v maximising t_v + beta*delta_v
+ *   gate   VWL_GATE_CDA    threshold gamma*exp(-D_i) (section 4.2; asym_verify)
+ *          VWL_GATE_FIXED  threshold gamma: accept_i = softmax(t_i)[d] >
+ *                          gamma*softmax(b_i)[d]; D is not computed (D[r] is
+ *                          written as NaN) and gamma_eff[r] = gamma
+ *
+ * Everything else (inputs, outputs, layouts, workspace, errors) is as for
+ * asym_verify, which equals asym_verify_variant(..., VWL_DELTA_A_MINUS_B,
+ * VWL_GATE_CDA, ...).  `a` may be null, and is never read, with
+ * VWL_GATE_FIXED and VWL_DELTA_T_MINUS_B.  An unknown enum value returns
+ * VWL_ERR_PARAM.
+ * --------------------------------------------------------------------------- */
+typedef enum { VWL_DELTA_A_MINUS_B = 0, VWL_DELTA_A = 1, VWL_DELTA_T_MINUS_B = 2 } vwl_delta_source;
+typedef enum { VWL_GATE_CDA = 0, VWL_GATE_FIXED = 1 } vwl_gate;
+
+vwl_status asym_verify_variant(const void *a, const void *b, const void *t,
+                               const int32_t *draft,
+                               int B, int K, int V, vwl_dtype dt, float beta, float gamma,
+                               vwl_delta_source delta, vwl_gate gate,
+                               float *D, float *gamma_eff, uint8_t *accept, int32_t *fused,
+                               int32_t *accept_len, int32_t *token, int32_t *dev_err,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Largest vocabulary a RAPID call accepts (2^21 logits per row). */
 #define VWL_RAPID_MAX_V 2097152
 
@@ -178,6 +211,12 @@ vwl_status rapid_verify(const void *z, const void *y, const int32_t *draft,
  * mode 0 = AsymSpec, 1 = RAPID (G in place of K).
  * --------------------------------------------------------------------------- */
 vwl_status vwl_plan_info(int mode, int B, int K, int V, vwl_dtype dt, int64_t out[6]);
+
+/* The same for one AsymSpec variant (the plan depends on the variant's
+ * register use); vwl_plan_info(0, ...) is the VWL_DELTA_A_MINUS_B,
+ * VWL_GATE_CDA plan. */
+vwl_status vwl_asym_plan_info(int B, int K, int V, vwl_dtype dt, vwl_delta_source delta, vwl_gate gate,
+                              int64_t out[6]);
 
 /* Host-only argument check of asym_verify / rapid_verify: the same checks,
  * in the same order, without launching anything.  Lets a caller (or a test

@@ -60,14 +60,21 @@ def _rel_close(dev, ref, rtol):
 
 
 def compare_asym(dev: dict, ora, K: int, rtol: float = REL_TOL, identical=None,
-                 d_floor: float = D_ABS_FLOOR) -> Report:
+                 d_floor: float = D_ABS_FLOOR, gate: str = "cda") -> Report:
     """dev: numpy arrays D, gamma_eff, accept, fused, accept_len, token;
     ora: oracle.AsymResult; identical: bool [B, K+1], rows whose two drafter
-    views are bitwise equal."""
+    views are bitwise equal.  Under the fixed gate the device reports no D
+    (NaN) and gamma_eff must be gamma exactly."""
     rep = Report()
     D_o, D_d = ora.D, np.asarray(dev["D"], np.float64)
     g_o = ora.gamma_eff
     g_d = np.asarray(dev["gamma_eff"], np.float64)
+    if gate == "fixed":
+        if not np.all(np.isnan(D_d)):
+            rep.fail("D must be NaN under the fixed gate")
+        if np.any(g_d != g_o):
+            rep.fail("gamma_eff must be gamma exactly under the fixed gate")
+        return _compare_asym_decisions(rep, dev, ora, K)
     if identical is not None:
         ident = np.asarray(identical, bool)
         if np.any(D_d[ident] != 0.0):
@@ -87,7 +94,11 @@ def compare_asym(dev: dict, ora, K: int, rtol: float = REL_TOL, identical=None,
     if np.any(badg):
         rep.fail("gamma_eff outside %g relative on %d rows" % (rtol, int(badg.sum())))
     rep.stats["D_max_rel"] = float(np.max(np.abs(D_d[nz] - D_o[nz]) / np.abs(D_o[nz]))) if np.any(nz) else 0.0
+    return _compare_asym_decisions(rep, dev, ora, K)
 
+
+def _compare_asym_decisions(rep: Report, dev: dict, ora, K: int) -> Report:
+    """Fused tokens, acceptance flags, accept lengths and emitted tokens."""
     # fused tokens
     gap = ora.gap
     top = np.maximum(np.abs(ora.top), 1.0)

@@ -185,3 +185,28 @@ def test_rapid_vocabulary_limit(lib):
                       ctypes.c_size_t(1 << 40), ctypes.c_size_t(1))
     assert lib.vwl_rapid_check(*args(vmax)) == 0
     assert lib.vwl_rapid_check(*args(vmax + 1)) == 2
+
+
+def _variant(lib, a, delta, gate, ws):
+    """asym_verify_variant with placeholder device pointers: every case here
+    returns from the host-side checks, before anything touches a device."""
+    p = lambda x: ctypes.c_void_p(x) if x else None
+    return lib.asym_verify_variant(p(a), p(A + 0x1000), p(A + 0x2000), p(A + 0x3000), 2, 2, 100, 0,
+                                   ctypes.c_float(1.0), ctypes.c_float(0.5), delta, gate,
+                                   p(A + 0x4000), p(A + 0x5000), p(A + 0x6000), p(A + 0x7000),
+                                   p(A + 0x8000), p(A + 0x9000), None, p(ws), ctypes.c_size_t(0), None)
+
+
+def test_asym_variant_argument_codes(lib):
+    """Unknown fusion source or gate: VWL_ERR_PARAM; a is required except
+    for the fixed gate with delta = t - b (which then fails only on the
+    missing workspace)."""
+    assert _variant(lib, A, 3, 0, 0) == 4
+    assert _variant(lib, A, -1, 0, 0) == 4
+    assert _variant(lib, A, 0, 2, 0) == 4
+    for delta in (0, 1, 2):
+        assert _variant(lib, 0, delta, 0, 0) == 1
+    assert _variant(lib, 0, 0, 1, 0) == 1
+    assert _variant(lib, 0, 1, 1, 0) == 1
+    assert _variant(lib, 0, 2, 1, 0) == 5
+    assert _variant(lib, A, 2, 1, 0) == 5

@@ -14,6 +14,9 @@ Entry points (same names as the C ABI):
 * ``asym_verify`` -- AsymSpec verification (AsymSpec reading notes, sections
   4.1-4.2): JSD of the two drafter views, CDA threshold gamma*exp(-D),
   acceptance test, first-rejection scan, delta-fusion token.
+* ``asym_verify_variant`` -- the same pass with the fusion source and the
+  gate of the AsymSpec notes' mechanism ablation: delta = a - b, a or t - b;
+  the CDA threshold or a fixed gamma.
 * ``rapid_verify`` -- RAPID verification (RAPID notes, key designs 2-4):
   augmented target with tail protection, rejection test against it, and the
   adjusted residual draw from caller-supplied uniforms.
@@ -40,8 +43,11 @@ MAX_K = 63
 _lib = None
 _lib_lock = threading.Lock()
 
+DELTA_SOURCES = {"a-b": 0, "a": 1, "t-b": 2}  # vwl_delta_source
+GATES = {"cda": 0, "fixed": 1}                 # vwl_gate
+
 SYMBOLS = ("vwl_status_string", "vwl_version", "vwl_workspace_reset",
-           "vwl_asym_workspace_bytes", "asym_verify",
+           "vwl_asym_workspace_bytes", "asym_verify", "asym_verify_variant", "vwl_asym_plan_info",
            "vwl_rapid_workspace_bytes", "rapid_verify",
            "vwl_plan_info", "vwl_asym_check", "vwl_rapid_check",
            "vwl_set_plan_override", "vwl_set_phase_event")
@@ -78,6 +84,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.vwl_rapid_workspace_bytes.restype = sz
         lib.asym_verify.argtypes = [P, P, P, P, i, i, i, i, f, f, P, P, P, P, P, P, P, P, sz, P]
         lib.asym_verify.restype = i
+        lib.asym_verify_variant.argtypes = [P, P, P, P, i, i, i, i, f, f, i, i, P, P, P, P, P, P, P, P, sz, P]
+        lib.asym_verify_variant.restype = i
+        lib.vwl_asym_plan_info.argtypes = [i, i, i, i, i, i, ctypes.POINTER(ctypes.c_int64)]
+        lib.vwl_asym_plan_info.restype = i
         lib.rapid_verify.argtypes = [P, P, P, P, P, i, i, i, i, f, f, P, P, P, P, P, P, P, P, sz, P]
         lib.rapid_verify.restype = i
         lib.vwl_plan_info.argtypes = [i, i, i, i, i, ctypes.POINTER(ctypes.c_int64)]
@@ -160,6 +170,16 @@ def plan_info(mode: str, B: int, K: int, V: int, dtype: torch.dtype) -> dict:
             "threads": out[4], "rows": out[5]}
 
 
+def asym_plan_info(B: int, K: int, V: int, dtype: torch.dtype, delta: str = "a-b", gate: str = "cda") -> dict:
+    """Launch plan of one AsymSpec variant on the current device."""
+    lib = load_library()
+    out = (ctypes.c_int64 * 6)()
+    dt = VWL_BF16 if dtype == torch.bfloat16 else VWL_F32
+    _check(lib.vwl_asym_plan_info(B, K, V, dt, DELTA_SOURCES[delta], GATES[gate], out))
+    return {"team": out[0], "vec_per_thread": out[1], "teams": out[2], "grid": out[3],
+            "threads": out[4], "rows": out[5]}
+
+
 def set_plan_override(mode: str, vec_per_thread: int = 0, max_teams: int = 0) -> None:
     """Tuning hook: pin vectors per thread / cap teams (0 = automatic)."""
     _check(load_library().vwl_set_plan_override(0 if mode == "asym" else 1, vec_per_thread, max_teams))
@@ -227,6 +247,45 @@ def asym_verify(a: torch.Tensor, b: torch.Tensor, t: torch.Tensor, draft: torch.
                            _ptr(out.D), _ptr(out.gamma_eff), _ptr(out.accept) if K > 0 else None,
                            _ptr(out.fused), _ptr(out.accept_len), _ptr(out.token), _ptr(out.dev_err),
                            _ptr(ws), ws.numel(), ctypes.c_void_p(stream.cuda_stream))
+    _check(code)
+    return out
+
+
+def asym_verify_variant(a: Optional[torch.Tensor], b: torch.Tensor, t: torch.Tensor, draft: torch.Tensor,
+                        beta: float, gamma: float, delta: str = "a-b", gate: str = "cda", *,
+                        out: Optional[AsymOut] = None, workspace: Optional[torch.Tensor] = None) -> AsymOut:
+    """AsymSpec verification with fusion source ``delta`` ("a-b", "a", "t-b")
+    and threshold ``gate`` ("cda": gamma*exp(-D); "fixed": gamma, D not
+    computed and returned as NaN).  ``a`` may be None only for
+    delta="t-b" with gate="fixed", the one variant that never reads it."""
+    lib = load_library()
+    if delta not in DELTA_SOURCES or gate not in GATES:
+        raise ValueError("delta must be one of %s and gate one of %s" % (list(DELTA_SOURCES), list(GATES)))
+    _dev_tensor(t, "t")
+    dt = _dt(t)
+    _dev_tensor(b, "b", t.dtype)
+    if a is not None:
+        _dev_tensor(a, "a", t.dtype)
+        if a.shape != t.shape:
+            raise ValueError("a, b, t must share one [B, K+1, V] shape")
+    elif not (delta == "t-b" and gate == "fixed"):
+        raise ValueError("a is required unless delta='t-b' and gate='fixed'")
+    if t.dim() != 3 or b.shape != t.shape:
+        raise ValueError("a, b, t must share one [B, K+1, V] shape")
+    B, P, V = t.shape
+    K = P - 1
+    _dev_tensor(draft, "draft", torch.int32)
+    if tuple(draft.shape) != (B, K):
+        raise ValueError("draft must be [B, K]")
+    if out is None:
+        out = asym_out(B, K, t.device)
+    stream = torch.cuda.current_stream(t.device)
+    ws = workspace if workspace is not None else _workspace(0, B, K, V, dt, t.device, stream)
+    code = lib.asym_verify_variant(_ptr(a), _ptr(b), _ptr(t), _ptr(draft) if K > 0 else None,
+                                   B, K, V, dt, float(beta), float(gamma), DELTA_SOURCES[delta], GATES[gate],
+                                   _ptr(out.D), _ptr(out.gamma_eff), _ptr(out.accept) if K > 0 else None,
+                                   _ptr(out.fused), _ptr(out.accept_len), _ptr(out.token), _ptr(out.dev_err),
+                                   _ptr(ws), ws.numel(), ctypes.c_void_p(stream.cuda_stream))
     _check(code)
     return out
 

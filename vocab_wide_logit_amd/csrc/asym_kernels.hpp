@@ -1,5 +1,13 @@
 // AsymSpec verification pass (AsymSpec reading notes, section 4.1
-// "contrastive delta-fusion" and section 4.2 "CDA gate").
+// "contrastive delta-fusion" and section 4.2 "CDA gate"), with the variants
+// of the notes' mechanism ablation as template choices:
+//   DS    fusion source delta: a - b (the context gain), a (raw full-context
+//         logits) or t - b (two-model difference, as in speculative
+//         contrastive decoding)
+//   GATE  the CDA threshold gamma*exp(-D), or the fixed threshold gamma
+//         (no divergence: the JSD pass and the team wait are skipped, and a
+//         is not read at all when delta = t - b)
+// Each translation unit asym_<delta>.hip instantiates one fusion source.
 //
 // Launch 1, asym_rows_kernel: each logit row (one draft position of one
 // request: a_i, b_i, t_i) is split over a team of W workgroups; each
@@ -23,6 +31,8 @@
 // Launch 2, asym_finalize_kernel: one wave per row combines the W records
 // (D, gamma*exp(-D), fused token, acceptance test of the draft); the wave
 // that completes a request runs the first-rejection scan.
+#pragma once
+
 #include "vwl_device.hpp"
 #include "vwl_internal.hpp"
 
@@ -35,10 +45,23 @@ namespace vwl {
 //   5     lowest index of the fused maximum (low 32 bits)
 //   6     JSD partial sum_v Mx_v * g_v over the chunk (double bits)
 
-// The delta-fusion score t + beta*(a - b), evaluated the same way everywhere.
+// The delta-fusion score t + beta*delta, evaluated the same way everywhere.
+template <int DS>
 __device__ __forceinline__ float fused_score(float a, float b, float t, float beta) {
-    return __fmaf_rn(beta, __fsub_rn(a, b), t);
+    if constexpr (DS == kDeltaAMinusB)
+        return __fmaf_rn(beta, __fsub_rn(a, b), t);
+    else if constexpr (DS == kDeltaA)
+        return __fmaf_rn(beta, a, t);
+    else
+        return __fmaf_rn(beta, __fsub_rn(t, b), t);
 }
+
+// Whether a variant reads a at all, and whether it needs a's log-sum-exp.
+template <int DS, int GATE>
+struct AsymUse {
+    static constexpr bool kLseA = GATE == kGateCda;
+    static constexpr bool kReadA = kLseA || DS != kDeltaTMinusB;
+};
 
 // JSD term of one element.  With x = ln p - ln q (nats), d = |x| log2e,
 // rho = 2^-d (ratio of the smaller to the larger probability) and
@@ -183,13 +206,16 @@ __device__ __forceinline__ void g2lds16(const uint4 *src, uint4 *lds_wave_base) 
                                      16, 0, 0);
 }
 
-// Stream row r's chunk into LDS (waves 1-3: wave x+1 issues all of tensor x).
-template <int DT, int NV>
+// Stream row r's chunk into LDS (waves 1-3: wave x+1 issues all of tensor x;
+// wave 1 idles when a is not read).
+template <int DT, int NV, bool READ_A>
 __device__ __forceinline__ void prefetch_bulk(AsymStage<NV> &stage, long long r, int V, int W, int member, int chunk,
                                               const uint4 *A4, const uint4 *B4, const uint4 *T4) {
     const int lane = threadIdx.x & 63;
     const RowSplit<DT> s = row_split<DT>(r, V, W, member, chunk);
     const int x = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) - 1;
+    if (!READ_A && x == 0)
+        return;
     const uint4 *base = T4;
     if (x == 0)
         base = A4;
@@ -219,13 +245,14 @@ __device__ __forceinline__ void prefetch_bulk(AsymStage<NV> &stage, long long r,
 }
 
 // Head/tail scalars of row r (wave 0's first lanes), widened to fp32.
-template <int DT>
+template <int DT, bool READ_A>
 __device__ __forceinline__ void prefetch_scalars(long long r, int V, int W, int member, int chunk, const void *a,
                                                  const void *b, const void *t, float &na, float &nb, float &nt) {
     const RowSplit<DT> s = row_split<DT>(r, V, W, member, chunk);
     if ((int)threadIdx.x < s.nsc) {
         const size_t off = (size_t)r * (size_t)V + scalar_index<DT>(s, threadIdx.x);
-        na = load_scalar<DT>(a, off);
+        if (READ_A)
+            na = load_scalar<DT>(a, off);
         nb = load_scalar<DT>(b, off);
         nt = load_scalar<DT>(t, off);
     }
@@ -234,7 +261,7 @@ __device__ __forceinline__ void prefetch_scalars(long long r, int V, int W, int 
 // Passes A+B over one row's chunk held in registers (raw a, b, t plus the
 // head/tail scalar): online softmax statistics, the fused maximum and its
 // lowest index, reduced over the workgroup; thread 0 publishes the record.
-template <int DT, int NV>
+template <int DT, int NV, int DS, int GATE>
 __device__ __forceinline__ void asym_pass_ab(const AsymParams &P, long long row, int member, const RowSplit<DT> &sp,
                                              const uint4 (&ra)[NV], const uint4 (&rb)[NV], const uint4 (&rt)[NV],
                                              float sa, float sb, float st, float *lds_f, double *lds_d, int *lds_i) {
@@ -253,22 +280,24 @@ __device__ __forceinline__ void asym_pass_ab(const AsymParams &P, long long row,
             float xa[EPV], xb[EPV], xt[EPV];
 #pragma unroll
             for (int e = 0; e < EPV; ++e) {
-                xa[e] = widen<DT>(ra[j], e);
+                xa[e] = AsymUse<DS, GATE>::kReadA ? widen<DT>(ra[j], e) : 0.0f;
                 xb[e] = widen<DT>(rb[j], e);
                 xt[e] = widen<DT>(rt[j], e);
-                fmax_t = fmaxf(fmax_t, fused_score(xa[e], xb[e], xt[e], P.beta));
+                fmax_t = fmaxf(fmax_t, fused_score<DS>(xa[e], xb[e], xt[e], P.beta));
             }
-            online_group<EPV>(la, xa);
+            if (AsymUse<DS, GATE>::kLseA)
+                online_group<EPV>(la, xa);
             online_group<EPV>(lb, xb);
             online_group<EPV>(lt, xt);
         }
     }
     float fs = NEG_INF;
     if (has_sc) {
-        fs = fused_score(sa, sb, st, P.beta);
+        fs = fused_score<DS>(sa, sb, st, P.beta);
         fmax_t = fmaxf(fmax_t, fs);
         const float x1a[1] = {sa}, x1b[1] = {sb}, x1t[1] = {st};
-        online_group<1>(la, x1a);
+        if (AsymUse<DS, GATE>::kLseA)
+            online_group<1>(la, x1a);
         online_group<1>(lb, x1b);
         online_group<1>(lt, x1t);
     }
@@ -287,8 +316,8 @@ __device__ __forceinline__ void asym_pass_ab(const AsymParams &P, long long row,
             if (!found && tid + j * kThreads < sp.nv) {
 #pragma unroll
                 for (int e = 0; e < EPV; ++e) {
-                    if (!found && fused_score(widen<DT>(ra[j], e), widen<DT>(rb[j], e), widen<DT>(rt[j], e),
-                                              P.beta) == Fm) {
+                    const float ea = AsymUse<DS, GATE>::kReadA ? widen<DT>(ra[j], e) : 0.0f;
+                    if (!found && fused_score<DS>(ea, widen<DT>(rb[j], e), widen<DT>(rt[j], e), P.beta) == Fm) {
                         fi = min(fi, sp.first_elem + (tid + j * kThreads) * EPV + e);
                         found = true;
                     }
@@ -310,9 +339,20 @@ __device__ __forceinline__ void asym_pass_ab(const AsymParams &P, long long row,
     }
 }
 
-template <int DT, int NV>
-__global__ __launch_bounds__(kThreads, (NV <= 1 ? 4 : NV <= 4 ? 3 : 2)) void asym_rows_kernel(AsymParams P) {
+// Resident waves per SIMD the row kernel is built for: the CDA variants keep
+// a pending row's a and b in registers across the team wait.
+template <int NV, int GATE>
+constexpr int asym_rows_waves() {
+    if constexpr (GATE == kGateCda)
+        return NV <= 1 ? 4 : NV <= 4 ? 3 : 2;
+    else
+        return NV <= 4 ? 4 : 3;
+}
+
+template <int DT, int NV, int DS, int GATE>
+__global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, GATE>())) void asym_rows_kernel(AsymParams P) {
     constexpr int EPV = Elem<DT>::kPerVec;
+    constexpr bool READ_A = AsymUse<DS, GATE>::kReadA;
     __shared__ AsymStage<NV> stage;
     __shared__ float lds_f[kWaves * 4];
     __shared__ double lds_d[kWaves * 3];
@@ -341,9 +381,9 @@ __global__ __launch_bounds__(kThreads, (NV <= 1 ? 4 : NV <= 4 ? 3 : 2)) void asy
     // pending row waits for its team while the next row's passes A+B run.
     auto issue = [&](long long r) {
         if (!wave0)
-            prefetch_bulk<DT, NV>(stage, r, V, W, member, P.chunk, A4, B4, T4);
+            prefetch_bulk<DT, NV, READ_A>(stage, r, V, W, member, P.chunk, A4, B4, T4);
         else
-            prefetch_scalars<DT>(r, V, W, member, P.chunk, P.a, P.b, P.t, na, nb, nt);
+            prefetch_scalars<DT, READ_A>(r, V, W, member, P.chunk, P.a, P.b, P.t, na, nb, nt);
     };
     uint4 ra[NV], rb[NV], rt[NV];
     float sa, sb, st;
@@ -352,7 +392,8 @@ __global__ __launch_bounds__(kThreads, (NV <= 1 ? 4 : NV <= 4 ? 3 : 2)) void asy
         __syncthreads(); // every wave's pieces have landed
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
-            ra[j] = stage.v[0][j][tid];
+            if (READ_A)
+                ra[j] = stage.v[0][j][tid];
             rb[j] = stage.v[1][j][tid];
             rt[j] = stage.v[2][j][tid];
         }
@@ -368,7 +409,18 @@ __global__ __launch_bounds__(kThreads, (NV <= 1 ? 4 : NV <= 4 ? 3 : 2)) void asy
     if (row + P.n_teams < P.R)
         issue(row + P.n_teams);
     RowSplit<DT> sp = row_split<DT>(row, V, W, member, P.chunk);
-    asym_pass_ab<DT, NV>(P, row, member, sp, ra, rb, rt, sa, sb, st, lds_f, lds_d, lds_i);
+    asym_pass_ab<DT, NV, DS, GATE>(P, row, member, sp, ra, rb, rt, sa, sb, st, lds_f, lds_d, lds_i);
+    if constexpr (GATE == kGateFixed) {
+        // no divergence: each row is one pass, with the next row streaming in
+        for (long long next = row + P.n_teams; next < P.R; next += P.n_teams) {
+            take();
+            if (next + P.n_teams < P.R)
+                issue(next + P.n_teams);
+            sp = row_split<DT>(next, V, W, member, P.chunk);
+            asym_pass_ab<DT, NV, DS, GATE>(P, next, member, sp, ra, rb, rt, sa, sb, st, lds_f, lds_d, lds_i);
+        }
+        return;
+    }
     for (;;) {
         // the pending row's a, b (raw) and head/tail scalars
         uint4 pa[NV], pb[NV];
@@ -387,7 +439,7 @@ __global__ __launch_bounds__(kThreads, (NV <= 1 ? 4 : NV <= 4 ? 3 : 2)) void asy
             if (next + P.n_teams < P.R)
                 issue(next + P.n_teams);
             sp = row_split<DT>(next, V, W, member, P.chunk);
-            asym_pass_ab<DT, NV>(P, next, member, sp, ra, rb, rt, sa, sb, st, lds_f, lds_d, lds_i);
+            asym_pass_ab<DT, NV, DS, GATE>(P, next, member, sp, ra, rb, rt, sa, sb, st, lds_f, lds_d, lds_i);
         }
 
         // ---- the pending row: wait for its team, then pass C ----
@@ -441,8 +493,9 @@ __global__ __launch_bounds__(kThreads, (NV <= 1 ? 4 : NV <= 4 ? 3 : 2)) void asy
 }
 
 // One wave per row: combine the W records, write the row outputs, and let
-// the wave that completes a request run its first-rejection scan.
-template <int DT>
+// the wave that completes a request run its first-rejection scan.  Under the
+// fixed gate D is not computed (NaN is written) and the threshold is gamma.
+template <int DT, int GATE>
 __global__ __launch_bounds__(kThreads) void asym_finalize_kernel(AsymParams P) {
     const int lane = threadIdx.x & 63;
     const long long row = (long long)blockIdx.x * kWaves + (threadIdx.x >> 6);
@@ -462,7 +515,8 @@ __global__ __launch_bounds__(kThreads) void asym_finalize_kernel(AsymParams P) {
     int fidx = 0x7fffffff;
     for (int w = lane; w < P.W; w += 64) {
         const uint64_t *r = rec_row + (size_t)w * kRecWords;
-        jsum += as_f64(ld_relaxed(r + 6));
+        if (GATE == kGateCda)
+            jsum += as_f64(ld_relaxed(r + 6));
         if (unpack_hi(ld_relaxed(r + 4)) == fbest)
             fidx = min(fidx, (int)(uint32_t)ld_relaxed(r + 5));
     }
@@ -470,10 +524,14 @@ __global__ __launch_bounds__(kThreads) void asym_finalize_kernel(AsymParams P) {
     fidx = wave_min_int(fidx);
     if (lane != 0)
         return;
-    const double Dr = -0.5 * kLn2d * jsum;
-    const double ge = (double)P.gamma * exp(-Dr);
-    P.D[row] = (float)Dr;
-    P.geff[row] = (float)ge;
+    const double Dr = GATE == kGateCda ? -0.5 * kLn2d * jsum : 0.0; // enters the test only under CDA
+    if (GATE == kGateCda) {
+        P.D[row] = (float)Dr;
+        P.geff[row] = (float)((double)P.gamma * exp(-Dr));
+    } else {
+        P.D[row] = __builtin_nanf("");
+        P.geff[row] = P.gamma;
+    }
     P.fused[row] = fidx;
     const int Pn = P.K + 1;
     const long long bi = row / Pn;
@@ -512,36 +570,37 @@ __global__ __launch_bounds__(kThreads) void asym_finalize_kernel(AsymParams P) {
     }
 }
 
-template <int DT, int NV>
-static int blocks_per_cu() {
+template <int DT, int NV, int DS, int GATE>
+static int blocks_per_cu_t() {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, asym_rows_kernel<DT, NV>, kThreads, 0) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, asym_rows_kernel<DT, NV, DS, GATE>, kThreads, 0) !=
+        hipSuccess)
         return 0;
     return n;
 }
 
-int asym_blocks_per_cu(int dt, int nv) {
-    if (dt == DT_BF16) {
-        switch (nv) {
-        case 1: return blocks_per_cu<DT_BF16, 1>();
-        case 2: return blocks_per_cu<DT_BF16, 2>();
-        case 4: return blocks_per_cu<DT_BF16, 4>();
-        case 8: return blocks_per_cu<DT_BF16, 8>();
-        }
-    } else {
-        switch (nv) {
-        case 1: return blocks_per_cu<DT_F32, 1>();
-        case 2: return blocks_per_cu<DT_F32, 2>();
-        case 4: return blocks_per_cu<DT_F32, 4>();
-        case 8: return blocks_per_cu<DT_F32, 8>();
-        }
+template <int DT, int DS, int GATE>
+static int blocks_per_cu_nv(int nv) {
+    switch (nv) {
+    case 1: return blocks_per_cu_t<DT, 1, DS, GATE>();
+    case 2: return blocks_per_cu_t<DT, 2, DS, GATE>();
+    case 4: return blocks_per_cu_t<DT, 4, DS, GATE>();
+    case 8: return blocks_per_cu_t<DT, 8, DS, GATE>();
     }
     return 0;
 }
 
-template <int DT, int NV>
+template <int DS>
+int asym_blocks_per_cu_ds(int dt, int nv, int gate) {
+    if (dt == DT_BF16)
+        return gate == kGateCda ? blocks_per_cu_nv<DT_BF16, DS, kGateCda>(nv)
+                                : blocks_per_cu_nv<DT_BF16, DS, kGateFixed>(nv);
+    return gate == kGateCda ? blocks_per_cu_nv<DT_F32, DS, kGateCda>(nv) : blocks_per_cu_nv<DT_F32, DS, kGateFixed>(nv);
+}
+
+template <int DT, int NV, int DS, int GATE>
 static hipError_t launch_t(const Plan &plan, const AsymParams &p, hipStream_t s, hipEvent_t after_rows) {
-    hipLaunchKernelGGL((asym_rows_kernel<DT, NV>), dim3(plan.grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((asym_rows_kernel<DT, NV, DS, GATE>), dim3(plan.grid), dim3(kThreads), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
@@ -551,27 +610,29 @@ static hipError_t launch_t(const Plan &plan, const AsymParams &p, hipStream_t s,
             return e;
     }
     const unsigned fin = (unsigned)((p.R + kWaves - 1) / kWaves);
-    hipLaunchKernelGGL((asym_finalize_kernel<DT>), dim3(fin), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((asym_finalize_kernel<DT, GATE>), dim3(fin), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 
-hipError_t launch_asym(int dt, const Plan &plan, const AsymParams &p, hipStream_t s, hipEvent_t after_rows) {
-    if (dt == DT_BF16) {
-        switch (plan.nv) {
-        case 1: return launch_t<DT_BF16, 1>(plan, p, s, after_rows);
-        case 2: return launch_t<DT_BF16, 2>(plan, p, s, after_rows);
-        case 4: return launch_t<DT_BF16, 4>(plan, p, s, after_rows);
-        case 8: return launch_t<DT_BF16, 8>(plan, p, s, after_rows);
-        }
-    } else {
-        switch (plan.nv) {
-        case 1: return launch_t<DT_F32, 1>(plan, p, s, after_rows);
-        case 2: return launch_t<DT_F32, 2>(plan, p, s, after_rows);
-        case 4: return launch_t<DT_F32, 4>(plan, p, s, after_rows);
-        case 8: return launch_t<DT_F32, 8>(plan, p, s, after_rows);
-        }
+template <int DT, int DS, int GATE>
+static hipError_t launch_nv(const Plan &plan, const AsymParams &p, hipStream_t s, hipEvent_t after_rows) {
+    switch (plan.nv) {
+    case 1: return launch_t<DT, 1, DS, GATE>(plan, p, s, after_rows);
+    case 2: return launch_t<DT, 2, DS, GATE>(plan, p, s, after_rows);
+    case 4: return launch_t<DT, 4, DS, GATE>(plan, p, s, after_rows);
+    case 8: return launch_t<DT, 8, DS, GATE>(plan, p, s, after_rows);
     }
     return hipErrorInvalidValue;
+}
+
+template <int DS>
+hipError_t launch_asym_ds(int dt, int gate, const Plan &plan, const AsymParams &p, hipStream_t s,
+                          hipEvent_t after_rows) {
+    if (dt == DT_BF16)
+        return gate == kGateCda ? launch_nv<DT_BF16, DS, kGateCda>(plan, p, s, after_rows)
+                                : launch_nv<DT_BF16, DS, kGateFixed>(plan, p, s, after_rows);
+    return gate == kGateCda ? launch_nv<DT_F32, DS, kGateCda>(plan, p, s, after_rows)
+                            : launch_nv<DT_F32, DS, kGateFixed>(plan, p, s, after_rows);
 }
 
 } // namespace vwl

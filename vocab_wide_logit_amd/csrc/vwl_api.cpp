@@ -14,6 +14,29 @@
 
 using namespace vwl;
 
+namespace vwl {
+
+hipError_t launch_asym(int dt, int ds, int gate, const Plan &plan, const AsymParams &p, hipStream_t s,
+                              hipEvent_t after_rows) {
+    switch (ds) {
+    case kDeltaAMinusB: return launch_asym_ds<kDeltaAMinusB>(dt, gate, plan, p, s, after_rows);
+    case kDeltaA: return launch_asym_ds<kDeltaA>(dt, gate, plan, p, s, after_rows);
+    case kDeltaTMinusB: return launch_asym_ds<kDeltaTMinusB>(dt, gate, plan, p, s, after_rows);
+    }
+    return hipErrorInvalidValue;
+}
+
+int asym_blocks_per_cu(int dt, int nv, int ds, int gate) {
+    switch (ds) {
+    case kDeltaAMinusB: return asym_blocks_per_cu_ds<kDeltaAMinusB>(dt, nv, gate);
+    case kDeltaA: return asym_blocks_per_cu_ds<kDeltaA>(dt, nv, gate);
+    case kDeltaTMinusB: return asym_blocks_per_cu_ds<kDeltaTMinusB>(dt, nv, gate);
+    }
+    return 0;
+}
+
+} // namespace vwl
+
 namespace {
 
 constexpr int kNvChoices[4] = {1, 2, 4, 8};
@@ -27,7 +50,7 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 struct DeviceInfo {
     bool ready = false;
     int cus = 0;
-    int asym_bpc[2][4] = {};
+    int asym_bpc[2][4][3][2] = {}; // [dtype][nv][delta source][gate]
     int rapid_bpc[2][4] = {};
 };
 constexpr int kMaxDevices = 64;
@@ -52,7 +75,9 @@ const DeviceInfo *device_info() {
         d.cus = cus;
         for (int dt = 0; dt < 2; ++dt)
             for (int k = 0; k < 4; ++k) {
-                d.asym_bpc[dt][k] = asym_blocks_per_cu(dt, kNvChoices[k]);
+                for (int ds = 0; ds < 3; ++ds)
+                    for (int g = 0; g < 2; ++g)
+                        d.asym_bpc[dt][k][ds][g] = asym_blocks_per_cu(dt, kNvChoices[k], ds, g);
                 d.rapid_bpc[dt][k] = rapid_blocks_per_cu(dt, kNvChoices[k]);
             }
         d.ready = true;
@@ -77,7 +102,7 @@ int team_size(int V, int dt, int nv, int lanes) {
 // chunk (fewer members per row).  Teams are then evened out over rounds.
 // Every member of the grid is resident at once, so no team waits on a
 // member that cannot start.
-bool make_plan(int mode, int dt, long long R, int V, Plan &plan) {
+bool make_plan(int mode, int dt, long long R, int V, Plan &plan, int ds = 0, int gate = 0) {
     const DeviceInfo *d = device_info();
     if (!d)
         return false;
@@ -87,7 +112,7 @@ bool make_plan(int mode, int dt, long long R, int V, Plan &plan) {
         const int nv = kNvChoices[k];
         if (g_force_nv[mode] && nv != g_force_nv[mode])
             continue;
-        const int bpc = mode == 0 ? d->asym_bpc[dt][k] : d->rapid_bpc[dt][k];
+        const int bpc = mode == 0 ? d->asym_bpc[dt][k][ds][gate] : d->rapid_bpc[dt][k];
         if (bpc <= 0)
             continue;
         const int lanes = mode == 0 ? kAsymLanes : kRapidLanes;
@@ -178,12 +203,14 @@ size_t vwl_rapid_workspace_bytes(int B, int G, int V, vwl_dtype dt) {
     return ws_layout(B, G + 1, V, elem_bytes(dt), true).total;
 }
 
-vwl_status vwl_asym_check(const void *a, const void *b, const void *t, const int32_t *draft,
-                          int B, int K, int V, int dt, float beta, float gamma,
-                          const void *D, const void *gamma_eff, const void *accept,
-                          const void *fused, const void *accept_len, const void *token,
-                          const void *workspace, size_t workspace_bytes, size_t needed_bytes) {
-    if (!a || !b || !t || !D || !gamma_eff || !fused || !accept_len || !token)
+// The checks of an AsymSpec call; `need_a` is false only for the variant
+// that never reads a (fixed gate, delta = t - b).
+static vwl_status asym_check_impl(bool need_a, const void *a, const void *b, const void *t, const int32_t *draft,
+                                  int B, int K, int V, int dt, float beta, float gamma,
+                                  const void *D, const void *gamma_eff, const void *accept,
+                                  const void *fused, const void *accept_len, const void *token,
+                                  const void *workspace, size_t workspace_bytes, size_t needed_bytes) {
+    if ((need_a && !a) || !b || !t || !D || !gamma_eff || !fused || !accept_len || !token)
         return VWL_ERR_NULL;
     if (K > 0 && (!draft || !accept))
         return VWL_ERR_NULL;
@@ -201,6 +228,15 @@ vwl_status vwl_asym_check(const void *a, const void *b, const void *t, const int
     if (!aligned(workspace, 256))
         return VWL_ERR_ALIGN;
     return VWL_OK;
+}
+
+vwl_status vwl_asym_check(const void *a, const void *b, const void *t, const int32_t *draft,
+                          int B, int K, int V, int dt, float beta, float gamma,
+                          const void *D, const void *gamma_eff, const void *accept,
+                          const void *fused, const void *accept_len, const void *token,
+                          const void *workspace, size_t workspace_bytes, size_t needed_bytes) {
+    return asym_check_impl(true, a, b, t, draft, B, K, V, dt, beta, gamma, D, gamma_eff, accept, fused, accept_len,
+                           token, workspace, workspace_bytes, needed_bytes);
 }
 
 vwl_status vwl_rapid_check(const void *z, const void *y, const int32_t *draft,
@@ -250,6 +286,30 @@ vwl_status vwl_plan_info(int mode, int B, int K, int V, vwl_dtype dt, int64_t ou
     return VWL_OK;
 }
 
+vwl_status vwl_asym_plan_info(int B, int K, int V, vwl_dtype dt, vwl_delta_source delta, vwl_gate gate,
+                              int64_t out[6]) {
+    if (!out)
+        return VWL_ERR_NULL;
+    if ((delta != VWL_DELTA_A_MINUS_B && delta != VWL_DELTA_A && delta != VWL_DELTA_T_MINUS_B) ||
+        (gate != VWL_GATE_CDA && gate != VWL_GATE_FIXED))
+        return VWL_ERR_PARAM;
+    if (!shape_ok(B, K, V))
+        return VWL_ERR_SHAPE;
+    if (dt != VWL_F32 && dt != VWL_BF16)
+        return VWL_ERR_DTYPE;
+    Plan plan;
+    const long long R = (long long)B * (K + 1);
+    if (!make_plan(0, dt, R, V, plan, (int)delta, (int)gate))
+        return VWL_ERR_HIP;
+    out[0] = plan.W;
+    out[1] = plan.nv;
+    out[2] = plan.n_teams;
+    out[3] = plan.grid;
+    out[4] = kThreads;
+    out[5] = R;
+    return VWL_OK;
+}
+
 /* Tuning hook: pin the vectors-per-thread choice (1, 2, 4 or 8) and/or cap
  * the number of teams of one mode; 0 restores the automatic plan. */
 vwl_status vwl_set_plan_override(int mode, int nv, int max_teams) {
@@ -269,21 +329,28 @@ vwl_status vwl_set_phase_event(void *hip_event) {
     return VWL_OK;
 }
 
-vwl_status asym_verify(const void *a, const void *b, const void *t, const int32_t *draft,
-                       int B, int K, int V, vwl_dtype dt, float beta, float gamma,
-                       float *D, float *gamma_eff, uint8_t *accept, int32_t *fused,
-                       int32_t *accept_len, int32_t *token, int32_t *dev_err,
-                       void *workspace, size_t workspace_bytes, hipStream_t stream) {
+vwl_status asym_verify_variant(const void *a, const void *b, const void *t, const int32_t *draft,
+                               int B, int K, int V, vwl_dtype dt, float beta, float gamma,
+                               vwl_delta_source delta, vwl_gate gate,
+                               float *D, float *gamma_eff, uint8_t *accept, int32_t *fused,
+                               int32_t *accept_len, int32_t *token, int32_t *dev_err,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (delta != VWL_DELTA_A_MINUS_B && delta != VWL_DELTA_A && delta != VWL_DELTA_T_MINUS_B)
+        return VWL_ERR_PARAM;
+    if (gate != VWL_GATE_CDA && gate != VWL_GATE_FIXED)
+        return VWL_ERR_PARAM;
+    // a is read unless the gate is fixed and the fusion source is t - b
+    const bool need_a = gate == VWL_GATE_CDA || delta != VWL_DELTA_T_MINUS_B;
     const size_t need = vwl_asym_workspace_bytes(B, K, V, dt);
-    const vwl_status st = vwl_asym_check(a, b, t, draft, B, K, V, (int)dt, beta, gamma, D, gamma_eff,
-                                         accept, fused, accept_len, token, workspace, workspace_bytes, need);
+    const vwl_status st = asym_check_impl(need_a, a, b, t, draft, B, K, V, (int)dt, beta, gamma, D, gamma_eff,
+                                          accept, fused, accept_len, token, workspace, workspace_bytes, need);
     if (st != VWL_OK)
         return st;
     if (dev_err && !aligned(dev_err, 4))
         return VWL_ERR_ALIGN;
     const long long R = (long long)B * (K + 1);
     Plan plan;
-    if (!make_plan(0, (int)dt, R, V, plan))
+    if (!make_plan(0, (int)dt, R, V, plan, (int)delta, (int)gate))
         return VWL_ERR_HIP;
     const WsLayout L = ws_layout(B, K + 1, V, elem_bytes(dt), false);
     char *ws = static_cast<char *>(workspace);
@@ -315,7 +382,19 @@ vwl_status asym_verify(const void *a, const void *b, const void *t, const int32_
     p.req_ctr = reinterpret_cast<uint32_t *>(ws + L.req_ctr);
     p.row_info = reinterpret_cast<uint32_t *>(ws + L.row_info);
     p.rec = reinterpret_cast<uint64_t *>(ws + L.rec);
-    return launch_asym((int)dt, plan, p, stream, g_phase_event.load()) == hipSuccess ? VWL_OK : VWL_ERR_HIP;
+    return launch_asym((int)dt, (int)delta, (int)gate, plan, p, stream, g_phase_event.load()) == hipSuccess
+               ? VWL_OK
+               : VWL_ERR_HIP;
+}
+
+vwl_status asym_verify(const void *a, const void *b, const void *t, const int32_t *draft,
+                       int B, int K, int V, vwl_dtype dt, float beta, float gamma,
+                       float *D, float *gamma_eff, uint8_t *accept, int32_t *fused,
+                       int32_t *accept_len, int32_t *token, int32_t *dev_err,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return asym_verify_variant(a, b, t, draft, B, K, V, dt, beta, gamma, VWL_DELTA_A_MINUS_B, VWL_GATE_CDA, D,
+                               gamma_eff, accept, fused, accept_len, token, dev_err, workspace, workspace_bytes,
+                               stream);
 }
 
 vwl_status rapid_verify(const void *z, const void *y, const int32_t *draft,

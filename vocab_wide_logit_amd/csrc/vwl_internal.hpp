@@ -115,15 +115,29 @@ struct Plan {
     int grid;
 };
 
+// AsymSpec variants (values match vwl_delta_source / vwl_gate of the C ABI).
+enum { kDeltaAMinusB = 0, kDeltaA = 1, kDeltaTMinusB = 2 };
+enum { kGateCda = 0, kGateFixed = 1 };
+
 // Launchers (return hipSuccess or the launch error).
 // `after_rows`, when non-null, is recorded on `s` between the row kernel and
-// the kernels that follow it.
-hipError_t launch_asym(int dt, const Plan &plan, const AsymParams &p, hipStream_t s, hipEvent_t after_rows);
+// the kernels that follow it.  The AsymSpec launcher of fusion source DS is
+// instantiated in its own translation unit (asym_<delta>.hip).
+template <int DS>
+hipError_t launch_asym_ds(int dt, int gate, const Plan &plan, const AsymParams &p, hipStream_t s,
+                          hipEvent_t after_rows);
 hipError_t launch_rapid(int dt, const Plan &plan, const RapidParams &p, hipStream_t s, hipEvent_t after_rows);
 hipError_t launch_fill_zero(void *ptr, size_t bytes, hipStream_t s);
 
 // Resident workgroups per CU of each kernel instance (0 when unknown).
-int asym_blocks_per_cu(int dt, int nv);
+template <int DS>
+int asym_blocks_per_cu_ds(int dt, int nv, int gate);
 int rapid_blocks_per_cu(int dt, int nv);
+
+// Dispatch over the fusion source (defined with the C ABI, outside the kernel
+// translation units, so each of those instantiates only its own source).
+hipError_t launch_asym(int dt, int ds, int gate, const Plan &plan, const AsymParams &p, hipStream_t s,
+                       hipEvent_t after_rows);
+int asym_blocks_per_cu(int dt, int nv, int ds, int gate);
 
 } // namespace vwl

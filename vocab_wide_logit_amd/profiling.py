@@ -22,7 +22,7 @@ CSRC = os.path.join(PKG, "csrc")
 
 # sources whose change invalidates a recorded traffic figure, per mode
 KERNEL_SOURCES = {
-    "asym": ("asym.hip", "vwl_device.hpp", "vwl_internal.hpp"),
+    "asym": ("asym_kernels.hpp", "asym_ab.hip", "vwl_device.hpp", "vwl_internal.hpp"),
     "rapid": ("rapid.hip", "vwl_device.hpp", "vwl_internal.hpp"),
 }
 ROW_KERNEL_RE = {"asym": r"asym_rows_kernel", "rapid": r"rapid_rows_kernel"}

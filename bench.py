@@ -25,6 +25,7 @@ if ROOT not in sys.path:
 METRIC = "verified logit rows/s (B·(K+1)·V) and achieved HBM GB/s vs peak, 1 GPU"
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "asym_rows_kernel_bf16_B256_K4_V151936_traffic.txt")
+VALU_SUMMARY = os.path.join(ROOT, "profiles", "asym_rows_kernel_bf16_B256_K4_V151936_valu.txt")
 
 
 def _say(msg):
@@ -46,11 +47,12 @@ def _events(n):
     return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
 
-def time_asym(vwl, x, steps, warmup, copies=1):
-    """asym_verify calls on torch's current stream (the stream the library
-    launches on), each bracketed by events, with the library recording a
-    third event right after the row kernel.  Returns (wall seconds, per-call
-    ms, per-call row-kernel ms)."""
+def time_asym(vwl, x, steps, warmup, copies=1, delta="a-b", gate="cda"):
+    """asym_verify calls (asym_verify_variant for another fusion source or
+    gate) on torch's current stream (the stream the library launches on),
+    each bracketed by events, with the library recording a third event right
+    after the row kernel.  Returns (wall seconds, per-call ms, per-call
+    row-kernel ms)."""
     import torch
     sets = _device_inputs(vwl, x, copies)
     B, K = x.B, x.K
@@ -58,9 +60,15 @@ def time_asym(vwl, x, steps, warmup, copies=1):
     stream = torch.cuda.current_stream()
     ws = vwl._workspace(0, B, K, x.V, vwl.VWL_BF16 if x.dtype == "bf16" else vwl.VWL_F32,
                         torch.device("cuda", torch.cuda.current_device()), stream)
+    def call(a, b, t, d):
+        if delta == "a-b" and gate == "cda":
+            vwl.asym_verify(a, b, t, d, x.beta, x.gamma, out=out, workspace=ws)
+        else:
+            vwl.asym_verify_variant(a, b, t, d, x.beta, x.gamma, delta, gate, out=out, workspace=ws)
+
     for i in range(warmup):
         (a, b, t), d = sets[i % copies]
-        vwl.asym_verify(a, b, t, d, x.beta, x.gamma, out=out, workspace=ws)
+        call(a, b, t, d)
     start, mid, end = _events(steps), _events(steps), _events(steps)
     for e in mid:
         e.record(stream)  # creates the underlying HIP event
@@ -70,7 +78,7 @@ def time_asym(vwl, x, steps, warmup, copies=1):
         (a, b, t), d = sets[i % copies]
         start[i].record(stream)
         vwl.set_phase_event(mid[i])
-        vwl.asym_verify(a, b, t, d, x.beta, x.gamma, out=out, workspace=ws)
+        call(a, b, t, d)
         end[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -229,6 +237,13 @@ def main():
                      "bytes_per_launch": bytes_per_call, "avg_launch_ms": ms_rows,
                      "p10_ms": _pct(rows_ms, 0.1), "p90_ms": _pct(rows_ms, 0.9)},
     }
+    valu = profiling.read_summary(VALU_SUMMARY, "asym")
+    if valu is not None:
+        # the kernel's co-bound: VALU issue, from the committed SQ counter run
+        result["roofline"]["valu"] = {
+            "busy": float(valu["valu_busy"]), "insts_per_launch": float(valu["SQ_INSTS_VALU"]),
+            "floor_ms_at_full_issue": float(valu["valu_cycles_per_simd"]) / 2.4e9 * 1e3,
+            "source": os.path.relpath(VALU_SUMMARY, ROOT)}
     if not args.no_extra:
         _say("secondary: B=64 K=2 bf16 (4 rotating input sets), RAPID B=16 G=10 fp32, stream reference")
         x2 = W.batched_asym()
@@ -240,6 +255,18 @@ def main():
         ms3 = _median(per3)
         b3 = r3.algorithmic_bytes()
         sgbs = stream_read_gbs()
+        # the ablation variants on the same inputs (bytes actually read:
+        # the fixed gate with delta = t - b skips a)
+        variants = {}
+        for delta, gate in (("a", "cda"), ("t-b", "cda"), ("a-b", "fixed"), ("a", "fixed"), ("t-b", "fixed")):
+            _, pv, rv = time_asym(vwl, x, args.steps, args.warmup, delta=delta, gate=gate)
+            nbytes = bytes_per_call * (2 if (delta, gate) == ("t-b", "fixed") else 3) // 3
+            mr = _median(rv)
+            variants["delta=%s,gate=%s" % (delta, gate)] = {
+                "median_call_ms": _median(pv), "median_row_kernel_ms": mr,
+                "row_kernel_gbs": nbytes / (mr * 1e-3) / 1e9,
+                "plan": vwl.asym_plan_info(x.B, x.K, x.V, torch.bfloat16, delta, gate)}
+        result["variants_" + x.name] = variants
         result["stream_read_gbs"] = sgbs
         result["roofline"]["frac_of_stream"] = achieved / sgbs
         result["secondary"] = {

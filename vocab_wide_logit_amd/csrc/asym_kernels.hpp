@@ -103,54 +103,65 @@ __device__ __forceinline__ float jsd_term(float la2, float lb2, float x) {
     return M * (ax < 1.5f ? g_poly : g_closed);
 }
 
-// Row log-sum-exps, in log2 units, of two tensors from the W records of a
+// Row log-sum-exps, in log2 units, of N tensors from the W records of a
 // row: log2 sum_w s_w 2^(c_w - C), C = max c_w, in fp64 and in one fixed
 // order (lane w handles members w, w+64, ...; butterfly sums), so every
 // caller gets the same bits.  The references are integers, so each term is
 // an exact power-of-two rescale.  Called by one whole wave.  Tensor k has its
-// sums in word sk and its reference in the low (hik = false) or high half of
-// word ck.
-__device__ __forceinline__ void team_lse2x(const uint64_t *rec_row, int W, int s0, int c0w, bool hi0,
-                                           int s1, int c1w, bool hi1, double &L0, double &L1) {
+// sums in word sw[k] and its reference in the low (hi[k] = false) or high
+// half of word cw[k].
+template <int N>
+__device__ __forceinline__ void team_lse(const uint64_t *rec_row, int W, const int (&sw)[N], const int (&cw)[N],
+                                         const bool (&hi)[N], double (&L)[N]) {
     const int lane = threadIdx.x & 63;
     const float NEG = -3.0e38f;
-    float C0 = NEG, C1 = NEG;
-    double a0[2] = {0.0, 0.0}, a1[2] = {0.0, 0.0};
-    float r0[2] = {NEG, NEG}, r1[2] = {NEG, NEG};
+    auto ref = [&](const uint64_t *r, int k) {
+        const uint64_t x = ld_relaxed(r + cw[k]);
+        return hi[k] ? unpack_hi(x) : unpack_lo(x);
+    };
+    double a[N][2];
+    float r[N][2], C[N];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int w = lane + 64 * k;
+    for (int k = 0; k < N; ++k) {
+        a[k][0] = a[k][1] = 0.0;
+        r[k][0] = r[k][1] = NEG;
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int w = lane + 64 * h;
         if (w < W) {
-            const uint64_t *r = rec_row + (size_t)w * kRecWords;
-            const uint64_t x0 = ld_relaxed(r + c0w), x1 = ld_relaxed(r + c1w);
-            r0[k] = hi0 ? unpack_hi(x0) : unpack_lo(x0);
-            r1[k] = hi1 ? unpack_hi(x1) : unpack_lo(x1);
-            a0[k] = as_f64(ld_relaxed(r + s0));
-            a1[k] = as_f64(ld_relaxed(r + s1));
+            const uint64_t *rw = rec_row + (size_t)w * kRecWords;
+#pragma unroll
+            for (int k = 0; k < N; ++k) {
+                r[k][h] = ref(rw, k);
+                a[k][h] = as_f64(ld_relaxed(rw + sw[k]));
+            }
         }
     }
-    C0 = fmaxf(r0[0], r0[1]);
-    C1 = fmaxf(r1[0], r1[1]);
+#pragma unroll
+    for (int k = 0; k < N; ++k)
+        C[k] = fmaxf(r[k][0], r[k][1]);
     for (int w = lane + 128; w < W; w += 64) { // teams wider than 128 members
-        const uint64_t *r = rec_row + (size_t)w * kRecWords;
-        const uint64_t x0 = ld_relaxed(r + c0w), x1 = ld_relaxed(r + c1w);
-        C0 = fmaxf(C0, hi0 ? unpack_hi(x0) : unpack_lo(x0));
-        C1 = fmaxf(C1, hi1 ? unpack_hi(x1) : unpack_lo(x1));
+        const uint64_t *rw = rec_row + (size_t)w * kRecWords;
+#pragma unroll
+        for (int k = 0; k < N; ++k)
+            C[k] = fmaxf(C[k], ref(rw, k));
     }
-    C0 = wave_max(C0);
-    C1 = wave_max(C1);
-    double t0 = scale_pow2(a0[0], r0[0] - C0) + scale_pow2(a0[1], r0[1] - C0);
-    double t1 = scale_pow2(a1[0], r1[0] - C1) + scale_pow2(a1[1], r1[1] - C1);
+    double t[N];
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        C[k] = wave_max(C[k]);
+        t[k] = scale_pow2(a[k][0], r[k][0] - C[k]) + scale_pow2(a[k][1], r[k][1] - C[k]);
+    }
     for (int w = lane + 128; w < W; w += 64) { // teams wider than 128 members
-        const uint64_t *r = rec_row + (size_t)w * kRecWords;
-        const uint64_t x0 = ld_relaxed(r + c0w), x1 = ld_relaxed(r + c1w);
-        t0 += scale_pow2(as_f64(ld_relaxed(r + s0)), (hi0 ? unpack_hi(x0) : unpack_lo(x0)) - C0);
-        t1 += scale_pow2(as_f64(ld_relaxed(r + s1)), (hi1 ? unpack_hi(x1) : unpack_lo(x1)) - C1);
+        const uint64_t *rw = rec_row + (size_t)w * kRecWords;
+#pragma unroll
+        for (int k = 0; k < N; ++k)
+            t[k] += scale_pow2(as_f64(ld_relaxed(rw + sw[k])), ref(rw, k) - C[k]);
     }
-    t0 = wave_sum(t0);
-    t1 = wave_sum(t1);
-    L0 = (double)C0 + log2(t0);
-    L1 = (double)C1 + log2(t1);
+#pragma unroll
+    for (int k = 0; k < N; ++k)
+        L[k] = (double)C[k] + log2(wave_sum(t[k]));
 }
 
 // Online sum-of-exp state of one tensor over a thread's elements, fed one
@@ -452,13 +463,13 @@ __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, GATE>())) void asym_
                 set_dev_err(P.dev_err, 4);
             return;
         }
-        if (wave0) {
-            double La2, Lb2;
-            team_lse2x(rec_row, W, 0, 3, false, 1, 3, true, La2, Lb2);
-            if (tid == 0) {
-                sh_row[0] = La2;
-                sh_row[1] = Lb2;
-            }
+        // L_a on wave 0 and L_b on wave 1, side by side
+        const int cw = __builtin_amdgcn_readfirstlane(tid >> 6);
+        if (cw < 2) {
+            double L[1];
+            team_lse<1>(rec_row, W, {cw}, {3}, {cw == 1}, L);
+            if ((tid & 63) == 0)
+                sh_row[cw] = L[0];
         }
         __syncthreads();
         const float la_c = (float)sh_row[0]; // row log-sum-exps, log2 units
@@ -504,9 +515,9 @@ __global__ __launch_bounds__(kThreads) void asym_finalize_kernel(AsymParams P) {
     if (row >= P.R)
         return;
     const uint64_t *rec_row = P.rec + (size_t)row * P.Wmax * kRecWords;
-    double Lb2, Lt2;
-    team_lse2x(rec_row, P.W, 1, 3, true, 2, 4, false, Lb2, Lt2);
-    const double Lb = Lb2 * kLn2d, Lt = Lt2 * kLn2d;
+    double L2[2];
+    team_lse<2>(rec_row, P.W, {1, 2}, {3, 4}, {true, false}, L2);
+    const double Lb = L2[0] * kLn2d, Lt = L2[1] * kLn2d;
     float fbest = -__builtin_inff();
     for (int w = lane; w < P.W; w += 64)
         fbest = fmaxf(fbest, unpack_hi(ld_relaxed(rec_row + (size_t)w * kRecWords + 4)));

@@ -4,6 +4,7 @@ uses to attach the measured traffic of the row kernel to its roofline figure.
 
     python -m vocab_wide_logit_amd.profiling stats  <kernel_stats.csv> <kernel_trace.csv> <out.txt> <command...>
     python -m vocab_wide_logit_amd.profiling pmc    <fetch counter csv> <write counter csv> <out.txt> <command...>
+    python -m vocab_wide_logit_amd.profiling sq     <SQ counter csv> <out.txt> <command...>
 
 The traffic summary scales the row kernel's FETCH_SIZE and WRITE_SIZE (KiB per
 dispatch) by what the same counters read for a plain elementwise copy of a
@@ -140,9 +141,41 @@ def summarize_pmc(fetch_csv: str, write_csv: str, out_path: str, command: str, m
     return res
 
 
-def read_traffic(path: str, mode: str = "asym"):
-    """Traffic bytes per launch recorded in a summary, or None when the file
-    is missing or the kernel sources changed since it was taken."""
+SQ_COUNTERS = ("SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_VALU",
+               "SQ_INSTS_SALU", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "GRBM_GUI_ACTIVE")
+N_SIMD = 256 * 4      # compute units x SIMDs
+N_XCD = 8             # GRBM_GUI_ACTIVE is summed over the accelerator complex dies
+
+
+def summarize_sq(sq_csv: str, out_path: str, command: str, mode: str = "asym") -> dict:
+    """Instruction-issue counters of the row kernel, per dispatch, and the
+    VALU busy fraction: SQ_ACTIVE_INST_VALU counts quad-cycles (one per
+    wave64 VALU instruction on a 16-lane SIMD, more for transcendentals),
+    summed over all SIMDs; GRBM_GUI_ACTIVE counts busy cycles per die."""
+    kre = ROW_KERNEL_RE[mode]
+    res = {"mode": mode, "kernel_regex": kre, "source_hash": source_hash(mode)}
+    n = 0
+    for c in SQ_COUNTERS:
+        v, n = _per_dispatch(sq_csv, c, kre)
+        res[c] = v
+    res["dispatches"] = n
+    cycles = res["GRBM_GUI_ACTIVE"] / N_XCD
+    valu_cycles = res["SQ_ACTIVE_INST_VALU"] * 4.0 / N_SIMD
+    res["kernel_cycles"] = cycles
+    res["valu_cycles_per_simd"] = valu_cycles
+    res["valu_busy"] = valu_cycles / cycles
+    res["valu_cycles_per_inst"] = 4.0 * res["SQ_ACTIVE_INST_VALU"] / res["SQ_INSTS_VALU"]
+    lines = ["# VALU issue of the row kernel from rocprofv3 SQ counters", "",
+             "command: " + command, ""]
+    lines += ["%s: %s" % (k, v) for k, v in res.items()]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return res
+
+
+def read_summary(path: str, mode: str = "asym"):
+    """Key/value pairs of a counter summary, or None when the file is missing
+    or the kernel sources changed since it was taken."""
     if not os.path.exists(path):
         return None
     kv = {}
@@ -153,7 +186,14 @@ def read_traffic(path: str, mode: str = "asym"):
                 kv[k] = v
     if kv.get("source_hash") != source_hash(mode) or kv.get("mode") != mode:
         return None
-    return float(kv["traffic_bytes_per_launch"])
+    return kv
+
+
+def read_traffic(path: str, mode: str = "asym"):
+    """Traffic bytes per launch recorded in a summary, or None when the file
+    is missing or the kernel sources changed since it was taken."""
+    kv = read_summary(path, mode)
+    return None if kv is None else float(kv["traffic_bytes_per_launch"])
 
 
 def main(argv):
@@ -161,6 +201,8 @@ def main(argv):
         summarize_stats(argv[1], argv[3], " ".join(argv[4:]), trace_csv=argv[2])
     elif len(argv) >= 4 and argv[0] == "pmc":
         print(summarize_pmc(argv[1], argv[2], argv[3], " ".join(argv[4:])))
+    elif len(argv) >= 3 and argv[0] == "sq":
+        print(summarize_sq(argv[1], argv[2], " ".join(argv[3:])))
     else:
         print(__doc__)
         return 2

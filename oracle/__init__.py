@@ -19,6 +19,10 @@ with ctypes and marshals numpy arrays.  Each entry point follows the pages:
   ``phat = softmax(zhat/T)``), key design 3 (tail protection below 10% of the
   peak) and key design 4 (residual ``norm(max(p - phat, p - q, 0))``), with
   rejection sampling against the augmented target (overall framework).
+* ``e2sci`` -- E2-SCI notes, key design 3 (online adaptive verification:
+  per-position JSD of drafter and target against the window's threshold,
+  the EWMA credit state r = (1-beta) r + beta * accept_len/W, and the next
+  threshold clamp(T_base + alpha*omega*(r - tau_credit), T_min, T_max)).
 * ``rapid_zhat`` / ``rapid_phat`` -- the same definitions for one row, used
   by the pins.
 
@@ -74,6 +78,8 @@ def _load():
     lib.vwl_oracle_rapid_zhat.restype = i
     lib.vwl_oracle_rapid_phat.argtypes = [P, P, i, d, d, P]
     lib.vwl_oracle_rapid_phat.restype = i
+    lib.vwl_oracle_e2sci.argtypes = [P, P, i, i, i, i, P, P, P, d, d, d, d, d, d, P, P, P, P, P, i]
+    lib.vwl_oracle_e2sci.restype = i
     lib.vwl_oracle_max_threads.argtypes = []
     lib.vwl_oracle_max_threads.restype = i
     _lib = lib
@@ -154,6 +160,54 @@ def asym(a, b, t, draft, beta: float, gamma: float, dtype: str = "f32",
         raise RuntimeError("oracle asym failed with code %d" % rc)
     del R
     return AsymResult(lse, D, ge, fused, gap, top, acc, margin, alen, tok)
+
+
+@dataclass
+class E2sciParams:
+    """Controller constants of the E2-SCI threshold update (key design 3);
+    the pages fix only the EWMA decay (0.3), the rest are the caller's."""
+    alpha: float = 1.0
+    tau_credit: float = 0.5
+    T_base: float = 0.1
+    T_min: float = 0.01
+    T_max: float = 0.3
+    ewma: float = 0.3
+
+
+@dataclass
+class E2sciResult:
+    D: np.ndarray           # [B, W]
+    accept: np.ndarray      # [B, W] uint8
+    accept_len: np.ndarray  # [B] int32
+    r_hat: np.ndarray       # [B] updated smoothed acceptance
+    T_next: np.ndarray      # [B] threshold of the next window
+
+
+def e2sci(y, z, T, omega, r_hat, params: E2sciParams = E2sciParams(), dtype: str = "f32",
+          nthreads: int = 0) -> E2sciResult:
+    """Oracle of the E2-SCI adaptive JSD acceptance on [B, W, V] rows of
+    drafter (y) and target (z) logits; T, omega, r_hat are [B] float32 (the
+    values the device receives) and the constants are widened from float32."""
+    lib = _load()
+    sy, dt = _stored(y, dtype)
+    sz, _ = _stored(z, dtype)
+    B, Wn, V = sy.shape
+    T = np.ascontiguousarray(T, dtype=np.float32).reshape(B)
+    omega = np.ascontiguousarray(omega, dtype=np.float32).reshape(B)
+    r_hat = np.ascontiguousarray(r_hat, dtype=np.float32).reshape(B)
+    f = lambda v: float(np.float32(v))
+    D = np.zeros((B, Wn))
+    acc = np.zeros((B, Wn), np.uint8)
+    alen = np.zeros(B, np.int32)
+    r_out = np.zeros(B)
+    T_out = np.zeros(B)
+    rc = lib.vwl_oracle_e2sci(_ptr(sy), _ptr(sz), dt, B, Wn, V, _ptr(T), _ptr(omega), _ptr(r_hat),
+                              f(params.alpha), f(params.tau_credit), f(params.T_base), f(params.T_min),
+                              f(params.T_max), f(params.ewma), _ptr(D), _ptr(acc), _ptr(alen),
+                              _ptr(r_out), _ptr(T_out), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle e2sci failed with code %d" % rc)
+    return E2sciResult(D, acc, alen, r_out, T_out)
 
 
 @dataclass

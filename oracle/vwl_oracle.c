@@ -101,6 +101,24 @@ static double logsumexp(const double *x, int n)
     return m + log(s);
 }
 
+/* Jensen-Shannon divergence of P = softmax(x) and Q = softmax(y) given their
+ * log-sum-exps: 1/2 KL(P||M) + 1/2 KL(Q||M), M = (P+Q)/2, natural log; a term
+ * whose probability is 0 contributes 0. */
+static double jsd(const double *x, double Lx, const double *y, double Ly, int V)
+{
+    double kl = 0.0;
+    for (int v = 0; v < V; ++v) {
+        const double p = exp(x[v] - Lx);
+        const double q = exp(y[v] - Ly);
+        const double m = 0.5 * (p + q);
+        if (p > 0.0)
+            kl += p * log(p / m);
+        if (q > 0.0)
+            kl += q * log(q / m);
+    }
+    return 0.5 * kl;
+}
+
 /* ======================================================================
  * AsymSpec
  * ====================================================================== */
@@ -163,19 +181,7 @@ int vwl_oracle_asym(const void *a, const void *b, const void *t, int dtype,
                 lse[3 * r + 1] = Lb;
                 lse[3 * r + 2] = Lt;
 
-                /* D = 1/2 KL(P||M) + 1/2 KL(Q||M), M = (P+Q)/2, natural log,
-                 * a term whose probability is 0 contributes 0. */
-                double kl = 0.0;
-                for (int v = 0; v < V; ++v) {
-                    const double p = exp(xa[v] - La);
-                    const double q = exp(xb[v] - Lb);
-                    const double m = 0.5 * (p + q);
-                    if (p > 0.0)
-                        kl += p * log(p / m);
-                    if (q > 0.0)
-                        kl += q * log(q / m);
-                }
-                const double Dr = 0.5 * kl;
+                const double Dr = jsd(xa, La, xb, Lb, V);
                 D[r] = Dr;
                 /* the acceptance threshold: CDA relaxes gamma by exp(-D) */
                 geff[r] = (gate == 0) ? gamma * exp(-Dr) : gamma;
@@ -458,6 +464,83 @@ int vwl_oracle_rapid(const void *z, const void *y, int dtype,
         free(w);
     }
     return bad_alloc2 ? 2 : 0;
+}
+
+/* ======================================================================
+ * E2-SCI adaptive JSD acceptance ("E2-SCI: Elastic Edge-Cloud Speculative
+ * Decoding via Credit Inertia" notes, key design 3 "online adaptive
+ * verification", with the credit state of key design 1)
+ *
+ * Inputs: y (drafter) and z (target) stored rows [B][W][V] (W draft
+ * positions of one window per request); T_in[B] the threshold this window is
+ * verified with; omega[B] the adaptive weight from the caller's predictor;
+ * r_in[B] the smoothed acceptance rate before this window; alpha, tau
+ * (tau_credit), T_base, T_min, T_max, ewma (the EWMA decay beta).
+ * Outputs:
+ *   D[B][W]        JSD(softmax(y_i) || softmax(z_i)), natural log
+ *   accept[B][W]   D <= T_in (a divergence above the threshold rejects)
+ *   accept_len[B]  first rejected position, or W
+ *   r_out[B]       (1 - ewma) * r_in + ewma * accept_len / W
+ *   T_out[B]       max(T_min, min(T_base + alpha * omega * (r_out - tau), T_max))
+ * ====================================================================== */
+int vwl_oracle_e2sci(const void *y, const void *z, int dtype, int B, int W, int V,
+                     const float *T_in, const float *omega, const float *r_in,
+                     double alpha, double tau, double T_base, double T_min, double T_max, double ewma,
+                     double *D, uint8_t *accept, int32_t *accept_len, double *r_out, double *T_out,
+                     int nthreads)
+{
+    if (B < 1 || W < 1 || V < 1 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16))
+        return 1;
+    const long R = (long)B * W;
+    set_threads(nthreads);
+    int bad_alloc = 0;
+#pragma omp parallel
+    {
+        double *xy = malloc(sizeof(double) * (size_t)V);
+        double *xz = malloc(sizeof(double) * (size_t)V);
+        if (!xy || !xz) {
+#pragma omp atomic write
+            bad_alloc = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (long r = 0; r < R; ++r) {
+                const size_t off = (size_t)r * (size_t)V;
+                for (int v = 0; v < V; ++v) {
+                    xy[v] = widen(y, dtype, off + v);
+                    xz[v] = widen(z, dtype, off + v);
+                }
+                const double Dr = jsd(xy, logsumexp(xy, V), xz, logsumexp(xz, V), V);
+                D[r] = Dr;
+                accept[r] = (Dr <= (double)T_in[r / W]) ? 1 : 0;
+            }
+        }
+        free(xy);
+        free(xz);
+    }
+    if (bad_alloc)
+        return 2;
+    for (int bi = 0; bi < B; ++bi) {
+        int n = W;
+        for (int i = 0; i < W; ++i) {
+            if (!accept[(long)bi * W + i]) {
+                n = i;
+                break;
+            }
+        }
+        accept_len[bi] = n;
+        /* credit state: EWMA of the window's accepted fraction */
+        const double p_acc = (double)n / (double)W;
+        const double r = (1.0 - ewma) * (double)r_in[bi] + ewma * p_acc;
+        r_out[bi] = r;
+        /* threshold of the next window: base plus the credit term, clamped */
+        double T = T_base + alpha * (double)omega[bi] * (r - tau);
+        if (T > T_max)
+            T = T_max;
+        if (T < T_min)
+            T = T_min;
+        T_out[bi] = T;
+    }
+    return 0;
 }
 
 /* ======================================================================

@@ -415,6 +415,97 @@ def test_fixed_gate_against_cda(oracle_lib):
     assert np.any(rc.accept > rf.accept)  # CDA does relax somewhere on these rows
 
 
+# ------------------------------------------------ E2-SCI adaptive acceptance
+# E2-SCI notes, key design 3: per-position JSD of drafter and target against
+# the window's threshold, the EWMA credit state and the clamped threshold.
+
+def _e2sci_rows(B, Wn, V, seed, scale=2.0):
+    rng = np.random.default_rng(seed)
+    y = rng.normal(0, scale, size=(B, Wn, V)).astype(np.float32)
+    z = (y + rng.normal(0, 0.7, size=y.shape)).astype(np.float32)
+    return y, z
+
+
+@pytest.mark.parametrize("V", [2, 7, 1000])
+def test_e2sci_jsd_matches_scipy(oracle_lib, V):
+    y, z = _e2sci_rows(3, 4, V, 40 + V)
+    r = oracle.e2sci(y, z, np.full(3, 0.1), np.ones(3), np.full(3, 0.5))
+    for bi in range(3):
+        for i in range(4):
+            p = softmax(y[bi, i].astype(np.float64))
+            q = softmax(z[bi, i].astype(np.float64))
+            assert abs(r.D[bi, i] - jensenshannon(p, q) ** 2) <= 1e-12 + 1e-10 * r.D[bi, i]
+
+
+def test_e2sci_threshold_is_inclusive(oracle_lib):
+    """A divergence above the threshold rejects, one equal to it does not:
+    identical rows (D = 0) pass at T = 0; a row passes at the float32 just
+    above its D and fails at the one just below."""
+    y, z = _e2sci_rows(2, 3, 300, 41)
+    z[0] = y[0]
+    r = oracle.e2sci(y, z, np.zeros(2, np.float32), np.ones(2), np.full(2, 0.5))
+    assert np.all(r.D[0] == 0.0) and np.all(r.accept[0] == 1) and r.accept_len[0] == 3
+    assert np.all(r.D[1] > 0.0) and np.all(r.accept[1] == 0) and r.accept_len[1] == 0
+    d = r.D[1, 0]
+    up = np.nextafter(np.float32(d), np.float32(1.0))
+    dn = np.nextafter(np.float32(d), np.float32(0.0))
+    assert r.accept[1, 0] == 0
+    ru = oracle.e2sci(y, z, np.array([0.0, up], np.float32), np.ones(2), np.full(2, 0.5))
+    rd = oracle.e2sci(y, z, np.array([0.0, dn], np.float32), np.ones(2), np.full(2, 0.5))
+    assert ru.accept[1, 0] == 1 and rd.accept[1, 0] == 0
+
+
+def test_e2sci_scan_stops_at_first_rejection(oracle_lib):
+    y, z = _e2sci_rows(1, 6, 500, 42)
+    z[0, [0, 1, 3]] = y[0, [0, 1, 3]]      # D = 0 at positions 0, 1, 3
+    r = oracle.e2sci(y, z, np.zeros(1, np.float32), np.ones(1), np.full(1, 0.5))
+    np.testing.assert_array_equal(r.accept[0], [1, 1, 0, 1, 0, 0])
+    assert r.accept_len[0] == 2
+
+
+def test_e2sci_ewma_closed_form(oracle_lib):
+    """With every window fully accepted (T above ln 2) the credit state follows
+    r_n = 1 - (1 - r_0)(1 - beta)^n; fully rejected (T below 0), r_0 (1 - beta)^n;
+    beta = 0.3 as printed on the page."""
+    beta = GOLDEN["e2sci_ewma"]["value"]
+    prm = oracle.E2sciParams(ewma=beta)
+    y, z = _e2sci_rows(2, 4, 64, 43)
+    r0 = np.array([0.2, 0.9], np.float32)
+    for T, target in ((1.0, 1.0), (-1.0, 0.0)):
+        r = r0.copy()
+        for n in range(1, 6):
+            out = oracle.e2sci(y, z, np.full(2, T, np.float32), np.ones(2), r, prm)
+            r = out.r_hat.astype(np.float32)
+            want = target + (r0.astype(np.float64) - target) * (1 - beta) ** n
+            np.testing.assert_allclose(out.r_hat, want, rtol=0, atol=1e-6)
+    # a half-accepted window moves r halfway by beta
+    z2 = z.copy()
+    z2[0, :2] = y[0, :2]
+    out = oracle.e2sci(y, z2, np.zeros(2, np.float32), np.ones(2), np.array([0.0, 0.0], np.float32), prm)
+    assert out.accept_len[0] == 2 and abs(out.r_hat[0] - float(np.float32(beta)) * 0.5) < 1e-15
+
+
+def test_e2sci_threshold_update(oracle_lib):
+    """Delta T = alpha * omega * (r - tau): positive above the neutral credit,
+    negative below, linear in omega; the result is clamped to [T_min, T_max]."""
+    prm = oracle.E2sciParams(alpha=0.5, tau_credit=0.5, T_base=0.1, T_min=0.02, T_max=0.25, ewma=1.0)
+    y, z = _e2sci_rows(4, 4, 64, 44)
+    z[:2] = y[:2]                          # requests 0, 1 accept everything: r = 1
+    T_in = np.zeros(4, np.float32)
+    omega = np.array([0.2, 0.4, 0.2, 0.4], np.float32)
+    out = oracle.e2sci(y, z, T_in, omega, np.zeros(4, np.float32), prm)
+    np.testing.assert_array_equal(out.accept_len, [4, 4, 0, 0])
+    f = lambda v: float(np.float32(v))
+    for bi in range(4):
+        r = float(out.r_hat[bi])
+        want = f(0.1) + f(0.5) * float(omega[bi]) * (r - f(0.5))
+        assert abs(out.T_next[bi] - min(max(want, f(0.02)), f(0.25))) < 1e-12
+    assert out.T_next[0] > f(0.1) and out.T_next[2] < f(0.1)
+    assert abs((out.T_next[1] - f(0.1)) - 2 * (out.T_next[0] - f(0.1))) < 1e-9
+    big = oracle.e2sci(y, z, T_in, np.full(4, 100.0, np.float32), np.zeros(4, np.float32), prm)
+    np.testing.assert_array_equal(big.T_next, [f(0.25), f(0.25), f(0.02), f(0.02)])
+
+
 def test_page_defaults_in_workloads():
     """The named workloads use the pages' hyperparameters (AsymSpec notes 4.4;
     RAPID notes, hyperparameters)."""

@@ -28,6 +28,12 @@ Recipe (one logit row = one draft position of one request):
   (every ``t + beta*(a - b)`` with ``beta >= 0``) then has an exact tie at its
   maximum, and ``a`` has an exact tie at its maximum, whatever the evaluation
   order or precision.
+* E2-SCI: target ``z_t = z + N(0, 0.5^2)``; drafter ``y = z + N(0,
+  sigma^2)`` with ``sigma`` uniform on [0.1, 1.0] per row (a spread of
+  divergences); "identical" rows set ``y := z_t`` bit for bit (divergence
+  exactly 0).  The caller-owned controller state is drawn per request:
+  threshold ``T`` uniform on [0.02, 0.2], weight ``omega`` on [0.5, 2],
+  smoothed acceptance ``r_hat`` on [0, 1], each rounded to float32.
 * RAPID: ``base = z``; target ``z_t = base + N(0, 0.5^2)``; drafter ``y =
   base + N(0, 1)`` except in an exact fraction of rows where the spike is
   displaced as above.  Drafts ``x_i`` are samples from the drafter's
@@ -253,6 +259,87 @@ def gen_asym(B: int, K: int, V: int, dtype: str = F32, seed: int = SEED_BASE,
 
 
 # --------------------------------------------------------------------------
+# E2-SCI inputs
+# --------------------------------------------------------------------------
+@dataclass
+class E2sciInputs:
+    """Drafter logits y and target logits z, each [B, W, V] float32 holding
+    values exact in ``dtype`` (W draft positions of one window per
+    request), and the caller-owned controller state per request."""
+
+    y: np.ndarray
+    z: np.ndarray
+    T: np.ndarray       # [B] float32 threshold of this window
+    omega: np.ndarray   # [B] float32 adaptive weight
+    r_hat: np.ndarray   # [B] float32 smoothed acceptance before this window
+    dtype: str
+    seed: int
+    identical: np.ndarray = field(default=None)  # bool [B, W]
+    name: str = ""
+
+    @property
+    def B(self):
+        return self.y.shape[0]
+
+    @property
+    def W(self):
+        return self.y.shape[1]
+
+    @property
+    def V(self):
+        return self.y.shape[2]
+
+    def algorithmic_bytes(self) -> int:
+        es = 2 if self.dtype == BF16 else 4
+        return 2 * self.y.shape[0] * self.y.shape[1] * self.V * es
+
+
+def gen_e2sci(B: int, W: int, V: int, dtype: str = F32, seed: int = SEED_BASE + 5,
+              identical_frac: float = 0.0, noise_lo: float = 0.1, noise_hi: float = 1.0,
+              base_std: float = 2.0, spike: float = 8.0, target_std: float = 0.5,
+              T_range=(0.02, 0.2), name: str = "") -> E2sciInputs:
+    """Generate one E2-SCI workload following the module recipe."""
+    if B < 1 or W < 1 or V < 1:
+        raise ValueError("need B >= 1, W >= 1, V >= 1")
+    R = B * W
+    ss = np.random.SeedSequence(seed)
+    s_rows, s_sel, s_state = ss.spawn(3)
+    sel = np.random.default_rng(s_sel)
+    ident_rows = _choose_rows(sel, np.arange(R), int(round(identical_frac * R)))
+    identical = np.zeros(R, bool)
+    identical[ident_rows] = True
+    y = np.empty((R, V), np.float32)
+    z = np.empty((R, V), np.float32)
+    row_seeds = s_rows.spawn(R)
+
+    def make_row(r, bufs):
+        base, n = bufs
+        g = np.random.default_rng(row_seeds[r])
+        g.standard_normal(out=base)
+        base *= base_std
+        base[int(g.integers(0, V))] += spike
+        sigma = g.uniform(noise_lo, noise_hi)
+        g.standard_normal(out=n)
+        n *= target_std
+        n += base
+        z[r] = _to_dtype(n, dtype)
+        g.standard_normal(out=n)
+        n *= sigma
+        n += base
+        y[r] = _to_dtype(n, dtype)
+        if identical[r]:
+            y[r] = z[r]
+
+    _parallel_rows(R, V, 2, make_row)
+    st = np.random.default_rng(s_state)
+    T = st.uniform(T_range[0], T_range[1], size=B).astype(np.float32)
+    omega = st.uniform(0.5, 2.0, size=B).astype(np.float32)
+    r_hat = st.uniform(0.0, 1.0, size=B).astype(np.float32)
+    return E2sciInputs(y=y.reshape(B, W, V), z=z.reshape(B, W, V), T=T, omega=omega, r_hat=r_hat,
+                       dtype=dtype, seed=seed, identical=identical.reshape(B, W), name=name)
+
+
+# --------------------------------------------------------------------------
 # RAPID inputs
 # --------------------------------------------------------------------------
 @dataclass
@@ -399,3 +486,15 @@ def large_asym(seed: int = SEED_BASE + 4, beta: float = 1.0, gamma: float = 0.5)
     return gen_asym(256, 4, VOCAB_QWEN3, BF16, seed, displaced_frac=0.3,
                     identical_frac=0.2, tie_frac=0.05, beta=beta, gamma=gamma,
                     name="asym_large_B256_K4_V151936_bf16")
+
+
+def e2sci_single(seed: int = SEED_BASE + 5) -> E2sciInputs:
+    """B=1 (the pages' real-time batch), W=8 drafts, V=151936, bf16."""
+    return gen_e2sci(1, 8, VOCAB_QWEN3, BF16, seed, identical_frac=0.25,
+                     name="e2sci_B1_W8_V151936_bf16")
+
+
+def e2sci_batched(seed: int = SEED_BASE + 6) -> E2sciInputs:
+    """B=64 requests, W=8 drafts, V=151936, bf16."""
+    return gen_e2sci(64, 8, VOCAB_QWEN3, BF16, seed, identical_frac=0.1,
+                     name="e2sci_B64_W8_V151936_bf16")

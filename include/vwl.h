@@ -2,11 +2,14 @@
  * vwl.h -- speculative verification and logit fusion over vocabulary-wide
  * logit rows, on AMD Instinct MI355X (gfx950).
  *
- * Two entry points, one per method:
+ * Entry points, one per method (plus the AsymSpec ablation variants):
  *
  *   asym_verify   AsymSpec ("AsymSpec: Context-Asymmetric Speculative
  *                 Decoding for Agentic LLMs" reading notes, section 4.1
  *                 "contrastive delta-fusion" and section 4.2 "CDA gate").
+ *   e2sci_verify  E2-SCI ("E2-SCI: Elastic Edge-Cloud Speculative Decoding
+ *                 via Credit Inertia" notes, key design 3 "online adaptive
+ *                 verification").
  *   rapid_verify  RAPID ("RAPID: Long-Context Inference with
  *                 Retrieval-Augmented Speculative Decoding" notes, key
  *                 designs 2 "retrieval-augmented target distribution",
@@ -154,6 +157,57 @@ vwl_status asym_verify_variant(const void *a, const void *b, const void *t,
                                float *D, float *gamma_eff, uint8_t *accept, int32_t *fused,
                                int32_t *accept_len, int32_t *token, int32_t *dev_err,
                                void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * E2-SCI adaptive JSD acceptance ("E2-SCI: Elastic Edge-Cloud Speculative
+ * Decoding via Credit Inertia" notes, key design 3 "online adaptive
+ * verification", with the credit state of key design 1)
+ *
+ * One window of W drafts per request b, verified against the window's
+ * threshold T_in[b]; then the caller-owned credit state moves on:
+ *   D_i      = JSD(softmax(y_i) || softmax(z_i)), natural log, in [0, ln 2]
+ *   accept_i = D_i <= T_in[b]     (a divergence above the threshold rejects)
+ *   accept_len[b] = first i with accept_i == 0, else W
+ *   r_hat[b] := (1 - ewma) * r_hat[b] + ewma * accept_len[b] / W
+ *   T_out[b]  = max(T_min, min(T_base + alpha * omega[b] * (r_hat[b] - tau_credit), T_max))
+ * The page's EWMA decay is 0.3; the other constants are the caller's (the
+ * page gives none).  omega is the adaptive weight of the page's predictor,
+ * which needs trained weights and stays with the caller.
+ *
+ * Inputs:
+ *   y, z      [B][W][V] drafter and target logits of dtype `dt`, 16-byte
+ *             aligned; W >= 1 draft positions per request, W <= VWL_MAX_K+1.
+ *   T_in, omega  [B] fp32 device arrays.
+ *   r_hat     [B] fp32 device array, read and updated in place.
+ *   params    host pointer; every constant finite, T_min <= T_max,
+ *             0 <= ewma <= 1, else VWL_ERR_PARAM.
+ * Outputs: D [B][W] fp32, accept [B][W] uint8, accept_len [B] int32,
+ *   T_out [B] fp32 (may alias T_in: each row reads its threshold before the
+ *   request's last row writes the next one), dev_err nullable.
+ * Workspace: vwl_e2sci_workspace_bytes, with the same rules as the others.
+ * Precision: as asym_verify (fp32 lanes, fp64 combines); the decision
+ *   D <= T and the state update are taken in fp64.
+ * --------------------------------------------------------------------------- */
+typedef struct {
+    float alpha;      /* gain of the credit term */
+    float tau_credit; /* neutral credit level */
+    float T_base;     /* base threshold */
+    float T_min;      /* lower safety bound */
+    float T_max;      /* upper safety bound */
+    float ewma;       /* EWMA decay of the credit state (0.3 on the page) */
+} vwl_e2sci_params;
+
+size_t vwl_e2sci_workspace_bytes(int B, int W, int V, vwl_dtype dt);
+
+vwl_status e2sci_verify(const void *y, const void *z, int B, int W, int V, vwl_dtype dt,
+                        const float *T_in, const float *omega, float *r_hat,
+                        const vwl_e2sci_params *params,
+                        float *D, uint8_t *accept, int32_t *accept_len, float *T_out,
+                        int32_t *dev_err, void *workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/* Launch plan of e2sci_verify (same fields as vwl_plan_info; [5] = B*W). */
+vwl_status vwl_e2sci_plan_info(int B, int W, int V, vwl_dtype dt, int64_t out[6]);
 
 /* Largest vocabulary a RAPID call accepts (2^21 logits per row). */
 #define VWL_RAPID_MAX_V 2097152

@@ -15,6 +15,10 @@ Rules:
   D (a relative bound is void at D = 0, which a single-token row or two rows
   that differ by a constant reach exactly in the oracle); for drafter rows
   that are bitwise identical the device must return exactly 0 and gamma.
+* E2-SCI: D as above; a position is ambiguous when its divergence is within
+  1e-5 relative of the window threshold; the credit state and the next
+  threshold within 1e-6 relative on the requests whose decisive positions
+  are clear.
 * RAPID: a draft test is ambiguous when |u*q - phat| <= 1e-6 * max(u*q, phat)
   or the draft's augmented logit is within 1e-6 of the tail threshold; a draw
   is ambiguous when u*S is within 1e-6*S of an end of the chosen interval or
@@ -200,4 +204,53 @@ def compare_rapid(dev: dict, ora, G: int, u_accept=None, rtol: float = REL_TOL) 
             rep.fail("emit_dist outside tolerance on %d entries" % int(bad.sum()))
         rep.stats["emit_tv_max"] = float(np.max(0.5 * np.sum(np.abs(d - o), axis=1)[ok_rows])) if ok_rows.any() else 0.0
         rep.stats["emit_rel_max"] = float(np.max((np.abs(d - o) / np.maximum(o, 1e-30))[ok_rows][o[ok_rows] > 1e-7])) if ok_rows.any() else 0.0
+    return rep
+
+
+def compare_e2sci(dev: dict, ora, T, identical=None, rtol: float = REL_TOL,
+                  d_floor: float = D_ABS_FLOOR, state_rtol: float = 1e-6) -> Report:
+    """dev: numpy arrays D, accept, accept_len, T_next, r_hat; ora:
+    oracle.E2sciResult; T: [B] thresholds of the window.  A position whose
+    oracle divergence is within 1e-5 relative (plus 1e-9) of its threshold is
+    ambiguous; a request is excluded, and counted, when a decisive position
+    (i <= accept length) is.  The credit state and the next threshold are
+    compared within 1e-6 relative (plus 1e-7) on the requests checked."""
+    rep = Report()
+    D_o, D_d = ora.D, np.asarray(dev["D"], np.float64)
+    if identical is not None:
+        ident = np.asarray(identical, bool)
+        if np.any(D_d[ident] != 0.0):
+            rep.fail("D must be exactly 0 for identical rows (%d rows)" % int(np.sum(D_d[ident] != 0.0)))
+    zero = D_o == 0.0
+    if np.any(np.abs(D_d[zero]) > d_floor):
+        rep.fail("|D| above %g where the oracle's D is 0" % d_floor)
+    nz = ~zero
+    bad = np.abs(D_d[nz] - D_o[nz]) > rtol * np.abs(D_o[nz]) + d_floor
+    if np.any(bad):
+        rep.fail("D outside %g relative on %d rows" % (rtol, int(bad.sum())))
+    rep.stats["D_max_rel"] = float(np.max(np.abs(D_d[nz] - D_o[nz]) / np.abs(D_o[nz]))) if np.any(nz) else 0.0
+    T = np.asarray(T, np.float64).reshape(-1, 1)
+    amb = np.abs(D_o - T) <= rtol * np.maximum(np.abs(D_o), np.abs(T)) + d_floor
+    a_d = np.asarray(dev["accept"]).astype(np.uint8)
+    mism = (a_d != ora.accept) & ~amb
+    if np.any(mism):
+        rep.fail("accept mismatch on %d positions (first %s)" % (int(mism.sum()), np.argwhere(mism)[0].tolist()))
+    rep.stats["accept_ambiguous"] = int(amb.sum())
+    rep.stats["acceptance_rate"] = float(ora.accept.mean())
+    al_d = np.asarray(dev["accept_len"])
+    r_d = np.asarray(dev["r_hat"], np.float64)
+    t_d = np.asarray(dev["T_next"], np.float64)
+    Wn = D_o.shape[1]
+    for bi in range(D_o.shape[0]):
+        n = int(ora.accept_len[bi])
+        if amb[bi, :min(n + 1, Wn)].any():
+            rep.excluded += 1
+            continue
+        rep.checked += 1
+        if al_d[bi] != n:
+            rep.fail("accept_len mismatch at request %d: dev %d oracle %d" % (bi, al_d[bi], n))
+        if abs(r_d[bi] - ora.r_hat[bi]) > state_rtol * abs(ora.r_hat[bi]) + 1e-7:
+            rep.fail("r_hat mismatch at request %d: dev %r oracle %r" % (bi, r_d[bi], ora.r_hat[bi]))
+        if abs(t_d[bi] - ora.T_next[bi]) > state_rtol * abs(ora.T_next[bi]) + 1e-7:
+            rep.fail("T_next mismatch at request %d: dev %r oracle %r" % (bi, t_d[bi], ora.T_next[bi]))
     return rep

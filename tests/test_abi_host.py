@@ -210,3 +210,37 @@ def test_asym_variant_argument_codes(lib):
     assert _variant(lib, 0, 1, 1, 0) == 1
     assert _variant(lib, 0, 2, 1, 0) == 5
     assert _variant(lib, A, 2, 1, 0) == 5
+
+
+def _e2sci(lib, **kw):
+    """e2sci_verify with placeholder device pointers: every case here returns
+    from the host-side checks, before anything touches a device."""
+    args = dict(y=A, z=A + 0x1000, B=2, W=4, V=100, dt=0, T=A + 0x2000, om=A + 0x3000, r=A + 0x4000,
+                prm=(1.0, 0.5, 0.1, 0.01, 0.3, 0.3), D=A + 0x5000, acc=A + 0x6000, alen=A + 0x7000,
+                To=A + 0x8000, ws=0, wsb=0)
+    args.update(kw)
+    p = lambda x: ctypes.c_void_p(x) if x else None
+    import vocab_wide_logit_amd as vwl
+    prm = None if args["prm"] is None else ctypes.byref(vwl.E2sciParams(*args["prm"]))
+    return lib.e2sci_verify(p(args["y"]), p(args["z"]), args["B"], args["W"], args["V"], args["dt"],
+                            p(args["T"]), p(args["om"]), p(args["r"]), prm, p(args["D"]), p(args["acc"]),
+                            p(args["alen"]), p(args["To"]), None, p(args["ws"]), ctypes.c_size_t(args["wsb"]),
+                            None)
+
+
+def test_e2sci_argument_codes(lib):
+    assert lib.vwl_e2sci_workspace_bytes(2, 4, 100, 0) > 0
+    assert lib.vwl_e2sci_workspace_bytes(2, 0, 100, 0) == 0
+    assert _e2sci(lib) == 5                      # all good but no workspace
+    for k in ("y", "z", "T", "om", "r", "D", "acc", "alen", "To"):
+        assert _e2sci(lib, **{k: 0}) == 1, k
+    assert _e2sci(lib, prm=None) == 1
+    assert _e2sci(lib, W=0) == 2
+    assert _e2sci(lib, W=65) == 2
+    assert _e2sci(lib, B=0) == 2
+    assert _e2sci(lib, dt=5) == 3
+    assert _e2sci(lib, prm=(1.0, 0.5, 0.1, 0.3, 0.01, 0.3)) == 4      # T_min > T_max
+    assert _e2sci(lib, prm=(1.0, 0.5, 0.1, 0.01, 0.3, 1.5)) == 4      # ewma outside [0, 1]
+    assert _e2sci(lib, prm=(float("nan"), 0.5, 0.1, 0.01, 0.3, 0.3)) == 4
+    assert _e2sci(lib, y=A + 4) == 7
+    assert _e2sci(lib, T=A + 0x2002) == 7

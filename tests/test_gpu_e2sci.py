@@ -1,0 +1,142 @@
+"""GPU parity of ``e2sci_verify`` (E2-SCI notes, key design 3: per-position
+JSD of drafter and target against the window threshold, the EWMA credit
+state and the clamped next threshold) against the fp64 oracle, through the
+C ABI.  Rules in oracle/parity.py (compare_e2sci)."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from oracle.parity import compare_e2sci
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print("[e2sci] " + msg, flush=True)
+
+
+@pytest.fixture(scope="module")
+def vwl():
+    import vocab_wide_logit_amd as m
+    m.load_library()
+    return m
+
+
+def _oracle_params(prm):
+    return oracle.E2sciParams(alpha=prm.alpha, tau_credit=prm.tau_credit, T_base=prm.T_base,
+                              T_min=prm.T_min, T_max=prm.T_max, ewma=prm.ewma)
+
+
+def run_dev(vwl, x, prm, T=None, r_hat=None, in_place=False):
+    import torch
+    y = vwl.to_device_logits(x.y, x.dtype)
+    z = vwl.to_device_logits(x.z, x.dtype)
+    Td = torch.from_numpy(np.ascontiguousarray(x.T if T is None else T, np.float32)).cuda()
+    om = torch.from_numpy(np.ascontiguousarray(x.omega, np.float32)).cuda()
+    rh = torch.from_numpy(np.ascontiguousarray(x.r_hat if r_hat is None else r_hat, np.float32)).cuda()
+    out = vwl.e2sci_verify(y, z, Td, om, rh, prm, T_out=Td if in_place else None)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out._asdict().items()}
+
+
+def check(vwl, x, prm=None, label="", T=None, r_hat=None, in_place=False):
+    prm = prm if prm is not None else vwl.E2sciParams()
+    T = x.T if T is None else np.asarray(T, np.float32)
+    r_hat = x.r_hat if r_hat is None else np.asarray(r_hat, np.float32)
+    _say("case %s %s B=%d W=%d V=%d" % (label, x.dtype, x.B, x.W, x.V))
+    dev = run_dev(vwl, x, prm, T, r_hat, in_place)
+    ora = oracle.e2sci(x.y, x.z, T, x.omega, r_hat, _oracle_params(prm), x.dtype)
+    rep = compare_e2sci(dev, ora, T, identical=x.identical)
+    _say("  " + str(rep))
+    assert rep.ok, str(rep)
+    assert dev["dev_err"][0] == 0
+    return dev, ora, rep
+
+
+def test_tiny_fp32(vwl):
+    x = W.gen_e2sci(4, 4, 1024, "f32", seed=11, identical_frac=0.25)
+    check(vwl, x, label="B4_W4_V1024")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [1, 2, 17, 1027, 151937])
+@pytest.mark.parametrize("Wn", [1, 3, 8])
+def test_small_and_ragged(vwl, dtype, V, Wn):
+    x = W.gen_e2sci(3, Wn, V, dtype, seed=3000 + V + Wn, identical_frac=0.2)
+    check(vwl, x, label="small")
+
+
+def test_single_request_window(vwl):
+    """B = 1, the pages' real-time batch; W = 8 drafts at V = 151936."""
+    x = W.e2sci_single()
+    dev, ora, rep = check(vwl, x, label=x.name)
+    assert rep.checked + rep.excluded == 1
+
+
+def test_batched(vwl):
+    x = W.e2sci_batched()
+    dev, ora, rep = check(vwl, x, label=x.name)
+    assert rep.excluded <= 2
+    assert 0 < ora.accept.mean() < 1
+
+
+def test_thresholds_in_place_over_windows(vwl):
+    """Five windows in a row with the credit state and the threshold carried
+    on the device (T_out aliases T_in, r_hat updated in place); each window
+    is checked against the oracle fed the same state."""
+    import torch
+    prm = vwl.E2sciParams(alpha=0.4, tau_credit=0.5, T_base=0.08, T_min=0.02, T_max=0.2, ewma=0.3)
+    xs = [W.gen_e2sci(16, 4, 30000, "bf16", seed=500 + k, identical_frac=0.1) for k in range(5)]
+    T = torch.from_numpy(xs[0].T.copy()).cuda()
+    rh = torch.from_numpy(xs[0].r_hat.copy()).cuda()
+    om = torch.from_numpy(xs[0].omega.copy()).cuda()
+    for k, x in enumerate(xs):
+        T_before = T.cpu().numpy().copy()
+        r_before = rh.cpu().numpy().copy()
+        out = vwl.e2sci_verify(vwl.to_device_logits(x.y, x.dtype), vwl.to_device_logits(x.z, x.dtype),
+                               T, om, rh, prm, T_out=T)
+        torch.cuda.synchronize()
+        dev = {k2: v.cpu().numpy() for k2, v in out._asdict().items()}
+        assert out.T_next.data_ptr() == T.data_ptr()
+        ora = oracle.e2sci(x.y, x.z, T_before, xs[0].omega, r_before, _oracle_params(prm), x.dtype)
+        rep = compare_e2sci(dev, ora, T_before, identical=x.identical)
+        _say("  window %d %s" % (k, rep))
+        assert rep.ok, str(rep)
+
+
+@pytest.mark.parametrize("nv", [1, 2, 4, 8])
+def test_every_plan(vwl, nv):
+    import torch
+    x = W.gen_e2sci(6, 4, 40000, "bf16", seed=57, identical_frac=0.2)
+    try:
+        vwl.set_plan_override("asym", nv, 0)
+        plan = vwl.e2sci_plan_info(6, 4, 40000, torch.bfloat16)
+        assert plan["vec_per_thread"] == nv
+        check(vwl, x, label="plan %s" % plan)
+    finally:
+        vwl.set_plan_override("asym", 0, 0)
+
+
+def test_few_teams(vwl):
+    x = W.gen_e2sci(16, 5, 20000, "f32", seed=79)
+    try:
+        vwl.set_plan_override("asym", 1, 3)
+        check(vwl, x, label="3 teams")
+    finally:
+        vwl.set_plan_override("asym", 0, 0)
+
+
+def test_inclusive_threshold_and_clamps(vwl):
+    """Identical rows (D = 0) pass at T = 0; huge and tiny weights hit the
+    clamps exactly."""
+    x = W.gen_e2sci(8, 3, 5000, "f32", seed=80, identical_frac=0.0)
+    x.y[:4] = x.z[:4]
+    x.identical[:4] = True
+    x.omega[:] = 1e4
+    prm = vwl.E2sciParams(alpha=1.0, tau_credit=0.5, T_base=0.1, T_min=0.02, T_max=0.25, ewma=1.0)
+    dev, ora, rep = check(vwl, x, prm, T=np.zeros(8, np.float32), r_hat=np.zeros(8, np.float32))
+    np.testing.assert_array_equal(dev["accept_len"][:4], 3)
+    np.testing.assert_array_equal(dev["accept_len"][4:], 0)
+    np.testing.assert_array_equal(dev["T_next"], np.float32([0.25] * 4 + [0.02] * 4))
+    np.testing.assert_array_equal(dev["r_hat"], np.float32([1.0] * 4 + [0.0] * 4))

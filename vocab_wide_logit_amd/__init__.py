@@ -17,6 +17,9 @@ Entry points (same names as the C ABI):
 * ``asym_verify_variant`` -- the same pass with the fusion source and the
   gate of the AsymSpec notes' mechanism ablation: delta = a - b, a or t - b;
   the CDA threshold or a fixed gamma.
+* ``e2sci_verify`` -- E2-SCI adaptive JSD acceptance (E2-SCI notes, key
+  design 3): per-position divergence of drafter and target against the
+  window threshold, then the caller-owned credit state and next threshold.
 * ``rapid_verify`` -- RAPID verification (RAPID notes, key designs 2-4):
   augmented target with tail protection, rejection test against it, and the
   adjusted residual draw from caller-supplied uniforms.
@@ -50,7 +53,19 @@ SYMBOLS = ("vwl_status_string", "vwl_version", "vwl_workspace_reset",
            "vwl_asym_workspace_bytes", "asym_verify", "asym_verify_variant", "vwl_asym_plan_info",
            "vwl_rapid_workspace_bytes", "rapid_verify",
            "vwl_plan_info", "vwl_asym_check", "vwl_rapid_check",
-           "vwl_set_plan_override", "vwl_set_phase_event")
+           "vwl_set_plan_override", "vwl_set_phase_event",
+           "vwl_e2sci_workspace_bytes", "e2sci_verify", "vwl_e2sci_plan_info")
+
+
+class E2sciParams(ctypes.Structure):
+    """vwl_e2sci_params: constants of the E2-SCI threshold update.  The page
+    prints only the EWMA decay (0.3); the defaults of the others are this
+    binding's choice."""
+    _fields_ = [("alpha", ctypes.c_float), ("tau_credit", ctypes.c_float), ("T_base", ctypes.c_float),
+                ("T_min", ctypes.c_float), ("T_max", ctypes.c_float), ("ewma", ctypes.c_float)]
+
+    def __init__(self, alpha=1.0, tau_credit=0.5, T_base=0.1, T_min=0.01, T_max=0.3, ewma=0.3):
+        super().__init__(alpha, tau_credit, T_base, T_min, T_max, ewma)
 
 
 class VwlError(RuntimeError):
@@ -98,6 +113,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.vwl_rapid_check.restype = i
         lib.vwl_set_plan_override.argtypes = [i, i, i]
         lib.vwl_set_plan_override.restype = i
+        lib.vwl_e2sci_workspace_bytes.argtypes = [i, i, i, i]
+        lib.vwl_e2sci_workspace_bytes.restype = sz
+        lib.e2sci_verify.argtypes = [P, P, i, i, i, i, P, P, P, ctypes.POINTER(E2sciParams),
+                                     P, P, P, P, P, P, sz, P]
+        lib.e2sci_verify.restype = i
+        lib.vwl_e2sci_plan_info.argtypes = [i, i, i, i, ctypes.POINTER(ctypes.c_int64)]
+        lib.vwl_e2sci_plan_info.restype = i
         lib.vwl_set_phase_event.argtypes = [P]
         lib.vwl_set_phase_event.restype = i
         _lib = lib
@@ -141,9 +163,13 @@ _ws_lock = threading.Lock()
 def _workspace(mode: int, B: int, K: int, V: int, dt: int, device, stream) -> torch.Tensor:
     lib = load_library()
     need = (lib.vwl_asym_workspace_bytes if mode == 0 else lib.vwl_rapid_workspace_bytes)(B, K, V, dt)
+    return _workspace_sized((mode, B, K, V, dt), need, device, stream)
+
+
+def _workspace_sized(shape_key, need: int, device, stream) -> torch.Tensor:
     if need == 0:
         _check(2)
-    key = (device.index, stream.cuda_stream, mode, B, K, V, dt)
+    key = (device.index, stream.cuda_stream) + tuple(shape_key)
     with _ws_lock:
         ws = _ws_cache.get(key)
         if ws is None:
@@ -288,6 +314,63 @@ def asym_verify_variant(a: Optional[torch.Tensor], b: torch.Tensor, t: torch.Ten
                                    _ptr(ws), ws.numel(), ctypes.c_void_p(stream.cuda_stream))
     _check(code)
     return out
+
+
+class E2sciOut(NamedTuple):
+    D: torch.Tensor           # [B, W] float32
+    accept: torch.Tensor      # [B, W] uint8
+    accept_len: torch.Tensor  # [B] int32
+    T_next: torch.Tensor      # [B] float32 threshold of the next window
+    r_hat: torch.Tensor       # [B] float32 credit state (updated in place)
+    dev_err: torch.Tensor     # [1] int32
+
+
+def e2sci_plan_info(B: int, W: int, V: int, dtype: torch.dtype) -> dict:
+    lib = load_library()
+    out = (ctypes.c_int64 * 6)()
+    dt = VWL_BF16 if dtype == torch.bfloat16 else VWL_F32
+    _check(lib.vwl_e2sci_plan_info(B, W, V, dt, out))
+    return {"team": out[0], "vec_per_thread": out[1], "teams": out[2], "grid": out[3],
+            "threads": out[4], "rows": out[5]}
+
+
+def e2sci_verify(y: torch.Tensor, z: torch.Tensor, T: torch.Tensor, omega: torch.Tensor,
+                 r_hat: torch.Tensor, params: Optional[E2sciParams] = None, *,
+                 T_out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> E2sciOut:
+    """E2-SCI adaptive JSD acceptance of one window per request on the
+    current stream.  y: drafter logits, z: target logits, [B, W, V];
+    T, omega, r_hat: [B] float32 device tensors (r_hat is updated in place);
+    the next thresholds go to T_out (a new tensor when None; pass T itself to
+    update in place)."""
+    lib = load_library()
+    _dev_tensor(y, "y")
+    dt = _dt(y)
+    _dev_tensor(z, "z", y.dtype)
+    if y.dim() != 3 or z.shape != y.shape:
+        raise ValueError("y and z must share one [B, W, V] shape")
+    B, Wn, V = y.shape
+    for name, x in (("T", T), ("omega", omega), ("r_hat", r_hat)):
+        _dev_tensor(x, name, torch.float32)
+        if tuple(x.shape) != (B,):
+            raise ValueError("%s must be [B]" % name)
+    if T_out is None:
+        T_out = torch.empty(B, dtype=torch.float32, device=y.device)
+    _dev_tensor(T_out, "T_out", torch.float32)
+    params = params if params is not None else E2sciParams()
+    kw = dict(device=y.device)
+    D = torch.empty(B, Wn, dtype=torch.float32, **kw)
+    acc = torch.empty(B, Wn, dtype=torch.uint8, **kw)
+    alen = torch.empty(B, dtype=torch.int32, **kw)
+    err = torch.zeros(1, dtype=torch.int32, **kw)
+    stream = torch.cuda.current_stream(y.device)
+    if workspace is None:
+        need = int(lib.vwl_e2sci_workspace_bytes(B, Wn, V, dt))
+        workspace = _workspace_sized(("e2sci", B, Wn, V, dt), need, y.device, stream)
+    code = lib.e2sci_verify(_ptr(y), _ptr(z), B, Wn, V, dt, _ptr(T), _ptr(omega), _ptr(r_hat),
+                            ctypes.byref(params), _ptr(D), _ptr(acc), _ptr(alen), _ptr(T_out), _ptr(err),
+                            _ptr(workspace), workspace.numel(), ctypes.c_void_p(stream.cuda_stream))
+    _check(code)
+    return E2sciOut(D, acc, alen, T_out, r_hat, err)
 
 
 class RapidOut(NamedTuple):

@@ -8,6 +8,8 @@
 //         (no divergence: the JSD pass and the team wait are skipped, and a
 //         is not read at all when delta = t - b)
 // Each translation unit asym_<delta>.hip instantiates one fusion source.
+// DS = kDeltaNone reads only a and b (no verifier row, no fused token): the
+// two-tensor divergence pass of E2-SCI's adaptive acceptance (e2sci.hip).
 //
 // Launch 1, asym_rows_kernel: each logit row (one draft position of one
 // request: a_i, b_i, t_i) is split over a team of W workgroups; each
@@ -61,6 +63,8 @@ template <int DS, int GATE>
 struct AsymUse {
     static constexpr bool kLseA = GATE == kGateCda;
     static constexpr bool kReadA = kLseA || DS != kDeltaTMinusB;
+    static constexpr bool kReadT = DS != kDeltaNone; // the verifier row and the fused token
+    static constexpr int kTensors = kReadT ? 3 : 2;
 };
 
 // JSD term of one element.  With x = ln p - ln q (nats), d = |x| log2e,
@@ -204,9 +208,9 @@ __device__ __forceinline__ double rescale_to(const OnlineLse &st, float C) {
 // LDS staging of one row's chunk: [tensor][vector slot][thread], 16 bytes
 // each.  Every lane later reads back exactly the vectors it issued itself,
 // so only its own wave's loads have to be complete.
-template <int NV>
+template <int NV, int NT>
 struct AsymStage {
-    uint4 v[3][NV][kThreads];
+    uint4 v[NT][NV][kThreads];
 };
 
 // Direct global -> LDS load of one 16-byte vector per lane (the LDS address
@@ -218,14 +222,14 @@ __device__ __forceinline__ void g2lds16(const uint4 *src, uint4 *lds_wave_base) 
 }
 
 // Stream row r's chunk into LDS (waves 1-3: wave x+1 issues all of tensor x;
-// wave 1 idles when a is not read).
-template <int DT, int NV, bool READ_A>
-__device__ __forceinline__ void prefetch_bulk(AsymStage<NV> &stage, long long r, int V, int W, int member, int chunk,
-                                              const uint4 *A4, const uint4 *B4, const uint4 *T4) {
+// wave 1 idles when a is not read, wave 3 when t is not).
+template <int DT, int NV, int NT, bool READ_A>
+__device__ __forceinline__ void prefetch_bulk(AsymStage<NV, NT> &stage, long long r, int V, int W, int member,
+                                              int chunk, const uint4 *A4, const uint4 *B4, const uint4 *T4) {
     const int lane = threadIdx.x & 63;
     const RowSplit<DT> s = row_split<DT>(r, V, W, member, chunk);
     const int x = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) - 1;
-    if (!READ_A && x == 0)
+    if ((!READ_A && x == 0) || x >= NT)
         return;
     const uint4 *base = T4;
     if (x == 0)
@@ -256,7 +260,7 @@ __device__ __forceinline__ void prefetch_bulk(AsymStage<NV> &stage, long long r,
 }
 
 // Head/tail scalars of row r (wave 0's first lanes), widened to fp32.
-template <int DT, bool READ_A>
+template <int DT, bool READ_A, bool READ_T>
 __device__ __forceinline__ void prefetch_scalars(long long r, int V, int W, int member, int chunk, const void *a,
                                                  const void *b, const void *t, float &na, float &nb, float &nt) {
     const RowSplit<DT> s = row_split<DT>(r, V, W, member, chunk);
@@ -265,7 +269,51 @@ __device__ __forceinline__ void prefetch_scalars(long long r, int V, int W, int 
         if (READ_A)
             na = load_scalar<DT>(a, off);
         nb = load_scalar<DT>(b, off);
-        nt = load_scalar<DT>(t, off);
+        if (READ_T)
+            nt = load_scalar<DT>(t, off);
+    }
+}
+
+// Pass AB of the two-tensor (divergence only) kind: online softmax
+// statistics of a and b, reduced over the workgroup; thread 0 publishes
+// record words 0, 1 (sums) and 3 (references).
+template <int DT, int NV>
+__device__ __forceinline__ void pair_pass_ab(const AsymParams &P, long long row, int member, const RowSplit<DT> &sp,
+                                             const uint4 (&ra)[NV], const uint4 (&rb)[NV], float sa, float sb,
+                                             float *lds_f, double *lds_d) {
+    constexpr int EPV = Elem<DT>::kPerVec;
+    const int tid = threadIdx.x;
+    OnlineLse la, lb;
+    online_init(la);
+    online_init(lb);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        if (tid + j * kThreads < sp.nv) {
+            float xa[EPV], xb[EPV];
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) {
+                xa[e] = widen<DT>(ra[j], e);
+                xb[e] = widen<DT>(rb[j], e);
+            }
+            online_group<EPV>(la, xa);
+            online_group<EPV>(lb, xb);
+        }
+    }
+    if (tid < sp.nsc) {
+        const float x1a[1] = {sa}, x1b[1] = {sb};
+        online_group<1>(la, x1a);
+        online_group<1>(lb, x1b);
+    }
+    float mx[2] = {la.c, lb.c};
+    block_max<2>(mx, lds_f);
+    double S[2] = {rescale_to(la, mx[0]), rescale_to(lb, mx[1])};
+    block_sum<2>(S, lds_d);
+    if (tid == 0) {
+        uint64_t *rec = P.rec + ((size_t)row * P.Wmax + member) * kRecWords;
+        st_relaxed(rec + 0, f64_bits(S[0]));
+        st_relaxed(rec + 1, f64_bits(S[1]));
+        st_relaxed(rec + 3, pack2(mx[0], mx[1]));
+        publish_add_nr(P.row_ctr + (size_t)row * 16, 1u);
     }
 }
 
@@ -352,19 +400,23 @@ __device__ __forceinline__ void asym_pass_ab(const AsymParams &P, long long row,
 
 // Resident waves per SIMD the row kernel is built for: the CDA variants keep
 // a pending row's a and b in registers across the team wait.
-template <int NV, int GATE>
+template <int NV, int DS, int GATE>
 constexpr int asym_rows_waves() {
-    if constexpr (GATE == kGateCda)
+    if constexpr (DS == kDeltaNone)
+        return NV <= 2 ? 4 : NV <= 4 ? 3 : 2;
+    else if constexpr (GATE == kGateCda)
         return NV <= 1 ? 4 : NV <= 4 ? 3 : 2;
     else
         return NV <= 4 ? 4 : 3;
 }
 
 template <int DT, int NV, int DS, int GATE>
-__global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, GATE>())) void asym_rows_kernel(AsymParams P) {
+__global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, DS, GATE>())) void asym_rows_kernel(AsymParams P) {
     constexpr int EPV = Elem<DT>::kPerVec;
     constexpr bool READ_A = AsymUse<DS, GATE>::kReadA;
-    __shared__ AsymStage<NV> stage;
+    constexpr bool READ_T = AsymUse<DS, GATE>::kReadT;
+    constexpr int NT = AsymUse<DS, GATE>::kTensors;
+    __shared__ AsymStage<NV, NT> stage;
     __shared__ float lds_f[kWaves * 4];
     __shared__ double lds_d[kWaves * 3];
     __shared__ int lds_i[kWaves];
@@ -392,9 +444,9 @@ __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, GATE>())) void asym_
     // pending row waits for its team while the next row's passes A+B run.
     auto issue = [&](long long r) {
         if (!wave0)
-            prefetch_bulk<DT, NV, READ_A>(stage, r, V, W, member, P.chunk, A4, B4, T4);
+            prefetch_bulk<DT, NV, NT, READ_A>(stage, r, V, W, member, P.chunk, A4, B4, T4);
         else
-            prefetch_scalars<DT, READ_A>(r, V, W, member, P.chunk, P.a, P.b, P.t, na, nb, nt);
+            prefetch_scalars<DT, READ_A, READ_T>(r, V, W, member, P.chunk, P.a, P.b, P.t, na, nb, nt);
     };
     uint4 ra[NV], rb[NV], rt[NV];
     float sa, sb, st;
@@ -406,7 +458,8 @@ __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, GATE>())) void asym_
             if (READ_A)
                 ra[j] = stage.v[0][j][tid];
             rb[j] = stage.v[1][j][tid];
-            rt[j] = stage.v[2][j][tid];
+            if (READ_T)
+                rt[j] = stage.v[NT - 1][j][tid];
         }
         sa = na;
         sb = nb;
@@ -415,12 +468,20 @@ __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, GATE>())) void asym_
     };
 
     long long row = team;
+    RowSplit<DT> sp;
+    auto pass_ab = [&](long long r) {
+        if constexpr (READ_T)
+            asym_pass_ab<DT, NV, DS, GATE>(P, r, member, sp, ra, rb, rt, sa, sb, st, lds_f, lds_d, lds_i);
+        else
+            pair_pass_ab<DT, NV>(P, r, member, sp, ra, rb, sa, sb, lds_f, lds_d);
+    };
+
     issue(row);
     take();
     if (row + P.n_teams < P.R)
         issue(row + P.n_teams);
-    RowSplit<DT> sp = row_split<DT>(row, V, W, member, P.chunk);
-    asym_pass_ab<DT, NV, DS, GATE>(P, row, member, sp, ra, rb, rt, sa, sb, st, lds_f, lds_d, lds_i);
+    sp = row_split<DT>(row, V, W, member, P.chunk);
+    pass_ab(row);
     if constexpr (GATE == kGateFixed) {
         // no divergence: each row is one pass, with the next row streaming in
         for (long long next = row + P.n_teams; next < P.R; next += P.n_teams) {
@@ -428,7 +489,7 @@ __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, GATE>())) void asym_
             if (next + P.n_teams < P.R)
                 issue(next + P.n_teams);
             sp = row_split<DT>(next, V, W, member, P.chunk);
-            asym_pass_ab<DT, NV, DS, GATE>(P, next, member, sp, ra, rb, rt, sa, sb, st, lds_f, lds_d, lds_i);
+            pass_ab(next);
         }
         return;
     }
@@ -450,7 +511,7 @@ __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, GATE>())) void asym_
             if (next + P.n_teams < P.R)
                 issue(next + P.n_teams);
             sp = row_split<DT>(next, V, W, member, P.chunk);
-            asym_pass_ab<DT, NV, DS, GATE>(P, next, member, sp, ra, rb, rt, sa, sb, st, lds_f, lds_d, lds_i);
+            pass_ab(next);
         }
 
         // ---- the pending row: wait for its team, then pass C ----
@@ -603,10 +664,17 @@ static int blocks_per_cu_nv(int nv) {
 
 template <int DS>
 int asym_blocks_per_cu_ds(int dt, int nv, int gate) {
-    if (dt == DT_BF16)
-        return gate == kGateCda ? blocks_per_cu_nv<DT_BF16, DS, kGateCda>(nv)
-                                : blocks_per_cu_nv<DT_BF16, DS, kGateFixed>(nv);
-    return gate == kGateCda ? blocks_per_cu_nv<DT_F32, DS, kGateCda>(nv) : blocks_per_cu_nv<DT_F32, DS, kGateFixed>(nv);
+    if constexpr (DS == kDeltaNone) { // the divergence pass exists under the CDA kind only
+        if (gate != kGateCda)
+            return 0;
+        return dt == DT_BF16 ? blocks_per_cu_nv<DT_BF16, DS, kGateCda>(nv) : blocks_per_cu_nv<DT_F32, DS, kGateCda>(nv);
+    } else {
+        if (dt == DT_BF16)
+            return gate == kGateCda ? blocks_per_cu_nv<DT_BF16, DS, kGateCda>(nv)
+                                    : blocks_per_cu_nv<DT_BF16, DS, kGateFixed>(nv);
+        return gate == kGateCda ? blocks_per_cu_nv<DT_F32, DS, kGateCda>(nv)
+                                : blocks_per_cu_nv<DT_F32, DS, kGateFixed>(nv);
+    }
 }
 
 template <int DT, int NV, int DS, int GATE>

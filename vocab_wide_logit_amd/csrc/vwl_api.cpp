@@ -31,6 +31,7 @@ int asym_blocks_per_cu(int dt, int nv, int ds, int gate) {
     case kDeltaAMinusB: return asym_blocks_per_cu_ds<kDeltaAMinusB>(dt, nv, gate);
     case kDeltaA: return asym_blocks_per_cu_ds<kDeltaA>(dt, nv, gate);
     case kDeltaTMinusB: return asym_blocks_per_cu_ds<kDeltaTMinusB>(dt, nv, gate);
+    case kDeltaNone: return asym_blocks_per_cu_ds<kDeltaNone>(dt, nv, gate);
     }
     return 0;
 }
@@ -50,7 +51,7 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 struct DeviceInfo {
     bool ready = false;
     int cus = 0;
-    int asym_bpc[2][4][3][2] = {}; // [dtype][nv][delta source][gate]
+    int asym_bpc[2][4][4][2] = {}; // [dtype][nv][delta source or kDeltaNone][gate]
     int rapid_bpc[2][4] = {};
 };
 constexpr int kMaxDevices = 64;
@@ -75,7 +76,7 @@ const DeviceInfo *device_info() {
         d.cus = cus;
         for (int dt = 0; dt < 2; ++dt)
             for (int k = 0; k < 4; ++k) {
-                for (int ds = 0; ds < 3; ++ds)
+                for (int ds = 0; ds < 4; ++ds)
                     for (int g = 0; g < 2; ++g)
                         d.asym_bpc[dt][k][ds][g] = asym_blocks_per_cu(dt, kNvChoices[k], ds, g);
                 d.rapid_bpc[dt][k] = rapid_blocks_per_cu(dt, kNvChoices[k]);
@@ -395,6 +396,95 @@ vwl_status asym_verify(const void *a, const void *b, const void *t, const int32_
     return asym_verify_variant(a, b, t, draft, B, K, V, dt, beta, gamma, VWL_DELTA_A_MINUS_B, VWL_GATE_CDA, D,
                                gamma_eff, accept, fused, accept_len, token, dev_err, workspace, workspace_bytes,
                                stream);
+}
+
+size_t vwl_e2sci_workspace_bytes(int B, int W, int V, vwl_dtype dt) {
+    if (W < 1 || !shape_ok(B, W - 1, V) || (dt != VWL_F32 && dt != VWL_BF16))
+        return 0;
+    return ws_layout(B, W, V, elem_bytes(dt), false).total;
+}
+
+vwl_status e2sci_verify(const void *y, const void *z, int B, int W, int V, vwl_dtype dt,
+                        const float *T_in, const float *omega, float *r_hat, const vwl_e2sci_params *params,
+                        float *D, uint8_t *accept, int32_t *accept_len, float *T_out,
+                        int32_t *dev_err, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!y || !z || !T_in || !omega || !r_hat || !params || !D || !accept || !accept_len || !T_out)
+        return VWL_ERR_NULL;
+    if (W < 1 || !shape_ok(B, W - 1, V))
+        return VWL_ERR_SHAPE;
+    if (dt != VWL_F32 && dt != VWL_BF16)
+        return VWL_ERR_DTYPE;
+    const vwl_e2sci_params &q = *params;
+    if (!finite_f(q.alpha) || !finite_f(q.tau_credit) || !finite_f(q.T_base) || !finite_f(q.T_min) ||
+        !finite_f(q.T_max) || !(q.T_min <= q.T_max) || !(q.ewma >= 0.0f && q.ewma <= 1.0f))
+        return VWL_ERR_PARAM;
+    if (!aligned(y, 16) || !aligned(z, 16) || !aligned(T_in, 4) || !aligned(omega, 4) || !aligned(r_hat, 4) ||
+        !aligned(D, 4) || !aligned(accept_len, 4) || !aligned(T_out, 4) || (dev_err && !aligned(dev_err, 4)))
+        return VWL_ERR_ALIGN;
+    const size_t need = vwl_e2sci_workspace_bytes(B, W, V, dt);
+    if (!workspace || workspace_bytes < need)
+        return VWL_ERR_WORKSPACE;
+    if (!aligned(workspace, 256))
+        return VWL_ERR_ALIGN;
+    const long long R = (long long)B * W;
+    Plan plan;
+    if (!make_plan(0, (int)dt, R, V, plan, kDeltaNone, kGateCda))
+        return VWL_ERR_HIP;
+    const WsLayout L = ws_layout(B, W, V, elem_bytes(dt), false);
+    char *ws = static_cast<char *>(workspace);
+    AsymParams p{};
+    p.a = y;
+    p.b = z;
+    p.t = nullptr;
+    p.R = R;
+    p.B = B;
+    p.K = W - 1;
+    p.V = V;
+    p.W = plan.W;
+    p.n_teams = plan.n_teams;
+    p.Wmax = L.Wmax;
+    p.chunk = member_chunk(V, (int)dt, plan.W);
+    p.D = D;
+    p.accept = accept;
+    p.acc_len = accept_len;
+    p.dev_err = dev_err;
+    p.ctl = reinterpret_cast<uint32_t *>(ws + L.ctl);
+    p.row_ctr = reinterpret_cast<uint32_t *>(ws + L.row_ctr);
+    p.req_ctr = reinterpret_cast<uint32_t *>(ws + L.req_ctr);
+    p.row_info = reinterpret_cast<uint32_t *>(ws + L.row_info);
+    p.rec = reinterpret_cast<uint64_t *>(ws + L.rec);
+    p.win = W;
+    p.thr_in = T_in;
+    p.omega = omega;
+    p.r_hat = r_hat;
+    p.thr_out = T_out;
+    p.e_alpha = q.alpha;
+    p.e_tau = q.tau_credit;
+    p.e_Tbase = q.T_base;
+    p.e_Tmin = q.T_min;
+    p.e_Tmax = q.T_max;
+    p.e_ewma = q.ewma;
+    return launch_e2sci((int)dt, plan, p, stream, g_phase_event.load()) == hipSuccess ? VWL_OK : VWL_ERR_HIP;
+}
+
+vwl_status vwl_e2sci_plan_info(int B, int W, int V, vwl_dtype dt, int64_t out[6]) {
+    if (!out)
+        return VWL_ERR_NULL;
+    if (W < 1 || !shape_ok(B, W - 1, V))
+        return VWL_ERR_SHAPE;
+    if (dt != VWL_F32 && dt != VWL_BF16)
+        return VWL_ERR_DTYPE;
+    Plan plan;
+    const long long R = (long long)B * W;
+    if (!make_plan(0, dt, R, V, plan, kDeltaNone, kGateCda))
+        return VWL_ERR_HIP;
+    out[0] = plan.W;
+    out[1] = plan.nv;
+    out[2] = plan.n_teams;
+    out[3] = plan.grid;
+    out[4] = kThreads;
+    out[5] = R;
+    return VWL_OK;
 }
 
 vwl_status rapid_verify(const void *z, const void *y, const int32_t *draft,

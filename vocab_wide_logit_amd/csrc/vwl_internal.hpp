@@ -85,6 +85,11 @@ struct AsymParams {
     int32_t *fused, *acc_len, *token, *dev_err;
     uint32_t *ctl, *row_ctr, *req_ctr, *row_info;
     uint64_t *rec;
+    // E2-SCI (a = drafter y, b = target z; `win` rows per request)
+    int win;
+    const float *thr_in, *omega;
+    float *r_hat, *thr_out;
+    double e_alpha, e_tau, e_Tbase, e_Tmin, e_Tmax, e_ewma;
 };
 
 struct RapidParams {
@@ -115,8 +120,9 @@ struct Plan {
     int grid;
 };
 
-// AsymSpec variants (values match vwl_delta_source / vwl_gate of the C ABI).
-enum { kDeltaAMinusB = 0, kDeltaA = 1, kDeltaTMinusB = 2 };
+// AsymSpec variants (values match vwl_delta_source / vwl_gate of the C ABI);
+// kDeltaNone is the two-tensor divergence pass of E2-SCI.
+enum { kDeltaAMinusB = 0, kDeltaA = 1, kDeltaTMinusB = 2, kDeltaNone = 3 };
 enum { kGateCda = 0, kGateFixed = 1 };
 
 // Launchers (return hipSuccess or the launch error).
@@ -126,6 +132,7 @@ enum { kGateCda = 0, kGateFixed = 1 };
 template <int DS>
 hipError_t launch_asym_ds(int dt, int gate, const Plan &plan, const AsymParams &p, hipStream_t s,
                           hipEvent_t after_rows);
+hipError_t launch_e2sci(int dt, const Plan &plan, const AsymParams &p, hipStream_t s, hipEvent_t after_rows);
 hipError_t launch_rapid(int dt, const Plan &plan, const RapidParams &p, hipStream_t s, hipEvent_t after_rows);
 hipError_t launch_fill_zero(void *ptr, size_t bytes, hipStream_t s);
 

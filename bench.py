@@ -5,9 +5,11 @@ One step = one ``asym_verify`` call over the large batched AsymSpec workload
 inputs resident in HBM.  Prints one JSON line: verified logit rows/s; the
 dominant kernel's roofline (algorithmic HBM bytes per launch over its
 event-timed duration, against 8 TB/s, with the measured traffic of the
-committed counter summary while the kernel sources still match it); the
-B=64/K=2 workload and the RAPID pass as secondary figures; and the fp64 CPU
-oracle timed on the host as a reported baseline.
+committed counter summary while the kernel sources still match it, and its
+VALU issue from the committed SQ summary); as secondary figures the B=64/K=2
+workload, the RAPID pass, the AsymSpec ablation variants on the large
+workload and the E2-SCI adaptive acceptance on B=64 and B=1 windows; and the
+fp64 CPU oracle timed on the host as a reported baseline.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu-baseline]
                     [--no-extra] [--calib-copy]
@@ -109,6 +111,38 @@ def time_rapid(vwl, x, steps, warmup):
         start[i].record(stream)
         vwl.set_phase_event(mid[i])
         vwl.rapid_verify(z, y, d, ua, us, x.eta, x.T, out=out)
+        end[i].record(stream)
+    torch.cuda.synchronize()
+    vwl.set_phase_event(None)
+    return ([s.elapsed_time(e) for s, e in zip(start, end)],
+            [s.elapsed_time(m) for s, m in zip(start, mid)])
+
+
+def time_e2sci(vwl, x, steps, warmup, copies=4):
+    """e2sci_verify calls with the state carried on the device (thresholds
+    updated in place), rotating `copies` input sets; per-call and row-kernel
+    ms from events, as for the AsymSpec pass."""
+    import torch
+    sets = [(vwl.to_device_logits(x.y, x.dtype), vwl.to_device_logits(x.z, x.dtype))]
+    for _ in range(1, copies):
+        sets.append(tuple(t.clone() for t in sets[0]))
+    T = torch.from_numpy(x.T.copy()).cuda()
+    om = torch.from_numpy(x.omega.copy()).cuda()
+    rh = torch.from_numpy(x.r_hat.copy()).cuda()
+    prm = vwl.E2sciParams()
+    for i in range(warmup):
+        y, z = sets[i % copies]
+        vwl.e2sci_verify(y, z, T, om, rh, prm, T_out=T)
+    stream = torch.cuda.current_stream()
+    start, mid, end = _events(steps), _events(steps), _events(steps)
+    for e in mid:
+        e.record(stream)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        y, z = sets[i % copies]
+        start[i].record(stream)
+        vwl.set_phase_event(mid[i])
+        vwl.e2sci_verify(y, z, T, om, rh, prm, T_out=T)
         end[i].record(stream)
     torch.cuda.synchronize()
     vwl.set_phase_event(None)
@@ -245,7 +279,8 @@ def main():
             "floor_ms_at_full_issue": float(valu["valu_cycles_per_simd"]) / 2.4e9 * 1e3,
             "source": os.path.relpath(VALU_SUMMARY, ROOT)}
     if not args.no_extra:
-        _say("secondary: B=64 K=2 bf16 (4 rotating input sets), RAPID B=16 G=10 fp32, stream reference")
+        _say("secondary: B=64 K=2 bf16 (4 rotating input sets), RAPID B=16 G=10 fp32, stream reference, "
+             "ablation variants, E2-SCI windows")
         x2 = W.batched_asym()
         _, per2, rows2 = time_asym(vwl, x2, args.steps, args.warmup, copies=4)
         ms2 = _median(per2)
@@ -278,6 +313,14 @@ def main():
                       "gbs": b3 / (ms3 * 1e-3) / 1e9, "frac_of_peak": b3 / (ms3 * 1e-3) / 1e9 / PEAK_HBM_GBS,
                       "eta": r3.eta},
         }
+        for xe in (W.e2sci_batched(), W.e2sci_single()):
+            pe, re_ = time_e2sci(vwl, xe, args.steps, args.warmup)
+            me, mre = _median(pe), _median(re_)
+            be = xe.algorithmic_bytes()
+            result["secondary"][xe.name] = {
+                "rows_per_s": xe.B * xe.W / (me * 1e-3), "median_call_ms": me, "median_row_kernel_ms": mre,
+                "row_kernel_gbs": be / (mre * 1e-3) / 1e9, "frac_of_peak": be / (mre * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                "plan": vwl.e2sci_plan_info(xe.B, xe.W, xe.V, torch.bfloat16)}
     if not args.no_cpu_baseline:
         _say("timing the fp64 oracle on the host")
         result["cpu_baseline"] = cpu_baseline(x)

@@ -19,6 +19,10 @@ with ctypes and marshals numpy arrays.  Each entry point follows the pages:
   ``phat = softmax(zhat/T)``), key design 3 (tail protection below 10% of the
   peak) and key design 4 (residual ``norm(max(p - phat, p - q, 0))``), with
   rejection sampling against the augmented target (overall framework).
+* ``asym_xfam`` -- the AsymSpec pass across model families (AsymSpec
+  notes, analysis of cross-family pairs): the drafter's gain reaches the
+  verifier through a vocabulary alignment, generation restricted to the
+  paired tokens.
 * ``e2sci`` -- E2-SCI notes, key design 3 (online adaptive verification:
   per-position JSD of drafter and target against the window's threshold,
   the EWMA credit state r = (1-beta) r + beta * accept_len/W, and the next
@@ -78,6 +82,8 @@ def _load():
     lib.vwl_oracle_rapid_zhat.restype = i
     lib.vwl_oracle_rapid_phat.argtypes = [P, P, i, d, d, P]
     lib.vwl_oracle_rapid_phat.restype = i
+    lib.vwl_oracle_asym_xfam.argtypes = [P, P, i, P, i, P, i, P, i, i, d, d, P, P, P, P, P, P, P, P, P, P, i]
+    lib.vwl_oracle_asym_xfam.restype = i
     lib.vwl_oracle_e2sci.argtypes = [P, P, i, i, i, i, P, P, P, d, d, d, d, d, d, P, P, P, P, P, i]
     lib.vwl_oracle_e2sci.restype = i
     lib.vwl_oracle_max_threads.argtypes = []
@@ -159,6 +165,41 @@ def asym(a, b, t, draft, beta: float, gamma: float, dtype: str = "f32",
     if rc != 0:
         raise RuntimeError("oracle asym failed with code %d" % rc)
     del R
+    return AsymResult(lse, D, ge, fused, gap, top, acc, margin, alen, tok)
+
+
+def asym_xfam(a, b, t, vmap, draft, beta: float, gamma: float, dtype: str = "f32",
+              nthreads: int = 0) -> AsymResult:
+    """Oracle of the cross-family AsymSpec pass: drafter rows a, b [B, K+1, Vd],
+    verifier rows t [B, K+1, Vt], vmap [Vt] (drafter id paired with each
+    verifier token, or -1), drafts [B, K] in verifier ids."""
+    lib = _load()
+    sa, dt = _stored(a, dtype)
+    sb, _ = _stored(b, dtype)
+    st, _ = _stored(t, dtype)
+    B, P, Vd = sa.shape
+    Vt = st.shape[2]
+    if st.shape[:2] != (B, P) or sb.shape != sa.shape:
+        raise ValueError("a, b must be [B, K+1, Vd] and t [B, K+1, Vt]")
+    K = P - 1
+    vmap = np.ascontiguousarray(vmap, dtype=np.int32).reshape(Vt)
+    draft = np.ascontiguousarray(draft, dtype=np.int32).reshape(B, K)
+    lse = np.zeros((B, P, 3))
+    D = np.zeros((B, P))
+    ge = np.zeros((B, P))
+    fused = np.zeros((B, P), np.int32)
+    gap = np.zeros((B, P))
+    top = np.zeros((B, P))
+    acc = np.zeros((B, max(K, 0)), np.uint8)
+    margin = np.zeros((B, max(K, 0)))
+    alen = np.zeros(B, np.int32)
+    tok = np.zeros(B, np.int32)
+    rc = lib.vwl_oracle_asym_xfam(_ptr(sa), _ptr(sb), Vd, _ptr(st), Vt, _ptr(vmap), dt, _ptr(draft), B, K,
+                                  float(np.float32(beta)), float(np.float32(gamma)),
+                                  _ptr(lse), _ptr(D), _ptr(ge), _ptr(fused), _ptr(gap), _ptr(top),
+                                  _ptr(acc), _ptr(margin), _ptr(alen), _ptr(tok), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle asym_xfam failed with code %d" % rc)
     return AsymResult(lse, D, ge, fused, gap, top, acc, margin, alen, tok)
 
 

@@ -467,6 +467,118 @@ int vwl_oracle_rapid(const void *z, const void *y, int dtype,
 }
 
 /* ======================================================================
+ * AsymSpec across model families (AsymSpec reading notes, the analysis of
+ * why cross-family pairs work at a discount): the drafter's context gain
+ * lives on the drafter's vocabulary and reaches the verifier through a
+ * vocabulary alignment of string-identical tokens (plus paired special
+ * tokens), with generation restricted to that shared subset.
+ *
+ * Inputs: a, b [B][K+1][Vd] drafter rows; t [B][K+1][Vt] verifier rows;
+ * vmap[Vt]: the drafter id paired with each verifier token, or -1; draft
+ * [B][K] in verifier ids.  Per row:
+ *   La, Lb over the drafter vocabulary, Lt over the verifier's;
+ *   D = JSD(softmax(a) || softmax(b)) on the drafter vocabulary;
+ *   fused = lowest verifier id v with vmap[v] >= 0 maximising
+ *           t[v] + beta * (a[vmap[v]] - b[vmap[v]])   (-1 if none is paired);
+ *   accept: d = draft, paired e = vmap[d]:
+ *           softmax(t)[d] > gamma * exp(-D) * softmax(b)[e]; a draft outside
+ *           [0, Vt) or without a pair is rejected.
+ * Outputs as vwl_oracle_asym (lse[R][3] = La, Lb, Lt).
+ * ====================================================================== */
+int vwl_oracle_asym_xfam(const void *a, const void *b, int Vd, const void *t, int Vt,
+                         const int32_t *vmap, int dtype, const int32_t *draft, int B, int K,
+                         double beta, double gamma,
+                         double *lse, double *D, double *geff, int32_t *fused, double *gap,
+                         double *top, uint8_t *accept, double *margin,
+                         int32_t *accept_len, int32_t *token, int nthreads)
+{
+    if (B < 1 || K < 0 || Vd < 1 || Vt < 1 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16))
+        return 1;
+    const int P = K + 1;
+    const long R = (long)B * P;
+    set_threads(nthreads);
+    int bad_alloc = 0;
+#pragma omp parallel
+    {
+        double *xa = malloc(sizeof(double) * (size_t)Vd);
+        double *xb = malloc(sizeof(double) * (size_t)Vd);
+        double *xt = malloc(sizeof(double) * (size_t)Vt);
+        if (!xa || !xb || !xt) {
+#pragma omp atomic write
+            bad_alloc = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (long r = 0; r < R; ++r) {
+                for (int v = 0; v < Vd; ++v) {
+                    xa[v] = widen(a, dtype, (size_t)r * (size_t)Vd + v);
+                    xb[v] = widen(b, dtype, (size_t)r * (size_t)Vd + v);
+                }
+                for (int v = 0; v < Vt; ++v)
+                    xt[v] = widen(t, dtype, (size_t)r * (size_t)Vt + v);
+                const double La = logsumexp(xa, Vd), Lb = logsumexp(xb, Vd), Lt = logsumexp(xt, Vt);
+                lse[3 * r + 0] = La;
+                lse[3 * r + 1] = Lb;
+                lse[3 * r + 2] = Lt;
+                const double Dr = jsd(xa, La, xb, Lb, Vd);
+                D[r] = Dr;
+                geff[r] = gamma * exp(-Dr);
+                /* fused token over the paired verifier tokens only */
+                double best = -INFINITY, second = -INFINITY;
+                int arg = -1;
+                for (int v = 0; v < Vt; ++v) {
+                    const int e = vmap[v];
+                    if (e < 0 || e >= Vd)
+                        continue;
+                    const double sc = xt[v] + beta * (xa[e] - xb[e]);
+                    if (arg < 0 || sc > best) {
+                        second = best;
+                        best = sc;
+                        arg = v;
+                    } else if (sc > second) {
+                        second = sc;
+                    }
+                }
+                fused[r] = arg;
+                gap[r] = (arg >= 0 && second > -INFINITY) ? best - second : INFINITY;
+                top[r] = best;
+                const long bi = r / P;
+                const int i = (int)(r % P);
+                if (i < K) {
+                    const int d = draft[bi * K + i];
+                    const int e = (d >= 0 && d < Vt) ? vmap[d] : -1;
+                    if (e < 0 || e >= Vd) {
+                        accept[bi * K + i] = 0;
+                        margin[bi * K + i] = NAN;
+                    } else {
+                        const double pt = exp(xt[d] - Lt);
+                        const double pb = exp(xb[e] - Lb);
+                        accept[bi * K + i] = (pt > geff[r] * pb) ? 1 : 0;
+                        margin[bi * K + i] = (xt[d] - Lt) - (xb[e] - Lb) - log(gamma) + Dr;
+                    }
+                }
+            }
+        }
+        free(xa);
+        free(xb);
+        free(xt);
+    }
+    if (bad_alloc)
+        return 2;
+    for (int bi = 0; bi < B; ++bi) {
+        int n = K;
+        for (int i = 0; i < K; ++i) {
+            if (!accept[(long)bi * K + i]) {
+                n = i;
+                break;
+            }
+        }
+        accept_len[bi] = n;
+        token[bi] = fused[(long)bi * P + n];
+    }
+    return 0;
+}
+
+/* ======================================================================
  * E2-SCI adaptive JSD acceptance ("E2-SCI: Elastic Edge-Cloud Speculative
  * Decoding via Credit Inertia" notes, key design 3 "online adaptive
  * verification", with the credit state of key design 1)

@@ -415,6 +415,85 @@ def test_fixed_gate_against_cda(oracle_lib):
     assert np.any(rc.accept > rf.accept)  # CDA does relax somewhere on these rows
 
 
+# ------------------------------------------------ AsymSpec across model families
+# AsymSpec notes, the analysis of cross-family pairs: the drafter's gain
+# reaches the verifier through a vocabulary alignment of string-identical
+# tokens, generation restricted to that shared subset.
+
+def test_xfam_identity_alignment_is_the_same_family_pass(oracle_lib):
+    """With one vocabulary and the identity alignment the cross-family pass
+    is the AsymSpec pass, bit for bit."""
+    x = W.gen_asym(5, 3, 777, "bf16", seed=60, identical_frac=0.2, tie_frac=0.2)
+    vmap = np.arange(777, dtype=np.int32)
+    r1 = oracle.asym_xfam(x.a, x.b, x.t, vmap, x.draft, 1.25, 0.5, "bf16")
+    r2 = oracle.asym(x.a, x.b, x.t, x.draft, 1.25, 0.5, "bf16")
+    for f in ("lse", "D", "gamma_eff", "fused", "gap", "top", "accept", "margin", "accept_len", "token"):
+        np.testing.assert_array_equal(getattr(r1, f), getattr(r2, f), err_msg=f)
+
+
+def test_xfam_relabelled_verifier_vocabulary(oracle_lib):
+    """Relabelling the verifier vocabulary (t'[v] = t[perm[v]], alignment
+    v -> perm[v], drafts mapped back) relabels the fused token and leaves
+    every other output unchanged."""
+    a, b, t, d = _rows(3, 2, 400, 61)
+    perm = np.random.default_rng(62).permutation(400).astype(np.int32)
+    inv = np.argsort(perm).astype(np.int32)
+    r1 = oracle.asym(a, b, t, d, 0.8, 0.6, "f32")
+    r2 = oracle.asym_xfam(a, b, np.ascontiguousarray(t[:, :, perm]), perm, inv[d], 0.8, 0.6, "f32")
+    np.testing.assert_array_equal(perm[r2.fused], r1.fused)
+    for f in ("D", "gamma_eff", "accept", "accept_len"):
+        np.testing.assert_array_equal(getattr(r1, f), getattr(r2, f), err_msg=f)
+    np.testing.assert_allclose(r2.margin, r1.margin, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(r2.lse, r1.lse, rtol=0, atol=1e-12)
+
+
+def test_xfam_unpaired_tokens_are_never_emitted_or_accepted(oracle_lib):
+    """Generation is restricted to the paired tokens: a verifier token with
+    no drafter pair is never the fused token, however large its logit, and a
+    draft on it is rejected; with no pair at all there is no fused token."""
+    x = W.gen_xfam(3, 2, 500, 450, 300, "f32", seed=63)
+    free = np.flatnonzero(x.vmap < 0)
+    t = x.t.copy()
+    t[:, :, free[0]] = 1e4
+    r = oracle.asym_xfam(x.a, x.b, t, x.vmap, x.draft, 1.0, 0.5, "f32")
+    assert np.all(x.vmap[r.fused] >= 0)
+    # the maximum over paired tokens, by brute force on the stored values
+    for bi in range(3):
+        for i in range(3):
+            s64 = np.full(450, -np.inf)
+            ok = x.vmap >= 0
+            e = x.vmap[ok]
+            s64[ok] = t[bi, i, ok].astype(np.float64) + (x.a[bi, i, e].astype(np.float64) - x.b[bi, i, e])
+            assert r.fused[bi, i] == int(np.argmax(s64))
+    d = x.draft.copy()
+    d[0, 0] = free[1]
+    r2 = oracle.asym_xfam(x.a, x.b, t, x.vmap, d, 1.0, 0.0, "f32")
+    assert r2.accept[0, 0] == 0 and np.isnan(r2.margin[0, 0]) and r2.accept_len[0] == 0
+    r3 = oracle.asym_xfam(x.a, x.b, t, np.full(450, -1, np.int32), x.draft, 1.0, 0.5, "f32")
+    assert np.all(r3.fused == -1) and np.all(r3.token == -1) and np.all(r3.accept == 0)
+
+
+def test_xfam_acceptance_against_scipy(oracle_lib):
+    """The test compares the verifier's probability of the draft with the
+    drafter's compressed-view probability of its pair."""
+    x = W.gen_xfam(4, 3, 600, 550, 400, "f32", seed=64)
+    r = oracle.asym_xfam(x.a, x.b, x.t, x.vmap, x.draft, 1.0, 0.5, "f32")
+    for j, v in enumerate((x.a, x.b, x.t)):   # each normaliser over its own vocabulary
+        np.testing.assert_allclose(r.lse[..., j], logsumexp(v.astype(np.float64), axis=2), rtol=0, atol=1e-12)
+    for bi in range(4):
+        for i in range(3):
+            dv = x.draft[bi, i]
+            e = x.vmap[dv]
+            lt = log_softmax(x.t[bi, i].astype(np.float64))[dv]
+            lb = log_softmax(x.b[bi, i].astype(np.float64))[e]
+            p = softmax(x.a[bi, i].astype(np.float64))
+            q = softmax(x.b[bi, i].astype(np.float64))
+            Dj = jensenshannon(p, q) ** 2
+            want = lt - lb - math.log(float(np.float32(0.5))) + Dj
+            assert abs(r.margin[bi, i] - want) < 1e-9
+            assert bool(r.accept[bi, i]) == (want > 0)
+
+
 # ------------------------------------------------ E2-SCI adaptive acceptance
 # E2-SCI notes, key design 3: per-position JSD of drafter and target against
 # the window's threshold, the EWMA credit state and the clamped threshold.

@@ -28,6 +28,14 @@ Recipe (one logit row = one draft position of one request):
   (every ``t + beta*(a - b)`` with ``beta >= 0``) then has an exact tie at its
   maximum, and ``a`` has an exact tie at its maximum, whatever the evaluation
   order or precision.
+* AsymSpec across families: drafter rows a, b over the drafter vocabulary
+  Vd as in AsymSpec; a vocabulary alignment pairs ``n_shared`` verifier ids
+  (a seeded random subset of the verifier vocabulary Vt, plus the last
+  ``n_special`` ids of each vocabulary paired in order, standing in for
+  special tokens) with distinct drafter ids (seeded random); the verifier row
+  is ``t[v] = z[map[v]] + N(0, 0.5^2)`` on paired ids and ``N(0, 2^2)``
+  elsewhere.  Drafts are the drafter's greedy tokens restricted to the
+  paired drafter ids, given as the paired verifier ids.
 * E2-SCI: target ``z_t = z + N(0, 0.5^2)``; drafter ``y = z + N(0,
   sigma^2)`` with ``sigma`` uniform on [0.1, 1.0] per row (a spread of
   divergences); "identical" rows set ``y := z_t`` bit for bit (divergence
@@ -256,6 +264,94 @@ def gen_asym(B: int, K: int, V: int, dtype: str = F32, seed: int = SEED_BASE,
                       displaced=displaced.reshape(B, K + 1),
                       identical=identical.reshape(B, K + 1),
                       tie=tie.reshape(B, K + 1), name=name)
+
+
+# --------------------------------------------------------------------------
+# AsymSpec across model families
+# --------------------------------------------------------------------------
+@dataclass
+class XfamInputs:
+    """Drafter rows a, b [B, K+1, Vd], verifier rows t [B, K+1, Vt], the
+    alignment vmap [Vt] int32 (paired drafter id or -1) and greedy drafts
+    [B, K] in verifier ids."""
+
+    a: np.ndarray
+    b: np.ndarray
+    t: np.ndarray
+    vmap: np.ndarray
+    draft: np.ndarray
+    dtype: str
+    beta: float
+    gamma: float
+    seed: int
+    name: str = ""
+
+    @property
+    def B(self):
+        return self.a.shape[0]
+
+    @property
+    def K(self):
+        return self.a.shape[1] - 1
+
+    @property
+    def Vd(self):
+        return self.a.shape[2]
+
+    @property
+    def Vt(self):
+        return self.t.shape[2]
+
+    def algorithmic_bytes(self) -> int:
+        es = 2 if self.dtype == BF16 else 4
+        rows = self.a.shape[0] * self.a.shape[1]
+        return rows * (2 * self.Vd + self.Vt) * es + 4 * self.Vt
+
+
+def gen_xfam(B: int, K: int, Vd: int, Vt: int, n_shared: int, dtype: str = F32, seed: int = SEED_BASE + 7,
+             n_special: int = 16, displaced_frac: float = 0.3, beta: float = 1.0, gamma: float = 0.5,
+             noise_std: float = 0.5, name: str = "") -> XfamInputs:
+    """Generate one cross-family workload following the module recipe."""
+    n_special = min(n_special, Vd, Vt)
+    if n_shared + n_special > min(Vd, Vt):
+        raise ValueError("more pairs than tokens")
+    x = gen_asym(B, K, Vd, dtype, seed, displaced_frac=displaced_frac, beta=beta, gamma=gamma,
+                 noise_std=noise_std)
+    ss = np.random.SeedSequence(seed + 1)
+    s_map, s_rows = ss.spawn(2)
+    g = np.random.default_rng(s_map)
+    vmap = np.full(Vt, -1, np.int32)
+    vt_ids = g.permutation(Vt - n_special)[:n_shared]
+    vd_ids = g.permutation(Vd - n_special)[:n_shared]
+    vmap[vt_ids] = vd_ids
+    vmap[Vt - n_special:] = np.arange(Vd - n_special, Vd, dtype=np.int32)
+    paired = vmap >= 0
+    R = B * (K + 1)
+    z = x.t.reshape(R, Vd)          # the AsymSpec verifier row: z + noise on the drafter vocabulary
+    t = np.empty((R, Vt), np.float32)
+    row_seeds = s_rows.spawn(R)
+
+    def make_row(r, bufs):
+        (n,) = bufs
+        gr = np.random.default_rng(row_seeds[r])
+        gr.standard_normal(out=n)
+        n *= 2.0
+        n[paired] = z[r, vmap[paired]].astype(np.float64) + noise_std * gr.standard_normal(int(paired.sum()))
+        t[r] = _to_dtype(n, dtype)
+
+    _parallel_rows(R, Vt, 1, make_row)
+    t = t.reshape(B, K + 1, Vt)
+    # greedy drafts on the paired drafter ids, as verifier ids
+    inv = np.full(Vd, -1, np.int64)
+    inv[vmap[paired]] = np.flatnonzero(paired)
+    pd = np.sort(vmap[paired])
+    draft = np.zeros((B, K), np.int32)
+    for bi in range(B):
+        for i in range(K):
+            row = x.a[bi, i, pd]
+            draft[bi, i] = inv[pd[int(np.argmax(row))]]
+    return XfamInputs(a=x.a, b=x.b, t=t, vmap=vmap, draft=draft, dtype=dtype, beta=float(beta),
+                      gamma=float(gamma), seed=seed, name=name)
 
 
 # --------------------------------------------------------------------------
@@ -498,3 +594,13 @@ def e2sci_batched(seed: int = SEED_BASE + 6) -> E2sciInputs:
     """B=64 requests, W=8 drafts, V=151936, bf16."""
     return gen_e2sci(64, 8, VOCAB_QWEN3, BF16, seed, identical_frac=0.1,
                      name="e2sci_B64_W8_V151936_bf16")
+
+
+VOCAB_SHARED_QWEN_LLAMA = 109566  # string-identical tokens of the page's alignment
+
+
+def xfam_batched(seed: int = SEED_BASE + 7) -> XfamInputs:
+    """B=64, K=2, Qwen-family drafter (Vd=151936), Llama-family verifier
+    (Vt=128256), 109,566 shared tokens plus 16 special pairs, bf16."""
+    return gen_xfam(64, 2, VOCAB_QWEN3, VOCAB_LLAMA31, VOCAB_SHARED_QWEN_LLAMA, BF16, seed,
+                    name="xfam_B64_K2_Vd151936_Vt128256_bf16")

@@ -150,6 +150,42 @@ def time_e2sci(vwl, x, steps, warmup, copies=4):
             [s.elapsed_time(m) for s, m in zip(start, mid)])
 
 
+def time_xfam(vwl, x, steps, warmup, copies=4):
+    """asym_verify_xfam calls rotating `copies` input sets; per-call and
+    row-pass ms (the event after the drafter and verifier passes)."""
+    import torch
+    base = [vwl.to_device_logits(getattr(x, n), x.dtype) for n in ("a", "b", "t")]
+    sets = [base] + [[t.clone() for t in base] for _ in range(1, copies)]
+    vm = torch.from_numpy(x.vmap).cuda()
+    d = torch.from_numpy(x.draft).cuda()
+    out = vwl.asym_out(x.B, x.K, "cuda")
+    for i in range(warmup):
+        a, b, t = sets[i % copies]
+        vwl.asym_verify_xfam(a, b, t, vm, d, x.beta, x.gamma, out=out)
+    stream = torch.cuda.current_stream()
+    start, mid, end = _events(steps), _events(steps), _events(steps)
+    for e in mid:
+        e.record(stream)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        a, b, t = sets[i % copies]
+        start[i].record(stream)
+        vwl.set_phase_event(mid[i])
+        vwl.asym_verify_xfam(a, b, t, vm, d, x.beta, x.gamma, out=out)
+        end[i].record(stream)
+    torch.cuda.synchronize()
+    vwl.set_phase_event(None)
+    return ([s.elapsed_time(e) for s, e in zip(start, end)],
+            [s.elapsed_time(m) for s, m in zip(start, mid)])
+
+
+def oracle_rows_per_s(fn, rows):
+    """The oracle timed once on a bounded sample of a workload (rows/s)."""
+    t0 = time.perf_counter()
+    fn()
+    return rows / (time.perf_counter() - t0)
+
+
 def stream_read_gbs(nbytes=1 << 30, reps=20):
     """Read bandwidth of a plain torch reduction over nbytes (a measured
     streaming reference on this GPU)."""
@@ -224,6 +260,7 @@ def main():
               "slices, described in the design notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    import numpy as np
     import torch
     import vocab_wide_logit_amd as vwl
     import workloads as W
@@ -313,6 +350,13 @@ def main():
                       "gbs": b3 / (ms3 * 1e-3) / 1e9, "frac_of_peak": b3 / (ms3 * 1e-3) / 1e9 / PEAK_HBM_GBS,
                       "eta": r3.eta},
         }
+        xf = W.xfam_batched()
+        pf, rf = time_xfam(vwl, xf, args.steps, args.warmup)
+        mf, mrf = _median(pf), _median(rf)
+        bf = xf.algorithmic_bytes()
+        result["secondary"][xf.name] = {
+            "rows_per_s": xf.B * (xf.K + 1) / (mf * 1e-3), "median_call_ms": mf, "median_row_passes_ms": mrf,
+            "gbs": bf / (mrf * 1e-3) / 1e9, "frac_of_peak": bf / (mrf * 1e-3) / 1e9 / PEAK_HBM_GBS}
         for xe in (W.e2sci_batched(), W.e2sci_single()):
             pe, re_ = time_e2sci(vwl, xe, args.steps, args.warmup)
             me, mre = _median(pe), _median(re_)
@@ -324,6 +368,32 @@ def main():
     if not args.no_cpu_baseline:
         _say("timing the fp64 oracle on the host")
         result["cpu_baseline"] = cpu_baseline(x)
+        if not args.no_extra:
+            # the oracle beside each secondary pass, on a bounded sample
+            # (the first 8 requests of each workload)
+            import oracle
+            n = 8
+            sl = lambda v: np.ascontiguousarray(v[:n])
+            sec = result["secondary"]
+            sec[x2.name]["cpu_oracle_rows_per_s"] = oracle_rows_per_s(
+                lambda: oracle.asym(sl(x2.a), sl(x2.b), sl(x2.t), sl(x2.draft), x2.beta, x2.gamma, x2.dtype),
+                n * (x2.K + 1))
+            sec[r3.name]["cpu_oracle_rows_per_s"] = oracle_rows_per_s(
+                lambda: oracle.rapid(sl(r3.z), sl(r3.y), sl(r3.draft), sl(r3.u_accept), sl(r3.u_sample),
+                                     r3.eta, r3.T, r3.dtype), n * (r3.G + 1))
+            for key, v in result["variants_" + x.name].items():
+                delta, gate = key.replace("delta=", "").replace("gate=", "").split(",")
+                v["cpu_oracle_rows_per_s"] = oracle_rows_per_s(
+                    lambda: oracle.asym(sl(x.a), sl(x.b), sl(x.t), sl(x.draft), x.beta, x.gamma, x.dtype,
+                                        delta=delta, gate=gate), n * (x.K + 1))
+            sec[xf.name]["cpu_oracle_rows_per_s"] = oracle_rows_per_s(
+                lambda: oracle.asym_xfam(sl(xf.a), sl(xf.b), sl(xf.t), xf.vmap, sl(xf.draft), xf.beta, xf.gamma,
+                                         xf.dtype), n * (xf.K + 1))
+            for xe in (W.e2sci_batched(), W.e2sci_single()):
+                m = min(n, xe.B)
+                sec[xe.name]["cpu_oracle_rows_per_s"] = oracle_rows_per_s(
+                    lambda: oracle.e2sci(xe.y[:m], xe.z[:m], xe.T[:m], xe.omega[:m], xe.r_hat[:m],
+                                         dtype=xe.dtype), m * xe.W)
     print(json.dumps(result), flush=True)
 
 

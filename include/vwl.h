@@ -71,6 +71,7 @@ typedef enum { VWL_F32 = 0, VWL_BF16 = 1 } vwl_dtype;
 #define VWL_DEVERR_DRAFT 1
 #define VWL_DEVERR_UNIFORM 2
 #define VWL_DEVERR_TIMEOUT 4
+#define VWL_DEVERR_MAP 8     /* a vocabulary-alignment entry outside [-1, Vd): treated as unpaired */
 
 #define VWL_MAX_K 63 /* drafts per request, both methods */
 
@@ -157,6 +158,40 @@ vwl_status asym_verify_variant(const void *a, const void *b, const void *t,
                                float *D, float *gamma_eff, uint8_t *accept, int32_t *fused,
                                int32_t *accept_len, int32_t *token, int32_t *dev_err,
                                void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * AsymSpec across model families (AsymSpec notes, the analysis of why
+ * cross-family pairs work at a discount): the drafter's context gain lives
+ * on the drafter's vocabulary and reaches the verifier through a vocabulary
+ * alignment (string-identical tokens plus paired special tokens), with
+ * generation restricted to the paired tokens.
+ *
+ *   a, b   [B][K+1][Vd] drafter logits (full and compressed context)
+ *   t      [B][K+1][Vt] verifier logits, its own vocabulary
+ *   vmap   [Vt] int32 device array: the drafter id paired with verifier
+ *          token v, or -1 (an entry outside [-1, Vd) is treated as -1 and
+ *          sets VWL_DEVERR_MAP)
+ *   draft  [B][K] int32 drafts as VERIFIER ids
+ * Per row: L_a, L_b over Vd, L_t over Vt; D = JSD(softmax(a) || softmax(b))
+ * on the drafter vocabulary; gamma_eff = gamma*exp(-D);
+ *   fused_i  = lowest verifier id v with vmap[v] >= 0 maximising
+ *              t_v + beta*(a[vmap v] - b[vmap v])  (-1 when nothing is paired)
+ *   accept_i = softmax(t_i)[d] > gamma_eff * softmax(b_i)[vmap d]; a draft
+ *              without a pair is rejected (a draft outside [0, Vt) also sets
+ *              VWL_DEVERR_DRAFT)
+ * accept_len, token as asym_verify.  Outputs, dtype rules and errors as
+ * asym_verify; Vt >= 1; the workspace comes from
+ * vwl_asym_xfam_workspace_bytes.  With Vt = Vd and the identity alignment
+ * the results equal asym_verify's.
+ * --------------------------------------------------------------------------- */
+size_t vwl_asym_xfam_workspace_bytes(int B, int K, int Vd, int Vt, vwl_dtype dt);
+
+vwl_status asym_verify_xfam(const void *a, const void *b, int Vd, const void *t, int Vt,
+                            const int32_t *vmap, const int32_t *draft,
+                            int B, int K, vwl_dtype dt, float beta, float gamma,
+                            float *D, float *gamma_eff, uint8_t *accept, int32_t *fused,
+                            int32_t *accept_len, int32_t *token, int32_t *dev_err,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * E2-SCI adaptive JSD acceptance ("E2-SCI: Elastic Edge-Cloud Speculative

@@ -244,3 +244,24 @@ def test_e2sci_argument_codes(lib):
     assert _e2sci(lib, prm=(float("nan"), 0.5, 0.1, 0.01, 0.3, 0.3)) == 4
     assert _e2sci(lib, y=A + 4) == 7
     assert _e2sci(lib, T=A + 0x2002) == 7
+
+
+def test_asym_xfam_argument_codes(lib):
+    """Host-side checks of the cross-family entry point (no device access)."""
+    p = lambda x: ctypes.c_void_p(x) if x else None
+
+    def call(a=A, vmap=A + 0xA000, Vd=100, Vt=90, B=2, K=2, dt=0, ws=0, wsb=0):
+        return lib.asym_verify_xfam(p(a), p(A + 0x1000), Vd, p(A + 0x2000), Vt, p(vmap), p(A + 0x3000), B, K, dt,
+                                    ctypes.c_float(1.0), ctypes.c_float(0.5), p(A + 0x4000), p(A + 0x5000),
+                                    p(A + 0x6000), p(A + 0x7000), p(A + 0x8000), p(A + 0x9000), None, p(ws),
+                                    ctypes.c_size_t(wsb), None)
+
+    assert lib.vwl_asym_xfam_workspace_bytes(2, 2, 100, 90, 0) > lib.vwl_asym_workspace_bytes(2, 2, 100, 0)
+    assert lib.vwl_asym_xfam_workspace_bytes(2, 2, 100, 0, 0) == 0
+    assert call() == 5          # everything valid except the missing workspace
+    assert call(vmap=0) == 1
+    assert call(a=0) == 1
+    assert call(Vt=0) == 2
+    assert call(Vd=0) == 2
+    assert call(dt=4) == 3
+    assert call(vmap=A + 0xA002, ws=0x100000, wsb=1 << 30) == 7

@@ -1,0 +1,128 @@
+"""GPU parity of ``asym_verify_xfam`` (AsymSpec across model families: the
+drafter's gain reaches the verifier through a vocabulary alignment, generation
+restricted to the paired tokens) against the fp64 oracle, through the C ABI.
+Rules as for asym_verify (oracle/parity.py)."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from oracle.parity import compare_asym
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print("[xfam] " + msg, flush=True)
+
+
+@pytest.fixture(scope="module")
+def vwl():
+    import vocab_wide_logit_amd as m
+    m.load_library()
+    return m
+
+
+def run_dev(vwl, x, beta=None, gamma=None, t=None, vmap=None, draft=None):
+    import torch
+    beta = x.beta if beta is None else beta
+    gamma = x.gamma if gamma is None else gamma
+    a = vwl.to_device_logits(x.a, x.dtype)
+    b = vwl.to_device_logits(x.b, x.dtype)
+    tt = vwl.to_device_logits(x.t if t is None else t, x.dtype)
+    vm = torch.from_numpy(np.ascontiguousarray(x.vmap if vmap is None else vmap, np.int32)).cuda()
+    d = torch.from_numpy(np.ascontiguousarray(x.draft if draft is None else draft, np.int32)).cuda()
+    out = vwl.asym_verify_xfam(a, b, tt, vm, d, beta, gamma)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out._asdict().items()}
+
+
+def check(vwl, x, beta=None, gamma=None, label="", t=None, vmap=None, draft=None, dev_err=0):
+    beta = x.beta if beta is None else beta
+    gamma = x.gamma if gamma is None else gamma
+    t = x.t if t is None else t
+    vmap = x.vmap if vmap is None else vmap
+    draft = x.draft if draft is None else draft
+    _say("case %s %s B=%d K=%d Vd=%d Vt=%d pairs=%d" % (label, x.dtype, x.B, x.K, x.Vd, x.Vt,
+                                                      int((np.asarray(vmap) >= 0).sum())))
+    dev = run_dev(vwl, x, beta, gamma, t, vmap, draft)
+    ora = oracle.asym_xfam(x.a, x.b, t, vmap, draft, beta, gamma, x.dtype)
+    rep = compare_asym(dev, ora, x.K, identical=np.all(x.a == x.b, axis=2))
+    _say("  " + str(rep))
+    assert rep.ok, str(rep)
+    assert dev["dev_err"][0] == dev_err
+    return dev, ora, rep
+
+
+def test_tiny_fp32(vwl):
+    check(vwl, W.gen_xfam(4, 2, 1024, 900, 700, "f32", seed=21), label="tiny")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("Vd,Vt,n", [(1, 1, 1), (7, 5, 3), (1027, 4099, 900), (5000, 4096, 3000),
+                                     (151937, 128257, 100000)])
+def test_shapes(vwl, dtype, Vd, Vt, n):
+    """Ragged vocabularies on both sides, a verifier larger than the drafter,
+    exact multiples of the verifier chunk, tiny rows."""
+    x = W.gen_xfam(3, 2, Vd, Vt, max(0, n - min(16, Vd, Vt)), dtype, seed=4000 + Vd + Vt,
+                   n_special=min(16, Vd, Vt))
+    check(vwl, x, label="shape")
+
+
+def test_batched_qwen_to_llama(vwl):
+    """B=64, K=2: Qwen-family drafter (151936), Llama-family verifier
+    (128256), 109,566 shared tokens plus special pairs, bf16."""
+    x = W.xfam_batched()
+    for beta, gamma in ((1.0, 0.5), (2.0, 0.4), (0.0, 1.0)):
+        dev, ora, rep = check(vwl, x, beta, gamma, label=x.name)
+        assert rep.excluded <= 2
+
+
+def test_identity_alignment_matches_asym_verify(vwl):
+    """One vocabulary, identity alignment: the same bits as asym_verify."""
+    import torch
+    x = W.gen_asym(8, 3, 30011, "bf16", seed=22, identical_frac=0.2, tie_frac=0.2)
+    a = vwl.to_device_logits(x.a, x.dtype)
+    b = vwl.to_device_logits(x.b, x.dtype)
+    t = vwl.to_device_logits(x.t, x.dtype)
+    d = torch.from_numpy(np.ascontiguousarray(x.draft)).cuda()
+    vm = torch.arange(x.V, dtype=torch.int32, device="cuda")
+    o1 = {k: v.cpu().numpy() for k, v in vwl.asym_verify(a, b, t, d, 1.0, 0.5)._asdict().items()}
+    o2 = {k: v.cpu().numpy() for k, v in vwl.asym_verify_xfam(a, b, t, vm, d, 1.0, 0.5)._asdict().items()}
+    for k in ("fused", "accept", "accept_len", "token", "D", "gamma_eff"):
+        assert np.array_equal(o1[k], o2[k]), k
+
+
+def test_unpaired_and_bad_entries(vwl):
+    """A huge logit on an unpaired verifier token is never emitted; a draft on
+    an unpaired token is rejected; an alignment entry outside [-1, Vd) counts
+    as unpaired and sets the map bit; a draft id outside [0, Vt) sets the
+    draft bit; no pair at all gives fused = -1."""
+    x = W.gen_xfam(4, 2, 3000, 2800, 2000, "f32", seed=23)
+    free = np.flatnonzero(x.vmap < 0)
+    t = x.t.copy()
+    t[:, :, free[0]] = 1e4
+    d = x.draft.copy()
+    d[0, 0] = free[1]
+    dev, ora, rep = check(vwl, x, t=t, draft=d, label="unpaired")
+    assert np.all(x.vmap[dev["fused"]] >= 0) and dev["accept"][0, 0] == 0
+    bad = x.vmap.copy()
+    bad[free[2]] = x.Vd + 5
+    bad[free[3]] = -7
+    check(vwl, x, vmap=bad, label="bad entries", dev_err=8)
+    d2 = x.draft.copy()
+    d2[1, 1] = x.Vt
+    dev, _, _ = check(vwl, x, draft=d2, label="draft out of range", dev_err=1)
+    assert dev["accept"][1, 1] == 0
+    dev, _, _ = check(vwl, x, vmap=np.full(x.Vt, -1, np.int32), label="no pairs")
+    assert np.all(dev["fused"] == -1) and np.all(dev["token"] == -1)
+
+
+@pytest.mark.parametrize("nv", [1, 2, 4, 8])
+def test_every_plan(vwl, nv):
+    x = W.gen_xfam(6, 2, 40000, 33000, 25000, "bf16", seed=24)
+    try:
+        vwl.set_plan_override("asym", nv, 0)
+        check(vwl, x, label="plan nv=%d" % nv)
+    finally:
+        vwl.set_plan_override("asym", 0, 0)

@@ -17,6 +17,9 @@ Entry points (same names as the C ABI):
 * ``asym_verify_variant`` -- the same pass with the fusion source and the
   gate of the AsymSpec notes' mechanism ablation: delta = a - b, a or t - b;
   the CDA threshold or a fixed gamma.
+* ``asym_verify_xfam`` -- the AsymSpec pass across model families: drafter
+  rows on the drafter vocabulary, verifier rows on the verifier's, joined by
+  a vocabulary alignment (verifier id -> paired drafter id or -1).
 * ``e2sci_verify`` -- E2-SCI adaptive JSD acceptance (E2-SCI notes, key
   design 3): per-position divergence of drafter and target against the
   window threshold, then the caller-owned credit state and next threshold.
@@ -41,6 +44,7 @@ VWL_BF16 = 1
 DEVERR_DRAFT = 1
 DEVERR_UNIFORM = 2
 DEVERR_TIMEOUT = 4
+DEVERR_MAP = 8
 MAX_K = 63
 
 _lib = None
@@ -54,7 +58,8 @@ SYMBOLS = ("vwl_status_string", "vwl_version", "vwl_workspace_reset",
            "vwl_rapid_workspace_bytes", "rapid_verify",
            "vwl_plan_info", "vwl_asym_check", "vwl_rapid_check",
            "vwl_set_plan_override", "vwl_set_phase_event",
-           "vwl_e2sci_workspace_bytes", "e2sci_verify", "vwl_e2sci_plan_info")
+           "vwl_e2sci_workspace_bytes", "e2sci_verify", "vwl_e2sci_plan_info",
+           "vwl_asym_xfam_workspace_bytes", "asym_verify_xfam")
 
 
 class E2sciParams(ctypes.Structure):
@@ -113,6 +118,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.vwl_rapid_check.restype = i
         lib.vwl_set_plan_override.argtypes = [i, i, i]
         lib.vwl_set_plan_override.restype = i
+        lib.vwl_asym_xfam_workspace_bytes.argtypes = [i, i, i, i, i]
+        lib.vwl_asym_xfam_workspace_bytes.restype = sz
+        lib.asym_verify_xfam.argtypes = [P, P, i, P, i, P, P, i, i, i, f, f, P, P, P, P, P, P, P, P, sz, P]
+        lib.asym_verify_xfam.restype = i
         lib.vwl_e2sci_workspace_bytes.argtypes = [i, i, i, i]
         lib.vwl_e2sci_workspace_bytes.restype = sz
         lib.e2sci_verify.argtypes = [P, P, i, i, i, i, P, P, P, ctypes.POINTER(E2sciParams),
@@ -312,6 +321,43 @@ def asym_verify_variant(a: Optional[torch.Tensor], b: torch.Tensor, t: torch.Ten
                                    _ptr(out.D), _ptr(out.gamma_eff), _ptr(out.accept) if K > 0 else None,
                                    _ptr(out.fused), _ptr(out.accept_len), _ptr(out.token), _ptr(out.dev_err),
                                    _ptr(ws), ws.numel(), ctypes.c_void_p(stream.cuda_stream))
+    _check(code)
+    return out
+
+
+def asym_verify_xfam(a: torch.Tensor, b: torch.Tensor, t: torch.Tensor, vmap: torch.Tensor,
+                     draft: torch.Tensor, beta: float, gamma: float, *, out: Optional[AsymOut] = None,
+                     workspace: Optional[torch.Tensor] = None) -> AsymOut:
+    """AsymSpec across model families on the current stream.  a, b: drafter
+    logits [B, K+1, Vd]; t: verifier logits [B, K+1, Vt]; vmap: [Vt] int32
+    (paired drafter id or -1); draft: [B, K] int32 verifier ids."""
+    lib = load_library()
+    _dev_tensor(a, "a")
+    dt = _dt(a)
+    _dev_tensor(b, "b", a.dtype)
+    _dev_tensor(t, "t", a.dtype)
+    if a.dim() != 3 or b.shape != a.shape or t.dim() != 3 or t.shape[:2] != a.shape[:2]:
+        raise ValueError("a, b must be [B, K+1, Vd] and t [B, K+1, Vt]")
+    B, P, Vd = a.shape
+    Vt = t.shape[2]
+    K = P - 1
+    _dev_tensor(vmap, "vmap", torch.int32)
+    if tuple(vmap.shape) != (Vt,):
+        raise ValueError("vmap must be [Vt]")
+    _dev_tensor(draft, "draft", torch.int32)
+    if tuple(draft.shape) != (B, K):
+        raise ValueError("draft must be [B, K]")
+    if out is None:
+        out = asym_out(B, K, a.device)
+    stream = torch.cuda.current_stream(a.device)
+    if workspace is None:
+        need = int(lib.vwl_asym_xfam_workspace_bytes(B, K, Vd, Vt, dt))
+        workspace = _workspace_sized(("xfam", B, K, Vd, Vt, dt), need, a.device, stream)
+    code = lib.asym_verify_xfam(_ptr(a), _ptr(b), Vd, _ptr(t), Vt, _ptr(vmap), _ptr(draft) if K > 0 else None,
+                                B, K, dt, float(beta), float(gamma),
+                                _ptr(out.D), _ptr(out.gamma_eff), _ptr(out.accept) if K > 0 else None,
+                                _ptr(out.fused), _ptr(out.accept_len), _ptr(out.token), _ptr(out.dev_err),
+                                _ptr(workspace), workspace.numel(), ctypes.c_void_p(stream.cuda_stream))
     _check(code)
     return out
 

@@ -9,7 +9,8 @@
 //         is not read at all when delta = t - b)
 // Each translation unit asym_<delta>.hip instantiates one fusion source.
 // DS = kDeltaNone reads only a and b (no verifier row, no fused token): the
-// two-tensor divergence pass of E2-SCI's adaptive acceptance (e2sci.hip).
+// two-tensor divergence pass behind E2-SCI and cross-family AsymSpec
+// (pair_pass.hip).
 //
 // Launch 1, asym_rows_kernel: each logit row (one draft position of one
 // request: a_i, b_i, t_i) is split over a team of W workgroups; each
@@ -113,10 +114,10 @@ __device__ __forceinline__ float jsd_term(float la2, float lb2, float x) {
 // caller gets the same bits.  The references are integers, so each term is
 // an exact power-of-two rescale.  Called by one whole wave.  Tensor k has its
 // sums in word sw[k] and its reference in the low (hi[k] = false) or high
-// half of word cw[k].
+// half of word cw[k].  Records are `stride` words apart.
 template <int N>
 __device__ __forceinline__ void team_lse(const uint64_t *rec_row, int W, const int (&sw)[N], const int (&cw)[N],
-                                         const bool (&hi)[N], double (&L)[N]) {
+                                         const bool (&hi)[N], double (&L)[N], int stride = kRecWords) {
     const int lane = threadIdx.x & 63;
     const float NEG = -3.0e38f;
     auto ref = [&](const uint64_t *r, int k) {
@@ -134,7 +135,7 @@ __device__ __forceinline__ void team_lse(const uint64_t *rec_row, int W, const i
     for (int h = 0; h < 2; ++h) {
         const int w = lane + 64 * h;
         if (w < W) {
-            const uint64_t *rw = rec_row + (size_t)w * kRecWords;
+            const uint64_t *rw = rec_row + (size_t)w * stride;
 #pragma unroll
             for (int k = 0; k < N; ++k) {
                 r[k][h] = ref(rw, k);
@@ -146,7 +147,7 @@ __device__ __forceinline__ void team_lse(const uint64_t *rec_row, int W, const i
     for (int k = 0; k < N; ++k)
         C[k] = fmaxf(r[k][0], r[k][1]);
     for (int w = lane + 128; w < W; w += 64) { // teams wider than 128 members
-        const uint64_t *rw = rec_row + (size_t)w * kRecWords;
+        const uint64_t *rw = rec_row + (size_t)w * stride;
 #pragma unroll
         for (int k = 0; k < N; ++k)
             C[k] = fmaxf(C[k], ref(rw, k));
@@ -158,7 +159,7 @@ __device__ __forceinline__ void team_lse(const uint64_t *rec_row, int W, const i
         t[k] = scale_pow2(a[k][0], r[k][0] - C[k]) + scale_pow2(a[k][1], r[k][1] - C[k]);
     }
     for (int w = lane + 128; w < W; w += 64) { // teams wider than 128 members
-        const uint64_t *rw = rec_row + (size_t)w * kRecWords;
+        const uint64_t *rw = rec_row + (size_t)w * stride;
 #pragma unroll
         for (int k = 0; k < N; ++k)
             t[k] += scale_pow2(as_f64(ld_relaxed(rw + sw[k])), ref(rw, k) - C[k]);

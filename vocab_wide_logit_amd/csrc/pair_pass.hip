@@ -1,0 +1,314 @@
+// Passes built on the two-tensor divergence kernel (asym_rows_kernel with
+// kDeltaNone): E2-SCI's adaptive acceptance and AsymSpec across model
+// families.
+//
+// E2-SCI adaptive JSD acceptance ("E2-SCI: Elastic Edge-Cloud Speculative
+// Decoding via Credit Inertia" notes, key design 3 "online adaptive
+// verification"; the credit state of key design 1).
+//
+// Launch 1: the two-tensor row kernel (asym_rows_kernel with kDeltaNone):
+// online softmax statistics of the drafter row y (tensor a) and the target
+// row z (tensor b), the team combine, and the JSD terms of each chunk.
+// Launch 2, e2sci_finalize_kernel: one wave per row sums the JSD partials
+// (D) and tests D <= T of the row's request; the wave that completes a
+// request finds the first rejection, updates the credit state
+//   r = (1 - beta) r + beta * accept_len / W
+// and writes the next window's threshold
+//   T = max(T_min, min(T_base + alpha * omega * (r - tau_credit), T_max)).
+#include "asym_kernels.hpp"
+
+namespace vwl {
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void e2sci_finalize_kernel(AsymParams P) {
+    const int lane = threadIdx.x & 63;
+    const long long row = (long long)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        P.ctl[0] = 0u; // ticket counter of the row kernel, for the next call
+    if (row >= P.R)
+        return;
+    const uint64_t *rec_row = P.rec + (size_t)row * P.Wmax * kRecWords;
+    double jsum = 0.0;
+    for (int w = lane; w < P.W; w += 64)
+        jsum += as_f64(ld_relaxed(rec_row + (size_t)w * kRecWords + 6));
+    jsum = wave_sum(jsum);
+    if (lane != 0)
+        return;
+    const double Dr = -0.5 * kLn2d * jsum;
+    const long long bi = row / P.win;
+    // the threshold is read before this row's arrival is counted, so the
+    // completing wave may overwrite it (thr_out may alias thr_in)
+    const uint32_t acc = Dr <= (double)P.thr_in[bi] ? 1u : 0u;
+    P.D[row] = (float)Dr;
+    P.accept[row] = (uint8_t)acc;
+    st_relaxed(P.row_info + (size_t)row * 2 + 1, acc);
+    P.row_ctr[(size_t)row * 16] = 0u; // arrivals of the row kernel, for the next call
+    uint32_t *rq = P.req_ctr + (size_t)bi * 16;
+    const uint32_t done = publish_add(rq, 1u);
+    if (done == (uint32_t)(P.win - 1)) {
+        const size_t r0 = (size_t)bi * P.win;
+        int n = P.win;
+        for (int k = 0; k < P.win; ++k) {
+            if (ld_relaxed(P.row_info + (r0 + k) * 2 + 1) == 0u) {
+                n = k;
+                break;
+            }
+        }
+        P.acc_len[bi] = n;
+        const double p_acc = (double)n / (double)P.win;
+        const double r = (1.0 - P.e_ewma) * (double)P.r_hat[bi] + P.e_ewma * p_acc;
+        double T = P.e_Tbase + P.e_alpha * (double)P.omega[bi] * (r - P.e_tau);
+        T = T > P.e_Tmax ? P.e_Tmax : T;
+        T = T < P.e_Tmin ? P.e_Tmin : T;
+        P.r_hat[bi] = (float)r;
+        P.thr_out[bi] = (float)T;
+        st_relaxed(rq, 0u);
+    }
+}
+
+template <int DT, int NV>
+static hipError_t launch_t(const Plan &plan, const AsymParams &p, hipStream_t s, hipEvent_t after_rows) {
+    hipLaunchKernelGGL((asym_rows_kernel<DT, NV, kDeltaNone, kGateCda>), dim3(plan.grid), dim3(kThreads), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    if (after_rows) {
+        e = hipEventRecord(after_rows, s);
+        if (e != hipSuccess)
+            return e;
+    }
+    const unsigned fin = (unsigned)((p.R + kWaves - 1) / kWaves);
+    hipLaunchKernelGGL((e2sci_finalize_kernel<DT>), dim3(fin), dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+template <int DT>
+static hipError_t launch_nv(const Plan &plan, const AsymParams &p, hipStream_t s, hipEvent_t after_rows) {
+    switch (plan.nv) {
+    case 1: return launch_t<DT, 1>(plan, p, s, after_rows);
+    case 2: return launch_t<DT, 2>(plan, p, s, after_rows);
+    case 4: return launch_t<DT, 4>(plan, p, s, after_rows);
+    case 8: return launch_t<DT, 8>(plan, p, s, after_rows);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_e2sci(int dt, const Plan &plan, const AsymParams &p, hipStream_t s, hipEvent_t after_rows) {
+    return dt == DT_BF16 ? launch_nv<DT_BF16>(plan, p, s, after_rows) : launch_nv<DT_F32>(plan, p, s, after_rows);
+}
+
+template int asym_blocks_per_cu_ds<kDeltaNone>(int dt, int nv, int gate);
+
+// ---------------------------------------------------------------------------
+// AsymSpec across model families (AsymSpec reading notes, the analysis of
+// cross-family pairs): the drafter rows a, b live on the drafter vocabulary
+// (V), the verifier row t on its own (Vt), and vmap[v] pairs verifier token
+// v with a drafter token (string-identical tokens and paired specials) or
+// is -1.  Generation is restricted to the paired tokens.
+//
+// Launch 1: the two-tensor row kernel over a, b (L_a, L_b, the JSD partials).
+// Launch 2, xfam_verifier_kernel: one workgroup per (row, chunk of the
+// verifier vocabulary): online softmax statistics of t, and the maximum of
+// t[v] + beta*(a[vmap v] - b[vmap v]) over the paired v with its lowest
+// index, the drafter values gathered through the alignment.
+// Launch 3, xfam_finalize_kernel: one wave per row combines both record
+// sets, tests the draft (a verifier id) against the drafter's compressed-view
+// probability of its pair, and scans each request.
+// ---------------------------------------------------------------------------
+
+// Workgroup b runs on die b % 8 (round-robin dispatch); the chunks of one row
+// go to workgroups of one die, so the row's gathered drafter values are
+// fetched into one L2.  Returns false for the padding workgroups.
+__device__ __forceinline__ bool xfam_item(const AsymParams &P, long long &row, int &chunk) {
+    constexpr int kDies = 8;
+    const long long b = blockIdx.x;
+    const long long die = b % kDies, k = b / kDies;
+    row = die + kDies * (k / P.vchunks);
+    chunk = (int)(k % P.vchunks);
+    return row < P.R;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void xfam_verifier_kernel(AsymParams P) {
+    __shared__ float lds_f[kWaves * 2];
+    __shared__ double lds_d[kWaves];
+    __shared__ int lds_i[kWaves];
+    long long row;
+    int chunk;
+    if (!xfam_item(P, row, chunk))
+        return;
+    const int tid = threadIdx.x;
+    const size_t trow = (size_t)row * (size_t)P.Vt, arow = (size_t)row * (size_t)P.V;
+    const int v0 = chunk * kXfamChunk;
+    const float NEG_INF = -__builtin_inff();
+    // Branch-free so every load of a phase is in flight at once: out-of-range
+    // elements read index 0 (always valid) and are masked afterwards.
+    float x[kXfamEpt], xa[kXfamEpt], xb[kXfamEpt];
+    int e[kXfamEpt];
+    bool bad_map = false;
+#pragma unroll
+    for (int k = 0; k < kXfamEpt; ++k) { // element v0 + k*256 + tid: coalesced per wave
+        const int v = v0 + k * kThreads + tid;
+        const int vc = v < P.Vt ? v : 0;
+        x[k] = load_scalar<DT>(P.tv, trow + vc);
+        e[k] = P.vmap[vc];
+    }
+#pragma unroll
+    for (int k = 0; k < kXfamEpt; ++k) {
+        const bool in = v0 + k * kThreads + tid < P.Vt;
+        bad_map |= in && (e[k] < -1 || e[k] >= P.V);
+        if (!in || e[k] < 0 || e[k] >= P.V)
+            e[k] = -1;
+        if (!in)
+            x[k] = NEG_INF;
+        const int ec = e[k] >= 0 ? e[k] : 0;
+        xa[k] = load_scalar<DT>(P.a, arow + ec);
+        xb[k] = load_scalar<DT>(P.b, arow + ec);
+    }
+    float best = NEG_INF;
+    int bidx = 0x7fffffff;
+#pragma unroll
+    for (int k = 0; k < kXfamEpt; ++k) {
+        if (e[k] >= 0) {
+            const float sc = fused_score<kDeltaAMinusB>(xa[k], xb[k], x[k], P.beta);
+            if (sc > best || bidx == 0x7fffffff) { // first paired element, then strictly larger
+                best = sc;
+                bidx = v0 + k * kThreads + tid;
+            }
+        }
+    }
+    OnlineLse st;
+    online_init(st);
+    online_group<kXfamEpt>(st, x);
+    float mx[2] = {st.c, best};
+    block_max<2>(mx, lds_f);
+    int fi = (best == mx[1]) ? bidx : 0x7fffffff;
+    double S[1] = {rescale_to(st, mx[0])};
+    block_sum_min<1>(S, fi, lds_d, lds_i);
+    if (tid == 0) {
+        uint64_t *r = P.vrec + ((size_t)row * P.vchunks + chunk) * kVrecWords;
+        r[0] = f64_bits(S[0]);
+        r[1] = pack2(mx[0], mx[1]);
+        r[2] = (uint64_t)(uint32_t)fi;
+    }
+    if (bad_map)
+        set_dev_err(P.dev_err, 8);
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void xfam_finalize_kernel(AsymParams P) {
+    const int lane = threadIdx.x & 63;
+    const long long row = (long long)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        P.ctl[0] = 0u; // ticket counter of the row kernel, for the next call
+    if (row >= P.R)
+        return;
+    // drafter side: L_b (log2 units) and the JSD partials
+    const uint64_t *rec_row = P.rec + (size_t)row * P.Wmax * kRecWords;
+    double Lb2[1];
+    team_lse<1>(rec_row, P.W, {1}, {3}, {true}, Lb2);
+    double jsum = 0.0;
+    for (int w = lane; w < P.W; w += 64)
+        jsum += as_f64(ld_relaxed(rec_row + (size_t)w * kRecWords + 6));
+    jsum = wave_sum(jsum);
+    // verifier side: L_t and the fused token over the chunk records
+    const uint64_t *vr = P.vrec + (size_t)row * P.vchunks * kVrecWords;
+    double Lt2[1];
+    team_lse<1>(vr, P.vchunks, {0}, {1}, {false}, Lt2, kVrecWords);
+    float fbest = -__builtin_inff();
+    for (int c = lane; c < P.vchunks; c += 64)
+        fbest = fmaxf(fbest, unpack_hi(vr[(size_t)c * kVrecWords + 1]));
+    fbest = wave_max(fbest);
+    int fidx = 0x7fffffff;
+    for (int c = lane; c < P.vchunks; c += 64)
+        if (unpack_hi(vr[(size_t)c * kVrecWords + 1]) == fbest)
+            fidx = min(fidx, (int)(uint32_t)vr[(size_t)c * kVrecWords + 2]);
+    fidx = wave_min_int(fidx);
+    if (fidx == 0x7fffffff)
+        fidx = -1; // no verifier token is paired
+    if (lane != 0)
+        return;
+    const double Lb = Lb2[0] * kLn2d, Lt = Lt2[0] * kLn2d;
+    const double Dr = -0.5 * kLn2d * jsum;
+    P.D[row] = (float)Dr;
+    P.geff[row] = (float)((double)P.gamma * exp(-Dr));
+    P.fused[row] = fidx;
+    const int Pn = P.K + 1;
+    const long long bi = row / Pn;
+    const int i = (int)(row - bi * Pn);
+    uint32_t acc = 0;
+    if (i < P.K) {
+        const int d = P.draft[bi * P.K + i];
+        if (d < 0 || d >= P.Vt) {
+            set_dev_err(P.dev_err, 1);
+        } else {
+            const int e = P.vmap[d];
+            if (e >= 0 && e < P.V) { // an unpaired draft is rejected
+                const double td = (double)load_scalar<DT>(P.tv, (size_t)row * (size_t)P.Vt + d);
+                const double bd = (double)load_scalar<DT>(P.b, (size_t)row * (size_t)P.V + e);
+                const double margin = (td - Lt) - (bd - Lb) - P.log_gamma + Dr;
+                acc = margin > 0.0 ? 1u : 0u;
+            }
+        }
+        P.accept[bi * P.K + i] = (uint8_t)acc;
+    }
+    st_relaxed(P.row_info + (size_t)row * 2 + 0, (uint32_t)fidx);
+    st_relaxed(P.row_info + (size_t)row * 2 + 1, acc);
+    P.row_ctr[(size_t)row * 16] = 0u; // arrivals of the row kernel, for the next call
+    uint32_t *rq = P.req_ctr + (size_t)bi * 16;
+    const uint32_t done = publish_add(rq, 1u);
+    if (done == (uint32_t)P.K) {
+        const size_t r0 = (size_t)bi * Pn;
+        int n = P.K;
+        for (int k = 0; k < P.K; ++k) {
+            if (ld_relaxed(P.row_info + (r0 + k) * 2 + 1) == 0u) {
+                n = k;
+                break;
+            }
+        }
+        P.acc_len[bi] = n;
+        P.token[bi] = (int32_t)ld_relaxed(P.row_info + (r0 + n) * 2 + 0);
+        st_relaxed(rq, 0u);
+    }
+}
+
+// Workgroups of the verifier pass: 8 dies x (rows per die) x chunks.
+inline long long xfam_verifier_grid(long long R, int chunks) { return 8 * ((R + 7) / 8) * (long long)chunks; }
+
+template <int DT, int NV>
+static hipError_t launch_x(const Plan &plan, const AsymParams &p, hipStream_t s, hipEvent_t after_rows) {
+    hipLaunchKernelGGL((asym_rows_kernel<DT, NV, kDeltaNone, kGateCda>), dim3(plan.grid), dim3(kThreads), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL((xfam_verifier_kernel<DT>), dim3((unsigned)xfam_verifier_grid(p.R, p.vchunks)),
+                       dim3(kThreads), 0, s, p);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    if (after_rows) {
+        e = hipEventRecord(after_rows, s);
+        if (e != hipSuccess)
+            return e;
+    }
+    const unsigned fin = (unsigned)((p.R + kWaves - 1) / kWaves);
+    hipLaunchKernelGGL((xfam_finalize_kernel<DT>), dim3(fin), dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+template <int DT>
+static hipError_t launch_xnv(const Plan &plan, const AsymParams &p, hipStream_t s, hipEvent_t after_rows) {
+    switch (plan.nv) {
+    case 1: return launch_x<DT, 1>(plan, p, s, after_rows);
+    case 2: return launch_x<DT, 2>(plan, p, s, after_rows);
+    case 4: return launch_x<DT, 4>(plan, p, s, after_rows);
+    case 8: return launch_x<DT, 8>(plan, p, s, after_rows);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_xfam(int dt, const Plan &plan, const AsymParams &p, hipStream_t s, hipEvent_t after_rows) {
+    return dt == DT_BF16 ? launch_xnv<DT_BF16>(plan, p, s, after_rows) : launch_xnv<DT_F32>(plan, p, s, after_rows);
+}
+
+} // namespace vwl

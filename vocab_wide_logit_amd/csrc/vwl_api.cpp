@@ -398,6 +398,90 @@ vwl_status asym_verify(const void *a, const void *b, const void *t, const int32_
                                stream);
 }
 
+// Cross-family workspace: the AsymSpec layout of the drafter rows followed by
+// the verifier records.
+static bool xfam_layout(int B, int K, int Vd, int Vt, vwl_dtype dt, WsLayout &L, size_t &vrec, size_t &total) {
+    if (!shape_ok(B, K, Vd) || !shape_ok(B, K, Vt) || (dt != VWL_F32 && dt != VWL_BF16))
+        return false;
+    const long long R = (long long)B * (K + 1);
+    const int C = xfam_chunks(Vt);
+    if (8 * ((R + 7) / 8) * (long long)C > 0x7fffffffLL) // workgroups of the verifier pass
+        return false;
+    L = ws_layout(B, K + 1, Vd, elem_bytes(dt), false);
+    vrec = L.total;
+    total = align256(vrec + (size_t)R * C * kVrecWords * 8);
+    return true;
+}
+
+size_t vwl_asym_xfam_workspace_bytes(int B, int K, int Vd, int Vt, vwl_dtype dt) {
+    WsLayout L;
+    size_t vrec, total;
+    return xfam_layout(B, K, Vd, Vt, dt, L, vrec, total) ? total : 0;
+}
+
+vwl_status asym_verify_xfam(const void *a, const void *b, int Vd, const void *t, int Vt, const int32_t *vmap,
+                            const int32_t *draft, int B, int K, vwl_dtype dt, float beta, float gamma,
+                            float *D, float *gamma_eff, uint8_t *accept, int32_t *fused,
+                            int32_t *accept_len, int32_t *token, int32_t *dev_err,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!vmap)
+        return VWL_ERR_NULL;
+    if (Vt < 1)
+        return VWL_ERR_SHAPE;
+    const size_t need = vwl_asym_xfam_workspace_bytes(B, K, Vd, Vt, dt);
+    // the same checks as asym_verify on the drafter shape, then the verifier's
+    const vwl_status st = asym_check_impl(true, a, b, t, draft, B, K, Vd, (int)dt, beta, gamma, D, gamma_eff,
+                                          accept, fused, accept_len, token, workspace, workspace_bytes,
+                                          need ? need : 1);
+    if (st != VWL_OK)
+        return st;
+    WsLayout L;
+    size_t vrec, total;
+    if (!xfam_layout(B, K, Vd, Vt, dt, L, vrec, total))
+        return VWL_ERR_SHAPE;
+    if (!aligned(vmap, 4) || (dev_err && !aligned(dev_err, 4)))
+        return VWL_ERR_ALIGN;
+    const long long R = (long long)B * (K + 1);
+    Plan plan;
+    if (!make_plan(0, (int)dt, R, Vd, plan, kDeltaNone, kGateCda))
+        return VWL_ERR_HIP;
+    char *ws = static_cast<char *>(workspace);
+    AsymParams p{};
+    p.a = a;
+    p.b = b;
+    p.t = nullptr;
+    p.tv = t;
+    p.Vt = Vt;
+    p.vchunks = xfam_chunks(Vt);
+    p.vmap = vmap;
+    p.vrec = reinterpret_cast<uint64_t *>(ws + vrec);
+    p.draft = draft;
+    p.R = R;
+    p.B = B;
+    p.K = K;
+    p.V = Vd;
+    p.W = plan.W;
+    p.n_teams = plan.n_teams;
+    p.Wmax = L.Wmax;
+    p.chunk = member_chunk(Vd, (int)dt, plan.W);
+    p.beta = beta;
+    p.gamma = gamma;
+    p.log_gamma = std::log((double)gamma);
+    p.D = D;
+    p.geff = gamma_eff;
+    p.accept = accept;
+    p.fused = fused;
+    p.acc_len = accept_len;
+    p.token = token;
+    p.dev_err = dev_err;
+    p.ctl = reinterpret_cast<uint32_t *>(ws + L.ctl);
+    p.row_ctr = reinterpret_cast<uint32_t *>(ws + L.row_ctr);
+    p.req_ctr = reinterpret_cast<uint32_t *>(ws + L.req_ctr);
+    p.row_info = reinterpret_cast<uint32_t *>(ws + L.row_info);
+    p.rec = reinterpret_cast<uint64_t *>(ws + L.rec);
+    return launch_xfam((int)dt, plan, p, stream, g_phase_event.load()) == hipSuccess ? VWL_OK : VWL_ERR_HIP;
+}
+
 size_t vwl_e2sci_workspace_bytes(int B, int W, int V, vwl_dtype dt) {
     if (W < 1 || !shape_ok(B, W - 1, V) || (dt != VWL_F32 && dt != VWL_BF16))
         return 0;

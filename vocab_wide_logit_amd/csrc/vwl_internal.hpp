@@ -85,6 +85,13 @@ struct AsymParams {
     int32_t *fused, *acc_len, *token, *dev_err;
     uint32_t *ctl, *row_ctr, *req_ctr, *row_info;
     uint64_t *rec;
+    // AsymSpec across families: verifier rows on their own vocabulary Vt,
+    // the alignment vmap[Vt] (paired drafter id or -1), per-(row, chunk)
+    // verifier records [R][vchunks][kVrecWords]
+    const void *tv;
+    int Vt, vchunks;
+    const int32_t *vmap;
+    uint64_t *vrec;
     // E2-SCI (a = drafter y, b = target z; `win` rows per request)
     int win;
     const float *thr_in, *omega;
@@ -133,6 +140,14 @@ template <int DS>
 hipError_t launch_asym_ds(int dt, int gate, const Plan &plan, const AsymParams &p, hipStream_t s,
                           hipEvent_t after_rows);
 hipError_t launch_e2sci(int dt, const Plan &plan, const AsymParams &p, hipStream_t s, hipEvent_t after_rows);
+hipError_t launch_xfam(int dt, const Plan &plan, const AsymParams &p, hipStream_t s, hipEvent_t after_rows);
+
+// Cross-family verifier pass: elements per thread and per workgroup chunk,
+// and the record of one (row, chunk).
+constexpr int kXfamEpt = 16;
+constexpr int kXfamChunk = kThreads * kXfamEpt;
+constexpr int kVrecWords = 4;
+inline int xfam_chunks(int Vt) { return (Vt + kXfamChunk - 1) / kXfamChunk; }
 hipError_t launch_rapid(int dt, const Plan &plan, const RapidParams &p, hipStream_t s, hipEvent_t after_rows);
 hipError_t launch_fill_zero(void *ptr, size_t bytes, hipStream_t s);
 

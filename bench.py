@@ -239,9 +239,22 @@ def cpu_baseline(x, runs=3):
         times.append(time.perf_counter() - t0)
     t = _median(times)
     rows = x.B * (x.K + 1)
+    # one thread on a bounded sample (the first 8 requests)
+    n = 8
+    t0 = time.perf_counter()
+    oracle.asym(x.a[:n], x.b[:n], x.t[:n], x.draft[:n], x.beta, x.gamma, x.dtype, nthreads=1)
+    t1 = time.perf_counter() - t0
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": rows / t, "unit": "rows/s", "cores": oracle.max_threads(), "kind": "oracle",
             "sample": "the full B=%d, K=%d, V=%d %s call (%d rows), median of %d runs (%.2f s each)" % (
-                x.B, x.K, x.V, x.dtype, rows, runs, t)}
+                x.B, x.K, x.V, x.dtype, rows, runs, t),
+            "one_thread_rows_per_s": n * (x.K + 1) / t1, "one_thread_sample": "the first %d requests" % n,
+            "nproc": os.cpu_count(), "cpu_model": model}
 
 
 def main():

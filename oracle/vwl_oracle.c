@@ -66,11 +66,16 @@ static double widen(const void *base, int dtype, size_t i)
     return (double)((const float *)base)[i];
 }
 
+/* Threads for the row loops of one call: nthreads > 0 asks for that many,
+ * 0 for the OpenMP default of the process (taken once, at the first call),
+ * so a one-thread call does not leave later calls single-threaded. */
 static void set_threads(int nthreads)
 {
 #ifdef _OPENMP
-    if (nthreads > 0)
-        omp_set_num_threads(nthreads);
+    static int default_threads = 0;
+    if (default_threads == 0)
+        default_threads = omp_get_max_threads();
+    omp_set_num_threads(nthreads > 0 ? nthreads : default_threads);
 #else
     (void)nthreads;
 #endif
@@ -79,6 +84,7 @@ static void set_threads(int nthreads)
 int vwl_oracle_max_threads(void)
 {
 #ifdef _OPENMP
+    set_threads(0);
     return omp_get_max_threads();
 #else
     return 1;

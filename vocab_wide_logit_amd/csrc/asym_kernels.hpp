@@ -72,22 +72,22 @@ struct AsymUse {
 // rho = 2^-d (ratio of the smaller to the larger probability) and
 // Mx = max(p, q), the element contributes
 //   p ln(2p/(p+q)) + q ln(2q/(p+q)) = -ln2 * Mx * g,
-//   g = (1+rho)(log2(1+rho) - 1) + rho*d                    (|x| >= 1.5)
-//     = (1+rho) * s * Q(s),  s = x^2                        (|x| <  1.5)
-// The closed form cancels to O(x^2) from O(x) pieces, so below 1.5 the
-// polynomial Q (fitted to the exact even function x tanh(x/2) - 2 ln
-// cosh(x/2) by jsd_poly_fit.py; 2.4e-7 relative in fp32) takes over; above it
-// the closed form is within 6e-7 relative.  Mx * g (<= 0) is returned.  x is
+//   g = (1+rho)(log2(1+rho) - 1) + rho*d                    (|x| >= 1.2)
+//     = (1+rho) * s * Q(s),  s = x^2                        (|x| <  1.2)
+// The closed form cancels to O(x^2) from O(x) pieces, so below 1.2 the
+// degree-4 polynomial Q (fitted to the exact even function x tanh(x/2) -
+// 2 ln cosh(x/2) by jsd_poly_fit.py; 3.1e-7 relative in fp32) takes over;
+// from 1.2 up the closed form is within 4.4e-7 relative.  Mx * g (<= 0) is returned.  x is
 // formed from a - b and the row log-sum-exp difference, so it carries no
 // rounding of the separate log-probabilities.  Finite for any finite or -inf
 // logits (d is capped at 128, where rho*d underflows to 0; x is NaN only when
 // both logits are -inf, and then Mx = 0).
-constexpr float kJsdQ0 = -0x1.715474p-3f;
-constexpr float kJsdQ1 = 0x1.715312p-6f;
-constexpr float kJsdQ2 = -0x1.48116ap-9f;
-constexpr float kJsdQ3 = 0x1.138e8ep-12f;
-constexpr float kJsdQ4 = -0x1.9e95e8p-16f;
-constexpr float kJsdQ5 = 0x1.9357fap-20f;
+constexpr float kJsdQ0 = -0x1.715472p-3f;
+constexpr float kJsdQ1 = 0x1.7150ccp-6f;
+constexpr float kJsdQ2 = -0x1.47a770p-9f;
+constexpr float kJsdQ3 = 0x1.0cd8e2p-12f;
+constexpr float kJsdQ4 = -0x1.465f7cp-16f;
+constexpr float kJsdX0 = 1.2f; // polynomial below, closed form at and above
 
 __device__ __forceinline__ float jsd_term(float la2, float lb2, float x) {
     const float M = __builtin_amdgcn_exp2f(fmaxf(la2, lb2));
@@ -99,13 +99,12 @@ __device__ __forceinline__ float jsd_term(float la2, float lb2, float x) {
     const float l2 = __builtin_amdgcn_logf(opr);
     const float g_closed = __fmaf_rn(opr, l2, __fmaf_rn(rho, d, -opr)); // opr*(l2 - 1) + rho*d
     const float s = x * x;
-    float q = __fmaf_rn(kJsdQ5, s, kJsdQ4);
-    q = __fmaf_rn(q, s, kJsdQ3);
+    float q = __fmaf_rn(kJsdQ4, s, kJsdQ3);
     q = __fmaf_rn(q, s, kJsdQ2);
     q = __fmaf_rn(q, s, kJsdQ1);
     q = __fmaf_rn(q, s, kJsdQ0);
     const float g_poly = opr * (s * q);
-    return M * (ax < 1.5f ? g_poly : g_closed);
+    return M * (ax < kJsdX0 ? g_poly : g_closed);
 }
 
 // Row log-sum-exps, in log2 units, of N tensors from the W records of a
@@ -306,9 +305,9 @@ __device__ __forceinline__ void pair_pass_ab(const AsymParams &P, long long row,
         online_group<1>(lb, x1b);
     }
     float mx[2] = {la.c, lb.c};
-    block_max<2>(mx, lds_f);
+    block_max<2, false>(mx, lds_f);
     double S[2] = {rescale_to(la, mx[0]), rescale_to(lb, mx[1])};
-    block_sum<2>(S, lds_d);
+    block_sum<2, false>(S, lds_d);
     if (tid == 0) {
         uint64_t *rec = P.rec + ((size_t)row * P.Wmax + member) * kRecWords;
         st_relaxed(rec + 0, f64_bits(S[0]));
@@ -362,7 +361,7 @@ __device__ __forceinline__ void asym_pass_ab(const AsymParams &P, long long row,
         online_group<1>(lt, x1t);
     }
     float mx[4] = {la.c, lb.c, lt.c, fmax_t};
-    block_max<4>(mx, lds_f);
+    block_max<4, false>(mx, lds_f);
     const float Ca = mx[0], Cb = mx[1], Ct = mx[2], Fm = mx[3];
 
     // lowest index of the workgroup's fused maximum (only its holders search)
@@ -386,7 +385,7 @@ __device__ __forceinline__ void asym_pass_ab(const AsymParams &P, long long row,
         }
     }
     double S[3] = {rescale_to(la, Ca), rescale_to(lb, Cb), rescale_to(lt, Ct)};
-    block_sum_min<3>(S, fi, lds_d, lds_i);
+    block_sum_min<3, false>(S, fi, lds_d, lds_i);
     if (tid == 0) {
         uint64_t *rec = P.rec + ((size_t)row * P.Wmax + member) * kRecWords;
         st_relaxed(rec + 0, f64_bits(S[0]));
@@ -411,6 +410,10 @@ constexpr int asym_rows_waves() {
         return NV <= 4 ? 4 : 3;
 }
 
+// The workgroup reductions run without their closing barriers: every reuse
+// of lds_f, lds_d and lds_i is separated from the previous reads by another
+// barrier (the next reduction's, the team wait's, the combine's, or the
+// staging barriers of the next row).
 template <int DT, int NV, int DS, int GATE>
 __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, DS, GATE>())) void asym_rows_kernel(AsymParams P) {
     constexpr int EPV = Elem<DT>::kPerVec;
@@ -555,7 +558,7 @@ __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, DS, GATE>())) void a
             J += jsd_term(__fmaf_rn(psa, kLog2e, -la_c), __fmaf_rn(psb, kLog2e, -lb_c),
                           ((psa - psb) - dl_hi) - dl_lo);
         double Jd[1] = {(double)J};
-        block_sum<1>(Jd, lds_d);
+        block_sum<1, false>(Jd, lds_d);
         if (tid == 0)
             P.rec[((size_t)row * P.Wmax + member) * kRecWords + 6] = f64_bits(Jd[0]);
 

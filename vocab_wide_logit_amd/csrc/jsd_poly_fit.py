@@ -29,7 +29,7 @@ def h_exact(x):
     return out
 
 
-def fit(x0=1.5, deg=5, n=4000):
+def fit(x0=1.2, deg=4, n=4000):
     k = np.arange(n)
     s = x0 ** 2 * 0.5 * (1 - np.cos(np.pi * (k + 0.5) / n))
     q = h_exact(np.sqrt(s)) / s
@@ -50,8 +50,8 @@ def check(cf, x0):
 
 
 if __name__ == "__main__":
-    x0 = float(sys.argv[1]) if len(sys.argv) > 1 else 1.5
-    deg = int(sys.argv[2]) if len(sys.argv) > 2 else 5
+    x0 = float(sys.argv[1]) if len(sys.argv) > 1 else 1.2
+    deg = int(sys.argv[2]) if len(sys.argv) > 2 else 4
     cf = fit(x0, deg)
     print("max relative error of the fp32 evaluation on (0, %g): %.3g" % (x0, check(cf, x0)))
     for i, c in enumerate(cf):

@@ -157,7 +157,10 @@ __device__ __forceinline__ double wave_sum(double x) {
 
 // Workgroup reductions: wave results go through LDS and every thread combines
 // the kWaves values in the same order, so all threads hold the same result.
-template <int N>
+// With TRAIL = false the closing barrier is left out: the caller guarantees
+// that another workgroup barrier separates the reads of `lds` from its next
+// write.
+template <int N, bool TRAIL = true>
 __device__ __forceinline__ void block_max(float (&x)[N], float *lds /* kWaves*N */) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -175,10 +178,11 @@ __device__ __forceinline__ void block_max(float (&x)[N], float *lds /* kWaves*N 
             m = fmaxf(m, lds[w * N + i]);
         x[i] = m;
     }
-    __syncthreads();
+    if (TRAIL)
+        __syncthreads();
 }
 
-template <int N>
+template <int N, bool TRAIL = true>
 __device__ __forceinline__ void block_sum(double (&x)[N], double *lds /* kWaves*N */) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -196,11 +200,12 @@ __device__ __forceinline__ void block_sum(double (&x)[N], double *lds /* kWaves*
             s += lds[w * N + i];
         x[i] = s;
     }
-    __syncthreads();
+    if (TRAIL)
+        __syncthreads();
 }
 
 // Sums of N doubles and the minimum of one int in a single LDS round.
-template <int N>
+template <int N, bool TRAIL = true>
 __device__ __forceinline__ void block_sum_min(double (&x)[N], int &imin, double *lds /* kWaves*N */,
                                               int *ldsi /* kWaves */) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -227,7 +232,8 @@ __device__ __forceinline__ void block_sum_min(double (&x)[N], int &imin, double 
     for (int w = 1; w < kWaves; ++w)
         r = min(r, ldsi[w]);
     imin = r;
-    __syncthreads();
+    if (TRAIL)
+        __syncthreads();
 }
 
 __device__ __forceinline__ int block_min_int(int x, int *lds /* kWaves */) {

@@ -216,3 +216,34 @@ def test_masked_logits(vwl):
         arr[..., 0] = np.where(np.isfinite(arr[..., 0]), arr[..., 0], 0.0)
     x.draft[:] = np.argmax(x.a[:, :2], axis=2)
     check(vwl, x, 1.0, 0.5, label="masked")
+
+
+def test_maximum_drafts(vwl):
+    """K = 63, the largest number of drafts a call takes (64 rows per
+    request), with identical drafter views so long accepted prefixes occur."""
+    x = W.gen_asym(3, 63, 2000, "bf16", seed=31, identical_frac=0.5)
+    dev, ora, rep = check(vwl, x, 1.0, 0.5, label="K=63")
+    assert dev["accept"].shape == (3, 63)
+
+
+def test_negative_beta_and_zero_gamma(vwl):
+    """A negative fusion strength flips the context gain's sign (any finite
+    beta is accepted); gamma = 0 accepts every draft with p_t(d) > 0."""
+    x = W.gen_asym(6, 3, 9000, "f32", seed=32, identical_frac=0.2)
+    check(vwl, x, -1.5, 0.5, label="beta=-1.5")
+    dev, ora, rep = check(vwl, x, 1.0, 0.0, label="gamma=0")
+    assert np.all(dev["accept"] == 1)
+
+
+def test_single_element_rows(vwl):
+    """V = 1: every softmax is the point mass, so D = 0 up to the rounding
+    of the two single-element log-sum-exps (exactly 0 is promised only for
+    bitwise-identical drafter rows), every fused token is 0, and the draft
+    (token 0) passes for gamma < 1.  At gamma = 1 the margin is 0 up to that
+    rounding: every draft sits in the ambiguity window and only parity
+    outside it is required."""
+    x = W.gen_asym(4, 3, 1, "f32", seed=33)
+    dev, ora, rep = check(vwl, x, 1.0, 0.5, label="V=1")
+    assert np.all(np.abs(dev["D"]) <= 1e-12) and np.all(dev["fused"] == 0) and np.all(dev["accept"] == 1)
+    dev, ora, rep = check(vwl, x, 1.0, 1.0, label="V=1 gamma=1")
+    assert rep.excluded == 4

@@ -158,3 +158,23 @@ def test_emitted_token_law(vwl, eta):
     sigma = np.sqrt(law * (1 - law) / N)
     _say("  law max |freq - law| / sigma = %.2f" % float(np.max(np.abs(freq - law) / sigma)))
     assert np.all(np.abs(freq - law) <= 5 * sigma + 1e-9)
+
+
+def test_rapid_maximum_drafts(vwl):
+    """G = 63, the largest number of drafts a call takes."""
+    x = W.gen_rapid(2, 63, 3000, "f32", seed=41)
+    check(vwl, x, 10.0, 1.0, label="G=63")
+
+
+def test_rapid_largest_vocabulary(vwl):
+    """V = VWL_RAPID_MAX_V (2^21), the tail's geometry limit (16 elements per
+    thread, 512 workgroups per request)."""
+    x = W.gen_rapid(1, 1, 1 << 21, "f32", seed=42)
+    check(vwl, x, 10.0, 1.0, label="V=2^21")
+
+
+def test_rapid_no_drafts(vwl):
+    """G = 0: the bonus row alone; the token is drawn from p."""
+    x = W.gen_rapid(3, 0, 5000, "f32", seed=43)
+    dev, ora, rep = check(vwl, x, 10.0, 1.0, label="G=0")
+    assert np.all(dev["accept_len"] == 0)

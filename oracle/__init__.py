@@ -19,6 +19,9 @@ with ctypes and marshals numpy arrays.  Each entry point follows the pages:
   ``phat = softmax(zhat/T)``), key design 3 (tail protection below 10% of the
   peak) and key design 4 (residual ``norm(max(p - phat, p - q, 0))``), with
   rejection sampling against the augmented target (overall framework).
+* ``asym_lmhead`` -- the AsymSpec pass on logits produced from hidden states
+  by the drafter's and the verifier's LM heads (fp64 library matmul, then
+  ``asym``), with the error bound of an fp32 product-sum of the heads.
 * ``asym_xfam`` -- the AsymSpec pass across model families (AsymSpec
   notes, analysis of cross-family pairs): the drafter's gain reaches the
   verifier through a vocabulary alignment, generation restricted to the
@@ -201,6 +204,78 @@ def asym_xfam(a, b, t, vmap, draft, beta: float, gamma: float, dtype: str = "f32
     if rc != 0:
         raise RuntimeError("oracle asym_xfam failed with code %d" % rc)
     return AsymResult(lse, D, ge, fused, gap, top, acc, margin, alen, tok)
+
+
+@dataclass
+class LmheadResult:
+    """The AsymSpec outputs on logits formed from hidden states and LM-head
+    weights, with the per-logit bound on the error of any fp32 summation
+    order of the H products (|h|.|W| * n * 2^-24 / (1 - n * 2^-24), n = H)."""
+    res: AsymResult
+    err_a: np.ndarray   # [B, K+1] largest bound over the row's a logits
+    err_b: np.ndarray   # [B, K+1]
+    err_t: np.ndarray   # [B, K+1]
+    err_bd: np.ndarray  # [B, K] bound of b at the draft
+    err_td: np.ndarray  # [B, K] bound of t at the draft
+
+
+def _widen_bf16(x: np.ndarray) -> np.ndarray:
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    bits = np.ascontiguousarray(x, np.float32).view(np.uint32)
+    if np.any(bits & 0xFFFF):
+        raise ValueError("LM-head inputs must be bf16-exact")
+    return x.astype(np.float64)
+
+
+def asym_lmhead(h_a, h_b, W_d, h_t, W_t, draft, beta: float, gamma: float, delta: str = "a-b",
+                gate: str = "cda", nthreads: int = 0) -> LmheadResult:
+    """Oracle of AsymSpec on logits produced from hidden states by LM heads:
+    a = h_a W_d^T, b = h_b W_d^T (the drafter's two views share its head),
+    t = h_t W_t^T; h_* are [B, K+1, H] and W_* [V, H], all bf16 values.  The
+    logits are formed in fp64 (a library matmul on the exactly widened
+    inputs); the pass then follows asym()."""
+    ha, hb, ht = (_widen_bf16(x) for x in (h_a, h_b, h_t))
+    Wd, Wt = _widen_bf16(W_d), _widen_bf16(W_t)
+    B, P, Hd = ha.shape
+    V = Wd.shape[0]
+    a = np.ascontiguousarray(ha.reshape(B * P, Hd) @ Wd.T).reshape(B, P, V)
+    b = np.ascontiguousarray(hb.reshape(B * P, Hd) @ Wd.T).reshape(B, P, V)
+    t = np.ascontiguousarray(ht.reshape(B * P, ht.shape[2]) @ Wt.T).reshape(B, P, V)
+    lib = _load()
+    K = P - 1
+    draft = np.ascontiguousarray(draft, dtype=np.int32).reshape(B, K)
+    lse = np.zeros((B, P, 3))
+    D = np.zeros((B, P))
+    ge = np.zeros((B, P))
+    fused = np.zeros((B, P), np.int32)
+    gap = np.zeros((B, P))
+    top = np.zeros((B, P))
+    acc = np.zeros((B, max(K, 0)), np.uint8)
+    margin = np.zeros((B, max(K, 0)))
+    alen = np.zeros(B, np.int32)
+    tok = np.zeros(B, np.int32)
+    rc = lib.vwl_oracle_asym(_ptr(a), _ptr(b), _ptr(t), 2, _ptr(draft), B, K, V,
+                             float(np.float32(beta)), float(np.float32(gamma)),
+                             DELTA_SOURCES[delta], GATES[gate], _ptr(lse), _ptr(D), _ptr(ge), _ptr(fused),
+                             _ptr(gap), _ptr(top), _ptr(acc), _ptr(margin), _ptr(alen), _ptr(tok), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle asym (lm head) failed with code %d" % rc)
+    res = AsymResult(lse, D, ge, fused, gap, top, acc, margin, alen, tok)
+    u = 2.0 ** -24
+
+    def bound(h, W):
+        n = h.shape[-1]
+        g = n * u / (1 - n * u)
+        return g * (np.abs(h.reshape(-1, n)) @ np.abs(W).T).reshape(B, P, -1)
+
+    ea, eb, et = bound(ha, Wd), bound(hb, Wd), bound(ht, Wt)
+    bi = np.arange(B)[:, None]
+    ii = np.arange(K)[None, :]
+    d = np.clip(draft, 0, V - 1)
+    return LmheadResult(res, ea.max(axis=2), eb.max(axis=2), et.max(axis=2),
+                        eb[bi, ii, d] if K else np.zeros((B, 0)), et[bi, ii, d] if K else np.zeros((B, 0)))
 
 
 @dataclass

@@ -53,6 +53,7 @@
 
 #define ORACLE_F32 0
 #define ORACLE_BF16 1
+#define ORACLE_F64 2 /* rows given as doubles (logits formed by the caller in fp64) */
 
 /* Exact widening of one stored logit to double. */
 static double widen(const void *base, int dtype, size_t i)
@@ -63,6 +64,8 @@ static double widen(const void *base, int dtype, size_t i)
         memcpy(&f, &bits, sizeof f);
         return (double)f;
     }
+    if (dtype == ORACLE_F64)
+        return ((const double *)base)[i];
     return (double)((const float *)base)[i];
 }
 
@@ -153,7 +156,7 @@ int vwl_oracle_asym(const void *a, const void *b, const void *t, int dtype,
                     double *top, uint8_t *accept, double *margin,
                     int32_t *accept_len, int32_t *token, int nthreads)
 {
-    if (B < 1 || K < 0 || V < 1 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16))
+    if (B < 1 || K < 0 || V < 1 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16 && dtype != ORACLE_F64))
         return 1;
     if (delta_src < 0 || delta_src > 2 || gate < 0 || gate > 1)
         return 1;

@@ -415,6 +415,43 @@ def test_fixed_gate_against_cda(oracle_lib):
     assert np.any(rc.accept > rf.accept)  # CDA does relax somewhere on these rows
 
 
+# ------------------------------------------------ AsymSpec from hidden states
+# The step before the pass on the AsymSpec pages: the logits are the LM
+# heads' products of the hidden states.
+
+def test_lmhead_identity_heads_reduce_to_the_pass(oracle_lib):
+    """With H = V and scaled identity heads the logits are c*h exactly, and
+    the LM-head oracle is the AsymSpec oracle on those rows, bit for bit."""
+    x = W.gen_asym(3, 2, 96, "bf16", seed=70, identical_frac=0.2, tie_frac=0.3)
+    for c in (1.0, 2.0):
+        Wh = (c * np.eye(96)).astype(np.float32)
+        r = oracle.asym_lmhead(x.a, x.b, Wh, x.t, Wh, x.draft, 1.0, 0.5).res
+        ref = oracle.asym(c * x.a, c * x.b, c * x.t, x.draft, 1.0, 0.5, "f32")
+        for f in ("lse", "D", "gamma_eff", "fused", "gap", "top", "accept", "margin", "accept_len", "token"):
+            np.testing.assert_array_equal(getattr(r, f), getattr(ref, f), err_msg=f)
+        rf = oracle.asym_lmhead(x.a, x.b, Wh, x.t, Wh, x.draft, 1.0, 0.5, gate="fixed").res
+        np.testing.assert_array_equal(rf.accept, oracle.asym(c * x.a, c * x.b, c * x.t, x.draft, 1.0, 0.5, "f32",
+                                                             gate="fixed").accept)
+
+
+def test_lmhead_error_bound_covers_fp32_sums(oracle_lib):
+    """The reported bound on an fp32 product-sum of the heads covers the
+    actual error of fp32 matrix products (two summation orders) of the same
+    inputs."""
+    x = W.gen_lmhead(2, 2, 700, 512, seed=71)
+    r = oracle.asym_lmhead(x.h_a, x.h_b, x.W_d, x.h_t, x.W_t, x.draft, 1.0, 0.5)
+    ha = x.h_a.reshape(-1, x.Hd)
+    exact = ha.astype(np.float64) @ x.W_d.astype(np.float64).T
+    f32 = (ha @ x.W_d.T).astype(np.float64)
+    seq = np.zeros((ha.shape[0], x.V), np.float32)
+    for k in range(x.Hd):          # one product at a time: the longest chain of roundings
+        seq = (seq + np.outer(ha[:, k], x.W_d[:, k])).astype(np.float32)
+    err = r.err_a.reshape(-1)
+    assert np.all(np.abs(f32 - exact).max(axis=1) <= err)
+    assert np.all(np.abs(seq.astype(np.float64) - exact).max(axis=1) <= err)
+    assert np.all(err < 1e-2)
+
+
 # ------------------------------------------------ AsymSpec across model families
 # AsymSpec notes, the analysis of cross-family pairs: the drafter's gain
 # reaches the verifier through a vocabulary alignment of string-identical

@@ -36,6 +36,15 @@ Recipe (one logit row = one draft position of one request):
   is ``t[v] = z[map[v]] + N(0, 0.5^2)`` on paired ids and ``N(0, 2^2)``
   elsewhere.  Drafts are the drafter's greedy tokens restricted to the
   paired drafter ids, given as the paired verifier ids.
+* AsymSpec from hidden states (LM heads): drafter head W_d [V, Hd] ~
+  N(0, (2/sqrt(Hd))^2) and hidden states h_a ~ N(0, 1), so the logits
+  h_a W_d^T are N(0, 2^2); each row plants a spike of +8 at a token s by
+  adding 8 w_s/|w_s|^2 (w_s = W_d[s]) to h_a; h_b = h_a + N(0, 0.25^2) (the
+  compressed view, logit noise ~0.5), with the spike moved to another token
+  in an exact 30% of rows.  The verifier head W_t = [W_d | W_x] (Ht = 2 Hd,
+  W_x ~ N(0, (0.5/sqrt(Hd))^2)) and h_t = [h_b + N(0, 0.1^2) | N(0, 1)], so
+  t ~ b + N(0, 0.5^2) (the verifier reads the compressed context).  Drafts
+  are the planted tokens s.  Everything is rounded to bf16.
 * E2-SCI: target ``z_t = z + N(0, 0.5^2)``; drafter ``y = z + N(0,
   sigma^2)`` with ``sigma`` uniform on [0.1, 1.0] per row (a spread of
   divergences); "identical" rows set ``y := z_t`` bit for bit (divergence
@@ -355,6 +364,93 @@ def gen_xfam(B: int, K: int, Vd: int, Vt: int, n_shared: int, dtype: str = F32, 
 
 
 # --------------------------------------------------------------------------
+# AsymSpec from hidden states and LM heads
+# --------------------------------------------------------------------------
+@dataclass
+class LmheadInputs:
+    """Hidden states h_a, h_b [B, K+1, Hd], h_t [B, K+1, Ht], heads W_d
+    [V, Hd], W_t [V, Ht] (float32 arrays holding bf16 values), drafts [B, K]."""
+
+    h_a: np.ndarray
+    h_b: np.ndarray
+    h_t: np.ndarray
+    W_d: np.ndarray
+    W_t: np.ndarray
+    draft: np.ndarray
+    beta: float
+    gamma: float
+    seed: int
+    dtype: str = BF16
+    name: str = ""
+
+    @property
+    def B(self):
+        return self.h_a.shape[0]
+
+    @property
+    def K(self):
+        return self.h_a.shape[1] - 1
+
+    @property
+    def V(self):
+        return self.W_d.shape[0]
+
+    @property
+    def Hd(self):
+        return self.W_d.shape[1]
+
+    @property
+    def Ht(self):
+        return self.W_t.shape[1]
+
+    def weight_bytes(self) -> int:
+        return 2 * self.V * (self.Hd + self.Ht)
+
+
+def gen_lmhead(B: int, K: int, V: int, Hd: int, seed: int = SEED_BASE + 8, displaced_frac: float = 0.3,
+               beta: float = 1.0, gamma: float = 0.5, name: str = "") -> LmheadInputs:
+    """Generate one LM-head workload following the module recipe (Ht = 2 Hd)."""
+    if B < 1 or K < 0 or V < 2 or Hd < 1:
+        raise ValueError("need B >= 1, K >= 0, V >= 2, Hd >= 1")
+    R = B * (K + 1)
+    ss = np.random.SeedSequence(seed)
+    s_w, s_h, s_sel = ss.spawn(3)
+    gw = np.random.default_rng(s_w)
+    W_d = round_to_bf16((gw.standard_normal((V, Hd)) * (2.0 / np.sqrt(Hd))).astype(np.float32))
+    W_x = round_to_bf16((gw.standard_normal((V, Hd)) * (0.5 / np.sqrt(Hd))).astype(np.float32))
+    W_t = np.ascontiguousarray(np.concatenate([W_d, W_x], axis=1))
+    sel = np.random.default_rng(s_sel)
+    disp = np.zeros(R, bool)
+    disp[_choose_rows(sel, np.arange(R), int(round(displaced_frac * R)))] = True
+    gh = np.random.default_rng(s_h)
+    h_a = np.empty((R, Hd), np.float32)
+    h_b = np.empty((R, Hd), np.float32)
+    h_t = np.empty((R, 2 * Hd), np.float32)
+    spike = np.empty(R, np.int64)
+    for r in range(R):
+        s = int(gh.integers(0, V))
+        w = W_d[s].astype(np.float64)
+        base = gh.standard_normal(Hd)
+        ha = base + 8.0 * w / np.dot(w, w)
+        hb = ha + 0.25 * gh.standard_normal(Hd)
+        if disp[r]:
+            s2 = int(gh.integers(0, V - 1))
+            s2 = s2 + 1 if s2 >= s else s2
+            w2 = W_d[s2].astype(np.float64)
+            hb = hb - 8.0 * w / np.dot(w, w) + 8.0 * w2 / np.dot(w2, w2)
+        h_a[r] = round_to_bf16(ha.astype(np.float32))
+        h_b[r] = round_to_bf16(hb.astype(np.float32))
+        hc = h_b[r].astype(np.float64) + 0.1 * gh.standard_normal(Hd)
+        h_t[r] = round_to_bf16(np.concatenate([hc, gh.standard_normal(Hd)]).astype(np.float32))
+        spike[r] = s
+    P = K + 1
+    draft = spike.reshape(B, P)[:, :K].astype(np.int32)
+    return LmheadInputs(h_a=h_a.reshape(B, P, Hd), h_b=h_b.reshape(B, P, Hd), h_t=h_t.reshape(B, P, 2 * Hd),
+                        W_d=W_d, W_t=W_t, draft=np.ascontiguousarray(draft), beta=float(beta),
+                        gamma=float(gamma), seed=seed, name=name)
+
+
+# --------------------------------------------------------------------------
 # E2-SCI inputs
 # --------------------------------------------------------------------------
 @dataclass
@@ -604,3 +700,12 @@ def xfam_batched(seed: int = SEED_BASE + 7) -> XfamInputs:
     (Vt=128256), 109,566 shared tokens plus 16 special pairs, bf16."""
     return gen_xfam(64, 2, VOCAB_QWEN3, VOCAB_LLAMA31, VOCAB_SHARED_QWEN_LLAMA, BF16, seed,
                     name="xfam_B64_K2_Vd151936_Vt128256_bf16")
+
+
+HIDDEN_QWEN3_4B = 2560   # the pages' main drafter (model card hidden size)
+
+
+def lmhead_batched(seed: int = SEED_BASE + 8) -> LmheadInputs:
+    """B=64, K=2, V=151936, Hd=2560 (Qwen3-4B drafter head), Ht=5120 (a
+    Qwen3-32B-sized verifier head), bf16."""
+    return gen_lmhead(64, 2, VOCAB_QWEN3, HIDDEN_QWEN3_4B, seed, name="lmhead_B64_K2_V151936_Hd2560_Ht5120_bf16")

@@ -194,6 +194,34 @@ vwl_status asym_verify_xfam(const void *a, const void *b, int Vd, const void *t,
                             void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * AsymSpec from hidden states (the step before the pass on the AsymSpec
+ * pages: the LM heads turn hidden states into logits).  The heads' products
+ * are formed on the matrix cores and the pass runs in their epilogue, so no
+ * logit row is written to memory:
+ *   a = h_a W_d^T, b = h_b W_d^T (the drafter's head, full and compressed
+ *   context), t = h_t W_t^T (the verifier's head); then everything as
+ *   asym_verify (delta = a - b, the CDA gate).
+ * Inputs, all bf16, row-major, 16-byte aligned:
+ *   h_a, h_b  [B][K+1][Hd]; h_t [B][K+1][Ht]; W_d [V][Hd]; W_t [V][Ht]
+ *   (one row of a head per vocabulary entry); Hd and Ht multiples of 64
+ *   (else VWL_ERR_SHAPE); draft [B][K] int32.
+ * Outputs as asym_verify.  Precision: each logit is an fp32 sum of exact
+ *   bf16 products (MFMA accumulation), so within Hd (or Ht) * 2^-24 *
+ *   sum_k |h_k w_k| of its value; the draft's logits in the test are fp64
+ *   dot products; statistics as asym_verify.
+ * Workspace: vwl_asym_lmhead_workspace_bytes (shape only), zero-filled
+ * before first use; left zero-filled where it must be.
+ * --------------------------------------------------------------------------- */
+size_t vwl_asym_lmhead_workspace_bytes(int B, int K, int V, int Hd, int Ht);
+
+vwl_status asym_verify_lmhead(const void *h_a, const void *h_b, const void *W_d,
+                              const void *h_t, const void *W_t, const int32_t *draft,
+                              int B, int K, int V, int Hd, int Ht, float beta, float gamma,
+                              float *D, float *gamma_eff, uint8_t *accept, int32_t *fused,
+                              int32_t *accept_len, int32_t *token, int32_t *dev_err,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * E2-SCI adaptive JSD acceptance ("E2-SCI: Elastic Edge-Cloud Speculative
  * Decoding via Credit Inertia" notes, key design 3 "online adaptive
  * verification", with the credit state of key design 1)

@@ -254,3 +254,58 @@ def compare_e2sci(dev: dict, ora, T, identical=None, rtol: float = REL_TOL,
         if abs(t_d[bi] - ora.T_next[bi]) > state_rtol * abs(ora.T_next[bi]) + 1e-7:
             rep.fail("T_next mismatch at request %d: dev %r oracle %r" % (bi, t_d[bi], ora.T_next[bi]))
     return rep
+
+
+def compare_lmhead(dev: dict, lm, K: int, beta: float, rtol: float = REL_TOL) -> Report:
+    """AsymSpec from hidden states: the device's logits carry the error of an
+    fp32 product-sum, bounded per logit by the oracle (lm: oracle.LmheadResult,
+    row maxima err_a, err_b, err_t).  The windows widen by those bounds: a
+    logit error e moves a log-sum-exp by at most e, the JSD by at most
+    2 (e_a + e_b), a margin (draft logits exact) by e_t + e_b + 2 (e_a + e_b),
+    and a fused score by e_t + |beta| (e_a + e_b)."""
+    ora = lm.res
+    rep = Report()
+    ea, eb, et = lm.err_a, lm.err_b, lm.err_t
+    dD = 2.0 * (ea + eb)
+    D_d = np.asarray(dev["D"], np.float64)
+    bad = np.abs(D_d - ora.D) > rtol * np.abs(ora.D) + dD + D_ABS_FLOOR
+    if np.any(bad):
+        rep.fail("D outside its window on %d rows" % int(bad.sum()))
+    g_d = np.asarray(dev["gamma_eff"], np.float64)
+    badg = np.abs(g_d - ora.gamma_eff) > (rtol + dD) * np.abs(ora.gamma_eff) + 1e-30
+    if np.any(badg):
+        rep.fail("gamma_eff outside its window on %d rows" % int(badg.sum()))
+    rep.stats["D_max_abs"] = float(np.max(np.abs(D_d - ora.D)))
+    rep.stats["D_window_max"] = float(np.max(dD))
+    gap_w = 2.0 * (et + abs(beta) * (ea + eb)) + GAP_EPS * np.maximum(np.abs(ora.top), 1.0)
+    amb_f = (ora.gap > 0.0) & (ora.gap <= gap_w)
+    f_d = np.asarray(dev["fused"])
+    mism_f = (f_d != ora.fused) & ~amb_f
+    if np.any(mism_f):
+        rep.fail("fused token mismatch on %d rows (first %s)" % (int(mism_f.sum()), np.argwhere(mism_f)[0].tolist()))
+    rep.stats["fused_ambiguous"] = int(amb_f.sum())
+    B = f_d.shape[0]
+    if K > 0:
+        m_w = (et + eb + dD)[:, :K] + MARGIN_EPS
+        amb_a = np.abs(ora.margin) <= m_w
+        a_d = np.asarray(dev["accept"]).astype(np.uint8)
+        mism_a = (a_d != ora.accept) & ~amb_a
+        if np.any(mism_a):
+            rep.fail("accept mismatch on %d drafts (first %s)" % (int(mism_a.sum()), np.argwhere(mism_a)[0].tolist()))
+        rep.stats["accept_ambiguous"] = int(amb_a.sum())
+        rep.stats["acceptance_rate"] = float(ora.accept.mean())
+    else:
+        amb_a = np.zeros((B, 0), bool)
+    al_d = np.asarray(dev["accept_len"])
+    tok_d = np.asarray(dev["token"])
+    for bi in range(B):
+        n = int(ora.accept_len[bi])
+        if (K > 0 and amb_a[bi, :min(n + 1, K)].any()) or amb_f[bi, n]:
+            rep.excluded += 1
+            continue
+        rep.checked += 1
+        if al_d[bi] != n:
+            rep.fail("accept_len mismatch at request %d: dev %d oracle %d" % (bi, al_d[bi], n))
+        if tok_d[bi] != ora.token[bi]:
+            rep.fail("token mismatch at request %d: dev %d oracle %d" % (bi, tok_d[bi], ora.token[bi]))
+    return rep

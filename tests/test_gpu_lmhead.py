@@ -1,0 +1,89 @@
+"""GPU parity of ``asym_verify_lmhead`` (AsymSpec from hidden states: the LM
+heads' products on the matrix cores with the pass in their epilogue) against
+the fp64 oracle (fp64 logits from the same bf16 inputs), through the C ABI.
+The windows widen by the oracle's bound on the fp32 product-sum of each
+logit (oracle/parity.py, compare_lmhead)."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from oracle.parity import compare_lmhead
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print("[lmhead] " + msg, flush=True)
+
+
+@pytest.fixture(scope="module")
+def vwl():
+    import vocab_wide_logit_amd as m
+    m.load_library()
+    return m
+
+
+def _bf(vwl, x):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16).cuda()
+
+
+def run_dev(vwl, x, beta, gamma):
+    import torch
+    d = torch.from_numpy(np.ascontiguousarray(x.draft)).cuda()
+    out = vwl.asym_verify_lmhead(_bf(vwl, x.h_a), _bf(vwl, x.h_b), _bf(vwl, x.W_d), _bf(vwl, x.h_t),
+                                 _bf(vwl, x.W_t), d, beta, gamma)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out._asdict().items()}
+
+
+def check(vwl, x, beta=None, gamma=None, label=""):
+    beta = x.beta if beta is None else beta
+    gamma = x.gamma if gamma is None else gamma
+    _say("case %s B=%d K=%d V=%d Hd=%d Ht=%d beta=%g gamma=%g" % (label, x.B, x.K, x.V, x.Hd, x.Ht, beta, gamma))
+    dev = run_dev(vwl, x, beta, gamma)
+    lm = oracle.asym_lmhead(x.h_a, x.h_b, x.W_d, x.h_t, x.W_t, x.draft, beta, gamma)
+    rep = compare_lmhead(dev, lm, x.K, beta)
+    _say("  " + str(rep))
+    assert rep.ok, str(rep)
+    assert dev["dev_err"][0] == 0
+    return dev, lm, rep
+
+
+def test_small(vwl):
+    x = W.gen_lmhead(3, 2, 1000, 128, seed=81)
+    check(vwl, x, label="small")
+
+
+@pytest.mark.parametrize("B,K,V,Hd", [(1, 0, 1, 64), (2, 1, 127, 64), (5, 4, 129, 192), (30, 2, 3001, 64),
+                                      (23, 3, 20000, 128)])
+def test_shapes(vwl, B, K, V, Hd):
+    """Row counts that are not multiples of the 64-row tile, vocabularies
+    below, at and past the 128-token tile, one token, no drafts."""
+    x = W.gen_lmhead(B, K, max(V, 2), Hd, seed=82 + V + B) if V > 1 else None
+    if x is None:  # one-token vocabulary: the generator needs two tokens to plant a spike
+        x = W.gen_lmhead(B, K, 2, Hd, seed=82)
+        x.W_d = np.ascontiguousarray(x.W_d[:1])
+        x.W_t = np.ascontiguousarray(x.W_t[:1])
+        x.draft[:] = 0
+    check(vwl, x, label="shape")
+
+
+def test_medium_vocabulary(vwl):
+    """The Qwen3 vocabulary with small heads: many vocabulary ranges per row."""
+    x = W.gen_lmhead(8, 2, 151936, 256, seed=83)
+    dev, lm, rep = check(vwl, x, label="V=151936")
+    assert rep.checked >= 6
+
+
+def test_bench_shape(vwl):
+    """B=64, K=2, V=151936, Hd=2560, Ht=5120: the shape the bench times.  At
+    these head widths the worst-case product-sum bound is wide (a few 1e-2 on
+    D), so more decisions fall in the windows; the deviations observed are
+    near the fp32 rounding of the statistics."""
+    x = W.lmhead_batched()
+    for beta, gamma in ((1.0, 0.5), (0.0, 1.0)):
+        dev, lm, rep = check(vwl, x, beta, gamma, label=x.name)
+        assert rep.checked >= 40
+        assert rep.stats["D_max_abs"] < 1e-5

@@ -20,6 +20,8 @@ Entry points (same names as the C ABI):
 * ``asym_verify_xfam`` -- the AsymSpec pass across model families: drafter
   rows on the drafter vocabulary, verifier rows on the verifier's, joined by
   a vocabulary alignment (verifier id -> paired drafter id or -1).
+* ``asym_verify_lmhead`` -- the AsymSpec pass from hidden states: the LM
+  heads' products on the matrix cores with the pass in their epilogue.
 * ``e2sci_verify`` -- E2-SCI adaptive JSD acceptance (E2-SCI notes, key
   design 3): per-position divergence of drafter and target against the
   window threshold, then the caller-owned credit state and next threshold.
@@ -59,7 +61,8 @@ SYMBOLS = ("vwl_status_string", "vwl_version", "vwl_workspace_reset",
            "vwl_plan_info", "vwl_asym_check", "vwl_rapid_check",
            "vwl_set_plan_override", "vwl_set_phase_event",
            "vwl_e2sci_workspace_bytes", "e2sci_verify", "vwl_e2sci_plan_info",
-           "vwl_asym_xfam_workspace_bytes", "asym_verify_xfam")
+           "vwl_asym_xfam_workspace_bytes", "asym_verify_xfam",
+           "vwl_asym_lmhead_workspace_bytes", "asym_verify_lmhead")
 
 
 class E2sciParams(ctypes.Structure):
@@ -118,6 +121,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.vwl_rapid_check.restype = i
         lib.vwl_set_plan_override.argtypes = [i, i, i]
         lib.vwl_set_plan_override.restype = i
+        lib.vwl_asym_lmhead_workspace_bytes.argtypes = [i, i, i, i, i]
+        lib.vwl_asym_lmhead_workspace_bytes.restype = sz
+        lib.asym_verify_lmhead.argtypes = [P, P, P, P, P, P, i, i, i, i, i, f, f, P, P, P, P, P, P, P, P, sz, P]
+        lib.asym_verify_lmhead.restype = i
         lib.vwl_asym_xfam_workspace_bytes.argtypes = [i, i, i, i, i]
         lib.vwl_asym_xfam_workspace_bytes.restype = sz
         lib.asym_verify_xfam.argtypes = [P, P, i, P, i, P, P, i, i, i, f, f, P, P, P, P, P, P, P, P, sz, P]
@@ -358,6 +365,41 @@ def asym_verify_xfam(a: torch.Tensor, b: torch.Tensor, t: torch.Tensor, vmap: to
                                 _ptr(out.D), _ptr(out.gamma_eff), _ptr(out.accept) if K > 0 else None,
                                 _ptr(out.fused), _ptr(out.accept_len), _ptr(out.token), _ptr(out.dev_err),
                                 _ptr(workspace), workspace.numel(), ctypes.c_void_p(stream.cuda_stream))
+    _check(code)
+    return out
+
+
+def asym_verify_lmhead(h_a: torch.Tensor, h_b: torch.Tensor, W_d: torch.Tensor, h_t: torch.Tensor,
+                       W_t: torch.Tensor, draft: torch.Tensor, beta: float, gamma: float, *,
+                       out: Optional[AsymOut] = None, workspace: Optional[torch.Tensor] = None) -> AsymOut:
+    """AsymSpec from hidden states on the current stream (bf16 tensors):
+    h_a, h_b [B, K+1, Hd], h_t [B, K+1, Ht], W_d [V, Hd], W_t [V, Ht];
+    draft [B, K] int32."""
+    lib = load_library()
+    for name, x in (("h_a", h_a), ("h_b", h_b), ("W_d", W_d), ("h_t", h_t), ("W_t", W_t)):
+        _dev_tensor(x, name, torch.bfloat16)
+    if h_a.dim() != 3 or h_b.shape != h_a.shape or h_t.dim() != 3 or h_t.shape[:2] != h_a.shape[:2]:
+        raise ValueError("h_a, h_b must be [B, K+1, Hd] and h_t [B, K+1, Ht]")
+    B, P, Hd = h_a.shape
+    Ht = h_t.shape[2]
+    V = W_d.shape[0]
+    if tuple(W_d.shape) != (V, Hd) or tuple(W_t.shape) != (V, Ht):
+        raise ValueError("W_d must be [V, Hd] and W_t [V, Ht]")
+    K = P - 1
+    _dev_tensor(draft, "draft", torch.int32)
+    if tuple(draft.shape) != (B, K):
+        raise ValueError("draft must be [B, K]")
+    if out is None:
+        out = asym_out(B, K, h_a.device)
+    stream = torch.cuda.current_stream(h_a.device)
+    if workspace is None:
+        need = int(lib.vwl_asym_lmhead_workspace_bytes(B, K, V, Hd, Ht))
+        workspace = _workspace_sized(("lmhead", B, K, V, Hd, Ht), need, h_a.device, stream)
+    code = lib.asym_verify_lmhead(_ptr(h_a), _ptr(h_b), _ptr(W_d), _ptr(h_t), _ptr(W_t),
+                                  _ptr(draft) if K > 0 else None, B, K, V, Hd, Ht, float(beta), float(gamma),
+                                  _ptr(out.D), _ptr(out.gamma_eff), _ptr(out.accept) if K > 0 else None,
+                                  _ptr(out.fused), _ptr(out.accept_len), _ptr(out.token), _ptr(out.dev_err),
+                                  _ptr(workspace), workspace.numel(), ctypes.c_void_p(stream.cuda_stream))
     _check(code)
     return out
 

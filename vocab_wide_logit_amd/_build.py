@@ -10,7 +10,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIBDIR, "libvwl.so")
-SOURCES = ["asym_ab.hip", "asym_a.hip", "asym_tb.hip", "pair_pass.hip", "rapid.hip", "vwl_api.cpp"]
+SOURCES = ["asym_ab.hip", "asym_a.hip", "asym_tb.hip", "pair_pass.hip", "lmhead.hip", "rapid.hip",
+           "vwl_api.cpp"]
 HEADERS = ["asym_kernels.hpp", "vwl_device.hpp", "vwl_internal.hpp"]
 
 ARCH = os.environ.get("VWL_OFFLOAD_ARCH", "gfx950")

@@ -1,0 +1,434 @@
+// AsymSpec from hidden states: the LM heads' products formed on the matrix
+// cores with the pass in their epilogue, so the logit rows never reach HBM
+// (the step before the AsymSpec pass on its pages: the drafter's head turns
+// the full- and compressed-context hidden states into a and b, the
+// verifier's head turns its hidden state into t).
+//
+//   a = h_a W_d^T, b = h_b W_d^T   (one drafter head, two views)
+//   t = h_t W_t^T
+//
+// Launch 1, lmhead_kernel<1>: each workgroup owns 64 rows and a range of the
+// vocabulary, walked in tiles of 128 tokens.  Per tile the 4 waves form a
+// [64 x 128] block of a, b (sharing each W_d tile) and then of t with bf16
+// MFMA 16x16x32 (fp32 accumulation), staged through LDS in 64-wide k
+// blocks; the epilogue folds the block into per-row online statistics of a,
+// b, t (integer references, as in the row kernel) and the fused maximum
+// t + beta*(a - b) with its lowest index.  One record per (row, range), in
+// the row kernel's record layout.
+// Launch 2, lmhead_combine_kernel: L_a, L_b per row from the records.
+// Launch 3, lmhead_kernel<2>: the same a, b blocks again (identical
+// arithmetic, so identical bits) and the JSD terms against L_a, L_b.
+// Launch 4, lmhead_finalize_kernel: D, the threshold, the fused token, the
+// draft's logits as fp64 dot products, the test and the scan.
+#include "asym_kernels.hpp"
+
+namespace vwl {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kLmRows = 64;  // rows per workgroup (4 MFMA row blocks of 16)
+constexpr int kLmCols = 128; // vocabulary per tile (32 per wave, 2 MFMA column blocks)
+constexpr int kLmKB = 64;    // k per LDS stage (2 MFMA k-steps of 32)
+
+// One stage: [rows][8 chunks of 8 bf16]; chunk c of row r sits in slot
+// c ^ (r & 7), so the 16 rows an MFMA operand read touches spread over the
+// banks.
+struct LmStage {
+    uint4 a[kLmRows * 8];
+    uint4 b[kLmRows * 8];
+    uint4 w[kLmCols * 8];
+};
+
+__device__ __forceinline__ int lm_slot(int r, int c) { return r * 8 + (c ^ (r & 7)); }
+
+// Stage rows [row0, row0 + NR) (rows past max_row repeat it) by k
+// [k0, k0 + 64) of a row-major bf16 matrix with H columns.  Lane L of a wave
+// instruction fills LDS slot base + L, so each wave instruction reads 8 whole
+// 128-byte row pieces.
+template <int NR>
+__device__ __forceinline__ void lm_stage(uint4 *dst, const uint16_t *M, long long row0, long long max_row, int H,
+                                         int k0) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    constexpr int kInstr = NR * 8 / 64;
+    for (int j = wave; j < kInstr; j += kWaves) {
+        const int p = j * 64 + lane;
+        const int r = p >> 3, slot = p & 7;
+        const int c = slot ^ (r & 7);
+        long long row = row0 + r;
+        if (row > max_row)
+            row = max_row;
+        g2lds16(reinterpret_cast<const uint4 *>(M + (size_t)row * (size_t)H + k0 + 8 * c), dst + j * 64);
+    }
+}
+
+__device__ __forceinline__ bf16x8_t lm_frag(const uint4 *tile, int r, int c) {
+    const uint4 v = tile[lm_slot(r, c)];
+    bf16x8_t f;
+    __builtin_memcpy(&f, &v, 16);
+    return f;
+}
+
+// All-reductions over the 16 lanes of a DPP row (the lanes that share rows
+// in the MFMA 16x16 accumulator layout).
+__device__ __forceinline__ float row16_max(float x) {
+    x = fmaxf(x, __int_as_float(dpp_i<kDppXor1>(__float_as_int(x))));
+    x = fmaxf(x, __int_as_float(dpp_i<kDppXor2>(__float_as_int(x))));
+    x = fmaxf(x, __int_as_float(dpp_i<kDppHalfMirror>(__float_as_int(x))));
+    return fmaxf(x, __int_as_float(dpp_i<kDppMirror>(__float_as_int(x))));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+    x += __int_as_float(dpp_i<kDppXor1>(__float_as_int(x)));
+    x += __int_as_float(dpp_i<kDppXor2>(__float_as_int(x)));
+    x += __int_as_float(dpp_i<kDppHalfMirror>(__float_as_int(x)));
+    return x + __int_as_float(dpp_i<kDppMirror>(__float_as_int(x)));
+}
+__device__ __forceinline__ int row16_min_int(int x) {
+    x = min(x, dpp_i<kDppXor1>(x));
+    x = min(x, dpp_i<kDppXor2>(x));
+    x = min(x, dpp_i<kDppHalfMirror>(x));
+    return min(x, dpp_i<kDppMirror>(x));
+}
+
+// The [64 x 128] block of one head for one or two sets of hidden states
+// (TWO: h0 and h1 share the head tile), accumulated over k in [0, H).
+template <bool TWO>
+__device__ __forceinline__ void lm_gemm(LmStage &st, const uint16_t *h0, const uint16_t *h1, const uint16_t *W,
+                                        long long row0, long long R, long long vt0, int V, int H,
+                                        f32x4_t (&acc0)[4][2], f32x4_t (&acc1)[4][2]) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            acc0[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            acc1[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+    for (int k0 = 0; k0 < H; k0 += kLmKB) {
+        __syncthreads(); // every wave is done with the previous stage
+        lm_stage<kLmRows>(st.a, h0, row0, R - 1, H, k0);
+        if (TWO)
+            lm_stage<kLmRows>(st.b, h1, row0, R - 1, H, k0);
+        lm_stage<kLmCols>(st.w, W, vt0, V - 1, H, k0);
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+#pragma unroll
+        for (int s = 0; s < kLmKB / 32; ++s) {
+            const int c = 4 * s + (lane >> 4);
+            bf16x8_t fw[2];
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+                fw[n] = lm_frag(st.w, 32 * wave + 16 * n + (lane & 15), c);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const bf16x8_t f0 = lm_frag(st.a, 16 * m + (lane & 15), c);
+#pragma unroll
+                for (int n = 0; n < 2; ++n)
+                    acc0[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f0, fw[n], acc0[m][n], 0, 0, 0);
+                if (TWO) {
+                    const bf16x8_t f1 = lm_frag(st.b, 16 * m + (lane & 15), c);
+#pragma unroll
+                    for (int n = 0; n < 2; ++n)
+                        acc1[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f1, fw[n], acc1[m][n], 0, 0, 0);
+                }
+            }
+        }
+    }
+}
+
+// Row of accumulator slot (m, j) in the workgroup's 64 rows, and column of
+// block n in the tile's 128.
+__device__ __forceinline__ int lm_row(int m, int j) { return 16 * m + 4 * ((threadIdx.x & 63) >> 4) + j; }
+__device__ __forceinline__ int lm_col(int n) { return 32 * (threadIdx.x >> 6) + 16 * n + (threadIdx.x & 15); }
+
+struct LmScratch {
+    float ref[kWaves][kLmRows][3];
+    float sum[kWaves][kLmRows][3];
+    float fm[kWaves][kLmRows];
+    int fi[kWaves][kLmRows];
+    float la[kLmRows], lb[kLmRows], dh[kLmRows], dlo[kLmRows]; // pass 2 row constants
+};
+
+// Per-row statistics of tensor k's block held as accumulators, written to
+// the wave's scratch: for each of the lane's rows (m, j) the integer
+// reference and the fp32 sum of 2^(x*log2e - ref) over the wave's 32 columns
+// (identical in the 16 lanes of a DPP row; lane 0 of the row writes).
+// Invalid columns count as -inf.
+__device__ __forceinline__ void lm_tile_stats(LmScratch &sc, int k, const f32x4_t (&x)[4][2], const bool (&cv)[2]) {
+    const float NEG_INF = -__builtin_inff();
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float x0 = cv[0] ? x[m][0][j] : NEG_INF, x1 = cv[1] ? x[m][1][j] : NEG_INF;
+            const float mx = row16_max(fmaxf(x0, x1));
+            const float c = __builtin_ceilf(fmaxf(mx, -1e30f) * kLog2e);
+            const float sm = row16_sum(__builtin_amdgcn_exp2f(__fmaf_rn(x0, kLog2e, -c)) +
+                                       __builtin_amdgcn_exp2f(__fmaf_rn(x1, kLog2e, -c)));
+            if ((threadIdx.x & 15) == 0) {
+                sc.ref[wave][lm_row(m, j)][k] = c;
+                sc.sum[wave][lm_row(m, j)][k] = sm;
+            }
+        }
+}
+
+// Merge a partial (reference c, sum s) into a running fp64 state.
+__device__ __forceinline__ void lm_merge(float &run_c, double &run_s, float c, double s) {
+    const float C = fmaxf(run_c, c);
+    run_s = scale_pow2(run_s, run_c - C) + scale_pow2(s, c - C);
+    run_c = C;
+}
+
+template <int PASS>
+__global__ __launch_bounds__(kThreads) void lmhead_kernel(LmheadParams P) {
+    __shared__ LmStage st;
+    __shared__ LmScratch sc;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // workgroup b runs on die b % 8: the row tiles of one vocabulary range
+    // share a die, so its head tiles come from one L2
+    const long long b = blockIdx.x;
+    const long long q = b / 8;
+    const int rtile = (int)(q % P.RT);
+    const int s = (int)(8 * (q / P.RT) + b % 8);
+    if (s >= P.S)
+        return;
+    const long long row0 = (long long)rtile * kLmRows;
+    const long long v_begin = (long long)s * P.range;
+    const long long v_end = min((long long)P.V, v_begin + P.range);
+    const float NEG = -3.0e38f;
+
+    if (PASS == 2) { // row constants of pass C
+        if (tid < kLmRows) {
+            const long long row = min(row0 + tid, P.R - 1);
+            const double La2 = P.rowstat[row * 2 + 0], Lb2 = P.rowstat[row * 2 + 1];
+            const double dl = (La2 - Lb2) * kLn2d;
+            sc.la[tid] = (float)La2;
+            sc.lb[tid] = (float)Lb2;
+            sc.dh[tid] = (float)dl;
+            sc.dlo[tid] = (float)(dl - (double)(float)dl);
+        }
+        __syncthreads();
+    }
+    // running per-row state (threads 0..63, row = tid)
+    float rc[3] = {NEG, NEG, NEG};
+    double rs[3] = {0.0, 0.0, 0.0};
+    float rfm = -__builtin_inff();
+    int rfi = 0x7fffffff;
+    double rj = 0.0;
+
+    for (long long vt0 = v_begin; vt0 < v_end; vt0 += kLmCols) {
+        bool cv[2];
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+            cv[n] = vt0 + lm_col(n) < v_end;
+        f32x4_t xa[4][2], xb[4][2];
+        lm_gemm<true>(st, P.ha, P.hb, P.Wd, row0, P.R, vt0, P.V, P.Hd, xa, xb);
+        if (PASS == 1) {
+            lm_tile_stats(sc, 0, xa, cv);
+            lm_tile_stats(sc, 1, xb, cv);
+            // the context gain, kept while t is formed
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int n = 0; n < 2; ++n)
+                    xa[m][n] = xa[m][n] - xb[m][n];
+            f32x4_t xt[4][2], unused[4][2];
+            lm_gemm<false>(st, P.ht, nullptr, P.Wt, row0, P.R, vt0, P.V, P.Ht, xt, unused);
+            lm_tile_stats(sc, 2, xt, cv);
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    // fused score t + beta*(a - b), its maximum and lowest column
+                    const float f0 = cv[0] ? __fmaf_rn(P.beta, xa[m][0][j], xt[m][0][j]) : -__builtin_inff();
+                    const float f1 = cv[1] ? __fmaf_rn(P.beta, xa[m][1][j], xt[m][1][j]) : -__builtin_inff();
+                    const bool second = f1 > f0;
+                    const float fb = second ? f1 : f0;
+                    const int col = lm_col(second ? 1 : 0);
+                    const float fm = row16_max(fb);
+                    const int fi = row16_min_int((fb == fm && (cv[0] || cv[1])) ? col : 0x7fffffff);
+                    if ((lane & 15) == 0) {
+                        sc.fm[wave][lm_row(m, j)] = fm;
+                        sc.fi[wave][lm_row(m, j)] = fi;
+                    }
+                }
+            __syncthreads();
+            if (tid < kLmRows) { // waves in column order; strict > keeps the lowest index
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) {
+#pragma unroll
+                    for (int k = 0; k < 3; ++k)
+                        lm_merge(rc[k], rs[k], sc.ref[w][tid][k], (double)sc.sum[w][tid][k]);
+                    if (sc.fm[w][tid] > rfm) {
+                        rfm = sc.fm[w][tid];
+                        rfi = (int)vt0 + sc.fi[w][tid];
+                    }
+                }
+            }
+        } else {
+            // JSD terms of the block against the row's log-sum-exps
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = lm_row(m, j);
+                    const float la_c = sc.la[r], lb_c = sc.lb[r], dh = sc.dh[r], dlo = sc.dlo[r];
+                    float J = 0.f;
+#pragma unroll
+                    for (int n = 0; n < 2; ++n) {
+                        if (cv[n]) {
+                            const float a = xa[m][n][j], bb = xb[m][n][j];
+                            J += jsd_term(__fmaf_rn(a, kLog2e, -la_c), __fmaf_rn(bb, kLog2e, -lb_c),
+                                          ((a - bb) - dh) - dlo);
+                        }
+                    }
+                    J = row16_sum(J);
+                    if ((lane & 15) == 0)
+                        sc.sum[wave][r][0] = J;
+                }
+            __syncthreads();
+            if (tid < kLmRows) {
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w)
+                    rj += (double)sc.sum[w][tid][0];
+            }
+        }
+    }
+    const long long row = row0 + tid;
+    if (tid < kLmRows && row < P.R) {
+        uint64_t *rec = P.rec + ((size_t)row * P.S + s) * kRecWords;
+        if (PASS == 1) {
+            rec[0] = f64_bits(rs[0]);
+            rec[1] = f64_bits(rs[1]);
+            rec[2] = f64_bits(rs[2]);
+            rec[3] = pack2(rc[0], rc[1]);
+            rec[4] = pack2(rc[2], rfm);
+            rec[5] = (uint64_t)(uint32_t)rfi;
+        } else {
+            rec[6] = f64_bits(rj);
+        }
+    }
+}
+
+// L_a, L_b (log2 units) of each row from its records: one wave per row.
+__global__ __launch_bounds__(kThreads) void lmhead_combine_kernel(LmheadParams P) {
+    const long long row = (long long)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (row >= P.R)
+        return;
+    double L[2];
+    team_lse<2>(P.rec + (size_t)row * P.S * kRecWords, P.S, {0, 1}, {3, 3}, {false, true}, L);
+    if ((threadIdx.x & 63) == 0) {
+        P.rowstat[row * 2 + 0] = L[0];
+        P.rowstat[row * 2 + 1] = L[1];
+    }
+}
+
+// fp64 dot product of two bf16 rows of length H (one whole wave).
+__device__ __forceinline__ double lm_dot(const uint16_t *x, const uint16_t *y, int H) {
+    double acc = 0.0;
+    for (int k = (threadIdx.x & 63) * 8; k < H; k += 64 * 8) {
+        const uint4 vx = *reinterpret_cast<const uint4 *>(x + k);
+        const uint4 vy = *reinterpret_cast<const uint4 *>(y + k);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            acc += (double)widen<DT_BF16>(vx, e) * (double)widen<DT_BF16>(vy, e);
+    }
+    return wave_sum(acc);
+}
+
+__global__ __launch_bounds__(kThreads) void lmhead_finalize_kernel(LmheadParams P) {
+    const int lane = threadIdx.x & 63;
+    const long long row = (long long)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (row >= P.R)
+        return;
+    const uint64_t *rec_row = P.rec + (size_t)row * P.S * kRecWords;
+    double L2[2];
+    team_lse<2>(rec_row, P.S, {1, 2}, {3, 4}, {true, false}, L2);
+    const double Lb = L2[0] * kLn2d, Lt = L2[1] * kLn2d;
+    float fbest = -__builtin_inff();
+    for (int w = lane; w < P.S; w += 64)
+        fbest = fmaxf(fbest, unpack_hi(rec_row[(size_t)w * kRecWords + 4]));
+    fbest = wave_max(fbest);
+    double jsum = 0.0;
+    int fidx = 0x7fffffff;
+    for (int w = lane; w < P.S; w += 64) {
+        const uint64_t *r = rec_row + (size_t)w * kRecWords;
+        jsum += as_f64(r[6]);
+        if (unpack_hi(r[4]) == fbest)
+            fidx = min(fidx, (int)(uint32_t)r[5]);
+    }
+    jsum = wave_sum(jsum);
+    fidx = wave_min_int(fidx);
+    const int Pn = P.K + 1;
+    const long long bi = row / Pn;
+    const int i = (int)(row - bi * Pn);
+    int d = -1;
+    double td = 0.0, bd = 0.0;
+    if (i < P.K) {
+        d = P.draft[bi * P.K + i];
+        if (d >= 0 && d < P.V) { // the draft's logits, exactly products of the stored values
+            td = lm_dot(P.ht + (size_t)row * P.Ht, P.Wt + (size_t)d * P.Ht, P.Ht);
+            bd = lm_dot(P.hb + (size_t)row * P.Hd, P.Wd + (size_t)d * P.Hd, P.Hd);
+        }
+    }
+    if (lane != 0)
+        return;
+    const double Dr = -0.5 * kLn2d * jsum;
+    P.D[row] = (float)Dr;
+    P.geff[row] = (float)((double)P.gamma * exp(-Dr));
+    P.fused[row] = fidx;
+    uint32_t acc = 0;
+    if (i < P.K) {
+        if (d < 0 || d >= P.V) {
+            set_dev_err(P.dev_err, 1);
+        } else {
+            const double margin = (td - Lt) - (bd - Lb) - P.log_gamma + Dr;
+            acc = margin > 0.0 ? 1u : 0u;
+        }
+        P.accept[bi * P.K + i] = (uint8_t)acc;
+    }
+    st_relaxed(P.row_info + (size_t)row * 2 + 0, (uint32_t)fidx);
+    st_relaxed(P.row_info + (size_t)row * 2 + 1, acc);
+    uint32_t *rq = P.req_ctr + (size_t)bi * 16;
+    const uint32_t done = publish_add(rq, 1u);
+    if (done == (uint32_t)P.K) {
+        const size_t r0 = (size_t)bi * Pn;
+        int n = P.K;
+        for (int k = 0; k < P.K; ++k) {
+            if (ld_relaxed(P.row_info + (r0 + k) * 2 + 1) == 0u) {
+                n = k;
+                break;
+            }
+        }
+        P.acc_len[bi] = n;
+        P.token[bi] = (int32_t)ld_relaxed(P.row_info + (r0 + n) * 2 + 0);
+        st_relaxed(rq, 0u);
+    }
+}
+
+hipError_t launch_lmhead(const LmheadParams &p, hipStream_t s, hipEvent_t after_rows) {
+    const unsigned grid = (unsigned)(8 * (long long)p.RT * ((p.S + 7) / 8));
+    const unsigned fin = (unsigned)((p.R + kWaves - 1) / kWaves);
+    hipLaunchKernelGGL((lmhead_kernel<1>), dim3(grid), dim3(kThreads), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(lmhead_combine_kernel, dim3(fin), dim3(kThreads), 0, s, p);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    hipLaunchKernelGGL((lmhead_kernel<2>), dim3(grid), dim3(kThreads), 0, s, p);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    if (after_rows) {
+        e = hipEventRecord(after_rows, s);
+        if (e != hipSuccess)
+            return e;
+    }
+    hipLaunchKernelGGL(lmhead_finalize_kernel, dim3(fin), dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+} // namespace vwl

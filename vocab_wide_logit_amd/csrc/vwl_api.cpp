@@ -482,6 +482,99 @@ vwl_status asym_verify_xfam(const void *a, const void *b, int Vd, const void *t,
     return launch_xfam((int)dt, plan, p, stream, g_phase_event.load()) == hipSuccess ? VWL_OK : VWL_ERR_HIP;
 }
 
+// LM-head pass geometry: row tiles of 64 and vocabulary ranges (multiples of
+// 128 tokens) for about 1536 workgroups; depends on the shape only.
+struct LmGeom {
+    int RT, S, range;
+    size_t rec, rowstat, req_ctr, row_info, total;
+};
+static bool lm_geometry(int B, int K, int V, int Hd, int Ht, LmGeom &g) {
+    if (!shape_ok(B, K, V) || Hd < 64 || Ht < 64 || Hd % 64 || Ht % 64)
+        return false;
+    const long long R = (long long)B * (K + 1);
+    const long long RT = (R + 63) / 64;
+    if (RT > (1LL << 24))
+        return false;
+    const long long tiles = ((long long)V + 127) / 128;
+    long long S = (1536 + RT - 1) / RT;
+    S = S < 1 ? 1 : (S > tiles ? tiles : S);
+    const long long range = ((tiles + S - 1) / S) * 128;
+    S = ((long long)V + range - 1) / range;
+    if (8 * RT * ((S + 7) / 8) > 0x7fffffffLL)
+        return false;
+    g.RT = (int)RT;
+    g.S = (int)S;
+    g.range = (int)range;
+    size_t off = 0;
+    g.rec = off;      off = align256(off + (size_t)R * S * kRecWords * 8);
+    g.rowstat = off;  off = align256(off + (size_t)R * 2 * 8);
+    g.req_ctr = off;  off = align256(off + (size_t)B * 16 * 4);
+    g.row_info = off; off = align256(off + (size_t)R * 2 * 4);
+    g.total = off;
+    return true;
+}
+
+size_t vwl_asym_lmhead_workspace_bytes(int B, int K, int V, int Hd, int Ht) {
+    LmGeom g;
+    return lm_geometry(B, K, V, Hd, Ht, g) ? g.total : 0;
+}
+
+vwl_status asym_verify_lmhead(const void *h_a, const void *h_b, const void *W_d, const void *h_t, const void *W_t,
+                              const int32_t *draft, int B, int K, int V, int Hd, int Ht, float beta, float gamma,
+                              float *D, float *gamma_eff, uint8_t *accept, int32_t *fused, int32_t *accept_len,
+                              int32_t *token, int32_t *dev_err, void *workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+    if (!h_a || !h_b || !W_d || !h_t || !W_t || !D || !gamma_eff || !fused || !accept_len || !token)
+        return VWL_ERR_NULL;
+    if (K > 0 && (!draft || !accept))
+        return VWL_ERR_NULL;
+    LmGeom g;
+    if (!lm_geometry(B, K, V, Hd, Ht, g))
+        return VWL_ERR_SHAPE;
+    if (!finite_f(beta) || !finite_f(gamma) || gamma < 0.0f)
+        return VWL_ERR_PARAM;
+    if (!aligned(h_a, 16) || !aligned(h_b, 16) || !aligned(W_d, 16) || !aligned(h_t, 16) || !aligned(W_t, 16) ||
+        !aligned(D, 4) || !aligned(gamma_eff, 4) || !aligned(fused, 4) || !aligned(accept_len, 4) ||
+        !aligned(token, 4) || (draft && !aligned(draft, 4)) || (dev_err && !aligned(dev_err, 4)))
+        return VWL_ERR_ALIGN;
+    if (!workspace || workspace_bytes < g.total)
+        return VWL_ERR_WORKSPACE;
+    if (!aligned(workspace, 256))
+        return VWL_ERR_ALIGN;
+    char *ws = static_cast<char *>(workspace);
+    LmheadParams p{};
+    p.ha = static_cast<const uint16_t *>(h_a);
+    p.hb = static_cast<const uint16_t *>(h_b);
+    p.ht = static_cast<const uint16_t *>(h_t);
+    p.Wd = static_cast<const uint16_t *>(W_d);
+    p.Wt = static_cast<const uint16_t *>(W_t);
+    p.draft = draft;
+    p.R = (long long)B * (K + 1);
+    p.B = B;
+    p.K = K;
+    p.V = V;
+    p.Hd = Hd;
+    p.Ht = Ht;
+    p.RT = g.RT;
+    p.S = g.S;
+    p.range = g.range;
+    p.beta = beta;
+    p.gamma = gamma;
+    p.log_gamma = std::log((double)gamma);
+    p.D = D;
+    p.geff = gamma_eff;
+    p.accept = accept;
+    p.fused = fused;
+    p.acc_len = accept_len;
+    p.token = token;
+    p.dev_err = dev_err;
+    p.rec = reinterpret_cast<uint64_t *>(ws + g.rec);
+    p.rowstat = reinterpret_cast<double *>(ws + g.rowstat);
+    p.req_ctr = reinterpret_cast<uint32_t *>(ws + g.req_ctr);
+    p.row_info = reinterpret_cast<uint32_t *>(ws + g.row_info);
+    return launch_lmhead(p, stream, g_phase_event.load()) == hipSuccess ? VWL_OK : VWL_ERR_HIP;
+}
+
 size_t vwl_e2sci_workspace_bytes(int B, int W, int V, vwl_dtype dt) {
     if (W < 1 || !shape_ok(B, W - 1, V) || (dt != VWL_F32 && dt != VWL_BF16))
         return 0;

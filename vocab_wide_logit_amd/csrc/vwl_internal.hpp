@@ -127,6 +127,27 @@ struct Plan {
     int grid;
 };
 
+// AsymSpec from hidden states and LM heads (bf16 throughout).
+struct LmheadParams {
+    const uint16_t *ha, *hb, *ht; // [R][Hd], [R][Hd], [R][Ht]
+    const uint16_t *Wd, *Wt;      // [V][Hd], [V][Ht]
+    const int32_t *draft;
+    long long R;
+    int B, K, V, Hd, Ht;
+    int RT;    // row tiles of 64
+    int S;     // vocabulary ranges (records per row)
+    int range; // tokens per range (a multiple of 128)
+    float beta, gamma;
+    double log_gamma;
+    float *D, *geff;
+    uint8_t *accept;
+    int32_t *fused, *acc_len, *token, *dev_err;
+    uint32_t *req_ctr, *row_info;
+    uint64_t *rec;    // [R][S][8], the row kernel's record layout
+    double *rowstat;  // [R][2] L_a, L_b (log2 units)
+};
+hipError_t launch_lmhead(const LmheadParams &p, hipStream_t s, hipEvent_t after_rows);
+
 // AsymSpec variants (values match vwl_delta_source / vwl_gate of the C ABI);
 // kDeltaNone is the two-tensor divergence pass of E2-SCI.
 enum { kDeltaAMinusB = 0, kDeltaA = 1, kDeltaTMinusB = 2, kDeltaNone = 3 };

@@ -8,7 +8,9 @@ event-timed duration, against 8 TB/s, with the measured traffic of the
 committed counter summary while the kernel sources still match it, and its
 VALU issue from the committed SQ summary); as secondary figures the B=64/K=2
 workload, the RAPID pass, the AsymSpec ablation variants on the large
-workload and the E2-SCI adaptive acceptance on B=64 and B=1 windows; and the
+workload, the cross-family pass, the fused LM-head pass (against the bf16
+matrix-core peak) and the E2-SCI adaptive acceptance on B=64 and B=1
+windows; and the
 fp64 CPU oracle timed on the host as a reported baseline.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu-baseline]
@@ -172,6 +174,36 @@ def time_xfam(vwl, x, steps, warmup, copies=4):
         start[i].record(stream)
         vwl.set_phase_event(mid[i])
         vwl.asym_verify_xfam(a, b, t, vm, d, x.beta, x.gamma, out=out)
+        end[i].record(stream)
+    torch.cuda.synchronize()
+    vwl.set_phase_event(None)
+    return ([s.elapsed_time(e) for s, e in zip(start, end)],
+            [s.elapsed_time(m) for s, m in zip(start, mid)])
+
+
+PEAK_BF16_TFLOPS = 2500.0  # dense bf16 matrix-core peak of one MI355X
+
+
+def time_lmhead(vwl, x, steps, warmup):
+    """asym_verify_lmhead calls on resident hidden states and heads; per-call
+    ms and the ms up to the end of the second GEMM pass."""
+    import numpy as np
+    import torch
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16).cuda()
+    ha, hb, Wd, ht, Wt = bf(x.h_a), bf(x.h_b), bf(x.W_d), bf(x.h_t), bf(x.W_t)
+    d = torch.from_numpy(x.draft).cuda()
+    out = vwl.asym_out(x.B, x.K, "cuda")
+    for _ in range(warmup):
+        vwl.asym_verify_lmhead(ha, hb, Wd, ht, Wt, d, x.beta, x.gamma, out=out)
+    stream = torch.cuda.current_stream()
+    start, mid, end = _events(steps), _events(steps), _events(steps)
+    for e in mid:
+        e.record(stream)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        start[i].record(stream)
+        vwl.set_phase_event(mid[i])
+        vwl.asym_verify_lmhead(ha, hb, Wd, ht, Wt, d, x.beta, x.gamma, out=out)
         end[i].record(stream)
     torch.cuda.synchronize()
     vwl.set_phase_event(None)
@@ -370,6 +402,16 @@ def main():
         result["secondary"][xf.name] = {
             "rows_per_s": xf.B * (xf.K + 1) / (mf * 1e-3), "median_call_ms": mf, "median_row_passes_ms": mrf,
             "gbs": bf / (mrf * 1e-3) / 1e9, "frac_of_peak": bf / (mrf * 1e-3) / 1e9 / PEAK_HBM_GBS}
+        xl = W.lmhead_batched()
+        pl, rl = time_lmhead(vwl, xl, min(args.steps, 50), min(args.warmup, 5))
+        ml = _median(pl)
+        Rl = xl.B * (xl.K + 1)
+        flops = 2.0 * Rl * xl.V * (2 * xl.Hd + xl.Ht) + 2.0 * Rl * xl.V * 2 * xl.Hd  # two passes
+        result["secondary"][xl.name] = {
+            "rows_per_s": Rl / (ml * 1e-3), "median_call_ms": ml, "median_gemm_passes_ms": _median(rl),
+            "tflops": flops / (ml * 1e-3) / 1e12, "frac_of_bf16_peak": flops / (ml * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "head_weight_gbs": (xl.weight_bytes() + 2 * xl.V * xl.Hd) / (ml * 1e-3) / 1e9,
+            "flops_per_call": flops}
         for xe in (W.e2sci_batched(), W.e2sci_single()):
             pe, re_ = time_e2sci(vwl, xe, args.steps, args.warmup)
             me, mre = _median(pe), _median(re_)
@@ -402,6 +444,10 @@ def main():
             sec[xf.name]["cpu_oracle_rows_per_s"] = oracle_rows_per_s(
                 lambda: oracle.asym_xfam(sl(xf.a), sl(xf.b), sl(xf.t), xf.vmap, sl(xf.draft), xf.beta, xf.gamma,
                                          xf.dtype), n * (xf.K + 1))
+            m2 = 2
+            sec[xl.name]["cpu_oracle_rows_per_s"] = oracle_rows_per_s(
+                lambda: oracle.asym_lmhead(xl.h_a[:m2], xl.h_b[:m2], xl.W_d, xl.h_t[:m2], xl.W_t, xl.draft[:m2],
+                                           xl.beta, xl.gamma), m2 * (xl.K + 1))
             for xe in (W.e2sci_batched(), W.e2sci_single()):
                 m = min(n, xe.B)
                 sec[xe.name]["cpu_oracle_rows_per_s"] = oracle_rows_per_s(

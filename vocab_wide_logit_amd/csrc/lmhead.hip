@@ -114,7 +114,7 @@ __device__ __forceinline__ void lm_gemm(LmStage &st, const uint16_t *h0, const u
         lm_stage<kLmCols>(st.w, W, vt0, V - 1, H, k0);
         __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-#pragma unroll
+#pragma unroll 1
         for (int s = 0; s < kLmKB / 32; ++s) {
             const int c = 4 * s + (lane >> 4);
             bf16x8_t fw[2];
@@ -183,7 +183,7 @@ __device__ __forceinline__ void lm_merge(float &run_c, double &run_s, float c, d
 }
 
 template <int PASS>
-__global__ __launch_bounds__(kThreads) void lmhead_kernel(LmheadParams P) {
+__global__ __launch_bounds__(kThreads, 3) void lmhead_kernel(LmheadParams P) {
     __shared__ LmStage st;
     __shared__ LmScratch sc;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;

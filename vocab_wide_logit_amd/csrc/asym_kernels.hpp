@@ -305,6 +305,7 @@ __device__ __forceinline__ void pair_pass_ab(const AsymParams &P, long long row,
         online_group<1>(lb, x1b);
     }
     float mx[2] = {la.c, lb.c};
+    __builtin_amdgcn_s_setprio(2); // the workgroup's serial section: reductions and publish
     block_max<2, false>(mx, lds_f);
     double S[2] = {rescale_to(la, mx[0]), rescale_to(lb, mx[1])};
     block_sum<2, false>(S, lds_d);
@@ -315,6 +316,7 @@ __device__ __forceinline__ void pair_pass_ab(const AsymParams &P, long long row,
         st_relaxed(rec + 3, pack2(mx[0], mx[1]));
         publish_add_nr(P.row_ctr + (size_t)row * 16, 1u);
     }
+    __builtin_amdgcn_s_setprio(0);
 }
 
 // Passes A+B over one row's chunk held in registers (raw a, b, t plus the
@@ -361,6 +363,7 @@ __device__ __forceinline__ void asym_pass_ab(const AsymParams &P, long long row,
         online_group<1>(lt, x1t);
     }
     float mx[4] = {la.c, lb.c, lt.c, fmax_t};
+    __builtin_amdgcn_s_setprio(2); // the workgroup's serial section: reductions and publish
     block_max<4, false>(mx, lds_f);
     const float Ca = mx[0], Cb = mx[1], Ct = mx[2], Fm = mx[3];
 
@@ -396,6 +399,7 @@ __device__ __forceinline__ void asym_pass_ab(const AsymParams &P, long long row,
         st_relaxed(rec + 5, (uint64_t)(uint32_t)fi);
         publish_add_nr(P.row_ctr + (size_t)row * 16, 1u);
     }
+    __builtin_amdgcn_s_setprio(0);
 }
 
 // Resident waves per SIMD the row kernel is built for: the CDA variants keep
@@ -413,7 +417,11 @@ constexpr int asym_rows_waves() {
 // The workgroup reductions run without their closing barriers: every reuse
 // of lds_f, lds_d and lds_i is separated from the previous reads by another
 // barrier (the next reduction's, the team wait's, the combine's, or the
-// staging barriers of the next row).
+// staging barriers of the next row).  The serial sections of a row (the
+// reductions, the record's publish, the team wait and the combine) run at a
+// raised wave priority: other workgroups' waves on the SIMD are then held
+// back in favour of the short chains that every member of a team waits on,
+// while the element passes run at the base priority.
 template <int DT, int NV, int DS, int GATE>
 __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, DS, GATE>())) void asym_rows_kernel(AsymParams P) {
     constexpr int EPV = Elem<DT>::kPerVec;
@@ -520,6 +528,7 @@ __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, DS, GATE>())) void a
 
         // ---- the pending row: wait for its team, then pass C ----
         const uint64_t *rec_row = P.rec + (size_t)row * P.Wmax * kRecWords;
+        __builtin_amdgcn_s_setprio(2);
         if (tid == 0)
             sh_u[1] = wait_at_least(P.row_ctr + (size_t)row * 16, (uint32_t)W) ? 1u : 0u;
         __syncthreads();
@@ -537,6 +546,7 @@ __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, DS, GATE>())) void a
                 sh_row[cw] = L[0];
         }
         __syncthreads();
+        __builtin_amdgcn_s_setprio(0);
         const float la_c = (float)sh_row[0]; // row log-sum-exps, log2 units
         const float lb_c = (float)sh_row[1];
         // L_a - L_b in nats as an unevaluated float pair
@@ -558,9 +568,11 @@ __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, DS, GATE>())) void a
             J += jsd_term(__fmaf_rn(psa, kLog2e, -la_c), __fmaf_rn(psb, kLog2e, -lb_c),
                           ((psa - psb) - dl_hi) - dl_lo);
         double Jd[1] = {(double)J};
+        __builtin_amdgcn_s_setprio(2);
         block_sum<1, false>(Jd, lds_d);
         if (tid == 0)
             P.rec[((size_t)row * P.Wmax + member) * kRecWords + 6] = f64_bits(Jd[0]);
+        __builtin_amdgcn_s_setprio(0);
 
         if (!has_next)
             break;

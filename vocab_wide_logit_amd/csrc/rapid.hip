@@ -11,7 +11,8 @@
 //                registers; online statistics of h, its maximum and the
 //                maximum's lowest index -> record
 // Several teams share each compute unit, so one team's wait overlaps the
-// others' loads and arithmetic.
+// others' loads and arithmetic; the serial sections (reductions, publish,
+// team wait, combine) run at a raised wave priority.
 // Launch 2 (the tail): per request, row statistics and the acceptance test
 // of each row, the first rejection, then the emitting row in fp64 (refined
 // normalisers, the augmented target's log-sum-exp, the residual
@@ -211,6 +212,7 @@ __global__ __launch_bounds__(kThreads, (NV <= 4 ? 5 : 4)) void rapid_rows_kernel
             online_group_r<1>(ly, b1, kc);
         }
         float mx[2] = {lz.c, ly.c};
+        __builtin_amdgcn_s_setprio(2); // serial section: reductions, publish, team wait, combine
         block_max<2>(mx, lds_f);
         double S[2] = {rescale_to_r(lz, mx[0]), rescale_to_r(ly, mx[1])};
         block_sum<2>(S, lds_d);
@@ -240,6 +242,7 @@ __global__ __launch_bounds__(kThreads, (NV <= 4 ? 5 : 4)) void rapid_rows_kernel
             }
         }
         __syncthreads();
+        __builtin_amdgcn_s_setprio(0);
 
         // ---- second pass: h = zhat/T = z/T + eta*(q - p); online statistics ----
         AugCoef ak;
@@ -271,6 +274,7 @@ __global__ __launch_bounds__(kThreads, (NV <= 4 ? 5 : 4)) void rapid_rows_kernel
             online_group_h<1>(lh, ak, z1, dq1, h1);
         }
         float hm[2] = {lh.c, hmax_t};
+        __builtin_amdgcn_s_setprio(2);
         block_max<2>(hm, lds_f);
         const float Ch = hm[0], Hm = hm[1];
         double Sh[1] = {rescale_to_r(lh, Ch)};
@@ -299,6 +303,7 @@ __global__ __launch_bounds__(kThreads, (NV <= 4 ? 5 : 4)) void rapid_rows_kernel
             rec[4] = pack_fi(Hm, hi);
             rec[5] = (uint64_t)__float_as_uint(Ch);
         }
+        __builtin_amdgcn_s_setprio(0);
     }
 }
 

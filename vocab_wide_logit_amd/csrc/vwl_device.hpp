@@ -78,14 +78,54 @@ __device__ __forceinline__ float load_scalar(const void *base, size_t idx) {
 // operation, so all lanes end with the same bits, in a fixed order: the
 // results are deterministic.
 // ---------------------------------------------------------------------------
+// Every lane has a valid source lane under the in-row controls used here, so
+// the move needs no "old" value and the compiler may fold it into its user.
 template <int CTRL>
 __device__ __forceinline__ int dpp_i(int x) {
-    return __builtin_amdgcn_update_dpp(x, x, CTRL, 0xf, 0xf, false);
+    return __builtin_amdgcn_mov_dpp(x, CTRL, 0xf, 0xf, false);
 }
 constexpr int kDppXor1 = 0xB1;       // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;       // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141;
 constexpr int kDppMirror = 0x140;
+constexpr int kDppBcast15 = 0x142;   // lane 15 of each row to the next row
+constexpr int kDppBcast31 = 0x143;   // lane 31 to rows 2 and 3
+// A row broadcast written to the rows in ROWS only; the other rows get `old`.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_bcast(int old, int x) {
+    return __builtin_amdgcn_update_dpp(old, x, CTRL, ROWS, 0xf, false);
+}
+
+// One combining step with the DPP operand folded into the max / min: x gets
+// op(x, x from the lane CTRL selects); rows outside ROWS keep x.  Written as
+// instructions so that no NaN canonicalisation of the moved value is added.
+// Wait states: the first step of a chain allows for any earlier VALU write
+// (five: a write of EXEC), the later ones for the previous step's write of x
+// (two), and each chain ends with two more before the next reader of x.
+#define VWL_DPP_STEP(NOPS, OP, CTRL_TEXT, ROWS_TEXT)                                            \
+    asm("s_nop " NOPS "\n\t" OP " %0, %0, %0 " CTRL_TEXT " row_mask:" ROWS_TEXT " bank_mask:0xf" \
+        : "+v"(x))
+#define VWL_DPP_END() asm("s_nop 1" : "+v"(x))
+__device__ __forceinline__ float fmax_dpp_steps(float x) { // in-row steps
+    VWL_DPP_STEP("4", "v_max_f32_dpp", "quad_perm:[1,0,3,2]", "0xf");
+    VWL_DPP_STEP("1", "v_max_f32_dpp", "quad_perm:[2,3,0,1]", "0xf");
+    VWL_DPP_STEP("1", "v_max_f32_dpp", "row_half_mirror", "0xf");
+    VWL_DPP_STEP("1", "v_max_f32_dpp", "row_mirror", "0xf");
+    return x;
+}
+__device__ __forceinline__ int imin_dpp_steps(int x) {
+    VWL_DPP_STEP("4", "v_min_i32_dpp", "quad_perm:[1,0,3,2]", "0xf");
+    VWL_DPP_STEP("1", "v_min_i32_dpp", "quad_perm:[2,3,0,1]", "0xf");
+    VWL_DPP_STEP("1", "v_min_i32_dpp", "row_half_mirror", "0xf");
+    VWL_DPP_STEP("1", "v_min_i32_dpp", "row_mirror", "0xf");
+    return x;
+}
+// Plain maximum of two floats without input canonicalisation.
+__device__ __forceinline__ float fmax_raw(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
 
 // Partner values across 16-lane rows and across 32-lane halves: returns the
 // pair (own, partner) in some order; only commutative uses are made of it.
@@ -101,22 +141,18 @@ __device__ __forceinline__ void swap32(int x, int &u, int &v) {
 }
 
 __device__ __forceinline__ float wave_max(float x) {
-    x = fmaxf(x, __int_as_float(dpp_i<kDppXor1>(__float_as_int(x))));
-    x = fmaxf(x, __int_as_float(dpp_i<kDppXor2>(__float_as_int(x))));
-    x = fmaxf(x, __int_as_float(dpp_i<kDppHalfMirror>(__float_as_int(x))));
-    x = fmaxf(x, __int_as_float(dpp_i<kDppMirror>(__float_as_int(x))));
+    x = fmax_dpp_steps(x);
+    VWL_DPP_END();
     int u, v;
     swap16(__float_as_int(x), u, v);
-    x = fmaxf(__int_as_float(u), __int_as_float(v));
+    x = fmax_raw(__int_as_float(u), __int_as_float(v));
     swap32(__float_as_int(x), u, v);
-    return fmaxf(__int_as_float(u), __int_as_float(v));
+    return fmax_raw(__int_as_float(u), __int_as_float(v));
 }
 
 __device__ __forceinline__ int wave_min_int(int x) {
-    x = min(x, dpp_i<kDppXor1>(x));
-    x = min(x, dpp_i<kDppXor2>(x));
-    x = min(x, dpp_i<kDppHalfMirror>(x));
-    x = min(x, dpp_i<kDppMirror>(x));
+    x = imin_dpp_steps(x);
+    VWL_DPP_END();
     int u, v;
     swap16(x, u, v);
     x = min(u, v);
@@ -155,6 +191,44 @@ __device__ __forceinline__ double wave_sum(double x) {
     return x;
 }
 
+// Reductions whose result is needed in lane 63 only (the wave's entry of a
+// workgroup reduction): after the in-row steps every lane of a row holds
+// its row's result; row 1 then adds row 0 and row 3 adds row 2 (broadcast of
+// lane 15), and rows 2 and 3 add lane 31 (rows 0 and 1).  The order is fixed,
+// so the result is deterministic.  Other lanes end with partial results.
+__device__ __forceinline__ float wave_max_last(float x) {
+    x = fmax_dpp_steps(x);
+    VWL_DPP_STEP("1", "v_max_f32_dpp", "row_bcast:15", "0xa");
+    VWL_DPP_STEP("1", "v_max_f32_dpp", "row_bcast:31", "0xc");
+    VWL_DPP_END();
+    return x;
+}
+
+__device__ __forceinline__ int wave_min_last(int x) {
+    x = imin_dpp_steps(x);
+    VWL_DPP_STEP("1", "v_min_i32_dpp", "row_bcast:15", "0xa");
+    VWL_DPP_STEP("1", "v_min_i32_dpp", "row_bcast:31", "0xc");
+    VWL_DPP_END();
+    return x;
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_d_bcast(double x) { // rows outside ROWS get +0.0
+    const long long b = __double_as_longlong(x);
+    const int lo = dpp_bcast<CTRL, ROWS>(0, (int)b), hi = dpp_bcast<CTRL, ROWS>(0, (int)(b >> 32));
+    return __longlong_as_double(((long long)hi << 32) | (long long)(uint32_t)lo);
+}
+
+__device__ __forceinline__ double wave_sum_last(double x) {
+    x += dpp_d<kDppXor1>(x);
+    x += dpp_d<kDppXor2>(x);
+    x += dpp_d<kDppHalfMirror>(x);
+    x += dpp_d<kDppMirror>(x);
+    x += dpp_d_bcast<kDppBcast15, 0xa>(x);
+    x += dpp_d_bcast<kDppBcast31, 0xc>(x);
+    return x;
+}
+
 // Workgroup reductions: wave results go through LDS and every thread combines
 // the kWaves values in the same order, so all threads hold the same result.
 // With TRAIL = false the closing barrier is left out: the caller guarantees
@@ -165,8 +239,8 @@ __device__ __forceinline__ void block_max(float (&x)[N], float *lds /* kWaves*N 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-        const float m = wave_max(x[i]);
-        if (lane == 0)
+        const float m = wave_max_last(x[i]);
+        if (lane == 63)
             lds[wave * N + i] = m;
     }
     __syncthreads();
@@ -175,7 +249,7 @@ __device__ __forceinline__ void block_max(float (&x)[N], float *lds /* kWaves*N 
         float m = lds[i];
 #pragma unroll
         for (int w = 1; w < kWaves; ++w)
-            m = fmaxf(m, lds[w * N + i]);
+            m = fmax_raw(m, lds[w * N + i]);
         x[i] = m;
     }
     if (TRAIL)
@@ -187,8 +261,8 @@ __device__ __forceinline__ void block_sum(double (&x)[N], double *lds /* kWaves*
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-        const double s = wave_sum(x[i]);
-        if (lane == 0)
+        const double s = wave_sum_last(x[i]);
+        if (lane == 63)
             lds[wave * N + i] = s;
     }
     __syncthreads();
@@ -211,12 +285,12 @@ __device__ __forceinline__ void block_sum_min(double (&x)[N], int &imin, double 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-        const double s = wave_sum(x[i]);
-        if (lane == 0)
+        const double s = wave_sum_last(x[i]);
+        if (lane == 63)
             lds[wave * N + i] = s;
     }
-    const int m = wave_min_int(imin);
-    if (lane == 0)
+    const int m = wave_min_last(imin);
+    if (lane == 63)
         ldsi[wave] = m;
     __syncthreads();
 #pragma unroll
@@ -238,8 +312,8 @@ __device__ __forceinline__ void block_sum_min(double (&x)[N], int &imin, double 
 
 __device__ __forceinline__ int block_min_int(int x, int *lds /* kWaves */) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int m = wave_min_int(x);
-    if (lane == 0)
+    const int m = wave_min_last(x);
+    if (lane == 63)
         lds[wave] = m;
     __syncthreads();
     int r = lds[0];

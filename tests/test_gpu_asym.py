@@ -169,6 +169,22 @@ def test_every_plan(vwl, nv):
         vwl.set_plan_override("asym", 0, 0)
 
 
+def test_wide_team(vwl):
+    """More than 128 members per row (one fp32 vector per thread): every
+    member-record loop of the combine and the finalize goes past the first
+    two members per lane."""
+    import torch
+    x = W.gen_asym(2, 2, 151937, "f32", seed=91, identical_frac=0.2, tie_frac=0.2)
+    try:
+        vwl.set_plan_override("asym", 1, 0)
+        plan = vwl.plan_info("asym", x.B, x.K, x.V, torch.float32)
+        assert plan["team"] > 128, plan
+        dev, ora, rep = check(vwl, x, 1.0, 0.5, label="wide team %s" % plan)
+        np.testing.assert_array_equal(dev["fused"], ora.fused)
+    finally:
+        vwl.set_plan_override("asym", 0, 0)
+
+
 def test_few_teams_many_rounds(vwl):
     """A capped team count forces many rows per team (counter reuse per row)."""
     x = W.gen_asym(16, 3, 20000, "f32", seed=77)

@@ -118,6 +118,19 @@ def test_every_plan(vwl, nv):
         vwl.set_plan_override("asym", 0, 0)
 
 
+def test_wide_team(vwl):
+    """More than 128 members per row (one fp32 vector per thread)."""
+    import torch
+    x = W.gen_e2sci(2, 3, 151937, "f32", seed=92, identical_frac=0.2)
+    try:
+        vwl.set_plan_override("asym", 1, 0)
+        plan = vwl.e2sci_plan_info(2, 3, 151937, torch.float32)
+        assert plan["team"] > 128, plan
+        check(vwl, x, label="wide team %s" % plan)
+    finally:
+        vwl.set_plan_override("asym", 0, 0)
+
+
 def test_few_teams(vwl):
     x = W.gen_e2sci(16, 5, 20000, "f32", seed=79)
     try:

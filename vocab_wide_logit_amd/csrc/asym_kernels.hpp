@@ -144,12 +144,15 @@ __device__ __forceinline__ void team_lse(const uint64_t *rec_row, int W, const i
     }
 #pragma unroll
     for (int k = 0; k < N; ++k)
-        C[k] = fmaxf(r[k][0], r[k][1]);
-    for (int w = lane + 128; w < W; w += 64) { // teams wider than 128 members
-        const uint64_t *rw = rec_row + (size_t)w * stride;
+        C[k] = fmax_raw(r[k][0], r[k][1]);
+    for (int w0 = 128; w0 < W; w0 += 64) { // teams wider than 128 members
+        const int w = w0 + lane;
+        if (w < W) {
+            const uint64_t *rw = rec_row + (size_t)w0 * stride + lane * stride;
 #pragma unroll
-        for (int k = 0; k < N; ++k)
-            C[k] = fmaxf(C[k], ref(rw, k));
+            for (int k = 0; k < N; ++k)
+                C[k] = fmax_raw(C[k], ref(rw, k));
+        }
     }
     double t[N];
 #pragma unroll
@@ -157,11 +160,14 @@ __device__ __forceinline__ void team_lse(const uint64_t *rec_row, int W, const i
         C[k] = wave_max(C[k]);
         t[k] = scale_pow2(a[k][0], r[k][0] - C[k]) + scale_pow2(a[k][1], r[k][1] - C[k]);
     }
-    for (int w = lane + 128; w < W; w += 64) { // teams wider than 128 members
-        const uint64_t *rw = rec_row + (size_t)w * stride;
+    for (int w0 = 128; w0 < W; w0 += 64) { // teams wider than 128 members
+        const int w = w0 + lane;
+        if (w < W) {
+            const uint64_t *rw = rec_row + (size_t)w0 * stride + lane * stride;
 #pragma unroll
-        for (int k = 0; k < N; ++k)
-            t[k] += scale_pow2(as_f64(ld_relaxed(rw + sw[k])), ref(rw, k) - C[k]);
+            for (int k = 0; k < N; ++k)
+                t[k] += scale_pow2(as_f64(ld_relaxed(rw + sw[k])), ref(rw, k) - C[k]);
+        }
     }
 #pragma unroll
     for (int k = 0; k < N; ++k)
@@ -418,10 +424,16 @@ constexpr int asym_rows_waves() {
 // of lds_f, lds_d and lds_i is separated from the previous reads by another
 // barrier (the next reduction's, the team wait's, the combine's, or the
 // staging barriers of the next row).  The serial sections of a row (the
-// reductions, the record's publish, the team wait and the combine) run at a
-// raised wave priority: other workgroups' waves on the SIMD are then held
-// back in favour of the short chains that every member of a team waits on,
-// while the element passes run at the base priority.
+// reductions, the record's publish, the team wait and the combine) run at
+// wave priority 2: other workgroups' waves on the SIMD are then held back in
+// favour of the short chains that every member of a team waits on.  The
+// element passes run at priority 0, except on a member that found its team
+// already complete when it came to wait (the team was waiting for it): its
+// pass C and the next row's passes A+B run at priority 1, so the team's
+// slowest member takes issue slots from co-resident members of other teams
+// that are ahead of their own teams.  The members of a team share their CUs
+// with different workgroups for the whole launch, so without this their
+// speeds differ persistently and the team runs at its slowest member's pace.
 template <int DT, int NV, int DS, int GATE>
 __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, DS, GATE>())) void asym_rows_kernel(AsymParams P) {
     constexpr int EPV = Elem<DT>::kPerVec;
@@ -530,9 +542,10 @@ __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, DS, GATE>())) void a
         const uint64_t *rec_row = P.rec + (size_t)row * P.Wmax * kRecWords;
         __builtin_amdgcn_s_setprio(2);
         if (tid == 0)
-            sh_u[1] = wait_at_least(P.row_ctr + (size_t)row * 16, (uint32_t)W) ? 1u : 0u;
+            sh_u[1] = wait_at_least_seen(P.row_ctr + (size_t)row * 16, (uint32_t)W);
         __syncthreads();
-        if (!sh_u[1]) {
+        const uint32_t seen = __builtin_amdgcn_readfirstlane(sh_u[1]);
+        if (seen == 0u) {
             if (tid == 0)
                 set_dev_err(P.dev_err, 4);
             return;
@@ -546,7 +559,11 @@ __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, DS, GATE>())) void a
                 sh_row[cw] = L[0];
         }
         __syncthreads();
-        __builtin_amdgcn_s_setprio(0);
+        const bool straggler = seen == 2u; // the team was waiting for this member
+        if (straggler)
+            __builtin_amdgcn_s_setprio(1);
+        else
+            __builtin_amdgcn_s_setprio(0);
         const float la_c = (float)sh_row[0]; // row log-sum-exps, log2 units
         const float lb_c = (float)sh_row[1];
         // L_a - L_b in nats as an unevaluated float pair
@@ -572,7 +589,10 @@ __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, DS, GATE>())) void a
         block_sum<1, false>(Jd, lds_d);
         if (tid == 0)
             P.rec[((size_t)row * P.Wmax + member) * kRecWords + 6] = f64_bits(Jd[0]);
-        __builtin_amdgcn_s_setprio(0);
+        if (straggler)
+            __builtin_amdgcn_s_setprio(1);
+        else
+            __builtin_amdgcn_s_setprio(0);
 
         if (!has_next)
             break;
@@ -597,7 +617,7 @@ __global__ __launch_bounds__(kThreads) void asym_finalize_kernel(AsymParams P) {
     const double Lb = L2[0] * kLn2d, Lt = L2[1] * kLn2d;
     float fbest = -__builtin_inff();
     for (int w = lane; w < P.W; w += 64)
-        fbest = fmaxf(fbest, unpack_hi(ld_relaxed(rec_row + (size_t)w * kRecWords + 4)));
+        fbest = fmax_raw(fbest, unpack_hi(ld_relaxed(rec_row + (size_t)w * kRecWords + 4)));
     fbest = wave_max(fbest);
     double jsum = 0.0;
     int fidx = 0x7fffffff;

@@ -391,6 +391,15 @@ __device__ __forceinline__ bool wait_at_least(const uint32_t *ctr, uint32_t targ
     return true;
 }
 
+// As wait_at_least, telling also whether any waiting was needed:
+// 2 = the target was already reached at the first look, 1 = reached after
+// waiting, 0 = the bound expired.
+__device__ __forceinline__ uint32_t wait_at_least_seen(const uint32_t *ctr, uint32_t target) {
+    if (ld_counter(ctr) >= target)
+        return 2u;
+    return wait_at_least(ctr, target) ? 1u : 0u;
+}
+
 __device__ __forceinline__ void set_dev_err(int32_t *dev_err, int bits) {
     if (dev_err)
         __hip_atomic_fetch_or(dev_err, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

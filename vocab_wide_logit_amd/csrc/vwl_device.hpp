@@ -229,6 +229,72 @@ __device__ __forceinline__ double wave_sum_last(double x) {
     return x;
 }
 
+// N independent lane-63 reductions advanced together, one step across all N
+// values at a time, so that their dependency chains overlap.
+#define VWL_DPPN_I(OP, CTRL, ROWS, K) OP " %" #K ", %" #K ", %" #K " " CTRL " row_mask:" ROWS " bank_mask:0xf\n\t"
+#define VWL_DPPN_STEP(NOPS, OP, CTRL, ROWS)                                                              \
+    do {                                                                                                 \
+        if constexpr (N == 1)                                                                            \
+            asm("s_nop " NOPS "\n\t" VWL_DPPN_I(OP, CTRL, ROWS, 0) : "+v"(x[0]));                        \
+        else if constexpr (N == 2)                                                                       \
+            asm("s_nop " NOPS "\n\t" VWL_DPPN_I(OP, CTRL, ROWS, 0) VWL_DPPN_I(OP, CTRL, ROWS, 1)         \
+                : "+v"(x[0]), "+v"(x[1]));                                                               \
+        else if constexpr (N == 3)                                                                       \
+            asm("s_nop " NOPS "\n\t" VWL_DPPN_I(OP, CTRL, ROWS, 0) VWL_DPPN_I(OP, CTRL, ROWS, 1)         \
+                    VWL_DPPN_I(OP, CTRL, ROWS, 2)                                                        \
+                : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]));                                                   \
+        else                                                                                             \
+            asm("s_nop " NOPS "\n\t" VWL_DPPN_I(OP, CTRL, ROWS, 0) VWL_DPPN_I(OP, CTRL, ROWS, 1)         \
+                    VWL_DPPN_I(OP, CTRL, ROWS, 2) VWL_DPPN_I(OP, CTRL, ROWS, 3)                          \
+                : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]));                                       \
+    } while (0)
+
+#define VWL_DPPN_END()                                                                                   \
+    do {                                                                                                 \
+        if constexpr (N == 1)                                                                            \
+            asm("s_nop 1" : "+v"(x[0]));                                                                 \
+        else if constexpr (N == 2)                                                                       \
+            asm("s_nop 1" : "+v"(x[0]), "+v"(x[1]));                                                     \
+        else if constexpr (N == 3)                                                                       \
+            asm("s_nop 1" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]));                                         \
+        else                                                                                             \
+            asm("s_nop 1" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]));                             \
+    } while (0)
+
+template <int N>
+__device__ __forceinline__ void wave_max_last_n(float (&x)[N]) {
+    static_assert(N >= 1 && N <= 4, "up to four values");
+    VWL_DPPN_STEP("4", "v_max_f32_dpp", "quad_perm:[1,0,3,2]", "0xf");
+    VWL_DPPN_STEP("1", "v_max_f32_dpp", "quad_perm:[2,3,0,1]", "0xf");
+    VWL_DPPN_STEP("1", "v_max_f32_dpp", "row_half_mirror", "0xf");
+    VWL_DPPN_STEP("1", "v_max_f32_dpp", "row_mirror", "0xf");
+    VWL_DPPN_STEP("1", "v_max_f32_dpp", "row_bcast:15", "0xa");
+    VWL_DPPN_STEP("1", "v_max_f32_dpp", "row_bcast:31", "0xc");
+    VWL_DPPN_END();
+}
+
+template <int N>
+__device__ __forceinline__ void wave_sum_last_n(double (&x)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        x[i] += dpp_d<kDppXor1>(x[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        x[i] += dpp_d<kDppXor2>(x[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        x[i] += dpp_d<kDppHalfMirror>(x[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        x[i] += dpp_d<kDppMirror>(x[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        x[i] += dpp_d_bcast<kDppBcast15, 0xa>(x[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        x[i] += dpp_d_bcast<kDppBcast31, 0xc>(x[i]);
+}
+
 // Workgroup reductions: wave results go through LDS and every thread combines
 // the kWaves values in the same order, so all threads hold the same result.
 // With TRAIL = false the closing barrier is left out: the caller guarantees
@@ -237,20 +303,24 @@ __device__ __forceinline__ double wave_sum_last(double x) {
 template <int N, bool TRAIL = true>
 __device__ __forceinline__ void block_max(float (&x)[N], float *lds /* kWaves*N */) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    float m[N];
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-        const float m = wave_max_last(x[i]);
-        if (lane == 63)
-            lds[wave * N + i] = m;
+    for (int i = 0; i < N; ++i)
+        m[i] = x[i];
+    wave_max_last_n<N>(m);
+    if (lane == 63) {
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            lds[wave * N + i] = m[i];
     }
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-        float m = lds[i];
+        float r = lds[i];
 #pragma unroll
         for (int w = 1; w < kWaves; ++w)
-            m = fmax_raw(m, lds[w * N + i]);
-        x[i] = m;
+            r = fmax_raw(r, lds[w * N + i]);
+        x[i] = r;
     }
     if (TRAIL)
         __syncthreads();
@@ -259,20 +329,24 @@ __device__ __forceinline__ void block_max(float (&x)[N], float *lds /* kWaves*N 
 template <int N, bool TRAIL = true>
 __device__ __forceinline__ void block_sum(double (&x)[N], double *lds /* kWaves*N */) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    double m[N];
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-        const double s = wave_sum_last(x[i]);
-        if (lane == 63)
-            lds[wave * N + i] = s;
+    for (int i = 0; i < N; ++i)
+        m[i] = x[i];
+    wave_sum_last_n<N>(m);
+    if (lane == 63) {
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            lds[wave * N + i] = m[i];
     }
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-        double s = lds[i];
+        double r = lds[i];
 #pragma unroll
         for (int w = 1; w < kWaves; ++w)
-            s += lds[w * N + i];
-        x[i] = s;
+            r += lds[w * N + i];
+        x[i] = r;
     }
     if (TRAIL)
         __syncthreads();
@@ -283,23 +357,26 @@ template <int N, bool TRAIL = true>
 __device__ __forceinline__ void block_sum_min(double (&x)[N], int &imin, double *lds /* kWaves*N */,
                                               int *ldsi /* kWaves */) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    double m[N];
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-        const double s = wave_sum_last(x[i]);
-        if (lane == 63)
-            lds[wave * N + i] = s;
+    for (int i = 0; i < N; ++i)
+        m[i] = x[i];
+    wave_sum_last_n<N>(m);
+    const int mi = wave_min_last(imin);
+    if (lane == 63) {
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            lds[wave * N + i] = m[i];
+        ldsi[wave] = mi;
     }
-    const int m = wave_min_last(imin);
-    if (lane == 63)
-        ldsi[wave] = m;
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-        double s = lds[i];
+        double r = lds[i];
 #pragma unroll
         for (int w = 1; w < kWaves; ++w)
-            s += lds[w * N + i];
-        x[i] = s;
+            r += lds[w * N + i];
+        x[i] = r;
     }
     int r = ldsi[0];
 #pragma unroll

@@ -409,6 +409,13 @@ __global__ __launch_bounds__(kThreads) void lmhead_finalize_kernel(LmheadParams 
     }
 }
 
+int lmhead_blocks_per_cu() {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, lmhead_kernel<1>, kThreads, 0) != hipSuccess)
+        return 0;
+    return n;
+}
+
 hipError_t launch_lmhead(const LmheadParams &p, hipStream_t s, hipEvent_t after_rows) {
     const unsigned grid = (unsigned)(8 * (long long)p.RT * ((p.S + 7) / 8));
     const unsigned fin = (unsigned)((p.R + kWaves - 1) / kWaves);

@@ -53,6 +53,7 @@ struct DeviceInfo {
     int cus = 0;
     int asym_bpc[2][4][4][2] = {}; // [dtype][nv][delta source or kDeltaNone][gate]
     int rapid_bpc[2][4] = {};
+    int lm_bpc = 0;
 };
 constexpr int kMaxDevices = 64;
 DeviceInfo g_dev[kMaxDevices];
@@ -81,6 +82,7 @@ const DeviceInfo *device_info() {
                         d.asym_bpc[dt][k][ds][g] = asym_blocks_per_cu(dt, kNvChoices[k], ds, g);
                 d.rapid_bpc[dt][k] = rapid_blocks_per_cu(dt, kNvChoices[k]);
             }
+        d.lm_bpc = lmhead_blocks_per_cu();
         d.ready = true;
     }
     return &d;
@@ -488,6 +490,9 @@ struct LmGeom {
     int RT, S, range;
     size_t rec, rowstat, req_ctr, row_info, total;
 };
+// Shapes and workspace layout.  The records hold one entry per (row,
+// vocabulary range) for up to one range per 128-column tile, so the size
+// does not depend on the device; lm_split picks the ranges at launch.
 static bool lm_geometry(int B, int K, int V, int Hd, int Ht, LmGeom &g) {
     if (!shape_ok(B, K, V) || Hd < 64 || Ht < 64 || Hd % 64 || Ht % 64)
         return false;
@@ -496,22 +501,39 @@ static bool lm_geometry(int B, int K, int V, int Hd, int Ht, LmGeom &g) {
     if (RT > (1LL << 24))
         return false;
     const long long tiles = ((long long)V + 127) / 128;
-    long long S = (1536 + RT - 1) / RT;
-    S = S < 1 ? 1 : (S > tiles ? tiles : S);
-    const long long range = ((tiles + S - 1) / S) * 128;
-    S = ((long long)V + range - 1) / range;
-    if (8 * RT * ((S + 7) / 8) > 0x7fffffffLL)
+    if (8 * RT * ((tiles + 7) / 8) > 0x7fffffffLL)
         return false;
     g.RT = (int)RT;
-    g.S = (int)S;
-    g.range = (int)range;
+    g.S = (int)tiles;
+    g.range = 128;
     size_t off = 0;
-    g.rec = off;      off = align256(off + (size_t)R * S * kRecWords * 8);
+    g.rec = off;      off = align256(off + (size_t)R * tiles * kRecWords * 8);
     g.rowstat = off;  off = align256(off + (size_t)R * 2 * 8);
     g.req_ctr = off;  off = align256(off + (size_t)B * 16 * 4);
     g.row_info = off; off = align256(off + (size_t)R * 2 * 4);
     g.total = off;
     return true;
+}
+
+// Vocabulary ranges of whole 128-column tiles for `capacity` resident
+// workgroups: the split that finishes in the fewest tile steps, counting the
+// rounds of workgroups the grid needs (8 x RT x ceil(S / 8) workgroups with
+// the die-aware numbering); ties go to the finer split.
+static void lm_split(LmGeom &g, int V, long long capacity) {
+    const long long tiles = ((long long)V + 127) / 128;
+    long long best_cost = -1, best_r = 1;
+    for (long long r = 1; r <= tiles; ++r) {
+        const long long S = (tiles + r - 1) / r;
+        const long long grid = 8 * (long long)g.RT * ((S + 7) / 8);
+        const long long rounds = capacity > 0 ? (grid + capacity - 1) / capacity : 1;
+        const long long cost = rounds * r;
+        if (best_cost < 0 || cost < best_cost) {
+            best_cost = cost;
+            best_r = r;
+        }
+    }
+    g.range = (int)(best_r * 128);
+    g.S = (int)(((long long)V + g.range - 1) / g.range);
 }
 
 size_t vwl_asym_lmhead_workspace_bytes(int B, int K, int V, int Hd, int Ht) {
@@ -533,6 +555,10 @@ vwl_status asym_verify_lmhead(const void *h_a, const void *h_b, const void *W_d,
         return VWL_ERR_SHAPE;
     if (!finite_f(beta) || !finite_f(gamma) || gamma < 0.0f)
         return VWL_ERR_PARAM;
+    const DeviceInfo *dev = device_info();
+    if (!dev)
+        return VWL_ERR_HIP;
+    lm_split(g, V, (long long)dev->cus * dev->lm_bpc);
     if (!aligned(h_a, 16) || !aligned(h_b, 16) || !aligned(W_d, 16) || !aligned(h_t, 16) || !aligned(W_t, 16) ||
         !aligned(D, 4) || !aligned(gamma_eff, 4) || !aligned(fused, 4) || !aligned(accept_len, 4) ||
         !aligned(token, 4) || (draft && !aligned(draft, 4)) || (dev_err && !aligned(dev_err, 4)))

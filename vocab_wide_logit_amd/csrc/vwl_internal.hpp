@@ -147,6 +147,7 @@ struct LmheadParams {
     double *rowstat;  // [R][2] L_a, L_b (log2 units)
 };
 hipError_t launch_lmhead(const LmheadParams &p, hipStream_t s, hipEvent_t after_rows);
+int lmhead_blocks_per_cu();
 
 // AsymSpec variants (values match vwl_delta_source / vwl_gate of the C ABI);
 // kDeltaNone is the two-tensor divergence pass of E2-SCI.

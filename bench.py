@@ -406,12 +406,19 @@ def main():
         pl, rl = time_lmhead(vwl, xl, min(args.steps, 50), min(args.warmup, 5))
         ml = _median(pl)
         Rl = xl.B * (xl.K + 1)
-        flops = 2.0 * Rl * xl.V * (2 * xl.Hd + xl.Ht) + 2.0 * Rl * xl.V * 2 * xl.Hd  # two passes
+        # algorithmic work: the three products once, each head read once; the
+        # launches recompute a and b in their second pass (executed figures)
+        flops = 2.0 * Rl * xl.V * (2 * xl.Hd + xl.Ht)
+        flops_exec = flops + 2.0 * Rl * xl.V * 2 * xl.Hd
+        wbytes = float(xl.weight_bytes())
+        bound_ms = max(flops / (PEAK_BF16_TFLOPS * 1e12), wbytes / (PEAK_HBM_GBS * 1e9)) * 1e3
         result["secondary"][xl.name] = {
             "rows_per_s": Rl / (ml * 1e-3), "median_call_ms": ml, "median_gemm_passes_ms": _median(rl),
             "tflops": flops / (ml * 1e-3) / 1e12, "frac_of_bf16_peak": flops / (ml * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-            "head_weight_gbs": (xl.weight_bytes() + 2 * xl.V * xl.Hd) / (ml * 1e-3) / 1e9,
-            "flops_per_call": flops}
+            "executed_tflops": flops_exec / (ml * 1e-3) / 1e12,
+            "head_weight_gbs": wbytes / (ml * 1e-3) / 1e9,
+            "roofline_bound_ms": bound_ms, "frac_of_roofline": bound_ms / ml,
+            "flops_per_call": flops, "executed_flops_per_call": flops_exec}
         for xe in (W.e2sci_batched(), W.e2sci_single()):
             pe, re_ = time_e2sci(vwl, xe, args.steps, args.warmup)
             me, mre = _median(pe), _median(re_)

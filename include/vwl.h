@@ -357,6 +357,15 @@ vwl_status vwl_rapid_check(const void *z, const void *y, const int32_t *draft,
  * plan except through the documented fp32 summation order of the partials. */
 vwl_status vwl_set_plan_override(int mode, int nv, int max_teams);
 
+/* Tuning and test hook of asym_verify_xfam, process-wide for later calls:
+ * general = 1 forces the general verifier pass (a and b gathered through
+ * vmap, used anyway when a row is not made of 16-byte aligned vectors);
+ * segs in 1..16 pins the staged pass's number of drafter segments per row.
+ * 0 restores the automatic choice; other values give VWL_ERR_PARAM.  The
+ * results do not depend on either choice except through the fp64 summation
+ * order of the verifier's softmax partials. */
+vwl_status vwl_set_xfam_override(int general, int segs);
+
 /* Profiling hook: while `hip_event` (a hipEvent_t) is non-null, every
  * asym_verify / rapid_verify call records it on the call's stream right after
  * enqueuing the row kernel and before the kernels that follow it, so a caller

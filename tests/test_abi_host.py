@@ -142,6 +142,14 @@ def test_plan_override_validation(lib):
     assert lib.vwl_set_plan_override(0, 0, 0) == 0
 
 
+def test_xfam_override_validation(lib):
+    assert lib.vwl_set_xfam_override(2, 0) == 4
+    assert lib.vwl_set_xfam_override(0, -1) == 4
+    assert lib.vwl_set_xfam_override(0, 17) == 4
+    assert lib.vwl_set_xfam_override(1, 16) == 0
+    assert lib.vwl_set_xfam_override(0, 0) == 0
+
+
 def test_bf16_marshalling_is_exact():
     """The binding's host->device bf16 conversion keeps the stored bits."""
     import torch

@@ -126,3 +126,88 @@ def test_every_plan(vwl, nv):
         check(vwl, x, label="plan nv=%d" % nv)
     finally:
         vwl.set_plan_override("asym", 0, 0)
+
+
+def test_repeated_drafter_ids_and_flag_reset(vwl):
+    """A map that pairs some drafter tokens with several verifier tokens meets
+    the pairs in verifier order (the flag set by the inversion); the next call
+    with a one-to-one map meets them in drafter order again, so the flag and
+    the inverse map were cleared."""
+    x = W.gen_xfam(4, 2, 3000, 2800, 2000, "bf16", seed=25)
+    vm = x.vmap.copy()
+    paired = np.flatnonzero(vm >= 0)
+    rep = paired[1::7]
+    vm[rep] = vm[paired[0::7][:len(rep)]]
+    assert len(np.unique(vm[vm >= 0])) < int((vm >= 0).sum())
+    check(vwl, x, vmap=vm, label="repeated drafter ids")
+    check(vwl, x, label="one-to-one again")
+    check(vwl, x, vmap=vm, label="repeated drafter ids again")
+
+
+def test_equal_scores_resolve_to_lowest_verifier_id(vwl):
+    """Two pairs with equal fused scores, the lower verifier id paired with
+    the higher drafter id: the drafter-order pass meets the higher verifier id
+    first and must still report the lower one."""
+    x = W.gen_xfam(4, 2, 3000, 2800, 2000, "f32", seed=26)
+    paired = np.flatnonzero(x.vmap >= 0)
+    v_lo = v_hi = None
+    for i in range(len(paired) - 1):
+        for j in range(i + 1, min(i + 50, len(paired))):
+            if x.vmap[paired[i]] > x.vmap[paired[j]]:
+                v_lo, v_hi = int(paired[i]), int(paired[j])
+                break
+        if v_lo is not None:
+            break
+    assert v_lo is not None and v_lo < v_hi
+    d_lo, d_hi = int(x.vmap[v_lo]), int(x.vmap[v_hi])
+    assert d_lo > d_hi
+    t = x.t.copy()
+    t[:, :, v_lo] = 60.0
+    t[:, :, v_hi] = 60.0
+    x.a[:, :, d_lo] = x.a[:, :, d_hi]
+    x.b[:, :, d_lo] = x.b[:, :, d_hi]
+    dev, ora, rep = check(vwl, x, t=t, label="planted tie")
+    assert np.all(dev["fused"] == v_lo)
+    assert np.all(ora.fused == v_lo)
+
+
+def _with_xfam(vwl, general=False, segs=0):
+    class _Ctx:
+        def __enter__(self):
+            vwl.set_xfam_override(general, segs)
+
+        def __exit__(self, *exc):
+            vwl.set_xfam_override(False, 0)
+    return _Ctx()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("Vd,Vt,n", [(8, 8, 6), (4096, 40000, 3000), (65544, 65544, 50000),
+                                     (151936, 128256, 100000)])
+def test_staged_and_general_passes(vwl, dtype, Vd, Vt, n):
+    """Vocabularies of whole 16-byte vectors take the staged verifier pass
+    (the verifier row in LDS parts: one part, two for bf16 past 64K tokens,
+    four for fp32 at 128K); each segment count and the general pass (a and b
+    gathered through the map) give the oracle's results."""
+    x = W.gen_xfam(3, 2, Vd, Vt, max(0, n - min(16, Vd, Vt)), dtype, seed=5000 + Vd + Vt,
+                   n_special=min(16, Vd, Vt))
+    for general, segs in ((False, 0), (False, 1), (False, 3), (False, 16), (True, 0)):
+        with _with_xfam(vwl, general, segs):
+            check(vwl, x, label="general" if general else "staged segs=%d" % segs)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_repeated_drafter_ids_both_passes(vwl, dtype):
+    """Repeated drafter ids over several verifier parts (bf16 and fp32 rows
+    past one part), staged with two segment counts and general, with a
+    one-to-one map in between (the flag and the inverse map are cleared)."""
+    x = W.gen_xfam(3, 2, 70000, 70000, 60000, dtype, seed=27)
+    vm = x.vmap.copy()
+    paired = np.flatnonzero(vm >= 0)
+    rep = paired[1::5]
+    vm[rep] = vm[paired[0::5][:len(rep)]]
+    for general, segs in ((False, 0), (False, 4), (True, 0)):
+        with _with_xfam(vwl, general, segs):
+            check(vwl, x, vmap=vm, label="repeated ids general=%s segs=%d" % (general, segs))
+            check(vwl, x, label="one-to-one general=%s segs=%d" % (general, segs))
+

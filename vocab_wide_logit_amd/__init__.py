@@ -59,7 +59,7 @@ SYMBOLS = ("vwl_status_string", "vwl_version", "vwl_workspace_reset",
            "vwl_asym_workspace_bytes", "asym_verify", "asym_verify_variant", "vwl_asym_plan_info",
            "vwl_rapid_workspace_bytes", "rapid_verify",
            "vwl_plan_info", "vwl_asym_check", "vwl_rapid_check",
-           "vwl_set_plan_override", "vwl_set_phase_event",
+           "vwl_set_plan_override", "vwl_set_xfam_override", "vwl_set_phase_event",
            "vwl_e2sci_workspace_bytes", "e2sci_verify", "vwl_e2sci_plan_info",
            "vwl_asym_xfam_workspace_bytes", "asym_verify_xfam",
            "vwl_asym_lmhead_workspace_bytes", "asym_verify_lmhead")
@@ -121,6 +121,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.vwl_rapid_check.restype = i
         lib.vwl_set_plan_override.argtypes = [i, i, i]
         lib.vwl_set_plan_override.restype = i
+        lib.vwl_set_xfam_override.argtypes = [i, i]
+        lib.vwl_set_xfam_override.restype = i
         lib.vwl_asym_lmhead_workspace_bytes.argtypes = [i, i, i, i, i]
         lib.vwl_asym_lmhead_workspace_bytes.restype = sz
         lib.asym_verify_lmhead.argtypes = [P, P, P, P, P, P, i, i, i, i, i, f, f, P, P, P, P, P, P, P, P, sz, P]
@@ -225,6 +227,12 @@ def asym_plan_info(B: int, K: int, V: int, dtype: torch.dtype, delta: str = "a-b
 def set_plan_override(mode: str, vec_per_thread: int = 0, max_teams: int = 0) -> None:
     """Tuning hook: pin vectors per thread / cap teams (0 = automatic)."""
     _check(load_library().vwl_set_plan_override(0 if mode == "asym" else 1, vec_per_thread, max_teams))
+
+
+def set_xfam_override(general: bool = False, segs: int = 0) -> None:
+    """Test/tuning hook of asym_verify_xfam: force the general verifier pass,
+    or pin the staged pass's drafter segments per row (0 = automatic)."""
+    _check(load_library().vwl_set_xfam_override(1 if general else 0, segs))
 
 
 def set_phase_event(event) -> None:

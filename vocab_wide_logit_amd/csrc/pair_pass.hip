@@ -106,19 +106,31 @@ template int asym_blocks_per_cu_ds<kDeltaNone>(int dt, int nv, int gate);
 // v with a drafter token (string-identical tokens and paired specials) or
 // is -1.  Generation is restricted to the paired tokens.
 //
-// Launch 1: the two-tensor row kernel over a, b (L_a, L_b, the JSD partials).
-// Launch 2, xfam_verifier_kernel: one workgroup per (row, chunk of the
-// verifier vocabulary): online softmax statistics of t, and the maximum of
-// t[v] + beta*(a[vmap v] - b[vmap v]) over the paired v with its lowest
-// index, the drafter values gathered through the alignment.
+// Staged pass (16-byte aligned rows; the usual case):
+//   Launch 0, xfam_invert_kernel: the inverse alignment xinv[d] = v + 1 for
+//     each pair (v, d), with a flag when some drafter token is paired twice.
+//   Launch 1: the two-tensor row kernel over a, b (L_a, L_b, the JSD partials).
+//   Launch 2, xfam_staged_kernel: one 1024-thread workgroup per (row, part of
+//     the verifier row, segment of the drafter row).  The part (at most
+//     128 KiB) is copied into LDS; the segment's a, b and xinv are streamed
+//     contiguously, and each pair (v, d) whose v lies in the part reads t[v]
+//     from LDS.  So t, a and b are read once from memory, with no gathers.
+//     Each workgroup also takes the online softmax statistics of one share of
+//     its part.  Under a map that pairs a drafter token twice (flag set) the
+//     pairs are met in verifier order instead: v over the share, a and b
+//     gathered through vmap.
+// General pass (any alignment): launch 2 is xfam_verifier_kernel, one
+// 256-thread workgroup per (row, 4096-token verifier chunk), a and b gathered
+// through vmap; no launch 0.
 // Launch 3, xfam_finalize_kernel: one wave per row combines both record
 // sets, tests the draft (a verifier id) against the drafter's compressed-view
-// probability of its pair, and scans each request.
+// probability of its pair, and scans each request; after a staged pass its
+// threads also clear the inverse alignment and the flag for the next call.
 // ---------------------------------------------------------------------------
 
 // Workgroup b runs on die b % 8 (round-robin dispatch); the chunks of one row
-// go to workgroups of one die, so the row's gathered drafter values are
-// fetched into one L2.  Returns false for the padding workgroups.
+// go to workgroups of one die, so what they share of the row is fetched into
+// one L2.  Returns false for the padding workgroups.
 __device__ __forceinline__ bool xfam_item(const AsymParams &P, long long &row, int &chunk) {
     constexpr int kDies = 8;
     const long long b = blockIdx.x;
@@ -126,6 +138,168 @@ __device__ __forceinline__ bool xfam_item(const AsymParams &P, long long &row, i
     row = die + kDies * (k / P.vchunks);
     chunk = (int)(k % P.vchunks);
     return row < P.R;
+}
+
+// One thread per verifier token: the inverse alignment (an entry outside
+// [-1, Vd) counts as unpaired and sets the map bit of dev_err).
+__global__ __launch_bounds__(kThreads) void xfam_invert_kernel(AsymParams P) {
+    const long long v = (long long)blockIdx.x * kThreads + threadIdx.x;
+    if (v >= P.Vt)
+        return;
+    const int d = P.vmap[v];
+    if (d < -1 || d >= P.V) {
+        set_dev_err(P.dev_err, 8);
+        return;
+    }
+    if (d < 0)
+        return;
+    uint32_t expected = 0u;
+    if (!__hip_atomic_compare_exchange_strong(P.xinv + d, &expected, (uint32_t)v + 1u, __ATOMIC_RELAXED,
+                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+        __hip_atomic_fetch_or(P.xdup, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The running fused maximum of a thread and its lowest verifier id: a score
+// replaces it when larger, or equal with a lower id (NaN scores never do).
+struct FusedBest {
+    float s;
+    int v;
+};
+__device__ __forceinline__ void fused_take(FusedBest &fb, float sc, int v) {
+    const bool take = (sc > fb.s) | ((sc == fb.s) & (v < fb.v)); // no short-circuit branch
+    fb.s = take ? sc : fb.s;
+    fb.v = take ? v : fb.v;
+}
+
+__device__ __forceinline__ uint32_t xword(const uint4 &w, int i) {
+    return i == 0 ? w.x : i == 1 ? w.y : i == 2 ? w.z : w.w;
+}
+
+// One element of the staged verifier part.
+template <int DT>
+__device__ __forceinline__ float lds_elem(const uint4 *part, int i) {
+    if (DT == DT_BF16)
+        return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(part)[i] << 16);
+    return reinterpret_cast<const float *>(part)[i];
+}
+
+constexpr int kXlWaves = kXlThreads / 64;
+
+template <int DT>
+__global__ __launch_bounds__(kXlThreads) void xfam_staged_kernel(AsymParams P) {
+    constexpr int EPV = Elem<DT>::kPerVec;
+    constexpr int XV = EPV / 4; // 16-byte vectors of xinv per vector of logits
+    __shared__ uint4 part[kXlLdsVecs];
+    __shared__ float lds_f[kXlWaves * 2];
+    __shared__ double lds_d[kXlWaves];
+    __shared__ int lds_i[kXlWaves];
+    long long row;
+    int chunk;
+    if (!xfam_item(P, row, chunk))
+        return;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int pi = chunk % P.xparts, seg = chunk / P.xparts;
+    const int plo = pi * P.xpartlen;
+    const int plen = min(P.xpartlen, P.Vt - plo); // a multiple of EPV
+    const float NEG_INF = -__builtin_inff();
+
+    // 1. the part into LDS: vector j*1024 + tid, straight from memory
+    {
+        const uint4 *src = reinterpret_cast<const uint4 *>(P.tv) + ((size_t)row * P.Vt + plo) / EPV;
+        const int nvec = plen / EPV;
+#pragma unroll
+        for (int j = 0; j < kXlLdsVecs / kXlThreads; ++j) {
+            const int vi = j * kXlThreads + tid;
+            if (vi < nvec)
+                g2lds16(src + vi, part + j * kXlThreads + wave * 64);
+        }
+    }
+    __syncthreads();
+
+    // 2. the pairs with v in this part
+    FusedBest fb{NEG_INF, 0x7fffffff};
+    const int dlo = seg * P.xseglen, dhi = min(P.V, dlo + P.xseglen);
+    if (ld_relaxed(P.xdup) == 0u) { // drafter order over the segment
+        const size_t rv = (size_t)row * P.V / EPV;
+        const uint4 *A4 = reinterpret_cast<const uint4 *>(P.a) + rv;
+        const uint4 *B4 = reinterpret_cast<const uint4 *>(P.b) + rv;
+        const uint4 *X4 = reinterpret_cast<const uint4 *>(P.xinv);
+        const int q1 = dhi > dlo ? dhi / EPV : 0;
+        for (int q = dlo / EPV + tid; q < q1; q += 2 * kXlThreads) {
+            // two vectors per thread in flight; the second may be past the
+            // segment and then re-reads the first
+            const int q2 = q + kXlThreads < q1 ? q + kXlThreads : q;
+            uint4 va[2], vb[2], vx[2][XV];
+            va[0] = A4[q];
+            vb[0] = B4[q];
+            va[1] = A4[q2];
+            vb[1] = B4[q2];
+#pragma unroll
+            for (int i = 0; i < XV; ++i) {
+                vx[0][i] = X4[(size_t)q * XV + i];
+                vx[1][i] = X4[(size_t)q2 * XV + i];
+            }
+            // every lane reads t for all its elements (unpaired ones read
+            // element 0, a broadcast), then masks their scores to NaN,
+            // which never replaces the running maximum
+            float tv[2][EPV];
+            bool in[2][EPV];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) {
+                    const int iv = (int)xword(vx[h][e >> 2], e & 3) - 1 - plo; // part-relative verifier id
+                    in[h][e] = (unsigned)iv < (unsigned)plen && (h == 0 || q2 != q);
+                    tv[h][e] = lds_elem<DT>(part, in[h][e] ? iv : 0);
+                }
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) {
+                    const float sc = fused_score<kDeltaAMinusB>(widen<DT>(va[h], e), widen<DT>(vb[h], e), tv[h][e],
+                                                                P.beta);
+                    fused_take(fb, in[h][e] ? sc : __builtin_nanf(""), (int)xword(vx[h][e >> 2], e & 3) - 1);
+                }
+        }
+    }
+    // 3. this segment's share of the part: L_t statistics (and, for a map
+    // that repeats a drafter id, the pairs in verifier order)
+    const int slo = min(plen, seg * P.xsharelen), shi = min(plen, slo + P.xsharelen);
+    OnlineLse st;
+    online_init(st);
+    for (int vi = slo / EPV + tid; vi < shi / EPV; vi += kXlThreads) {
+        const uint4 w = part[vi];
+        float x[EPV];
+#pragma unroll
+        for (int e = 0; e < EPV; ++e)
+            x[e] = widen<DT>(w, e);
+        online_group<EPV>(st, x);
+    }
+    if (ld_relaxed(P.xdup) != 0u) {
+        const size_t arow = (size_t)row * P.V;
+        for (int i = slo + tid; i < shi; i += kXlThreads) {
+            const int d = P.vmap[plo + i];
+            if (d >= 0 && d < P.V) {
+                const float sc = fused_score<kDeltaAMinusB>(load_scalar<DT>(P.a, arow + d),
+                                                            load_scalar<DT>(P.b, arow + d),
+                                                            lds_elem<DT>(part, i), P.beta);
+                fused_take(fb, sc, plo + i);
+            }
+        }
+    }
+    (void)lane;
+    // 4. the workgroup's record
+    float mx[2] = {st.c, fb.s};
+    block_max<2, true, kXlWaves>(mx, lds_f);
+    int fi = (fb.s == mx[1]) ? fb.v : 0x7fffffff;
+    double S[1] = {rescale_to(st, mx[0])};
+    block_sum_min<1, true, kXlWaves>(S, fi, lds_d, lds_i);
+    if (tid == 0) {
+        uint64_t *r = P.vrec + ((size_t)row * P.vchunks + chunk) * kVrecWords;
+        r[0] = f64_bits(S[0]);
+        r[1] = pack2(mx[0], mx[1]);
+        r[2] = (uint64_t)(uint32_t)fi;
+    }
 }
 
 template <int DT>
@@ -165,24 +339,17 @@ __global__ __launch_bounds__(kThreads) void xfam_verifier_kernel(AsymParams P) {
         xa[k] = load_scalar<DT>(P.a, arow + ec);
         xb[k] = load_scalar<DT>(P.b, arow + ec);
     }
-    float best = NEG_INF;
-    int bidx = 0x7fffffff;
+    FusedBest fb{NEG_INF, 0x7fffffff};
 #pragma unroll
-    for (int k = 0; k < kXfamEpt; ++k) {
-        if (e[k] >= 0) {
-            const float sc = fused_score<kDeltaAMinusB>(xa[k], xb[k], x[k], P.beta);
-            if (sc > best || bidx == 0x7fffffff) { // first paired element, then strictly larger
-                best = sc;
-                bidx = v0 + k * kThreads + tid;
-            }
-        }
-    }
+    for (int k = 0; k < kXfamEpt; ++k)
+        if (e[k] >= 0)
+            fused_take(fb, fused_score<kDeltaAMinusB>(xa[k], xb[k], x[k], P.beta), v0 + k * kThreads + tid);
     OnlineLse st;
     online_init(st);
     online_group<kXfamEpt>(st, x);
-    float mx[2] = {st.c, best};
+    float mx[2] = {st.c, fb.s};
     block_max<2>(mx, lds_f);
-    int fi = (best == mx[1]) ? bidx : 0x7fffffff;
+    int fi = (fb.s == mx[1]) ? fb.v : 0x7fffffff;
     double S[1] = {rescale_to(st, mx[0])};
     block_sum_min<1>(S, fi, lds_d, lds_i);
     if (tid == 0) {
@@ -201,6 +368,11 @@ __global__ __launch_bounds__(kThreads) void xfam_finalize_kernel(AsymParams P) {
     const long long row = (long long)blockIdx.x * kWaves + (threadIdx.x >> 6);
     if (blockIdx.x == 0 && threadIdx.x == 0)
         P.ctl[0] = 0u; // ticket counter of the row kernel, for the next call
+    // the inverse alignment and its flag, for the next call
+    if (P.xparts > 0)
+        for (long long d = (long long)blockIdx.x * kThreads + threadIdx.x; d <= P.V;
+             d += (long long)gridDim.x * kThreads)
+            P.xinv[d] = 0u; // d == V is the flag word
     if (row >= P.R)
         return;
     // drafter side: L_b (log2 units) and the JSD partials
@@ -277,12 +449,23 @@ inline long long xfam_verifier_grid(long long R, int chunks) { return 8 * ((R + 
 
 template <int DT, int NV>
 static hipError_t launch_x(const Plan &plan, const AsymParams &p, hipStream_t s, hipEvent_t after_rows) {
+    hipError_t e;
+    if (p.xparts > 0) {
+        hipLaunchKernelGGL(xfam_invert_kernel, dim3((unsigned)(((long long)p.Vt + kThreads - 1) / kThreads)),
+                           dim3(kThreads), 0, s, p);
+        e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
     hipLaunchKernelGGL((asym_rows_kernel<DT, NV, kDeltaNone, kGateCda>), dim3(plan.grid), dim3(kThreads), 0, s, p);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL((xfam_verifier_kernel<DT>), dim3((unsigned)xfam_verifier_grid(p.R, p.vchunks)),
-                       dim3(kThreads), 0, s, p);
+    const unsigned vgrid = (unsigned)xfam_verifier_grid(p.R, p.vchunks);
+    if (p.xparts > 0)
+        hipLaunchKernelGGL((xfam_staged_kernel<DT>), dim3(vgrid), dim3(kXlThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((xfam_verifier_kernel<DT>), dim3(vgrid), dim3(kThreads), 0, s, p);
     e = hipGetLastError();
     if (e != hipSuccess)
         return e;

@@ -6,6 +6,7 @@
 #include <cstdint>
 #include <cstring>
 #include <limits>
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 
@@ -62,6 +63,7 @@ std::mutex g_dev_mu;
 // Plan overrides for tuning sweeps (0 = automatic).
 int g_force_nv[2] = {0, 0};
 int g_force_teams[2] = {0, 0};
+int g_xfam_general = 0, g_xfam_segs = 0; // cross-family verifier pass overrides
 std::atomic<hipEvent_t> g_phase_event{nullptr};
 
 const DeviceInfo *device_info() {
@@ -327,6 +329,18 @@ vwl_status vwl_set_plan_override(int mode, int nv, int max_teams) {
     return VWL_OK;
 }
 
+/* Tuning and test hook of asym_verify_xfam: general = 1 forces the general
+ * verifier pass; segs (1..16) pins the staged pass's segment count; 0 = automatic. */
+vwl_status vwl_set_xfam_override(int general, int segs) {
+    if (general != 0 && general != 1)
+        return VWL_ERR_PARAM;
+    if (segs < 0 || segs > kXfamMaxSegs)
+        return VWL_ERR_PARAM;
+    g_xfam_general = general;
+    g_xfam_segs = segs;
+    return VWL_OK;
+}
+
 vwl_status vwl_set_phase_event(void *hip_event) {
     g_phase_event.store(static_cast<hipEvent_t>(hip_event));
     return VWL_OK;
@@ -400,25 +414,66 @@ vwl_status asym_verify(const void *a, const void *b, const void *t, const int32_
                                stream);
 }
 
-// Cross-family workspace: the AsymSpec layout of the drafter rows followed by
-// the verifier records.
-static bool xfam_layout(int B, int K, int Vd, int Vt, vwl_dtype dt, WsLayout &L, size_t &vrec, size_t &total) {
+// Cross-family workspace: the AsymSpec layout of the drafter rows, the
+// verifier records (enough for either verifier pass), then the inverse
+// alignment and its flag.
+static bool xfam_layout(int B, int K, int Vd, int Vt, vwl_dtype dt, WsLayout &L, size_t &vrec, size_t &xinv,
+                        size_t &total) {
     if (!shape_ok(B, K, Vd) || !shape_ok(B, K, Vt) || (dt != VWL_F32 && dt != VWL_BF16))
         return false;
     const long long R = (long long)B * (K + 1);
-    const int C = xfam_chunks(Vt);
-    if (8 * ((R + 7) / 8) * (long long)C > 0x7fffffffLL) // workgroups of the verifier pass
+    const long long C = std::max<long long>(xfam_chunks(Vt), (long long)xfam_parts(Vt, elem_bytes(dt)) * kXfamMaxSegs);
+    if (8 * ((R + 7) / 8) * C > 0x7fffffffLL) // workgroups of the verifier pass
         return false;
     L = ws_layout(B, K + 1, Vd, elem_bytes(dt), false);
     vrec = L.total;
-    total = align256(vrec + (size_t)R * C * kVrecWords * 8);
+    xinv = align256(vrec + (size_t)R * C * kVrecWords * 8);
+    total = align256(xinv + ((size_t)Vd + 64) * 4); // xinv[Vd], then the flag word
+    return true;
+}
+
+// Geometry of the staged verifier pass, or false when the general pass runs:
+// the rows must be made of whole 16-byte vectors at 16-byte aligned
+// addresses.  Parts: the fewest that fit kXlLdsVecs vectors, of equal length
+// (a multiple of 8 tokens).  Segments: the count (up to kXfamMaxSegs) that
+// minimises rounds of resident workgroups (one per CU) times the bytes one
+// workgroup moves (its part plus its segment's a, b and xinv).
+static bool xfam_staged_geometry(const void *a, const void *b, const void *t, int Vd, int Vt, int dt, long long R,
+                                 int cus, AsymParams &p) {
+    const int eb = elem_bytes(dt);
+    if (g_xfam_general || !aligned(a, 16) || !aligned(b, 16) || !aligned(t, 16) || ((long long)Vd * eb) % 16 ||
+        ((long long)Vt * eb) % 16)
+        return false;
+    const int parts = xfam_parts(Vt, eb);
+    const int partlen = (int)((((long long)Vt + parts - 1) / parts + 7) / 8 * 8);
+    if ((long long)partlen * eb > (long long)kXlLdsVecs * 16 || (long long)(parts - 1) * partlen >= Vt)
+        return false;
+    int best_s = 1;
+    double best_cost = 0.0;
+    for (int sg = 1; sg <= kXfamMaxSegs; ++sg) {
+        if (g_xfam_segs && sg != g_xfam_segs)
+            continue;
+        const long long seglen = (((long long)Vd + sg - 1) / sg + 7) / 8 * 8;
+        const long long rounds = (8 * ((R + 7) / 8) * parts * sg + cus - 1) / cus;
+        const double cost = (double)rounds * ((double)partlen * eb + (double)seglen * (2.0 * eb + 4.0));
+        if (sg == 1 || g_xfam_segs || cost < best_cost) {
+            best_cost = cost;
+            best_s = sg;
+        }
+    }
+    p.xparts = parts;
+    p.xpartlen = partlen;
+    p.xsegs = best_s;
+    p.xseglen = (int)((((long long)Vd + best_s - 1) / best_s + 7) / 8 * 8);
+    p.xsharelen = (int)((((long long)partlen + best_s - 1) / best_s + 7) / 8 * 8);
+    p.vchunks = parts * best_s;
     return true;
 }
 
 size_t vwl_asym_xfam_workspace_bytes(int B, int K, int Vd, int Vt, vwl_dtype dt) {
     WsLayout L;
-    size_t vrec, total;
-    return xfam_layout(B, K, Vd, Vt, dt, L, vrec, total) ? total : 0;
+    size_t vrec, xinv, total;
+    return xfam_layout(B, K, Vd, Vt, dt, L, vrec, xinv, total) ? total : 0;
 }
 
 vwl_status asym_verify_xfam(const void *a, const void *b, int Vd, const void *t, int Vt, const int32_t *vmap,
@@ -438,14 +493,17 @@ vwl_status asym_verify_xfam(const void *a, const void *b, int Vd, const void *t,
     if (st != VWL_OK)
         return st;
     WsLayout L;
-    size_t vrec, total;
-    if (!xfam_layout(B, K, Vd, Vt, dt, L, vrec, total))
+    size_t vrec, xinv, total;
+    if (!xfam_layout(B, K, Vd, Vt, dt, L, vrec, xinv, total))
         return VWL_ERR_SHAPE;
     if (!aligned(vmap, 4) || (dev_err && !aligned(dev_err, 4)))
         return VWL_ERR_ALIGN;
     const long long R = (long long)B * (K + 1);
     Plan plan;
     if (!make_plan(0, (int)dt, R, Vd, plan, kDeltaNone, kGateCda))
+        return VWL_ERR_HIP;
+    const DeviceInfo *dev = device_info();
+    if (!dev)
         return VWL_ERR_HIP;
     char *ws = static_cast<char *>(workspace);
     AsymParams p{};
@@ -454,9 +512,14 @@ vwl_status asym_verify_xfam(const void *a, const void *b, int Vd, const void *t,
     p.t = nullptr;
     p.tv = t;
     p.Vt = Vt;
-    p.vchunks = xfam_chunks(Vt);
+    if (!xfam_staged_geometry(a, b, t, Vd, Vt, (int)dt, R, dev->cus, p)) {
+        p.xparts = 0;
+        p.vchunks = xfam_chunks(Vt);
+    }
     p.vmap = vmap;
     p.vrec = reinterpret_cast<uint64_t *>(ws + vrec);
+    p.xinv = reinterpret_cast<uint32_t *>(ws + xinv);
+    p.xdup = p.xinv + Vd;
     p.draft = draft;
     p.R = R;
     p.B = B;

@@ -296,12 +296,12 @@ __device__ __forceinline__ void wave_sum_last_n(double (&x)[N]) {
 }
 
 // Workgroup reductions: wave results go through LDS and every thread combines
-// the kWaves values in the same order, so all threads hold the same result.
+// the WAVES values in the same order, so all threads hold the same result.
 // With TRAIL = false the closing barrier is left out: the caller guarantees
 // that another workgroup barrier separates the reads of `lds` from its next
-// write.
-template <int N, bool TRAIL = true>
-__device__ __forceinline__ void block_max(float (&x)[N], float *lds /* kWaves*N */) {
+// write.  WAVES is the workgroup's wave count (kWaves unless stated).
+template <int N, bool TRAIL = true, int WAVES = kWaves>
+__device__ __forceinline__ void block_max(float (&x)[N], float *lds /* WAVES*N */) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     float m[N];
 #pragma unroll
@@ -318,7 +318,7 @@ __device__ __forceinline__ void block_max(float (&x)[N], float *lds /* kWaves*N 
     for (int i = 0; i < N; ++i) {
         float r = lds[i];
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w)
+        for (int w = 1; w < WAVES; ++w)
             r = fmax_raw(r, lds[w * N + i]);
         x[i] = r;
     }
@@ -326,8 +326,8 @@ __device__ __forceinline__ void block_max(float (&x)[N], float *lds /* kWaves*N 
         __syncthreads();
 }
 
-template <int N, bool TRAIL = true>
-__device__ __forceinline__ void block_sum(double (&x)[N], double *lds /* kWaves*N */) {
+template <int N, bool TRAIL = true, int WAVES = kWaves>
+__device__ __forceinline__ void block_sum(double (&x)[N], double *lds /* WAVES*N */) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     double m[N];
 #pragma unroll
@@ -344,7 +344,7 @@ __device__ __forceinline__ void block_sum(double (&x)[N], double *lds /* kWaves*
     for (int i = 0; i < N; ++i) {
         double r = lds[i];
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w)
+        for (int w = 1; w < WAVES; ++w)
             r += lds[w * N + i];
         x[i] = r;
     }
@@ -353,9 +353,9 @@ __device__ __forceinline__ void block_sum(double (&x)[N], double *lds /* kWaves*
 }
 
 // Sums of N doubles and the minimum of one int in a single LDS round.
-template <int N, bool TRAIL = true>
-__device__ __forceinline__ void block_sum_min(double (&x)[N], int &imin, double *lds /* kWaves*N */,
-                                              int *ldsi /* kWaves */) {
+template <int N, bool TRAIL = true, int WAVES = kWaves>
+__device__ __forceinline__ void block_sum_min(double (&x)[N], int &imin, double *lds /* WAVES*N */,
+                                              int *ldsi /* WAVES */) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     double m[N];
 #pragma unroll
@@ -374,13 +374,13 @@ __device__ __forceinline__ void block_sum_min(double (&x)[N], int &imin, double 
     for (int i = 0; i < N; ++i) {
         double r = lds[i];
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w)
+        for (int w = 1; w < WAVES; ++w)
             r += lds[w * N + i];
         x[i] = r;
     }
     int r = ldsi[0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w)
+    for (int w = 1; w < WAVES; ++w)
         r = min(r, ldsi[w]);
     imin = r;
     if (TRAIL)

@@ -87,11 +87,18 @@ struct AsymParams {
     uint64_t *rec;
     // AsymSpec across families: verifier rows on their own vocabulary Vt,
     // the alignment vmap[Vt] (paired drafter id or -1), per-(row, chunk)
-    // verifier records [R][vchunks][kVrecWords]
+    // verifier records [R][vchunks][kVrecWords].  The staged verifier pass
+    // (xparts > 0) also uses the inverse alignment xinv[Vd] (verifier id + 1
+    // of drafter token d, 0 = none) and the flag xdup (some drafter token is
+    // paired twice), both zero between calls; the verifier row in xparts
+    // parts of xpartlen tokens, the drafter row in xsegs segments of xseglen
+    // tokens, and xsharelen tokens of a part per segment for L_t.
     const void *tv;
     int Vt, vchunks;
     const int32_t *vmap;
     uint64_t *vrec;
+    uint32_t *xinv, *xdup;
+    int xparts, xpartlen, xsegs, xseglen, xsharelen;
     // E2-SCI (a = drafter y, b = target z; `win` rows per request)
     int win;
     const float *thr_in, *omega;
@@ -170,6 +177,16 @@ constexpr int kXfamEpt = 16;
 constexpr int kXfamChunk = kThreads * kXfamEpt;
 constexpr int kVrecWords = 4;
 inline int xfam_chunks(int Vt) { return (Vt + kXfamChunk - 1) / kXfamChunk; }
+// Staged verifier pass: 1024-thread workgroups, each holding one part of a
+// verifier row (at most 128 KiB) in LDS; at most kXfamMaxSegs drafter
+// segments per row.
+constexpr int kXlThreads = 1024;
+constexpr int kXlLdsVecs = 8192;
+constexpr int kXfamMaxSegs = 16;
+inline int xfam_parts(int Vt, int elem_bytes) {
+    const int cap = kXlLdsVecs * 16 / elem_bytes;
+    return (Vt + cap - 1) / cap;
+}
 hipError_t launch_rapid(int dt, const Plan &plan, const RapidParams &p, hipStream_t s, hipEvent_t after_rows);
 hipError_t launch_fill_zero(void *ptr, size_t bytes, hipStream_t s);
 

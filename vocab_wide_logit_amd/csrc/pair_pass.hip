@@ -107,18 +107,20 @@ template int asym_blocks_per_cu_ds<kDeltaNone>(int dt, int nv, int gate);
 // is -1.  Generation is restricted to the paired tokens.
 //
 // Staged pass (16-byte aligned rows; the usual case):
-//   Launch 0, xfam_invert_kernel: the inverse alignment xinv[d] = v + 1 for
-//     each pair (v, d), with a flag when some drafter token is paired twice.
+//   Launch 0, xfam_invert_kernel: the inverse alignment per part of the
+//     verifier row, xkey[p][d] = i + 1 for each pair (v, d) with v the i-th
+//     token of part p, with a flag when two such v share a drafter token.
 //   Launch 1: the two-tensor row kernel over a, b (L_a, L_b, the JSD partials).
 //   Launch 2, xfam_staged_kernel: one 1024-thread workgroup per (row, part of
 //     the verifier row, segment of the drafter row).  The part (at most
-//     128 KiB) is copied into LDS; the segment's a, b and xinv are streamed
-//     contiguously, and each pair (v, d) whose v lies in the part reads t[v]
-//     from LDS.  So t, a and b are read once from memory, with no gathers.
-//     Each workgroup also takes the online softmax statistics of one share of
-//     its part.  Under a map that pairs a drafter token twice (flag set) the
-//     pairs are met in verifier order instead: v over the share, a and b
-//     gathered through vmap.
+//     128 KiB) is copied into LDS behind one vector of -inf; the segment's a,
+//     b and xkey[p] are streamed contiguously, and every drafter token reads
+//     t at the LDS address of its key (the -inf slot when it has no pair in
+//     the part).  So t, a and b are read once from memory, with no gathers.
+//     Each thread keeps its maximum score and the lowest key (so verifier id)
+//     reaching it.  Each workgroup also takes the online softmax statistics
+//     of one share of its part.  Under a flagged map the pairs are met in
+//     verifier order instead: v over the share, a and b gathered via vmap.
 // General pass (any alignment): launch 2 is xfam_verifier_kernel, one
 // 256-thread workgroup per (row, 4096-token verifier chunk), a and b gathered
 // through vmap; no launch 0.
@@ -140,8 +142,10 @@ __device__ __forceinline__ bool xfam_item(const AsymParams &P, long long &row, i
     return row < P.R;
 }
 
-// One thread per verifier token: the inverse alignment (an entry outside
-// [-1, Vd) counts as unpaired and sets the map bit of dev_err).
+// One thread per verifier token: its entry of the inverse alignment of its
+// part (an entry of vmap outside [-1, Vd) counts as unpaired and sets the
+// map bit of dev_err).
+template <int DT>
 __global__ __launch_bounds__(kThreads) void xfam_invert_kernel(AsymParams P) {
     const long long v = (long long)blockIdx.x * kThreads + threadIdx.x;
     if (v >= P.Vt)
@@ -153,9 +157,16 @@ __global__ __launch_bounds__(kThreads) void xfam_invert_kernel(AsymParams P) {
     }
     if (d < 0)
         return;
-    uint32_t expected = 0u;
-    if (!__hip_atomic_compare_exchange_strong(P.xinv + d, &expected, (uint32_t)v + 1u, __ATOMIC_RELAXED,
-                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+    // 16-bit keys set with an atomic OR on their 32-bit word: a key that was
+    // already set means a repeated drafter id (the flag; the keys are then
+    // not used)
+    const int pi = (int)(v / P.xpartlen);
+    const uint32_t key = (uint32_t)(v - (long long)pi * P.xpartlen) + 1u;
+    const size_t k = (size_t)pi * P.V + d;
+    const int shift = (int)(k & 1) * 16;
+    uint32_t *word = reinterpret_cast<uint32_t *>(P.xkey) + k / 2;
+    const uint32_t old = __hip_atomic_fetch_or(word, key << shift, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((old >> shift) & 0xffffu)
         __hip_atomic_fetch_or(P.xdup, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -175,21 +186,43 @@ __device__ __forceinline__ uint32_t xword(const uint4 &w, int i) {
     return i == 0 ? w.x : i == 1 ? w.y : i == 2 ? w.z : w.w;
 }
 
-// One element of the staged verifier part.
+// The keys of one vector of logits: 16 bytes for bf16, 8 for fp32.
+template <int DT> struct KeyVec;
+template <> struct KeyVec<DT_BF16> {
+    uint4 w;
+    __device__ __forceinline__ void load(const uint16_t *keys, size_t q) {
+        w = reinterpret_cast<const uint4 *>(keys)[q];
+    }
+    __device__ __forceinline__ uint32_t get(int e) const { return (xword(w, e >> 1) >> ((e & 1) * 16)) & 0xffffu; }
+};
+template <> struct KeyVec<DT_F32> {
+    uint2 w;
+    __device__ __forceinline__ void load(const uint16_t *keys, size_t q) {
+        w = reinterpret_cast<const uint2 *>(keys)[q];
+    }
+    __device__ __forceinline__ uint32_t get(int e) const {
+        return (((e >> 1) ? w.y : w.x) >> ((e & 1) * 16)) & 0xffffu;
+    }
+};
+
+// The staged verifier value at LDS byte address `addr`.
 template <int DT>
-__device__ __forceinline__ float lds_elem(const uint4 *part, int i) {
+__device__ __forceinline__ float lds_at(const uint4 *lds, uint32_t addr) {
+    const char *p = reinterpret_cast<const char *>(lds) + addr;
     if (DT == DT_BF16)
-        return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(part)[i] << 16);
-    return reinterpret_cast<const float *>(part)[i];
+        return __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t *>(p) << 16);
+    return *reinterpret_cast<const float *>(p);
 }
 
 constexpr int kXlWaves = kXlThreads / 64;
+constexpr int kXlUnroll = 4; // vectors of the segment per thread in flight
 
 template <int DT>
 __global__ __launch_bounds__(kXlThreads) void xfam_staged_kernel(AsymParams P) {
     constexpr int EPV = Elem<DT>::kPerVec;
-    constexpr int XV = EPV / 4; // 16-byte vectors of xinv per vector of logits
-    __shared__ uint4 part[kXlLdsVecs];
+    constexpr int U = kXlUnroll;
+    // [0]: -inf (the slot of drafter tokens without a pair here), then the part
+    __shared__ uint4 part[1 + kXlLdsVecs];
     __shared__ float lds_f[kXlWaves * 2];
     __shared__ double lds_d[kXlWaves];
     __shared__ int lds_i[kXlWaves];
@@ -197,13 +230,42 @@ __global__ __launch_bounds__(kXlThreads) void xfam_staged_kernel(AsymParams P) {
     int chunk;
     if (!xfam_item(P, row, chunk))
         return;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, wave = tid >> 6;
     const int pi = chunk % P.xparts, seg = chunk / P.xparts;
     const int plo = pi * P.xpartlen;
     const int plen = min(P.xpartlen, P.Vt - plo); // a multiple of EPV
     const float NEG_INF = -__builtin_inff();
+    const bool drafter_order = ld_relaxed(P.xdup) == 0u;
+    const size_t rv = (size_t)row * P.V / EPV;
+    const uint4 *A4 = reinterpret_cast<const uint4 *>(P.a) + rv;
+    const uint4 *B4 = reinterpret_cast<const uint4 *>(P.b) + rv;
+    const uint16_t *keys = P.xkey + (size_t)pi * P.V;
+    // LDS byte address of the token with key k: element k - 1 sits at
+    // 16 + (k - 1)*size, and key 0 lands in the -inf vector
+    constexpr uint32_t kEb = Elem<DT>::kBytes, kKeyBase = 16u - kEb;
+    const int dlo = seg * P.xseglen, dhi = min(P.V, dlo + P.xseglen);
+    const int q0 = dlo / EPV, q1 = dhi > dlo ? dhi / EPV : 0;
 
-    // 1. the part into LDS: vector j*1024 + tid, straight from memory
+    // Vectors q + u*1024 of the segment; one past the end re-reads vector q,
+    // which cannot change a maximum or a minimum.
+    uint4 va[U], vb[U];
+    KeyVec<DT> vk[U];
+    auto load_round = [&](int q) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int qu = q + u * kXlThreads < q1 ? q + u * kXlThreads : q;
+            va[u] = A4[qu];
+            vb[u] = B4[qu];
+            vk[u].load(keys, qu);
+        }
+    };
+
+    // 1. the part into LDS, straight from memory, with the first round of the
+    // segment already in flight
+    if (tid == 0) {
+        const uint32_t ni = DT == DT_BF16 ? 0xff80ff80u : 0xff800000u;
+        part[0] = make_uint4(ni, ni, ni, ni);
+    }
     {
         const uint4 *src = reinterpret_cast<const uint4 *>(P.tv) + ((size_t)row * P.Vt + plo) / EPV;
         const int nvec = plen / EPV;
@@ -211,87 +273,82 @@ __global__ __launch_bounds__(kXlThreads) void xfam_staged_kernel(AsymParams P) {
         for (int j = 0; j < kXlLdsVecs / kXlThreads; ++j) {
             const int vi = j * kXlThreads + tid;
             if (vi < nvec)
-                g2lds16(src + vi, part + j * kXlThreads + wave * 64);
+                g2lds16(src + vi, part + 1 + j * kXlThreads + wave * 64);
         }
     }
+    const int qs = q0 + tid;
+    if (drafter_order && qs < q1)
+        load_round(qs);
     __syncthreads();
 
-    // 2. the pairs with v in this part
-    FusedBest fb{NEG_INF, 0x7fffffff};
-    const int dlo = seg * P.xseglen, dhi = min(P.V, dlo + P.xseglen);
-    if (ld_relaxed(P.xdup) == 0u) { // drafter order over the segment
-        const size_t rv = (size_t)row * P.V / EPV;
-        const uint4 *A4 = reinterpret_cast<const uint4 *>(P.a) + rv;
-        const uint4 *B4 = reinterpret_cast<const uint4 *>(P.b) + rv;
-        const uint4 *X4 = reinterpret_cast<const uint4 *>(P.xinv);
-        const int q1 = dhi > dlo ? dhi / EPV : 0;
-        for (int q = dlo / EPV + tid; q < q1; q += 2 * kXlThreads) {
-            // two vectors per thread in flight; the second may be past the
-            // segment and then re-reads the first
-            const int q2 = q + kXlThreads < q1 ? q + kXlThreads : q;
-            uint4 va[2], vb[2], vx[2][XV];
-            va[0] = A4[q];
-            vb[0] = B4[q];
-            va[1] = A4[q2];
-            vb[1] = B4[q2];
+    // 2. drafter order: the maximum fused score over the segment's pairs in
+    // this part and the lowest key reaching it (keys grow with v).  A token
+    // without a pair here reads the -inf slot, so its score is -inf or NaN,
+    // and its key - 1 wraps to the largest value, so it never supplies the
+    // index, not even when the maximum is -inf.
+    float fm = NEG_INF;
+    uint32_t fw = 0xffffffffu; // key - 1 of the best pair: its index in the part
+    if (drafter_order) {
+        for (int q = qs; q < q1; q += U * kXlThreads) {
+            if (q != qs)
+                load_round(q);
+            float tv[U][EPV];
 #pragma unroll
-            for (int i = 0; i < XV; ++i) {
-                vx[0][i] = X4[(size_t)q * XV + i];
-                vx[1][i] = X4[(size_t)q2 * XV + i];
-            }
-            // every lane reads t for all its elements (unpaired ones read
-            // element 0, a broadcast), then masks their scores to NaN,
-            // which never replaces the running maximum
-            float tv[2][EPV];
-            bool in[2][EPV];
+            for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
+                for (int e = 0; e < EPV; ++e)
+                    tv[u][e] = lds_at<DT>(part, vk[u].get(e) * kEb + kKeyBase);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
 #pragma unroll
                 for (int e = 0; e < EPV; ++e) {
-                    const int iv = (int)xword(vx[h][e >> 2], e & 3) - 1 - plo; // part-relative verifier id
-                    in[h][e] = (unsigned)iv < (unsigned)plen && (h == 0 || q2 != q);
-                    tv[h][e] = lds_elem<DT>(part, in[h][e] ? iv : 0);
-                }
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int e = 0; e < EPV; ++e) {
-                    const float sc = fused_score<kDeltaAMinusB>(widen<DT>(va[h], e), widen<DT>(vb[h], e), tv[h][e],
+                    const float sc = fused_score<kDeltaAMinusB>(widen<DT>(va[u], e), widen<DT>(vb[u], e), tv[u][e],
                                                                 P.beta);
-                    fused_take(fb, in[h][e] ? sc : __builtin_nanf(""), (int)xword(vx[h][e >> 2], e & 3) - 1);
+                    const uint32_t key = vk[u].get(e) - 1u;
+                    const uint32_t lower = min(fw, key);
+                    fw = sc == fm ? lower : fw;
+                    fw = sc > fm ? key : fw;
+                    fm = fmax_raw(fm, sc);
                 }
         }
     }
-    // 3. this segment's share of the part: L_t statistics (and, for a map
-    // that repeats a drafter id, the pairs in verifier order)
+    // 3. this segment's share of the part: L_t statistics (and, for a
+    // flagged map, the pairs in verifier order)
     const int slo = min(plen, seg * P.xsharelen), shi = min(plen, slo + P.xsharelen);
     OnlineLse st;
     online_init(st);
     for (int vi = slo / EPV + tid; vi < shi / EPV; vi += kXlThreads) {
-        const uint4 w = part[vi];
+        const uint4 w = part[1 + vi];
         float x[EPV];
 #pragma unroll
         for (int e = 0; e < EPV; ++e)
             x[e] = widen<DT>(w, e);
         online_group<EPV>(st, x);
     }
-    if (ld_relaxed(P.xdup) != 0u) {
+    FusedBest fb{NEG_INF, 0x7fffffff};
+    if (!drafter_order) {
         const size_t arow = (size_t)row * P.V;
         for (int i = slo + tid; i < shi; i += kXlThreads) {
             const int d = P.vmap[plo + i];
             if (d >= 0 && d < P.V) {
-                const float sc = fused_score<kDeltaAMinusB>(load_scalar<DT>(P.a, arow + d),
-                                                            load_scalar<DT>(P.b, arow + d),
-                                                            lds_elem<DT>(part, i), P.beta);
+                const float sc =
+                    fused_score<kDeltaAMinusB>(load_scalar<DT>(P.a, arow + d), load_scalar<DT>(P.b, arow + d),
+                                               lds_at<DT>(part, 16u + (uint32_t)i * Elem<DT>::kBytes), P.beta);
                 fused_take(fb, sc, plo + i);
             }
         }
+        fm = fb.s;
     }
-    (void)lane;
-    // 4. the workgroup's record
-    float mx[2] = {st.c, fb.s};
+    // 4. the workgroup's maximum, then its lowest verifier id
+    float mx[2] = {st.c, fm};
     block_max<2, true, kXlWaves>(mx, lds_f);
-    int fi = (fb.s == mx[1]) ? fb.v : 0x7fffffff;
+    int fi = 0x7fffffff;
+    if (fm == mx[1]) {
+        if (!drafter_order)
+            fi = fb.v;
+        else if (fw != 0xffffffffu)
+            fi = plo + (int)fw;
+    }
     double S[1] = {rescale_to(st, mx[0])};
     block_sum_min<1, true, kXlWaves>(S, fi, lds_d, lds_i);
     if (tid == 0) {
@@ -369,10 +426,13 @@ __global__ __launch_bounds__(kThreads) void xfam_finalize_kernel(AsymParams P) {
     if (blockIdx.x == 0 && threadIdx.x == 0)
         P.ctl[0] = 0u; // ticket counter of the row kernel, for the next call
     // the inverse alignment and its flag, for the next call
-    if (P.xparts > 0)
-        for (long long d = (long long)blockIdx.x * kThreads + threadIdx.x; d <= P.V;
-             d += (long long)gridDim.x * kThreads)
-            P.xinv[d] = 0u; // d == V is the flag word
+    if (P.xparts > 0) {
+        const long long n = (long long)xfam_key_words(P.xparts, P.V); // word n is the flag
+        uint32_t *w = reinterpret_cast<uint32_t *>(P.xkey);
+        for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i <= n;
+             i += (long long)gridDim.x * kThreads)
+            w[i] = 0u;
+    }
     if (row >= P.R)
         return;
     // drafter side: L_b (log2 units) and the JSD partials
@@ -451,7 +511,7 @@ template <int DT, int NV>
 static hipError_t launch_x(const Plan &plan, const AsymParams &p, hipStream_t s, hipEvent_t after_rows) {
     hipError_t e;
     if (p.xparts > 0) {
-        hipLaunchKernelGGL(xfam_invert_kernel, dim3((unsigned)(((long long)p.Vt + kThreads - 1) / kThreads)),
+        hipLaunchKernelGGL(xfam_invert_kernel<DT>, dim3((unsigned)(((long long)p.Vt + kThreads - 1) / kThreads)),
                            dim3(kThreads), 0, s, p);
         e = hipGetLastError();
         if (e != hipSuccess)

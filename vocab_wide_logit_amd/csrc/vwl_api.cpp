@@ -415,9 +415,9 @@ vwl_status asym_verify(const void *a, const void *b, const void *t, const int32_
 }
 
 // Cross-family workspace: the AsymSpec layout of the drafter rows, the
-// verifier records (enough for either verifier pass), then the inverse
-// alignment and its flag.
-static bool xfam_layout(int B, int K, int Vd, int Vt, vwl_dtype dt, WsLayout &L, size_t &vrec, size_t &xinv,
+// verifier records (enough for either verifier pass), then the per-part
+// inverse alignment of the staged pass and its flag.
+static bool xfam_layout(int B, int K, int Vd, int Vt, vwl_dtype dt, WsLayout &L, size_t &vrec, size_t &xkey,
                         size_t &total) {
     if (!shape_ok(B, K, Vd) || !shape_ok(B, K, Vt) || (dt != VWL_F32 && dt != VWL_BF16))
         return false;
@@ -427,17 +427,18 @@ static bool xfam_layout(int B, int K, int Vd, int Vt, vwl_dtype dt, WsLayout &L,
         return false;
     L = ws_layout(B, K + 1, Vd, elem_bytes(dt), false);
     vrec = L.total;
-    xinv = align256(vrec + (size_t)R * C * kVrecWords * 8);
-    total = align256(xinv + ((size_t)Vd + 64) * 4); // xinv[Vd], then the flag word
+    xkey = align256(vrec + (size_t)R * C * kVrecWords * 8);
+    // xkey[parts][Vd], then the flag word
+    total = align256(xkey + (xfam_key_words(xfam_parts(Vt, elem_bytes(dt)), Vd) + 1) * 4);
     return true;
 }
 
 // Geometry of the staged verifier pass, or false when the general pass runs:
 // the rows must be made of whole 16-byte vectors at 16-byte aligned
-// addresses.  Parts: the fewest that fit kXlLdsVecs vectors, of equal length
-// (a multiple of 8 tokens).  Segments: the count (up to kXfamMaxSegs) that
+// addresses.  Parts: the fewest of at most xfam_part_cap tokens, of equal
+// length (a multiple of 8 tokens).  Segments: the count (up to kXfamMaxSegs) that
 // minimises rounds of resident workgroups (one per CU) times the bytes one
-// workgroup moves (its part plus its segment's a, b and xinv).
+// workgroup moves (its part plus its segment's a, b and inverse alignment).
 static bool xfam_staged_geometry(const void *a, const void *b, const void *t, int Vd, int Vt, int dt, long long R,
                                  int cus, AsymParams &p) {
     const int eb = elem_bytes(dt);
@@ -446,7 +447,7 @@ static bool xfam_staged_geometry(const void *a, const void *b, const void *t, in
         return false;
     const int parts = xfam_parts(Vt, eb);
     const int partlen = (int)((((long long)Vt + parts - 1) / parts + 7) / 8 * 8);
-    if ((long long)partlen * eb > (long long)kXlLdsVecs * 16 || (long long)(parts - 1) * partlen >= Vt)
+    if (partlen > xfam_part_cap(eb) || (long long)(parts - 1) * partlen >= Vt)
         return false;
     int best_s = 1;
     double best_cost = 0.0;
@@ -455,7 +456,7 @@ static bool xfam_staged_geometry(const void *a, const void *b, const void *t, in
             continue;
         const long long seglen = (((long long)Vd + sg - 1) / sg + 7) / 8 * 8;
         const long long rounds = (8 * ((R + 7) / 8) * parts * sg + cus - 1) / cus;
-        const double cost = (double)rounds * ((double)partlen * eb + (double)seglen * (2.0 * eb + 4.0));
+        const double cost = (double)rounds * ((double)partlen * eb + (double)seglen * (2.0 * eb + 2.0));
         if (sg == 1 || g_xfam_segs || cost < best_cost) {
             best_cost = cost;
             best_s = sg;
@@ -472,8 +473,8 @@ static bool xfam_staged_geometry(const void *a, const void *b, const void *t, in
 
 size_t vwl_asym_xfam_workspace_bytes(int B, int K, int Vd, int Vt, vwl_dtype dt) {
     WsLayout L;
-    size_t vrec, xinv, total;
-    return xfam_layout(B, K, Vd, Vt, dt, L, vrec, xinv, total) ? total : 0;
+    size_t vrec, xkey, total;
+    return xfam_layout(B, K, Vd, Vt, dt, L, vrec, xkey, total) ? total : 0;
 }
 
 vwl_status asym_verify_xfam(const void *a, const void *b, int Vd, const void *t, int Vt, const int32_t *vmap,
@@ -493,8 +494,8 @@ vwl_status asym_verify_xfam(const void *a, const void *b, int Vd, const void *t,
     if (st != VWL_OK)
         return st;
     WsLayout L;
-    size_t vrec, xinv, total;
-    if (!xfam_layout(B, K, Vd, Vt, dt, L, vrec, xinv, total))
+    size_t vrec, xkey, total;
+    if (!xfam_layout(B, K, Vd, Vt, dt, L, vrec, xkey, total))
         return VWL_ERR_SHAPE;
     if (!aligned(vmap, 4) || (dev_err && !aligned(dev_err, 4)))
         return VWL_ERR_ALIGN;
@@ -518,8 +519,8 @@ vwl_status asym_verify_xfam(const void *a, const void *b, int Vd, const void *t,
     }
     p.vmap = vmap;
     p.vrec = reinterpret_cast<uint64_t *>(ws + vrec);
-    p.xinv = reinterpret_cast<uint32_t *>(ws + xinv);
-    p.xdup = p.xinv + Vd;
+    p.xkey = reinterpret_cast<uint16_t *>(ws + xkey);
+    p.xdup = reinterpret_cast<uint32_t *>(ws + xkey) + xfam_key_words(xfam_parts(Vt, elem_bytes(dt)), Vd);
     p.draft = draft;
     p.R = R;
     p.B = B;

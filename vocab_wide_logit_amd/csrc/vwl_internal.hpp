@@ -88,16 +88,19 @@ struct AsymParams {
     // AsymSpec across families: verifier rows on their own vocabulary Vt,
     // the alignment vmap[Vt] (paired drafter id or -1), per-(row, chunk)
     // verifier records [R][vchunks][kVrecWords].  The staged verifier pass
-    // (xparts > 0) also uses the inverse alignment xinv[Vd] (verifier id + 1
-    // of drafter token d, 0 = none) and the flag xdup (some drafter token is
-    // paired twice), both zero between calls; the verifier row in xparts
-    // parts of xpartlen tokens, the drafter row in xsegs segments of xseglen
-    // tokens, and xsharelen tokens of a part per segment for L_t.
+    // (xparts > 0) splits the verifier row into xparts parts of xpartlen
+    // tokens and the drafter row into xsegs segments of xseglen tokens, with
+    // xsharelen tokens of a part per segment for L_t.  It uses the inverse
+    // alignment per part, xkey[xparts][Vd] (16 bits): for drafter token d
+    // paired with verifier token v = p*xpartlen + i of part p, i + 1, else 0;
+    // and the flag xdup (two verifier tokens of one part share a drafter
+    // token), the 32-bit word after the keys.  Both are zero between calls.
     const void *tv;
     int Vt, vchunks;
     const int32_t *vmap;
     uint64_t *vrec;
-    uint32_t *xinv, *xdup;
+    uint16_t *xkey;
+    uint32_t *xdup;
     int xparts, xpartlen, xsegs, xseglen, xsharelen;
     // E2-SCI (a = drafter y, b = target z; `win` rows per request)
     int win;
@@ -181,12 +184,19 @@ inline int xfam_chunks(int Vt) { return (Vt + kXfamChunk - 1) / kXfamChunk; }
 // verifier row (at most 128 KiB) in LDS; at most kXfamMaxSegs drafter
 // segments per row.
 constexpr int kXlThreads = 1024;
-constexpr int kXlLdsVecs = 8192;
+constexpr int kXlLdsVecs = 8192; // a part's 16-byte vectors, after one leading vector of -inf
 constexpr int kXfamMaxSegs = 16;
-inline int xfam_parts(int Vt, int elem_bytes) {
+// Tokens per part: what LDS holds, and below 2^16 so that i + 1 is a key.
+inline int xfam_part_cap(int elem_bytes) {
     const int cap = kXlLdsVecs * 16 / elem_bytes;
+    return cap < 65528 ? cap : 65528;
+}
+inline int xfam_parts(int Vt, int elem_bytes) {
+    const int cap = xfam_part_cap(elem_bytes);
     return (Vt + cap - 1) / cap;
 }
+// 32-bit words of the keys of the staged pass; the flag word follows them.
+__host__ __device__ inline size_t xfam_key_words(int parts, int Vd) { return ((size_t)parts * Vd + 1) / 2; }
 hipError_t launch_rapid(int dt, const Plan &plan, const RapidParams &p, hipStream_t s, hipEvent_t after_rows);
 hipError_t launch_fill_zero(void *ptr, size_t bytes, hipStream_t s);
 

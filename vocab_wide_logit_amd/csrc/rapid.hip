@@ -482,63 +482,83 @@ __device__ __forceinline__ bool tail_sync(uint32_t *ctr, uint32_t target, uint32
     return *sh_flag != 0u;
 }
 
-// Sums of word `word` of the request's We partials in one fixed order, the
+// Sums of NW words of the request's We partials, each in one fixed order, the
 // same in every workgroup: lane l of wave 0 adds up the partials
 // [l*m, (l+1)*m) in index order (m = ceil(We/64)); the lane totals are then
-// added in lane order.  When w >= 0 also returns E(w) and E(w + 1), where
-// E(k) is the same fixed-order sum over the partials before chunk k, so the
-// intervals [E(k), E(k+1)) of all chunks tile [0, E(We)) exactly.
-__device__ __forceinline__ double tail_parts(const double *parts, int We, int word, double *sh_lane,
-                                             double *sh_out, int w, double *pre0, double *pre1) {
+// added in lane order.  When w >= 0 also returns E(w) and E(w + 1) of each
+// word, where E(k) is the same fixed-order sum over the partials before chunk
+// k, so the intervals [E(k), E(k+1)) of all chunks tile [0, E(We)) exactly.
+template <int NW>
+__device__ __forceinline__ void tail_parts(const double *parts, int We, const int (&word)[NW],
+                                           double *sh_lane /* 3*64*NW */, double *sh_out /* 3*NW */, int w,
+                                           double (&total)[NW], double (&pre0)[NW], double (&pre1)[NW]) {
     const int tid = threadIdx.x;
     if (tid < 64) {
         const int m = (We + 63) / 64;
         const int k0 = tid * m, k1 = min(k0 + m, We);
-        double c = 0.0, e0 = 0.0, e1 = 0.0;
+        double c[NW], e0[NW], e1[NW];
+#pragma unroll
+        for (int j = 0; j < NW; ++j)
+            c[j] = e0[j] = e1[j] = 0.0;
         for (int k = k0; k < k1; ++k) {
-            if (k == w)
-                e0 = c;
-            c += ld_f64(parts + (size_t)k * kEmitWords + word);
-            if (k == w)
-                e1 = c;
+#pragma unroll
+            for (int j = 0; j < NW; ++j) {
+                if (k == w)
+                    e0[j] = c[j];
+                c[j] += ld_f64(parts + (size_t)k * kEmitWords + word[j]);
+                if (k == w)
+                    e1[j] = c[j];
+            }
         }
-        sh_lane[tid] = c;
-        sh_lane[64 + tid] = e0;
-        sh_lane[128 + tid] = e1;
+#pragma unroll
+        for (int j = 0; j < NW; ++j) {
+            sh_lane[(3 * j) * 64 + tid] = c[j];
+            sh_lane[(3 * j + 1) * 64 + tid] = e0[j];
+            sh_lane[(3 * j + 2) * 64 + tid] = e1[j];
+        }
         __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (tid == 0) {
-            double t = 0.0, a0 = 0.0, a1 = 0.0;
+            double t[NW], a0[NW], a1[NW];
+#pragma unroll
+            for (int j = 0; j < NW; ++j)
+                t[j] = a0[j] = a1[j] = 0.0;
             const int lw = (w >= 0) ? w / m : -1;
             for (int l = 0; l < 64; ++l) {
-                if (l == lw) {
-                    a0 = t + sh_lane[64 + l];
-                    a1 = t + sh_lane[128 + l];
+#pragma unroll
+                for (int j = 0; j < NW; ++j) {
+                    if (l == lw) {
+                        a0[j] = t[j] + sh_lane[(3 * j + 1) * 64 + l];
+                        a1[j] = t[j] + sh_lane[(3 * j + 2) * 64 + l];
+                    }
+                    t[j] += sh_lane[(3 * j) * 64 + l];
                 }
-                t += sh_lane[l];
             }
-            sh_out[0] = t;
-            sh_out[1] = a0;
-            sh_out[2] = a1;
+#pragma unroll
+            for (int j = 0; j < NW; ++j) {
+                sh_out[3 * j] = t[j];
+                sh_out[3 * j + 1] = a0[j];
+                sh_out[3 * j + 2] = a1[j];
+            }
         }
     }
     __syncthreads();
-    if (pre0) {
-        *pre0 = sh_out[1];
-        *pre1 = sh_out[2];
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+        total[j] = sh_out[3 * j];
+        pre0[j] = sh_out[3 * j + 1];
+        pre1[j] = sh_out[3 * j + 2];
     }
-    const double total = sh_out[0];
     __syncthreads();
-    return total;
 }
 
 template <int DT, int EPT>
 __global__ __launch_bounds__(kThreads) void rapid_tail_kernel(RapidParams P) {
     __shared__ double lds_d[kWaves * 2];
     __shared__ int lds_i[kWaves];
-    __shared__ double sh_lane[192];
-    __shared__ double sh_out[4];
+    __shared__ double sh_lane[384];
+    __shared__ double sh_out[6];
     __shared__ double sh_st[4];
-    __shared__ double sh_scan[kThreads];
+    __shared__ double sh_scan[kWaves];
     __shared__ uint32_t sh_u[2];
     const int tid = threadIdx.x;
     const int We = P.We;
@@ -589,7 +609,17 @@ __global__ __launch_bounds__(kThreads) void rapid_tail_kernel(RapidParams P) {
     uint32_t prot = 0; // tail-protected elements (bit e)
 
     // ---- phase 1: p', q' and the refined normalisers ----
+    // z and y at the augmented argmax (for Mhat), fetched early by thread 0
+    int hidx = -1;
+    double zxh = 0.0, yxh = 0.0;
     if (ok) {
+        if (tid == 0) {
+            hidx = (int)ld_f64(rs + 4);
+            if (resid && hidx >= 0 && hidx < P.V) {
+                zxh = (double)load_scalar<DT>(P.z, row_off + hidx) * invT;
+                yxh = (double)load_scalar<DT>(P.y, row_off + hidx) * invT;
+            }
+        }
         const double Lz = ld_f64(rs + 0), Ly = ld_f64(rs + 1);
         double s2[2] = {0.0, 0.0};
 #pragma unroll
@@ -617,17 +647,14 @@ __global__ __launch_bounds__(kThreads) void rapid_tail_kernel(RapidParams P) {
     // refined L_z, L_y (as factors on p', q') and Mhat
     double fz = 1.0, fy = 1.0, Mh = 0.0, Lz = 0.0, Ly = 0.0;
     if (ok) {
-        const double sz = tail_parts(parts, We, 3, sh_lane, sh_out, -1, nullptr, nullptr);
-        const double sy = tail_parts(parts, We, 4, sh_lane, sh_out, -1, nullptr, nullptr);
+        double szy[2], unused0[2], unused1[2];
+        tail_parts<2>(parts, We, {3, 4}, sh_lane, sh_out, -1, szy, unused0, unused1);
+        const double sz = szy[0], sy = szy[1];
         if (tid == 0) {
             const double lz = ld_f64(rs + 0) + log(sz), ly = ld_f64(rs + 1) + log(sy);
             double mh = ld_f64(rs + 2);
-            const int hidx = (int)ld_f64(rs + 4);
-            if (resid && hidx >= 0 && hidx < P.V) {
-                const double zx = (double)load_scalar<DT>(P.z, row_off + hidx) * invT;
-                const double yx = (double)load_scalar<DT>(P.y, row_off + hidx) * invT;
-                mh = zx + eta_d * (exp(yx - ly) - exp(zx - lz));
-            }
+            if (resid && hidx >= 0 && hidx < P.V)
+                mh = zxh + eta_d * (exp(yxh - ly) - exp(zxh - lz));
             sh_st[0] = lz;
             sh_st[1] = ly;
             sh_st[2] = mh;
@@ -661,8 +688,11 @@ __global__ __launch_bounds__(kThreads) void rapid_tail_kernel(RapidParams P) {
         if (tid == 0)
             st_f64(mine + 2, s1[0]);
         ok = tail_sync(bar, ++nbar * (uint32_t)We, &sh_u[0]);
-        if (ok)
-            fh = 1.0 / tail_parts(parts, We, 2, sh_lane, sh_out, -1, nullptr, nullptr);
+        if (ok) {
+            double sh1[1], unused0[1], unused1[1];
+            tail_parts<1>(parts, We, {2}, sh_lane, sh_out, -1, sh1, unused0, unused1);
+            fh = 1.0 / sh1[0];
+        }
     }
 
     // weights of element e: residual max(p - phat, p - q, 0), or p
@@ -702,12 +732,12 @@ __global__ __launch_bounds__(kThreads) void rapid_tail_kernel(RapidParams P) {
 
     // ---- phase 4: the draw ----
     if (ok) {
-        double pre0, pre1;
-        const double Sr = tail_parts(parts, We, 0, sh_lane, sh_out, w, &pre0, &pre1);
-        const bool use_r = resid && (Sr > 0.0);
-        double S = Sr;
-        if (!use_r)
-            S = tail_parts(parts, We, 1, sh_lane, sh_out, w, &pre0, &pre1);
+        // residual (word 0) and target (word 1) sums with this chunk's interval
+        double St[2], e0[2], e1[2];
+        tail_parts<2>(parts, We, {0, 1}, sh_lane, sh_out, w, St, e0, e1);
+        const bool use_r = resid && (St[0] > 0.0);
+        const double S = use_r ? St[0] : St[1];
+        const double pre0 = use_r ? e0[0] : e0[1], pre1 = use_r ? e1[0] : e1[1];
         const double u = clamp_uniform(P.u_sample[row], (w == 0 && tid == 0) ? P.dev_err : nullptr);
         const double target = u * S;
         const bool crossing_here = (pre0 <= target) && (target < pre1);
@@ -729,20 +759,27 @@ __global__ __launch_bounds__(kThreads) void rapid_tail_kernel(RapidParams P) {
                     P.emit_dist[(size_t)bi * P.V + v0 + e] = (float)(wt[e] * invS);
         }
         if (crossing_here) {
-            // exclusive scan of the per-thread sums, in thread order
-            sh_scan[tid] = tsum;
-            __syncthreads();
-            if (tid == 0) {
-                double c = pre0;
-                for (int k = 0; k < kThreads; ++k) {
-                    const double xk = sh_scan[k];
-                    sh_scan[k] = c;
-                    c += xk;
-                }
+            // exclusive scan of the per-thread sums in thread order: within
+            // each wave by lane shifts (fixed order), then the wave totals
+            const int lane = tid & 63, wave = tid >> 6;
+            double x = tsum;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const double y = __shfl_up(x, o, 64);
+                if (lane >= o)
+                    x += y;
             }
+            double excl = __shfl_up(x, 1, 64);
+            if (lane == 0)
+                excl = 0.0;
+            if (lane == 63)
+                sh_scan[wave] = x;
             __syncthreads();
+            double off = pre0;
+            for (int k = 0; k < wave; ++k)
+                off += sh_scan[k];
             int found = 0x7fffffff, last_pos = -1;
-            double c = sh_scan[tid];
+            double c = off + excl;
 #pragma unroll
             for (int e = 0; e < EPT; ++e) {
                 const int v = v0 + e;

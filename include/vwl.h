@@ -182,11 +182,11 @@ vwl_status asym_verify_variant(const void *a, const void *b, const void *t,
  * accept_len, token as asym_verify.  Outputs, dtype rules and errors as
  * asym_verify; Vt >= 1; the workspace comes from
  * vwl_asym_xfam_workspace_bytes.  With Vt = Vd and the identity alignment
- * the results equal asym_verify's.  Rows made of whole 16-byte vectors at
- * 16-byte aligned addresses (a, b, t aligned; Vd and Vt times the element
- * size multiples of 16) take a staged verifier pass that reads a, b and t
- * contiguously; any other layout takes a pass that gathers a and b through
- * vmap.  Both give the same results up to the fp64 summation order of L_t.
+ * the results equal asym_verify's.  When every row is made of whole 16-byte
+ * vectors (Vd and Vt times the element size multiples of 16) a staged
+ * verifier pass reads a, b and t contiguously; other vocabulary sizes take a
+ * pass that gathers a and b through vmap.  Both give the same results up to
+ * the fp64 summation order of L_t.
  * --------------------------------------------------------------------------- */
 size_t vwl_asym_xfam_workspace_bytes(int B, int K, int Vd, int Vt, vwl_dtype dt);
 

@@ -211,3 +211,4 @@ def test_repeated_drafter_ids_both_passes(vwl, dtype):
             check(vwl, x, vmap=vm, label="repeated ids general=%s segs=%d" % (general, segs))
             check(vwl, x, label="one-to-one general=%s segs=%d" % (general, segs))
 
+

@@ -434,8 +434,8 @@ static bool xfam_layout(int B, int K, int Vd, int Vt, vwl_dtype dt, WsLayout &L,
 }
 
 // Geometry of the staged verifier pass, or false when the general pass runs:
-// the rows must be made of whole 16-byte vectors at 16-byte aligned
-// addresses.  Parts: the fewest of at most xfam_part_cap tokens, of equal
+// the rows must be made of whole 16-byte vectors (the row pointers are
+// 16-byte aligned by the argument checks; rechecked here).  Parts: the fewest of at most xfam_part_cap tokens, of equal
 // length (a multiple of 8 tokens).  Segments: the count (up to kXfamMaxSegs) that
 // minimises rounds of resident workgroups (one per CU) times the bytes one
 // workgroup moves (its part plus its segment's a, b and inverse alignment).

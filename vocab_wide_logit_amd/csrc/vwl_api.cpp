@@ -61,9 +61,10 @@ DeviceInfo g_dev[kMaxDevices];
 std::mutex g_dev_mu;
 
 // Plan overrides for tuning sweeps (0 = automatic).
-int g_force_nv[2] = {0, 0};
-int g_force_teams[2] = {0, 0};
-int g_xfam_general = 0, g_xfam_segs = 0; // cross-family verifier pass overrides
+// Atomics, so a hook called while another thread plans a call is no data race.
+std::atomic<int> g_force_nv[2] = {0, 0};
+std::atomic<int> g_force_teams[2] = {0, 0};
+std::atomic<int> g_xfam_general{0}, g_xfam_segs{0}; // cross-family verifier pass overrides
 std::atomic<hipEvent_t> g_phase_event{nullptr};
 
 const DeviceInfo *device_info() {
@@ -115,7 +116,8 @@ bool make_plan(int mode, int dt, long long R, int V, Plan &plan, int ds = 0, int
     Plan best{};
     for (int k = 0; k < 4; ++k) {
         const int nv = kNvChoices[k];
-        if (g_force_nv[mode] && nv != g_force_nv[mode])
+        const int force_nv = g_force_nv[mode].load(std::memory_order_relaxed);
+        if (force_nv && nv != force_nv)
             continue;
         const int bpc = mode == 0 ? d->asym_bpc[dt][k][ds][gate] : d->rapid_bpc[dt][k];
         if (bpc <= 0)
@@ -128,8 +130,9 @@ bool make_plan(int mode, int dt, long long R, int V, Plan &plan, int ds = 0, int
             continue;
         if (teams > R)
             teams = R;
-        if (g_force_teams[mode] > 0 && g_force_teams[mode] < teams)
-            teams = g_force_teams[mode];
+        const int force_teams = g_force_teams[mode].load(std::memory_order_relaxed);
+        if (force_teams > 0 && force_teams < teams)
+            teams = force_teams;
         const long long rounds = (R + teams - 1) / teams;
         if (best_rounds < 0 || rounds < best_rounds || (rounds == best_rounds && nv > best.nv)) {
             best_rounds = rounds;
@@ -442,7 +445,8 @@ static bool xfam_layout(int B, int K, int Vd, int Vt, vwl_dtype dt, WsLayout &L,
 static bool xfam_staged_geometry(const void *a, const void *b, const void *t, int Vd, int Vt, int dt, long long R,
                                  int cus, AsymParams &p) {
     const int eb = elem_bytes(dt);
-    if (g_xfam_general || !aligned(a, 16) || !aligned(b, 16) || !aligned(t, 16) || ((long long)Vd * eb) % 16 ||
+    const int force_segs = g_xfam_segs.load(std::memory_order_relaxed);
+    if (g_xfam_general.load(std::memory_order_relaxed) || !aligned(a, 16) || !aligned(b, 16) || !aligned(t, 16) || ((long long)Vd * eb) % 16 ||
         ((long long)Vt * eb) % 16)
         return false;
     const int parts = xfam_parts(Vt, eb);
@@ -452,12 +456,12 @@ static bool xfam_staged_geometry(const void *a, const void *b, const void *t, in
     int best_s = 1;
     double best_cost = 0.0;
     for (int sg = 1; sg <= kXfamMaxSegs; ++sg) {
-        if (g_xfam_segs && sg != g_xfam_segs)
+        if (force_segs && sg != force_segs)
             continue;
         const long long seglen = (((long long)Vd + sg - 1) / sg + 7) / 8 * 8;
         const long long rounds = (8 * ((R + 7) / 8) * parts * sg + cus - 1) / cus;
         const double cost = (double)rounds * ((double)partlen * eb + (double)seglen * (2.0 * eb + 2.0));
-        if (sg == 1 || g_xfam_segs || cost < best_cost) {
+        if (sg == 1 || force_segs || cost < best_cost) {
             best_cost = cost;
             best_s = sg;
         }

@@ -215,7 +215,10 @@ __device__ __forceinline__ float lds_at(const uint4 *lds, uint32_t addr) {
 }
 
 constexpr int kXlWaves = kXlThreads / 64;
-constexpr int kXlUnroll = 4; // vectors of the segment per thread in flight
+// Vectors of the segment per thread per round.  One is fastest: at B = 64 a
+// call took 0.132-0.134 ms with one, 0.135, 0.137 and 0.144 ms with two,
+// three and four (the pass itself 51 us with one, 60 us with four).
+constexpr int kXlUnroll = 1;
 
 template <int DT>
 __global__ __launch_bounds__(kXlThreads) void xfam_staged_kernel(AsymParams P) {

@@ -611,17 +611,57 @@ __global__ __launch_bounds__(kThreads) void asym_finalize_kernel(AsymParams P) {
         P.ctl[0] = 0u; // ticket counter of the row kernel, for the next call
     if (row >= P.R)
         return;
+    const int Pn = P.K + 1;
+    const long long bi = row / Pn;
+    const int i = (int)(row - bi * Pn);
+    const size_t row_off = (size_t)row * (size_t)P.V;
+    // In flight together with the team sums: the draft's logits (lane 0) and
+    // the fused-maximum and JSD words of the lane's first two members.
+    int d = -1;
+    double td = 0.0, bd = 0.0;
+    if (lane == 0 && i < P.K) {
+        d = P.draft[bi * P.K + i];
+        if (d >= 0 && d < P.V) {
+            td = (double)load_scalar<DT>(P.t, row_off + d);
+            bd = (double)load_scalar<DT>(P.b, row_off + d);
+        }
+    }
     const uint64_t *rec_row = P.rec + (size_t)row * P.Wmax * kRecWords;
+    uint64_t w4[2] = {0, 0}, w5[2] = {0, 0}, w6[2] = {0, 0};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int w = lane + 64 * h;
+        if (w < P.W) {
+            const uint64_t *r = rec_row + (size_t)w * kRecWords;
+            w4[h] = ld_relaxed(r + 4);
+            w5[h] = ld_relaxed(r + 5);
+            if (GATE == kGateCda)
+                w6[h] = ld_relaxed(r + 6);
+        }
+    }
     double L2[2];
     team_lse<2>(rec_row, P.W, {1, 2}, {3, 4}, {true, false}, L2);
     const double Lb = L2[0] * kLn2d, Lt = L2[1] * kLn2d;
     float fbest = -__builtin_inff();
-    for (int w = lane; w < P.W; w += 64)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+        if (lane + 64 * h < P.W)
+            fbest = fmax_raw(fbest, unpack_hi(w4[h]));
+    for (int w = lane + 128; w < P.W; w += 64) // teams wider than 128 members
         fbest = fmax_raw(fbest, unpack_hi(ld_relaxed(rec_row + (size_t)w * kRecWords + 4)));
     fbest = wave_max(fbest);
     double jsum = 0.0;
     int fidx = 0x7fffffff;
-    for (int w = lane; w < P.W; w += 64) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        if (lane + 64 * h < P.W) {
+            if (GATE == kGateCda)
+                jsum += as_f64(w6[h]);
+            if (unpack_hi(w4[h]) == fbest)
+                fidx = min(fidx, (int)(uint32_t)w5[h]);
+        }
+    }
+    for (int w = lane + 128; w < P.W; w += 64) {
         const uint64_t *r = rec_row + (size_t)w * kRecWords;
         if (GATE == kGateCda)
             jsum += as_f64(ld_relaxed(r + 6));
@@ -641,18 +681,11 @@ __global__ __launch_bounds__(kThreads) void asym_finalize_kernel(AsymParams P) {
         P.geff[row] = P.gamma;
     }
     P.fused[row] = fidx;
-    const int Pn = P.K + 1;
-    const long long bi = row / Pn;
-    const int i = (int)(row - bi * Pn);
-    const size_t row_off = (size_t)row * (size_t)P.V;
     uint32_t acc = 0;
     if (i < P.K) {
-        const int d = P.draft[bi * P.K + i];
         if (d < 0 || d >= P.V) {
             set_dev_err(P.dev_err, 1);
         } else {
-            const double td = (double)load_scalar<DT>(P.t, row_off + d);
-            const double bd = (double)load_scalar<DT>(P.b, row_off + d);
             const double margin = (td - Lt) - (bd - Lb) - P.log_gamma + Dr;
             acc = margin > 0.0 ? 1u : 0u;
         }

@@ -438,12 +438,37 @@ __global__ __launch_bounds__(kThreads) void xfam_finalize_kernel(AsymParams P) {
     }
     if (row >= P.R)
         return;
+    const int Pn = P.K + 1;
+    const long long bi = row / Pn;
+    const int i = (int)(row - bi * Pn);
+    // the draft (a verifier id), its pair and their logits, fetched by lane 0
+    // while the records are combined
+    int d = -1, e = -1;
+    double td = 0.0, bd = 0.0;
+    if (lane == 0 && i < P.K) {
+        d = P.draft[bi * P.K + i];
+        if (d >= 0 && d < P.Vt) {
+            e = P.vmap[d];
+            td = (double)load_scalar<DT>(P.tv, (size_t)row * (size_t)P.Vt + d);
+            if (e >= 0 && e < P.V)
+                bd = (double)load_scalar<DT>(P.b, (size_t)row * (size_t)P.V + e);
+        }
+    }
     // drafter side: L_b (log2 units) and the JSD partials
     const uint64_t *rec_row = P.rec + (size_t)row * P.Wmax * kRecWords;
+    uint64_t w6[2] = {0, 0};
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+        if (lane + 64 * h < P.W)
+            w6[h] = ld_relaxed(rec_row + (size_t)(lane + 64 * h) * kRecWords + 6);
     double Lb2[1];
     team_lse<1>(rec_row, P.W, {1}, {3}, {true}, Lb2);
     double jsum = 0.0;
-    for (int w = lane; w < P.W; w += 64)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+        if (lane + 64 * h < P.W)
+            jsum += as_f64(w6[h]);
+    for (int w = lane + 128; w < P.W; w += 64) // teams wider than 128 members
         jsum += as_f64(ld_relaxed(rec_row + (size_t)w * kRecWords + 6));
     jsum = wave_sum(jsum);
     // verifier side: L_t and the fused token over the chunk records
@@ -468,19 +493,12 @@ __global__ __launch_bounds__(kThreads) void xfam_finalize_kernel(AsymParams P) {
     P.D[row] = (float)Dr;
     P.geff[row] = (float)((double)P.gamma * exp(-Dr));
     P.fused[row] = fidx;
-    const int Pn = P.K + 1;
-    const long long bi = row / Pn;
-    const int i = (int)(row - bi * Pn);
     uint32_t acc = 0;
     if (i < P.K) {
-        const int d = P.draft[bi * P.K + i];
         if (d < 0 || d >= P.Vt) {
             set_dev_err(P.dev_err, 1);
         } else {
-            const int e = P.vmap[d];
             if (e >= 0 && e < P.V) { // an unpaired draft is rejected
-                const double td = (double)load_scalar<DT>(P.tv, (size_t)row * (size_t)P.Vt + d);
-                const double bd = (double)load_scalar<DT>(P.b, (size_t)row * (size_t)P.V + e);
                 const double margin = (td - Lt) - (bd - Lb) - P.log_gamma + Dr;
                 acc = margin > 0.0 ? 1u : 0u;
             }

@@ -106,7 +106,8 @@ template int asym_blocks_per_cu_ds<kDeltaNone>(int dt, int nv, int gate);
 // v with a drafter token (string-identical tokens and paired specials) or
 // is -1.  Generation is restricted to the paired tokens.
 //
-// Staged pass (16-byte aligned rows; the usual case):
+// Staged pass (rows of whole 16-byte vectors: Vd and Vt times the element
+// size multiples of 16; the usual case):
 //   Launch 0, xfam_invert_kernel: the inverse alignment per part of the
 //     verifier row, xkey[p][d] = i + 1 for each pair (v, d) with v the i-th
 //     token of part p, with a flag when two such v share a drafter token.
@@ -121,7 +122,7 @@ template int asym_blocks_per_cu_ds<kDeltaNone>(int dt, int nv, int gate);
 //     reaching it.  Each workgroup also takes the online softmax statistics
 //     of one share of its part.  Under a flagged map the pairs are met in
 //     verifier order instead: v over the share, a and b gathered via vmap.
-// General pass (any alignment): launch 2 is xfam_verifier_kernel, one
+// General pass (any vocabulary sizes): launch 2 is xfam_verifier_kernel, one
 // 256-thread workgroup per (row, 4096-token verifier chunk), a and b gathered
 // through vmap; no launch 0.
 // Launch 3, xfam_finalize_kernel: one wave per row combines both record

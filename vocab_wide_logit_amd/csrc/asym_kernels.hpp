@@ -434,6 +434,38 @@ constexpr int asym_rows_waves() {
 // that are ahead of their own teams.  The members of a team share their CUs
 // with different workgroups for the whole launch, so without this their
 // speeds differ persistently and the team runs at its slowest member's pace.
+// AsymSpec across families, staged verifier pass: the inverse alignment per
+// part of the verifier row, built by the workgroups of the drafter's row
+// kernel before they leave (the pass that reads it is the next launch).
+// Workgroup b takes verifier tokens b*256 + tid, b*256 + tid + grid*256, ...
+// For a pair (v, d) with v the i-th token of part p, the 16-bit key
+// xkey[p][d] = i + 1 is set with an atomic OR on its 32-bit word; a key that
+// was already set means two verifier tokens of one part share drafter token
+// d, which sets the flag (the pass then meets the pairs in verifier order and
+// ignores the keys).  An entry of vmap outside [-1, Vd) counts as unpaired
+// and sets the map bit of dev_err.
+template <int DT>
+__device__ __forceinline__ void xfam_invert_slice(const AsymParams &P) {
+    for (long long v = (long long)blockIdx.x * kThreads + threadIdx.x; v < P.Vt;
+         v += (long long)gridDim.x * kThreads) {
+        const int d = P.vmap[v];
+        if (d < -1 || d >= P.V) {
+            set_dev_err(P.dev_err, 8);
+            continue;
+        }
+        if (d < 0)
+            continue;
+        const int pi = (int)(v / P.xpartlen);
+        const uint32_t key = (uint32_t)(v - (long long)pi * P.xpartlen) + 1u;
+        const size_t k = (size_t)pi * P.V + d;
+        const int shift = (int)(k & 1) * 16;
+        uint32_t *word = reinterpret_cast<uint32_t *>(P.xkey) + k / 2;
+        const uint32_t old = __hip_atomic_fetch_or(word, key << shift, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((old >> shift) & 0xffffu)
+            __hip_atomic_fetch_or(P.xdup, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 template <int DT, int NV, int DS, int GATE>
 __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, DS, GATE>())) void asym_rows_kernel(AsymParams P) {
     constexpr int EPV = Elem<DT>::kPerVec;
@@ -454,8 +486,12 @@ __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, DS, GATE>())) void a
     const uint32_t ticket = __builtin_amdgcn_readfirstlane(sh_u[0]);
     const int team = (int)(ticket / (uint32_t)P.W);
     const int member = (int)(ticket % (uint32_t)P.W);
-    if (team >= P.R)
+    if (team >= P.R) {
+        if constexpr (DS == kDeltaNone)
+            if (P.xparts > 0)
+                xfam_invert_slice<DT>(P);
         return;
+    }
     const uint4 *A4 = static_cast<const uint4 *>(P.a);
     const uint4 *B4 = static_cast<const uint4 *>(P.b);
     const uint4 *T4 = static_cast<const uint4 *>(P.t);
@@ -598,6 +634,9 @@ __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, DS, GATE>())) void a
             break;
         row = next;
     }
+    if constexpr (DS == kDeltaNone)
+        if (P.xparts > 0)
+            xfam_invert_slice<DT>(P);
 }
 
 // One wave per row: combine the W records, write the row outputs, and let

@@ -108,10 +108,11 @@ template int asym_blocks_per_cu_ds<kDeltaNone>(int dt, int nv, int gate);
 //
 // Staged pass (rows of whole 16-byte vectors: Vd and Vt times the element
 // size multiples of 16; the usual case):
-//   Launch 0, xfam_invert_kernel: the inverse alignment per part of the
-//     verifier row, xkey[p][d] = i + 1 for each pair (v, d) with v the i-th
-//     token of part p, with a flag when two such v share a drafter token.
-//   Launch 1: the two-tensor row kernel over a, b (L_a, L_b, the JSD partials).
+//   Launch 1: the two-tensor row kernel over a, b (L_a, L_b, the JSD
+//     partials); before leaving, its workgroups also build the inverse
+//     alignment per part of the verifier row (xfam_invert_slice: xkey[p][d] =
+//     i + 1 for each pair (v, d) with v the i-th token of part p, with a flag
+//     when two such v share a drafter token).
 //   Launch 2, xfam_staged_kernel: one 1024-thread workgroup per (row, part of
 //     the verifier row, segment of the drafter row).  The part (at most
 //     128 KiB) is copied into LDS behind one vector of -inf; the segment's a,
@@ -124,7 +125,7 @@ template int asym_blocks_per_cu_ds<kDeltaNone>(int dt, int nv, int gate);
 //     verifier order instead: v over the share, a and b gathered via vmap.
 // General pass (any vocabulary sizes): launch 2 is xfam_verifier_kernel, one
 // 256-thread workgroup per (row, 4096-token verifier chunk), a and b gathered
-// through vmap; no launch 0.
+// through vmap; no keys are built.
 // Launch 3, xfam_finalize_kernel: one wave per row combines both record
 // sets, tests the draft (a verifier id) against the drafter's compressed-view
 // probability of its pair, and scans each request; after a staged pass its
@@ -141,34 +142,6 @@ __device__ __forceinline__ bool xfam_item(const AsymParams &P, long long &row, i
     row = die + kDies * (k / P.vchunks);
     chunk = (int)(k % P.vchunks);
     return row < P.R;
-}
-
-// One thread per verifier token: its entry of the inverse alignment of its
-// part (an entry of vmap outside [-1, Vd) counts as unpaired and sets the
-// map bit of dev_err).
-template <int DT>
-__global__ __launch_bounds__(kThreads) void xfam_invert_kernel(AsymParams P) {
-    const long long v = (long long)blockIdx.x * kThreads + threadIdx.x;
-    if (v >= P.Vt)
-        return;
-    const int d = P.vmap[v];
-    if (d < -1 || d >= P.V) {
-        set_dev_err(P.dev_err, 8);
-        return;
-    }
-    if (d < 0)
-        return;
-    // 16-bit keys set with an atomic OR on their 32-bit word: a key that was
-    // already set means a repeated drafter id (the flag; the keys are then
-    // not used)
-    const int pi = (int)(v / P.xpartlen);
-    const uint32_t key = (uint32_t)(v - (long long)pi * P.xpartlen) + 1u;
-    const size_t k = (size_t)pi * P.V + d;
-    const int shift = (int)(k & 1) * 16;
-    uint32_t *word = reinterpret_cast<uint32_t *>(P.xkey) + k / 2;
-    const uint32_t old = __hip_atomic_fetch_or(word, key << shift, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if ((old >> shift) & 0xffffu)
-        __hip_atomic_fetch_or(P.xdup, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The running fused maximum of a thread and its lowest verifier id: a score
@@ -531,16 +504,9 @@ inline long long xfam_verifier_grid(long long R, int chunks) { return 8 * ((R + 
 
 template <int DT, int NV>
 static hipError_t launch_x(const Plan &plan, const AsymParams &p, hipStream_t s, hipEvent_t after_rows) {
-    hipError_t e;
-    if (p.xparts > 0) {
-        hipLaunchKernelGGL(xfam_invert_kernel<DT>, dim3((unsigned)(((long long)p.Vt + kThreads - 1) / kThreads)),
-                           dim3(kThreads), 0, s, p);
-        e = hipGetLastError();
-        if (e != hipSuccess)
-            return e;
-    }
+    // the row kernel's workgroups also build the staged pass's keys
     hipLaunchKernelGGL((asym_rows_kernel<DT, NV, kDeltaNone, kGateCda>), dim3(plan.grid), dim3(kThreads), 0, s, p);
-    e = hipGetLastError();
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
     const unsigned vgrid = (unsigned)xfam_verifier_grid(p.R, p.vchunks);

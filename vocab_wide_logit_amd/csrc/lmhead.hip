@@ -348,17 +348,20 @@ __global__ __launch_bounds__(kThreads) void lmhead_finalize_kernel(LmheadParams 
     double L2[2];
     team_lse<2>(rec_row, P.S, {1, 2}, {3, 4}, {true, false}, L2);
     const double Lb = L2[0] * kLn2d, Lt = L2[1] * kLn2d;
+    // branch-free loops, so that unrolled iterations issue their loads together
     float fbest = -__builtin_inff();
+#pragma unroll 4
     for (int w = lane; w < P.S; w += 64)
         fbest = fmaxf(fbest, unpack_hi(rec_row[(size_t)w * kRecWords + 4]));
     fbest = wave_max(fbest);
     double jsum = 0.0;
     int fidx = 0x7fffffff;
+#pragma unroll 4
     for (int w = lane; w < P.S; w += 64) {
         const uint64_t *r = rec_row + (size_t)w * kRecWords;
         jsum += as_f64(r[6]);
-        if (unpack_hi(r[4]) == fbest)
-            fidx = min(fidx, (int)(uint32_t)r[5]);
+        const int ix = (int)(uint32_t)r[5];
+        fidx = unpack_hi(r[4]) == fbest ? min(fidx, ix) : fidx;
     }
     jsum = wave_sum(jsum);
     fidx = wave_min_int(fidx);

@@ -103,16 +103,23 @@ int team_size(int V, int dt, int nv, int lanes) {
     return (int)w;
 }
 
-// Launch plan: among the vector-per-lane choices, the one that needs the
-// fewest rounds of rows per team at full residency; ties go to the larger
-// chunk (fewer members per row).  Teams are then evened out over rounds.
+// Launch plan: among the vector-per-lane choices, the one of least cost (see
+// below) at full residency.  Teams are then evened out over rounds.
 // Every member of the grid is resident at once, so no team waits on a
 // member that cannot start.
 bool make_plan(int mode, int dt, long long R, int V, Plan &plan, int ds = 0, int gate = 0) {
     const DeviceInfo *d = device_info();
     if (!d)
         return false;
+    // Cost of an AsymSpec plan in vector-steps per member: rounds of rows per
+    // team times (the vectors a member handles per row + 4 for the per-row
+    // team work), plus W/8 for the team's exchange.  Measured on the bench
+    // shapes, fewest rounds alone chose 8 vectors where 4 are faster
+    // (two-tensor pass at B = 64, single requests).  RAPID's row kernel keeps
+    // the fewest rounds (8 vectors at its bench shape; 4 are 12% slower).
+    // Ties go to more vectors.
     long long best_rounds = -1;
+    double best_cost = 0.0;
     Plan best{};
     for (int k = 0; k < 4; ++k) {
         const int nv = kNvChoices[k];
@@ -134,8 +141,10 @@ bool make_plan(int mode, int dt, long long R, int V, Plan &plan, int ds = 0, int
         if (force_teams > 0 && force_teams < teams)
             teams = force_teams;
         const long long rounds = (R + teams - 1) / teams;
-        if (best_rounds < 0 || rounds < best_rounds || (rounds == best_rounds && nv > best.nv)) {
+        const double cost = mode == 0 ? (double)rounds * (nv + 4) + W / 8.0 : (double)rounds;
+        if (best_rounds < 0 || cost < best_cost || (cost == best_cost && nv > best.nv)) {
             best_rounds = rounds;
+            best_cost = cost;
             best.nv = nv;
             best.W = W;
             best.n_teams = (int)((R + rounds - 1) / rounds);

@@ -218,23 +218,47 @@ def oracle_rows_per_s(fn, rows):
     return rows / (time.perf_counter() - t0)
 
 
-def stream_read_gbs(nbytes=1 << 30, reps=20):
-    """Read bandwidth of a plain torch reduction over nbytes (a measured
-    streaming reference on this GPU)."""
+# Launch shapes of the streaming reference (threads, workgroups per CU,
+# 16-byte loads in flight per thread); the best of them is reported.
+STREAM_SHAPES = ((256, 2, 4), (256, 32, 8), (512, 32, 8), (512, 32, 16))
+
+
+def stream_read_gbs(nbytes, reps=20):
+    """HBM read rate of the hand-written read-only streaming kernel
+    (libvwl_bench.so, 16-byte loads) over nbytes of device memory: the best
+    median over a few launch shapes.  Returns (GB/s, shape)."""
+    import ctypes
     import torch
-    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
-    for _ in range(3):
-        x.sum()
-    torch.cuda.synchronize()
-    s, e = _events(1)[0], _events(1)[0]
-    s.record()
-    for _ in range(reps):
-        x.sum()
-    e.record()
-    torch.cuda.synchronize()
-    ms = s.elapsed_time(e) / reps
-    del x
-    return nbytes / (ms * 1e-3) / 1e9
+    import vocab_wide_logit_amd as vwl
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(vwl.LIB_PATH), "libvwl_bench.so"))
+    lib.vwl_bench_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").random_()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    best = (0.0, None)
+    for threads, per_cu, unroll in STREAM_SHAPES:
+        def go():
+            rc = lib.vwl_bench_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), per_cu * cus, threads, unroll,
+                                           stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError("stream reference launch failed: %d" % rc)
+        for _ in range(3):
+            go()
+        ev = _events(reps + 1)
+        for i in range(reps):
+            ev[i].record(stream)
+            go()
+        ev[reps].record(stream)
+        torch.cuda.synchronize()
+        ms = _median([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        if gbs > best[0]:
+            best = (gbs, {"threads": threads, "workgroups": per_cu * cus, "loads_in_flight": unroll,
+                          "bytes": nbytes, "median_ms": ms})
+    del buf
+    return best
 
 
 def calib_copy():
@@ -371,7 +395,7 @@ def main():
         per3, rows3 = time_rapid(vwl, r3, args.steps, args.warmup)
         ms3 = _median(per3)
         b3 = r3.algorithmic_bytes()
-        sgbs = stream_read_gbs()
+        sgbs, sshape = stream_read_gbs(bytes_per_call)
         # the ablation variants on the same inputs (bytes actually read:
         # the fixed gate with delta = t - b skips a)
         variants = {}
@@ -385,6 +409,7 @@ def main():
                 "plan": vwl.asym_plan_info(x.B, x.K, x.V, torch.bfloat16, delta, gate)}
         result["variants_" + x.name] = variants
         result["stream_read_gbs"] = sgbs
+        result["stream_read_shape"] = sshape
         result["roofline"]["frac_of_stream"] = achieved / sgbs
         result["secondary"] = {
             x2.name: {"rows_per_s": x2.B * (x2.K + 1) / (ms2 * 1e-3), "median_call_ms": ms2,

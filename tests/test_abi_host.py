@@ -47,6 +47,26 @@ def test_library_exports_every_declared_symbol(lib):
     assert set(vwl.SYMBOLS) <= exported
 
 
+def test_bench_helper_exports_its_declarations():
+    """libvwl_bench.so (the streaming reference the benchmark compares
+    against) exports what include/vwl_bench.h declares."""
+    import vocab_wide_logit_amd as vwl
+    src = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "vwl_bench.h")).read(), flags=re.S)
+    names = re.findall(r"^\s*int\s+(\w+)\s*\(", src, flags=re.M)
+    assert names == ["vwl_bench_stream_read"]
+    path = os.path.join(os.path.dirname(vwl.LIB_PATH), "libvwl_bench.so")
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(names) <= exported
+    blib = ctypes.CDLL(path)
+    f = blib.vwl_bench_stream_read
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_void_p]
+    assert f(None, 16, None, 1, 64, 4, None) == 1          # null pointers, before any launch
+    assert f(16, 16, 16, 1, 96, 4, None) == 2              # block not a multiple of 64
+    assert f(16, 16, 16, 1, 64, 5, None) == 2              # unsupported unroll
+
+
 def test_status_strings(lib):
     for code in range(8):
         s = lib.vwl_status_string(code).decode()

@@ -63,7 +63,8 @@ typedef enum {
     VWL_ERR_PARAM = 4,     /* beta, gamma, eta or T out of range */
     VWL_ERR_WORKSPACE = 5, /* workspace smaller than the query returns */
     VWL_ERR_HIP = 6,       /* a HIP runtime call or kernel launch failed */
-    VWL_ERR_ALIGN = 7      /* a pointer is not aligned as documented */
+    VWL_ERR_ALIGN = 7,     /* a pointer is not aligned as documented */
+    VWL_ERR_SCRATCH = 8    /* asym_verify_noalloc: the shape needs more than its static scratch */
 } vwl_status;
 
 typedef enum { VWL_F32 = 0, VWL_BF16 = 1 } vwl_dtype;
@@ -125,6 +126,32 @@ vwl_status asym_verify(const void *a, const void *b, const void *t,
                        float *D, float *gamma_eff, uint8_t *accept, int32_t *fused,
                        int32_t *accept_len, int32_t *token, int32_t *dev_err,
                        void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * asym_verify without a workspace argument, for callers that cannot allocate
+ * device memory or hand the library any: code being captured into a HIP
+ * graph, tight serving loops, harnesses that forbid allocation.
+ *
+ * Same inputs, outputs, results (bit for bit) and errors as asym_verify; the
+ * workspace is a static device array of VWL_NOALLOC_SCRATCH_BYTES per device,
+ * held until the process ends.  The call allocates and frees nothing.  The
+ * first call on a device looks up the array's address and zero-fills it with
+ * a fill kernel on `stream`; every completed call leaves its counters at zero
+ * again.  A shape whose vwl_asym_workspace_bytes exceeds the scratch returns
+ * VWL_ERR_SCRATCH (at V = 151936 the scratch holds about 3,300 bf16 or
+ * 1,700 fp32 rows B*(K+1); the large B = 256, K = 4 bf16 batch needs 6.3 MB).
+ * All calls on one device share its scratch: two calls that may overlap on a
+ * device (different streams without ordering, or different host threads)
+ * race, and their results are undefined.  Order them.
+ * --------------------------------------------------------------------------- */
+#define VWL_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+vwl_status asym_verify_noalloc(const void *a, const void *b, const void *t,
+                               const int32_t *draft,
+                               int B, int K, int V, vwl_dtype dt, float beta, float gamma,
+                               float *D, float *gamma_eff, uint8_t *accept, int32_t *fused,
+                               int32_t *accept_len, int32_t *token, int32_t *dev_err,
+                               hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * AsymSpec variants: the mechanism ablation of the AsymSpec notes

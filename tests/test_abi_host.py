@@ -68,10 +68,23 @@ def test_bench_helper_exports_its_declarations():
 
 
 def test_status_strings(lib):
-    for code in range(8):
+    for code in range(9):
         s = lib.vwl_status_string(code).decode()
         assert s.startswith("VWL_")
     assert lib.vwl_version() >= 100
+
+
+def test_noalloc_refuses_shapes_beyond_its_scratch(lib):
+    """asym_verify_noalloc checks the shape's workspace against its 16 MiB
+    scratch before it touches any pointer or the device."""
+    lib.asym_verify_noalloc.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int] * 4 + [ctypes.c_float] * 2 + \
+        [ctypes.c_void_p] * 8
+    lib.asym_verify_noalloc.restype = ctypes.c_int
+    need = lib.vwl_asym_workspace_bytes(3400, 0, 151936, 1)
+    assert need > 16 << 20
+    assert lib.asym_verify_noalloc(None, None, None, None, 3400, 0, 151936, 1, 1.0, 0.5,
+                                   None, None, None, None, None, None, None, None) == 8
+    assert lib.vwl_asym_workspace_bytes(256, 4, 151936, 1) <= 16 << 20
 
 
 def test_workspace_sizes(lib):

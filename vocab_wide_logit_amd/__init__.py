@@ -62,7 +62,7 @@ SYMBOLS = ("vwl_status_string", "vwl_version", "vwl_workspace_reset",
            "vwl_set_plan_override", "vwl_set_xfam_override", "vwl_set_phase_event",
            "vwl_e2sci_workspace_bytes", "e2sci_verify", "vwl_e2sci_plan_info",
            "vwl_asym_xfam_workspace_bytes", "asym_verify_xfam",
-           "vwl_asym_lmhead_workspace_bytes", "asym_verify_lmhead")
+           "vwl_asym_lmhead_workspace_bytes", "asym_verify_lmhead", "asym_verify_noalloc")
 
 
 class E2sciParams(ctypes.Structure):
@@ -107,6 +107,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.vwl_rapid_workspace_bytes.restype = sz
         lib.asym_verify.argtypes = [P, P, P, P, i, i, i, i, f, f, P, P, P, P, P, P, P, P, sz, P]
         lib.asym_verify.restype = i
+        lib.asym_verify_noalloc.argtypes = [P, P, P, P, i, i, i, i, f, f, P, P, P, P, P, P, P, P]
+        lib.asym_verify_noalloc.restype = i
         lib.asym_verify_variant.argtypes = [P, P, P, P, i, i, i, i, f, f, i, i, P, P, P, P, P, P, P, P, sz, P]
         lib.asym_verify_variant.restype = i
         lib.vwl_asym_plan_info.argtypes = [i, i, i, i, i, i, ctypes.POINTER(ctypes.c_int64)]
@@ -297,6 +299,36 @@ def asym_verify(a: torch.Tensor, b: torch.Tensor, t: torch.Tensor, draft: torch.
                            _ptr(out.D), _ptr(out.gamma_eff), _ptr(out.accept) if K > 0 else None,
                            _ptr(out.fused), _ptr(out.accept_len), _ptr(out.token), _ptr(out.dev_err),
                            _ptr(ws), ws.numel(), ctypes.c_void_p(stream.cuda_stream))
+    _check(code)
+    return out
+
+
+def asym_verify_noalloc(a: torch.Tensor, b: torch.Tensor, t: torch.Tensor, draft: torch.Tensor,
+                        beta: float, gamma: float, *, out: Optional[AsymOut] = None) -> AsymOut:
+    """``asym_verify`` through the library's no-allocation entry point: the
+    workspace is the library's static per-device scratch (16 MiB), so the
+    call itself allocates nothing once ``out`` is given.  Calls that may
+    overlap on one device share that scratch and must be ordered."""
+    lib = load_library()
+    _dev_tensor(a, "a")
+    dt = _dt(a)
+    _dev_tensor(b, "b", a.dtype)
+    _dev_tensor(t, "t", a.dtype)
+    if a.dim() != 3 or b.shape != a.shape or t.shape != a.shape:
+        raise ValueError("a, b, t must share one [B, K+1, V] shape")
+    B, P, V = a.shape
+    K = P - 1
+    _dev_tensor(draft, "draft", torch.int32)
+    if tuple(draft.shape) != (B, K):
+        raise ValueError("draft must be [B, K]")
+    if out is None:
+        out = asym_out(B, K, a.device)
+    stream = torch.cuda.current_stream(a.device)
+    code = lib.asym_verify_noalloc(_ptr(a), _ptr(b), _ptr(t), _ptr(draft) if K > 0 else None,
+                                   B, K, V, dt, float(beta), float(gamma),
+                                   _ptr(out.D), _ptr(out.gamma_eff), _ptr(out.accept) if K > 0 else None,
+                                   _ptr(out.fused), _ptr(out.accept_len), _ptr(out.token), _ptr(out.dev_err),
+                                   ctypes.c_void_p(stream.cuda_stream))
     _check(code)
     return out
 

@@ -171,7 +171,46 @@ int member_chunk(int V, int dt, int W) {
     return (int)(c < 1 ? 1 : c);
 }
 
+// Scratch of asym_verify_noalloc: the AsymSpec workspace of one call, in a
+// file-scope device array instead of caller memory.  Each device holds its
+// own copy until the process ends.  The host may use its device address
+// only (from hipGetSymbolAddress, once per device); the array's name in
+// host code is a stand-in, not that address.
+constexpr size_t kScratchBytes = VWL_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+void *g_scratch_ptr[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+
 } // namespace
+
+static vwl_status asym_variant_impl(const void *a, const void *b, const void *t, const int32_t *draft,
+                                    int B, int K, int V, vwl_dtype dt, float beta, float gamma,
+                                    vwl_delta_source delta, vwl_gate gate,
+                                    float *D, float *gamma_eff, uint8_t *accept, int32_t *fused,
+                                    int32_t *accept_len, int32_t *token, int32_t *dev_err,
+                                    void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+// The current device's scratch address.  The first call on a device looks the
+// address up and zero-fills the array with a fill kernel on `stream` (the
+// workspace contract: zero before its first use; every completed call leaves
+// its counters at zero again).  No allocation.
+static vwl_status scratch_for_device(hipStream_t stream, void **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return VWL_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return VWL_ERR_HIP;
+        if (launch_fill_zero(p, kScratchBytes, stream) != hipSuccess)
+            return VWL_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return VWL_OK;
+}
 
 extern "C" {
 
@@ -185,6 +224,8 @@ const char *vwl_status_string(vwl_status s) {
     case VWL_ERR_WORKSPACE: return "VWL_ERR_WORKSPACE: workspace too small";
     case VWL_ERR_HIP: return "VWL_ERR_HIP: HIP runtime or launch failure";
     case VWL_ERR_ALIGN: return "VWL_ERR_ALIGN: a pointer is not aligned as required";
+    case VWL_ERR_SCRATCH:
+        return "VWL_ERR_SCRATCH: the shape needs more workspace than asym_verify_noalloc's 16 MiB scratch";
     }
     return "unknown vwl_status";
 }
@@ -364,6 +405,44 @@ vwl_status asym_verify_variant(const void *a, const void *b, const void *t, cons
                                float *D, float *gamma_eff, uint8_t *accept, int32_t *fused,
                                int32_t *accept_len, int32_t *token, int32_t *dev_err,
                                void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return asym_variant_impl(a, b, t, draft, B, K, V, dt, beta, gamma, delta, gate, D, gamma_eff, accept, fused,
+                             accept_len, token, dev_err, workspace, workspace_bytes, stream);
+}
+
+vwl_status asym_verify(const void *a, const void *b, const void *t, const int32_t *draft,
+                       int B, int K, int V, vwl_dtype dt, float beta, float gamma,
+                       float *D, float *gamma_eff, uint8_t *accept, int32_t *fused,
+                       int32_t *accept_len, int32_t *token, int32_t *dev_err,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return asym_verify_variant(a, b, t, draft, B, K, V, dt, beta, gamma, VWL_DELTA_A_MINUS_B, VWL_GATE_CDA, D,
+                               gamma_eff, accept, fused, accept_len, token, dev_err, workspace, workspace_bytes,
+                               stream);
+}
+
+vwl_status asym_verify_noalloc(const void *a, const void *b, const void *t, const int32_t *draft,
+                               int B, int K, int V, vwl_dtype dt, float beta, float gamma,
+                               float *D, float *gamma_eff, uint8_t *accept, int32_t *fused,
+                               int32_t *accept_len, int32_t *token, int32_t *dev_err, hipStream_t stream) {
+    const size_t need = vwl_asym_workspace_bytes(B, K, V, dt);
+    if (need > kScratchBytes)
+        return VWL_ERR_SCRATCH;
+    void *ws = nullptr;
+    const vwl_status st = scratch_for_device(stream, &ws);
+    if (st != VWL_OK)
+        return st;
+    // need == 0 (bad shape or dtype) is reported by the checks, in their order
+    return asym_variant_impl(a, b, t, draft, B, K, V, dt, beta, gamma, VWL_DELTA_A_MINUS_B, VWL_GATE_CDA, D,
+                             gamma_eff, accept, fused, accept_len, token, dev_err, ws, kScratchBytes, stream);
+}
+
+} // extern "C"
+
+static vwl_status asym_variant_impl(const void *a, const void *b, const void *t, const int32_t *draft,
+                                    int B, int K, int V, vwl_dtype dt, float beta, float gamma,
+                                    vwl_delta_source delta, vwl_gate gate,
+                                    float *D, float *gamma_eff, uint8_t *accept, int32_t *fused,
+                                    int32_t *accept_len, int32_t *token, int32_t *dev_err,
+                                    void *workspace, size_t workspace_bytes, hipStream_t stream) {
     if (delta != VWL_DELTA_A_MINUS_B && delta != VWL_DELTA_A && delta != VWL_DELTA_T_MINUS_B)
         return VWL_ERR_PARAM;
     if (gate != VWL_GATE_CDA && gate != VWL_GATE_FIXED)
@@ -416,15 +495,7 @@ vwl_status asym_verify_variant(const void *a, const void *b, const void *t, cons
                : VWL_ERR_HIP;
 }
 
-vwl_status asym_verify(const void *a, const void *b, const void *t, const int32_t *draft,
-                       int B, int K, int V, vwl_dtype dt, float beta, float gamma,
-                       float *D, float *gamma_eff, uint8_t *accept, int32_t *fused,
-                       int32_t *accept_len, int32_t *token, int32_t *dev_err,
-                       void *workspace, size_t workspace_bytes, hipStream_t stream) {
-    return asym_verify_variant(a, b, t, draft, B, K, V, dt, beta, gamma, VWL_DELTA_A_MINUS_B, VWL_GATE_CDA, D,
-                               gamma_eff, accept, fused, accept_len, token, dev_err, workspace, workspace_bytes,
-                               stream);
-}
+extern "C" {
 
 // Cross-family workspace: the AsymSpec layout of the drafter rows, the
 // verifier records (enough for either verifier pass), then the per-part

@@ -15,16 +15,19 @@
 // Launch 1, asym_rows_kernel: each logit row (one draft position of one
 // request: a_i, b_i, t_i) is split over a team of W workgroups; each
 // workgroup loads its chunk of the three rows once into registers and
-//   pass AB online softmax statistics (running max, sum of exp) of a, b, t,
-//           rescaled once per 16-byte group (fp32 within a group, fp64
-//           across groups and lanes), and the maximum of the fused score
-//           t + beta*(a - b); its lowest index is searched afterwards only
-//           by the threads that hold the workgroup maximum
-//           -> the chunk record is published
+//   pass AB softmax statistics of a, b, t: sums of 2^(x*log2e - c) against
+//           one integer reference c per thread and tensor, taken from the
+//           thread's first element (fp32 within a 16-byte group, fp64 across
+//           groups and lanes; a sum that overflows is recomputed with a
+//           reference per group), and the maximum of the fused score
+//           t + beta*(a - b) per vector slot; its lowest index is searched
+//           afterwards only by the threads that hold the workgroup maximum,
+//           in the one slot that holds it -> the chunk record is published
 //   pass C  once all W records of the row are in, the row log-sum-exps
 //           L_a, L_b (combined in one fixed order by every member) and the
 //           JSD terms of the chunk, from a and b still held in registers in
-//           their stored form; the row is read once.
+//           their stored form, one exponential per element (sqrt(p q) times
+//           a polynomial in x = ln p - ln q); the row is read once.
 // Each workgroup keeps two rows in flight: after publishing row r's record
 // it runs passes A+B of row r+1 (already streamed from HBM straight into
 // LDS) before it waits for row r's team and runs row r's pass C from a and
@@ -46,7 +49,7 @@ namespace vwl {
 //   3     references of the sums of a and b (two floats, log2 units)
 //   4     reference of the sum of t (log2 units), maximum of the fused score
 //   5     lowest index of the fused maximum (low 32 bits)
-//   6     JSD partial sum_v Mx_v * g_v over the chunk (double bits)
+//   6     the chunk's share of D, sum_v (p ln(2p/(p+q)) + q ln(2q/(p+q))) / 2 (double bits)
 
 // The delta-fusion score t + beta*delta, evaluated the same way everywhere.
 template <int DS>
@@ -105,6 +108,88 @@ __device__ __forceinline__ float jsd_term(float la2, float lb2, float x) {
     q = __fmaf_rn(q, s, kJsdQ0);
     const float g_poly = opr * (s * q);
     return M * (ax < kJsdX0 ? g_poly : g_closed);
+}
+
+// One element's share of D, (p ln(2p/(p+q)) + q ln(2q/(p+q))) / 2, from the
+// both-forms term above (any finite or -inf logits; exact fallback of the
+// polynomial path below).
+__device__ __forceinline__ float jsd_half_exact(float xa, float xb, float la_c, float lb_c, float dl) {
+    return (-0.5f * 0.69314718055994531f) *
+           jsd_term(__fmaf_rn(xa, kLog2e, -la_c), __fmaf_rn(xb, kLog2e, -lb_c), (xa - xb) - dl);
+}
+
+// The same share with one exponential: with x = ln p - ln q,
+//   (p ln(2p/(p+q)) + q ln(2q/(p+q))) / 2 = sqrt(p q) * Psi(x) / 2,
+//   Psi(x) = cosh(x/2) (x tanh(x/2) - 2 ln cosh(x/2)),
+// since (p+q)/2 = sqrt(p q) cosh(x/2).  Psi is even and analytic (nearest
+// singularities at x = +-i pi), so for |x| < kPsiX1 it is a polynomial in
+// u = (x / kPsiX1)^2: Psi(x)/2 = u * P(u), P of degree 9 fitted by
+// jsd_psi_fit.py (2.8e-7 relative in fp32).  sqrt(p q) = 2^h with h the mean
+// of the two log2-probabilities.  Elements with u > 1 or NaN (|x| >= kPsiX1,
+// -inf logits) are flagged and recomputed by jsd_half_exact.
+constexpr float kPsiX1 = 5.0f;
+constexpr float kPsiP0 = 0x1.8ffffcp+1f;
+constexpr float kPsiP1 = 0x1.77a1e6p-14f;
+constexpr float kPsiP2 = 0x1.b12480p+0f;
+constexpr float kPsiP3 = -0x1.0880a6p+1f;
+constexpr float kPsiP4 = 0x1.886c28p+1f;
+constexpr float kPsiP5 = -0x1.ff6474p+1f;
+constexpr float kPsiP6 = 0x1.035b9ep+2f;
+constexpr float kPsiP7 = -0x1.6a6f86p+1f;
+constexpr float kPsiP8 = 0x1.2e4e24p+0f;
+constexpr float kPsiP9 = -0x1.c01d9ep-3f;
+constexpr float kHalfLog2e = 0.72134752044448170f;
+
+// Row constants of pass C, from the row log-sum-exps in log2 units.
+struct JsdRow {
+    float hmid;  // (L_a + L_b) / 2, log2 units
+    float dlx;   // (L_a - L_b) ln 2 / kPsiX1
+    float la_c, lb_c, dl; // L_a, L_b (log2 units) and L_a - L_b (nats), for the exact fallback
+};
+
+__device__ __forceinline__ JsdRow jsd_row(double La2, double Lb2) {
+    JsdRow r;
+    r.hmid = (float)(0.5 * (La2 + Lb2));
+    r.dlx = (float)((La2 - Lb2) * (kLn2d / (double)kPsiX1));
+    r.la_c = (float)La2;
+    r.lb_c = (float)Lb2;
+    r.dl = (float)((La2 - Lb2) * kLn2d);
+    return r;
+}
+
+// D's share of one 16-byte vector of a and b (EPV elements), by the
+// polynomial path; elements it does not cover make the whole vector take
+// the exact path (rare: only elements with |x| >= 5 or -inf logits).
+template <int DT>
+__device__ __forceinline__ float jsd_vector(const uint4 &va, const uint4 &vb, const JsdRow &R) {
+    constexpr int EPV = Elem<DT>::kPerVec;
+    float J = 0.0f;
+    uint32_t um = 0u; // largest u, compared as bits (u >= 0; NaN and inf compare above 1.0)
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) {
+        const float xa = widen<DT>(va, e), xb = widen<DT>(vb, e);
+        const float S = __builtin_amdgcn_exp2f(__fmaf_rn(xa + xb, kHalfLog2e, -R.hmid));
+        const float xs = __fmaf_rn(xa - xb, 1.0f / kPsiX1, -R.dlx);
+        const float u = xs * xs;
+        float P = __fmaf_rn(kPsiP9, u, kPsiP8);
+        P = __fmaf_rn(P, u, kPsiP7);
+        P = __fmaf_rn(P, u, kPsiP6);
+        P = __fmaf_rn(P, u, kPsiP5);
+        P = __fmaf_rn(P, u, kPsiP4);
+        P = __fmaf_rn(P, u, kPsiP3);
+        P = __fmaf_rn(P, u, kPsiP2);
+        P = __fmaf_rn(P, u, kPsiP1);
+        P = __fmaf_rn(P, u, kPsiP0);
+        J = __fmaf_rn(S * u, P, J);
+        um = max(um, __float_as_uint(u));
+    }
+    if (um > 0x3f800000u) { // this lane: recompute the vector exactly
+        J = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e)
+            J += jsd_half_exact(widen<DT>(va, e), widen<DT>(vb, e), R.la_c, R.lb_c, R.dl);
+    }
+    return J;
 }
 
 // Row log-sum-exps, in log2 units, of N tensors from the W records of a
@@ -206,6 +291,51 @@ __device__ __forceinline__ void online_group(OnlineLse &st, const float (&x)[EPV
     st.c = c_new;
 }
 
+// Lazy variant of the same state: the reference is set once, from the
+// thread's first element, and never moved while the sums stay finite, so no
+// per-element maximum is needed.  Terms above 1 are exact in fp32 up to
+// 2^128; a sum that overflows to +inf (an element more than 88 nats above the
+// first one), or is NaN, sends the thread back to online_group, which gives
+// the same state by its own rule.  Every exponent argument is still an
+// element minus an integer, rounded once.
+__device__ __forceinline__ float lazy_ref(float x0) {
+    return __builtin_ceilf(fmaxf(x0, -1e30f) * kLog2e);
+}
+
+template <int EPV>
+__device__ __forceinline__ float lazy_group_sum(const float (&x)[EPV], float c) {
+    float e[EPV];
+#pragma unroll
+    for (int k = 0; k < EPV; ++k)
+        e[k] = __builtin_amdgcn_exp2f(__fmaf_rn(x[k], kLog2e, -c));
+    if constexpr (EPV == 8)
+        return ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+    else
+        return (e[0] + e[1]) + (e[2] + e[3]);
+}
+
+__device__ __forceinline__ bool lse_sum_finite(double s) { return s <= 1.7976931348623157e308; }
+
+// The thread's state over its vectors by online_group (the exact-reference
+// path of a thread whose lazy sum overflowed).
+template <int DT, int NV>
+__device__ __forceinline__ OnlineLse lse_by_groups(const uint4 (&r)[NV], int nv) {
+    constexpr int EPV = Elem<DT>::kPerVec;
+    OnlineLse st;
+    online_init(st);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        if ((int)threadIdx.x + j * kThreads < nv) {
+            float x[EPV];
+#pragma unroll
+            for (int e = 0; e < EPV; ++e)
+                x[e] = widen<DT>(r[j], e);
+            online_group<EPV>(st, x);
+        }
+    }
+    return st;
+}
+
 // Rescale a thread's state to the workgroup reference C (fp64, exact).
 __device__ __forceinline__ double rescale_to(const OnlineLse &st, float C) {
     return scale_pow2(st.s, st.c - C);
@@ -292,6 +422,10 @@ __device__ __forceinline__ void pair_pass_ab(const AsymParams &P, long long row,
     OnlineLse la, lb;
     online_init(la);
     online_init(lb);
+    if (tid < sp.nv) {
+        la.c = lazy_ref(widen<DT>(ra[0], 0));
+        lb.c = lazy_ref(widen<DT>(rb[0], 0));
+    }
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
         if (tid + j * kThreads < sp.nv) {
@@ -301,10 +435,14 @@ __device__ __forceinline__ void pair_pass_ab(const AsymParams &P, long long row,
                 xa[e] = widen<DT>(ra[j], e);
                 xb[e] = widen<DT>(rb[j], e);
             }
-            online_group<EPV>(la, xa);
-            online_group<EPV>(lb, xb);
+            la.s += (double)lazy_group_sum<EPV>(xa, la.c);
+            lb.s += (double)lazy_group_sum<EPV>(xb, lb.c);
         }
     }
+    if (!lse_sum_finite(la.s))
+        la = lse_by_groups<DT, NV>(ra, sp.nv);
+    if (!lse_sum_finite(lb.s))
+        lb = lse_by_groups<DT, NV>(rb, sp.nv);
     if (tid < sp.nsc) {
         const float x1a[1] = {sa}, x1b[1] = {sb};
         online_group<1>(la, x1a);
@@ -333,6 +471,8 @@ __device__ __forceinline__ void asym_pass_ab(const AsymParams &P, long long row,
                                              const uint4 (&ra)[NV], const uint4 (&rb)[NV], const uint4 (&rt)[NV],
                                              float sa, float sb, float st, float *lds_f, double *lds_d, int *lds_i) {
     constexpr int EPV = Elem<DT>::kPerVec;
+    constexpr bool LSE_A = AsymUse<DS, GATE>::kLseA;
+    constexpr bool READ_A = AsymUse<DS, GATE>::kReadA;
     const int tid = threadIdx.x;
     const float NEG_INF = -__builtin_inff();
     const bool has_sc = tid < sp.nsc;
@@ -340,30 +480,47 @@ __device__ __forceinline__ void asym_pass_ab(const AsymParams &P, long long row,
     online_init(la);
     online_init(lb);
     online_init(lt);
-    float fmax_t = NEG_INF;
+    if (tid < sp.nv) {
+        if (LSE_A)
+            la.c = lazy_ref(widen<DT>(ra[0], 0));
+        lb.c = lazy_ref(widen<DT>(rb[0], 0));
+        lt.c = lazy_ref(widen<DT>(rt[0], 0));
+    }
+    float vm[NV]; // fused maximum per vector slot
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
+        vm[j] = NEG_INF;
         if (tid + j * kThreads < sp.nv) {
             float xa[EPV], xb[EPV], xt[EPV];
 #pragma unroll
             for (int e = 0; e < EPV; ++e) {
-                xa[e] = AsymUse<DS, GATE>::kReadA ? widen<DT>(ra[j], e) : 0.0f;
+                xa[e] = READ_A ? widen<DT>(ra[j], e) : 0.0f;
                 xb[e] = widen<DT>(rb[j], e);
                 xt[e] = widen<DT>(rt[j], e);
-                fmax_t = fmaxf(fmax_t, fused_score<DS>(xa[e], xb[e], xt[e], P.beta));
+                vm[j] = fmaxf(vm[j], fused_score<DS>(xa[e], xb[e], xt[e], P.beta));
             }
-            if (AsymUse<DS, GATE>::kLseA)
-                online_group<EPV>(la, xa);
-            online_group<EPV>(lb, xb);
-            online_group<EPV>(lt, xt);
+            if (LSE_A)
+                la.s += (double)lazy_group_sum<EPV>(xa, la.c);
+            lb.s += (double)lazy_group_sum<EPV>(xb, lb.c);
+            lt.s += (double)lazy_group_sum<EPV>(xt, lt.c);
         }
     }
+    if (LSE_A && !lse_sum_finite(la.s))
+        la = lse_by_groups<DT, NV>(ra, sp.nv);
+    if (!lse_sum_finite(lb.s))
+        lb = lse_by_groups<DT, NV>(rb, sp.nv);
+    if (!lse_sum_finite(lt.s))
+        lt = lse_by_groups<DT, NV>(rt, sp.nv);
+    float fmax_t = vm[0];
+#pragma unroll
+    for (int j = 1; j < NV; ++j)
+        fmax_t = fmaxf(fmax_t, vm[j]);
     float fs = NEG_INF;
     if (has_sc) {
         fs = fused_score<DS>(sa, sb, st, P.beta);
         fmax_t = fmaxf(fmax_t, fs);
         const float x1a[1] = {sa}, x1b[1] = {sb}, x1t[1] = {st};
-        if (AsymUse<DS, GATE>::kLseA)
+        if (LSE_A)
             online_group<1>(la, x1a);
         online_group<1>(lb, x1b);
         online_group<1>(lt, x1t);
@@ -373,7 +530,8 @@ __device__ __forceinline__ void asym_pass_ab(const AsymParams &P, long long row,
     block_max<4, false>(mx, lds_f);
     const float Ca = mx[0], Cb = mx[1], Ct = mx[2], Fm = mx[3];
 
-    // lowest index of the workgroup's fused maximum (only its holders search)
+    // lowest index of the workgroup's fused maximum: only its holders
+    // search, in the first vector slot whose maximum it is
     int fi = 0x7fffffff;
     if (fmax_t == Fm) {
         if (has_sc && fs == Fm)
@@ -381,15 +539,16 @@ __device__ __forceinline__ void asym_pass_ab(const AsymParams &P, long long row,
         bool found = false;
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
-            if (!found && tid + j * kThreads < sp.nv) {
+            if (!found && tid + j * kThreads < sp.nv && vm[j] == Fm) {
+                found = true;
+                int e_hit = EPV - 1;
 #pragma unroll
-                for (int e = 0; e < EPV; ++e) {
-                    const float ea = AsymUse<DS, GATE>::kReadA ? widen<DT>(ra[j], e) : 0.0f;
-                    if (!found && fused_score<DS>(ea, widen<DT>(rb[j], e), widen<DT>(rt[j], e), P.beta) == Fm) {
-                        fi = min(fi, sp.first_elem + (tid + j * kThreads) * EPV + e);
-                        found = true;
-                    }
+                for (int e = EPV - 1; e >= 0; --e) {
+                    const float ea = READ_A ? widen<DT>(ra[j], e) : 0.0f;
+                    if (fused_score<DS>(ea, widen<DT>(rb[j], e), widen<DT>(rt[j], e), P.beta) == Fm)
+                        e_hit = e;
                 }
+                fi = min(fi, sp.first_elem + (tid + j * kThreads) * EPV + e_hit);
             }
         }
     }
@@ -508,9 +667,14 @@ __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, DS, GATE>())) void a
         else
             prefetch_scalars<DT, READ_A, READ_T>(r, V, W, member, P.chunk, P.a, P.b, P.t, na, nb, nt);
     };
-    uint4 ra[NV], rb[NV], rt[NV];
-    float sa, sb, st;
-    auto take = [&]() { // the staged row: LDS -> registers
+    // Two register banks: the row whose passes A+B run next is taken into
+    // one while the pending row's a and b (waiting for their pass C) stay in
+    // the other, alternating, so no bank is ever copied.
+    uint4 ra0[NV], rb0[NV], rt0[NV], ra1[NV], rb1[NV], rt1[NV];
+    float sa0, sb0, st0, sa1, sb1, st1;
+    RowSplit<DT> sp0, sp1;
+    auto take = [&](uint4(&ra)[NV], uint4(&rb)[NV], uint4(&rt)[NV], float &sa, float &sb,
+                    float &st) { // the staged row: LDS -> registers
         __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads(); // every wave's pieces have landed
 #pragma unroll
@@ -526,52 +690,46 @@ __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, DS, GATE>())) void a
         st = nt;
         __syncthreads(); // every wave has read its vectors before the refill
     };
-
-    long long row = team;
-    RowSplit<DT> sp;
-    auto pass_ab = [&](long long r) {
+    auto pass_ab = [&](long long r, const RowSplit<DT> &sp, const uint4(&ra)[NV], const uint4(&rb)[NV],
+                       const uint4(&rt)[NV], float sa, float sb, float st) {
         if constexpr (READ_T)
             asym_pass_ab<DT, NV, DS, GATE>(P, r, member, sp, ra, rb, rt, sa, sb, st, lds_f, lds_d, lds_i);
         else
             pair_pass_ab<DT, NV>(P, r, member, sp, ra, rb, sa, sb, lds_f, lds_d);
     };
 
+    long long row = team;
     issue(row);
-    take();
+    take(ra0, rb0, rt0, sa0, sb0, st0);
     if (row + P.n_teams < P.R)
         issue(row + P.n_teams);
-    sp = row_split<DT>(row, V, W, member, P.chunk);
-    pass_ab(row);
+    sp0 = row_split<DT>(row, V, W, member, P.chunk);
+    pass_ab(row, sp0, ra0, rb0, rt0, sa0, sb0, st0);
     if constexpr (GATE == kGateFixed) {
         // no divergence: each row is one pass, with the next row streaming in
         for (long long next = row + P.n_teams; next < P.R; next += P.n_teams) {
-            take();
+            take(ra0, rb0, rt0, sa0, sb0, st0);
             if (next + P.n_teams < P.R)
                 issue(next + P.n_teams);
-            sp = row_split<DT>(next, V, W, member, P.chunk);
-            pass_ab(next);
+            sp0 = row_split<DT>(next, V, W, member, P.chunk);
+            pass_ab(next, sp0, ra0, rb0, rt0, sa0, sb0, st0);
         }
         return;
     }
-    for (;;) {
-        // the pending row's a, b (raw) and head/tail scalars
-        uint4 pa[NV], pb[NV];
-#pragma unroll
-        for (int j = 0; j < NV; ++j) {
-            pa[j] = ra[j];
-            pb[j] = rb[j];
-        }
-        const float psa = sa, psb = sb;
-        const RowSplit<DT> psp = sp;
-
+    // One step: passes A+B of the next row (into bank N), then the pending
+    // row's (bank Q) team wait, combine and pass C.  Returns false when the
+    // pending row was the team's last, or on a timeout.
+    auto step = [&](uint4(&raN)[NV], uint4(&rbN)[NV], uint4(&rtN)[NV], float &saN, float &sbN, float &stN,
+                    RowSplit<DT> &spN, const uint4(&paQ)[NV], const uint4(&pbQ)[NV], float psa, float psb,
+                    const RowSplit<DT> &psp, bool &timed_out) -> bool {
         const long long next = row + P.n_teams;
         const bool has_next = next < P.R;
         if (has_next) {
-            take();
+            take(raN, rbN, rtN, saN, sbN, stN);
             if (next + P.n_teams < P.R)
                 issue(next + P.n_teams);
-            sp = row_split<DT>(next, V, W, member, P.chunk);
-            pass_ab(next);
+            spN = row_split<DT>(next, V, W, member, P.chunk);
+            pass_ab(next, spN, raN, rbN, rtN, saN, sbN, stN);
         }
 
         // ---- the pending row: wait for its team, then pass C ----
@@ -584,7 +742,8 @@ __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, DS, GATE>())) void a
         if (seen == 0u) {
             if (tid == 0)
                 set_dev_err(P.dev_err, 4);
-            return;
+            timed_out = true;
+            return false;
         }
         // L_a on wave 0 and L_b on wave 1, side by side
         const int cw = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -600,26 +759,14 @@ __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, DS, GATE>())) void a
             __builtin_amdgcn_s_setprio(1);
         else
             __builtin_amdgcn_s_setprio(0);
-        const float la_c = (float)sh_row[0]; // row log-sum-exps, log2 units
-        const float lb_c = (float)sh_row[1];
-        // L_a - L_b in nats as an unevaluated float pair
-        const double dl = (sh_row[0] - sh_row[1]) * kLn2d;
-        const float dl_hi = (float)dl, dl_lo = (float)(dl - (double)dl_hi);
+        const JsdRow jr = jsd_row(sh_row[0], sh_row[1]); // row log-sum-exps, log2 units
         float J = 0.f;
 #pragma unroll
-        for (int j = 0; j < NV; ++j) {
-            if (tid + j * kThreads < psp.nv) {
-#pragma unroll
-                for (int e = 0; e < EPV; ++e) {
-                    const float xa = widen<DT>(pa[j], e), xb = widen<DT>(pb[j], e);
-                    J += jsd_term(__fmaf_rn(xa, kLog2e, -la_c), __fmaf_rn(xb, kLog2e, -lb_c),
-                                  ((xa - xb) - dl_hi) - dl_lo);
-                }
-            }
-        }
+        for (int j = 0; j < NV; ++j)
+            if (tid + j * kThreads < psp.nv)
+                J += jsd_vector<DT>(paQ[j], pbQ[j], jr);
         if (tid < psp.nsc)
-            J += jsd_term(__fmaf_rn(psa, kLog2e, -la_c), __fmaf_rn(psb, kLog2e, -lb_c),
-                          ((psa - psb) - dl_hi) - dl_lo);
+            J += jsd_half_exact(psa, psb, jr.la_c, jr.lb_c, jr.dl);
         double Jd[1] = {(double)J};
         __builtin_amdgcn_s_setprio(2);
         block_sum<1, false>(Jd, lds_d);
@@ -629,11 +776,20 @@ __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, DS, GATE>())) void a
             __builtin_amdgcn_s_setprio(1);
         else
             __builtin_amdgcn_s_setprio(0);
-
         if (!has_next)
-            break;
+            return false;
         row = next;
+        return true;
+    };
+    bool timed_out = false;
+    for (;;) {
+        if (!step(ra1, rb1, rt1, sa1, sb1, st1, sp1, ra0, rb0, sa0, sb0, sp0, timed_out))
+            break;
+        if (!step(ra0, rb0, rt0, sa0, sb0, st0, sp0, ra1, rb1, sa1, sb1, sp1, timed_out))
+            break;
     }
+    if (timed_out)
+        return;
     if constexpr (DS == kDeltaNone)
         if (P.xparts > 0)
             xfam_invert_slice<DT>(P);
@@ -711,7 +867,7 @@ __global__ __launch_bounds__(kThreads) void asym_finalize_kernel(AsymParams P) {
     fidx = wave_min_int(fidx);
     if (lane != 0)
         return;
-    const double Dr = GATE == kGateCda ? -0.5 * kLn2d * jsum : 0.0; // enters the test only under CDA
+    const double Dr = GATE == kGateCda ? jsum : 0.0; // enters the test only under CDA
     if (GATE == kGateCda) {
         P.D[row] = (float)Dr;
         P.geff[row] = (float)((double)P.gamma * exp(-Dr));

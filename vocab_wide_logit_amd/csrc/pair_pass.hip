@@ -34,7 +34,7 @@ __global__ __launch_bounds__(kThreads) void e2sci_finalize_kernel(AsymParams P) 
     jsum = wave_sum(jsum);
     if (lane != 0)
         return;
-    const double Dr = -0.5 * kLn2d * jsum;
+    const double Dr = jsum;
     const long long bi = row / P.win;
     // the threshold is read before this row's arrival is counted, so the
     // completing wave may overwrite it (thr_out may alias thr_in)
@@ -463,7 +463,7 @@ __global__ __launch_bounds__(kThreads) void xfam_finalize_kernel(AsymParams P) {
     if (lane != 0)
         return;
     const double Lb = Lb2[0] * kLn2d, Lt = Lt2[0] * kLn2d;
-    const double Dr = -0.5 * kLn2d * jsum;
+    const double Dr = jsum;
     P.D[row] = (float)Dr;
     P.geff[row] = (float)((double)P.gamma * exp(-Dr));
     P.fused[row] = fidx;

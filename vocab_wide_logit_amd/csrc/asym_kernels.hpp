@@ -195,11 +195,20 @@ __device__ __forceinline__ float jsd_vector(const uint4 &va, const uint4 &vb, co
 // Row log-sum-exps, in log2 units, of N tensors from the W records of a
 // row: log2 sum_w s_w 2^(c_w - C), C = max c_w, in fp64 and in one fixed
 // order (lane w handles members w, w+64, ...; butterfly sums), so every
-// caller gets the same bits.  The references are integers, so each term is
+// caller gets the same bits.  F32ACC takes the final logarithm to fp32
+// accuracy only (what the divergence pass rounds its constants to).  The references are integers, so each term is
 // an exact power-of-two rescale.  Called by one whole wave.  Tensor k has its
 // sums in word sw[k] and its reference in the low (hi[k] = false) or high
 // half of word cw[k].  Records are `stride` words apart.
-template <int N>
+// log2 of a positive double to fp32 accuracy (about 1e-7 absolute): the
+// exponent plus the fp32 logarithm of the mantissa.
+__device__ __forceinline__ double log2_f32acc(double s) {
+    int e = 0;
+    const double m = frexp(s, &e);
+    return (double)e + (double)__builtin_amdgcn_logf((float)m);
+}
+
+template <int N, bool F32ACC = false>
 __device__ __forceinline__ void team_lse(const uint64_t *rec_row, int W, const int (&sw)[N], const int (&cw)[N],
                                          const bool (&hi)[N], double (&L)[N], int stride = kRecWords) {
     const int lane = threadIdx.x & 63;
@@ -256,7 +265,7 @@ __device__ __forceinline__ void team_lse(const uint64_t *rec_row, int W, const i
     }
 #pragma unroll
     for (int k = 0; k < N; ++k)
-        L[k] = (double)C[k] + log2(wave_sum(t[k]));
+        L[k] = (double)C[k] + (F32ACC ? log2_f32acc(wave_sum(t[k])) : log2(wave_sum(t[k])));
 }
 
 // Online sum-of-exp state of one tensor over a thread's elements, fed one
@@ -410,11 +419,13 @@ __device__ __forceinline__ void prefetch_scalars(long long r, int V, int W, int 
     }
 }
 
-// Pass AB of the two-tensor (divergence only) kind: online softmax
-// statistics of a and b, reduced over the workgroup; thread 0 publishes
-// record words 0, 1 (sums) and 3 (references).
+// Exact-reference pass AB of the two-tensor (divergence only) kind, the
+// fallback of pair_pass_ab: softmax statistics of a and b against one
+// reference per thread (moved by online_group where a sum overflows),
+// reduced over the workgroup; thread 0 publishes record words 0, 1 (sums)
+// and 3 (references).
 template <int DT, int NV>
-__device__ __forceinline__ void pair_pass_ab(const AsymParams &P, long long row, int member, const RowSplit<DT> &sp,
+__device__ __forceinline__ void pair_pass_ab_exact(const AsymParams &P, long long row, int member, const RowSplit<DT> &sp,
                                              const uint4 (&ra)[NV], const uint4 (&rb)[NV], float sa, float sb,
                                              float *lds_f, double *lds_d) {
     constexpr int EPV = Elem<DT>::kPerVec;
@@ -463,11 +474,12 @@ __device__ __forceinline__ void pair_pass_ab(const AsymParams &P, long long row,
     __builtin_amdgcn_s_setprio(0);
 }
 
-// Passes A+B over one row's chunk held in registers (raw a, b, t plus the
-// head/tail scalar): online softmax statistics, the fused maximum and its
+// Exact-reference passes A+B over one row's chunk held in registers (raw
+// a, b, t plus the head/tail scalar), the fallback of asym_pass_ab: softmax
+// statistics against one reference per thread, the fused maximum and its
 // lowest index, reduced over the workgroup; thread 0 publishes the record.
 template <int DT, int NV, int DS, int GATE>
-__device__ __forceinline__ void asym_pass_ab(const AsymParams &P, long long row, int member, const RowSplit<DT> &sp,
+__device__ __forceinline__ void asym_pass_ab_exact(const AsymParams &P, long long row, int member, const RowSplit<DT> &sp,
                                              const uint4 (&ra)[NV], const uint4 (&rb)[NV], const uint4 (&rt)[NV],
                                              float sa, float sb, float st, float *lds_f, double *lds_d, int *lds_i) {
     constexpr int EPV = Elem<DT>::kPerVec;
@@ -567,6 +579,213 @@ __device__ __forceinline__ void asym_pass_ab(const AsymParams &P, long long row,
     __builtin_amdgcn_s_setprio(0);
 }
 
+// LDS of the fast row reductions.
+struct RowLds {
+    double q[3 * 64];   // quad partial sums (quad_sum_post)
+    float wmax[kWaves]; // fused maximum per wave
+    float cref[3];      // the workgroup's references of a, b, t (log2 units)
+    uint32_t flag;      // set when a thread's sum against them overflowed
+    int idx;            // lowest index of the fused maximum (LDS atomic min)
+};
+
+// The workgroup's references for the chunk just taken: by wave 0, the
+// integer ceiling of the largest first element of its lanes' first vectors,
+// per tensor (lane 63 writes them; the caller's next barrier publishes
+// them).  Every thread then sums 2^(x*log2e - c) against the same c, so the
+// workgroup needs no maximum of references and no rescaling; the element
+// that gave c contributes at least 1/2, so nothing that matters underflows,
+// and a sum that overflows (an element 88 nats above c) sends the whole
+// workgroup to the exact-reference pass.
+template <int DT, int NV, bool READ_A, bool READ_T>
+__device__ __forceinline__ void wg_refs(RowLds &L, const RowSplit<DT> &sp, const uint4 (&ra)[NV],
+                                        const uint4 (&rb)[NV], const uint4 (&rt)[NV]) {
+    const float NEG_INF = -__builtin_inff();
+    const bool v0 = (int)threadIdx.x < sp.nv;
+    float m[3] = {READ_A && v0 ? widen<DT>(ra[0], 0) : NEG_INF, v0 ? widen<DT>(rb[0], 0) : NEG_INF,
+                  READ_T && v0 ? widen<DT>(rt[0], 0) : NEG_INF};
+    wave_max_last_n<3>(m);
+    if (threadIdx.x == 63) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+            L.cref[k] = lazy_ref(m[k]);
+    }
+}
+
+// Fast pass AB of the two-tensor kind (E2-SCI, cross-family drafter rows):
+// sums of a and b against the workgroup references; lane 63 of wave 0
+// publishes record words 0, 1 and 3.
+template <int DT, int NV>
+__device__ __forceinline__ void pair_pass_ab(const AsymParams &P, long long row, int member, const RowSplit<DT> &sp,
+                                             const uint4 (&ra)[NV], const uint4 (&rb)[NV], float sa, float sb,
+                                             RowLds &L, float *lds_f, double *lds_d) {
+    constexpr int EPV = Elem<DT>::kPerVec;
+    const int tid = threadIdx.x;
+    const float ca = L.cref[0], cb = L.cref[1];
+    float ga[NV], gb[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        ga[j] = gb[j] = 0.0f;
+        if (tid + j * kThreads < sp.nv) {
+            float xa[EPV], xb[EPV];
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) {
+                xa[e] = widen<DT>(ra[j], e);
+                xb[e] = widen<DT>(rb[j], e);
+            }
+            ga[j] = lazy_group_sum<EPV>(xa, ca);
+            gb[j] = lazy_group_sum<EPV>(xb, cb);
+        }
+    }
+    double S[2] = {0.0, 0.0};
+#pragma unroll
+    for (int j = 0; j < NV; j += 2) {
+        S[0] += (double)(j + 1 < NV ? ga[j] + ga[j + 1] : ga[j]);
+        S[1] += (double)(j + 1 < NV ? gb[j] + gb[j + 1] : gb[j]);
+    }
+    if (tid < sp.nsc) {
+        S[0] += (double)__builtin_amdgcn_exp2f(__fmaf_rn(sa, kLog2e, -ca));
+        S[1] += (double)__builtin_amdgcn_exp2f(__fmaf_rn(sb, kLog2e, -cb));
+    }
+    if (!(lse_sum_finite(S[0]) && lse_sum_finite(S[1])))
+        L.flag = 1u;
+    __builtin_amdgcn_s_setprio(2); // the workgroup's serial section: reductions and publish
+    quad_sum_post<2>(S, L.q);
+    __syncthreads();
+    if (L.flag != 0u) { // rare: the exact-reference pass (uniform branch)
+        pair_pass_ab_exact<DT, NV>(P, row, member, sp, ra, rb, sa, sb, lds_f, lds_d);
+        if (tid == 63)
+            L.flag = 0u;
+        return;
+    }
+    if (tid < 64) {
+        quad_sum_finish<2>(S, L.q);
+        if (tid == 63) {
+            uint64_t *rec = P.rec + ((size_t)row * P.Wmax + member) * kRecWords;
+            st_relaxed(rec + 0, f64_bits(S[0]));
+            st_relaxed(rec + 1, f64_bits(S[1]));
+            st_relaxed(rec + 3, pack2(ca, cb));
+            publish_add_nr(P.row_ctr + (size_t)row * 16, 1u);
+        }
+    }
+    __builtin_amdgcn_s_setprio(0);
+}
+
+// Fast passes A+B over one row's chunk held in registers (raw a, b, t plus
+// the head/tail scalar): sums against the workgroup references, the fused
+// maximum per vector slot; one workgroup maximum, then the lowest index of
+// it (only its holders search, in the first slot that holds it, and merge
+// by an LDS atomic minimum); lane 63 of wave 0 publishes the record.
+template <int DT, int NV, int DS, int GATE>
+__device__ __forceinline__ void asym_pass_ab(const AsymParams &P, long long row, int member, const RowSplit<DT> &sp,
+                                             const uint4 (&ra)[NV], const uint4 (&rb)[NV], const uint4 (&rt)[NV],
+                                             float sa, float sb, float st, RowLds &L, float *lds_f, double *lds_d,
+                                             int *lds_i) {
+    constexpr int EPV = Elem<DT>::kPerVec;
+    constexpr bool LSE_A = AsymUse<DS, GATE>::kLseA;
+    constexpr bool READ_A = AsymUse<DS, GATE>::kReadA;
+    const int tid = threadIdx.x;
+    const float NEG_INF = -__builtin_inff();
+    const bool has_sc = tid < sp.nsc;
+    const float ca = L.cref[0], cb = L.cref[1], ct = L.cref[2];
+    float vm[NV], ga[NV], gb[NV], gt[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        vm[j] = NEG_INF;
+        ga[j] = gb[j] = gt[j] = 0.0f;
+        if (tid + j * kThreads < sp.nv) {
+            float xa[EPV], xb[EPV], xt[EPV];
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) {
+                xa[e] = READ_A ? widen<DT>(ra[j], e) : 0.0f;
+                xb[e] = widen<DT>(rb[j], e);
+                xt[e] = widen<DT>(rt[j], e);
+                vm[j] = fmaxf(vm[j], fused_score<DS>(xa[e], xb[e], xt[e], P.beta));
+            }
+            if (LSE_A)
+                ga[j] = lazy_group_sum<EPV>(xa, ca);
+            gb[j] = lazy_group_sum<EPV>(xb, cb);
+            gt[j] = lazy_group_sum<EPV>(xt, ct);
+        }
+    }
+    double S[3] = {0.0, 0.0, 0.0};
+#pragma unroll
+    for (int j = 0; j < NV; j += 2) {
+        if (LSE_A)
+            S[0] += (double)(j + 1 < NV ? ga[j] + ga[j + 1] : ga[j]);
+        S[1] += (double)(j + 1 < NV ? gb[j] + gb[j + 1] : gb[j]);
+        S[2] += (double)(j + 1 < NV ? gt[j] + gt[j + 1] : gt[j]);
+    }
+    float fmax_t = vm[0];
+#pragma unroll
+    for (int j = 1; j < NV; ++j)
+        fmax_t = fmaxf(fmax_t, vm[j]);
+    float fs = NEG_INF;
+    if (has_sc) {
+        fs = fused_score<DS>(sa, sb, st, P.beta);
+        fmax_t = fmaxf(fmax_t, fs);
+        if (LSE_A)
+            S[0] += (double)__builtin_amdgcn_exp2f(__fmaf_rn(sa, kLog2e, -ca));
+        S[1] += (double)__builtin_amdgcn_exp2f(__fmaf_rn(sb, kLog2e, -cb));
+        S[2] += (double)__builtin_amdgcn_exp2f(__fmaf_rn(st, kLog2e, -ct));
+    }
+    if (!(lse_sum_finite(S[0]) && lse_sum_finite(S[1]) && lse_sum_finite(S[2])))
+        L.flag = 1u;
+    __builtin_amdgcn_s_setprio(2); // the workgroup's serial section: reductions and publish
+    float fm[1] = {fmax_t};
+    wave_max_last_n<1>(fm);
+    if ((tid & 63) == 63)
+        L.wmax[tid >> 6] = fm[0];
+    quad_sum_post<3>(S, L.q);
+    __syncthreads();
+    if (L.flag != 0u) { // rare: the exact-reference pass (uniform branch)
+        asym_pass_ab_exact<DT, NV, DS, GATE>(P, row, member, sp, ra, rb, rt, sa, sb, st, lds_f, lds_d, lds_i);
+        if (tid == 63)
+            L.flag = 0u;
+        return;
+    }
+    float Fm = L.wmax[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w)
+        Fm = fmax_raw(Fm, L.wmax[w]);
+    if (fmax_t == Fm) {
+        int fi = 0x7fffffff;
+        if (has_sc && fs == Fm)
+            fi = scalar_index<DT>(sp, tid);
+        bool found = false;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            if (!found && tid + j * kThreads < sp.nv && vm[j] == Fm) {
+                found = true;
+                int e_hit = EPV - 1;
+#pragma unroll
+                for (int e = EPV - 1; e >= 0; --e) {
+                    const float ea = READ_A ? widen<DT>(ra[j], e) : 0.0f;
+                    if (fused_score<DS>(ea, widen<DT>(rb[j], e), widen<DT>(rt[j], e), P.beta) == Fm)
+                        e_hit = e;
+                }
+                fi = min(fi, sp.first_elem + (tid + j * kThreads) * EPV + e_hit);
+            }
+        }
+        __hip_atomic_fetch_min(&L.idx, fi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    if (tid < 64)
+        quad_sum_finish<3>(S, L.q);
+    __syncthreads();
+    if (tid == 63) {
+        const int fi = L.idx;
+        L.idx = 0x7fffffff;
+        uint64_t *rec = P.rec + ((size_t)row * P.Wmax + member) * kRecWords;
+        st_relaxed(rec + 0, f64_bits(S[0]));
+        st_relaxed(rec + 1, f64_bits(S[1]));
+        st_relaxed(rec + 2, f64_bits(S[2]));
+        st_relaxed(rec + 3, pack2(ca, cb));
+        st_relaxed(rec + 4, pack2(ct, Fm));
+        st_relaxed(rec + 5, (uint64_t)(uint32_t)fi);
+        publish_add_nr(P.row_ctr + (size_t)row * 16, 1u);
+    }
+    __builtin_amdgcn_s_setprio(0);
+}
+
 // Resident waves per SIMD the row kernel is built for: the CDA variants keep
 // a pending row's a and b in registers across the team wait.
 template <int NV, int DS, int GATE>
@@ -637,10 +856,15 @@ __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, DS, GATE>())) void a
     __shared__ int lds_i[kWaves];
     __shared__ double sh_row[2];
     __shared__ uint32_t sh_u[2];
+    __shared__ RowLds rl;
 
     const int tid = threadIdx.x;
     if (tid == 0)
         sh_u[0] = __hip_atomic_fetch_add(&P.ctl[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 63) {
+        rl.flag = 0u;
+        rl.idx = 0x7fffffff;
+    }
     __syncthreads();
     const uint32_t ticket = __builtin_amdgcn_readfirstlane(sh_u[0]);
     const int team = (int)(ticket / (uint32_t)P.W);
@@ -673,8 +897,10 @@ __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, DS, GATE>())) void a
     uint4 ra0[NV], rb0[NV], rt0[NV], ra1[NV], rb1[NV], rt1[NV];
     float sa0, sb0, st0, sa1, sb1, st1;
     RowSplit<DT> sp0, sp1;
-    auto take = [&](uint4(&ra)[NV], uint4(&rb)[NV], uint4(&rt)[NV], float &sa, float &sb,
-                    float &st) { // the staged row: LDS -> registers
+    // The staged row: LDS -> registers; wave 0 also sets the workgroup's
+    // references for the row (published by the closing barrier).
+    auto take = [&](uint4(&ra)[NV], uint4(&rb)[NV], uint4(&rt)[NV], float &sa, float &sb, float &st,
+                    const RowSplit<DT> &sp) {
         __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads(); // every wave's pieces have landed
 #pragma unroll
@@ -688,30 +914,32 @@ __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, DS, GATE>())) void a
         sa = na;
         sb = nb;
         st = nt;
+        if (wave0)
+            wg_refs<DT, NV, READ_A, READ_T>(rl, sp, ra, rb, rt);
         __syncthreads(); // every wave has read its vectors before the refill
     };
     auto pass_ab = [&](long long r, const RowSplit<DT> &sp, const uint4(&ra)[NV], const uint4(&rb)[NV],
                        const uint4(&rt)[NV], float sa, float sb, float st) {
         if constexpr (READ_T)
-            asym_pass_ab<DT, NV, DS, GATE>(P, r, member, sp, ra, rb, rt, sa, sb, st, lds_f, lds_d, lds_i);
+            asym_pass_ab<DT, NV, DS, GATE>(P, r, member, sp, ra, rb, rt, sa, sb, st, rl, lds_f, lds_d, lds_i);
         else
-            pair_pass_ab<DT, NV>(P, r, member, sp, ra, rb, sa, sb, lds_f, lds_d);
+            pair_pass_ab<DT, NV>(P, r, member, sp, ra, rb, sa, sb, rl, lds_f, lds_d);
     };
 
     long long row = team;
     issue(row);
-    take(ra0, rb0, rt0, sa0, sb0, st0);
+    sp0 = row_split<DT>(row, V, W, member, P.chunk);
+    take(ra0, rb0, rt0, sa0, sb0, st0, sp0);
     if (row + P.n_teams < P.R)
         issue(row + P.n_teams);
-    sp0 = row_split<DT>(row, V, W, member, P.chunk);
     pass_ab(row, sp0, ra0, rb0, rt0, sa0, sb0, st0);
     if constexpr (GATE == kGateFixed) {
         // no divergence: each row is one pass, with the next row streaming in
         for (long long next = row + P.n_teams; next < P.R; next += P.n_teams) {
-            take(ra0, rb0, rt0, sa0, sb0, st0);
+            sp0 = row_split<DT>(next, V, W, member, P.chunk);
+            take(ra0, rb0, rt0, sa0, sb0, st0, sp0);
             if (next + P.n_teams < P.R)
                 issue(next + P.n_teams);
-            sp0 = row_split<DT>(next, V, W, member, P.chunk);
             pass_ab(next, sp0, ra0, rb0, rt0, sa0, sb0, st0);
         }
         return;
@@ -725,10 +953,10 @@ __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, DS, GATE>())) void a
         const long long next = row + P.n_teams;
         const bool has_next = next < P.R;
         if (has_next) {
-            take(raN, rbN, rtN, saN, sbN, stN);
+            spN = row_split<DT>(next, V, W, member, P.chunk);
+            take(raN, rbN, rtN, saN, sbN, stN, spN);
             if (next + P.n_teams < P.R)
                 issue(next + P.n_teams);
-            spN = row_split<DT>(next, V, W, member, P.chunk);
             pass_ab(next, spN, raN, rbN, rtN, saN, sbN, stN);
         }
 
@@ -749,7 +977,7 @@ __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, DS, GATE>())) void a
         const int cw = __builtin_amdgcn_readfirstlane(tid >> 6);
         if (cw < 2) {
             double L[1];
-            team_lse<1>(rec_row, W, {cw}, {3}, {cw == 1}, L);
+            team_lse<1, true>(rec_row, W, {cw}, {3}, {cw == 1}, L);
             if ((tid & 63) == 0)
                 sh_row[cw] = L[0];
         }
@@ -769,9 +997,13 @@ __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, DS, GATE>())) void a
             J += jsd_half_exact(psa, psb, jr.la_c, jr.lb_c, jr.dl);
         double Jd[1] = {(double)J};
         __builtin_amdgcn_s_setprio(2);
-        block_sum<1, false>(Jd, lds_d);
-        if (tid == 0)
-            P.rec[((size_t)row * P.Wmax + member) * kRecWords + 6] = f64_bits(Jd[0]);
+        quad_sum_post<1>(Jd, rl.q);
+        __syncthreads();
+        if (tid < 64) {
+            quad_sum_finish<1>(Jd, rl.q);
+            if (tid == 63)
+                P.rec[((size_t)row * P.Wmax + member) * kRecWords + 6] = f64_bits(Jd[0]);
+        }
         if (straggler)
             __builtin_amdgcn_s_setprio(1);
         else

@@ -295,6 +295,34 @@ __device__ __forceinline__ void wave_sum_last_n(double (&x)[N]) {
         x[i] += dpp_d_bcast<kDppBcast31, 0xc>(x[i]);
 }
 
+// Workgroup sums whose result one lane needs (lane 63 of wave 0): two quad
+// steps in every wave, the 64 quad partials of each value through LDS, then
+// wave 0 alone folds them.  Every wave writes its partials before the
+// barrier the caller places next; `finish` (wave 0, after that barrier)
+// returns the sums in lane 63, in one fixed order.  `lds` holds 64*N doubles.
+template <int N>
+__device__ __forceinline__ void quad_sum_post(double (&x)[N], double *lds) {
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        x[i] += dpp_d<kDppXor1>(x[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        x[i] += dpp_d<kDppXor2>(x[i]);
+    if ((threadIdx.x & 3) == 0) {
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            lds[i * 64 + (threadIdx.x >> 2)] = x[i];
+    }
+}
+template <int N>
+__device__ __forceinline__ void quad_sum_finish(double (&x)[N], const double *lds) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        x[i] = lds[i * 64 + lane];
+    wave_sum_last_n<N>(x);
+}
+
 // Workgroup reductions: wave results go through LDS and every thread combines
 // the WAVES values in the same order, so all threads hold the same result.
 // With TRAIL = false the closing barrier is left out: the caller guarantees

@@ -263,3 +263,31 @@ def test_single_element_rows(vwl):
     assert np.all(np.abs(dev["D"]) <= 1e-12) and np.all(dev["fused"] == 0) and np.all(dev["accept"] == 1)
     dev, ora, rep = check(vwl, x, 1.0, 1.0, label="V=1 gamma=1")
     assert rep.excluded == 4
+
+
+def test_one_workspace_across_shapes(vwl):
+    """One caller workspace, sized for the largest shape, reused by calls of
+    three different shapes in a row (larger, smaller, larger again): every
+    call leaves the workspace zero-filled, so each result stays within the
+    parity rules."""
+    import torch
+    cases = [W.gen_asym(8, 4, 151936, "bf16", seed=W.SEED_BASE + 50),
+             W.gen_asym(4, 2, 1024, "f32", seed=W.SEED_BASE + 51),
+             W.gen_asym(3, 6, 50257, "f32", seed=W.SEED_BASE + 52)]
+    need = max(vwl.workspace_bytes("asym", x.B, x.K, x.V, torch.bfloat16 if x.dtype == "bf16" else torch.float32)
+               for x in cases)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for x in cases * 2:
+        _say("case shared-workspace %s B=%d K=%d V=%d" % (x.dtype, x.B, x.K, x.V))
+        a = vwl.to_device_logits(x.a, x.dtype)
+        b = vwl.to_device_logits(x.b, x.dtype)
+        t = vwl.to_device_logits(x.t, x.dtype)
+        d = torch.from_numpy(np.ascontiguousarray(x.draft)).cuda()
+        out = vwl.asym_verify(a, b, t, d, x.beta, x.gamma, workspace=ws)
+        torch.cuda.synchronize()
+        dev = {k: v.cpu().numpy() for k, v in out._asdict().items()}
+        ora = oracle.asym(x.a, x.b, x.t, x.draft, x.beta, x.gamma, x.dtype)
+        rep = compare_asym(dev, ora, x.K, identical=np.all(x.a == x.b, axis=2))
+        _say("  " + str(rep))
+        assert rep.ok and dev["dev_err"][0] == 0, str(rep)
+        assert int(ws.count_nonzero()) == 0, "the call left workspace bytes set"

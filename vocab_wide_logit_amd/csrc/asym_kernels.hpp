@@ -208,6 +208,122 @@ __device__ __forceinline__ double log2_f32acc(double s) {
     return (double)e + (double)__builtin_amdgcn_logf((float)m);
 }
 
+// 2^d for d <= 0 to fp32 accuracy (about 1e-7 relative): an exact power of
+// two times the fp32 exponential of the fraction.
+__device__ __forceinline__ double exp2_f32acc(double d) {
+    const double k = floor(d);
+    return ldexp((double)__builtin_amdgcn_exp2f((float)(d - k)), (int)fmax(k, -1100.0));
+}
+
+// One member's published log-sum-exp of a tensor over its chunk: the word
+// of l = c + log2(S) (log2 units; -inf for S = 0; fp32-accurate logarithm)
+// with -0.0 made +0.0 and the sign bit flipped, so every value gives a
+// nonzero word and zero means "not yet published".  Self-contained: a
+// reader that sees the word has the value, with no ordering against other
+// stores.
+__device__ __forceinline__ uint64_t lse_word(double S, float c) {
+    const double l = (S == 0.0 ? -__builtin_inf() : (double)c + log2_f32acc(S)) + 0.0;
+    return f64_bits(l) ^ 0x8000000000000000ull;
+}
+__device__ __forceinline__ double lse_of_word(uint64_t w) { return as_f64(w ^ 0x8000000000000000ull); }
+
+// Record of one (row, member) for the finalize kernel (read after the row
+// kernel ends) and, under the CDA gate, the two words pass C of the other
+// members waits for.
+__device__ __forceinline__ void publish_member(const AsymParams &P, long long row, int member, int nsums,
+                                               const double *S, uint64_t w3, uint64_t w4, int fi, bool lse_words) {
+    uint64_t *rec = P.rec + ((size_t)row * P.Wmax + member) * kRecWords;
+    for (int k = 0; k < nsums; ++k)
+        st_relaxed(rec + k, f64_bits(S[k]));
+    st_relaxed(rec + 3, w3);
+    if (nsums == 3) {
+        st_relaxed(rec + 4, w4);
+        st_relaxed(rec + 5, (uint64_t)(uint32_t)fi);
+    }
+    if (lse_words) {
+        uint64_t *lw = P.lsum + ((size_t)row * P.Wmax + member) * 2;
+        st_relaxed(lw + 0, lse_word(S[0], unpack_lo(w3)));
+        st_relaxed(lw + 1, lse_word(S[1], unpack_hi(w3)));
+    }
+}
+
+// The row's records and published words back to zero for the next call,
+// by the finalize wave of the row after it has read them (lane w clears
+// member w, the lane that read it).  Every call thus leaves its workspace
+// zero-filled, whatever shape it had, so a later call of any shape finds
+// zero where it waits for a published word.
+__device__ __forceinline__ void clear_row_exchange(const AsymParams &P, long long row) {
+    for (int w = threadIdx.x & 63; w < P.W; w += 64) {
+        uint64_t *r = P.rec + ((size_t)row * P.Wmax + w) * kRecWords;
+#pragma unroll
+        for (int k = 0; k < kRecWords; ++k)
+            st_relaxed(r + k, 0ull);
+        uint64_t *lw = P.lsum + ((size_t)row * P.Wmax + w) * 2;
+        st_relaxed(lw + 0, 0ull);
+        st_relaxed(lw + 1, 0ull);
+    }
+}
+
+// Row log-sum-exps (log2 units) of a and b from the W members' published
+// words, by one whole wave (wave 0: it issues none of the staging loads, so
+// waiting for its own loads here never waits for those): lane w takes
+// members w, w + 64, ... in order, waiting (bounded) until each block of 64
+// members' words is in, and folds them online; then M + log2 sum 2^(m - M)
+// over the lanes (fp64, fp32-accurate exponentials and logarithm, one fixed
+// order, so every caller gets the same bits).  Returns 2 when every word was
+// in at the first look, 1 after waiting, 0 when the wait bound expired.
+__device__ __forceinline__ void lse_fold(double l, double &m, double &s) {
+    const double NEG_INF = -__builtin_inf();
+    if (l > m) {
+        s = (m == NEG_INF ? 0.0 : s * exp2_f32acc(m - l)) + 1.0;
+        m = l;
+    } else if (l > NEG_INF) {
+        s += exp2_f32acc(l - m);
+    } else if (!(l == NEG_INF)) {
+        s = l; // NaN propagates
+    }
+}
+__device__ __forceinline__ double lse_total(double m, double s) {
+    const float Mf = wave_max((float)m);
+    const double M = (double)Mf;
+    const double t = (m == -__builtin_inf()) ? 0.0 : s * exp2_f32acc(m - M); // m - M < 1 (M is m rounded to fp32)
+    const double tot = wave_sum(t);
+    return (Mf == -__builtin_inff()) ? -__builtin_inf() : M + log2_f32acc(tot);
+}
+__device__ __forceinline__ uint32_t lse_poll(const uint64_t *lw, int W, double &La, double &Lb) {
+    const int lane = threadIdx.x & 63;
+    const double NEG_INF = -__builtin_inf();
+    double ma = NEG_INF, sa = 0.0, mb = NEG_INF, sb = 0.0;
+    uint32_t status = 2u;
+    uint64_t t0 = 0;
+    for (int w0 = 0; w0 < W; w0 += 64) {
+        const int w = w0 + lane;
+        uint64_t va = 0, vb = 0;
+        for (;;) {
+            if (w < W && va == 0)
+                va = ld_relaxed(lw + (size_t)w * 2);
+            if (w < W && vb == 0)
+                vb = ld_relaxed(lw + (size_t)w * 2 + 1);
+            if (__builtin_amdgcn_ballot_w64(w < W && (va == 0 || vb == 0)) == 0)
+                break;
+            if (status == 2u) {
+                status = 1u;
+                t0 = wall_clock64();
+            }
+            __builtin_amdgcn_s_sleep(1);
+            if (wall_clock64() - t0 > kWaitLimitTicks)
+                return 0u;
+        }
+        if (w < W) {
+            lse_fold(lse_of_word(va), ma, sa);
+            lse_fold(lse_of_word(vb), mb, sb);
+        }
+    }
+    La = lse_total(ma, sa);
+    Lb = lse_total(mb, sb);
+    return status;
+}
+
 template <int N, bool F32ACC = false>
 __device__ __forceinline__ void team_lse(const uint64_t *rec_row, int W, const int (&sw)[N], const int (&cw)[N],
                                          const bool (&hi)[N], double (&L)[N], int stride = kRecWords) {
@@ -358,13 +474,44 @@ struct AsymStage {
     uint4 v[NT][NV][kThreads];
 };
 
-// Direct global -> LDS load of one 16-byte vector per lane (the LDS address
-// of the wave is uniform; lane L lands at base + 16*L).
+// Direct global -> LDS load of one 16-byte vector per lane from the lane's
+// own address (the LDS address of the wave is uniform; lane L lands at
+// lds_wave_base + 16*L).  The compiler tracks these loads: it waits for them
+// before any LDS access that may alias them.
 __device__ __forceinline__ void g2lds16(const uint4 *src, uint4 *lds_wave_base) {
     __builtin_amdgcn_global_load_lds(static_cast<const void *>(src),
-                                     (__attribute__((address_space(3))) void *)(lds_wave_base),
-                                     16, 0, 0);
+                                     (__attribute__((address_space(3))) void *)(lds_wave_base), 16, 0, 0);
 }
+
+// Direct global -> LDS load of one 16-byte vector per lane: the wave reads
+// the 64 vectors at the uniform `sbase` (lane L at sbase + 16*L) into LDS
+// at the uniform `lds_wave` (lane L at lds_wave + 16*L).  Issued from
+// inline assembly, so the compiler does not treat later LDS accesses as
+// possibly aliasing it and adds no wait for it before them; the kernel
+// waits for these loads itself (vmcnt(0) and a barrier before the staged
+// row is read).  The address is an SGPR base plus the lane's byte offset,
+// with no vector arithmetic.  The compiler does not check hazards against
+// the instructions inside the assembly, so it begins with the wait states
+// the hardware requires before a vector memory instruction reads an SGPR
+// that a VALU instruction (here v_readfirstlane) may have just written (5),
+// which also covers the one after a write of M0.
+__device__ __forceinline__ const uint4 *uniform_ptr(const uint4 *p) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    return reinterpret_cast<const uint4 *>(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ void g2lds16_wave(const uint4 *sbase, const uint4 *lds_wave) {
+    const uint4 *ub = uniform_ptr(sbase);
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds_wave));
+    const uint32_t voff = (threadIdx.x & 63) * 16u;
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(ub), "{m0}"(m0) : "memory");
+}
+
+// Workgroup barrier for LDS data only: the wave's LDS operations complete,
+// then s_barrier.  Unlike __syncthreads() it does not wait for the wave's
+// global loads, so the next row's staging loads stay in flight across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Stream row r's chunk into LDS (waves 1-3: wave x+1 issues all of tensor x;
 // wave 1 idles when a is not read, wave 3 when t is not).
@@ -381,42 +528,54 @@ __device__ __forceinline__ void prefetch_bulk(AsymStage<NV, NT> &stage, long lon
         base = A4;
     else if (x == 1)
         base = B4;
-    const uint4 *src = base + s.vec0 + lane;
+    const uint4 *ub = uniform_ptr(base + s.vec0); // the per-load bases below are scalar adds
     uint4 *dst = &stage.v[x][0][0];
     if (s.nv >= NV * kThreads) { // the whole slot (uniform)
-        // uniform base per vector slot, lane offset plus an immediate per sub-block
-        const uint4 *ub = base + s.vec0;
 #pragma unroll
-        for (int j = 0; j < NV; ++j) {
-            const uint4 *jb = ub + j * kThreads;
+        for (int j = 0; j < NV; ++j)
 #pragma unroll
             for (int v = 0; v < kWaves; ++v)
-                g2lds16(jb + (lane + v * 64), dst + j * kThreads + v * 64);
-        }
+                g2lds16_wave(ub + j * kThreads + v * 64, dst + j * kThreads + v * 64);
     } else {
+        const int rem = s.nv - lane; // this lane loads the sub-blocks that start below rem
 #pragma unroll
         for (int j = 0; j < NV; ++j)
 #pragma unroll
             for (int v = 0; v < kWaves; ++v) {
-                if (v * 64 + lane + j * kThreads < s.nv)
-                    g2lds16(src + v * 64 + j * kThreads, dst + j * kThreads + v * 64);
+                if (j * kThreads + v * 64 < rem)
+                    g2lds16_wave(ub + j * kThreads + v * 64, dst + j * kThreads + v * 64);
             }
     }
 }
 
-// Head/tail scalars of row r (wave 0's first lanes), widened to fp32.
+// Head/tail scalars of row r (wave 0's first lanes), as raw bits: they are
+// widened when the row is taken, so the loads stay in flight until then.
+// Every lane of wave 0 loads (lanes past the scalars read a valid element of
+// the row and ignore it), so no merge of the loaded registers forces an early
+// wait either.
+template <int DT>
+__device__ __forceinline__ uint32_t load_raw(const void *base, size_t idx) {
+    if (DT == DT_BF16)
+        return static_cast<uint32_t>(static_cast<const uint16_t *>(base)[idx]);
+    return static_cast<const uint32_t *>(base)[idx];
+}
+template <int DT>
+__device__ __forceinline__ float widen_raw(uint32_t x) {
+    return DT == DT_BF16 ? __uint_as_float(x << 16) : __uint_as_float(x);
+}
+
 template <int DT, bool READ_A, bool READ_T>
 __device__ __forceinline__ void prefetch_scalars(long long r, int V, int W, int member, int chunk, const void *a,
-                                                 const void *b, const void *t, float &na, float &nb, float &nt) {
+                                                 const void *b, const void *t, uint32_t &na, uint32_t &nb,
+                                                 uint32_t &nt) {
     const RowSplit<DT> s = row_split<DT>(r, V, W, member, chunk);
-    if ((int)threadIdx.x < s.nsc) {
-        const size_t off = (size_t)r * (size_t)V + scalar_index<DT>(s, threadIdx.x);
-        if (READ_A)
-            na = load_scalar<DT>(a, off);
-        nb = load_scalar<DT>(b, off);
-        if (READ_T)
-            nt = load_scalar<DT>(t, off);
-    }
+    const int k = (int)threadIdx.x < s.nsc ? (int)threadIdx.x : 0;
+    const size_t off = (size_t)r * (size_t)V + (s.nsc > 0 ? (size_t)scalar_index<DT>(s, k) : 0);
+    if (READ_A)
+        na = load_raw<DT>(a, off);
+    nb = load_raw<DT>(b, off);
+    if (READ_T)
+        nt = load_raw<DT>(t, off);
 }
 
 // Exact-reference pass AB of the two-tensor (divergence only) kind, the
@@ -464,13 +623,8 @@ __device__ __forceinline__ void pair_pass_ab_exact(const AsymParams &P, long lon
     block_max<2, false>(mx, lds_f);
     double S[2] = {rescale_to(la, mx[0]), rescale_to(lb, mx[1])};
     block_sum<2, false>(S, lds_d);
-    if (tid == 0) {
-        uint64_t *rec = P.rec + ((size_t)row * P.Wmax + member) * kRecWords;
-        st_relaxed(rec + 0, f64_bits(S[0]));
-        st_relaxed(rec + 1, f64_bits(S[1]));
-        st_relaxed(rec + 3, pack2(mx[0], mx[1]));
-        publish_add_nr(P.row_ctr + (size_t)row * 16, 1u);
-    }
+    if (tid == 0)
+        publish_member(P, row, member, 2, S, pack2(mx[0], mx[1]), 0, 0, true);
     __builtin_amdgcn_s_setprio(0);
 }
 
@@ -566,17 +720,18 @@ __device__ __forceinline__ void asym_pass_ab_exact(const AsymParams &P, long lon
     }
     double S[3] = {rescale_to(la, Ca), rescale_to(lb, Cb), rescale_to(lt, Ct)};
     block_sum_min<3, false>(S, fi, lds_d, lds_i);
-    if (tid == 0) {
-        uint64_t *rec = P.rec + ((size_t)row * P.Wmax + member) * kRecWords;
-        st_relaxed(rec + 0, f64_bits(S[0]));
-        st_relaxed(rec + 1, f64_bits(S[1]));
-        st_relaxed(rec + 2, f64_bits(S[2]));
-        st_relaxed(rec + 3, pack2(Ca, Cb));
-        st_relaxed(rec + 4, pack2(Ct, Fm));
-        st_relaxed(rec + 5, (uint64_t)(uint32_t)fi);
-        publish_add_nr(P.row_ctr + (size_t)row * 16, 1u);
-    }
+    if (tid == 0)
+        publish_member(P, row, member, 3, S, pack2(Ca, Cb), pack2(Ct, Fm), fi, GATE == kGateCda);
     __builtin_amdgcn_s_setprio(0);
+}
+
+// The wave's index, computed where it is used: an LDS address held across
+// the row loop would take a register the loop needs (and be spilled to
+// scratch, whose reload waits for the staging loads in flight).
+__device__ __forceinline__ int fresh_wave() {
+    int w = (int)threadIdx.x;
+    asm volatile("" : "+v"(w));
+    return __builtin_amdgcn_readfirstlane(w >> 6);
 }
 
 // LDS of the fast row reductions.
@@ -650,7 +805,7 @@ __device__ __forceinline__ void pair_pass_ab(const AsymParams &P, long long row,
         L.flag = 1u;
     __builtin_amdgcn_s_setprio(2); // the workgroup's serial section: reductions and publish
     quad_sum_post<2>(S, L.q);
-    __syncthreads();
+    lds_barrier();
     if (L.flag != 0u) { // rare: the exact-reference pass (uniform branch)
         pair_pass_ab_exact<DT, NV>(P, row, member, sp, ra, rb, sa, sb, lds_f, lds_d);
         if (tid == 63)
@@ -659,13 +814,8 @@ __device__ __forceinline__ void pair_pass_ab(const AsymParams &P, long long row,
     }
     if (tid < 64) {
         quad_sum_finish<2>(S, L.q);
-        if (tid == 63) {
-            uint64_t *rec = P.rec + ((size_t)row * P.Wmax + member) * kRecWords;
-            st_relaxed(rec + 0, f64_bits(S[0]));
-            st_relaxed(rec + 1, f64_bits(S[1]));
-            st_relaxed(rec + 3, pack2(ca, cb));
-            publish_add_nr(P.row_ctr + (size_t)row * 16, 1u);
-        }
+        if (tid == 63)
+            publish_member(P, row, member, 2, S, pack2(ca, cb), 0, 0, true);
     }
     __builtin_amdgcn_s_setprio(0);
 }
@@ -734,9 +884,9 @@ __device__ __forceinline__ void asym_pass_ab(const AsymParams &P, long long row,
     float fm[1] = {fmax_t};
     wave_max_last_n<1>(fm);
     if ((tid & 63) == 63)
-        L.wmax[tid >> 6] = fm[0];
+        L.wmax[fresh_wave()] = fm[0];
     quad_sum_post<3>(S, L.q);
-    __syncthreads();
+    lds_barrier();
     if (L.flag != 0u) { // rare: the exact-reference pass (uniform branch)
         asym_pass_ab_exact<DT, NV, DS, GATE>(P, row, member, sp, ra, rb, rt, sa, sb, st, lds_f, lds_d, lds_i);
         if (tid == 63)
@@ -770,18 +920,11 @@ __device__ __forceinline__ void asym_pass_ab(const AsymParams &P, long long row,
     }
     if (tid < 64)
         quad_sum_finish<3>(S, L.q);
-    __syncthreads();
+    lds_barrier();
     if (tid == 63) {
         const int fi = L.idx;
         L.idx = 0x7fffffff;
-        uint64_t *rec = P.rec + ((size_t)row * P.Wmax + member) * kRecWords;
-        st_relaxed(rec + 0, f64_bits(S[0]));
-        st_relaxed(rec + 1, f64_bits(S[1]));
-        st_relaxed(rec + 2, f64_bits(S[2]));
-        st_relaxed(rec + 3, pack2(ca, cb));
-        st_relaxed(rec + 4, pack2(ct, Fm));
-        st_relaxed(rec + 5, (uint64_t)(uint32_t)fi);
-        publish_add_nr(P.row_ctr + (size_t)row * 16, 1u);
+        publish_member(P, row, member, 3, S, pack2(ca, cb), pack2(ct, Fm), fi, GATE == kGateCda);
     }
     __builtin_amdgcn_s_setprio(0);
 }
@@ -881,7 +1024,7 @@ __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, DS, GATE>())) void a
     const float NEG_INF = -__builtin_inff();
     const int V = P.V, W = P.W;
     const bool wave0 = tid < 64;
-    float na = NEG_INF, nb = NEG_INF, nt = NEG_INF;
+    uint32_t na = 0u, nb = 0u, nt = 0u; // head/tail scalars of the staged row (raw bits)
 
     // Rows of this team: team, team + n_teams, ...  Two are in flight: the
     // pending row waits for its team while the next row's passes A+B run.
@@ -911,12 +1054,12 @@ __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, DS, GATE>())) void a
             if (READ_T)
                 rt[j] = stage.v[NT - 1][j][tid];
         }
-        sa = na;
-        sb = nb;
-        st = nt;
+        sa = widen_raw<DT>(na);
+        sb = widen_raw<DT>(nb);
+        st = widen_raw<DT>(nt);
         if (wave0)
             wg_refs<DT, NV, READ_A, READ_T>(rl, sp, ra, rb, rt);
-        __syncthreads(); // every wave has read its vectors before the refill
+        lds_barrier(); // every wave has read its vectors before the refill
     };
     auto pass_ab = [&](long long r, const RowSplit<DT> &sp, const uint4(&ra)[NV], const uint4(&rb)[NV],
                        const uint4(&rt)[NV], float sa, float sb, float st) {
@@ -960,12 +1103,19 @@ __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, DS, GATE>())) void a
             pass_ab(next, spN, raN, rbN, rtN, saN, sbN, stN);
         }
 
-        // ---- the pending row: wait for its team, then pass C ----
-        const uint64_t *rec_row = P.rec + (size_t)row * P.Wmax * kRecWords;
+        // ---- the pending row: its team's log-sum-exps of a and b, waited
+        // for and combined by wave 0, then pass C ----
         __builtin_amdgcn_s_setprio(2);
-        if (tid == 0)
-            sh_u[1] = wait_at_least_seen(P.row_ctr + (size_t)row * 16, (uint32_t)W);
-        __syncthreads();
+        if (wave0) {
+            double La = 0.0, Lb = 0.0;
+            const uint32_t st = lse_poll(P.lsum + (size_t)row * P.Wmax * 2, W, La, Lb);
+            if (tid == 0) {
+                sh_row[0] = La;
+                sh_row[1] = Lb;
+                sh_u[1] = st;
+            }
+        }
+        lds_barrier();
         const uint32_t seen = __builtin_amdgcn_readfirstlane(sh_u[1]);
         if (seen == 0u) {
             if (tid == 0)
@@ -973,15 +1123,6 @@ __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, DS, GATE>())) void a
             timed_out = true;
             return false;
         }
-        // L_a on wave 0 and L_b on wave 1, side by side
-        const int cw = __builtin_amdgcn_readfirstlane(tid >> 6);
-        if (cw < 2) {
-            double L[1];
-            team_lse<1, true>(rec_row, W, {cw}, {3}, {cw == 1}, L);
-            if ((tid & 63) == 0)
-                sh_row[cw] = L[0];
-        }
-        __syncthreads();
         const bool straggler = seen == 2u; // the team was waiting for this member
         if (straggler)
             __builtin_amdgcn_s_setprio(1);
@@ -998,7 +1139,7 @@ __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, DS, GATE>())) void a
         double Jd[1] = {(double)J};
         __builtin_amdgcn_s_setprio(2);
         quad_sum_post<1>(Jd, rl.q);
-        __syncthreads();
+        lds_barrier();
         if (tid < 64) {
             quad_sum_finish<1>(Jd, rl.q);
             if (tid == 63)
@@ -1097,6 +1238,7 @@ __global__ __launch_bounds__(kThreads) void asym_finalize_kernel(AsymParams P) {
     }
     jsum = wave_sum(jsum);
     fidx = wave_min_int(fidx);
+    clear_row_exchange(P, row);
     if (lane != 0)
         return;
     const double Dr = GATE == kGateCda ? jsum : 0.0; // enters the test only under CDA
@@ -1134,6 +1276,10 @@ __global__ __launch_bounds__(kThreads) void asym_finalize_kernel(AsymParams P) {
         }
         P.acc_len[bi] = n;
         P.token[bi] = (int32_t)ld_relaxed(P.row_info + (r0 + n) * 2 + 0);
+        for (int k = 0; k <= P.K; ++k) { // per-row results back to zero for the next call
+            st_relaxed(P.row_info + (r0 + k) * 2 + 0, 0u);
+            st_relaxed(P.row_info + (r0 + k) * 2 + 1, 0u);
+        }
         st_relaxed(rq, 0u);
     }
 }

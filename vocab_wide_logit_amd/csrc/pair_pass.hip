@@ -32,6 +32,7 @@ __global__ __launch_bounds__(kThreads) void e2sci_finalize_kernel(AsymParams P) 
     for (int w = lane; w < P.W; w += 64)
         jsum += as_f64(ld_relaxed(rec_row + (size_t)w * kRecWords + 6));
     jsum = wave_sum(jsum);
+    clear_row_exchange(P, row);
     if (lane != 0)
         return;
     const double Dr = jsum;
@@ -62,6 +63,8 @@ __global__ __launch_bounds__(kThreads) void e2sci_finalize_kernel(AsymParams P) 
         T = T < P.e_Tmin ? P.e_Tmin : T;
         P.r_hat[bi] = (float)r;
         P.thr_out[bi] = (float)T;
+        for (int k = 0; k < P.win; ++k) // per-row results back to zero for the next call
+            st_relaxed(P.row_info + (r0 + k) * 2 + 1, 0u);
         st_relaxed(rq, 0u);
     }
 }
@@ -460,6 +463,13 @@ __global__ __launch_bounds__(kThreads) void xfam_finalize_kernel(AsymParams P) {
     fidx = wave_min_int(fidx);
     if (fidx == 0x7fffffff)
         fidx = -1; // no verifier token is paired
+    clear_row_exchange(P, row);
+    for (int c = lane; c < P.vchunks; c += 64) { // the verifier records too (lane c read chunk c)
+        uint64_t *r = P.vrec + ((size_t)row * P.vchunks + c) * kVrecWords;
+#pragma unroll
+        for (int k = 0; k < kVrecWords; ++k)
+            r[k] = 0ull;
+    }
     if (lane != 0)
         return;
     const double Lb = Lb2[0] * kLn2d, Lt = Lt2[0] * kLn2d;
@@ -495,6 +505,10 @@ __global__ __launch_bounds__(kThreads) void xfam_finalize_kernel(AsymParams P) {
         }
         P.acc_len[bi] = n;
         P.token[bi] = (int32_t)ld_relaxed(P.row_info + (r0 + n) * 2 + 0);
+        for (int k = 0; k <= P.K; ++k) { // per-row results back to zero for the next call
+            st_relaxed(P.row_info + (r0 + k) * 2 + 0, 0u);
+            st_relaxed(P.row_info + (r0 + k) * 2 + 1, 0u);
+        }
         st_relaxed(rq, 0u);
     }
 }

@@ -490,6 +490,7 @@ static vwl_status asym_variant_impl(const void *a, const void *b, const void *t,
     p.req_ctr = reinterpret_cast<uint32_t *>(ws + L.req_ctr);
     p.row_info = reinterpret_cast<uint32_t *>(ws + L.row_info);
     p.rec = reinterpret_cast<uint64_t *>(ws + L.rec);
+    p.lsum = reinterpret_cast<uint64_t *>(ws + L.lsum);
     return launch_asym((int)dt, (int)delta, (int)gate, plan, p, stream, g_phase_event.load()) == hipSuccess
                ? VWL_OK
                : VWL_ERR_HIP;
@@ -629,6 +630,7 @@ vwl_status asym_verify_xfam(const void *a, const void *b, int Vd, const void *t,
     p.req_ctr = reinterpret_cast<uint32_t *>(ws + L.req_ctr);
     p.row_info = reinterpret_cast<uint32_t *>(ws + L.row_info);
     p.rec = reinterpret_cast<uint64_t *>(ws + L.rec);
+    p.lsum = reinterpret_cast<uint64_t *>(ws + L.lsum);
     return launch_xfam((int)dt, plan, p, stream, g_phase_event.load()) == hipSuccess ? VWL_OK : VWL_ERR_HIP;
 }
 
@@ -804,6 +806,7 @@ vwl_status e2sci_verify(const void *y, const void *z, int B, int W, int V, vwl_d
     p.req_ctr = reinterpret_cast<uint32_t *>(ws + L.req_ctr);
     p.row_info = reinterpret_cast<uint32_t *>(ws + L.row_info);
     p.rec = reinterpret_cast<uint64_t *>(ws + L.rec);
+    p.lsum = reinterpret_cast<uint64_t *>(ws + L.lsum);
     p.win = W;
     p.thr_in = T_in;
     p.omega = omega;

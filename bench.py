@@ -94,15 +94,19 @@ def time_asym(vwl, x, steps, warmup, copies=1, delta="a-b", gate="cda"):
     return wall, per, rows
 
 
-def time_rapid(vwl, x, steps, warmup):
+def time_rapid(vwl, x, steps, warmup, copies=4):
+    """rapid_verify calls rotating `copies` input sets (four sets of the
+    B=16 workload are 722 MB, past the 256 MB last-level cache, so each call
+    reads its rows from HBM); per-call and row-kernel ms from events."""
     import torch
-    z = vwl.to_device_logits(x.z, x.dtype)
-    y = vwl.to_device_logits(x.y, x.dtype)
+    base = (vwl.to_device_logits(x.z, x.dtype), vwl.to_device_logits(x.y, x.dtype))
+    sets = [base] + [tuple(t.clone() for t in base) for _ in range(1, copies)]
     d = torch.from_numpy(x.draft).cuda()
     ua = torch.from_numpy(x.u_accept).cuda()
     us = torch.from_numpy(x.u_sample).cuda()
     out = vwl.rapid_out(x.B, x.G, x.V, "cuda")
-    for _ in range(warmup):
+    for i in range(warmup):
+        z, y = sets[i % copies]
         vwl.rapid_verify(z, y, d, ua, us, x.eta, x.T, out=out)
     stream = torch.cuda.current_stream()
     start, mid, end = _events(steps), _events(steps), _events(steps)
@@ -110,6 +114,7 @@ def time_rapid(vwl, x, steps, warmup):
         e.record(stream)
     torch.cuda.synchronize()
     for i in range(steps):
+        z, y = sets[i % copies]
         start[i].record(stream)
         vwl.set_phase_event(mid[i])
         vwl.rapid_verify(z, y, d, ua, us, x.eta, x.T, out=out)
@@ -313,6 +318,98 @@ def cpu_baseline(x, runs=3):
             "nproc": os.cpu_count(), "cpu_model": model}
 
 
+def latency(vwl, x, steps, warmup, copies=4):
+    """Per-call latency of asym_verify on a small workload: median and p10/p90
+    over `steps` calls after `warmup`, rotating `copies` input sets.  These
+    calls are bound by launch and synchronisation latency, not by bytes (the
+    inputs are a few MB at most and stay in the last-level cache)."""
+    _, per, rows = time_asym(vwl, x, steps, warmup, copies=copies)
+    return {"B": x.B, "K": x.K, "V": x.V, "logits": x.dtype, "median_call_us": _median(per) * 1e3,
+            "p10_call_us": _pct(per, 0.1) * 1e3, "p90_call_us": _pct(per, 0.9) * 1e3,
+            "median_row_kernel_us": _median(rows) * 1e3,
+            "bound": "latency (launches and the per-row exchange), inputs cache-resident"}
+
+
+def secondary(args, vwl, W, x, bytes_per_call):
+    """The secondary measurements: single-request and tiny latency, the
+    B=64/K=2 workload and RAPID B=16 (each rotating four input sets, so they
+    read from HBM), the streaming reference, the ablation variants on the
+    large inputs, the cross-family pass, the fused LM-head pass and the E2-SCI
+    windows."""
+    import torch
+    _say("secondary: latency (B=1 and B=4), B=64 K=2 bf16, RAPID B=16 G=10 fp32, stream reference, "
+         "ablation variants, cross-family, LM-head, E2-SCI windows")
+    out = {"latency": {}}
+    for xs in (W.single_asym(), W.tiny_asym()):
+        out["latency"][xs.name] = latency(vwl, xs, args.steps, args.warmup)
+    x2 = W.batched_asym()
+    _, per2, rows2 = time_asym(vwl, x2, args.steps, args.warmup, copies=4)
+    ms2 = _median(per2)
+    b2 = x2.algorithmic_bytes()
+    r3 = W.rapid_c3()
+    per3, rows3 = time_rapid(vwl, r3, args.steps, args.warmup, copies=4)
+    ms3 = _median(per3)
+    b3 = r3.algorithmic_bytes()
+    out["stream_read_gbs"], out["stream_read_shape"] = stream_read_gbs(bytes_per_call)
+    # the ablation variants on the large inputs (bytes actually read: the
+    # fixed gate with delta = t - b skips a)
+    variants = {}
+    for delta, gate in (("a", "cda"), ("t-b", "cda"), ("a-b", "fixed"), ("a", "fixed"), ("t-b", "fixed")):
+        _, pv, rv = time_asym(vwl, x, args.steps, args.warmup, delta=delta, gate=gate)
+        nbytes = bytes_per_call * (2 if (delta, gate) == ("t-b", "fixed") else 3) // 3
+        mr = _median(rv)
+        variants["delta=%s,gate=%s" % (delta, gate)] = {
+            "median_call_ms": _median(pv), "median_row_kernel_ms": mr,
+            "row_kernel_gbs": nbytes / (mr * 1e-3) / 1e9,
+            "plan": vwl.asym_plan_info(x.B, x.K, x.V, torch.bfloat16, delta, gate)}
+    out["variants"] = variants
+    sec = {
+        x2.name: {"rows_per_s": x2.B * (x2.K + 1) / (ms2 * 1e-3), "median_call_ms": ms2,
+                  "median_row_kernel_ms": _median(rows2), "input_sets": 4,
+                  "gbs": b2 / (ms2 * 1e-3) / 1e9, "frac_of_peak": b2 / (ms2 * 1e-3) / 1e9 / PEAK_HBM_GBS},
+        r3.name: {"rows_per_s": r3.B * (r3.G + 1) / (ms3 * 1e-3), "median_call_ms": ms3,
+                  "median_row_kernel_ms": _median(rows3), "input_sets": 4,
+                  "gbs": b3 / (ms3 * 1e-3) / 1e9, "frac_of_peak": b3 / (ms3 * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                  "row_kernel_gbs": b3 / (_median(rows3) * 1e-3) / 1e9, "eta": r3.eta},
+    }
+    xf = W.xfam_batched()
+    pf, rf = time_xfam(vwl, xf, args.steps, args.warmup)
+    mf, mrf = _median(pf), _median(rf)
+    bf = xf.algorithmic_bytes()
+    sec[xf.name] = {
+        "rows_per_s": xf.B * (xf.K + 1) / (mf * 1e-3), "median_call_ms": mf, "median_row_passes_ms": mrf,
+        "input_sets": 4, "gbs": bf / (mrf * 1e-3) / 1e9, "frac_of_peak": bf / (mrf * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    xl = W.lmhead_batched()
+    pl, rl = time_lmhead(vwl, xl, min(args.steps, 50), min(args.warmup, 5))
+    ml = _median(pl)
+    Rl = xl.B * (xl.K + 1)
+    # algorithmic work: the three products once, each head read once; the
+    # launches recompute a and b in their second pass (executed figures)
+    flops = 2.0 * Rl * xl.V * (2 * xl.Hd + xl.Ht)
+    flops_exec = flops + 2.0 * Rl * xl.V * 2 * xl.Hd
+    wbytes = float(xl.weight_bytes())
+    bound_ms = max(flops / (PEAK_BF16_TFLOPS * 1e12), wbytes / (PEAK_HBM_GBS * 1e9)) * 1e3
+    sec[xl.name] = {
+        "rows_per_s": Rl / (ml * 1e-3), "median_call_ms": ml, "median_gemm_passes_ms": _median(rl),
+        "tflops": flops / (ml * 1e-3) / 1e12, "frac_of_bf16_peak": flops / (ml * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "executed_tflops": flops_exec / (ml * 1e-3) / 1e12,
+        "head_weight_gbs": wbytes / (ml * 1e-3) / 1e9,
+        "roofline_bound_ms": bound_ms, "frac_of_roofline": bound_ms / ml,
+        "flops_per_call": flops, "executed_flops_per_call": flops_exec}
+    for xe in (W.e2sci_batched(), W.e2sci_single()):
+        pe, re_ = time_e2sci(vwl, xe, args.steps, args.warmup)
+        me, mre = _median(pe), _median(re_)
+        be = xe.algorithmic_bytes()
+        sec[xe.name] = {
+            "rows_per_s": xe.B * xe.W / (me * 1e-3), "median_call_ms": me, "median_row_kernel_ms": mre,
+            "input_sets": 4, "row_kernel_gbs": be / (mre * 1e-3) / 1e9,
+            "frac_of_peak": be / (mre * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "plan": vwl.e2sci_plan_info(xe.B, xe.W, xe.V, torch.bfloat16)}
+    out["secondary"] = sec
+    out["inputs"] = (x2, r3, xf, xl)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -342,11 +439,16 @@ def main():
         calib_copy()
     _say("generating B=256 K=4 V=151936 bf16 inputs")
     x = W.large_asym()
-    plan = vwl.plan_info("asym", x.B, x.K, x.V, torch.bfloat16)
-    _say("plan %s; timing %d steps after %d warmup" % (plan, args.steps, args.warmup))
-    wall, per, rows_ms = time_asym(vwl, x, args.steps, args.warmup)
     rows = x.B * (x.K + 1)
     bytes_per_call = x.algorithmic_bytes()
+    plan = vwl.plan_info("asym", x.B, x.K, x.V, torch.bfloat16)
+    extra = None
+    if not args.no_extra:
+        # The secondary workloads run first: they are measurements of their
+        # own, and the headline is then timed on a GPU at its working clocks.
+        extra = secondary(args, vwl, W, x, bytes_per_call)
+    _say("plan %s; timing %d steps after %d warmup" % (plan, args.steps, args.warmup))
+    wall, per, rows_ms = time_asym(vwl, x, args.steps, args.warmup)
     ms_step = wall * 1e3 / args.steps
     ms_rows = sum(rows_ms) / len(rows_ms)
     ms_call = sum(per) / len(per)
@@ -384,74 +486,14 @@ def main():
             "busy": float(valu["valu_busy"]), "insts_per_launch": float(valu["SQ_INSTS_VALU"]),
             "floor_ms_at_full_issue": float(valu["valu_cycles_per_simd"]) / 2.4e9 * 1e3,
             "source": os.path.relpath(VALU_SUMMARY, ROOT)}
-    if not args.no_extra:
-        _say("secondary: B=64 K=2 bf16 (4 rotating input sets), RAPID B=16 G=10 fp32, stream reference, "
-             "ablation variants, E2-SCI windows")
-        x2 = W.batched_asym()
-        _, per2, rows2 = time_asym(vwl, x2, args.steps, args.warmup, copies=4)
-        ms2 = _median(per2)
-        b2 = x2.algorithmic_bytes()
-        r3 = W.rapid_c3()
-        per3, rows3 = time_rapid(vwl, r3, args.steps, args.warmup)
-        ms3 = _median(per3)
-        b3 = r3.algorithmic_bytes()
-        sgbs, sshape = stream_read_gbs(bytes_per_call)
-        # the ablation variants on the same inputs (bytes actually read:
-        # the fixed gate with delta = t - b skips a)
-        variants = {}
-        for delta, gate in (("a", "cda"), ("t-b", "cda"), ("a-b", "fixed"), ("a", "fixed"), ("t-b", "fixed")):
-            _, pv, rv = time_asym(vwl, x, args.steps, args.warmup, delta=delta, gate=gate)
-            nbytes = bytes_per_call * (2 if (delta, gate) == ("t-b", "fixed") else 3) // 3
-            mr = _median(rv)
-            variants["delta=%s,gate=%s" % (delta, gate)] = {
-                "median_call_ms": _median(pv), "median_row_kernel_ms": mr,
-                "row_kernel_gbs": nbytes / (mr * 1e-3) / 1e9,
-                "plan": vwl.asym_plan_info(x.B, x.K, x.V, torch.bfloat16, delta, gate)}
-        result["variants_" + x.name] = variants
-        result["stream_read_gbs"] = sgbs
-        result["stream_read_shape"] = sshape
-        result["roofline"]["frac_of_stream"] = achieved / sgbs
-        result["secondary"] = {
-            x2.name: {"rows_per_s": x2.B * (x2.K + 1) / (ms2 * 1e-3), "median_call_ms": ms2,
-                      "median_row_kernel_ms": _median(rows2),
-                      "gbs": b2 / (ms2 * 1e-3) / 1e9, "frac_of_peak": b2 / (ms2 * 1e-3) / 1e9 / PEAK_HBM_GBS},
-            r3.name: {"rows_per_s": r3.B * (r3.G + 1) / (ms3 * 1e-3), "median_call_ms": ms3,
-                      "median_row_kernel_ms": _median(rows3),
-                      "gbs": b3 / (ms3 * 1e-3) / 1e9, "frac_of_peak": b3 / (ms3 * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                      "eta": r3.eta},
-        }
-        xf = W.xfam_batched()
-        pf, rf = time_xfam(vwl, xf, args.steps, args.warmup)
-        mf, mrf = _median(pf), _median(rf)
-        bf = xf.algorithmic_bytes()
-        result["secondary"][xf.name] = {
-            "rows_per_s": xf.B * (xf.K + 1) / (mf * 1e-3), "median_call_ms": mf, "median_row_passes_ms": mrf,
-            "gbs": bf / (mrf * 1e-3) / 1e9, "frac_of_peak": bf / (mrf * 1e-3) / 1e9 / PEAK_HBM_GBS}
-        xl = W.lmhead_batched()
-        pl, rl = time_lmhead(vwl, xl, min(args.steps, 50), min(args.warmup, 5))
-        ml = _median(pl)
-        Rl = xl.B * (xl.K + 1)
-        # algorithmic work: the three products once, each head read once; the
-        # launches recompute a and b in their second pass (executed figures)
-        flops = 2.0 * Rl * xl.V * (2 * xl.Hd + xl.Ht)
-        flops_exec = flops + 2.0 * Rl * xl.V * 2 * xl.Hd
-        wbytes = float(xl.weight_bytes())
-        bound_ms = max(flops / (PEAK_BF16_TFLOPS * 1e12), wbytes / (PEAK_HBM_GBS * 1e9)) * 1e3
-        result["secondary"][xl.name] = {
-            "rows_per_s": Rl / (ml * 1e-3), "median_call_ms": ml, "median_gemm_passes_ms": _median(rl),
-            "tflops": flops / (ml * 1e-3) / 1e12, "frac_of_bf16_peak": flops / (ml * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-            "executed_tflops": flops_exec / (ml * 1e-3) / 1e12,
-            "head_weight_gbs": wbytes / (ml * 1e-3) / 1e9,
-            "roofline_bound_ms": bound_ms, "frac_of_roofline": bound_ms / ml,
-            "flops_per_call": flops, "executed_flops_per_call": flops_exec}
-        for xe in (W.e2sci_batched(), W.e2sci_single()):
-            pe, re_ = time_e2sci(vwl, xe, args.steps, args.warmup)
-            me, mre = _median(pe), _median(re_)
-            be = xe.algorithmic_bytes()
-            result["secondary"][xe.name] = {
-                "rows_per_s": xe.B * xe.W / (me * 1e-3), "median_call_ms": me, "median_row_kernel_ms": mre,
-                "row_kernel_gbs": be / (mre * 1e-3) / 1e9, "frac_of_peak": be / (mre * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                "plan": vwl.e2sci_plan_info(xe.B, xe.W, xe.V, torch.bfloat16)}
+    if extra is not None:
+        result["variants_" + x.name] = extra["variants"]
+        result["stream_read_gbs"] = extra["stream_read_gbs"]
+        result["stream_read_shape"] = extra["stream_read_shape"]
+        result["roofline"]["frac_of_stream"] = achieved / extra["stream_read_gbs"]
+        result["latency"] = extra["latency"]
+        result["secondary"] = extra["secondary"]
+        x2, r3, xf, xl = extra["inputs"]
     if not args.no_cpu_baseline:
         _say("timing the fp64 oracle on the host")
         result["cpu_baseline"] = cpu_baseline(x)

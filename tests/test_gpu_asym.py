@@ -39,7 +39,10 @@ def run_dev(vwl, x, beta=None, gamma=None):
     return {k: v.cpu().numpy() for k, v in out._asdict().items()}
 
 
-def check(vwl, x, beta=None, gamma=None, label=""):
+def check(vwl, x, beta=None, gamma=None, label="", max_excluded=0):
+    """Parity of one call; at most max_excluded requests may fall in the
+    ambiguity windows (the oracle's classifiers find none in these
+    workloads, so the default is zero: a test cannot pass by excluding)."""
     beta = x.beta if beta is None else beta
     gamma = x.gamma if gamma is None else gamma
     _say("case %s %s B=%d K=%d V=%d beta=%g gamma=%g" % (label, x.dtype, x.B, x.K, x.V, beta, gamma))
@@ -49,6 +52,7 @@ def check(vwl, x, beta=None, gamma=None, label=""):
     _say("  " + str(rep))
     assert rep.ok, str(rep)
     assert dev["dev_err"][0] == 0
+    assert rep.excluded <= max_excluded, "%d requests excluded" % rep.excluded
     return dev, ora, rep
 
 
@@ -261,7 +265,7 @@ def test_single_element_rows(vwl):
     x = W.gen_asym(4, 3, 1, "f32", seed=33)
     dev, ora, rep = check(vwl, x, 1.0, 0.5, label="V=1")
     assert np.all(np.abs(dev["D"]) <= 1e-12) and np.all(dev["fused"] == 0) and np.all(dev["accept"] == 1)
-    dev, ora, rep = check(vwl, x, 1.0, 1.0, label="V=1 gamma=1")
+    dev, ora, rep = check(vwl, x, 1.0, 1.0, label="V=1 gamma=1", max_excluded=4)
     assert rep.excluded == 4
 
 

@@ -38,7 +38,7 @@ def run_dev(vwl, x, beta, gamma, delta, gate, drop_a=False):
     return {k: v.cpu().numpy() for k, v in out._asdict().items()}
 
 
-def check(vwl, x, delta, gate, beta=1.0, gamma=0.5, label="", drop_a=False):
+def check(vwl, x, delta, gate, beta=1.0, gamma=0.5, label="", drop_a=False, max_excluded=0):
     _say("case %s delta=%s gate=%s %s B=%d K=%d V=%d beta=%g gamma=%g" % (
         label, delta, gate, x.dtype, x.B, x.K, x.V, beta, gamma))
     dev = run_dev(vwl, x, beta, gamma, delta, gate, drop_a)
@@ -47,6 +47,7 @@ def check(vwl, x, delta, gate, beta=1.0, gamma=0.5, label="", drop_a=False):
     _say("  " + str(rep))
     assert rep.ok, str(rep)
     assert dev["dev_err"][0] == 0
+    assert rep.excluded <= max_excluded, "%d requests excluded" % rep.excluded
     return dev, ora, rep
 
 

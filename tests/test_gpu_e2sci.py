@@ -40,7 +40,7 @@ def run_dev(vwl, x, prm, T=None, r_hat=None, in_place=False):
     return {k: v.cpu().numpy() for k, v in out._asdict().items()}
 
 
-def check(vwl, x, prm=None, label="", T=None, r_hat=None, in_place=False):
+def check(vwl, x, prm=None, label="", T=None, r_hat=None, in_place=False, max_excluded=0):
     prm = prm if prm is not None else vwl.E2sciParams()
     T = x.T if T is None else np.asarray(T, np.float32)
     r_hat = x.r_hat if r_hat is None else np.asarray(r_hat, np.float32)
@@ -51,6 +51,7 @@ def check(vwl, x, prm=None, label="", T=None, r_hat=None, in_place=False):
     _say("  " + str(rep))
     assert rep.ok, str(rep)
     assert dev["dev_err"][0] == 0
+    assert rep.excluded <= max_excluded, "%d requests excluded" % rep.excluded
     return dev, ora, rep
 
 

@@ -41,8 +41,15 @@ def run_dev(vwl, x, eta=None, T=None, want=True):
     return {k: (v.cpu().numpy() if v is not None else None) for k, v in out._asdict().items()}
 
 
-def check(vwl, x, eta=None, T=None, label="", min_checked=0):
+def check(vwl, x, eta=None, T=None, label="", min_checked=None):
+    """Parity of one call.  Draws are excluded when u*S lies within 1e-6*S of
+    an interval end; with V tokens each interval is about S/V wide, so the
+    share of excluded draws grows with V (two or three of the sixteen at
+    V = 128256).  At least min_checked requests must be checked (by
+    default all but a quarter, and at least all but one)."""
     eta = x.eta if eta is None else eta
+    if min_checked is None:
+        min_checked = x.B - max(1, x.B // 4)
     T = x.T if T is None else T
     _say("case %s %s B=%d G=%d V=%d eta=%g T=%g" % (label, x.dtype, x.B, x.G, x.V, eta, T))
     dev = run_dev(vwl, x, eta, T)
@@ -62,12 +69,12 @@ def c3():
 
 @pytest.mark.parametrize("eta", W.C3_ETAS)
 def test_rapid_b16_g10_v128256(vwl, c3, eta):
-    check(vwl, c3, eta, 1.0, label="B16_G10_V128256", min_checked=8)
+    check(vwl, c3, eta, 1.0, label="B16_G10_V128256", min_checked=13)
 
 
 def test_rapid_upward_eta(vwl, c3):
     for eta in (40.0, 50.0):
-        check(vwl, c3, eta, 1.0, label="upward")
+        check(vwl, c3, eta, 1.0, label="upward", min_checked=13)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

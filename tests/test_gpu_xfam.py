@@ -37,7 +37,7 @@ def run_dev(vwl, x, beta=None, gamma=None, t=None, vmap=None, draft=None):
     return {k: v.cpu().numpy() for k, v in out._asdict().items()}
 
 
-def check(vwl, x, beta=None, gamma=None, label="", t=None, vmap=None, draft=None, dev_err=0):
+def check(vwl, x, beta=None, gamma=None, label="", t=None, vmap=None, draft=None, dev_err=0, max_excluded=0):
     beta = x.beta if beta is None else beta
     gamma = x.gamma if gamma is None else gamma
     t = x.t if t is None else t
@@ -51,6 +51,7 @@ def check(vwl, x, beta=None, gamma=None, label="", t=None, vmap=None, draft=None
     _say("  " + str(rep))
     assert rep.ok, str(rep)
     assert dev["dev_err"][0] == dev_err
+    assert rep.excluded <= max_excluded, "%d requests excluded" % rep.excluded
     return dev, ora, rep
 
 

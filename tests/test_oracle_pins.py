@@ -826,3 +826,109 @@ def test_sampler_law_general_case(oracle_lib):
     r = np.maximum(p - m, 0)
     np.testing.assert_allclose(law, m + (1 - m.sum()) * r / r.sum(), atol=3e-3)
     assert np.max(np.abs(law - p)) > 1e-2
+
+
+# ------------------------------------------------- the ambiguity classifiers
+# The parity rules exclude a request when one of these oracle outputs puts a
+# decision within 1e-6 of its threshold, so each is pinned on rows built so
+# that its value is known by hand.
+
+def test_fused_gap_constructed(oracle_lib):
+    """gap = top1 - top2 of the fp64 fused score t + beta*(a - b), counting a
+    repeated maximum (gap 0, an exact tie), wherever the runner-up sits; inf
+    for a one-token row.  Dyadic values: every score is exact."""
+    V = 6
+    zero = np.zeros(V, np.float32)
+    cases = [  # (t, a, beta, gap, fused)
+        ([0.0, 2.0, 1.5, 0.25, 1.0, -1.0], zero, 1.0, 0.5, 1),       # runner-up after the maximum
+        ([1.5, 0.25, 2.0, 1.0, -1.0, 0.0], zero, 1.0, 0.5, 2),       # runner-up before it
+        ([2.0, 0.0, 2.0, 1.0, -1.0, 0.0], zero, 1.0, 0.0, 0),        # repeated maximum: exact tie
+        ([-3.0, -2.75, -3.5, -4.0, -5.0, -6.0], zero, 1.0, 0.25, 1),
+        ([1.0, 1.25, 0.0, 0.0, 0.0, 0.0], [0.5, 0, 0, 0, 0, 0], 2.0, 0.75, 0),  # steered by delta = a - b
+        ([1.0, 1.25, 0.0, 0.0, 0.0, 0.0], [0.5, 0, 0, 0, 0, 0], -2.0, 1.25, 1),  # negative beta
+    ]
+    for t_row, a_row, beta, gap, fused in cases:
+        t = np.asarray(t_row, np.float32)[None, None]
+        a = np.asarray(a_row, np.float32)[None, None]
+        r = _asym(a, np.zeros_like(a), t, np.zeros((1, 0), np.int32), beta=beta)
+        assert r.gap[0, 0] == gap and r.fused[0, 0] == fused
+    one = np.zeros((1, 1, 1), np.float32)
+    assert np.isinf(_asym(one, one, one, np.zeros((1, 0), np.int32)).gap[0, 0])
+
+
+def test_acceptance_closeness_constructed(oracle_lib):
+    """acc_rel = |u*q(x) - phat(x)| / max(u*q(x), phat(x)) at the draft.
+    eta = 0 and a flat target: p = phat = 1/4 everywhere (no tail); the
+    drafter holds all its mass on token 0 (q = 1).  The relative distance is
+    taken against the larger side, and equality rejects."""
+    z = np.zeros((2, 4), np.float32)
+    y = np.array([[0.0, -np.inf, -np.inf, -np.inf]] * 2, np.float32)
+    for u, rel, acc in [(0.125, 0.5, 1), (0.25, 0.0, 0), (0.5, 0.5, 0), (0.75, 2.0 / 3.0, 0)]:
+        r = _rapid_one(z, y, [0], [u], [0.5, 0.5], 0.0, 1.0)
+        assert r.q_draft[0, 0] == 1.0 and r.phat_draft[0, 0] == 0.25
+        assert r.acc_rel[0, 0] == pytest.approx(rel, abs=1e-15)
+        assert r.accept[0, 0] == acc
+        # every token sits at the peak: ln 10 below the tail threshold's side
+        assert r.tail_d_dist[0, 0] == pytest.approx(math.log(10.0), rel=1e-15)
+
+
+def test_tail_distance_two_tokens(oracle_lib):
+    """Two tokens, flat target (p = 1/2) and a drafter on token 0 (q = (1, 0)):
+    zhat = z + eta*(q - p) = (eta/2, -eta/2), so token 1 sits eta below the
+    peak and tail_d_dist there is |-eta - ln 0.1|.  At eta = 2 token 1 is
+    above 10% of the peak (phat = 1/(1 + e^2)); at eta = 4 it is below and
+    keeps p = 1/2."""
+    z = np.zeros((2, 2), np.float32)
+    y = np.array([[0.0, -np.inf]] * 2, np.float32)
+    for eta, phat1 in [(2.0, 1.0 / (1.0 + math.exp(2.0))), (4.0, 0.5)]:
+        r = _rapid_one(z, y, [1], [0.5], [0.5, 0.5], eta, 1.0)
+        assert r.tail_d_dist[0, 0] == pytest.approx(abs(-eta - math.log(0.1)), rel=1e-12)
+        assert r.phat_draft[0, 0] == pytest.approx(phat1, rel=1e-12)
+        assert r.q_draft[0, 0] == 0.0 and r.acc_rel[0, 0] == 1.0 and r.accept[0, 0] == 1
+        r0 = _rapid_one(z, y, [0], [0.5], [0.5, 0.5], eta, 1.0)
+        ph0 = 1.0 / (1.0 + math.exp(-eta))
+        assert r0.tail_d_dist[0, 0] == pytest.approx(-math.log(0.1), rel=1e-12)
+        assert r0.phat_draft[0, 0] == pytest.approx(ph0, rel=1e-12)
+        # u*q = 1/2 against the augmented phat (not p = 1/2): accepted
+        assert r0.acc_rel[0, 0] == pytest.approx((ph0 - 0.5) / ph0, rel=1e-12) and r0.accept[0, 0] == 1
+
+
+def test_tail_close_counts_emitting_row(oracle_lib):
+    """tail_close counts the emitting row's tokens within 1e-6 of the tail
+    threshold (zhat/T - Mhat = ln 0.1).  eta = 0, so zhat = z: two tokens at
+    fp32(ln 0.1) (1e-8 from it), one 1e-3 away, the rest far below.  The
+    drafter puts its mass on token 4, far in the target's tail, so the draft
+    is rejected and row 0 is the emitting row; row 1 is flat."""
+    l01 = math.log(0.1)
+    z0 = [0.0, l01, l01, l01 + 1e-3, -20.0, -20.0, -20.0, -20.0]
+    y0 = [-np.inf] * 8
+    y0[4] = 0.0
+    z = np.array([z0, [0.0] * 8], np.float32)
+    y = np.array([y0, [0.0] * 8], np.float32)
+    r = _rapid_one(z, y, [4], [0.5], [0.5, 0.5], 0.0, 1.0)
+    assert r.accept_len[0] == 0
+    assert r.tail_close[0] == 2
+    # the same row as the second position, after an accepted first draft
+    # (flat row, u = 0): row 1 emits and its tokens are the ones counted
+    z2 = np.array([[0.0] * 8, z0, [0.0] * 8], np.float32)
+    y2 = np.array([[0.0] * 8, y0, [0.0] * 8], np.float32)
+    r2 = _rapid_one(z2, y2, [0, 4], [0.0, 0.5], [0.5, 0.5, 0.5], 0.0, 1.0)
+    assert r2.accept_len[0] == 1
+    assert r2.tail_close[0] == 2
+
+
+def test_draw_slack_constructed(oracle_lib):
+    """draw_slack = min(u*S - c_{k-1}, c_k - u*S) / S at the drawn token k.
+    eta = 0, flat target (p = 1/4), drafter on token 0 (q = (1,0,0,0)), draft
+    0 rejected at u = 1/2 (u*q = 1/2 > 1/4): the residual max(p - q, 0) is
+    (0, 1/4, 1/4, 1/4), S = 3/4, cumulative (0, 1/4, 1/2, 3/4)."""
+    z = np.zeros((2, 4), np.float32)
+    y = np.array([[0.0, -np.inf, -np.inf, -np.inf]] * 2, np.float32)
+    # fp32(1/3) is 1/3 + 1e-8: u*S lands 7.5e-9 past the end of token 1
+    for us, tok, slack in [(0.5, 2, 1.0 / 6.0), (0.25, 1, 1.0 / 12.0), (0.625, 2, 1.0 / 24.0),
+                           (1.0 / 3.0, 2, 0.0)]:
+        us32 = float(np.float32(us))
+        r = _rapid_one(z, y, [0], [0.5], [us32, 0.5], 0.0, 1.0)
+        assert r.accept_len[0] == 0 and r.resid_S[0] == 0.75
+        assert r.token[0] == tok
+        assert r.draw_slack[0] == pytest.approx(slack, abs=1e-7)

@@ -263,18 +263,34 @@ vwl_status asym_verify_lmhead(const void *h_a, const void *h_b, const void *W_d,
  *   accept_i = D_i <= T_in[b]     (a divergence above the threshold rejects)
  *   accept_len[b] = first i with accept_i == 0, else W
  *   r_hat[b] := (1 - ewma) * r_hat[b] + ewma * accept_len[b] / W
- *   T_out[b]  = max(T_min, min(T_base + alpha * omega[b] * (r_hat[b] - tau_credit), T_max))
- * The page's EWMA decay is 0.3; the other constants are the caller's (the
- * page gives none).  omega is the adaptive weight of the page's predictor,
- * which needs trained weights and stays with the caller.
+ *   T_prop    = max(T_min, min(T_base + alpha * omega[b] * (r_hat[b] - tau_credit), T_max))
+ * then the stabilisers the same passage names (hysteresis, a minimum refresh
+ * interval, a fall-back to a conservative threshold when the acceptance
+ * drops below delta; the page gives no rule, this is the library's reading),
+ * in this order, with p_acc = accept_len[b] / W:
+ *   p_acc < delta                       -> T_out = T_safe, age := 0
+ *   else age[b] + 1 < min_refresh       -> T_out = T_in,   age := age + 1
+ *   else |T_prop - T_in| > hysteresis   -> T_out = T_prop, age := 0
+ *   else                                -> T_out = T_in,   age := age + 1
+ * (age saturates at INT32_MAX).  Zero-initialised stabiliser fields switch
+ * them off: T_out is then T_prop.  The page's EWMA decay is 0.3; the other
+ * constants are the caller's (the page gives none).  omega is the adaptive
+ * weight of the page's predictor, which needs trained weights and stays with
+ * the caller.
  *
  * Inputs:
  *   y, z      [B][W][V] drafter and target logits of dtype `dt`, 16-byte
  *             aligned; W >= 1 draft positions per request, W <= VWL_MAX_K+1.
  *   T_in, omega  [B] fp32 device arrays.
  *   r_hat     [B] fp32 device array, read and updated in place.
+ *   age       [B] int32 device array, read and updated in place: windows
+ *             the request's current threshold has been in effect before this
+ *             one (0 when the threshold was just set).  May be null when
+ *             min_refresh <= 1 (every window may refresh; no count is kept).
  *   params    host pointer; every constant finite, T_min <= T_max,
- *             0 <= ewma <= 1, else VWL_ERR_PARAM.
+ *             0 <= ewma <= 1, hysteresis >= 0, min_refresh >= 0, and
+ *             T_min <= T_safe <= T_max when delta > 0, else VWL_ERR_PARAM;
+ *             min_refresh > 1 with a null age is VWL_ERR_NULL.
  * Outputs: D [B][W] fp32, accept [B][W] uint8, accept_len [B] int32,
  *   T_out [B] fp32 (may alias T_in: each row reads its threshold before the
  *   request's last row writes the next one), dev_err nullable.
@@ -289,12 +305,16 @@ typedef struct {
     float T_min;      /* lower safety bound */
     float T_max;      /* upper safety bound */
     float ewma;       /* EWMA decay of the credit state (0.3 on the page) */
+    float hysteresis; /* dead band: a smaller threshold change is not made */
+    int32_t min_refresh; /* windows a threshold stays in effect at least */
+    float delta;      /* acceptance floor of the safety check (0: off) */
+    float T_safe;     /* conservative threshold of the safety check */
 } vwl_e2sci_params;
 
 size_t vwl_e2sci_workspace_bytes(int B, int W, int V, vwl_dtype dt);
 
 vwl_status e2sci_verify(const void *y, const void *z, int B, int W, int V, vwl_dtype dt,
-                        const float *T_in, const float *omega, float *r_hat,
+                        const float *T_in, const float *omega, float *r_hat, int32_t *age,
                         const vwl_e2sci_params *params,
                         float *D, uint8_t *accept, int32_t *accept_len, float *T_out,
                         int32_t *dev_err, void *workspace, size_t workspace_bytes,

@@ -210,7 +210,8 @@ def asym_xfam(a, b, t, vmap, draft, beta: float, gamma: float, dtype: str = "f32
 class LmheadResult:
     """The AsymSpec outputs on logits formed from hidden states and LM-head
     weights, with the per-logit bound on the error of any fp32 summation
-    order of the H products (|h|.|W| * n * 2^-24 / (1 - n * 2^-24), n = H)."""
+    order of the H products (|h|.|W| * n * 2^-24 / (1 - n * 2^-24), n = H;
+    zero where the inputs are dyadic enough that no partial sum rounds)."""
     res: AsymResult
     err_a: np.ndarray   # [B, K+1] largest bound over the row's a logits
     err_b: np.ndarray   # [B, K+1]
@@ -265,12 +266,43 @@ def asym_lmhead(h_a, h_b, W_d, h_t, W_t, draft, beta: float, gamma: float, delta
     res = AsymResult(lse, D, ge, fused, gap, top, acc, margin, alen, tok)
     u = 2.0 ** -24
 
-    def bound(h, W):
+    def lowest_bit(x):
+        """Smallest power of two that divides every nonzero entry of the bf16
+        array x, from its bit patterns (the implicit leading one included), or
+        None if all entries are zero; 0.0 if any is infinite or NaN."""
+        x = np.asarray(x)
+        bits = x if x.dtype == np.uint16 else (np.ascontiguousarray(x, np.float32).view(np.uint32) >> 16)
+        seen = np.flatnonzero(np.bincount(bits.astype(np.uint16).ravel(), minlength=65536))
+        seen = seen[(seen & 0x7FFF) != 0]
+        if seen.size == 0:
+            return None
+        e = (seen >> 7) & 0xFF
+        if np.any(e == 0xFF):
+            return 0.0
+        sig = np.where(e == 0, seen & 0x7F, (seen & 0x7F) | 0x80).astype(np.int64)
+        low = (sig & -sig).astype(np.float64)
+        return float(np.min(np.ldexp(low, np.maximum(e, 1) - 127 - 7)))
+
+    def bound(h, W, hs, Ws):
+        """|h|.|W| * n u / (1 - n u), or 0 where the sum is exact in any order:
+        every product of two bf16 values is exact in fp32, every product and
+        every partial sum is an integer multiple of q = lowest_bit(h) *
+        lowest_bit(W), and when q >= 2^-149 (no product underflows) and the
+        absolute sum is at most 2^24 q (and finite in fp32) each such multiple
+        is representable in fp32, so no product or addition rounds."""
         n = h.shape[-1]
         g = n * u / (1 - n * u)
-        return g * (np.abs(h.reshape(-1, n)) @ np.abs(W).T).reshape(B, P, -1)
+        qh, qw = lowest_bit(hs), lowest_bit(Ws)
+        if qh is None or qw is None:
+            return np.zeros((B, P, W.shape[0]))
+        q = qh * qw
+        limit = min(2.0 ** 24 * q, float(np.finfo(np.float32).max)) if q >= 2.0 ** -149 else -1.0
+        if n * float(np.max(np.abs(h))) * float(np.max(np.abs(W))) <= limit:
+            return np.zeros((B, P, W.shape[0]))      # every sum is below the limit
+        s = (np.abs(h.reshape(-1, n)) @ np.abs(W).T).reshape(B, P, -1)
+        return np.where(s <= limit, 0.0, g * s)
 
-    ea, eb, et = bound(ha, Wd), bound(hb, Wd), bound(ht, Wt)
+    ea, eb, et = bound(ha, Wd, h_a, W_d), bound(hb, Wd, h_b, W_d), bound(ht, Wt, h_t, W_t)
     bi = np.arange(B)[:, None]
     ii = np.arange(K)[None, :]
     d = np.clip(draft, 0, V - 1)
@@ -281,13 +313,20 @@ def asym_lmhead(h_a, h_b, W_d, h_t, W_t, draft, beta: float, gamma: float, delta
 @dataclass
 class E2sciParams:
     """Controller constants of the E2-SCI threshold update (key design 3);
-    the pages fix only the EWMA decay (0.3), the rest are the caller's."""
+    the pages fix only the EWMA decay (0.3), the rest are the caller's.
+    The last four are the stabilisers the same passage names without a rule
+    or constants (their reading is in e2sci_stabilise); their defaults
+    switch them off."""
     alpha: float = 1.0
     tau_credit: float = 0.5
     T_base: float = 0.1
     T_min: float = 0.01
     T_max: float = 0.3
     ewma: float = 0.3
+    hysteresis: float = 0.0   # dead band on the threshold change
+    min_refresh: int = 1      # windows a threshold stays in effect at least
+    delta: float = 0.0        # acceptance floor of the safety check
+    T_safe: float = 0.0       # conservative threshold the safety check falls back to
 
 
 @dataclass
@@ -296,14 +335,52 @@ class E2sciResult:
     accept: np.ndarray      # [B, W] uint8
     accept_len: np.ndarray  # [B] int32
     r_hat: np.ndarray       # [B] updated smoothed acceptance
-    T_next: np.ndarray      # [B] threshold of the next window
+    T_next: np.ndarray      # [B] threshold of the next window (after the stabilisers)
+    T_prop: np.ndarray = None       # [B] clamped proposal T_base + alpha*omega*(r - tau)
+    age: np.ndarray = None          # [B] windows the next threshold has already been in effect
+    hyst_margin: np.ndarray = None  # [B] |T_prop - T_in| - hysteresis where the dead band decided, else NaN
+
+
+def e2sci_stabilise(T_in: float, T_prop: float, p_acc: float, age_in: int, prm: E2sciParams):
+    """The E2-SCI stabilisers of one request after one window (key design 3
+    names hysteresis, a minimum refresh interval and a hard safety check that
+    falls back to a conservative threshold when Acc(T_pred) < delta; the page
+    gives no rule or constant, so this is the plainest reading, applied in
+    this order):
+      1. safety check: the window's accepted fraction p_acc (accepted prefix
+         length / W, measured at the predicted threshold T_in) below delta
+         sets the next threshold to T_safe and restarts the interval;
+      2. minimum refresh interval: a threshold stays in effect for at least
+         min_refresh windows; age_in counts the windows it was in effect
+         before this one, so a refresh is allowed once age_in + 1 >=
+         min_refresh;
+      3. hysteresis: a refresh adopts the clamped proposal T_prop only when
+         it differs from T_in by more than the dead band.
+    Returns (T_next, age_out, margin); age_out is 0 when the threshold was
+    set anew (by 1 or 3) and age_in + 1 otherwise (saturating at 2^31 - 1);
+    margin is |T_prop - T_in| - hysteresis where step 3 decided, else NaN.
+    Arithmetic in float64 on the float32 inputs and constants."""
+    f = lambda v: float(np.float32(v))
+    T_in, T_prop, delta, h = float(T_in), float(T_prop), f(prm.delta), f(prm.hysteresis)
+    nxt = min(int(age_in) + 1, 2 ** 31 - 1)
+    if p_acc < delta:
+        return f(prm.T_safe), 0, float("nan")
+    if nxt < int(prm.min_refresh):
+        return T_in, nxt, float("nan")
+    margin = abs(T_prop - T_in) - h
+    if margin > 0.0:
+        return T_prop, 0, margin
+    return T_in, nxt, margin
 
 
 def e2sci(y, z, T, omega, r_hat, params: E2sciParams = E2sciParams(), dtype: str = "f32",
-          nthreads: int = 0) -> E2sciResult:
+          nthreads: int = 0, age=None) -> E2sciResult:
     """Oracle of the E2-SCI adaptive JSD acceptance on [B, W, V] rows of
     drafter (y) and target (z) logits; T, omega, r_hat are [B] float32 (the
-    values the device receives) and the constants are widened from float32."""
+    values the device receives) and the constants are widened from float32.
+    age ([B] int, default zeros) is the stabilisers' count of windows each
+    request's threshold has been in effect; the next thresholds are the
+    clamped proposals passed through e2sci_stabilise."""
     lib = _load()
     sy, dt = _stored(y, dtype)
     sz, _ = _stored(z, dtype)
@@ -323,7 +400,13 @@ def e2sci(y, z, T, omega, r_hat, params: E2sciParams = E2sciParams(), dtype: str
                               _ptr(r_out), _ptr(T_out), int(nthreads))
     if rc != 0:
         raise RuntimeError("oracle e2sci failed with code %d" % rc)
-    return E2sciResult(D, acc, alen, r_out, T_out)
+    age = np.zeros(B, np.int64) if age is None else np.asarray(age, np.int64).reshape(B)
+    T_next = np.zeros(B)
+    age_out = np.zeros(B, np.int64)
+    margin = np.full(B, np.nan)
+    for bi in range(B):
+        T_next[bi], age_out[bi], margin[bi] = e2sci_stabilise(T[bi], T_out[bi], alen[bi] / Wn, age[bi], params)
+    return E2sciResult(D, acc, alen, r_out, T_next, T_out, age_out, margin)
 
 
 @dataclass

@@ -214,7 +214,10 @@ def compare_e2sci(dev: dict, ora, T, identical=None, rtol: float = REL_TOL,
     oracle divergence is within 1e-5 relative (plus 1e-9) of its threshold is
     ambiguous; a request is excluded, and counted, when a decisive position
     (i <= accept length) is.  The credit state and the next threshold are
-    compared within 1e-6 relative (plus 1e-7) on the requests checked."""
+    compared within 1e-6 relative (plus 1e-7) on the requests checked.  With
+    the stabilisers on, a request whose dead-band decision lies within 1e-9 of
+    the band (|T_prop - T_in| - hysteresis) is excluded too, and the device's
+    window count, when given (dev["age"]), must equal the oracle's."""
     rep = Report()
     D_o, D_d = ora.D, np.asarray(dev["D"], np.float64)
     if identical is not None:
@@ -240,12 +243,16 @@ def compare_e2sci(dev: dict, ora, T, identical=None, rtol: float = REL_TOL,
     al_d = np.asarray(dev["accept_len"])
     r_d = np.asarray(dev["r_hat"], np.float64)
     t_d = np.asarray(dev["T_next"], np.float64)
+    age_d = dev.get("age")
+    hm = getattr(ora, "hyst_margin", None)
     Wn = D_o.shape[1]
     for bi in range(D_o.shape[0]):
         n = int(ora.accept_len[bi])
-        if amb[bi, :min(n + 1, Wn)].any():
+        if amb[bi, :min(n + 1, Wn)].any() or (hm is not None and abs(hm[bi]) <= 1e-9):
             rep.excluded += 1
             continue
+        if age_d is not None and int(age_d[bi]) != int(ora.age[bi]):
+            rep.fail("age mismatch at request %d: dev %d oracle %d" % (bi, int(age_d[bi]), int(ora.age[bi])))
         rep.checked += 1
         if al_d[bi] != n:
             rep.fail("accept_len mismatch at request %d: dev %d oracle %d" % (bi, al_d[bi], n))

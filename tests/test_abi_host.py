@@ -257,14 +257,15 @@ def _e2sci(lib, **kw):
     """e2sci_verify with placeholder device pointers: every case here returns
     from the host-side checks, before anything touches a device."""
     args = dict(y=A, z=A + 0x1000, B=2, W=4, V=100, dt=0, T=A + 0x2000, om=A + 0x3000, r=A + 0x4000,
-                prm=(1.0, 0.5, 0.1, 0.01, 0.3, 0.3), D=A + 0x5000, acc=A + 0x6000, alen=A + 0x7000,
+                age=0, prm=(1.0, 0.5, 0.1, 0.01, 0.3, 0.3), D=A + 0x5000, acc=A + 0x6000, alen=A + 0x7000,
                 To=A + 0x8000, ws=0, wsb=0)
     args.update(kw)
     p = lambda x: ctypes.c_void_p(x) if x else None
     import vocab_wide_logit_amd as vwl
     prm = None if args["prm"] is None else ctypes.byref(vwl.E2sciParams(*args["prm"]))
     return lib.e2sci_verify(p(args["y"]), p(args["z"]), args["B"], args["W"], args["V"], args["dt"],
-                            p(args["T"]), p(args["om"]), p(args["r"]), prm, p(args["D"]), p(args["acc"]),
+                            p(args["T"]), p(args["om"]), p(args["r"]), p(args["age"]), prm, p(args["D"]),
+                            p(args["acc"]),
                             p(args["alen"]), p(args["To"]), None, p(args["ws"]), ctypes.c_size_t(args["wsb"]),
                             None)
 
@@ -285,6 +286,20 @@ def test_e2sci_argument_codes(lib):
     assert _e2sci(lib, prm=(float("nan"), 0.5, 0.1, 0.01, 0.3, 0.3)) == 4
     assert _e2sci(lib, y=A + 4) == 7
     assert _e2sci(lib, T=A + 0x2002) == 7
+    # the stabilisers: hysteresis >= 0, min_refresh >= 0, T_safe within [T_min, T_max] when delta > 0,
+    # a count array when min_refresh > 1
+    base = (1.0, 0.5, 0.1, 0.01, 0.3, 0.3)
+    assert _e2sci(lib, prm=base + (0.01, 1, 0.25, 0.05)) == 5
+    assert _e2sci(lib, prm=base + (-0.01, 1, 0.0, 0.0)) == 4
+    assert _e2sci(lib, prm=base + (float("inf"), 1, 0.0, 0.0)) == 4
+    assert _e2sci(lib, prm=base + (0.0, -1, 0.0, 0.0)) == 4
+    assert _e2sci(lib, prm=base + (0.0, 1, 0.25, 0.5)) == 4
+    assert _e2sci(lib, prm=base + (0.0, 1, 0.25, 0.001)) == 4
+    assert _e2sci(lib, prm=base + (0.0, 1, 0.0, 0.5)) == 5            # delta 0: T_safe unused
+    assert _e2sci(lib, prm=base + (0.0, 1, float("nan"), 0.05)) == 4
+    assert _e2sci(lib, prm=base + (0.0, 3, 0.0, 0.0)) == 1            # min_refresh 3 needs age
+    assert _e2sci(lib, prm=base + (0.0, 3, 0.0, 0.0), age=A + 0x9000) == 5
+    assert _e2sci(lib, prm=base + (0.0, 3, 0.0, 0.0), age=A + 0x9002) == 7
 
 
 def test_asym_xfam_argument_codes(lib):

@@ -25,28 +25,30 @@ def vwl():
 
 def _oracle_params(prm):
     return oracle.E2sciParams(alpha=prm.alpha, tau_credit=prm.tau_credit, T_base=prm.T_base,
-                              T_min=prm.T_min, T_max=prm.T_max, ewma=prm.ewma)
+                              T_min=prm.T_min, T_max=prm.T_max, ewma=prm.ewma, hysteresis=prm.hysteresis,
+                              min_refresh=prm.min_refresh, delta=prm.delta, T_safe=prm.T_safe)
 
 
-def run_dev(vwl, x, prm, T=None, r_hat=None, in_place=False):
+def run_dev(vwl, x, prm, T=None, r_hat=None, in_place=False, age=None):
     import torch
     y = vwl.to_device_logits(x.y, x.dtype)
     z = vwl.to_device_logits(x.z, x.dtype)
     Td = torch.from_numpy(np.ascontiguousarray(x.T if T is None else T, np.float32)).cuda()
     om = torch.from_numpy(np.ascontiguousarray(x.omega, np.float32)).cuda()
     rh = torch.from_numpy(np.ascontiguousarray(x.r_hat if r_hat is None else r_hat, np.float32)).cuda()
-    out = vwl.e2sci_verify(y, z, Td, om, rh, prm, T_out=Td if in_place else None)
+    ag = None if age is None else torch.from_numpy(np.ascontiguousarray(age, np.int32)).cuda()
+    out = vwl.e2sci_verify(y, z, Td, om, rh, prm, age=ag, T_out=Td if in_place else None)
     torch.cuda.synchronize()
-    return {k: v.cpu().numpy() for k, v in out._asdict().items()}
+    return {k: (v.cpu().numpy() if v is not None else None) for k, v in out._asdict().items()}
 
 
-def check(vwl, x, prm=None, label="", T=None, r_hat=None, in_place=False, max_excluded=0):
+def check(vwl, x, prm=None, label="", T=None, r_hat=None, in_place=False, max_excluded=0, age=None):
     prm = prm if prm is not None else vwl.E2sciParams()
     T = x.T if T is None else np.asarray(T, np.float32)
     r_hat = x.r_hat if r_hat is None else np.asarray(r_hat, np.float32)
     _say("case %s %s B=%d W=%d V=%d" % (label, x.dtype, x.B, x.W, x.V))
-    dev = run_dev(vwl, x, prm, T, r_hat, in_place)
-    ora = oracle.e2sci(x.y, x.z, T, x.omega, r_hat, _oracle_params(prm), x.dtype)
+    dev = run_dev(vwl, x, prm, T, r_hat, in_place, age)
+    ora = oracle.e2sci(x.y, x.z, T, x.omega, r_hat, _oracle_params(prm), x.dtype, age=age)
     rep = compare_e2sci(dev, ora, T, identical=x.identical)
     _say("  " + str(rep))
     assert rep.ok, str(rep)
@@ -98,7 +100,7 @@ def test_thresholds_in_place_over_windows(vwl):
         out = vwl.e2sci_verify(vwl.to_device_logits(x.y, x.dtype), vwl.to_device_logits(x.z, x.dtype),
                                T, om, rh, prm, T_out=T)
         torch.cuda.synchronize()
-        dev = {k2: v.cpu().numpy() for k2, v in out._asdict().items()}
+        dev = {k2: (v.cpu().numpy() if v is not None else None) for k2, v in out._asdict().items()}
         assert out.T_next.data_ptr() == T.data_ptr()
         ora = oracle.e2sci(x.y, x.z, T_before, xs[0].omega, r_before, _oracle_params(prm), x.dtype)
         rep = compare_e2sci(dev, ora, T_before, identical=x.identical)
@@ -149,8 +151,57 @@ def test_inclusive_threshold_and_clamps(vwl):
     x.identical[:4] = True
     x.omega[:] = 1e4
     prm = vwl.E2sciParams(alpha=1.0, tau_credit=0.5, T_base=0.1, T_min=0.02, T_max=0.25, ewma=1.0)
-    dev, ora, rep = check(vwl, x, prm, T=np.zeros(8, np.float32), r_hat=np.zeros(8, np.float32))
+    # the identical rows sit on the threshold (D = T = 0) and are ambiguous by
+    # construction: the four are excluded by the rules and checked here directly
+    dev, ora, rep = check(vwl, x, prm, T=np.zeros(8, np.float32), r_hat=np.zeros(8, np.float32), max_excluded=4)
     np.testing.assert_array_equal(dev["accept_len"][:4], 3)
     np.testing.assert_array_equal(dev["accept_len"][4:], 0)
     np.testing.assert_array_equal(dev["T_next"], np.float32([0.25] * 4 + [0.02] * 4))
     np.testing.assert_array_equal(dev["r_hat"], np.float32([1.0] * 4 + [0.0] * 4))
+
+
+def test_stabilisers_batched(vwl):
+    """The stabilisers on the batched workload: a dead band, a refresh
+    interval of 3 windows with ages spread over 0..4, and a safety floor that
+    some windows fall under; thresholds and counts match the oracle."""
+    x = W.e2sci_batched()
+    prm = vwl.E2sciParams(alpha=0.4, tau_credit=0.5, T_base=0.08, T_min=0.02, T_max=0.2, ewma=0.3,
+                          hysteresis=0.01, min_refresh=3, delta=0.25, T_safe=0.03)
+    age = (np.arange(x.B) % 5).astype(np.int32)
+    dev, ora, rep = check(vwl, x, prm, label="stabilised " + x.name, age=age, max_excluded=2)
+    p_acc = ora.accept_len / x.W
+    assert np.any(p_acc < 0.25) and np.any((p_acc >= 0.25) & (age + 1 < 3))
+    assert np.any(ora.age == 0) and np.any(ora.age > 0)
+    ok = np.isfinite(ora.hyst_margin)
+    assert np.any(ora.hyst_margin[ok] > 0) and np.any(ora.hyst_margin[ok] <= 0)
+
+
+def test_stabilisers_over_windows(vwl):
+    """Eight windows with the threshold, credit state and window count all
+    carried on the device (T_out aliases T_in); each window is checked
+    against the oracle fed the device's state before it."""
+    import torch
+    prm = vwl.E2sciParams(alpha=0.6, tau_credit=0.5, T_base=0.08, T_min=0.02, T_max=0.2, ewma=0.3,
+                          hysteresis=0.005, min_refresh=2, delta=0.2, T_safe=0.03)
+    xs = [W.gen_e2sci(16, 4, 30000, "bf16", seed=700 + k, identical_frac=0.1) for k in range(8)]
+    T = torch.from_numpy(xs[0].T.copy()).cuda()
+    rh = torch.from_numpy(xs[0].r_hat.copy()).cuda()
+    om = torch.from_numpy(xs[0].omega.copy()).cuda()
+    age = torch.zeros(16, dtype=torch.int32, device="cuda")
+    held = 0
+    for k, x in enumerate(xs):
+        T_before = T.cpu().numpy().copy()
+        r_before = rh.cpu().numpy().copy()
+        a_before = age.cpu().numpy().copy()
+        out = vwl.e2sci_verify(vwl.to_device_logits(x.y, x.dtype), vwl.to_device_logits(x.z, x.dtype),
+                               T, om, rh, prm, age=age, T_out=T)
+        torch.cuda.synchronize()
+        dev = {k2: (v.cpu().numpy() if v is not None else None) for k2, v in out._asdict().items()}
+        ora = oracle.e2sci(x.y, x.z, T_before, xs[0].omega, r_before, _oracle_params(prm), x.dtype,
+                           age=a_before)
+        rep = compare_e2sci(dev, ora, T_before, identical=x.identical)
+        _say("  window %d %s" % (k, rep))
+        assert rep.ok, str(rep)
+        assert rep.excluded <= 1
+        held += int(np.sum(ora.age > 0))
+    assert held > 0

@@ -87,3 +87,18 @@ def test_bench_shape(vwl):
         dev, lm, rep = check(vwl, x, beta, gamma, label=x.name)
         assert rep.checked >= 40
         assert rep.stats["D_max_abs"] < 1e-5
+
+
+def test_bench_shape_exact_products(vwl):
+    """The bench shape with signed power-of-two heads and hidden states: every
+    fp32 product-sum is exact, so the device's logits equal the fp64 ones,
+    the oracle's product bound is zero and the windows are the plain ones of
+    the pass (D to 1e-5 relative); at most two requests may be excluded."""
+    x = W.lmhead_dyadic()
+    for beta, gamma in ((1.0, 0.5), (0.0, 1.0)):
+        dev, lm, rep = check(vwl, x, beta, gamma, label=x.name)
+        for e in (lm.err_a, lm.err_b, lm.err_t):
+            assert np.all(e == 0.0)
+        assert rep.stats["D_window_max"] == 0.0
+        assert rep.excluded <= 2
+        assert rep.checked >= x.B - 2

@@ -77,6 +77,22 @@ def test_rapid_upward_eta(vwl, c3):
         check(vwl, c3, eta, 1.0, label="upward", min_checked=13)
 
 
+def test_rapid_eta_changes_decisions(vwl):
+    """Full vocabulary with a +13 spike: the target's mass sits on few tokens,
+    so the augmentation strength moves accept lengths and emitted tokens.
+    Parity at each eta, and the oracle's decisions must differ between the
+    unaugmented target and the augmented ones (else this case would not test
+    the augmentation at this width)."""
+    x = W.rapid_spiked()
+    lens = {}
+    for eta in (0.0, 5.0, 10.0, 20.0):
+        dev, ora, rep = check(vwl, x, eta, 1.0, label="spiked", min_checked=13)
+        lens[eta] = (np.asarray(ora.accept_len).copy(), np.asarray(ora.token).copy())
+    for eta in (5.0, 10.0, 20.0):
+        assert not np.array_equal(lens[eta][0], lens[0.0][0])
+    assert not np.array_equal(lens[20.0][0], lens[5.0][0])
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("V", [1, 2, 3, 5, 17, 1000, 1027, 4097, 9001])
 @pytest.mark.parametrize("G", [0, 1, 3, 10])

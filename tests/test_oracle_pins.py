@@ -452,6 +452,55 @@ def test_lmhead_error_bound_covers_fp32_sums(oracle_lib):
     assert np.all(err < 1e-2)
 
 
+def test_lmhead_dyadic_products_are_exact(oracle_lib):
+    """With signed power-of-two entries every fp32 summation order of the
+    head products gives the fp64 logits exactly (checked on three orders),
+    and the oracle reports a zero bound for them."""
+    x = W.gen_lmhead_dyadic(2, 2, 300, 512, seed=72)
+    r = oracle.asym_lmhead(x.h_a, x.h_b, x.W_d, x.h_t, x.W_t, x.draft, 1.0, 0.5)
+    for h, Wm in ((x.h_a, x.W_d), (x.h_b, x.W_d), (x.h_t, x.W_t)):
+        hh = h.reshape(-1, h.shape[-1])
+        exact = hh.astype(np.float64) @ Wm.astype(np.float64).T
+        np.testing.assert_array_equal((hh @ Wm.T).astype(np.float64), exact)
+        for order in (range(hh.shape[1]), range(hh.shape[1] - 1, -1, -1)):
+            seq = np.zeros(exact.shape, np.float32)
+            for k in order:
+                seq = (seq + np.outer(hh[:, k], Wm[:, k])).astype(np.float32)
+            np.testing.assert_array_equal(seq.astype(np.float64), exact)
+    for e in (r.err_a, r.err_b, r.err_t, r.err_bd, r.err_td):
+        assert np.all(e == 0.0)
+    # the planted structure survives: spikes make the drafts the drafter's top tokens
+    a = x.h_a.reshape(-1, x.Hd).astype(np.float64) @ x.W_d.astype(np.float64).T
+    top = a.reshape(x.B, x.K + 1, x.V)[:, :x.K].argmax(axis=2)
+    assert np.mean(top == x.draft) > 0.8
+
+
+def test_lmhead_bound_nonzero_when_a_sum_can_round(oracle_lib):
+    """One fine entry among coarse ones: 32 ones and 2^-20 need 26 significant
+    bits, an fp32 order that adds the fine term last rounds it away, and the
+    oracle's bound must be nonzero and cover that error."""
+    n = 32
+    h = np.ones((1, 2, n), np.float32)
+    h[0, 0, 0] = 2.0 ** -20
+    Wm = np.ones((2, n), np.float32)
+    r = oracle.asym_lmhead(h, h, Wm, h, Wm, np.zeros((1, 1), np.int32), 1.0, 0.5)
+    exact = 31.0 + 2.0 ** -20
+    rounded = float(np.float32(np.float32(31.0) + np.float32(2.0 ** -20)))
+    assert rounded != exact
+    assert r.err_a[0, 0] >= abs(rounded - exact) > 0.0
+    # a row of ones only (no fine term) is exact again
+    assert r.err_a[0, 1] > 0.0          # the bound is per call: q is the finest bit of all of h
+    h2 = np.ones((1, 2, n), np.float32)
+    r2 = oracle.asym_lmhead(h2, h2, Wm, h2, Wm, np.zeros((1, 1), np.int32), 1.0, 0.5)
+    assert np.all(r2.err_a == 0.0)
+    # products that underflow fp32 (2^-80 * 2^-80) are not exact: the bound stays
+    tiny = np.full((1, 2, n), 2.0 ** -80, np.float32)
+    Wt = np.full((2, n), 2.0 ** -80, np.float32)
+    r3 = oracle.asym_lmhead(tiny, tiny, Wt, tiny, Wt, np.zeros((1, 1), np.int32), 1.0, 0.5)
+    assert np.all(r3.err_a > 0.0)
+    assert float(np.float32(2.0 ** -80) * np.float32(2.0 ** -80)) == 0.0
+
+
 # ------------------------------------------------ AsymSpec across model families
 # AsymSpec notes, the analysis of cross-family pairs: the drafter's gain
 # reaches the verifier through a vocabulary alignment of string-identical
@@ -620,6 +669,98 @@ def test_e2sci_threshold_update(oracle_lib):
     assert abs((out.T_next[1] - f(0.1)) - 2 * (out.T_next[0] - f(0.1))) < 1e-9
     big = oracle.e2sci(y, z, T_in, np.full(4, 100.0, np.float32), np.zeros(4, np.float32), prm)
     np.testing.assert_array_equal(big.T_next, [f(0.25), f(0.25), f(0.02), f(0.02)])
+
+
+# The stabilisers of the same passage (hysteresis, a minimum refresh
+# interval, a safety fall-back when the acceptance drops below delta): the
+# page names them without a rule; the oracle's reading is pinned on
+# constructed sequences whose outcome follows from that reading by hand.
+
+def test_e2sci_stabilisers_off_by_default(oracle_lib):
+    """Default constants leave the page's update untouched: the next threshold
+    is the clamped proposal on every request, whatever the age."""
+    y, z = _e2sci_rows(6, 4, 200, 45)
+    z[:2] = y[:2]
+    rng = np.random.default_rng(45)
+    T_in = rng.uniform(0.0, 0.3, 6).astype(np.float32)
+    out = oracle.e2sci(y, z, T_in, np.ones(6, np.float32), np.full(6, 0.5, np.float32),
+                       age=np.array([0, 1, 5, 0, 7, 2]))
+    np.testing.assert_array_equal(out.T_next, out.T_prop)
+    assert np.all((out.age == 0) | (out.T_prop == T_in.astype(np.float64)))
+
+
+def test_e2sci_hysteresis_dead_band():
+    """A proposal within the dead band of the current threshold (either side)
+    keeps it; one beyond it is adopted, and the age restarts."""
+    f = lambda v: float(np.float32(v))
+    prm = oracle.E2sciParams(hysteresis=0.005)
+    T0 = f(0.1)
+    for dT, moves in ((0.0049, False), (-0.0049, False), (0.0051, True), (-0.0051, True)):
+        T, age, m = oracle.e2sci_stabilise(T0, T0 + dT, 0.5, 3, prm)
+        assert (T != T0) == moves and (age == 0) == moves, dT
+        assert T == (T0 + dT if moves else T0)
+        assert abs(m - (abs(dT) - f(0.005))) < 1e-12
+    # a proposal oscillating by +-0.003 around the threshold never moves it
+    # with a 0.005 band; with a 0.002 band it follows every proposal
+    props = [T0 + (0.003 if k % 2 else -0.003) for k in range(8)]
+    for band, follows in ((0.005, False), (0.002, True)):
+        T, age = T0, 0
+        seen = []
+        for pr in props:
+            T, age, _ = oracle.e2sci_stabilise(T, pr, 0.5, age, oracle.E2sciParams(hysteresis=band))
+            seen.append(T)
+        assert seen == (props if follows else [T0] * 8)
+
+
+def test_e2sci_minimum_refresh_interval():
+    """With a minimum interval of 3 windows a threshold set at age 0 holds for
+    two more windows and the proposal is adopted on the third; a fresh
+    proposal on every window therefore lands on windows 3, 6, 9."""
+    prm = oracle.E2sciParams(min_refresh=3)
+    T, age = 0.1, 0
+    changes = []
+    for k in range(1, 10):
+        T_new, age, _ = oracle.e2sci_stabilise(T, 0.1 + 0.01 * k, 0.5, age, prm)
+        if T_new != T:
+            changes.append(k)
+        T = T_new
+    assert changes == [3, 6, 9]
+    # min_refresh 0 or 1: every window may refresh
+    for m in (0, 1):
+        T, age, _ = oracle.e2sci_stabilise(0.1, 0.2, 0.5, 0, oracle.E2sciParams(min_refresh=m))
+        assert T == 0.2 and age == 0
+
+
+def test_e2sci_safety_fallback():
+    """An accepted fraction below delta sets the conservative threshold at
+    once, inside the refresh interval and inside the dead band; one equal to
+    delta does not trigger it."""
+    f = lambda v: float(np.float32(v))
+    prm = oracle.E2sciParams(hysteresis=0.5, min_refresh=5, delta=0.25, T_safe=0.02)
+    T, age, m = oracle.e2sci_stabilise(0.1, 0.1, 0.125, 0, prm)
+    assert T == f(0.02) and age == 0 and np.isnan(m)
+    T, age, _ = oracle.e2sci_stabilise(0.1, 0.3, 0.25, 0, prm)     # p_acc == delta: interval holds
+    assert T == 0.1 and age == 1
+
+
+def test_e2sci_stabilised_window(oracle_lib):
+    """End to end on rows: requests whose drafter equals the target accept
+    the whole window (p_acc = 1) and get the proposal (outside the band);
+    requests that reject at once (p_acc = 0 < delta) fall back to T_safe;
+    a request still inside its refresh interval keeps its threshold."""
+    f = lambda v: float(np.float32(v))
+    prm = oracle.E2sciParams(alpha=0.5, tau_credit=0.5, T_base=0.1, T_min=0.02, T_max=0.25, ewma=1.0,
+                             hysteresis=0.01, min_refresh=2, delta=0.5, T_safe=0.03)
+    y, z = _e2sci_rows(4, 4, 64, 46)
+    z[[0, 3]] = y[[0, 3]]
+    T_in = np.zeros(4, np.float32)
+    out = oracle.e2sci(y, z, T_in, np.ones(4, np.float32), np.zeros(4, np.float32), prm,
+                       age=np.array([1, 1, 0, 0]))
+    np.testing.assert_array_equal(out.accept_len, [4, 0, 0, 4])
+    assert out.T_prop[0] == f(0.25)                          # 0.1 + 0.5 * (1 - 0.5), clamped to T_max
+    assert out.T_next[0] == f(0.25) and out.age[0] == 0
+    assert out.T_next[1] == f(0.03) and out.T_next[2] == f(0.03) and out.age[1] == out.age[2] == 0
+    assert out.T_next[3] == 0.0 and out.age[3] == 1          # age 0 + 1 < 2: held
 
 
 def test_page_defaults_in_workloads():

@@ -70,10 +70,13 @@ class E2sciParams(ctypes.Structure):
     prints only the EWMA decay (0.3); the defaults of the others are this
     binding's choice."""
     _fields_ = [("alpha", ctypes.c_float), ("tau_credit", ctypes.c_float), ("T_base", ctypes.c_float),
-                ("T_min", ctypes.c_float), ("T_max", ctypes.c_float), ("ewma", ctypes.c_float)]
+                ("T_min", ctypes.c_float), ("T_max", ctypes.c_float), ("ewma", ctypes.c_float),
+                ("hysteresis", ctypes.c_float), ("min_refresh", ctypes.c_int32), ("delta", ctypes.c_float),
+                ("T_safe", ctypes.c_float)]
 
-    def __init__(self, alpha=1.0, tau_credit=0.5, T_base=0.1, T_min=0.01, T_max=0.3, ewma=0.3):
-        super().__init__(alpha, tau_credit, T_base, T_min, T_max, ewma)
+    def __init__(self, alpha=1.0, tau_credit=0.5, T_base=0.1, T_min=0.01, T_max=0.3, ewma=0.3,
+                 hysteresis=0.0, min_refresh=1, delta=0.0, T_safe=0.0):
+        super().__init__(alpha, tau_credit, T_base, T_min, T_max, ewma, hysteresis, min_refresh, delta, T_safe)
 
 
 class VwlError(RuntimeError):
@@ -135,7 +138,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.asym_verify_xfam.restype = i
         lib.vwl_e2sci_workspace_bytes.argtypes = [i, i, i, i]
         lib.vwl_e2sci_workspace_bytes.restype = sz
-        lib.e2sci_verify.argtypes = [P, P, i, i, i, i, P, P, P, ctypes.POINTER(E2sciParams),
+        lib.e2sci_verify.argtypes = [P, P, i, i, i, i, P, P, P, P, ctypes.POINTER(E2sciParams),
                                      P, P, P, P, P, P, sz, P]
         lib.e2sci_verify.restype = i
         lib.vwl_e2sci_plan_info.argtypes = [i, i, i, i, ctypes.POINTER(ctypes.c_int64)]
@@ -451,6 +454,7 @@ class E2sciOut(NamedTuple):
     T_next: torch.Tensor      # [B] float32 threshold of the next window
     r_hat: torch.Tensor       # [B] float32 credit state (updated in place)
     dev_err: torch.Tensor     # [1] int32
+    age: Optional[torch.Tensor] = None  # [B] int32 stabiliser window count (updated in place), if given
 
 
 def e2sci_plan_info(B: int, W: int, V: int, dtype: torch.dtype) -> dict:
@@ -464,12 +468,14 @@ def e2sci_plan_info(B: int, W: int, V: int, dtype: torch.dtype) -> dict:
 
 def e2sci_verify(y: torch.Tensor, z: torch.Tensor, T: torch.Tensor, omega: torch.Tensor,
                  r_hat: torch.Tensor, params: Optional[E2sciParams] = None, *,
+                 age: Optional[torch.Tensor] = None,
                  T_out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> E2sciOut:
     """E2-SCI adaptive JSD acceptance of one window per request on the
     current stream.  y: drafter logits, z: target logits, [B, W, V];
     T, omega, r_hat: [B] float32 device tensors (r_hat is updated in place);
-    the next thresholds go to T_out (a new tensor when None; pass T itself to
-    update in place)."""
+    age: [B] int32 device tensor of the stabilisers' window count, updated in
+    place (needed when params.min_refresh > 1); the next thresholds go to
+    T_out (a new tensor when None; pass T itself to update in place)."""
     lib = load_library()
     _dev_tensor(y, "y")
     dt = _dt(y)
@@ -484,6 +490,10 @@ def e2sci_verify(y: torch.Tensor, z: torch.Tensor, T: torch.Tensor, omega: torch
     if T_out is None:
         T_out = torch.empty(B, dtype=torch.float32, device=y.device)
     _dev_tensor(T_out, "T_out", torch.float32)
+    if age is not None:
+        _dev_tensor(age, "age", torch.int32)
+        if tuple(age.shape) != (B,):
+            raise ValueError("age must be [B]")
     params = params if params is not None else E2sciParams()
     kw = dict(device=y.device)
     D = torch.empty(B, Wn, dtype=torch.float32, **kw)
@@ -495,10 +505,10 @@ def e2sci_verify(y: torch.Tensor, z: torch.Tensor, T: torch.Tensor, omega: torch
         need = int(lib.vwl_e2sci_workspace_bytes(B, Wn, V, dt))
         workspace = _workspace_sized(("e2sci", B, Wn, V, dt), need, y.device, stream)
     code = lib.e2sci_verify(_ptr(y), _ptr(z), B, Wn, V, dt, _ptr(T), _ptr(omega), _ptr(r_hat),
-                            ctypes.byref(params), _ptr(D), _ptr(acc), _ptr(alen), _ptr(T_out), _ptr(err),
+                            _ptr(age) if age is not None else None, ctypes.byref(params), _ptr(D), _ptr(acc), _ptr(alen), _ptr(T_out), _ptr(err),
                             _ptr(workspace), workspace.numel(), ctypes.c_void_p(stream.cuda_stream))
     _check(code)
-    return E2sciOut(D, acc, alen, T_out, r_hat, err)
+    return E2sciOut(D, acc, alen, T_out, r_hat, err, age)
 
 
 class RapidOut(NamedTuple):

@@ -14,7 +14,11 @@
 // request finds the first rejection, updates the credit state
 //   r = (1 - beta) r + beta * accept_len / W
 // and writes the next window's threshold
-//   T = max(T_min, min(T_base + alpha * omega * (r - tau_credit), T_max)).
+//   T = max(T_min, min(T_base + alpha * omega * (r - tau_credit), T_max)),
+// passed through the stabilisers of the same passage: an accepted fraction
+// below delta falls back to T_safe; otherwise the current threshold is kept
+// while it has been in effect for fewer than min_refresh windows or while
+// the proposal lies within the hysteresis band of it.
 #include "asym_kernels.hpp"
 
 namespace vwl {
@@ -61,6 +65,19 @@ __global__ __launch_bounds__(kThreads) void e2sci_finalize_kernel(AsymParams P) 
         double T = P.e_Tbase + P.e_alpha * (double)P.omega[bi] * (r - P.e_tau);
         T = T > P.e_Tmax ? P.e_Tmax : T;
         T = T < P.e_Tmin ? P.e_Tmin : T;
+        // stabilisers: safety fall-back, minimum refresh interval, dead band
+        const double T_cur = (double)P.thr_in[bi];
+        const int age_in = P.age ? P.age[bi] : 0;
+        const int age_next = age_in < 0x7fffffff ? age_in + 1 : age_in;
+        int age_out = 0;
+        if (p_acc < P.e_delta) {
+            T = P.e_Tsafe;
+        } else if (age_next < P.e_minref || !(fabs(T - T_cur) > P.e_hyst)) {
+            T = T_cur;
+            age_out = age_next;
+        }
+        if (P.age)
+            P.age[bi] = age_out;
         P.r_hat[bi] = (float)r;
         P.thr_out[bi] = (float)T;
         for (int k = 0; k < P.win; ++k) // per-row results back to zero for the next call

@@ -758,7 +758,8 @@ size_t vwl_e2sci_workspace_bytes(int B, int W, int V, vwl_dtype dt) {
 }
 
 vwl_status e2sci_verify(const void *y, const void *z, int B, int W, int V, vwl_dtype dt,
-                        const float *T_in, const float *omega, float *r_hat, const vwl_e2sci_params *params,
+                        const float *T_in, const float *omega, float *r_hat, int32_t *age,
+                        const vwl_e2sci_params *params,
                         float *D, uint8_t *accept, int32_t *accept_len, float *T_out,
                         int32_t *dev_err, void *workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!y || !z || !T_in || !omega || !r_hat || !params || !D || !accept || !accept_len || !T_out)
@@ -769,10 +770,15 @@ vwl_status e2sci_verify(const void *y, const void *z, int B, int W, int V, vwl_d
         return VWL_ERR_DTYPE;
     const vwl_e2sci_params &q = *params;
     if (!finite_f(q.alpha) || !finite_f(q.tau_credit) || !finite_f(q.T_base) || !finite_f(q.T_min) ||
-        !finite_f(q.T_max) || !(q.T_min <= q.T_max) || !(q.ewma >= 0.0f && q.ewma <= 1.0f))
+        !finite_f(q.T_max) || !(q.T_min <= q.T_max) || !(q.ewma >= 0.0f && q.ewma <= 1.0f) ||
+        !finite_f(q.hysteresis) || !(q.hysteresis >= 0.0f) || q.min_refresh < 0 || !finite_f(q.delta) ||
+        !finite_f(q.T_safe) || (q.delta > 0.0f && !(q.T_min <= q.T_safe && q.T_safe <= q.T_max)))
         return VWL_ERR_PARAM;
+    if (q.min_refresh > 1 && !age)
+        return VWL_ERR_NULL;
     if (!aligned(y, 16) || !aligned(z, 16) || !aligned(T_in, 4) || !aligned(omega, 4) || !aligned(r_hat, 4) ||
-        !aligned(D, 4) || !aligned(accept_len, 4) || !aligned(T_out, 4) || (dev_err && !aligned(dev_err, 4)))
+        !aligned(D, 4) || !aligned(accept_len, 4) || !aligned(T_out, 4) || (dev_err && !aligned(dev_err, 4)) ||
+        (age && !aligned(age, 4)))
         return VWL_ERR_ALIGN;
     const size_t need = vwl_e2sci_workspace_bytes(B, W, V, dt);
     if (!workspace || workspace_bytes < need)
@@ -818,6 +824,11 @@ vwl_status e2sci_verify(const void *y, const void *z, int B, int W, int V, vwl_d
     p.e_Tmin = q.T_min;
     p.e_Tmax = q.T_max;
     p.e_ewma = q.ewma;
+    p.e_hyst = q.hysteresis;
+    p.e_delta = q.delta;
+    p.e_Tsafe = q.T_safe;
+    p.e_minref = q.min_refresh;
+    p.age = age;
     return launch_e2sci((int)dt, plan, p, stream, g_phase_event.load()) == hipSuccess ? VWL_OK : VWL_ERR_HIP;
 }
 

@@ -113,6 +113,9 @@ struct AsymParams {
     const float *thr_in, *omega;
     float *r_hat, *thr_out;
     double e_alpha, e_tau, e_Tbase, e_Tmin, e_Tmax, e_ewma;
+    double e_hyst, e_delta, e_Tsafe; // stabilisers of the threshold update
+    int e_minref;
+    int32_t *age;                    // [B] windows in effect of each threshold, nullable
 };
 
 struct RapidParams {

@@ -45,6 +45,15 @@ Recipe (one logit row = one draft position of one request):
   W_x ~ N(0, (0.5/sqrt(Hd))^2)) and h_t = [h_b + N(0, 0.1^2) | N(0, 1)], so
   t ~ b + N(0, 0.5^2) (the verifier reads the compressed context).  Drafts
   are the planted tokens s.  Everything is rounded to bf16.
+* LM heads with dyadic entries (the exact-product variant): every weight and
+  hidden value is a signed power of two, W_d = +-1/8 and h = +-1/4 with
+  random signs (logits N(0, 1.6^2)); the spike of +8 at s flips 128 of the
+  coordinates where h and W_d[s] disagree in sign; h_b flips 64 random
+  coordinates of h_a (logit noise 0.5) and, in an exact 30% of rows, undoes
+  the spike's flips and plants it at s' instead; h_t = [h_b with 16 flips |
+  +-1/4] and W_x = +-1/32.  Every product is a multiple of 2^-7 and every
+  logit's absolute product-sum stays below 2^7, so an fp32 sum of the
+  products is exact in any order.
 * E2-SCI: target ``z_t = z + N(0, 0.5^2)``; drafter ``y = z + N(0,
   sigma^2)`` with ``sigma`` uniform on [0.1, 1.0] per row (a spread of
   divergences); "identical" rows set ``y := z_t`` bit for bit (divergence
@@ -57,7 +66,10 @@ Recipe (one logit row = one draft position of one request):
   tempered softmax, drawn with the Gumbel-max construction (``argmax(y/T +
   G)``, ``G`` standard Gumbel) from a separate seeded stream.  Acceptance
   and residual uniforms are ``k * 2^-24`` with ``k`` uniform on
-  ``[0, 2^24)``: exact in float32 and never 1.
+  ``[0, 2^24)``: exact in float32 and never 1.  The spiked RAPID variant
+  raises the planted spike to +13, so that the target's mass concentrates on
+  few tokens and the augmentation strength eta changes the accept/reject and
+  residual decisions at the full vocabulary.
 """
 from __future__ import annotations
 
@@ -120,6 +132,19 @@ def _choose_rows(rng: np.random.Generator, pool: np.ndarray, count: int) -> np.n
     if count <= 0:
         return np.zeros(0, dtype=np.int64)
     return np.sort(rng.permutation(pool)[:count])
+
+
+def _flip(h: np.ndarray, coords: np.ndarray) -> None:
+    h[coords] = -h[coords]
+
+
+def _plant(g: np.random.Generator, h: np.ndarray, w: np.ndarray, m: int) -> np.ndarray:
+    """Flip m coordinates of h whose sign disagrees with w's (raising h.w by
+    2 m |h_i w_i|); returns the flipped coordinates."""
+    dis = np.flatnonzero(np.sign(h) != np.sign(w))
+    c = g.choice(dis, size=min(m, dis.size), replace=False)
+    _flip(h, c)
+    return c
 
 
 def _parallel_rows(R: int, V: int, nbuf: int, fn) -> None:
@@ -486,6 +511,56 @@ class E2sciInputs:
         return 2 * self.y.shape[0] * self.y.shape[1] * self.V * es
 
 
+def gen_lmhead_dyadic(B: int, K: int, V: int, Hd: int, seed: int = SEED_BASE + 9,
+                      displaced_frac: float = 0.3, beta: float = 1.0, gamma: float = 0.5,
+                      name: str = "") -> LmheadInputs:
+    """LM-head workload whose products are exact in fp32 (module recipe,
+    the dyadic variant; Ht = 2 Hd)."""
+    if B < 1 or K < 0 or V < 2 or Hd < 128:
+        raise ValueError("need B >= 1, K >= 0, V >= 2, Hd >= 128")
+    R = B * (K + 1)
+    ss = np.random.SeedSequence(seed)
+    s_w, s_h, s_sel = ss.spawn(3)
+    gw = np.random.default_rng(s_w)
+
+    def signs(shape, mag):
+        return (gw.integers(0, 2, size=shape, dtype=np.int8).astype(np.float32) * 2 - 1) * np.float32(mag)
+
+    W_d = signs((V, Hd), 0.125)
+    W_t = np.ascontiguousarray(np.concatenate([W_d, signs((V, Hd), 1.0 / 32)], axis=1))
+    sel = np.random.default_rng(s_sel)
+    disp = np.zeros(R, bool)
+    disp[_choose_rows(sel, np.arange(R), int(round(displaced_frac * R)))] = True
+    gh = np.random.default_rng(s_h)
+    h_a = np.empty((R, Hd), np.float32)
+    h_b = np.empty((R, Hd), np.float32)
+    h_t = np.empty((R, 2 * Hd), np.float32)
+    spike = np.empty(R, np.int64)
+    for r in range(R):
+        s = int(gh.integers(0, V))
+        h = (gh.integers(0, 2, size=Hd).astype(np.float32) * 2 - 1) * np.float32(0.25)
+        planted = _plant(gh, h, W_d[s], 128)
+        h_a[r] = h
+        hb = h.copy()
+        if disp[r]:
+            s2 = int(gh.integers(0, V - 1))
+            s2 = s2 + 1 if s2 >= s else s2
+            _flip(hb, planted)
+            _plant(gh, hb, W_d[s2], 128)
+        _flip(hb, gh.choice(Hd, size=64, replace=False))
+        h_b[r] = hb
+        hc = hb.copy()
+        _flip(hc, gh.choice(Hd, size=16, replace=False))
+        h_t[r, :Hd] = hc
+        h_t[r, Hd:] = (gh.integers(0, 2, size=Hd).astype(np.float32) * 2 - 1) * np.float32(0.25)
+        spike[r] = s
+    P = K + 1
+    draft = spike.reshape(B, P)[:, :K].astype(np.int32)
+    return LmheadInputs(h_a=h_a.reshape(B, P, Hd), h_b=h_b.reshape(B, P, Hd), h_t=h_t.reshape(B, P, 2 * Hd),
+                        W_d=W_d, W_t=W_t, draft=np.ascontiguousarray(draft), beta=float(beta),
+                        gamma=float(gamma), seed=seed, name=name)
+
+
 def gen_e2sci(B: int, W: int, V: int, dtype: str = F32, seed: int = SEED_BASE + 5,
               identical_frac: float = 0.0, noise_lo: float = 0.1, noise_hi: float = 1.0,
               base_std: float = 2.0, spike: float = 8.0, target_std: float = 0.5,
@@ -673,6 +748,12 @@ def rapid_c3(seed: int = SEED_BASE + 3, eta: float = 10.0) -> RapidInputs:
                      name="rapid_B16_G10_V128256_f32")
 
 
+def rapid_spiked(seed: int = SEED_BASE + 60, eta: float = 10.0) -> RapidInputs:
+    """B=16, G=10, V=128256, fp32, T=1, spike +13: eta changes decisions."""
+    return gen_rapid(16, 10, VOCAB_LLAMA31, F32, seed, displaced_frac=0.4, eta=eta, T=1.0, spike=13.0,
+                     name="rapid_spiked_B16_G10_V128256_f32")
+
+
 def large_asym(seed: int = SEED_BASE + 4, beta: float = 1.0, gamma: float = 0.5) -> AsymInputs:
     """B=256, K=4, V=151936, bf16; 20% identical drafter rows, 5% planted ties."""
     return gen_asym(256, 4, VOCAB_QWEN3, BF16, seed, displaced_frac=0.3,
@@ -709,3 +790,10 @@ def lmhead_batched(seed: int = SEED_BASE + 8) -> LmheadInputs:
     """B=64, K=2, V=151936, Hd=2560 (Qwen3-4B drafter head), Ht=5120 (a
     Qwen3-32B-sized verifier head), bf16."""
     return gen_lmhead(64, 2, VOCAB_QWEN3, HIDDEN_QWEN3_4B, seed, name="lmhead_B64_K2_V151936_Hd2560_Ht5120_bf16")
+
+
+def lmhead_dyadic(seed: int = SEED_BASE + 9) -> LmheadInputs:
+    """The LM-head bench shape (B=64, K=2, V=151936, Hd=2560, Ht=5120) with
+    signed power-of-two entries, so the logits are exact in fp32."""
+    return gen_lmhead_dyadic(64, 2, VOCAB_QWEN3, HIDDEN_QWEN3_4B, seed,
+                             name="lmhead_dyadic_B64_K2_V151936_Hd2560_Ht5120_bf16")

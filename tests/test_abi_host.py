@@ -321,3 +321,34 @@ def test_asym_xfam_argument_codes(lib):
     assert call(Vd=0) == 2
     assert call(dt=4) == 3
     assert call(vmap=A + 0xA002, ws=0x100000, wsb=1 << 30) == 7
+
+
+def test_divergence_polynomial_constants():
+    """The one-exponential divergence term of the kernels: the fp32 Horner
+    evaluation of u * P(u) with the coefficients compiled into the HIP
+    source matches Psi(x)/2 = cosh(x/2) (x tanh(x/2) - 2 ln cosh(x/2)) / 2
+    (evaluated in fp64) within 4e-7 relative on |x| < kPsiX1, the range the
+    kernels use it on; the identity itself, for one element with x = ln p -
+    ln q, gives that element's share of the JSD, checked here on random
+    (p, q)."""
+    import re
+    src = open(os.path.join(ROOT, "vocab_wide_logit_amd", "csrc", "asym_kernels.hpp")).read()
+    x1 = float(re.search(r"constexpr float kPsiX1 = ([0-9.]+)f;", src).group(1))
+    cf = {int(k): float.fromhex(v) for k, v in re.findall(r"constexpr float kPsiP(\d) = (-?0x[0-9a-fA-Fp.+-]+)f;", src)}
+    deg = max(cf)
+    assert sorted(cf) == list(range(deg + 1))
+    x = np.linspace(1e-3, x1 * (1 - 1e-7), 200001)
+    u = (((x.astype(np.float32) * np.float32(1.0 / x1))) ** 2).astype(np.float32)
+    acc = np.float32(cf[deg])
+    for k in range(deg - 1, -1, -1):
+        acc = (acc * u + np.float32(cf[k])).astype(np.float32)
+    val = (acc * u).astype(np.float64)
+    xu = x1 * np.sqrt(u.astype(np.float64))
+    exact = np.cosh(xu / 2) * (xu * np.tanh(xu / 2) - 2 * np.log(np.cosh(xu / 2))) / 2
+    assert np.max(np.abs(val / exact - 1)) < 4e-7
+    rng = np.random.default_rng(5)
+    p, q = rng.uniform(1e-6, 1, 1000), rng.uniform(1e-6, 1, 1000)
+    xs = np.log(p) - np.log(q)
+    share = (p * np.log(2 * p / (p + q)) + q * np.log(2 * q / (p + q))) / 2
+    psi = np.cosh(xs / 2) * (xs * np.tanh(xs / 2) - 2 * np.log(np.cosh(xs / 2)))
+    np.testing.assert_allclose(np.sqrt(p * q) * psi / 2, share, rtol=1e-9, atol=1e-15)

@@ -295,3 +295,17 @@ def test_one_workspace_across_shapes(vwl):
         _say("  " + str(rep))
         assert rep.ok and dev["dev_err"][0] == 0, str(rep)
         assert int(ws.count_nonzero()) == 0, "the call left workspace bytes set"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_wide_disagreement(vwl, dtype):
+    """Drafter rows whose log-probability ratio x = ln p - ln q spreads over
+    [-7, 7]: the divergence pass evaluates |x| < 4 by its polynomial and
+    recomputes vectors holding a larger |x| exactly, so every row mixes both
+    paths, with elements on both sides of the switch; D within 1e-5 relative."""
+    x = W.gen_asym(6, 2, 40000, dtype, seed=34, identical_frac=0.0)
+    rng = np.random.default_rng(34)
+    shift = rng.uniform(-7.0, 7.0, size=x.a.shape)
+    x.b = W._to_dtype(x.a.astype(np.float64) + shift, dtype)
+    dev, ora, rep = check(vwl, x, label="wide disagreement")
+    assert np.all(ora.D > 0.05)

@@ -40,7 +40,9 @@
  *     matching *_workspace_bytes query returns for the same shape (the size
  *     depends on the shape and dtype only, not on the device).  It must be
  *     zero-filled before its first use (vwl_workspace_reset does that); every
- *     completed call leaves it zero-filled again.  Two calls that share one
+ *     completed call leaves every counter, flag and exchange word that a
+ *     later call reads before writing back at zero (the rest holds values a
+ *     later call overwrites before reading them).  Two calls that share one
  *     workspace must be ordered (same stream, or synchronised).
  *   - Results are bitwise deterministic for identical inputs, shape and device.
  */

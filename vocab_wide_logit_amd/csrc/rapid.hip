@@ -14,10 +14,10 @@
 // others' loads and arithmetic; the serial sections (reductions, publish,
 // team wait, combine) run at a raised wave priority.
 // Launch 2 (the tail): per request, row statistics and the acceptance test
-// of each row, the first rejection, then the emitting row in fp64 (refined
-// normalisers, the augmented target's log-sum-exp, the residual
-// max(p - phat, p - q, 0) or p, and the inverse-CDF draw in vocabulary
-// order), phase by phase across the request's workgroups.
+// of each row, the first rejection, then the emitting
+// row in fp64 (refined normalisers, the augmented target's log-sum-exp, the
+// residual max(p - phat, p - q, 0) or p, and the inverse-CDF draw in
+// vocabulary order), phase by phase across the request's workgroups.
 #include "vwl_device.hpp"
 #include "vwl_internal.hpp"
 
@@ -148,6 +148,177 @@ __device__ __forceinline__ void online_group_h(OnlineLseR &st, const AugCoef &k,
 __device__ __forceinline__ void split_f64(double x, float &hi, float &lo) {
     hi = (float)x;
     lo = (float)(x - (double)hi);
+}
+
+// Reductions within the 16-lane segment of a wave that holds one row.
+__device__ __forceinline__ float seg16_max(float v) {
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1)
+        v = fmaxf(v, __shfl_xor(v, m, 16));
+    return v;
+}
+__device__ __forceinline__ double seg16_sum(double v) {
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1)
+        v += __shfl_xor(v, m, 16);
+    return v;
+}
+__device__ __forceinline__ int seg16_min_int(int v) {
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1)
+        v = min(v, __shfl_xor(v, m, 16));
+    return v;
+}
+
+// Row statistics and the acceptance test of one row, by one 16-lane segment
+// of a wave (so a wave handles four rows at once): all record words of the
+// row are loaded in one round.  The segment's lane 0 leaves L_z, L_y, Mhat,
+// L_zhat, the argmax and the acceptance flag in `slot`; with `write` it
+// also stores the row's outputs and clears the row's arrival counter.  Every
+// lane of the segment must call it (the reductions are segment-wide).
+template <int DT>
+__device__ __forceinline__ void tail_row(const RapidParams &P, long long row, bool write, double *slot) {
+    const int lane = threadIdx.x & 15;
+    const int Pn = P.G + 1;
+    const long long bi = row / Pn;
+    const int i = (int)(row - bi * Pn);
+    const size_t row_off = (size_t)row * (size_t)P.V;
+    // the draft's logits, early (independent of the records)
+    int x = -1;
+    double zx = 0.0, yx = 0.0;
+    if (i < P.G) {
+        x = P.draft[bi * P.G + i];
+        if (lane == 0 && x >= 0 && x < P.V) {
+            zx = (double)load_scalar<DT>(P.z, row_off + x) * P.invT64;
+            yx = (double)load_scalar<DT>(P.y, row_off + x) * P.invT64;
+        }
+    }
+    const uint64_t *rec_row = P.rec + (size_t)row * P.Wmax * kRecWords;
+    const float NEG = -3.0e38f;
+    float cz = NEG, cy = NEG, ch = NEG, mh = -__builtin_inff();
+    double sz = 0.0, sy = 0.0, sh = 0.0;
+    int hidx = 0x7fffffff;
+    // first pass: references and the maximum (loads kept for the second)
+    uint64_t w0[2] = {0, 0}, w1[2] = {0, 0}, w2[2] = {0, 0}, w3[2] = {0, 0}, w4[2] = {0, 0}, w5[2] = {0, 0};
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int w = lane + 16 * k;
+        if (w < P.W) {
+            const uint64_t *r = rec_row + (size_t)w * kRecWords;
+            w0[k] = ld_relaxed(r + 0);
+            w1[k] = ld_relaxed(r + 1);
+            w2[k] = ld_relaxed(r + 2);
+            w3[k] = ld_relaxed(r + 3);
+            w4[k] = ld_relaxed(r + 4);
+            w5[k] = ld_relaxed(r + 5);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        if (lane + 16 * k < P.W) {
+            cz = fmaxf(cz, unpack_lo(w2[k]));
+            cy = fmaxf(cy, unpack_hi(w2[k]));
+            ch = fmaxf(ch, unpack_lo(w5[k]));
+            const float m = unpack_lo(w4[k]);
+            const int ix = (int)(uint32_t)(w4[k] >> 32);
+            if (m > mh || (m == mh && ix < hidx)) {
+                mh = m;
+                hidx = ix;
+            }
+        }
+    }
+    for (int w = lane + 32; w < P.W; w += 16) { // teams wider than 32 members
+        const uint64_t *r = rec_row + (size_t)w * kRecWords;
+        const uint64_t a2 = ld_relaxed(r + 2), a4 = ld_relaxed(r + 4), a5 = ld_relaxed(r + 5);
+        cz = fmaxf(cz, unpack_lo(a2));
+        cy = fmaxf(cy, unpack_hi(a2));
+        ch = fmaxf(ch, unpack_lo(a5));
+        const float m = unpack_lo(a4);
+        const int ix = (int)(uint32_t)(a4 >> 32);
+        if (m > mh || (m == mh && ix < hidx)) {
+            mh = m;
+            hidx = ix;
+        }
+    }
+    cz = seg16_max(cz);
+    cy = seg16_max(cy);
+    ch = seg16_max(ch);
+    const float mh_all = seg16_max(mh);
+    hidx = seg16_min_int(mh == mh_all ? hidx : 0x7fffffff);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        if (lane + 16 * k < P.W) {
+            sz += scale_pow2(as_f64(w0[k]), unpack_lo(w2[k]) - cz);
+            sy += scale_pow2(as_f64(w1[k]), unpack_hi(w2[k]) - cy);
+            sh += scale_pow2(as_f64(w3[k]), unpack_lo(w5[k]) - ch);
+        }
+    }
+    for (int w = lane + 32; w < P.W; w += 16) {
+        const uint64_t *r = rec_row + (size_t)w * kRecWords;
+        const uint64_t a2 = ld_relaxed(r + 2), a5 = ld_relaxed(r + 5);
+        sz += scale_pow2(as_f64(ld_relaxed(r + 0)), unpack_lo(a2) - cz);
+        sy += scale_pow2(as_f64(ld_relaxed(r + 1)), unpack_hi(a2) - cy);
+        sh += scale_pow2(as_f64(ld_relaxed(r + 3)), unpack_lo(a5) - ch);
+    }
+    sz = seg16_sum(sz);
+    sy = seg16_sum(sy);
+    sh = seg16_sum(sh);
+    if (lane != 0)
+        return;
+    const double Lz = ((double)cz + log2(sz)) * kLn2d;
+    const double Ly = ((double)cy + log2(sy)) * kLn2d;
+    const double Lh = ((double)ch + log2(sh)) * kLn2d;
+    const double eta_d = P.eta_d;
+    // Mhat: the augmented logit at the argmax, recomputed in fp64
+    double Mh = (double)mh_all * kLn2d;
+    if (hidx >= 0 && hidx < P.V) {
+        const double zm = (double)load_scalar<DT>(P.z, row_off + hidx) * P.invT64;
+        const double ym = (double)load_scalar<DT>(P.y, row_off + hidx) * P.invT64;
+        Mh = zm + eta_d * (exp(ym - Ly) - exp(zm - Lz));
+    } else {
+        hidx = -1;
+    }
+    slot[0] = Lz;
+    slot[1] = Ly;
+    slot[2] = Mh;
+    slot[3] = Lh;
+    slot[4] = (double)hidx;
+    if (write) {
+        double *rs = P.rowstat + (size_t)row * kRowStatWords;
+        st_f64(rs + 0, Lz);
+        st_f64(rs + 1, Ly);
+        st_f64(rs + 2, Mh);
+        st_f64(rs + 3, Lh);
+        st_f64(rs + 4, (double)hidx);
+    }
+    uint32_t acc = 0;
+    if (i < P.G) {
+        const long long k = bi * P.G + i;
+        float phd = 0.f, qd = 0.f;
+        if (x < 0 || x >= P.V) {
+            if (write)
+                set_dev_err(P.dev_err, 1);
+        } else {
+            const double p = exp(zx - Lz);
+            const double q = exp(yx - Ly);
+            const double h = zx + eta_d * (q - p);
+            const double ph = (h - Mh < -2.302585092994046) ? p : exp(h - Lh);
+            const double u = clamp_uniform(P.u_accept[k], write ? P.dev_err : nullptr);
+            acc = (u * q < ph) ? 1u : 0u;
+            phd = (float)ph;
+            qd = (float)q;
+        }
+        if (write) {
+            P.accept[k] = (uint8_t)acc;
+            if (P.p_hat_draft)
+                P.p_hat_draft[k] = phd;
+            if (P.q_draft)
+                P.q_draft[k] = qd;
+        }
+    }
+    slot[5] = (double)acc;
+    if (write)
+        st_relaxed(P.row_ctr + (size_t)row * 16, 0u); // the row's arrivals, for the next call
 }
 
 template <int DT, int NV>
@@ -299,9 +470,9 @@ __global__ __launch_bounds__(kThreads, (NV <= 4 ? 5 : 4)) void rapid_rows_kernel
         hi = block_min_int(hi, lds_i);
         if (tid == 0) {
             uint64_t *rec = P.rec + ((size_t)row * P.Wmax + member) * kRecWords;
-            rec[3] = f64_bits(Sh[0]);
-            rec[4] = pack_fi(Hm, hi);
-            rec[5] = (uint64_t)__float_as_uint(Ch);
+            st_relaxed(rec + 3, f64_bits(Sh[0]));
+            st_relaxed(rec + 4, pack_fi(Hm, hi));
+            st_relaxed(rec + 5, (uint64_t)__float_as_uint(Ch));
         }
         __builtin_amdgcn_s_setprio(0);
     }
@@ -310,164 +481,36 @@ __global__ __launch_bounds__(kThreads, (NV <= 4 ? 5 : 4)) void rapid_rows_kernel
 // ---------------------------------------------------------------------------
 // Launch 2, the tail: one team of We workgroups per request; workgroup w
 // owns the EPT * 256 elements of the request's emitting row starting at
-// w * EPT * 256 (EPT contiguous elements per thread).  Phases, separated by
+// w * EPT * 256 (EPT contiguous elements per thread).  Every workgroup
+// combines the records of all the request's rows (row statistics, Mhat in
+// fp64 at the argmax, the draft's tail-protected phat and q and the
+// acceptance test, one row per 16-lane segment; workgroup 0 writes them
+// out), so each knows the accept
+// length n and the emitting row's statistics at once.  Phases, separated by
 // barriers of the request's team:
-//   0  one wave per row of the request: row statistics from the W records
-//      (Mhat recomputed in fp64 at the argmax), the draft's tail-protected
-//      phat and q and the acceptance test
-//   1  accept length n; per element p' = exp(z/T - L_z), q' = exp(y/T - L_y)
-//      around the row pass's values (kept in registers) -> chunk sums ->
-//      L_z, L_y refined in fp64, Mhat recomputed with them
-//   2  (residual rows) e = exp(h - Mhat), kept, and the tail-protection flag
-//      -> chunk sums -> L_zhat in fp64
-//   3  residual max(p - phat, p - q, 0) (or p) per element -> chunk sums
-//   4  the chunk that holds u * S walks its elements in vocabulary order;
+//   1  per element, around the row pass's log-sum-exps,
+//      p' = exp(z/T - L_z), q' = exp(y/T - L_y), h' = z/T + eta (q' - p')
+//      and e' = exp(h' - M) (M the row pass's maximum of h), kept in
+//      registers -> chunk sums of p', q', e', e'q', e'p'.
+//   2  (residual rows) the refined normalisers f_z = 1 / sum p', f_y =
+//      1 / sum q' make p = f_z p' and q = f_y q' sum to one; they move h by
+//      d = eta (q' (f_y - 1) - p' (f_z - 1)), of the order of the row
+//      pass's rounding (1e-7 relative), so sum exp(h - M) = sum e' + eta
+//      (f_y - 1) sum e'q' - eta (f_z - 1) sum e'p' to second order in d and
+//      phat = e' exp(d) / that sum; Mhat is recomputed in fp64 at the
+//      argmax.  Residual max(p - phat, p - q, 0) per element -> chunk sums.
+//   3  the chunk that holds u * S walks its elements in vocabulary order;
 //      emit_dist when requested.
+// A bonus row (n = G) draws from p, whose normalisation does not move the
+// draw, so it goes from phase 1 (sums of p') straight to phase 3.
 // Chunk intervals come from one fixed-order running sum evaluated the same
 // way by every workgroup, so they tile [0, S) exactly.  Everything on the
 // emitting row is fp64, with three exponentials per element.
 // With n < G the residual of row n is drawn from (p of row n when the
 // residual is all zero); with n = G, p of the bonus row.
-// Per-request partials [B][We][8]: 0 residual/target weights, 1 target,
-// 2 exp(h - Mhat), 3 p', 4 q'.
+// Per-request partials [B][We][8]: 0 residual weights, 1 p, 2 e', 3 p',
+// 4 q', 5 e'q', 6 e'p'.
 // ---------------------------------------------------------------------------
-
-// Row statistics and the acceptance test of one row (one whole wave): all
-// record words of the row are loaded in one round.
-template <int DT>
-__device__ __forceinline__ void tail_row(const RapidParams &P, long long row) {
-    const int lane = threadIdx.x & 63;
-    const int Pn = P.G + 1;
-    const long long bi = row / Pn;
-    const int i = (int)(row - bi * Pn);
-    const size_t row_off = (size_t)row * (size_t)P.V;
-    // the draft's logits, early (independent of the records)
-    int x = -1;
-    double zx = 0.0, yx = 0.0;
-    if (i < P.G) {
-        x = P.draft[bi * P.G + i];
-        if (lane == 0 && x >= 0 && x < P.V) {
-            zx = (double)load_scalar<DT>(P.z, row_off + x) * P.invT64;
-            yx = (double)load_scalar<DT>(P.y, row_off + x) * P.invT64;
-        }
-    }
-    const uint64_t *rec_row = P.rec + (size_t)row * P.Wmax * kRecWords;
-    const float NEG = -3.0e38f;
-    float cz = NEG, cy = NEG, ch = NEG, mh = -__builtin_inff();
-    double sz = 0.0, sy = 0.0, sh = 0.0;
-    int hidx = 0x7fffffff;
-    // first pass: references and the maximum (loads kept for the second)
-    uint64_t w0[2] = {0, 0}, w1[2] = {0, 0}, w2[2] = {0, 0}, w3[2] = {0, 0}, w4[2] = {0, 0}, w5[2] = {0, 0};
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int w = lane + 64 * k;
-        if (w < P.W) {
-            const uint64_t *r = rec_row + (size_t)w * kRecWords;
-            w0[k] = ld_relaxed(r + 0);
-            w1[k] = ld_relaxed(r + 1);
-            w2[k] = ld_relaxed(r + 2);
-            w3[k] = ld_relaxed(r + 3);
-            w4[k] = ld_relaxed(r + 4);
-            w5[k] = ld_relaxed(r + 5);
-        }
-    }
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        if (lane + 64 * k < P.W) {
-            cz = fmaxf(cz, unpack_lo(w2[k]));
-            cy = fmaxf(cy, unpack_hi(w2[k]));
-            ch = fmaxf(ch, unpack_lo(w5[k]));
-            const float m = unpack_lo(w4[k]);
-            const int ix = (int)(uint32_t)(w4[k] >> 32);
-            if (m > mh || (m == mh && ix < hidx)) {
-                mh = m;
-                hidx = ix;
-            }
-        }
-    }
-    for (int w = lane + 128; w < P.W; w += 64) { // teams wider than 128 members
-        const uint64_t *r = rec_row + (size_t)w * kRecWords;
-        const uint64_t a2 = ld_relaxed(r + 2), a4 = ld_relaxed(r + 4), a5 = ld_relaxed(r + 5);
-        cz = fmaxf(cz, unpack_lo(a2));
-        cy = fmaxf(cy, unpack_hi(a2));
-        ch = fmaxf(ch, unpack_lo(a5));
-        const float m = unpack_lo(a4);
-        const int ix = (int)(uint32_t)(a4 >> 32);
-        if (m > mh || (m == mh && ix < hidx)) {
-            mh = m;
-            hidx = ix;
-        }
-    }
-    cz = wave_max(cz);
-    cy = wave_max(cy);
-    ch = wave_max(ch);
-    const float mh_all = wave_max(mh);
-    hidx = wave_min_int(mh == mh_all ? hidx : 0x7fffffff);
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        if (lane + 64 * k < P.W) {
-            sz += scale_pow2(as_f64(w0[k]), unpack_lo(w2[k]) - cz);
-            sy += scale_pow2(as_f64(w1[k]), unpack_hi(w2[k]) - cy);
-            sh += scale_pow2(as_f64(w3[k]), unpack_lo(w5[k]) - ch);
-        }
-    }
-    for (int w = lane + 128; w < P.W; w += 64) {
-        const uint64_t *r = rec_row + (size_t)w * kRecWords;
-        const uint64_t a2 = ld_relaxed(r + 2), a5 = ld_relaxed(r + 5);
-        sz += scale_pow2(as_f64(ld_relaxed(r + 0)), unpack_lo(a2) - cz);
-        sy += scale_pow2(as_f64(ld_relaxed(r + 1)), unpack_hi(a2) - cy);
-        sh += scale_pow2(as_f64(ld_relaxed(r + 3)), unpack_lo(a5) - ch);
-    }
-    sz = wave_sum(sz);
-    sy = wave_sum(sy);
-    sh = wave_sum(sh);
-    if (lane != 0)
-        return;
-    const double Lz = ((double)cz + log2(sz)) * kLn2d;
-    const double Ly = ((double)cy + log2(sy)) * kLn2d;
-    const double Lh = ((double)ch + log2(sh)) * kLn2d;
-    const double eta_d = P.eta_d;
-    // Mhat: the augmented logit at the argmax, recomputed in fp64
-    double Mh = (double)mh_all * kLn2d;
-    if (hidx >= 0 && hidx < P.V) {
-        const double zm = (double)load_scalar<DT>(P.z, row_off + hidx) * P.invT64;
-        const double ym = (double)load_scalar<DT>(P.y, row_off + hidx) * P.invT64;
-        Mh = zm + eta_d * (exp(ym - Ly) - exp(zm - Lz));
-    } else {
-        hidx = -1;
-    }
-    // read by the other workgroups of this launch: device-scope stores
-    double *rs = P.rowstat + (size_t)row * kRowStatWords;
-    st_f64(rs + 0, Lz);
-    st_f64(rs + 1, Ly);
-    st_f64(rs + 2, Mh);
-    st_f64(rs + 3, Lh);
-    st_f64(rs + 4, (double)hidx);
-    uint32_t acc = 0;
-    if (i < P.G) {
-        const long long k = bi * P.G + i;
-        float phd = 0.f, qd = 0.f;
-        if (x < 0 || x >= P.V) {
-            set_dev_err(P.dev_err, 1);
-        } else {
-            const double p = exp(zx - Lz);
-            const double q = exp(yx - Ly);
-            const double h = zx + eta_d * (q - p);
-            const double ph = (h - Mh < -2.302585092994046) ? p : exp(h - Lh);
-            const double u = clamp_uniform(P.u_accept[k], P.dev_err);
-            acc = (u * q < ph) ? 1u : 0u;
-            phd = (float)ph;
-            qd = (float)q;
-        }
-        P.accept[k] = (uint8_t)acc;
-        if (P.p_hat_draft)
-            P.p_hat_draft[k] = phd;
-        if (P.q_draft)
-            P.q_draft[k] = qd;
-    }
-    st_relaxed(P.row_info + (size_t)row * 2 + 1, acc);
-    P.row_ctr[(size_t)row * 16] = 0u; // arrivals of the row kernel, for the next call
-}
 
 // Barrier of a request's team: every wave's stores complete, one arrival
 // per workgroup, wait for `target` arrivals.  Returns false on timeout.
@@ -551,14 +594,108 @@ __device__ __forceinline__ void tail_parts(const double *parts, int We, const in
     __syncthreads();
 }
 
+// Partial sums exchanged between a request's workgroups as self-validating
+// words: a published sum x >= 0 is stored as the bits of x + 0.0 with the
+// sign bit flipped, which is never zero, and a word still zero has not been
+// published yet; so a reader polls the words themselves (one round trip, no
+// arrival counter).  The request's last workgroup to leave clears them.
+__device__ __forceinline__ uint64_t part_word(double x) {
+    return static_cast<uint64_t>(__double_as_longlong(x + 0.0)) ^ 0x8000000000000000ull;
+}
+__device__ __forceinline__ double part_value(uint64_t u) { return as_f64(u ^ 0x8000000000000000ull); }
+
+// As tail_parts, with each lane of wave 0 waiting for the words it sums to
+// be published; returns false (in every thread) when a wait exceeds the
+// bound.  Called by the whole workgroup.
+template <int NW>
+__device__ __forceinline__ bool tail_parts_poll(const double *parts, int We, const int (&word)[NW],
+                                                double *sh_lane /* 3*64*NW */, double *sh_out /* 3*NW */,
+                                                uint32_t *sh_flag, int w, double (&total)[NW], double (&pre0)[NW],
+                                                double (&pre1)[NW]) {
+    const int tid = threadIdx.x;
+    if (tid < 64) {
+        const int m = (We + 63) / 64;
+        const int k0 = tid * m, k1 = min(k0 + m, We);
+        double c[NW], e0[NW], e1[NW];
+#pragma unroll
+        for (int j = 0; j < NW; ++j)
+            c[j] = e0[j] = e1[j] = 0.0;
+        bool ok = true;
+        uint64_t t0 = 0;
+        for (int k = k0; k < k1 && ok; ++k) {
+#pragma unroll
+            for (int j = 0; j < NW; ++j) {
+                const uint64_t *a = reinterpret_cast<const uint64_t *>(parts + (size_t)k * kEmitWords + word[j]);
+                uint64_t u = ld_relaxed(a);
+                while (u == 0u && ok) {
+                    if (t0 == 0)
+                        t0 = wall_clock64();
+                    __builtin_amdgcn_s_sleep(1);
+                    u = ld_relaxed(a);
+                    if (u == 0u && wall_clock64() - t0 > kWaitLimitTicks)
+                        ok = false;
+                }
+                if (k == w)
+                    e0[j] = c[j];
+                c[j] += part_value(u);
+                if (k == w)
+                    e1[j] = c[j];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NW; ++j) {
+            sh_lane[(3 * j) * 64 + tid] = c[j];
+            sh_lane[(3 * j + 1) * 64 + tid] = e0[j];
+            sh_lane[(3 * j + 2) * 64 + tid] = e1[j];
+        }
+        const bool all_ok = __all(ok);
+        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (tid == 0) {
+            double t[NW], a0[NW], a1[NW];
+#pragma unroll
+            for (int j = 0; j < NW; ++j)
+                t[j] = a0[j] = a1[j] = 0.0;
+            const int lw = (w >= 0) ? w / m : -1;
+            for (int l = 0; l < 64; ++l) {
+#pragma unroll
+                for (int j = 0; j < NW; ++j) {
+                    if (l == lw) {
+                        a0[j] = t[j] + sh_lane[(3 * j + 1) * 64 + l];
+                        a1[j] = t[j] + sh_lane[(3 * j + 2) * 64 + l];
+                    }
+                    t[j] += sh_lane[(3 * j) * 64 + l];
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < NW; ++j) {
+                sh_out[3 * j] = t[j];
+                sh_out[3 * j + 1] = a0[j];
+                sh_out[3 * j + 2] = a1[j];
+            }
+            *sh_flag = all_ok ? 1u : 0u;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+        total[j] = sh_out[3 * j];
+        pre0[j] = sh_out[3 * j + 1];
+        pre1[j] = sh_out[3 * j + 2];
+    }
+    const bool ok = *sh_flag != 0u;
+    __syncthreads();
+    return ok;
+}
+
 template <int DT, int EPT>
-__global__ __launch_bounds__(kThreads) void rapid_tail_kernel(RapidParams P) {
-    __shared__ double lds_d[kWaves * 2];
+__global__ __launch_bounds__(kThreads, (EPT <= 8 ? 4 : 3)) void rapid_tail_kernel(RapidParams P) {
+    __shared__ double lds_d[kWaves * 5];
     __shared__ int lds_i[kWaves];
-    __shared__ double sh_lane[384];
-    __shared__ double sh_out[6];
+    __shared__ double sh_lane[3 * 64 * 5];
+    __shared__ double sh_out[3 * 5];
     __shared__ double sh_st[4];
     __shared__ double sh_scan[kWaves];
+    __shared__ double sh_rows[(kMaxDrafts + 1) * 6];
     __shared__ uint32_t sh_u[2];
     const int tid = threadIdx.x;
     const int We = P.We;
@@ -566,152 +703,145 @@ __global__ __launch_bounds__(kThreads) void rapid_tail_kernel(RapidParams P) {
     const int Pn = P.G + 1;
     if (blockIdx.x == 0 && tid == 0)
         P.ctl[0] = 0u; // ticket counter of the row kernel, for the next call
-    uint32_t *bar = P.req_ctr + (size_t)bi * 16 + 4;
     uint32_t *leave = P.req_ctr + (size_t)bi * 16 + 5;
     double *parts = P.emit + (size_t)bi * We * kEmitWords;
-    double *mine = parts + (size_t)w * kEmitWords;
-    uint32_t nbar = 0;
+    uint64_t *mine = reinterpret_cast<uint64_t *>(parts + (size_t)w * kEmitWords);
     bool ok = true;
 
-    // ---- phase 0: the request's rows ----
-    for (int r = w * kWaves + (tid >> 6); r < Pn; r += We * kWaves)
-        tail_row<DT>(P, (long long)bi * Pn + r);
-    ok = tail_sync(bar, ++nbar * (uint32_t)We, &sh_u[0]);
-
-    // ---- accept length and the emitting row ----
-    int n = P.G;
-    if (ok) {
-        if (tid < 64) {
-            int first = P.G;
-            for (int k = tid; k < P.G; k += 64)
-                if (ld_relaxed(P.row_info + ((size_t)bi * Pn + k) * 2 + 1) == 0u) {
-                    first = k;
-                    break;
-                }
-            first = wave_min_int(first);
-            if (tid == 0)
-                sh_u[1] = (uint32_t)first;
-        }
-        __syncthreads();
-        n = (int)sh_u[1];
-        if (w == 0 && tid == 0)
-            P.acc_len[bi] = n;
+    // ---- the request's rows: statistics and acceptance, in every
+    // workgroup (one wave per row; workgroup 0 also writes the outputs), so
+    // each finds the accept length and the emitting row without a barrier ----
+    for (int r0 = (tid >> 6) * 4; r0 < Pn; r0 += kWaves * 4) {
+        const int r = r0 + ((tid & 63) >> 4);
+        if (r < Pn) // whole 16-lane segments
+            tail_row<DT>(P, (long long)bi * Pn + r, w == 0, sh_rows + r * 6);
     }
+    __syncthreads();
+    if (tid == 0) {
+        int first = P.G;
+        for (int k = 0; k < P.G; ++k)
+            if (sh_rows[k * 6 + 5] == 0.0) {
+                first = k;
+                break;
+            }
+        sh_u[1] = (uint32_t)first;
+    }
+    __syncthreads();
+    const int n = (int)sh_u[1];
+    if (w == 0 && tid == 0)
+        P.acc_len[bi] = n;
     const long long row = (long long)bi * Pn + n;
     const size_t row_off = (size_t)row * (size_t)P.V;
     const bool resid = n < P.G;
-    const double *rs = P.rowstat + (size_t)row * kRowStatWords;
+    const double *rs = sh_rows + n * 6;
     const int v0 = (w * kThreads + tid) * EPT;
     const double invT = P.invT64, eta_d = P.eta_d;
+    const double Lz = rs[0], Ly = rs[1], Mr = rs[2];
 
-    // per element, kept across the phases: p', q', exp(h - Mhat)
-    double pc[EPT], qc[EPT], ec[EPT];
-    uint32_t prot = 0; // tail-protected elements (bit e)
-
-    // ---- phase 1: p', q' and the refined normalisers ----
     // z and y at the augmented argmax (for Mhat), fetched early by thread 0
     int hidx = -1;
     double zxh = 0.0, yxh = 0.0;
-    if (ok) {
-        if (tid == 0) {
-            hidx = (int)ld_f64(rs + 4);
-            if (resid && hidx >= 0 && hidx < P.V) {
-                zxh = (double)load_scalar<DT>(P.z, row_off + hidx) * invT;
-                yxh = (double)load_scalar<DT>(P.y, row_off + hidx) * invT;
-            }
+    if (tid == 0) {
+        hidx = (int)rs[4];
+        if (resid && hidx >= 0 && hidx < P.V) {
+            zxh = (double)load_scalar<DT>(P.z, row_off + hidx) * invT;
+            yxh = (double)load_scalar<DT>(P.y, row_off + hidx) * invT;
         }
-        const double Lz = ld_f64(rs + 0), Ly = ld_f64(rs + 1);
-        double s2[2] = {0.0, 0.0};
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-            pc[e] = 0.0;
-            qc[e] = 0.0;
-            ec[e] = 0.0;
-            const int v = v0 + e;
-            if (v < P.V) {
-                pc[e] = exp((double)load_scalar<DT>(P.z, row_off + v) * invT - Lz);
-                s2[0] += pc[e];
-                if (resid) {
-                    qc[e] = exp((double)load_scalar<DT>(P.y, row_off + v) * invT - Ly);
-                    s2[1] += qc[e];
-                }
-            }
-        }
-        block_sum<2>(s2, lds_d);
-        if (tid == 0) {
-            st_f64(mine + 3, s2[0]);
-            st_f64(mine + 4, resid ? s2[1] : 1.0);
-        }
-        ok = tail_sync(bar, ++nbar * (uint32_t)We, &sh_u[0]);
-    }
-    // refined L_z, L_y (as factors on p', q') and Mhat
-    double fz = 1.0, fy = 1.0, Mh = 0.0, Lz = 0.0, Ly = 0.0;
-    if (ok) {
-        double szy[2], unused0[2], unused1[2];
-        tail_parts<2>(parts, We, {3, 4}, sh_lane, sh_out, -1, szy, unused0, unused1);
-        const double sz = szy[0], sy = szy[1];
-        if (tid == 0) {
-            const double lz = ld_f64(rs + 0) + log(sz), ly = ld_f64(rs + 1) + log(sy);
-            double mh = ld_f64(rs + 2);
-            if (resid && hidx >= 0 && hidx < P.V)
-                mh = zxh + eta_d * (exp(yxh - ly) - exp(zxh - lz));
-            sh_st[0] = lz;
-            sh_st[1] = ly;
-            sh_st[2] = mh;
-            sh_st[3] = 1.0 / sz; // p = p' / sum p'  (exp(L_z,row - L_z) = 1/sz)
-        }
-        __syncthreads();
-        Lz = sh_st[0];
-        Ly = sh_st[1];
-        Mh = sh_st[2];
-        fz = sh_st[3];
-        fy = 1.0 / sy;
     }
 
-    // ---- phase 2 (residual rows): e = exp(h - Mhat) -> L_zhat ----
-    double fh = 0.0; // exp(Mhat - L_zhat)
-    if (ok && resid) {
+    // ---- phase 1: p', q', e' per element, kept; chunk sums ----
+    double pc[EPT], qc[EPT], ec[EPT];
+    float zc[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        pc[e] = qc[e] = ec[e] = 0.0;
+        zc[e] = 0.0f;
+    }
+    if (resid) {
+        double s5[5] = {0.0, 0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const int v = v0 + e;
+            if (v < P.V) {
+                zc[e] = load_scalar<DT>(P.z, row_off + v);
+                const double zs = (double)zc[e] * invT;
+                pc[e] = exp(zs - Lz);
+                qc[e] = exp((double)load_scalar<DT>(P.y, row_off + v) * invT - Ly);
+                ec[e] = exp(zs + eta_d * (qc[e] - pc[e]) - Mr);
+                s5[0] += pc[e];
+                s5[1] += qc[e];
+                s5[2] += ec[e];
+                s5[3] += ec[e] * qc[e];
+                s5[4] += ec[e] * pc[e];
+            }
+        }
+        block_sum<5>(s5, lds_d);
+        if (tid == 0) {
+            st_relaxed(mine + 3, part_word(s5[0]));
+            st_relaxed(mine + 4, part_word(s5[1]));
+            st_relaxed(mine + 2, part_word(s5[2]));
+            st_relaxed(mine + 5, part_word(s5[3]));
+            st_relaxed(mine + 6, part_word(s5[4]));
+        }
+    } else {
         double s1[1] = {0.0};
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
             const int v = v0 + e;
             if (v < P.V) {
-                const double p = pc[e] * fz, q = qc[e] * fy;
-                const double h = (double)load_scalar<DT>(P.z, row_off + v) * invT + eta_d * (q - p);
-                ec[e] = exp(h - Mh);
-                if (h - Mh < -2.302585092994046)
-                    prot |= 1u << e;
-                s1[0] += ec[e];
+                pc[e] = exp((double)load_scalar<DT>(P.z, row_off + v) * invT - Lz);
+                s1[0] += pc[e];
             }
         }
         block_sum<1>(s1, lds_d);
         if (tid == 0)
-            st_f64(mine + 2, s1[0]);
-        ok = tail_sync(bar, ++nbar * (uint32_t)We, &sh_u[0]);
-        if (ok) {
-            double sh1[1], unused0[1], unused1[1];
-            tail_parts<1>(parts, We, {2}, sh_lane, sh_out, -1, sh1, unused0, unused1);
-            fh = 1.0 / sh1[0];
-        }
+            st_relaxed(mine + 3, part_word(s1[0]));
     }
 
-    // weights of element e: residual max(p - phat, p - q, 0), or p
+    // ---- phase 2 (residual rows): refined factors, residual sums ----
+    double fz = 1.0, fy = 1.0, Mh = 0.0, iE = 0.0;
+    if (resid) {
+        double t5[5], unused0[5], unused1[5];
+        ok = tail_parts_poll<5>(parts, We, {3, 4, 2, 5, 6}, sh_lane, sh_out, &sh_u[0], -1, t5, unused0, unused1);
+        if (tid == 0) {
+            const double gz = 1.0 / t5[0], gy = 1.0 / t5[1];
+            double mh = Mr;
+            if (hidx >= 0 && hidx < P.V)
+                mh = zxh + eta_d * (exp(yxh - Ly) * gy - exp(zxh - Lz) * gz);
+            // sum of exp(h - M) over the row with h = h' + d, to first order in d
+            const double E = t5[2] + eta_d * ((gy - 1.0) * t5[3] - (gz - 1.0) * t5[4]);
+            sh_st[0] = gz;
+            sh_st[1] = gy;
+            sh_st[2] = mh;
+            sh_st[3] = 1.0 / E;
+        }
+        __syncthreads();
+        fz = sh_st[0];
+        fy = sh_st[1];
+        Mh = sh_st[2];
+        iE = sh_st[3];
+    }
+
+    // weights of element e: residual max(p - phat, p - q, 0), or p' for a
+    // bonus row (the draw normalises by the sum)
     auto weights = [&](int e, double &r, double &p) {
-        p = pc[e] * fz;
         if (!resid) {
+            p = pc[e];
             r = 0.0;
             return;
         }
+        p = pc[e] * fz;
         const double q = qc[e] * fy;
-        const double ph = ((prot >> e) & 1u) ? p : ec[e] * fh;
-        double d = p - ph;
-        if (p - q > d)
-            d = p - q;
-        r = d > 0.0 ? d : 0.0;
+        const double d = eta_d * (qc[e] * (fy - 1.0) - pc[e] * (fz - 1.0));
+        const double h = (double)zc[e] * invT + eta_d * (qc[e] - pc[e]) + d;
+        const double ph = (h - Mh < -2.302585092994046) ? p : ec[e] * (1.0 + d * (1.0 + 0.5 * d)) * iE;
+        double dd = p - ph;
+        if (p - q > dd)
+            dd = p - q;
+        r = dd > 0.0 ? dd : 0.0;
     };
 
-    // ---- phase 3: residual and target sums ----
-    if (ok) {
+    if (ok && resid) {
         double s2[2] = {0.0, 0.0};
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
@@ -724,17 +854,29 @@ __global__ __launch_bounds__(kThreads) void rapid_tail_kernel(RapidParams P) {
         }
         block_sum<2>(s2, lds_d);
         if (tid == 0) {
-            st_f64(mine + 0, s2[0]);
-            st_f64(mine + 1, s2[1]);
+            st_relaxed(mine + 0, part_word(s2[0]));
+            st_relaxed(mine + 1, part_word(s2[1]));
         }
-        ok = tail_sync(bar, ++nbar * (uint32_t)We, &sh_u[0]);
     }
 
-    // ---- phase 4: the draw ----
+    // ---- phase 3: the draw ----
+    // residual (word 0) and target (word 1) sums with this chunk's interval;
+    // a bonus row's target sums are word 3
+    double St[2] = {0.0, 0.0}, e0[2] = {0.0, 0.0}, e1[2] = {0.0, 0.0};
     if (ok) {
-        // residual (word 0) and target (word 1) sums with this chunk's interval
-        double St[2], e0[2], e1[2];
-        tail_parts<2>(parts, We, {0, 1}, sh_lane, sh_out, w, St, e0, e1);
+        if (resid) {
+            ok = tail_parts_poll<2>(parts, We, {0, 1}, sh_lane, sh_out, &sh_u[0], w, St, e0, e1);
+        } else {
+            double t1[1], a0[1], a1[1];
+            ok = tail_parts_poll<1>(parts, We, {3}, sh_lane, sh_out, &sh_u[0], w, t1, a0, a1);
+            St[0] = 0.0;
+            St[1] = t1[0];
+            e0[0] = e1[0] = 0.0;
+            e0[1] = a0[0];
+            e1[1] = a1[0];
+        }
+    }
+    if (ok) {
         const bool use_r = resid && (St[0] > 0.0);
         const double S = use_r ? St[0] : St[1];
         const double pre0 = use_r ? e0[0] : e0[1], pre1 = use_r ? e1[0] : e1[1];
@@ -804,18 +946,19 @@ __global__ __launch_bounds__(kThreads) void rapid_tail_kernel(RapidParams P) {
     }
     if (!ok && tid == 0)
         set_dev_err(P.dev_err, 4);
-    (void)Lz;
-    (void)Ly;
 
-    // the request's last workgroup to leave returns its counters to zero
-    wait_stores_complete();
+    // the request's last workgroup to leave (every other one has read all
+    // the partials it needs) clears the partial words and the counter
     __syncthreads();
-    if (tid == 0) {
-        const uint32_t left = __hip_atomic_fetch_add(leave, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (left == (uint32_t)We - 1u) {
-            st_relaxed(bar, 0u);
+    if (tid == 0)
+        sh_u[1] = publish_add(leave, 1u) == (uint32_t)We - 1u ? 1u : 0u;
+    __syncthreads();
+    if (sh_u[1] != 0u) {
+        uint64_t *all = reinterpret_cast<uint64_t *>(parts);
+        for (int k = tid; k < We * kEmitWords; k += kThreads)
+            st_relaxed(all + k, 0ull);
+        if (tid == 0)
             st_relaxed(leave, 0u);
-        }
     }
 }
 

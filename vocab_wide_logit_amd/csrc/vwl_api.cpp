@@ -162,6 +162,7 @@ bool make_plan(int mode, int dt, long long R, int V, Plan &plan, int ds = 0, int
 bool finite_f(float x) { return std::isfinite(x); }
 
 static_assert(VWL_RAPID_MAX_V == kRapidMaxV, "RAPID vocabulary limit out of step with the tail geometry");
+static_assert(VWL_MAX_K == kMaxDrafts, "draft limit out of step with the tail's per-row slots");
 
 // Vectors per member: the widest row body (no head) split evenly over W.
 int member_chunk(int V, int dt, int W) {

@@ -38,6 +38,7 @@ constexpr int kRecWords = 8;
 constexpr int kEmitMaxChunks = 512; // tail workgroups per request (at most)
 constexpr int kRapidMaxV = kThreads * 16 * kEmitMaxChunks; // largest RAPID vocabulary
 constexpr int kRowStatWords = 8;
+constexpr int kMaxDrafts = 63; // drafts per request (the API's limit)
 constexpr int kEmitWords = 8;
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }

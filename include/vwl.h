@@ -66,10 +66,20 @@ typedef enum {
     VWL_ERR_WORKSPACE = 5, /* workspace smaller than the query returns */
     VWL_ERR_HIP = 6,       /* a HIP runtime call or kernel launch failed */
     VWL_ERR_ALIGN = 7,     /* a pointer is not aligned as documented */
-    VWL_ERR_SCRATCH = 8    /* asym_verify_noalloc: the shape needs more than its static scratch */
+    VWL_ERR_SCRATCH = 8,   /* asym_verify_noalloc: the shape needs more than its static scratch */
+    VWL_STATUS_INT_MIN_ = -2147483647 - 1, /* not codes: they give the enum the range of an int */
+    VWL_STATUS_INT_MAX_ = 2147483647
 } vwl_status;
 
-typedef enum { VWL_F32 = 0, VWL_BF16 = 1 } vwl_dtype;
+/* Logit storage.  Every enum of this header spans the whole int range, so
+ * any int a C caller passes is a value of the type (an unknown one is
+ * refused with a status, never undefined behaviour). */
+typedef enum {
+    VWL_F32 = 0,
+    VWL_BF16 = 1,
+    VWL_DTYPE_INT_MIN_ = -2147483647 - 1,
+    VWL_DTYPE_INT_MAX_ = 2147483647
+} vwl_dtype;
 
 #define VWL_DEVERR_DRAFT 1
 #define VWL_DEVERR_UNIFORM 2
@@ -78,8 +88,9 @@ typedef enum { VWL_F32 = 0, VWL_BF16 = 1 } vwl_dtype;
 
 #define VWL_MAX_K 63 /* drafts per request, both methods */
 
-/* Human-readable name of a status code (static storage). */
-const char *vwl_status_string(vwl_status s);
+/* Human-readable name of a status code (static storage); any int is
+ * accepted, values that are no vwl_status give "unknown vwl_status". */
+const char *vwl_status_string(int status);
 
 /* Library version as an integer: major*10000 + minor*100 + patch. */
 int vwl_version(void);
@@ -177,8 +188,14 @@ vwl_status asym_verify_noalloc(const void *a, const void *b, const void *t,
  * VWL_GATE_FIXED and VWL_DELTA_T_MINUS_B.  An unknown enum value returns
  * VWL_ERR_PARAM.
  * --------------------------------------------------------------------------- */
-typedef enum { VWL_DELTA_A_MINUS_B = 0, VWL_DELTA_A = 1, VWL_DELTA_T_MINUS_B = 2 } vwl_delta_source;
-typedef enum { VWL_GATE_CDA = 0, VWL_GATE_FIXED = 1 } vwl_gate;
+typedef enum {
+    VWL_DELTA_A_MINUS_B = 0,
+    VWL_DELTA_A = 1,
+    VWL_DELTA_T_MINUS_B = 2,
+    VWL_DELTA_INT_MIN_ = -2147483647 - 1,
+    VWL_DELTA_INT_MAX_ = 2147483647
+} vwl_delta_source;
+typedef enum { VWL_GATE_CDA = 0, VWL_GATE_FIXED = 1, VWL_GATE_INT_MIN_ = -2147483647 - 1, VWL_GATE_INT_MAX_ = 2147483647 } vwl_gate;
 
 vwl_status asym_verify_variant(const void *a, const void *b, const void *t,
                                const int32_t *draft,

@@ -309,3 +309,30 @@ def test_wide_disagreement(vwl, dtype):
     x.b = W._to_dtype(x.a.astype(np.float64) + shift, dtype)
     dev, ora, rep = check(vwl, x, label="wide disagreement")
     assert np.all(ora.D > 0.05)
+
+
+def test_beside_a_running_kernel(vwl):
+    """asym_verify launched while a chain of large GEMMs runs on a second
+    stream of the same (default) priority.  The row kernel's workgroups then
+    start only as the GEMM's workgroups retire, so its teams fill gradually;
+    tickets are taken in start order, so every started member's team has all
+    its earlier members started, and a partial team waits only for members
+    that start once some workgroup retires.  Parity, dev_err == 0, and the
+    GEMM's result is unaffected."""
+    import torch
+    x = W.batched_asym()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    A = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16, generator=g)
+    Bm = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16, generator=g)
+    ref = (A[:64].float() @ Bm.float()).cpu()
+    torch.cuda.synchronize()
+    s2 = torch.cuda.Stream()
+    with torch.cuda.stream(s2):
+        outs = [A @ Bm for _ in range(6)]
+    _say("GEMM chain queued on a second stream")
+    dev, ora, rep = check(vwl, x, label="beside a GEMM chain")
+    torch.cuda.synchronize()
+    assert rep.checked == x.B
+    for o in outs:
+        np.testing.assert_allclose(o[:64].float().cpu().numpy(), ref.numpy(), rtol=2e-2, atol=2.0)

@@ -215,8 +215,8 @@ static vwl_status scratch_for_device(hipStream_t stream, void **out) {
 
 extern "C" {
 
-const char *vwl_status_string(vwl_status s) {
-    switch (s) {
+const char *vwl_status_string(int status) {
+    switch (status) { // an int: a C caller may pass any value
     case VWL_OK: return "VWL_OK";
     case VWL_ERR_NULL: return "VWL_ERR_NULL: a required pointer is null";
     case VWL_ERR_SHAPE: return "VWL_ERR_SHAPE: B, K/G or V out of range";

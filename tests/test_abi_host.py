@@ -352,3 +352,19 @@ def test_divergence_polynomial_constants():
     share = (p * np.log(2 * p / (p + q)) + q * np.log(2 * q / (p + q))) / 2
     psi = np.cosh(xs / 2) * (xs * np.tanh(xs / 2) - 2 * np.log(np.cosh(xs / 2)))
     np.testing.assert_allclose(np.sqrt(p * q) * psi / 2, share, rtol=1e-9, atol=1e-15)
+
+
+def test_binding_drops_cached_workspaces_after_a_timeout():
+    """The binding's workspace cache: drop_workspaces() empties it, and
+    check_dev_err() drops it exactly when the timeout bit is set (host-side
+    logic only; the tensors here live on the CPU)."""
+    import torch
+    import vocab_wide_logit_amd as vwl
+    vwl.drop_workspaces()
+    vwl._ws_cache[("probe", 1)] = torch.zeros(4, dtype=torch.uint8)
+    assert vwl.check_dev_err(torch.tensor([vwl.VWL_DEVERR_DRAFT | vwl.VWL_DEVERR_UNIFORM], dtype=torch.int32)) == 3
+    assert len(vwl._ws_cache) == 1
+    assert vwl.check_dev_err(torch.tensor([vwl.VWL_DEVERR_TIMEOUT], dtype=torch.int32)) == 4
+    assert len(vwl._ws_cache) == 0
+    vwl._ws_cache[("probe", 2)] = torch.zeros(4, dtype=torch.uint8)
+    assert vwl.drop_workspaces() == 1 and not vwl._ws_cache

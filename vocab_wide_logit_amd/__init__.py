@@ -178,9 +178,38 @@ def _dev_tensor(x: torch.Tensor, name: str, dtype=None) -> torch.Tensor:
 
 
 # Workspace cache: one zero-filled buffer per (device, stream, mode, shape).
-# The kernels leave it zero-filled after every completed call.
+# The kernels leave it ready for the next call after every completed call.
+# A call that ends with the timeout bit (VWL_DEVERR_TIMEOUT, 4) in dev_err
+# leaves its workspace undefined: the caller drops the cached buffers with
+# drop_workspaces() (or passes a fresh workspace) before the next call.  The
+# binding does not look at dev_err itself, since reading it waits for the
+# device.
 _ws_cache: dict = {}
 _ws_lock = threading.Lock()
+
+VWL_DEVERR_DRAFT = 1
+VWL_DEVERR_UNIFORM = 2
+VWL_DEVERR_TIMEOUT = 4
+VWL_DEVERR_MAP = 8
+
+
+def drop_workspaces() -> int:
+    """Forget every cached workspace (the next calls allocate zero-filled
+    ones); returns how many were dropped.  Needed after a call whose dev_err
+    has the timeout bit, whose workspace is then undefined."""
+    with _ws_lock:
+        n = len(_ws_cache)
+        _ws_cache.clear()
+    return n
+
+
+def check_dev_err(dev_err: torch.Tensor) -> int:
+    """Read a call's dev_err (waits for the device), drop the cached
+    workspaces when it carries the timeout bit, and return its value."""
+    v = int(dev_err.reshape(-1)[0].item())
+    if v & VWL_DEVERR_TIMEOUT:
+        drop_workspaces()
+    return v
 
 
 def _workspace(mode: int, B: int, K: int, V: int, dt: int, device, stream) -> torch.Tensor:

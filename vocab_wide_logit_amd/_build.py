@@ -16,7 +16,7 @@ BENCH_LIB = os.path.join(LIBDIR, "libvwl_bench.so")
 BENCH_SOURCES = ["stream_ref.hip"]
 SOURCES = ["asym_ab.hip", "asym_a.hip", "asym_tb.hip", "pair_pass.hip", "lmhead.hip", "rapid.hip",
            "vwl_api.cpp"]
-HEADERS = ["asym_kernels.hpp", "vwl_device.hpp", "vwl_internal.hpp"]
+HEADERS = ["asym_kernels.hpp", "vwl_device.hpp", "vwl_internal.hpp", "vwl_stage.hpp"]
 
 ARCH = os.environ.get("VWL_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

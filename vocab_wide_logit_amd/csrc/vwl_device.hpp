@@ -323,12 +323,28 @@ __device__ __forceinline__ void quad_sum_finish(double (&x)[N], const double *ld
     wave_sum_last_n<N>(x);
 }
 
+// Workgroup barrier for LDS data only: the wave's LDS operations complete,
+// then s_barrier.  Unlike __syncthreads() it does not wait for the wave's
+// global loads, so staging loads in flight (direct global -> LDS loads of a
+// later row) stay in flight across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <bool LDS_ONLY>
+__device__ __forceinline__ void wg_barrier() {
+    if constexpr (LDS_ONLY)
+        lds_barrier();
+    else
+        __syncthreads();
+}
+
 // Workgroup reductions: wave results go through LDS and every thread combines
 // the WAVES values in the same order, so all threads hold the same result.
 // With TRAIL = false the closing barrier is left out: the caller guarantees
 // that another workgroup barrier separates the reads of `lds` from its next
-// write.  WAVES is the workgroup's wave count (kWaves unless stated).
-template <int N, bool TRAIL = true, int WAVES = kWaves>
+// write.  WAVES is the workgroup's wave count (kWaves unless stated).  With
+// LDS_ONLY the barriers are LDS-only (lds_barrier), for callers with staging
+// loads in flight.
+template <int N, bool TRAIL = true, int WAVES = kWaves, bool LDS_ONLY = false>
 __device__ __forceinline__ void block_max(float (&x)[N], float *lds /* WAVES*N */) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     float m[N];
@@ -341,7 +357,7 @@ __device__ __forceinline__ void block_max(float (&x)[N], float *lds /* WAVES*N *
         for (int i = 0; i < N; ++i)
             lds[wave * N + i] = m[i];
     }
-    __syncthreads();
+    wg_barrier<LDS_ONLY>();
 #pragma unroll
     for (int i = 0; i < N; ++i) {
         float r = lds[i];
@@ -351,10 +367,10 @@ __device__ __forceinline__ void block_max(float (&x)[N], float *lds /* WAVES*N *
         x[i] = r;
     }
     if (TRAIL)
-        __syncthreads();
+        wg_barrier<LDS_ONLY>();
 }
 
-template <int N, bool TRAIL = true, int WAVES = kWaves>
+template <int N, bool TRAIL = true, int WAVES = kWaves, bool LDS_ONLY = false>
 __device__ __forceinline__ void block_sum(double (&x)[N], double *lds /* WAVES*N */) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     double m[N];
@@ -367,7 +383,7 @@ __device__ __forceinline__ void block_sum(double (&x)[N], double *lds /* WAVES*N
         for (int i = 0; i < N; ++i)
             lds[wave * N + i] = m[i];
     }
-    __syncthreads();
+    wg_barrier<LDS_ONLY>();
 #pragma unroll
     for (int i = 0; i < N; ++i) {
         double r = lds[i];
@@ -377,7 +393,7 @@ __device__ __forceinline__ void block_sum(double (&x)[N], double *lds /* WAVES*N
         x[i] = r;
     }
     if (TRAIL)
-        __syncthreads();
+        wg_barrier<LDS_ONLY>();
 }
 
 // Sums of N doubles and the minimum of one int in a single LDS round.
@@ -415,17 +431,18 @@ __device__ __forceinline__ void block_sum_min(double (&x)[N], int &imin, double 
         __syncthreads();
 }
 
+template <bool LDS_ONLY = false>
 __device__ __forceinline__ int block_min_int(int x, int *lds /* kWaves */) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int m = wave_min_last(x);
     if (lane == 63)
         lds[wave] = m;
-    __syncthreads();
+    wg_barrier<LDS_ONLY>();
     int r = lds[0];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w)
         r = min(r, lds[w]);
-    __syncthreads();
+    wg_barrier<LDS_ONLY>();
     return r;
 }
 

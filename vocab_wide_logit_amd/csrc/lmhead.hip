@@ -27,7 +27,8 @@ namespace vwl {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kLmRows = 64;  // rows per workgroup (4 MFMA row blocks of 16)
+constexpr int kLmRows = kLmRowTile; // rows per workgroup
+constexpr int kLmM = kLmRows / 16;   // MFMA row blocks of 16
 constexpr int kLmCols = 128; // vocabulary per tile (32 per wave, 2 MFMA column blocks)
 constexpr int kLmKB = 64;    // k per LDS stage (2 MFMA k-steps of 32)
 
@@ -42,25 +43,48 @@ struct LmStage {
 
 __device__ __forceinline__ int lm_slot(int r, int c) { return r * 8 + (c ^ (r & 7)); }
 
-// Stage rows [row0, row0 + NR) (rows past max_row repeat it) by k
-// [k0, k0 + 64) of a row-major bf16 matrix with H columns.  Lane L of a wave
-// instruction fills LDS slot base + L, so each wave instruction reads 8 whole
-// 128-byte row pieces.
+// Staging of rows [row0, row0 + NR) (rows past max_row repeat it) of a
+// row-major bf16 matrix with H columns, one 64-wide k block at a time.
+// Instruction j of the block (issued by wave j mod 4) fills LDS slots
+// 64 j .. 64 j + 63, so each instruction reads 8 whole 128-byte row pieces.
+// The lane's byte offsets from the block's base are the same for every k
+// block of a tile, so they are formed once per tile; per block the loads
+// are a scalar base plus those offsets, with no vector arithmetic.
 template <int NR>
-__device__ __forceinline__ void lm_stage(uint4 *dst, const uint16_t *M, long long row0, long long max_row, int H,
-                                         int k0) {
+struct LmLoads {
+    static constexpr int kN = NR * 8 / 64 / kWaves; // instructions per wave
+    static_assert(NR * 8 % (64 * kWaves) == 0, "every wave issues the same number of stage loads");
+    uint32_t off[kN]; // lane byte offsets from the block base
+    uint32_t lds[kN]; // LDS destinations (wave-uniform)
+};
+
+template <int NR>
+__device__ __forceinline__ void lm_loads(LmLoads<NR> &L, uint4 *dst, long long row0, long long max_row, int H) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    constexpr int kInstr = NR * 8 / 64;
-    for (int j = wave; j < kInstr; j += kWaves) {
+#pragma unroll
+    for (int i = 0; i < LmLoads<NR>::kN; ++i) {
+        const int j = wave + i * kWaves;
         const int p = j * 64 + lane;
         const int r = p >> 3, slot = p & 7;
         const int c = slot ^ (r & 7);
-        long long row = row0 + r;
-        if (row > max_row)
-            row = max_row;
-        g2lds16(reinterpret_cast<const uint4 *>(M + (size_t)row * (size_t)H + k0 + 8 * c), dst + j * 64);
+        const long long row = row0 + r > max_row ? max_row : row0 + r;
+        L.off[i] = (uint32_t)(((row - row0) * (long long)H + 8 * c) * 2);
+        L.lds[i] = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(dst + j * 64));
     }
+}
+
+// Issue one k block: `base` is the wave-uniform address of (row0, k0).  The
+// loads are inline assembly (an SGPR base plus the lane's offset; `s_nop 4`
+// gives the wait states the hardware needs after M0 or the base is
+// written), so the compiler does not track them: lm_gemm waits for them
+// explicitly before its barrier.
+template <int NR>
+__device__ __forceinline__ void lm_issue(const LmLoads<NR> &L, const uint16_t *base) {
+#pragma unroll
+    for (int i = 0; i < LmLoads<NR>::kN; ++i)
+        asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(L.off[i]), "s"(base), "{m0}"(L.lds[i])
+                     : "memory");
 }
 
 __device__ __forceinline__ bf16x8_t lm_frag(const uint4 *tile, int r, int c) {
@@ -96,22 +120,34 @@ __device__ __forceinline__ int row16_min_int(int x) {
 template <bool TWO>
 __device__ __forceinline__ void lm_gemm(LmStage &st, const uint16_t *h0, const uint16_t *h1, const uint16_t *W,
                                         long long row0, long long R, long long vt0, int V, int H,
-                                        f32x4_t (&acc0)[4][2], f32x4_t (&acc1)[4][2]) {
+                                        f32x4_t (&acc0)[kLmM][2], f32x4_t (&acc1)[kLmM][2]) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < kLmM; ++m)
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
             acc0[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             acc1[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
+    LmLoads<kLmRows> la;
+    LmLoads<kLmCols> lw;
+    lm_loads(la, st.a, row0, R - 1, H);
+    lm_loads(lw, st.w, vt0, V - 1, H);
+    const uint32_t lds_b = (uint32_t)(reinterpret_cast<uintptr_t>(st.b) - reinterpret_cast<uintptr_t>(st.a));
+    const uint16_t *pa = h0 + row0 * H, *pw = W + vt0 * H;
+    const uint16_t *pb = TWO ? h1 + row0 * H : nullptr;
     for (int k0 = 0; k0 < H; k0 += kLmKB) {
         __syncthreads(); // every wave is done with the previous stage
-        lm_stage<kLmRows>(st.a, h0, row0, R - 1, H, k0);
-        if (TWO)
-            lm_stage<kLmRows>(st.b, h1, row0, R - 1, H, k0);
-        lm_stage<kLmCols>(st.w, W, vt0, V - 1, H, k0);
+        lm_issue(la, pa + k0);
+        if (TWO) {
+            LmLoads<kLmRows> lb = la; // same rows and slots, the second view's LDS tile
+#pragma unroll
+            for (int i = 0; i < LmLoads<kLmRows>::kN; ++i)
+                lb.lds[i] += lds_b;
+            lm_issue(lb, pb + k0);
+        }
+        lm_issue(lw, pw + k0);
         __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
 #pragma unroll 1
@@ -122,7 +158,7 @@ __device__ __forceinline__ void lm_gemm(LmStage &st, const uint16_t *h0, const u
             for (int n = 0; n < 2; ++n)
                 fw[n] = lm_frag(st.w, 32 * wave + 16 * n + (lane & 15), c);
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
+            for (int m = 0; m < kLmM; ++m) {
                 const bf16x8_t f0 = lm_frag(st.a, 16 * m + (lane & 15), c);
 #pragma unroll
                 for (int n = 0; n < 2; ++n)
@@ -156,11 +192,11 @@ struct LmScratch {
 // reference and the fp32 sum of 2^(x*log2e - ref) over the wave's 32 columns
 // (identical in the 16 lanes of a DPP row; lane 0 of the row writes).
 // Invalid columns count as -inf.
-__device__ __forceinline__ void lm_tile_stats(LmScratch &sc, int k, const f32x4_t (&x)[4][2], const bool (&cv)[2]) {
+__device__ __forceinline__ void lm_tile_stats(LmScratch &sc, int k, const f32x4_t (&x)[kLmM][2], const bool (&cv)[2]) {
     const float NEG_INF = -__builtin_inff();
     const int wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < kLmM; ++m)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const float x0 = cv[0] ? x[m][0][j] : NEG_INF, x1 = cv[1] ? x[m][1][j] : NEG_INF;
@@ -224,22 +260,22 @@ __global__ __launch_bounds__(kThreads, 3) void lmhead_kernel(LmheadParams P) {
 #pragma unroll
         for (int n = 0; n < 2; ++n)
             cv[n] = vt0 + lm_col(n) < v_end;
-        f32x4_t xa[4][2], xb[4][2];
+        f32x4_t xa[kLmM][2], xb[kLmM][2];
         lm_gemm<true>(st, P.ha, P.hb, P.Wd, row0, P.R, vt0, P.V, P.Hd, xa, xb);
         if (PASS == 1) {
             lm_tile_stats(sc, 0, xa, cv);
             lm_tile_stats(sc, 1, xb, cv);
             // the context gain, kept while t is formed
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
+            for (int m = 0; m < kLmM; ++m)
 #pragma unroll
                 for (int n = 0; n < 2; ++n)
                     xa[m][n] = xa[m][n] - xb[m][n];
-            f32x4_t xt[4][2], unused[4][2];
+            f32x4_t xt[kLmM][2], unused[kLmM][2];
             lm_gemm<false>(st, P.ht, nullptr, P.Wt, row0, P.R, vt0, P.V, P.Ht, xt, unused);
             lm_tile_stats(sc, 2, xt, cv);
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
+            for (int m = 0; m < kLmM; ++m)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     // fused score t + beta*(a - b), its maximum and lowest column
@@ -271,7 +307,7 @@ __global__ __launch_bounds__(kThreads, 3) void lmhead_kernel(LmheadParams P) {
         } else {
             // JSD terms of the block against the row's log-sum-exps
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
+            for (int m = 0; m < kLmM; ++m)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int r = lm_row(m, j);

@@ -635,7 +635,7 @@ vwl_status asym_verify_xfam(const void *a, const void *b, int Vd, const void *t,
     return launch_xfam((int)dt, plan, p, stream, g_phase_event.load()) == hipSuccess ? VWL_OK : VWL_ERR_HIP;
 }
 
-// LM-head pass geometry: row tiles of 64 and vocabulary ranges (multiples of
+// LM-head pass geometry: row tiles of kLmRowTile and vocabulary ranges (multiples of
 // 128 tokens) for about 1536 workgroups; depends on the shape only.
 struct LmGeom {
     int RT, S, range;
@@ -648,7 +648,7 @@ static bool lm_geometry(int B, int K, int V, int Hd, int Ht, LmGeom &g) {
     if (!shape_ok(B, K, V) || Hd < 64 || Ht < 64 || Hd % 64 || Ht % 64)
         return false;
     const long long R = (long long)B * (K + 1);
-    const long long RT = (R + 63) / 64;
+    const long long RT = (R + kLmRowTile - 1) / kLmRowTile;
     if (RT > (1LL << 24))
         return false;
     const long long tiles = ((long long)V + 127) / 128;

@@ -166,6 +166,8 @@ struct LmheadParams {
     uint64_t *rec;    // [R][S][8], the row kernel's record layout
     double *rowstat;  // [R][2] L_a, L_b (log2 units)
 };
+// Rows per workgroup of the LM-head pass (MFMA row blocks of 16).
+constexpr int kLmRowTile = 64;
 hipError_t launch_lmhead(const LmheadParams &p, hipStream_t s, hipEvent_t after_rows);
 int lmhead_blocks_per_cu();
 

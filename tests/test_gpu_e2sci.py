@@ -205,3 +205,25 @@ def test_stabilisers_over_windows(vwl):
         assert rep.excluded <= 1
         held += int(np.sum(ora.age > 0))
     assert held > 0
+
+
+def test_preallocated_outputs(vwl):
+    """``out=`` buffers: two calls in a row into the same buffers give the
+    results of calls that allocate their own, and the returned tensors are
+    the buffers themselves."""
+    import torch
+    x = W.gen_e2sci(3, 8, 20011, "bf16", seed=77)
+    prm = vwl.E2sciParams()
+    y = vwl.to_device_logits(x.y, x.dtype)
+    z = vwl.to_device_logits(x.z, x.dtype)
+    mk = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+    buf = vwl.e2sci_out(x.B, x.W, "cuda")
+    for _ in range(2):
+        ref = vwl.e2sci_verify(y, z, mk(x.T), mk(x.omega), mk(x.r_hat), prm)
+        got = vwl.e2sci_verify(y, z, mk(x.T), mk(x.omega), mk(x.r_hat), prm, out=buf)
+        torch.cuda.synchronize()
+        assert got.D.data_ptr() == buf.D.data_ptr() and got.dev_err.data_ptr() == buf.dev_err.data_ptr()
+        for k in ("D", "accept", "accept_len", "T_next", "r_hat", "dev_err"):
+            assert torch.equal(getattr(ref, k), getattr(got, k)), k
+    with pytest.raises(ValueError):
+        vwl.e2sci_verify(y, z, mk(x.T), mk(x.omega), mk(x.r_hat), prm, out=vwl.e2sci_out(x.B, x.W + 1, "cuda"))

@@ -495,16 +495,34 @@ def e2sci_plan_info(B: int, W: int, V: int, dtype: torch.dtype) -> dict:
             "threads": out[4], "rows": out[5]}
 
 
+class E2sciBuffers(NamedTuple):
+    """Preallocated per-call outputs of ``e2sci_verify(..., out=...)``."""
+    D: torch.Tensor           # [B, W] float32
+    accept: torch.Tensor      # [B, W] uint8
+    accept_len: torch.Tensor  # [B] int32
+    dev_err: torch.Tensor     # [1] int32, bits OR-ed in across calls
+
+
+def e2sci_out(B: int, W: int, device) -> E2sciBuffers:
+    """Preallocated outputs for ``e2sci_verify(..., out=...)``."""
+    kw = dict(device=device)
+    return E2sciBuffers(torch.empty(B, W, dtype=torch.float32, **kw), torch.empty(B, W, dtype=torch.uint8, **kw),
+                        torch.empty(B, dtype=torch.int32, **kw), torch.zeros(1, dtype=torch.int32, **kw))
+
+
 def e2sci_verify(y: torch.Tensor, z: torch.Tensor, T: torch.Tensor, omega: torch.Tensor,
                  r_hat: torch.Tensor, params: Optional[E2sciParams] = None, *,
                  age: Optional[torch.Tensor] = None,
-                 T_out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> E2sciOut:
+                 T_out: Optional[torch.Tensor] = None, out: Optional[E2sciBuffers] = None,
+                 workspace: Optional[torch.Tensor] = None) -> E2sciOut:
     """E2-SCI adaptive JSD acceptance of one window per request on the
     current stream.  y: drafter logits, z: target logits, [B, W, V];
     T, omega, r_hat: [B] float32 device tensors (r_hat is updated in place);
     age: [B] int32 device tensor of the stabilisers' window count, updated in
     place (needed when params.min_refresh > 1); the next thresholds go to
-    T_out (a new tensor when None; pass T itself to update in place)."""
+    T_out (a new tensor when None; pass T itself to update in place).  With
+    ``out`` (from ``e2sci_out``) the call allocates nothing once the
+    workspace is cached; its dev_err keeps the bits of earlier calls."""
     lib = load_library()
     _dev_tensor(y, "y")
     dt = _dt(y)
@@ -524,11 +542,16 @@ def e2sci_verify(y: torch.Tensor, z: torch.Tensor, T: torch.Tensor, omega: torch
         if tuple(age.shape) != (B,):
             raise ValueError("age must be [B]")
     params = params if params is not None else E2sciParams()
-    kw = dict(device=y.device)
-    D = torch.empty(B, Wn, dtype=torch.float32, **kw)
-    acc = torch.empty(B, Wn, dtype=torch.uint8, **kw)
-    alen = torch.empty(B, dtype=torch.int32, **kw)
-    err = torch.zeros(1, dtype=torch.int32, **kw)
+    if out is None:
+        out = e2sci_out(B, Wn, y.device)
+    else:
+        for name, x, shape, dtype in (("D", out.D, (B, Wn), torch.float32), ("accept", out.accept, (B, Wn), torch.uint8),
+                                      ("accept_len", out.accept_len, (B,), torch.int32),
+                                      ("dev_err", out.dev_err, (1,), torch.int32)):
+            _dev_tensor(x, "out." + name, dtype)
+            if tuple(x.shape) != shape:
+                raise ValueError("out.%s must be %s" % (name, list(shape)))
+    D, acc, alen, err = out
     stream = torch.cuda.current_stream(y.device)
     if workspace is None:
         need = int(lib.vwl_e2sci_workspace_bytes(B, Wn, V, dt))

@@ -63,7 +63,7 @@ def time_asym(vwl, x, steps, warmup, copies=1, delta="a-b", gate="cda"):
     out = vwl.asym_out(B, K, "cuda")
     stream = torch.cuda.current_stream()
     ws = vwl._workspace(0, B, K, x.V, vwl.VWL_BF16 if x.dtype == "bf16" else vwl.VWL_F32,
-                        torch.device("cuda", torch.cuda.current_device()), stream)
+                        torch.device("cuda", torch.cuda.current_device()), stream.cuda_stream)
     def call(a, b, t, d):
         if delta == "a-b" and gate == "cda":
             vwl.asym_verify(a, b, t, d, x.beta, x.gamma, out=out, workspace=ws)

@@ -168,7 +168,7 @@ def _ptr(x: Optional[torch.Tensor]):
 
 
 def _dev_tensor(x: torch.Tensor, name: str, dtype=None) -> torch.Tensor:
-    if not isinstance(x, torch.Tensor) or x.device.type != "cuda":
+    if not isinstance(x, torch.Tensor) or not x.is_cuda:
         raise TypeError("%s must be a device tensor" % name)
     if dtype is not None and x.dtype != dtype:
         raise TypeError("%s must have dtype %s" % (name, dtype))
@@ -212,20 +212,38 @@ def check_dev_err(dev_err: torch.Tensor) -> int:
     return v
 
 
-def _workspace(mode: int, B: int, K: int, V: int, dt: int, device, stream) -> torch.Tensor:
-    lib = load_library()
-    need = (lib.vwl_asym_workspace_bytes if mode == 0 else lib.vwl_rapid_workspace_bytes)(B, K, V, dt)
+def _stream_ptr(device) -> int:
+    """Raw handle of the current stream of `device` (the cheap query when
+    this torch build has it: a call's host overhead bounds small calls)."""
+    if _raw_stream is not None:
+        return _raw_stream(device.index)
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _workspace(mode: int, B: int, K: int, V: int, dt: int, device, stream: int) -> torch.Tensor:
+    def need():
+        lib = load_library()
+        return (lib.vwl_asym_workspace_bytes if mode == 0 else lib.vwl_rapid_workspace_bytes)(B, K, V, dt)
     return _workspace_sized((mode, B, K, V, dt), need, device, stream)
 
 
-def _workspace_sized(shape_key, need: int, device, stream) -> torch.Tensor:
-    if need == 0:
+def _workspace_sized(shape_key, need, device, stream: int) -> torch.Tensor:
+    """The cached workspace of (device, stream, shape); `need()` gives its
+    size in bytes and is asked only when none is cached."""
+    key = (device.index, stream) + tuple(shape_key)
+    ws = _ws_cache.get(key)
+    if ws is not None:
+        return ws
+    n = int(need())
+    if n == 0:
         _check(2)
-    key = (device.index, stream.cuda_stream) + tuple(shape_key)
     with _ws_lock:
         ws = _ws_cache.get(key)
         if ws is None:
-            ws = torch.zeros(need, dtype=torch.uint8, device=device)
+            ws = torch.zeros(n, dtype=torch.uint8, device=device)
             _ws_cache[key] = ws
         return ws
 
@@ -324,13 +342,13 @@ def asym_verify(a: torch.Tensor, b: torch.Tensor, t: torch.Tensor, draft: torch.
         raise ValueError("draft must be [B, K]")
     if out is None:
         out = asym_out(B, K, a.device)
-    stream = torch.cuda.current_stream(a.device)
+    stream = _stream_ptr(a.device)
     ws = workspace if workspace is not None else _workspace(0, B, K, V, dt, a.device, stream)
     code = lib.asym_verify(_ptr(a), _ptr(b), _ptr(t), _ptr(draft) if K > 0 else None,
                            B, K, V, dt, float(beta), float(gamma),
                            _ptr(out.D), _ptr(out.gamma_eff), _ptr(out.accept) if K > 0 else None,
                            _ptr(out.fused), _ptr(out.accept_len), _ptr(out.token), _ptr(out.dev_err),
-                           _ptr(ws), ws.numel(), ctypes.c_void_p(stream.cuda_stream))
+                           _ptr(ws), ws.numel(), ctypes.c_void_p(stream))
     _check(code)
     return out
 
@@ -355,12 +373,12 @@ def asym_verify_noalloc(a: torch.Tensor, b: torch.Tensor, t: torch.Tensor, draft
         raise ValueError("draft must be [B, K]")
     if out is None:
         out = asym_out(B, K, a.device)
-    stream = torch.cuda.current_stream(a.device)
+    stream = _stream_ptr(a.device)
     code = lib.asym_verify_noalloc(_ptr(a), _ptr(b), _ptr(t), _ptr(draft) if K > 0 else None,
                                    B, K, V, dt, float(beta), float(gamma),
                                    _ptr(out.D), _ptr(out.gamma_eff), _ptr(out.accept) if K > 0 else None,
                                    _ptr(out.fused), _ptr(out.accept_len), _ptr(out.token), _ptr(out.dev_err),
-                                   ctypes.c_void_p(stream.cuda_stream))
+                                   ctypes.c_void_p(stream))
     _check(code)
     return out
 
@@ -393,13 +411,13 @@ def asym_verify_variant(a: Optional[torch.Tensor], b: torch.Tensor, t: torch.Ten
         raise ValueError("draft must be [B, K]")
     if out is None:
         out = asym_out(B, K, t.device)
-    stream = torch.cuda.current_stream(t.device)
+    stream = _stream_ptr(t.device)
     ws = workspace if workspace is not None else _workspace(0, B, K, V, dt, t.device, stream)
     code = lib.asym_verify_variant(_ptr(a), _ptr(b), _ptr(t), _ptr(draft) if K > 0 else None,
                                    B, K, V, dt, float(beta), float(gamma), DELTA_SOURCES[delta], GATES[gate],
                                    _ptr(out.D), _ptr(out.gamma_eff), _ptr(out.accept) if K > 0 else None,
                                    _ptr(out.fused), _ptr(out.accept_len), _ptr(out.token), _ptr(out.dev_err),
-                                   _ptr(ws), ws.numel(), ctypes.c_void_p(stream.cuda_stream))
+                                   _ptr(ws), ws.numel(), ctypes.c_void_p(stream))
     _check(code)
     return out
 
@@ -428,15 +446,15 @@ def asym_verify_xfam(a: torch.Tensor, b: torch.Tensor, t: torch.Tensor, vmap: to
         raise ValueError("draft must be [B, K]")
     if out is None:
         out = asym_out(B, K, a.device)
-    stream = torch.cuda.current_stream(a.device)
+    stream = _stream_ptr(a.device)
     if workspace is None:
-        need = int(lib.vwl_asym_xfam_workspace_bytes(B, K, Vd, Vt, dt))
-        workspace = _workspace_sized(("xfam", B, K, Vd, Vt, dt), need, a.device, stream)
+        workspace = _workspace_sized(("xfam", B, K, Vd, Vt, dt),
+                                     lambda: lib.vwl_asym_xfam_workspace_bytes(B, K, Vd, Vt, dt), a.device, stream)
     code = lib.asym_verify_xfam(_ptr(a), _ptr(b), Vd, _ptr(t), Vt, _ptr(vmap), _ptr(draft) if K > 0 else None,
                                 B, K, dt, float(beta), float(gamma),
                                 _ptr(out.D), _ptr(out.gamma_eff), _ptr(out.accept) if K > 0 else None,
                                 _ptr(out.fused), _ptr(out.accept_len), _ptr(out.token), _ptr(out.dev_err),
-                                _ptr(workspace), workspace.numel(), ctypes.c_void_p(stream.cuda_stream))
+                                _ptr(workspace), workspace.numel(), ctypes.c_void_p(stream))
     _check(code)
     return out
 
@@ -463,15 +481,15 @@ def asym_verify_lmhead(h_a: torch.Tensor, h_b: torch.Tensor, W_d: torch.Tensor, 
         raise ValueError("draft must be [B, K]")
     if out is None:
         out = asym_out(B, K, h_a.device)
-    stream = torch.cuda.current_stream(h_a.device)
+    stream = _stream_ptr(h_a.device)
     if workspace is None:
-        need = int(lib.vwl_asym_lmhead_workspace_bytes(B, K, V, Hd, Ht))
-        workspace = _workspace_sized(("lmhead", B, K, V, Hd, Ht), need, h_a.device, stream)
+        workspace = _workspace_sized(("lmhead", B, K, V, Hd, Ht),
+                                     lambda: lib.vwl_asym_lmhead_workspace_bytes(B, K, V, Hd, Ht), h_a.device, stream)
     code = lib.asym_verify_lmhead(_ptr(h_a), _ptr(h_b), _ptr(W_d), _ptr(h_t), _ptr(W_t),
                                   _ptr(draft) if K > 0 else None, B, K, V, Hd, Ht, float(beta), float(gamma),
                                   _ptr(out.D), _ptr(out.gamma_eff), _ptr(out.accept) if K > 0 else None,
                                   _ptr(out.fused), _ptr(out.accept_len), _ptr(out.token), _ptr(out.dev_err),
-                                  _ptr(workspace), workspace.numel(), ctypes.c_void_p(stream.cuda_stream))
+                                  _ptr(workspace), workspace.numel(), ctypes.c_void_p(stream))
     _check(code)
     return out
 
@@ -552,13 +570,13 @@ def e2sci_verify(y: torch.Tensor, z: torch.Tensor, T: torch.Tensor, omega: torch
             if tuple(x.shape) != shape:
                 raise ValueError("out.%s must be %s" % (name, list(shape)))
     D, acc, alen, err = out
-    stream = torch.cuda.current_stream(y.device)
+    stream = _stream_ptr(y.device)
     if workspace is None:
-        need = int(lib.vwl_e2sci_workspace_bytes(B, Wn, V, dt))
-        workspace = _workspace_sized(("e2sci", B, Wn, V, dt), need, y.device, stream)
+        workspace = _workspace_sized(("e2sci", B, Wn, V, dt),
+                                     lambda: lib.vwl_e2sci_workspace_bytes(B, Wn, V, dt), y.device, stream)
     code = lib.e2sci_verify(_ptr(y), _ptr(z), B, Wn, V, dt, _ptr(T), _ptr(omega), _ptr(r_hat),
                             _ptr(age) if age is not None else None, ctypes.byref(params), _ptr(D), _ptr(acc), _ptr(alen), _ptr(T_out), _ptr(err),
-                            _ptr(workspace), workspace.numel(), ctypes.c_void_p(stream.cuda_stream))
+                            _ptr(workspace), workspace.numel(), ctypes.c_void_p(stream))
     _check(code)
     return E2sciOut(D, acc, alen, T_out, r_hat, err, age)
 
@@ -610,14 +628,14 @@ def rapid_verify(z: torch.Tensor, y: torch.Tensor, draft: torch.Tensor,
         raise ValueError("draft, u_accept must be [B, G] and u_sample [B, G+1]")
     if out is None:
         out = rapid_out(B, G, V, z.device, want_probs, want_dist)
-    stream = torch.cuda.current_stream(z.device)
+    stream = _stream_ptr(z.device)
     ws = workspace if workspace is not None else _workspace(1, B, G, V, dt, z.device, stream)
     code = lib.rapid_verify(_ptr(z), _ptr(y), _ptr(draft) if G > 0 else None,
                             _ptr(u_accept) if G > 0 else None, _ptr(u_sample),
                             B, G, V, dt, float(eta), float(T),
                             _ptr(out.accept) if G > 0 else None, _ptr(out.accept_len), _ptr(out.token),
                             _ptr(out.p_hat_draft), _ptr(out.q_draft), _ptr(out.emit_dist),
-                            _ptr(out.dev_err), _ptr(ws), ws.numel(), ctypes.c_void_p(stream.cuda_stream))
+                            _ptr(out.dev_err), _ptr(ws), ws.numel(), ctypes.c_void_p(stream))
     _check(code)
     return out
 

@@ -319,16 +319,73 @@ def cpu_baseline(x, runs=3):
             "nproc": os.cpu_count(), "cpu_model": model}
 
 
+def graph_call_ms(fn, steps, warmup):
+    """Per-call device time of `fn` captured once in a HIP graph and replayed:
+    each replay bracketed by events on the current stream, so the host's
+    per-call cost (argument checks, launches) is outside the timed span.
+    The call must allocate nothing (outputs and workspace given)."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(2):
+            fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        fn()
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        g.replay()
+    stream = torch.cuda.current_stream()
+    start, end = _events(steps), _events(steps)
+    for e in start:
+        e.record(stream)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        start[i].record(stream)
+        g.replay()
+        end[i].record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in zip(start, end)]
+
+
 def latency(vwl, x, steps, warmup, copies=4):
     """Per-call latency of asym_verify on a small workload: median and p10/p90
-    over `steps` calls after `warmup`, rotating `copies` input sets.  These
-    calls are bound by launch and synchronisation latency, not by bytes (the
-    inputs are a few MB at most and stay in the last-level cache)."""
+    over `steps` calls after `warmup`, rotating `copies` input sets, and the
+    same call replayed from a captured graph (device time without the host's
+    per-call cost).  These calls are bound by launch and synchronisation
+    latency, not by bytes (the inputs are a few MB at most and stay in the
+    last-level cache)."""
+    import torch
     _, per, rows = time_asym(vwl, x, steps, warmup, copies=copies)
+    (a, b, t), d = _device_inputs(vwl, x)[0]
+    ws = torch.zeros(vwl.workspace_bytes("asym", x.B, x.K, x.V, a.dtype), dtype=torch.uint8, device="cuda")
+    out = vwl.asym_out(x.B, x.K, "cuda")
+    gper = graph_call_ms(lambda: vwl.asym_verify(a, b, t, d, x.beta, x.gamma, out=out, workspace=ws),
+                         steps, warmup)
     return {"B": x.B, "K": x.K, "V": x.V, "logits": x.dtype, "median_call_us": _median(per) * 1e3,
             "p10_call_us": _pct(per, 0.1) * 1e3, "p90_call_us": _pct(per, 0.9) * 1e3,
             "median_row_kernel_us": _median(rows) * 1e3,
+            "median_graph_call_us": _median(gper) * 1e3,
             "bound": "latency (launches and the per-row exchange), inputs cache-resident"}
+
+
+def e2sci_graph_call_ms(vwl, x, steps, warmup):
+    """e2sci_verify of one input set replayed from a captured graph, the
+    state carried on the device (see graph_call_ms)."""
+    import torch
+    y, z = vwl.to_device_logits(x.y, x.dtype), vwl.to_device_logits(x.z, x.dtype)
+    T = torch.from_numpy(x.T.copy()).cuda()
+    om = torch.from_numpy(x.omega.copy()).cuda()
+    rh = torch.from_numpy(x.r_hat.copy()).cuda()
+    prm = vwl.E2sciParams()
+    ws = torch.zeros(int(vwl.load_library().vwl_e2sci_workspace_bytes(x.B, x.W, x.V, vwl._dt(y))),
+                     dtype=torch.uint8, device="cuda")
+    out = vwl.e2sci_out(x.B, x.W, "cuda")
+    return graph_call_ms(lambda: vwl.e2sci_verify(y, z, T, om, rh, prm, T_out=T, out=out, workspace=ws),
+                         steps, warmup)
 
 
 def secondary(args, vwl, W, x, bytes_per_call):
@@ -406,6 +463,8 @@ def secondary(args, vwl, W, x, bytes_per_call):
             "input_sets": 4, "row_kernel_gbs": be / (mre * 1e-3) / 1e9,
             "frac_of_peak": be / (mre * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "plan": vwl.e2sci_plan_info(xe.B, xe.W, xe.V, torch.bfloat16)}
+        if xe.B == 1:
+            sec[xe.name]["median_graph_call_ms"] = _median(e2sci_graph_call_ms(vwl, xe, args.steps, args.warmup))
     out["secondary"] = sec
     out["inputs"] = (x2, r3, xf, xl)
     return out

@@ -124,19 +124,18 @@ __device__ __forceinline__ float jsd_half_exact(float xa, float xb, float la_c, 
 //   Psi(x) = cosh(x/2) (x tanh(x/2) - 2 ln cosh(x/2)),
 // since (p+q)/2 = sqrt(p q) cosh(x/2).  Psi is even and analytic (nearest
 // singularities at x = +-i pi), so for |x| < kPsiX1 it is a polynomial in
-// u = (x / kPsiX1)^2: Psi(x)/2 = u * P(u), P of degree 7 fitted by
-// jsd_psi_fit.py (3.5e-7 relative in fp32).  sqrt(p q) = 2^h with h the mean
+// u = (x / kPsiX1)^2: Psi(x)/2 = u * P(u), P of degree 6 fitted by
+// jsd_psi_fit.py (2.1e-7 relative in fp32 on |x| < 3).  sqrt(p q) = 2^h with h the mean
 // of the two log2-probabilities.  Elements with u > 1 or NaN (|x| >= kPsiX1,
 // -inf logits) are flagged and recomputed by jsd_half_exact.
-constexpr float kPsiX1 = 4.0f;
-constexpr float kPsiP0 = 0x1.fffff8p+0f;
-constexpr float kPsiP1 = 0x1.117372p-14f;
-constexpr float kPsiP2 = 0x1.c58246p-2f;
-constexpr float kPsiP3 = -0x1.5d1374p-2f;
-constexpr float kPsiP4 = 0x1.375ac8p-2f;
-constexpr float kPsiP5 = -0x1.b802a6p-3f;
-constexpr float kPsiP6 = 0x1.915e84p-4f;
-constexpr float kPsiP7 = -0x1.4f064cp-6f;
+constexpr float kPsiX1 = 3.0f;
+constexpr float kPsiP0 = 0x1.1ffffep+0f;
+constexpr float kPsiP1 = 0x1.22577cp-17f;
+constexpr float kPsiP2 = 0x1.4360c6p-4f;
+constexpr float kPsiP3 = -0x1.1b3e12p-5f;
+constexpr float kPsiP4 = 0x1.2216eap-6f;
+constexpr float kPsiP5 = -0x1.c2aa72p-8f;
+constexpr float kPsiP6 = 0x1.64f9b8p-10f;
 constexpr float kHalfLog2e = 0.72134752044448170f;
 
 // Row constants of pass C, from the row log-sum-exps in log2 units.
@@ -158,7 +157,7 @@ __device__ __forceinline__ JsdRow jsd_row(double La2, double Lb2) {
 
 // D's share of one 16-byte vector of a and b (EPV elements), by the
 // polynomial path; elements it does not cover make the whole vector take
-// the exact path (rare: only elements with |x| >= 4 or -inf logits).
+// the exact path (rare: only elements with |x| >= kPsiX1 or -inf logits).
 template <int DT>
 __device__ __forceinline__ float jsd_vector(const uint4 &va, const uint4 &vb, const JsdRow &R) {
     constexpr int EPV = Elem<DT>::kPerVec;
@@ -170,8 +169,7 @@ __device__ __forceinline__ float jsd_vector(const uint4 &va, const uint4 &vb, co
         const float S = __builtin_amdgcn_exp2f(__fmaf_rn(xa + xb, kHalfLog2e, -R.hmid));
         const float xs = __fmaf_rn(xa - xb, 1.0f / kPsiX1, -R.dlx);
         const float u = xs * xs;
-        float P = __fmaf_rn(kPsiP7, u, kPsiP6);
-        P = __fmaf_rn(P, u, kPsiP5);
+        float P = __fmaf_rn(kPsiP6, u, kPsiP5);
         P = __fmaf_rn(P, u, kPsiP4);
         P = __fmaf_rn(P, u, kPsiP3);
         P = __fmaf_rn(P, u, kPsiP2);

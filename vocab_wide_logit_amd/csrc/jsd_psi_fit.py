@@ -37,7 +37,7 @@ def psi_half(x):
     return out
 
 
-def fit(x1=4.0, deg=7, n=6000, iters=80):
+def fit(x1=3.0, deg=6, n=6000, iters=80):
     k = np.arange(n)
     u = 0.5 * (1 - np.cos(np.pi * (k + 0.5) / n))
     f = psi_half(x1 * np.sqrt(u)) / u
@@ -65,8 +65,8 @@ def check(cf, x1):
 
 
 if __name__ == "__main__":
-    x1 = float(sys.argv[1]) if len(sys.argv) > 1 else 4.0
-    deg = int(sys.argv[2]) if len(sys.argv) > 2 else 7
+    x1 = float(sys.argv[1]) if len(sys.argv) > 1 else 3.0
+    deg = int(sys.argv[2]) if len(sys.argv) > 2 else 6
     cf = fit(x1, deg)
     print("max relative error of the fp32 evaluation on (0, %g): %.3g" % (x1, check(cf, x1)))
     for i, c in enumerate(cf):

@@ -43,25 +43,85 @@ __device__ __forceinline__ double clamp_uniform(float u, int32_t *dev_err) {
 }
 
 
-// Row log-sum-exp in log2 units from the W records (fixed order; same
-// scheme as the AsymSpec kernel: integer references, exact power-of-two
-// rescales, butterfly sums).  Called by one whole wave.
-__device__ __forceinline__ double team_lse2_r(const uint64_t *rec_row, int W, int word, int cword, bool hi) {
+// Phase-1 exchange of the row kernel without a counter: each member
+// publishes its sums of z and y and their references as three words that
+// are never zero (a sum's bits with the sign flipped; the two references'
+// bits, each with its sign flipped, -0.0 made +0.0 first), so a reader that
+// sees a word has its value, with no ordering against other stores.  One
+// whole wave polls the team's words and folds them in fixed order: the
+// largest reference C, then sum_w s_w 2^(c_w - C) (exact power-of-two
+// rescales, since the references are integers; lane w takes members w,
+// w + 64, ..., then butterfly sums), so every member gets the same bits;
+// the row log-sum-exp is C + log2 of the sum (log2 units).  Returns 2 when
+// every word was in at the first look, 1 after waiting, 0 when the wait
+// bound expired.
+__device__ __forceinline__ uint64_t sum_word(double x) { return f64_bits(x + 0.0) ^ 0x8000000000000000ull; }
+__device__ __forceinline__ double word_sum(uint64_t w) { return as_f64(w ^ 0x8000000000000000ull); }
+__device__ __forceinline__ uint64_t refs_word(float cz, float cy) {
+    return ((uint64_t)(__float_as_uint(cy + 0.0f) ^ 0x80000000u) << 32) |
+           (uint64_t)(__float_as_uint(cz + 0.0f) ^ 0x80000000u);
+}
+__device__ __forceinline__ float word_ref(uint64_t w, bool hi) {
+    return __uint_as_float((uint32_t)(hi ? (w >> 32) : w) ^ 0x80000000u);
+}
+__device__ __forceinline__ uint32_t rapid_poll(const uint64_t *xw, int W, double &Lz2, double &Ly2) {
     const int lane = threadIdx.x & 63;
-    float C = -3.0e38f;
-    for (int w = lane; w < W; w += 64) {
-        const uint64_t x = ld_relaxed(rec_row + (size_t)w * kRecWords + cword);
-        C = fmaxf(C, __uint_as_float(hi ? (uint32_t)(x >> 32) : (uint32_t)x));
+    uint32_t status = 2u;
+    uint64_t t0 = 0;
+    float Cz = -3.0e38f, Cy = -3.0e38f;
+    uint64_t f0 = 0, f1 = 0, f2 = 0; // the words of member `lane`
+    for (int w0 = 0; w0 < W; w0 += 64) {
+        const int w = w0 + lane;
+        const uint64_t *m = xw + (size_t)w * 4;
+        uint64_t v0 = 0, v1 = 0, v2 = 0;
+        for (;;) {
+            if (w < W) {
+                if (v0 == 0)
+                    v0 = ld_relaxed(m + 0);
+                if (v1 == 0)
+                    v1 = ld_relaxed(m + 1);
+                if (v2 == 0)
+                    v2 = ld_relaxed(m + 2);
+            }
+            if (__builtin_amdgcn_ballot_w64(w < W && (v0 == 0 || v1 == 0 || v2 == 0)) == 0)
+                break;
+            if (status == 2u) {
+                status = 1u;
+                t0 = wall_clock64();
+            }
+            __builtin_amdgcn_s_sleep(1);
+            if (wall_clock64() - t0 > kWaitLimitTicks)
+                return 0u;
+        }
+        if (w < W) {
+            Cz = fmaxf(Cz, word_ref(v2, false));
+            Cy = fmaxf(Cy, word_ref(v2, true));
+        }
+        if (w0 == 0) {
+            f0 = v0;
+            f1 = v1;
+            f2 = v2;
+        }
     }
-    C = wave_max(C);
-    double s = 0.0;
+    Cz = wave_max(Cz);
+    Cy = wave_max(Cy);
+    double sz = 0.0, sy = 0.0;
     for (int w = lane; w < W; w += 64) {
-        const uint64_t *r = rec_row + (size_t)w * kRecWords;
-        const uint64_t x = ld_relaxed(r + cword);
-        s += scale_pow2(as_f64(ld_relaxed(r + word)), __uint_as_float(hi ? (uint32_t)(x >> 32) : (uint32_t)x) - C);
+        uint64_t v0 = f0, v1 = f1, v2 = f2;
+        if (w >= 64) { // published and final: the reload sees the same words
+            const uint64_t *m = xw + (size_t)w * 4;
+            v0 = ld_relaxed(m + 0);
+            v1 = ld_relaxed(m + 1);
+            v2 = ld_relaxed(m + 2);
+        }
+        sz += scale_pow2(word_sum(v0), word_ref(v2, false) - Cz);
+        sy += scale_pow2(word_sum(v1), word_ref(v2, true) - Cy);
     }
-    s = wave_sum(s);
-    return (double)C + log2(s);
+    sz = wave_sum(sz);
+    sy = wave_sum(sy);
+    Lz2 = (double)Cz + log2(sz);
+    Ly2 = (double)Cy + log2(sy);
+    return status;
 }
 
 // Online sum-of-exp state of one tensor over a thread's elements, fed one
@@ -174,7 +234,8 @@ __device__ __forceinline__ int seg16_min_int(int v) {
 // of a wave (so a wave handles four rows at once): all record words of the
 // row are loaded in one round.  The segment's lane 0 leaves L_z, L_y, Mhat,
 // L_zhat, the argmax and the acceptance flag in `slot`; with `write` it
-// also stores the row's outputs and clears the row's arrival counter.  Every
+// also stores the row's outputs and clears the row kernel's published words
+// of the row.  Every
 // lane of the segment must call it (the reductions are segment-wide).
 template <int DT>
 __device__ __forceinline__ void tail_row(const RapidParams &P, long long row, bool write, double *slot) {
@@ -263,6 +324,14 @@ __device__ __forceinline__ void tail_row(const RapidParams &P, long long row, bo
     sz = seg16_sum(sz);
     sy = seg16_sum(sy);
     sh = seg16_sum(sh);
+    if (write) { // the row kernel's published words back to zero, for the next call
+        for (int w = lane; w < P.W; w += 16) {
+            uint64_t *xw = P.xw + ((size_t)row * P.Wmax + w) * 4;
+            st_relaxed(xw + 0, 0ull);
+            st_relaxed(xw + 1, 0ull);
+            st_relaxed(xw + 2, 0ull);
+        }
+    }
     if (lane != 0)
         return;
     const double Lz = ((double)cz + log2(sz)) * kLn2d;
@@ -317,8 +386,6 @@ __device__ __forceinline__ void tail_row(const RapidParams &P, long long row, bo
         }
     }
     slot[5] = (double)acc;
-    if (write)
-        st_relaxed(P.row_ctr + (size_t)row * 16, 0u); // the row's arrivals, for the next call
 }
 
 template <int DT, int NV>
@@ -388,15 +455,24 @@ __global__ __launch_bounds__(kThreads, (NV <= 4 ? 5 : 4)) void rapid_rows_kernel
         double S[2] = {rescale_to_r(lz, mx[0]), rescale_to_r(ly, mx[1])};
         block_sum<2>(S, lds_d);
 
-        const uint64_t *rec_row = P.rec + (size_t)row * P.Wmax * kRecWords;
-        uint32_t *ctr = P.row_ctr + (size_t)row * 16;
         if (tid == 0) {
             uint64_t *rec = P.rec + ((size_t)row * P.Wmax + member) * kRecWords;
             st_relaxed(rec + 0, f64_bits(S[0]));
             st_relaxed(rec + 1, f64_bits(S[1]));
             st_relaxed(rec + 2, (uint64_t)__float_as_uint(mx[0]) | ((uint64_t)__float_as_uint(mx[1]) << 32));
-            publish_add(ctr, 1u);
-            sh_u[1] = wait_at_least(ctr, (uint32_t)P.W) ? 1u : 0u;
+            uint64_t *xw = P.xw + ((size_t)row * P.Wmax + member) * 4;
+            st_relaxed(xw + 0, sum_word(S[0]));
+            st_relaxed(xw + 1, sum_word(S[1]));
+            st_relaxed(xw + 2, refs_word(mx[0], mx[1]));
+        }
+        if (tid < 64) {
+            double Lz2 = 0.0, Ly2 = 0.0;
+            const uint32_t st = rapid_poll(P.xw + (size_t)row * P.Wmax * 4, P.W, Lz2, Ly2);
+            if (tid == 0) {
+                sh_row[0] = Lz2;
+                sh_row[1] = Ly2;
+                sh_u[1] = st;
+            }
         }
         __syncthreads();
         if (!sh_u[1]) {
@@ -404,15 +480,6 @@ __global__ __launch_bounds__(kThreads, (NV <= 4 ? 5 : 4)) void rapid_rows_kernel
                 set_dev_err(P.dev_err, 4);
             return;
         }
-        if (tid < 64) {
-            const double Lz2 = team_lse2_r(rec_row, P.W, 0, 2, false);
-            const double Ly2 = team_lse2_r(rec_row, P.W, 1, 2, true);
-            if (tid == 0) {
-                sh_row[0] = Lz2;
-                sh_row[1] = Ly2;
-            }
-        }
-        __syncthreads();
         __builtin_amdgcn_s_setprio(0);
 
         // ---- second pass: h = zhat/T = z/T + eta*(q - p); online statistics ----

@@ -921,6 +921,7 @@ vwl_status rapid_verify(const void *z, const void *y, const int32_t *draft,
     p.rec = reinterpret_cast<uint64_t *>(ws + L.rec);
     p.rowstat = reinterpret_cast<double *>(ws + L.rowstat);
     p.emit = reinterpret_cast<double *>(ws + L.emit);
+    p.xw = reinterpret_cast<uint64_t *>(ws + L.lsum);
     return launch_rapid((int)dt, plan, p, stream, g_phase_event.load()) == hipSuccess ? VWL_OK : VWL_ERR_HIP;
 }
 

@@ -23,10 +23,12 @@ constexpr int kThreads = 256; // threads per workgroup (4 wave64)
 //            R x 4 f64  AsymSpec: L_a, L_b, L_t (log2 units), fused token
 //   emit     B x We x 8 f64  RAPID only: per-chunk residual, target,
 //                             augmented-target and normaliser sums
-//   lsum     R x Wmax x 2 u64  AsymSpec row kernel only: each member's
-//            log-sum-exps of a and b (log2 units), in the form lse_word()
-//            gives them; zero means "not yet published" (the finalize
-//            kernels clear them for the next call)
+//   lsum     R x Wmax x 2 u64  AsymSpec: each member's log-sum-exps of a
+//            and b (log2 units), in the form lse_word() gives them
+//            R x Wmax x 4 u64  RAPID: each member's sums of z and y and
+//            their references, as rapid_words() gives them
+//            zero means "not yet published" (the finalize kernels, and the
+//            RAPID tail, clear them for the next call)
 struct WsLayout {
     size_t ctl, row_ctr, req_ctr, row_info, rec, rowstat, emit, lsum, total;
     int Wmax;
@@ -72,7 +74,7 @@ inline WsLayout ws_layout(int B, int P, int V, int elem_bytes, bool rapid) {
     L.rec = off;      off = align256(off + R * (size_t)L.Wmax * kRecWords * 8);
     L.rowstat = off;  off = align256(off + R * (rapid ? kRowStatWords : 4) * 8);
     L.emit = off;     off = align256(off + (rapid ? (size_t)B * (size_t)L.We * kEmitWords * 8 : 0));
-    L.lsum = off;     off = align256(off + (rapid ? 0 : R * (size_t)L.Wmax * 2 * 8));
+    L.lsum = off;     off = align256(off + R * (size_t)L.Wmax * (rapid ? 4 : 2) * 8);
     L.total = off;
     return L;
 }
@@ -136,6 +138,7 @@ struct RapidParams {
     uint32_t *ctl, *row_ctr, *req_ctr, *row_info;
     uint64_t *rec;
     double *rowstat, *emit;
+    uint64_t *xw; // [R][Wmax][4] published phase-1 words of the row kernel
 };
 
 // A launch plan: vectors per thread per tensor (template choice), team size,

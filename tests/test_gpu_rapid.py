@@ -201,3 +201,17 @@ def test_rapid_no_drafts(vwl):
     x = W.gen_rapid(3, 0, 5000, "f32", seed=43)
     dev, ora, rep = check(vwl, x, 10.0, 1.0, label="G=0")
     assert np.all(dev["accept_len"] == 0)
+
+
+def test_rapid_back_to_back_calls_reuse_the_workspace(vwl):
+    """Two calls of one shape on different inputs share the cached workspace:
+    every published exchange word of the first call must be back to zero
+    before the second (teams of more than 16 members, so members other than
+    each row segment's first lane are covered)."""
+    try:
+        vwl.set_plan_override("rapid", 1, 0)
+        for seed in (61, 62, 63):
+            x = W.gen_rapid(3, 4, 50000, "f32", seed=seed, eta=8.0, T=0.8)
+            check(vwl, x, label="reuse seed=%d" % seed)
+    finally:
+        vwl.set_plan_override("rapid", 0, 0)

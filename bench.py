@@ -403,6 +403,26 @@ def graph_call_ms(fn, steps, warmup):
     return [a.elapsed_time(b) for a, b in zip(start, end)]
 
 
+def prepared_call_ms(call, steps, warmup):
+    """Per-call time of a prepared call (arguments checked and marshalled
+    once): each invocation bracketed by events on the current stream."""
+    import torch
+    settle_clocks()
+    for _ in range(warmup):
+        call()
+    stream = torch.cuda.current_stream()
+    start, end = _events(steps), _events(steps)
+    for e in start:
+        e.record(stream)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        start[i].record(stream)
+        call()
+        end[i].record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in zip(start, end)]
+
+
 def latency(vwl, x, steps, warmup, copies=4):
     """Per-call latency of asym_verify on a small workload: median and p10/p90
     over `steps` calls after `warmup`, rotating `copies` input sets, and the
@@ -417,16 +437,20 @@ def latency(vwl, x, steps, warmup, copies=4):
     out = vwl.asym_out(x.B, x.K, "cuda")
     gper = graph_call_ms(lambda: vwl.asym_verify(a, b, t, d, x.beta, x.gamma, out=out, workspace=ws),
                          steps, warmup)
+    pper = prepared_call_ms(vwl.asym_verify(a, b, t, d, x.beta, x.gamma, out=out, workspace=ws, prepare=True),
+                            steps, warmup)
     return {"B": x.B, "K": x.K, "V": x.V, "logits": x.dtype, "median_call_us": _median(per) * 1e3,
             "p10_call_us": _pct(per, 0.1) * 1e3, "p90_call_us": _pct(per, 0.9) * 1e3,
             "median_row_kernel_us": _median(rows) * 1e3,
             "median_graph_call_us": _median(gper) * 1e3,
+            "median_prepared_call_us": _median(pper) * 1e3,
             "bound": "latency (launches and the per-row exchange), inputs cache-resident"}
 
 
 def e2sci_graph_call_ms(vwl, x, steps, warmup):
-    """e2sci_verify of one input set replayed from a captured graph, the
-    state carried on the device (see graph_call_ms)."""
+    """e2sci_verify of one input set replayed from a captured graph and as a
+    prepared call, the state carried on the device (see graph_call_ms and
+    prepared_call_ms); returns both lists."""
     import torch
     y, z = vwl.to_device_logits(x.y, x.dtype), vwl.to_device_logits(x.z, x.dtype)
     T = torch.from_numpy(x.T.copy()).cuda()
@@ -436,8 +460,11 @@ def e2sci_graph_call_ms(vwl, x, steps, warmup):
     ws = torch.zeros(int(vwl.load_library().vwl_e2sci_workspace_bytes(x.B, x.W, x.V, vwl._dt(y))),
                      dtype=torch.uint8, device="cuda")
     out = vwl.e2sci_out(x.B, x.W, "cuda")
-    return graph_call_ms(lambda: vwl.e2sci_verify(y, z, T, om, rh, prm, T_out=T, out=out, workspace=ws),
+    g = graph_call_ms(lambda: vwl.e2sci_verify(y, z, T, om, rh, prm, T_out=T, out=out, workspace=ws),
+                      steps, warmup)
+    p = prepared_call_ms(vwl.e2sci_verify(y, z, T, om, rh, prm, T_out=T, out=out, workspace=ws, prepare=True),
                          steps, warmup)
+    return g, p
 
 
 def secondary(args, vwl, W, x, bytes_per_call):
@@ -516,7 +543,9 @@ def secondary(args, vwl, W, x, bytes_per_call):
             "frac_of_peak": be / (mre * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "plan": vwl.e2sci_plan_info(xe.B, xe.W, xe.V, torch.bfloat16)}
         if xe.B == 1:
-            sec[xe.name]["median_graph_call_ms"] = _median(e2sci_graph_call_ms(vwl, xe, args.steps, args.warmup))
+            g, pc = e2sci_graph_call_ms(vwl, xe, args.steps, args.warmup)
+            sec[xe.name]["median_graph_call_ms"] = _median(g)
+            sec[xe.name]["median_prepared_call_ms"] = _median(pc)
     out["secondary"] = sec
     out["inputs"] = (x2, r3, xf, xl)
     return out

@@ -155,6 +155,26 @@ def _check(code: int) -> None:
         raise VwlError(code, msg)
 
 
+class PreparedCall:
+    """A library call whose arguments were checked and marshalled once (from
+    ``asym_verify``, ``e2sci_verify`` or ``rapid_verify`` with
+    ``prepare=True``).  Each ``()`` issues the same C call again on the
+    stream that was current at preparation, with the same input, output and
+    workspace memory (the caller refills the inputs in place), and returns
+    the output tuple.  It keeps those tensors alive.  For serving loops in
+    which the host's per-call checks would dominate a small call's latency."""
+    __slots__ = ("_fn", "_args", "_keep", "out")
+
+    def __init__(self, fn, args, keep, out):
+        self._fn, self._args, self._keep, self.out = fn, args, keep, out
+
+    def __call__(self):
+        code = self._fn(*self._args)
+        if code:
+            _check(code)
+        return self.out
+
+
 def _dt(x: torch.Tensor) -> int:
     if x.dtype == torch.float32:
         return VWL_F32
@@ -322,12 +342,13 @@ def asym_out(B: int, K: int, device) -> AsymOut:
 
 def asym_verify(a: torch.Tensor, b: torch.Tensor, t: torch.Tensor, draft: torch.Tensor,
                 beta: float, gamma: float, *, out: Optional[AsymOut] = None,
-                workspace: Optional[torch.Tensor] = None) -> AsymOut:
+                workspace: Optional[torch.Tensor] = None, prepare: bool = False):
     """AsymSpec verification of [B, K+1, V] logit rows on the current stream.
 
     a: drafter logits on the full context; b: drafter logits on the
     compressed context; t: verifier logits; draft: [B, K] int32 draft ids.
-    Returns D, gamma_eff, accept, fused, accept_len, token and dev_err."""
+    Returns D, gamma_eff, accept, fused, accept_len, token and dev_err; with
+    prepare=True, a PreparedCall that issues this call (nothing runs yet)."""
     lib = load_library()
     _dev_tensor(a, "a")
     dt = _dt(a)
@@ -344,12 +365,14 @@ def asym_verify(a: torch.Tensor, b: torch.Tensor, t: torch.Tensor, draft: torch.
         out = asym_out(B, K, a.device)
     stream = _stream_ptr(a.device)
     ws = workspace if workspace is not None else _workspace(0, B, K, V, dt, a.device, stream)
-    code = lib.asym_verify(_ptr(a), _ptr(b), _ptr(t), _ptr(draft) if K > 0 else None,
-                           B, K, V, dt, float(beta), float(gamma),
-                           _ptr(out.D), _ptr(out.gamma_eff), _ptr(out.accept) if K > 0 else None,
-                           _ptr(out.fused), _ptr(out.accept_len), _ptr(out.token), _ptr(out.dev_err),
-                           _ptr(ws), ws.numel(), ctypes.c_void_p(stream))
-    _check(code)
+    args = (_ptr(a), _ptr(b), _ptr(t), _ptr(draft) if K > 0 else None,
+            B, K, V, dt, float(beta), float(gamma),
+            _ptr(out.D), _ptr(out.gamma_eff), _ptr(out.accept) if K > 0 else None,
+            _ptr(out.fused), _ptr(out.accept_len), _ptr(out.token), _ptr(out.dev_err),
+            _ptr(ws), ws.numel(), ctypes.c_void_p(stream))
+    if prepare:
+        return PreparedCall(lib.asym_verify, args, (a, b, t, draft, ws), out)
+    _check(lib.asym_verify(*args))
     return out
 
 
@@ -532,7 +555,7 @@ def e2sci_verify(y: torch.Tensor, z: torch.Tensor, T: torch.Tensor, omega: torch
                  r_hat: torch.Tensor, params: Optional[E2sciParams] = None, *,
                  age: Optional[torch.Tensor] = None,
                  T_out: Optional[torch.Tensor] = None, out: Optional[E2sciBuffers] = None,
-                 workspace: Optional[torch.Tensor] = None) -> E2sciOut:
+                 workspace: Optional[torch.Tensor] = None, prepare: bool = False):
     """E2-SCI adaptive JSD acceptance of one window per request on the
     current stream.  y: drafter logits, z: target logits, [B, W, V];
     T, omega, r_hat: [B] float32 device tensors (r_hat is updated in place);
@@ -540,7 +563,8 @@ def e2sci_verify(y: torch.Tensor, z: torch.Tensor, T: torch.Tensor, omega: torch
     place (needed when params.min_refresh > 1); the next thresholds go to
     T_out (a new tensor when None; pass T itself to update in place).  With
     ``out`` (from ``e2sci_out``) the call allocates nothing once the
-    workspace is cached; its dev_err keeps the bits of earlier calls."""
+    workspace is cached; its dev_err keeps the bits of earlier calls.  With
+    prepare=True, returns a PreparedCall that issues this call."""
     lib = load_library()
     _dev_tensor(y, "y")
     dt = _dt(y)
@@ -574,11 +598,14 @@ def e2sci_verify(y: torch.Tensor, z: torch.Tensor, T: torch.Tensor, omega: torch
     if workspace is None:
         workspace = _workspace_sized(("e2sci", B, Wn, V, dt),
                                      lambda: lib.vwl_e2sci_workspace_bytes(B, Wn, V, dt), y.device, stream)
-    code = lib.e2sci_verify(_ptr(y), _ptr(z), B, Wn, V, dt, _ptr(T), _ptr(omega), _ptr(r_hat),
-                            _ptr(age) if age is not None else None, ctypes.byref(params), _ptr(D), _ptr(acc), _ptr(alen), _ptr(T_out), _ptr(err),
-                            _ptr(workspace), workspace.numel(), ctypes.c_void_p(stream))
-    _check(code)
-    return E2sciOut(D, acc, alen, T_out, r_hat, err, age)
+    args = (_ptr(y), _ptr(z), B, Wn, V, dt, _ptr(T), _ptr(omega), _ptr(r_hat),
+            _ptr(age) if age is not None else None, ctypes.byref(params), _ptr(D), _ptr(acc), _ptr(alen),
+            _ptr(T_out), _ptr(err), _ptr(workspace), workspace.numel(), ctypes.c_void_p(stream))
+    result = E2sciOut(D, acc, alen, T_out, r_hat, err, age)
+    if prepare:
+        return PreparedCall(lib.e2sci_verify, args, (y, z, T, omega, r_hat, age, params, T_out, workspace), result)
+    _check(lib.e2sci_verify(*args))
+    return result
 
 
 class RapidOut(NamedTuple):
@@ -608,11 +635,12 @@ def rapid_verify(z: torch.Tensor, y: torch.Tensor, draft: torch.Tensor,
                  u_accept: torch.Tensor, u_sample: torch.Tensor, eta: float, T: float,
                  *, want_probs: bool = False, want_dist: bool = False,
                  out: Optional[RapidOut] = None,
-                 workspace: Optional[torch.Tensor] = None) -> RapidOut:
+                 workspace: Optional[torch.Tensor] = None, prepare: bool = False):
     """RAPID verification of [B, G+1, V] logit rows on the current stream.
 
     z: target logits; y: RAG-drafter logits; draft: [B, G] int32;
-    u_accept: [B, G] and u_sample: [B, G+1] float32 uniforms in [0, 1)."""
+    u_accept: [B, G] and u_sample: [B, G+1] float32 uniforms in [0, 1).
+    With prepare=True, returns a PreparedCall that issues this call."""
     lib = load_library()
     _dev_tensor(z, "z")
     dt = _dt(z)
@@ -630,13 +658,15 @@ def rapid_verify(z: torch.Tensor, y: torch.Tensor, draft: torch.Tensor,
         out = rapid_out(B, G, V, z.device, want_probs, want_dist)
     stream = _stream_ptr(z.device)
     ws = workspace if workspace is not None else _workspace(1, B, G, V, dt, z.device, stream)
-    code = lib.rapid_verify(_ptr(z), _ptr(y), _ptr(draft) if G > 0 else None,
-                            _ptr(u_accept) if G > 0 else None, _ptr(u_sample),
-                            B, G, V, dt, float(eta), float(T),
-                            _ptr(out.accept) if G > 0 else None, _ptr(out.accept_len), _ptr(out.token),
-                            _ptr(out.p_hat_draft), _ptr(out.q_draft), _ptr(out.emit_dist),
-                            _ptr(out.dev_err), _ptr(ws), ws.numel(), ctypes.c_void_p(stream))
-    _check(code)
+    args = (_ptr(z), _ptr(y), _ptr(draft) if G > 0 else None,
+            _ptr(u_accept) if G > 0 else None, _ptr(u_sample),
+            B, G, V, dt, float(eta), float(T),
+            _ptr(out.accept) if G > 0 else None, _ptr(out.accept_len), _ptr(out.token),
+            _ptr(out.p_hat_draft), _ptr(out.q_draft), _ptr(out.emit_dist),
+            _ptr(out.dev_err), _ptr(ws), ws.numel(), ctypes.c_void_p(stream))
+    if prepare:
+        return PreparedCall(lib.rapid_verify, args, (z, y, draft, u_accept, u_sample, ws), out)
+    _check(lib.rapid_verify(*args))
     return out
 
 

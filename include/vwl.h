@@ -151,8 +151,8 @@ vwl_status asym_verify(const void *a, const void *b, const void *t,
  * first call on a device looks up the array's address and zero-fills it with
  * a fill kernel on `stream`; every completed call leaves its counters at zero
  * again.  A shape whose vwl_asym_workspace_bytes exceeds the scratch returns
- * VWL_ERR_SCRATCH (at V = 151936 the scratch holds about 3,300 bf16 or
- * 1,700 fp32 rows B*(K+1); the large B = 256, K = 4 bf16 batch needs 6.3 MB).
+ * VWL_ERR_SCRATCH (at V = 151936 the scratch holds 2,781 bf16 or 1,403 fp32
+ * rows B*(K+1); the large B = 256, K = 4 bf16 batch needs 7.7 MB).
  * All calls on one device share its scratch: two calls that may overlap on a
  * device (different streams without ordering, or different host threads)
  * race, and their results are undefined.  Order them.

@@ -873,7 +873,6 @@ __device__ __forceinline__ void xfam_invert_slice(const AsymParams &P) {
 
 template <int DT, int NV, int DS, int GATE>
 __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, DS, GATE>())) void asym_rows_kernel(AsymParams P) {
-    constexpr int EPV = Elem<DT>::kPerVec;
     constexpr bool READ_A = AsymUse<DS, GATE>::kReadA;
     constexpr bool READ_T = AsymUse<DS, GATE>::kReadT;
     constexpr int NT = AsymUse<DS, GATE>::kTensors;
@@ -905,7 +904,6 @@ __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, DS, GATE>())) void a
     const uint4 *A4 = static_cast<const uint4 *>(P.a);
     const uint4 *B4 = static_cast<const uint4 *>(P.b);
     const uint4 *T4 = static_cast<const uint4 *>(P.t);
-    const float NEG_INF = -__builtin_inff();
     const int V = P.V, W = P.W;
     const bool wave0 = tid < 64;
     uint32_t na = 0u, nb = 0u, nt = 0u; // head/tail scalars of the staged row (raw bits)
@@ -1052,20 +1050,12 @@ __global__ __launch_bounds__(kThreads, (asym_rows_waves<NV, DS, GATE>())) void a
             xfam_invert_slice<DT>(P);
 }
 
-// One wave per row: combine the W records, write the row outputs, and let
-// the wave that completes a request run its first-rejection scan.  Under the
-// fixed gate D is not computed (NaN is written) and the threshold is gamma.
+// Row i of request bi, by one whole wave.
 template <int DT, int GATE>
-__global__ __launch_bounds__(kThreads) void asym_finalize_kernel(AsymParams P) {
-    const int lane = threadIdx.x & 63;
-    const long long row = (long long)blockIdx.x * kWaves + (threadIdx.x >> 6);
-    if (blockIdx.x == 0 && threadIdx.x == 0)
-        P.ctl[0] = 0u; // ticket counter of the row kernel, for the next call
-    if (row >= P.R)
-        return;
+__device__ __forceinline__ void asym_finalize_row(const AsymParams &P, long long bi, int i, int lane,
+                                                  uint32_t *sh_acc, int *sh_fi) {
     const int Pn = P.K + 1;
-    const long long bi = row / Pn;
-    const int i = (int)(row - bi * Pn);
+    const long long row = bi * Pn + i;
     const size_t row_off = (size_t)row * (size_t)P.V;
     // In flight together with the team sums: the draft's logits (lane 0) and
     // the fused-maximum and JSD words of the lane's first two members.
@@ -1144,27 +1134,38 @@ __global__ __launch_bounds__(kThreads) void asym_finalize_kernel(AsymParams P) {
         }
         P.accept[bi * P.K + i] = (uint8_t)acc;
     }
-    st_relaxed(P.row_info + (size_t)row * 2 + 0, (uint32_t)fidx);
-    st_relaxed(P.row_info + (size_t)row * 2 + 1, acc);
-    P.row_ctr[(size_t)row * 16] = 0u; // arrivals of the row kernel, for the next call
-    uint32_t *rq = P.req_ctr + (size_t)bi * 16;
-    const uint32_t done = publish_add(rq, 1u);
-    if (done == (uint32_t)P.K) {
-        const size_t r0 = (size_t)bi * Pn;
+    sh_acc[i] = acc;
+    sh_fi[i] = fidx;
+}
+
+// One workgroup per request, one wave per row (up to 16 waves; wave w takes
+// rows w, w + 16, ...): combine the row's W records and write its outputs; the rows' accept
+// flags and fused tokens meet in LDS, and one thread runs the request's
+// first-rejection scan.  Under the fixed gate D is not computed (NaN is
+// written) and the threshold is gamma.
+template <int DT, int GATE>
+__global__ __launch_bounds__(kFinMaxThreads) void asym_finalize_kernel(AsymParams P) {
+    __shared__ uint32_t sh_acc[kMaxDrafts + 1];
+    __shared__ int sh_fi[kMaxDrafts + 1];
+    const int lane = threadIdx.x & 63;
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        P.ctl[0] = 0u; // ticket counter of the row kernel, for the next call
+    const int Pn = P.K + 1;
+    const long long bi = blockIdx.x;
+    for (int i = (int)(threadIdx.x >> 6); i < Pn; i += (int)(blockDim.x >> 6)) {
+        asym_finalize_row<DT, GATE>(P, bi, i, lane, sh_acc, sh_fi);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
         int n = P.K;
         for (int k = 0; k < P.K; ++k) {
-            if (ld_relaxed(P.row_info + (r0 + k) * 2 + 1) == 0u) {
+            if (sh_acc[k] == 0u) {
                 n = k;
                 break;
             }
         }
         P.acc_len[bi] = n;
-        P.token[bi] = (int32_t)ld_relaxed(P.row_info + (r0 + n) * 2 + 0);
-        for (int k = 0; k <= P.K; ++k) { // per-row results back to zero for the next call
-            st_relaxed(P.row_info + (r0 + k) * 2 + 0, 0u);
-            st_relaxed(P.row_info + (r0 + k) * 2 + 1, 0u);
-        }
-        st_relaxed(rq, 0u);
+        P.token[bi] = sh_fi[n];
     }
 }
 
@@ -1214,8 +1215,7 @@ static hipError_t launch_t(const Plan &plan, const AsymParams &p, hipStream_t s,
         if (e != hipSuccess)
             return e;
     }
-    const unsigned fin = (unsigned)((p.R + kWaves - 1) / kWaves);
-    hipLaunchKernelGGL((asym_finalize_kernel<DT, GATE>), dim3(fin), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((asym_finalize_kernel<DT, GATE>), dim3((unsigned)p.B), dim3(fin_threads(p.K + 1)), 0, s, p);
     return hipGetLastError();
 }
 

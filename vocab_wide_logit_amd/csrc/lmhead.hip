@@ -375,11 +375,10 @@ __device__ __forceinline__ double lm_dot(const uint16_t *x, const uint16_t *y, i
     return wave_sum(acc);
 }
 
-__global__ __launch_bounds__(kThreads) void lmhead_finalize_kernel(LmheadParams P) {
-    const int lane = threadIdx.x & 63;
-    const long long row = (long long)blockIdx.x * kWaves + (threadIdx.x >> 6);
-    if (row >= P.R)
-        return;
+// Row i of request bi, by one whole wave.
+__device__ __forceinline__ void lmhead_finalize_row(const LmheadParams &P, long long bi, int i, int lane,
+                                                    uint32_t *sh_acc, int *sh_fi) {
+    const long long row = bi * (P.K + 1) + i;
     const uint64_t *rec_row = P.rec + (size_t)row * P.S * kRecWords;
     double L2[2];
     team_lse<2>(rec_row, P.S, {1, 2}, {3, 4}, {true, false}, L2);
@@ -401,9 +400,6 @@ __global__ __launch_bounds__(kThreads) void lmhead_finalize_kernel(LmheadParams 
     }
     jsum = wave_sum(jsum);
     fidx = wave_min_int(fidx);
-    const int Pn = P.K + 1;
-    const long long bi = row / Pn;
-    const int i = (int)(row - bi * Pn);
     int d = -1;
     double td = 0.0, bd = 0.0;
     if (i < P.K) {
@@ -429,22 +425,29 @@ __global__ __launch_bounds__(kThreads) void lmhead_finalize_kernel(LmheadParams 
         }
         P.accept[bi * P.K + i] = (uint8_t)acc;
     }
-    st_relaxed(P.row_info + (size_t)row * 2 + 0, (uint32_t)fidx);
-    st_relaxed(P.row_info + (size_t)row * 2 + 1, acc);
-    uint32_t *rq = P.req_ctr + (size_t)bi * 16;
-    const uint32_t done = publish_add(rq, 1u);
-    if (done == (uint32_t)P.K) {
-        const size_t r0 = (size_t)bi * Pn;
+    sh_acc[i] = acc;
+    sh_fi[i] = fidx;
+}
+
+// One workgroup per request: one wave per row (up to 16 waves; wave w takes
+// rows w, w + 16, ...), then one thread scans the request's accept flags.
+__global__ __launch_bounds__(kFinMaxThreads) void lmhead_finalize_kernel(LmheadParams P) {
+    __shared__ uint32_t sh_acc[kMaxDrafts + 1];
+    __shared__ int sh_fi[kMaxDrafts + 1];
+    const long long bi = blockIdx.x;
+    for (int i = (int)(threadIdx.x >> 6); i < P.K + 1; i += (int)(blockDim.x >> 6))
+        lmhead_finalize_row(P, bi, i, threadIdx.x & 63, sh_acc, sh_fi);
+    __syncthreads();
+    if (threadIdx.x == 0) {
         int n = P.K;
         for (int k = 0; k < P.K; ++k) {
-            if (ld_relaxed(P.row_info + (r0 + k) * 2 + 1) == 0u) {
+            if (sh_acc[k] == 0u) {
                 n = k;
                 break;
             }
         }
         P.acc_len[bi] = n;
-        P.token[bi] = (int32_t)ld_relaxed(P.row_info + (r0 + n) * 2 + 0);
-        st_relaxed(rq, 0u);
+        P.token[bi] = sh_fi[n];
     }
 }
 
@@ -473,7 +476,7 @@ hipError_t launch_lmhead(const LmheadParams &p, hipStream_t s, hipEvent_t after_
         if (e != hipSuccess)
             return e;
     }
-    hipLaunchKernelGGL(lmhead_finalize_kernel, dim3(fin), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(lmhead_finalize_kernel, dim3((unsigned)p.B), dim3(fin_threads(p.K + 1)), 0, s, p);
     return hipGetLastError();
 }
 

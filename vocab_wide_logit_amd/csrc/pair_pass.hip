@@ -9,9 +9,9 @@
 // Launch 1: the two-tensor row kernel (asym_rows_kernel with kDeltaNone):
 // online softmax statistics of the drafter row y (tensor a) and the target
 // row z (tensor b), the team combine, and the JSD terms of each chunk.
-// Launch 2, e2sci_finalize_kernel: one wave per row sums the JSD partials
-// (D) and tests D <= T of the row's request; the wave that completes a
-// request finds the first rejection, updates the credit state
+// Launch 2, e2sci_finalize_kernel: one workgroup per request; one wave per
+// row sums the JSD partials (D) and tests D <= T of the request; then one
+// thread finds the first rejection, updates the credit state
 //   r = (1 - beta) r + beta * accept_len / W
 // and writes the next window's threshold
 //   T = max(T_min, min(T_base + alpha * omega * (r - tau_credit), T_max)),
@@ -24,66 +24,65 @@
 namespace vwl {
 
 template <int DT>
-__global__ __launch_bounds__(kThreads) void e2sci_finalize_kernel(AsymParams P) {
+__global__ __launch_bounds__(kFinMaxThreads) void e2sci_finalize_kernel(AsymParams P) {
+    __shared__ uint32_t sh_acc[kMaxDrafts + 1]; // a window holds at most VWL_MAX_K + 1 rows
     const int lane = threadIdx.x & 63;
-    const long long row = (long long)blockIdx.x * kWaves + (threadIdx.x >> 6);
     if (blockIdx.x == 0 && threadIdx.x == 0)
         P.ctl[0] = 0u; // ticket counter of the row kernel, for the next call
-    if (row >= P.R)
-        return;
-    const uint64_t *rec_row = P.rec + (size_t)row * P.Wmax * kRecWords;
-    double jsum = 0.0;
-    for (int w = lane; w < P.W; w += 64)
-        jsum += as_f64(ld_relaxed(rec_row + (size_t)w * kRecWords + 6));
-    jsum = wave_sum(jsum);
-    clear_row_exchange(P, row);
-    if (lane != 0)
-        return;
-    const double Dr = jsum;
-    const long long bi = row / P.win;
-    // the threshold is read before this row's arrival is counted, so the
-    // completing wave may overwrite it (thr_out may alias thr_in)
-    const uint32_t acc = Dr <= (double)P.thr_in[bi] ? 1u : 0u;
-    P.D[row] = (float)Dr;
-    P.accept[row] = (uint8_t)acc;
-    st_relaxed(P.row_info + (size_t)row * 2 + 1, acc);
-    P.row_ctr[(size_t)row * 16] = 0u; // arrivals of the row kernel, for the next call
-    uint32_t *rq = P.req_ctr + (size_t)bi * 16;
-    const uint32_t done = publish_add(rq, 1u);
-    if (done == (uint32_t)(P.win - 1)) {
-        const size_t r0 = (size_t)bi * P.win;
-        int n = P.win;
-        for (int k = 0; k < P.win; ++k) {
-            if (ld_relaxed(P.row_info + (r0 + k) * 2 + 1) == 0u) {
-                n = k;
-                break;
-            }
-        }
-        P.acc_len[bi] = n;
-        const double p_acc = (double)n / (double)P.win;
-        const double r = (1.0 - P.e_ewma) * (double)P.r_hat[bi] + P.e_ewma * p_acc;
-        double T = P.e_Tbase + P.e_alpha * (double)P.omega[bi] * (r - P.e_tau);
-        T = T > P.e_Tmax ? P.e_Tmax : T;
-        T = T < P.e_Tmin ? P.e_Tmin : T;
-        // stabilisers: safety fall-back, minimum refresh interval, dead band
-        const double T_cur = (double)P.thr_in[bi];
-        const int age_in = P.age ? P.age[bi] : 0;
-        const int age_next = age_in < 0x7fffffff ? age_in + 1 : age_in;
-        int age_out = 0;
-        if (p_acc < P.e_delta) {
-            T = P.e_Tsafe;
-        } else if (age_next < P.e_minref || !(fabs(T - T_cur) > P.e_hyst)) {
-            T = T_cur;
-            age_out = age_next;
-        }
-        if (P.age)
-            P.age[bi] = age_out;
-        P.r_hat[bi] = (float)r;
-        P.thr_out[bi] = (float)T;
-        for (int k = 0; k < P.win; ++k) // per-row results back to zero for the next call
-            st_relaxed(P.row_info + (r0 + k) * 2 + 1, 0u);
-        st_relaxed(rq, 0u);
+    const long long bi = blockIdx.x;
+    const double T_cur = (double)P.thr_in[bi];
+    // the request's credit state, in flight while the rows are combined
+    float r_in = 0.0f, om = 0.0f;
+    int age_in = 0;
+    if (threadIdx.x == 0) {
+        r_in = P.r_hat[bi];
+        om = P.omega[bi];
+        age_in = P.age ? P.age[bi] : 0;
     }
+    for (int i = (int)(threadIdx.x >> 6); i < P.win; i += (int)(blockDim.x >> 6)) {
+        const long long row = bi * P.win + i;
+        const uint64_t *rec_row = P.rec + (size_t)row * P.Wmax * kRecWords;
+        double jsum = 0.0;
+        for (int w = lane; w < P.W; w += 64)
+            jsum += as_f64(ld_relaxed(rec_row + (size_t)w * kRecWords + 6));
+        jsum = wave_sum(jsum);
+        clear_row_exchange(P, row);
+        if (lane == 0) {
+            const uint32_t acc = jsum <= T_cur ? 1u : 0u;
+            P.D[row] = (float)jsum;
+            P.accept[row] = (uint8_t)acc;
+            sh_acc[i] = acc;
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x != 0)
+        return;
+    int n = P.win;
+    for (int k = 0; k < P.win; ++k) {
+        if (sh_acc[k] == 0u) {
+            n = k;
+            break;
+        }
+    }
+    P.acc_len[bi] = n;
+    const double p_acc = (double)n / (double)P.win;
+    const double r = (1.0 - P.e_ewma) * (double)r_in + P.e_ewma * p_acc;
+    double T = P.e_Tbase + P.e_alpha * (double)om * (r - P.e_tau);
+    T = T > P.e_Tmax ? P.e_Tmax : T;
+    T = T < P.e_Tmin ? P.e_Tmin : T;
+    // stabilisers: safety fall-back, minimum refresh interval, dead band
+    const int age_next = age_in < 0x7fffffff ? age_in + 1 : age_in;
+    int age_out = 0;
+    if (p_acc < P.e_delta) {
+        T = P.e_Tsafe;
+    } else if (age_next < P.e_minref || !(fabs(T - T_cur) > P.e_hyst)) {
+        T = T_cur;
+        age_out = age_next;
+    }
+    if (P.age)
+        P.age[bi] = age_out;
+    P.r_hat[bi] = (float)r;
+    P.thr_out[bi] = (float)T; // thr_out may alias thr_in: every row has been tested above
 }
 
 template <int DT, int NV>
@@ -97,8 +96,7 @@ static hipError_t launch_t(const Plan &plan, const AsymParams &p, hipStream_t s,
         if (e != hipSuccess)
             return e;
     }
-    const unsigned fin = (unsigned)((p.R + kWaves - 1) / kWaves);
-    hipLaunchKernelGGL((e2sci_finalize_kernel<DT>), dim3(fin), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((e2sci_finalize_kernel<DT>), dim3((unsigned)p.B), dim3(fin_threads(p.win)), 0, s, p);
     return hipGetLastError();
 }
 
@@ -146,10 +144,11 @@ template int asym_blocks_per_cu_ds<kDeltaNone>(int dt, int nv, int gate);
 // General pass (any vocabulary sizes): launch 2 is xfam_verifier_kernel, one
 // 256-thread workgroup per (row, 4096-token verifier chunk), a and b gathered
 // through vmap; no keys are built.
-// Launch 3, xfam_finalize_kernel: one wave per row combines both record
-// sets, tests the draft (a verifier id) against the drafter's compressed-view
-// probability of its pair, and scans each request; after a staged pass its
-// threads also clear the inverse alignment and the flag for the next call.
+// Launch 3, xfam_finalize_kernel: one workgroup per request; one wave per
+// row combines both record sets and tests the draft (a verifier id) against
+// the drafter's compressed-view probability of its pair, and one thread
+// scans the request; after a staged pass its threads also clear the inverse
+// alignment and the flag for the next call.
 // ---------------------------------------------------------------------------
 
 // Workgroup b runs on die b % 8 (round-robin dispatch); the chunks of one row
@@ -416,25 +415,11 @@ __global__ __launch_bounds__(kThreads) void xfam_verifier_kernel(AsymParams P) {
         set_dev_err(P.dev_err, 8);
 }
 
+// Row i of request bi, by one whole wave.
 template <int DT>
-__global__ __launch_bounds__(kThreads) void xfam_finalize_kernel(AsymParams P) {
-    const int lane = threadIdx.x & 63;
-    const long long row = (long long)blockIdx.x * kWaves + (threadIdx.x >> 6);
-    if (blockIdx.x == 0 && threadIdx.x == 0)
-        P.ctl[0] = 0u; // ticket counter of the row kernel, for the next call
-    // the inverse alignment and its flag, for the next call
-    if (P.xparts > 0) {
-        const long long n = (long long)xfam_key_words(P.xparts, P.V); // word n is the flag
-        uint32_t *w = reinterpret_cast<uint32_t *>(P.xkey);
-        for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i <= n;
-             i += (long long)gridDim.x * kThreads)
-            w[i] = 0u;
-    }
-    if (row >= P.R)
-        return;
-    const int Pn = P.K + 1;
-    const long long bi = row / Pn;
-    const int i = (int)(row - bi * Pn);
+__device__ __forceinline__ void xfam_finalize_row(const AsymParams &P, long long bi, int i, int lane,
+                                                  uint32_t *sh_acc, int *sh_fi) {
+    const long long row = bi * (P.K + 1) + i;
     // the draft (a verifier id), its pair and their logits, fetched by lane 0
     // while the records are combined
     int d = -1, e = -1;
@@ -506,27 +491,40 @@ __global__ __launch_bounds__(kThreads) void xfam_finalize_kernel(AsymParams P) {
         }
         P.accept[bi * P.K + i] = (uint8_t)acc;
     }
-    st_relaxed(P.row_info + (size_t)row * 2 + 0, (uint32_t)fidx);
-    st_relaxed(P.row_info + (size_t)row * 2 + 1, acc);
-    P.row_ctr[(size_t)row * 16] = 0u; // arrivals of the row kernel, for the next call
-    uint32_t *rq = P.req_ctr + (size_t)bi * 16;
-    const uint32_t done = publish_add(rq, 1u);
-    if (done == (uint32_t)P.K) {
-        const size_t r0 = (size_t)bi * Pn;
+    sh_acc[i] = acc;
+    sh_fi[i] = fidx;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kFinMaxThreads) void xfam_finalize_kernel(AsymParams P) {
+    __shared__ uint32_t sh_acc[kMaxDrafts + 1];
+    __shared__ int sh_fi[kMaxDrafts + 1];
+    const int lane = threadIdx.x & 63;
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        P.ctl[0] = 0u; // ticket counter of the row kernel, for the next call
+    // the inverse alignment and its flag, for the next call
+    if (P.xparts > 0) {
+        const long long n = (long long)xfam_key_words(P.xparts, P.V); // word n is the flag
+        uint32_t *w = reinterpret_cast<uint32_t *>(P.xkey);
+        for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i <= n;
+             i += (long long)gridDim.x * blockDim.x)
+            w[i] = 0u;
+    }
+    const int Pn = P.K + 1;
+    const long long bi = blockIdx.x;
+    for (int i = (int)(threadIdx.x >> 6); i < Pn; i += (int)(blockDim.x >> 6))
+        xfam_finalize_row<DT>(P, bi, i, lane, sh_acc, sh_fi);
+    __syncthreads();
+    if (threadIdx.x == 0) {
         int n = P.K;
         for (int k = 0; k < P.K; ++k) {
-            if (ld_relaxed(P.row_info + (r0 + k) * 2 + 1) == 0u) {
+            if (sh_acc[k] == 0u) {
                 n = k;
                 break;
             }
         }
         P.acc_len[bi] = n;
-        P.token[bi] = (int32_t)ld_relaxed(P.row_info + (r0 + n) * 2 + 0);
-        for (int k = 0; k <= P.K; ++k) { // per-row results back to zero for the next call
-            st_relaxed(P.row_info + (r0 + k) * 2 + 0, 0u);
-            st_relaxed(P.row_info + (r0 + k) * 2 + 1, 0u);
-        }
-        st_relaxed(rq, 0u);
+        P.token[bi] = sh_fi[n];
     }
 }
 
@@ -553,8 +551,7 @@ static hipError_t launch_x(const Plan &plan, const AsymParams &p, hipStream_t s,
         if (e != hipSuccess)
             return e;
     }
-    const unsigned fin = (unsigned)((p.R + kWaves - 1) / kWaves);
-    hipLaunchKernelGGL((xfam_finalize_kernel<DT>), dim3(fin), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((xfam_finalize_kernel<DT>), dim3((unsigned)p.B), dim3(fin_threads(p.K + 1)), 0, s, p);
     return hipGetLastError();
 }
 

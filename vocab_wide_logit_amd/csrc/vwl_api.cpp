@@ -487,9 +487,6 @@ static vwl_status asym_variant_impl(const void *a, const void *b, const void *t,
     p.token = token;
     p.dev_err = dev_err;
     p.ctl = reinterpret_cast<uint32_t *>(ws + L.ctl);
-    p.row_ctr = reinterpret_cast<uint32_t *>(ws + L.row_ctr);
-    p.req_ctr = reinterpret_cast<uint32_t *>(ws + L.req_ctr);
-    p.row_info = reinterpret_cast<uint32_t *>(ws + L.row_info);
     p.rec = reinterpret_cast<uint64_t *>(ws + L.rec);
     p.lsum = reinterpret_cast<uint64_t *>(ws + L.lsum);
     return launch_asym((int)dt, (int)delta, (int)gate, plan, p, stream, g_phase_event.load()) == hipSuccess
@@ -627,9 +624,6 @@ vwl_status asym_verify_xfam(const void *a, const void *b, int Vd, const void *t,
     p.token = token;
     p.dev_err = dev_err;
     p.ctl = reinterpret_cast<uint32_t *>(ws + L.ctl);
-    p.row_ctr = reinterpret_cast<uint32_t *>(ws + L.row_ctr);
-    p.req_ctr = reinterpret_cast<uint32_t *>(ws + L.req_ctr);
-    p.row_info = reinterpret_cast<uint32_t *>(ws + L.row_info);
     p.rec = reinterpret_cast<uint64_t *>(ws + L.rec);
     p.lsum = reinterpret_cast<uint64_t *>(ws + L.lsum);
     return launch_xfam((int)dt, plan, p, stream, g_phase_event.load()) == hipSuccess ? VWL_OK : VWL_ERR_HIP;
@@ -639,7 +633,7 @@ vwl_status asym_verify_xfam(const void *a, const void *b, int Vd, const void *t,
 // 128 tokens) for about 1536 workgroups; depends on the shape only.
 struct LmGeom {
     int RT, S, range;
-    size_t rec, rowstat, req_ctr, row_info, total;
+    size_t rec, rowstat, total;
 };
 // Shapes and workspace layout.  The records hold one entry per (row,
 // vocabulary range) for up to one range per 128-column tile, so the size
@@ -660,8 +654,6 @@ static bool lm_geometry(int B, int K, int V, int Hd, int Ht, LmGeom &g) {
     size_t off = 0;
     g.rec = off;      off = align256(off + (size_t)R * tiles * kRecWords * 8);
     g.rowstat = off;  off = align256(off + (size_t)R * 2 * 8);
-    g.req_ctr = off;  off = align256(off + (size_t)B * 16 * 4);
-    g.row_info = off; off = align256(off + (size_t)R * 2 * 4);
     g.total = off;
     return true;
 }
@@ -747,8 +739,6 @@ vwl_status asym_verify_lmhead(const void *h_a, const void *h_b, const void *W_d,
     p.dev_err = dev_err;
     p.rec = reinterpret_cast<uint64_t *>(ws + g.rec);
     p.rowstat = reinterpret_cast<double *>(ws + g.rowstat);
-    p.req_ctr = reinterpret_cast<uint32_t *>(ws + g.req_ctr);
-    p.row_info = reinterpret_cast<uint32_t *>(ws + g.row_info);
     return launch_lmhead(p, stream, g_phase_event.load()) == hipSuccess ? VWL_OK : VWL_ERR_HIP;
 }
 
@@ -809,9 +799,6 @@ vwl_status e2sci_verify(const void *y, const void *z, int B, int W, int V, vwl_d
     p.acc_len = accept_len;
     p.dev_err = dev_err;
     p.ctl = reinterpret_cast<uint32_t *>(ws + L.ctl);
-    p.row_ctr = reinterpret_cast<uint32_t *>(ws + L.row_ctr);
-    p.req_ctr = reinterpret_cast<uint32_t *>(ws + L.req_ctr);
-    p.row_info = reinterpret_cast<uint32_t *>(ws + L.row_info);
     p.rec = reinterpret_cast<uint64_t *>(ws + L.rec);
     p.lsum = reinterpret_cast<uint64_t *>(ws + L.lsum);
     p.win = W;
@@ -915,9 +902,7 @@ vwl_status rapid_verify(const void *z, const void *y, const int32_t *draft,
     p.q_draft = q_draft;
     p.emit_dist = emit_dist;
     p.ctl = reinterpret_cast<uint32_t *>(ws + L.ctl);
-    p.row_ctr = reinterpret_cast<uint32_t *>(ws + L.row_ctr);
     p.req_ctr = reinterpret_cast<uint32_t *>(ws + L.req_ctr);
-    p.row_info = reinterpret_cast<uint32_t *>(ws + L.row_info);
     p.rec = reinterpret_cast<uint64_t *>(ws + L.rec);
     p.rowstat = reinterpret_cast<double *>(ws + L.rowstat);
     p.emit = reinterpret_cast<double *>(ws + L.emit);

@@ -13,11 +13,9 @@ constexpr int kThreads = 256; // threads per workgroup (4 wave64)
 // Workspace layout (bytes, each block 256-byte aligned).  Sizes depend only on
 // the call's shape, never on the device, so they can be queried on any host.
 //
-//   ctl      64 x u32   [0] ticket counter, [16] exit counter
-//   row_ctr  R x 16 u32 per row: [0] phase-1 arrivals, [1] phase-2 arrivals
-//   req_ctr  B x 16 u32 per request: rows finished; RAPID tail [4] phase
-//            arrivals, [5] departures
-//   row_info R x 2 u32  per row: fused token, accept flag (request scan input)
+//   ctl      64 x u32   [0] ticket counter of the row kernel
+//   req_ctr  B x 16 u32 RAPID only: per request, the tail's [4] phase
+//            arrivals and [5] departures
 //   rec      R x Wmax x 8 u64  per (row, member) record (see the kernels)
 //   rowstat  R x 8 f64  RAPID: L_z, L_y, Mhat, L_zhat, argmax of zhat
 //            R x 4 f64  AsymSpec: L_a, L_b, L_t (log2 units), fused token
@@ -26,17 +24,20 @@ constexpr int kThreads = 256; // threads per workgroup (4 wave64)
 //   lsum     R x Wmax x 2 u64  AsymSpec: each member's log-sum-exps of a
 //            and b (log2 units), in the form lse_word() gives them
 //            R x Wmax x 4 u64  RAPID: each member's sums of z and y and
-//            their references, as rapid_words() gives them
+//            their references as the row kernel publishes them
 //            zero means "not yet published" (the finalize kernels, and the
 //            RAPID tail, clear them for the next call)
 struct WsLayout {
-    size_t ctl, row_ctr, req_ctr, row_info, rec, rowstat, emit, lsum, total;
+    size_t ctl, req_ctr, rec, rowstat, emit, lsum, total;
     int Wmax;
     int We;  // RAPID: workgroups per request in the tail
     int ept; // RAPID: emitting-row elements per thread in the tail
 };
 
 constexpr int kRecWords = 8;
+// Threads of a per-request finalize workgroup: one wave per row, at most 16.
+constexpr int kFinMaxThreads = 1024;
+inline unsigned fin_threads(int rows) { return 64u * (unsigned)(rows < 16 ? (rows < 1 ? 1 : rows) : 16); }
 constexpr int kEmitMaxChunks = 512; // tail workgroups per request (at most)
 constexpr int kRapidMaxV = kThreads * 16 * kEmitMaxChunks; // largest RAPID vocabulary
 constexpr int kRowStatWords = 8;
@@ -68,9 +69,7 @@ inline WsLayout ws_layout(int B, int P, int V, int elem_bytes, bool rapid) {
     }
     size_t off = 0;
     L.ctl = off;      off = align256(off + 64 * 4);
-    L.row_ctr = off;  off = align256(off + R * 16 * 4);
-    L.req_ctr = off;  off = align256(off + (size_t)B * 16 * 4);
-    L.row_info = off; off = align256(off + R * 2 * 4);
+    L.req_ctr = off;  off = align256(off + (rapid ? (size_t)B * 16 * 4 : 0));
     L.rec = off;      off = align256(off + R * (size_t)L.Wmax * kRecWords * 8);
     L.rowstat = off;  off = align256(off + R * (rapid ? kRowStatWords : 4) * 8);
     L.emit = off;     off = align256(off + (rapid ? (size_t)B * (size_t)L.We * kEmitWords * 8 : 0));
@@ -91,7 +90,7 @@ struct AsymParams {
     float *D, *geff;
     uint8_t *accept;
     int32_t *fused, *acc_len, *token, *dev_err;
-    uint32_t *ctl, *row_ctr, *req_ctr, *row_info;
+    uint32_t *ctl;
     uint64_t *rec;
     uint64_t *lsum; // [R][Wmax][2] published log-sum-exps of a and b
     // AsymSpec across families: verifier rows on their own vocabulary Vt,
@@ -135,7 +134,7 @@ struct RapidParams {
     uint8_t *accept;
     int32_t *acc_len, *token, *dev_err;
     float *p_hat_draft, *q_draft, *emit_dist;
-    uint32_t *ctl, *row_ctr, *req_ctr, *row_info;
+    uint32_t *ctl, *req_ctr;
     uint64_t *rec;
     double *rowstat, *emit;
     uint64_t *xw; // [R][Wmax][4] published phase-1 words of the row kernel
@@ -165,7 +164,6 @@ struct LmheadParams {
     float *D, *geff;
     uint8_t *accept;
     int32_t *fused, *acc_len, *token, *dev_err;
-    uint32_t *req_ctr, *row_info;
     uint64_t *rec;    // [R][S][8], the row kernel's record layout
     double *rowstat;  // [R][2] L_a, L_b (log2 units)
 };

@@ -319,13 +319,15 @@ __device__ __forceinline__ uint32_t lse_poll(const uint64_t *lw, int W, double &
     return status;
 }
 
-template <int N, bool F32ACC = false>
+template <int N, bool F32ACC = false, bool PLAIN = false>
 __device__ __forceinline__ void team_lse(const uint64_t *rec_row, int W, const int (&sw)[N], const int (&cw)[N],
                                          const bool (&hi)[N], double (&L)[N], int stride = kRecWords) {
     const int lane = threadIdx.x & 63;
     const float NEG = -3.0e38f;
+    // PLAIN: records written by an earlier kernel, read with ordinary loads
+    auto ld = [&](const uint64_t *p) { return PLAIN ? *p : ld_relaxed(p); };
     auto ref = [&](const uint64_t *r, int k) {
-        const uint64_t x = ld_relaxed(r + cw[k]);
+        const uint64_t x = ld(r + cw[k]);
         return hi[k] ? unpack_hi(x) : unpack_lo(x);
     };
     double a[N][2];
@@ -343,7 +345,7 @@ __device__ __forceinline__ void team_lse(const uint64_t *rec_row, int W, const i
 #pragma unroll
             for (int k = 0; k < N; ++k) {
                 r[k][h] = ref(rw, k);
-                a[k][h] = as_f64(ld_relaxed(rw + sw[k]));
+                a[k][h] = as_f64(ld(rw + sw[k]));
             }
         }
     }
@@ -371,7 +373,7 @@ __device__ __forceinline__ void team_lse(const uint64_t *rec_row, int W, const i
             const uint64_t *rw = rec_row + (size_t)w0 * stride + lane * stride;
 #pragma unroll
             for (int k = 0; k < N; ++k)
-                t[k] += scale_pow2(as_f64(ld_relaxed(rw + sw[k])), ref(rw, k) - C[k]);
+                t[k] += scale_pow2(as_f64(ld(rw + sw[k])), ref(rw, k) - C[k]);
         }
     }
 #pragma unroll

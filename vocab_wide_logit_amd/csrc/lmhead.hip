@@ -355,7 +355,7 @@ __global__ __launch_bounds__(kThreads) void lmhead_combine_kernel(LmheadParams P
     if (row >= P.R)
         return;
     double L[2];
-    team_lse<2>(P.rec + (size_t)row * P.S * kRecWords, P.S, {0, 1}, {3, 3}, {false, true}, L);
+    team_lse<2, false, true>(P.rec + (size_t)row * P.S * kRecWords, P.S, {0, 1}, {3, 3}, {false, true}, L);
     if ((threadIdx.x & 63) == 0) {
         P.rowstat[row * 2 + 0] = L[0];
         P.rowstat[row * 2 + 1] = L[1];
@@ -363,14 +363,27 @@ __global__ __launch_bounds__(kThreads) void lmhead_combine_kernel(LmheadParams P
 }
 
 // fp64 dot product of two bf16 rows of length H (one whole wave).
+// Five 512-element blocks per round are loaded together (a block past the
+// end re-reads the lane's first vector and is skipped), then summed in
+// element order.
 __device__ __forceinline__ double lm_dot(const uint16_t *x, const uint16_t *y, int H) {
+    constexpr int U = 5;
+    const int k_lane = (threadIdx.x & 63) * 8;
     double acc = 0.0;
-    for (int k = (threadIdx.x & 63) * 8; k < H; k += 64 * 8) {
-        const uint4 vx = *reinterpret_cast<const uint4 *>(x + k);
-        const uint4 vy = *reinterpret_cast<const uint4 *>(y + k);
+    for (int k0 = k_lane; k0 < H; k0 += 64 * 8 * U) {
+        uint4 vx[U], vy[U];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            acc += (double)widen<DT_BF16>(vx, e) * (double)widen<DT_BF16>(vy, e);
+        for (int u = 0; u < U; ++u) {
+            const int k = k0 + 64 * 8 * u < H ? k0 + 64 * 8 * u : k_lane;
+            vx[u] = *reinterpret_cast<const uint4 *>(x + k);
+            vy[u] = *reinterpret_cast<const uint4 *>(y + k);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (k0 + 64 * 8 * u < H)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    acc += (double)widen<DT_BF16>(vx[u], e) * (double)widen<DT_BF16>(vy[u], e);
     }
     return wave_sum(acc);
 }
@@ -381,7 +394,7 @@ __device__ __forceinline__ void lmhead_finalize_row(const LmheadParams &P, long 
     const long long row = bi * (P.K + 1) + i;
     const uint64_t *rec_row = P.rec + (size_t)row * P.S * kRecWords;
     double L2[2];
-    team_lse<2>(rec_row, P.S, {1, 2}, {3, 4}, {true, false}, L2);
+    team_lse<2, false, true>(rec_row, P.S, {1, 2}, {3, 4}, {true, false}, L2);
     const double Lb = L2[0] * kLn2d, Lt = L2[1] * kLn2d;
     // branch-free loops, so that unrolled iterations issue their loads together
     float fbest = -__builtin_inff();

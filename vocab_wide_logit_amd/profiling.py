@@ -7,6 +7,7 @@ uses to attach the measured traffic of the row kernel to its roofline figure.
     python -m vocab_wide_logit_amd.profiling sq     <SQ counter csv> <out.txt> [--grid=N] <command...>
     python -m vocab_wide_logit_amd.profiling kernel <trace csv> <fetch csv> <write csv> <SQ csv> <out.txt>
                                                     <kernel regex> <grid> <algorithmic bytes> <workload> <command...>
+    python -m vocab_wide_logit_amd.profiling counters <counter csv> <out.txt> <kernel regex> <workload> <command...>
 
 The traffic summary scales the row kernel's FETCH_SIZE and WRITE_SIZE (KiB per
 dispatch) by what the same counters read for a plain elementwise copy of a
@@ -252,6 +253,37 @@ def read_traffic(path: str, mode: str = "asym"):
     return None if kv is None else float(kv["traffic_bytes_per_launch"])
 
 
+def summarize_counters(csv_path: str, out_path: str, command: str, kernel_re: str, workload: str) -> dict:
+    """Every counter of one --pmc run, per dispatch of the kernels matching
+    kernel_re (summed over its instances within a dispatch, averaged over
+    the dispatches), with the derived rates the counters allow: the L2 hit
+    fraction (TCC_HIT_sum, TCC_MISS_sum), the texture addressers' busy
+    fraction (TA_BUSY_avr over GRBM_GUI_ACTIVE / 8 dies) and the matrix
+    cores' busy fraction (SQ_VALU_MFMA_BUSY_CYCLES per SIMD over the same)."""
+    names = sorted({_col(r, "Counter_Name") for r in _rows(csv_path)})
+    out = {"kernel_regex": kernel_re, "workload": workload}
+    for n in names:
+        try:
+            out[n], out["dispatches"] = _per_dispatch(csv_path, n, kernel_re)
+        except ValueError:
+            pass
+    if "TCC_HIT_sum" in out and "TCC_MISS_sum" in out:
+        out["l2_hit_fraction"] = out["TCC_HIT_sum"] / max(1.0, out["TCC_HIT_sum"] + out["TCC_MISS_sum"])
+        out["l2_line_requests"] = out["TCC_HIT_sum"] + out["TCC_MISS_sum"]
+    if "GRBM_GUI_ACTIVE" in out:
+        die_cycles = out["GRBM_GUI_ACTIVE"] / 8.0
+        out["die_cycles"] = die_cycles
+        if "TA_BUSY_avr" in out:
+            out["ta_busy"] = out["TA_BUSY_avr"] / die_cycles
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in out:
+            out["mfma_busy"] = out["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024.0 / die_cycles
+    lines = ["# %s: counters per dispatch from rocprofv3" % workload, "", "command: " + command, ""]
+    lines += ["%s: %s" % (k, v) for k, v in out.items()]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return out
+
+
 def _grid_arg(argv):
     """An optional leading --grid=N (workgroups of the launches to keep)."""
     if argv and argv[0].startswith("--grid="):
@@ -268,6 +300,8 @@ def main(argv):
     elif len(argv) >= 3 and argv[0] == "sq":
         grid, rest = _grid_arg(argv[3:])
         print(summarize_sq(argv[1], argv[2], " ".join(rest), grid_wgs=grid))
+    elif len(argv) >= 5 and argv[0] == "counters":
+        print(summarize_counters(argv[1], argv[2], " ".join(argv[5:]), argv[3], argv[4]))
     elif len(argv) >= 10 and argv[0] == "kernel":
         print(summarize_kernel(argv[1], argv[2], argv[3], argv[4], argv[5], " ".join(argv[10:]), argv[6],
                                int(argv[7]), float(argv[8]), argv[9]))

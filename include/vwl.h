@@ -246,8 +246,9 @@ vwl_status asym_verify_xfam(const void *a, const void *b, int Vd, const void *t,
 /* ---------------------------------------------------------------------------
  * AsymSpec from hidden states (the step before the pass on the AsymSpec
  * pages: the LM heads turn hidden states into logits).  The heads' products
- * are formed on the matrix cores and the pass runs in their epilogue, so no
- * logit row is written to memory:
+ * are formed on the matrix cores with the row statistics in their epilogue;
+ * t is never written, and the drafter's logit pairs (a, b) are written once
+ * to the workspace, as fp32, for the JSD pass:
  *   a = h_a W_d^T, b = h_b W_d^T (the drafter's head, full and compressed
  *   context), t = h_t W_t^T (the verifier's head); then everything as
  *   asym_verify (delta = a - b, the CDA gate).
@@ -259,8 +260,9 @@ vwl_status asym_verify_xfam(const void *a, const void *b, int Vd, const void *t,
  *   bf16 products (MFMA accumulation), so within Hd (or Ht) * 2^-24 *
  *   sum_k |h_k w_k| of its value; the draft's logits in the test are fp64
  *   dot products; statistics as asym_verify.
- * Workspace: vwl_asym_lmhead_workspace_bytes (shape only), zero-filled
- * before first use; left zero-filled where it must be.
+ * Workspace: vwl_asym_lmhead_workspace_bytes (shape only; about
+ * 8 * B * (K+1) * V bytes, the stored pairs, plus the per-row records),
+ * zero-filled before first use; left zero-filled where it must be.
  * --------------------------------------------------------------------------- */
 size_t vwl_asym_lmhead_workspace_bytes(int B, int K, int V, int Hd, int Ht);
 

@@ -102,3 +102,36 @@ def test_bench_shape_exact_products(vwl):
         assert rep.stats["D_window_max"] == 0.0
         assert rep.excluded <= 2
         assert rep.checked >= x.B - 2
+
+
+def test_back_to_back_calls_reuse_the_workspace(vwl):
+    """Calls of one shape share a workspace: the records, statistics, stored
+    logit pairs and JSD partials one call leaves there must not reach the
+    next (x, then y, then x again)."""
+    x = W.gen_lmhead(6, 3, 9000, 128, seed=84)
+    y = W.gen_lmhead(6, 3, 9000, 128, seed=85)
+    _say("case back-to-back B=6 K=3 V=9000 Hd=128")
+    d1 = run_dev(vwl, x, x.beta, x.gamma)
+    d2 = run_dev(vwl, y, y.beta, y.gamma)
+    d3 = run_dev(vwl, x, x.beta, x.gamma)
+    for k in d1:
+        assert np.array_equal(d1[k], d3[k], equal_nan=True), k
+    lm = oracle.asym_lmhead(y.h_a, y.h_b, y.W_d, y.h_t, y.W_t, y.draft, y.beta, y.gamma)
+    rep = compare_lmhead(d2, lm, y.K, y.beta)
+    assert rep.ok, str(rep)
+
+
+def test_bad_draft_ids(vwl):
+    """A draft id outside [0, V) sets bit 0 of dev_err and rejects that draft;
+    the other rows are unaffected."""
+    x = W.gen_lmhead(4, 3, 3000, 64, seed=86)
+    x.draft[0, 0] = -1
+    x.draft[1, 2] = x.V
+    _say("case bad drafts B=4 K=3 V=3000 Hd=64")
+    dev = run_dev(vwl, x, 1.0, 0.5)
+    assert dev["dev_err"][0] & 1
+    assert dev["accept"][0, 0] == 0 and dev["accept"][1, 2] == 0
+    assert dev["accept_len"][0] == 0 and dev["accept_len"][1] <= 2
+    lm = oracle.asym_lmhead(x.h_a, x.h_b, x.W_d, x.h_t, x.W_t, x.draft, 1.0, 0.5)
+    rep = compare_lmhead(dev, lm, x.K, 1.0)
+    assert rep.ok, str(rep)

@@ -37,14 +37,14 @@ def test_counter_summary_rates(tmp_path):
     p = str(tmp_path / "c.csv")
     rows = []
     for d in (1, 2):
-        rows += [(d, "void vwl::lmhead_kernel<2>(P)", 1024, 256, "TCC_HIT_sum", 80.0),
-                 (d, "void vwl::lmhead_kernel<2>(P)", 1024, 256, "TCC_MISS_sum", 20.0),
-                 (d, "void vwl::lmhead_kernel<2>(P)", 1024, 256, "GRBM_GUI_ACTIVE", 8000.0),
-                 (d, "void vwl::lmhead_kernel<2>(P)", 1024, 256, "TA_BUSY_avr", 250.0),
-                 (d, "void vwl::lmhead_kernel<2>(P)", 1024, 256, "SQ_VALU_MFMA_BUSY_CYCLES", 1024.0 * 500.0)]
+        rows += [(d, "void vwl::lmhead_jsd_kernel(P)", 1024, 256, "TCC_HIT_sum", 80.0),
+                 (d, "void vwl::lmhead_jsd_kernel(P)", 1024, 256, "TCC_MISS_sum", 20.0),
+                 (d, "void vwl::lmhead_jsd_kernel(P)", 1024, 256, "GRBM_GUI_ACTIVE", 8000.0),
+                 (d, "void vwl::lmhead_jsd_kernel(P)", 1024, 256, "TA_BUSY_avr", 250.0),
+                 (d, "void vwl::lmhead_jsd_kernel(P)", 1024, 256, "SQ_VALU_MFMA_BUSY_CYCLES", 1024.0 * 500.0)]
     _write(p, rows)
     out = str(tmp_path / "s.txt")
-    r = P.summarize_counters(p, out, "cmd", r"lmhead_kernel<2>", "w")
+    r = P.summarize_counters(p, out, "cmd", r"lmhead_jsd_kernel", "w")
     assert r["dispatches"] == 2
     assert r["l2_hit_fraction"] == pytest.approx(0.8)
     assert r["ta_busy"] == pytest.approx(0.25)   # 250 busy of 8000 / 8 cycles per die

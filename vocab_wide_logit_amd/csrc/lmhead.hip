@@ -1,31 +1,33 @@
 // AsymSpec from hidden states: the LM heads' products formed on the matrix
-// cores with the pass in their epilogue, so the logit rows never reach HBM
-// (the step before the AsymSpec pass on its pages: the drafter's head turns
-// the full- and compressed-context hidden states into a and b, the
-// verifier's head turns its hidden state into t).
+// cores with the row statistics in their epilogue (the step before the
+// AsymSpec pass on its pages: the drafter's head turns the full- and
+// compressed-context hidden states into a and b, the verifier's head turns
+// its hidden state into t).
 //
 //   a = h_a W_d^T, b = h_b W_d^T   (one drafter head, two views)
 //   t = h_t W_t^T
 //
-// Launch 1, lmhead_kernel<1>: each workgroup owns 64 rows and a range of the
+// Launch 1, lmhead_kernel: each workgroup owns 64 rows and a range of the
 // vocabulary, walked in tiles of 128 tokens.  Per tile the 4 waves form a
 // [64 x 128] block of a, b (sharing each W_d tile) and then of t with bf16
 // MFMA 16x16x32 (fp32 accumulation), staged through LDS in 64-wide k
 // blocks; the epilogue folds the block into per-row online statistics of a,
 // b, t (integer references, as in the row kernel) and the fused maximum
-// t + beta*(a - b) with its lowest index.  One record per (row, range), in
-// the row kernel's record layout.
-// Launch 2, lmhead_combine_kernel: L_a, L_b per row from the records.
-// Launch 3, lmhead_kernel<2>: the same a, b blocks again (identical
-// arithmetic, so identical bits) and the JSD terms against L_a, L_b.
-// Launch 4, lmhead_finalize_kernel: D, the threshold, the fused token, the
-// draft's logits as fp64 dot products, the test and the scan.
+// t + beta*(a - b) with its lowest index, and stores the (a, b) pairs as
+// fp32 for the JSD.  One record per (row, range), in the row kernel's record
+// layout.
+// Launch 2, lmhead_combine_kernel: per row, L_a, L_b, L_t and the fused
+// token from the records, and the draft's logits as fp64 dot products.
+// Launch 3, lmhead_jsd_kernel: the JSD terms of the stored pairs against
+// L_a, L_b, one partial sum per (row, 4096-token chunk).
+// Launch 4, lmhead_finalize_kernel: D, the threshold, the test and the scan.
 #include "asym_kernels.hpp"
 
 namespace vwl {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kLmRows = kLmRowTile; // rows per workgroup
 constexpr int kLmM = kLmRows / 16;   // MFMA row blocks of 16
@@ -184,7 +186,6 @@ struct LmScratch {
     float sum[kWaves][kLmRows][3];
     float fm[kWaves][kLmRows];
     int fi[kWaves][kLmRows];
-    float la[kLmRows], lb[kLmRows], dh[kLmRows], dlo[kLmRows]; // pass 2 row constants
 };
 
 // Per-row statistics of tensor k's block held as accumulators, written to
@@ -218,7 +219,6 @@ __device__ __forceinline__ void lm_merge(float &run_c, double &run_s, float c, d
     run_c = C;
 }
 
-template <int PASS>
 __global__ __launch_bounds__(kThreads, 3) void lmhead_kernel(LmheadParams P) {
     __shared__ LmStage st;
     __shared__ LmScratch sc;
@@ -236,24 +236,11 @@ __global__ __launch_bounds__(kThreads, 3) void lmhead_kernel(LmheadParams P) {
     const long long v_end = min((long long)P.V, v_begin + P.range);
     const float NEG = -3.0e38f;
 
-    if (PASS == 2) { // row constants of pass C
-        if (tid < kLmRows) {
-            const long long row = min(row0 + tid, P.R - 1);
-            const double La2 = P.rowstat[row * 2 + 0], Lb2 = P.rowstat[row * 2 + 1];
-            const double dl = (La2 - Lb2) * kLn2d;
-            sc.la[tid] = (float)La2;
-            sc.lb[tid] = (float)Lb2;
-            sc.dh[tid] = (float)dl;
-            sc.dlo[tid] = (float)(dl - (double)(float)dl);
-        }
-        __syncthreads();
-    }
     // running per-row state (threads 0..63, row = tid)
     float rc[3] = {NEG, NEG, NEG};
     double rs[3] = {0.0, 0.0, 0.0};
     float rfm = -__builtin_inff();
     int rfi = 0x7fffffff;
-    double rj = 0.0;
 
     for (long long vt0 = v_begin; vt0 < v_end; vt0 += kLmCols) {
         bool cv[2];
@@ -262,103 +249,75 @@ __global__ __launch_bounds__(kThreads, 3) void lmhead_kernel(LmheadParams P) {
             cv[n] = vt0 + lm_col(n) < v_end;
         f32x4_t xa[kLmM][2], xb[kLmM][2];
         lm_gemm<true>(st, P.ha, P.hb, P.Wd, row0, P.R, vt0, P.V, P.Hd, xa, xb);
-        if (PASS == 1) {
-            lm_tile_stats(sc, 0, xa, cv);
-            lm_tile_stats(sc, 1, xb, cv);
-            // the context gain, kept while t is formed
-#pragma unroll
-            for (int m = 0; m < kLmM; ++m)
-#pragma unroll
-                for (int n = 0; n < 2; ++n)
-                    xa[m][n] = xa[m][n] - xb[m][n];
-            f32x4_t xt[kLmM][2], unused[kLmM][2];
-            lm_gemm<false>(st, P.ht, nullptr, P.Wt, row0, P.R, vt0, P.V, P.Ht, xt, unused);
-            lm_tile_stats(sc, 2, xt, cv);
+        // the pairs for the JSD pass, streamed (read once, by the next
+        // launch but one): lg has a row for every row of the tile and a
+        // column for every column of the tile, so the stores need no guard
+        // (the pairs past R or V are never read).  The row stride is re-read
+        // opaquely per tile, so the 16 row offsets are formed here rather
+        // than held in registers across the loop.
+        {
+            long long lgs = P.lgs;
+            asm volatile("" : "+s"(lgs));
+            f32x2_t *q = reinterpret_cast<f32x2_t *>(P.lg) + (row0 + lm_row(0, 0)) * lgs + vt0 + lm_col(0);
 #pragma unroll
             for (int m = 0; m < kLmM; ++m)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    // fused score t + beta*(a - b), its maximum and lowest column
-                    const float f0 = cv[0] ? __fmaf_rn(P.beta, xa[m][0][j], xt[m][0][j]) : -__builtin_inff();
-                    const float f1 = cv[1] ? __fmaf_rn(P.beta, xa[m][1][j], xt[m][1][j]) : -__builtin_inff();
-                    const bool second = f1 > f0;
-                    const float fb = second ? f1 : f0;
-                    const int col = lm_col(second ? 1 : 0);
-                    const float fm = row16_max(fb);
-                    const int fi = row16_min_int((fb == fm && (cv[0] || cv[1])) ? col : 0x7fffffff);
-                    if ((lane & 15) == 0) {
-                        sc.fm[wave][lm_row(m, j)] = fm;
-                        sc.fi[wave][lm_row(m, j)] = fi;
-                    }
+                    f32x2_t *qr = q + (long long)(16 * m + j) * lgs;
+                    __builtin_nontemporal_store(f32x2_t{xa[m][0][j], xb[m][0][j]}, qr);
+                    __builtin_nontemporal_store(f32x2_t{xa[m][1][j], xb[m][1][j]}, qr + 16);
                 }
-            __syncthreads();
-            if (tid < kLmRows) { // waves in column order; strict > keeps the lowest index
+        }
+        lm_tile_stats(sc, 0, xa, cv);
+        lm_tile_stats(sc, 1, xb, cv);
 #pragma unroll
-                for (int w = 0; w < kWaves; ++w) {
+        for (int m = 0; m < kLmM; ++m)
 #pragma unroll
-                    for (int k = 0; k < 3; ++k)
-                        lm_merge(rc[k], rs[k], sc.ref[w][tid][k], (double)sc.sum[w][tid][k]);
-                    if (sc.fm[w][tid] > rfm) {
-                        rfm = sc.fm[w][tid];
-                        rfi = (int)vt0 + sc.fi[w][tid];
-                    }
+            for (int n = 0; n < 2; ++n)
+                xa[m][n] = xa[m][n] - xb[m][n];
+        f32x4_t xt[kLmM][2], unused[kLmM][2];
+        lm_gemm<false>(st, P.ht, nullptr, P.Wt, row0, P.R, vt0, P.V, P.Ht, xt, unused);
+        lm_tile_stats(sc, 2, xt, cv);
+#pragma unroll
+        for (int m = 0; m < kLmM; ++m)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                // fused score t + beta*(a - b), its maximum and lowest column
+                const float f0 = cv[0] ? __fmaf_rn(P.beta, xa[m][0][j], xt[m][0][j]) : -__builtin_inff();
+                const float f1 = cv[1] ? __fmaf_rn(P.beta, xa[m][1][j], xt[m][1][j]) : -__builtin_inff();
+                const bool second = f1 > f0;
+                const float fb = second ? f1 : f0;
+                const int col = lm_col(second ? 1 : 0);
+                const float fm = row16_max(fb);
+                const int fi = row16_min_int((fb == fm && (cv[0] || cv[1])) ? col : 0x7fffffff);
+                if ((lane & 15) == 0) {
+                    sc.fm[wave][lm_row(m, j)] = fm;
+                    sc.fi[wave][lm_row(m, j)] = fi;
                 }
             }
-        } else {
-            // JSD terms of the block against the row's log-sum-exps
+        __syncthreads();
+        if (tid < kLmRows) { // waves in column order; strict > keeps the lowest index
 #pragma unroll
-            for (int m = 0; m < kLmM; ++m)
+            for (int w = 0; w < kWaves; ++w) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r = lm_row(m, j);
-                    const float la_c = sc.la[r], lb_c = sc.lb[r], dh = sc.dh[r], dlo = sc.dlo[r];
-                    float J = 0.f;
-#pragma unroll
-                    for (int n = 0; n < 2; ++n) {
-                        if (cv[n]) {
-                            const float a = xa[m][n][j], bb = xb[m][n][j];
-                            J += jsd_term(__fmaf_rn(a, kLog2e, -la_c), __fmaf_rn(bb, kLog2e, -lb_c),
-                                          ((a - bb) - dh) - dlo);
-                        }
-                    }
-                    J = row16_sum(J);
-                    if ((lane & 15) == 0)
-                        sc.sum[wave][r][0] = J;
+                for (int k = 0; k < 3; ++k)
+                    lm_merge(rc[k], rs[k], sc.ref[w][tid][k], (double)sc.sum[w][tid][k]);
+                if (sc.fm[w][tid] > rfm) {
+                    rfm = sc.fm[w][tid];
+                    rfi = (int)vt0 + sc.fi[w][tid];
                 }
-            __syncthreads();
-            if (tid < kLmRows) {
-#pragma unroll
-                for (int w = 0; w < kWaves; ++w)
-                    rj += (double)sc.sum[w][tid][0];
             }
         }
     }
     const long long row = row0 + tid;
     if (tid < kLmRows && row < P.R) {
         uint64_t *rec = P.rec + ((size_t)row * P.S + s) * kRecWords;
-        if (PASS == 1) {
-            rec[0] = f64_bits(rs[0]);
-            rec[1] = f64_bits(rs[1]);
-            rec[2] = f64_bits(rs[2]);
-            rec[3] = pack2(rc[0], rc[1]);
-            rec[4] = pack2(rc[2], rfm);
-            rec[5] = (uint64_t)(uint32_t)rfi;
-        } else {
-            rec[6] = f64_bits(rj);
-        }
-    }
-}
-
-// L_a, L_b (log2 units) of each row from its records: one wave per row.
-__global__ __launch_bounds__(kThreads) void lmhead_combine_kernel(LmheadParams P) {
-    const long long row = (long long)blockIdx.x * kWaves + (threadIdx.x >> 6);
-    if (row >= P.R)
-        return;
-    double L[2];
-    team_lse<2, false, true>(P.rec + (size_t)row * P.S * kRecWords, P.S, {0, 1}, {3, 3}, {false, true}, L);
-    if ((threadIdx.x & 63) == 0) {
-        P.rowstat[row * 2 + 0] = L[0];
-        P.rowstat[row * 2 + 1] = L[1];
+        rec[0] = f64_bits(rs[0]);
+        rec[1] = f64_bits(rs[1]);
+        rec[2] = f64_bits(rs[2]);
+        rec[3] = pack2(rc[0], rc[1]);
+        rec[4] = pack2(rc[2], rfm);
+        rec[5] = (uint64_t)(uint32_t)rfi;
     }
 }
 
@@ -388,52 +347,99 @@ __device__ __forceinline__ double lm_dot(const uint16_t *x, const uint16_t *y, i
     return wave_sum(acc);
 }
 
-// Row i of request bi, by one whole wave.
+// Launch 2: one workgroup per row.  L_a, L_b, L_t (log2 units) and the fused
+// token from the row's records (each thread folds every 256th record,
+// five at a time, then the workgroup merges the threads' states), and for a
+// draft row the draft's logits t_d, b_d as fp64 dot products of the stored
+// values.  rowstat[row] = {L_a, L_b, L_t, fused token, t_d, b_d}.
+__global__ __launch_bounds__(kThreads) void lmhead_combine_kernel(LmheadParams P) {
+    __shared__ float shf[kWaves * 4];
+    __shared__ double shd[kWaves * 3];
+    __shared__ int shi[kWaves];
+    const long long row = blockIdx.x;
+    const uint64_t *rec_row = P.rec + (size_t)row * P.S * kRecWords;
+    const float NEG = -3.0e38f;
+    float C[3] = {NEG, NEG, NEG};
+    double sum[3] = {0.0, 0.0, 0.0};
+    float fbest = -__builtin_inff();
+    int fidx = 0x7fffffff;
+    constexpr int U = 5;
+    for (int w0 = threadIdx.x; w0 < P.S; w0 += kThreads * U) {
+        uint64_t r[U][6];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int w = w0 + kThreads * u < P.S ? w0 + kThreads * u : w0;
+#pragma unroll
+            for (int k = 0; k < 6; ++k)
+                r[u][k] = rec_row[(size_t)w * kRecWords + k];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (w0 + kThreads * u < P.S) {
+                lm_merge(C[0], sum[0], unpack_lo(r[u][3]), as_f64(r[u][0]));
+                lm_merge(C[1], sum[1], unpack_hi(r[u][3]), as_f64(r[u][1]));
+                lm_merge(C[2], sum[2], unpack_lo(r[u][4]), as_f64(r[u][2]));
+                const float fm = unpack_hi(r[u][4]);
+                const int fi = (int)(uint32_t)r[u][5];
+                fidx = fm > fbest ? fi : (fm == fbest ? min(fidx, fi) : fidx);
+                fbest = fmaxf(fbest, fm);
+            }
+        }
+    }
+    float m[4] = {C[0], C[1], C[2], fbest};
+    block_max<4>(m, shf);
+    double t[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+        t[k] = scale_pow2(sum[k], C[k] - m[k]);
+    int imin = fbest == m[3] ? fidx : 0x7fffffff;
+    block_sum_min<3>(t, imin, shd, shi);
+    const int wave = threadIdx.x >> 6;
+    double *rs = P.rowstat + row * kLmStat;
+    if (threadIdx.x == 0) {
+        rs[0] = (double)m[0] + log2(t[0]);
+        rs[1] = (double)m[1] + log2(t[1]);
+        rs[2] = (double)m[2] + log2(t[2]);
+        rs[3] = (double)imin;
+    }
+    const long long bi = row / (P.K + 1);
+    const int i = (int)(row % (P.K + 1));
+    if (i < P.K && wave < 2) {
+        const int d = P.draft[bi * P.K + i];
+        if (d >= 0 && d < P.V) { // the draft's logits, exactly products of the stored values
+            const double x = wave == 0 ? lm_dot(P.ht + (size_t)row * P.Ht, P.Wt + (size_t)d * P.Ht, P.Ht)
+                                       : lm_dot(P.hb + (size_t)row * P.Hd, P.Wd + (size_t)d * P.Hd, P.Hd);
+            if ((threadIdx.x & 63) == 0)
+                rs[4 + wave] = x;
+        }
+    }
+}
+
+// Row i of request bi from its statistics and JSD partials, by one whole
+// wave; lane 0 writes the row's outputs.
 __device__ __forceinline__ void lmhead_finalize_row(const LmheadParams &P, long long bi, int i, int lane,
                                                     uint32_t *sh_acc, int *sh_fi) {
     const long long row = bi * (P.K + 1) + i;
-    const uint64_t *rec_row = P.rec + (size_t)row * P.S * kRecWords;
-    double L2[2];
-    team_lse<2, false, true>(rec_row, P.S, {1, 2}, {3, 4}, {true, false}, L2);
-    const double Lb = L2[0] * kLn2d, Lt = L2[1] * kLn2d;
-    // branch-free loops, so that unrolled iterations issue their loads together
-    float fbest = -__builtin_inff();
-#pragma unroll 4
-    for (int w = lane; w < P.S; w += 64)
-        fbest = fmaxf(fbest, unpack_hi(rec_row[(size_t)w * kRecWords + 4]));
-    fbest = wave_max(fbest);
     double jsum = 0.0;
-    int fidx = 0x7fffffff;
-#pragma unroll 4
-    for (int w = lane; w < P.S; w += 64) {
-        const uint64_t *r = rec_row + (size_t)w * kRecWords;
-        jsum += as_f64(r[6]);
-        const int ix = (int)(uint32_t)r[5];
-        fidx = unpack_hi(r[4]) == fbest ? min(fidx, ix) : fidx;
-    }
+    for (int c = lane; c < P.jc; c += 64)
+        jsum += P.jpart[row * P.jc + c];
     jsum = wave_sum(jsum);
-    fidx = wave_min_int(fidx);
-    int d = -1;
-    double td = 0.0, bd = 0.0;
-    if (i < P.K) {
-        d = P.draft[bi * P.K + i];
-        if (d >= 0 && d < P.V) { // the draft's logits, exactly products of the stored values
-            td = lm_dot(P.ht + (size_t)row * P.Ht, P.Wt + (size_t)d * P.Ht, P.Ht);
-            bd = lm_dot(P.hb + (size_t)row * P.Hd, P.Wd + (size_t)d * P.Hd, P.Hd);
-        }
-    }
     if (lane != 0)
         return;
+    const double *rs = P.rowstat + row * kLmStat;
+    const int fidx = (int)rs[3];
     const double Dr = -0.5 * kLn2d * jsum;
     P.D[row] = (float)Dr;
     P.geff[row] = (float)((double)P.gamma * exp(-Dr));
     P.fused[row] = fidx;
     uint32_t acc = 0;
     if (i < P.K) {
+        const int d = P.draft[bi * P.K + i];
         if (d < 0 || d >= P.V) {
             set_dev_err(P.dev_err, 1);
         } else {
-            const double margin = (td - Lt) - (bd - Lb) - P.log_gamma + Dr;
+            const double Lb = rs[1] * kLn2d, Lt = rs[2] * kLn2d;
+            const double margin = (rs[4] - Lt) - (rs[5] - Lb) - P.log_gamma + Dr;
             acc = margin > 0.0 ? 1u : 0u;
         }
         P.accept[bi * P.K + i] = (uint8_t)acc;
@@ -442,8 +448,53 @@ __device__ __forceinline__ void lmhead_finalize_row(const LmheadParams &P, long 
     sh_fi[i] = fidx;
 }
 
-// One workgroup per request: one wave per row (up to 16 waves; wave w takes
-// rows w, w + 16, ...), then one thread scans the request's accept flags.
+// Launch 3: the JSD terms of one row's stored pairs in [4096 c, 4096 c + 4096)
+// against the row's log-sum-exps, workgroup (row, c).  Each load instruction
+// reads 4 KB of consecutive pairs (streamed: they are read once); a thread
+// sums its 16 terms in fp32, the workgroup in fp64.
+__global__ __launch_bounds__(kThreads) void lmhead_jsd_kernel(LmheadParams P) {
+    __shared__ double sh[kWaves];
+    const long long row = blockIdx.x / P.jc;
+    const int c = (int)(blockIdx.x % P.jc);
+    const double La2 = P.rowstat[row * kLmStat + 0], Lb2 = P.rowstat[row * kLmStat + 1];
+    const double dl = (La2 - Lb2) * kLn2d;
+    const float la = (float)La2, lb = (float)Lb2, dh = (float)dl, dlo = (float)(dl - (double)dh);
+    // two pairs per 16-byte vector; a vector starting below V lies inside the
+    // row, whose stride is even
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    const f4v *src = reinterpret_cast<const f4v *>(P.lg + (size_t)row * P.lgs * 2);
+    const long long e0 = (long long)c * kLmJsdChunk + 2 * threadIdx.x;
+    constexpr int kVec = kLmJsdPairs / 2;
+    f4v v[kVec];
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) {
+        const long long e = e0 + 2LL * kThreads * i;
+        v[i] = e < P.V ? __builtin_nontemporal_load(src + (e >> 1)) : f4v{0.f, 0.f, 0.f, 0.f};
+    }
+    float J = 0.f;
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) {
+        const long long e = e0 + 2LL * kThreads * i;
+        if (e < P.V)
+            J += jsd_term(__fmaf_rn(v[i].x, kLog2e, -la), __fmaf_rn(v[i].y, kLog2e, -lb), ((v[i].x - v[i].y) - dh) - dlo);
+        if (e + 1 < P.V)
+            J += jsd_term(__fmaf_rn(v[i].z, kLog2e, -la), __fmaf_rn(v[i].w, kLog2e, -lb), ((v[i].z - v[i].w) - dh) - dlo);
+    }
+    const double w = wave_sum((double)J);
+    if ((threadIdx.x & 63) == 0)
+        sh[threadIdx.x >> 6] = w;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double t = 0.0;
+#pragma unroll
+        for (int k = 0; k < kWaves; ++k)
+            t += sh[k];
+        P.jpart[row * P.jc + c] = t;
+    }
+}
+
+// Launch 4: one workgroup per request, one wave per row (up to 16 waves; wave
+// w takes rows w, w + 16, ...), then one thread scans the accept flags.
 __global__ __launch_bounds__(kFinMaxThreads) void lmhead_finalize_kernel(LmheadParams P) {
     __shared__ uint32_t sh_acc[kMaxDrafts + 1];
     __shared__ int sh_fi[kMaxDrafts + 1];
@@ -466,29 +517,28 @@ __global__ __launch_bounds__(kFinMaxThreads) void lmhead_finalize_kernel(LmheadP
 
 int lmhead_blocks_per_cu() {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, lmhead_kernel<1>, kThreads, 0) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, lmhead_kernel, kThreads, 0) != hipSuccess)
         return 0;
     return n;
 }
 
 hipError_t launch_lmhead(const LmheadParams &p, hipStream_t s, hipEvent_t after_rows) {
     const unsigned grid = (unsigned)(8 * (long long)p.RT * ((p.S + 7) / 8));
-    const unsigned fin = (unsigned)((p.R + kWaves - 1) / kWaves);
-    hipLaunchKernelGGL((lmhead_kernel<1>), dim3(grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(lmhead_kernel, dim3(grid), dim3(kThreads), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
-        return e;
-    hipLaunchKernelGGL(lmhead_combine_kernel, dim3(fin), dim3(kThreads), 0, s, p);
-    if ((e = hipGetLastError()) != hipSuccess)
-        return e;
-    hipLaunchKernelGGL((lmhead_kernel<2>), dim3(grid), dim3(kThreads), 0, s, p);
-    if ((e = hipGetLastError()) != hipSuccess)
         return e;
     if (after_rows) {
         e = hipEventRecord(after_rows, s);
         if (e != hipSuccess)
             return e;
     }
+    hipLaunchKernelGGL(lmhead_combine_kernel, dim3((unsigned)p.R), dim3(kThreads), 0, s, p);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(lmhead_jsd_kernel, dim3((unsigned)(p.R * p.jc)), dim3(kThreads), 0, s, p);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
     hipLaunchKernelGGL(lmhead_finalize_kernel, dim3((unsigned)p.B), dim3(fin_threads(p.K + 1)), 0, s, p);
     return hipGetLastError();
 }

@@ -629,31 +629,45 @@ vwl_status asym_verify_xfam(const void *a, const void *b, int Vd, const void *t,
     return launch_xfam((int)dt, plan, p, stream, g_phase_event.load()) == hipSuccess ? VWL_OK : VWL_ERR_HIP;
 }
 
-// LM-head pass geometry: row tiles of kLmRowTile and vocabulary ranges (multiples of
-// 128 tokens) for about 1536 workgroups; depends on the shape only.
+// LM-head pass geometry: row tiles of kLmRowTile, vocabulary ranges
+// (multiples of 128 tokens) and the JSD pass's chunks.
 struct LmGeom {
-    int RT, S, range;
-    size_t rec, rowstat, total;
+    int RT, S, range, jc;
+    long long lgs;
+    size_t rec, rowstat, lg, jpart, total;
 };
 // Shapes and workspace layout.  The records hold one entry per (row,
 // vocabulary range) for up to one range per 128-column tile, so the size
-// does not depend on the device; lm_split picks the ranges at launch.
+// does not depend on the device; lm_split picks the ranges at launch.  Every
+// launch's work-items must number below 2^32.
 static bool lm_geometry(int B, int K, int V, int Hd, int Ht, LmGeom &g) {
     if (!shape_ok(B, K, V) || Hd < 64 || Ht < 64 || Hd % 64 || Ht % 64)
         return false;
     const long long R = (long long)B * (K + 1);
     const long long RT = (R + kLmRowTile - 1) / kLmRowTile;
+    const long long max_wgs = 0xffffffffLL / kThreads;
     if (RT > (1LL << 24))
         return false;
     const long long tiles = ((long long)V + 127) / 128;
-    if (8 * RT * ((tiles + 7) / 8) > 0x7fffffffLL)
+    if (8 * RT * ((tiles + 7) / 8) > max_wgs)
+        return false;
+    const long long jc = ((long long)V + kLmJsdChunk - 1) / kLmJsdChunk;
+    if (R * jc > max_wgs)
+        return false;
+    // the stored pairs cover whole tiles: RT * 64 rows of whole 128-token tiles
+    const long long lgs = tiles * 128;
+    if ((long double)(RT * kLmRowTile) * (long double)lgs * 8.0L > 4.0e18L)
         return false;
     g.RT = (int)RT;
     g.S = (int)tiles;
     g.range = 128;
+    g.jc = (int)jc;
+    g.lgs = lgs;
     size_t off = 0;
     g.rec = off;      off = align256(off + (size_t)R * tiles * kRecWords * 8);
-    g.rowstat = off;  off = align256(off + (size_t)R * 2 * 8);
+    g.rowstat = off;  off = align256(off + (size_t)R * kLmStat * 8);
+    g.jpart = off;    off = align256(off + (size_t)R * jc * 8);
+    g.lg = off;       off = align256(off + (size_t)(RT * kLmRowTile) * (size_t)lgs * 8);
     g.total = off;
     return true;
 }
@@ -739,6 +753,10 @@ vwl_status asym_verify_lmhead(const void *h_a, const void *h_b, const void *W_d,
     p.dev_err = dev_err;
     p.rec = reinterpret_cast<uint64_t *>(ws + g.rec);
     p.rowstat = reinterpret_cast<double *>(ws + g.rowstat);
+    p.lg = reinterpret_cast<float *>(ws + g.lg);
+    p.lgs = g.lgs;
+    p.jpart = reinterpret_cast<double *>(ws + g.jpart);
+    p.jc = g.jc;
     return launch_lmhead(p, stream, g_phase_event.load()) == hipSuccess ? VWL_OK : VWL_ERR_HIP;
 }
 

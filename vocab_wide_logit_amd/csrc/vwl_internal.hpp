@@ -165,10 +165,19 @@ struct LmheadParams {
     uint8_t *accept;
     int32_t *fused, *acc_len, *token, *dev_err;
     uint64_t *rec;    // [R][S][8], the row kernel's record layout
-    double *rowstat;  // [R][2] L_a, L_b (log2 units)
+    double *rowstat;  // [R][kLmStat] L_a, L_b, L_t (log2 units), fused token, t_d, b_d
+    float *lg;        // [RT * 64][lgs][2] the logit pairs (a, b) of the first launch
+    long long lgs;    // pairs per row of lg (V rounded up to whole 128-token tiles)
+    double *jpart;    // [R][jc] the JSD pass's partial sums
+    int jc;           // JSD chunks per row
 };
 // Rows per workgroup of the LM-head pass (MFMA row blocks of 16).
 constexpr int kLmRowTile = 64;
+constexpr int kLmStat = 6; // per-row statistics of the LM-head path
+// JSD pass over the stored pairs: 16 pairs per thread, so a workgroup chunk
+// is 4096 tokens.
+constexpr int kLmJsdPairs = 16;
+constexpr int kLmJsdChunk = kThreads * kLmJsdPairs;
 hipError_t launch_lmhead(const LmheadParams &p, hipStream_t s, hipEvent_t after_rows);
 int lmhead_blocks_per_cu();
 

@@ -181,19 +181,77 @@ __device__ __forceinline__ void lm_gemm(LmStage &st, const uint16_t *h0, const u
 __device__ __forceinline__ int lm_row(int m, int j) { return 16 * m + 4 * ((threadIdx.x & 63) >> 4) + j; }
 __device__ __forceinline__ int lm_col(int n) { return 32 * (threadIdx.x >> 6) + 16 * n + (threadIdx.x & 15); }
 
+// The waves' partials of a tile: a's and b's statistics, then t's and the
+// fused maxima with their columns.
 struct LmScratch {
-    float ref[kWaves][kLmRows][3];
-    float sum[kWaves][kLmRows][3];
-    float fm[kWaves][kLmRows];
-    int fi[kWaves][kLmRows];
+    float ref0[kWaves][kLmRows]; // a, then t
+    float sum0[kWaves][kLmRows];
+    float ref1[kWaves][kLmRows]; // b, then the fused maxima
+    union {
+        float sum1[kWaves][kLmRows]; // b
+        int fi[kWaves][kLmRows];     // the fused maxima's columns
+    };
 };
+// Running per-row state of the workgroup's rows across its tiles (in LDS,
+// so that no register holds it across the k loops).
+struct LmRun {
+    double s[3][kLmRows];
+    float c[3][kLmRows];
+    float fm[kLmRows];
+    int fi[kLmRows];
+};
+// Merge a partial (reference c, sum s) into a running fp64 state.
+__device__ __forceinline__ void lm_merge(float &run_c, double &run_s, float c, double s) {
+    const float C = fmaxf(run_c, c);
+    run_s = scale_pow2(run_s, run_c - C) + scale_pow2(s, c - C);
+    run_c = C;
+}
 
-// Per-row statistics of tensor k's block held as accumulators, written to
+// Fold the waves' partials into the running state: threads 0..63, one row
+// each, the waves in column order.  AB: a and b (tensors 0 and 1); else t
+// (tensor 2) and the fused maxima (a strict > keeps the lowest index).
+__device__ __forceinline__ void lm_fold_one(LmRun &run, int k, const float (&ref)[kWaves][kLmRows],
+                                            const float (&sum)[kWaves][kLmRows]) {
+    const int tid = threadIdx.x;
+    float c = run.c[k][tid];
+    double sm = run.s[k][tid];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+        lm_merge(c, sm, ref[w][tid], (double)sum[w][tid]);
+    run.c[k][tid] = c;
+    run.s[k][tid] = sm;
+}
+template <bool AB>
+__device__ __forceinline__ void lm_fold(LmRun &run, const LmScratch &sc, long long vt0) {
+    const int tid = threadIdx.x;
+    if (tid >= kLmRows)
+        return;
+    if (AB) {
+        lm_fold_one(run, 0, sc.ref0, sc.sum0);
+        lm_fold_one(run, 1, sc.ref1, sc.sum1);
+    } else {
+        lm_fold_one(run, 2, sc.ref0, sc.sum0);
+        float fm = run.fm[tid];
+        int fi = run.fi[tid];
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            if (sc.ref1[w][tid] > fm) {
+                fm = sc.ref1[w][tid];
+                fi = (int)vt0 + sc.fi[w][tid];
+            }
+        }
+        run.fm[tid] = fm;
+        run.fi[tid] = fi;
+    }
+}
+
+// Per-row statistics of one tensor's block held as accumulators, written to
 // the wave's scratch: for each of the lane's rows (m, j) the integer
 // reference and the fp32 sum of 2^(x*log2e - ref) over the wave's 32 columns
 // (identical in the 16 lanes of a DPP row; lane 0 of the row writes).
 // Invalid columns count as -inf.
-__device__ __forceinline__ void lm_tile_stats(LmScratch &sc, int k, const f32x4_t (&x)[kLmM][2], const bool (&cv)[2]) {
+__device__ __forceinline__ void lm_tile_stats(float (&ref)[kWaves][kLmRows], float (&sum)[kWaves][kLmRows],
+                                              const f32x4_t (&x)[kLmM][2], const bool (&cv)[2]) {
     const float NEG_INF = -__builtin_inff();
     const int wave = threadIdx.x >> 6;
 #pragma unroll
@@ -206,22 +264,17 @@ __device__ __forceinline__ void lm_tile_stats(LmScratch &sc, int k, const f32x4_
             const float sm = row16_sum(__builtin_amdgcn_exp2f(__fmaf_rn(x0, kLog2e, -c)) +
                                        __builtin_amdgcn_exp2f(__fmaf_rn(x1, kLog2e, -c)));
             if ((threadIdx.x & 15) == 0) {
-                sc.ref[wave][lm_row(m, j)][k] = c;
-                sc.sum[wave][lm_row(m, j)][k] = sm;
+                ref[wave][lm_row(m, j)] = c;
+                sum[wave][lm_row(m, j)] = sm;
             }
         }
 }
 
-// Merge a partial (reference c, sum s) into a running fp64 state.
-__device__ __forceinline__ void lm_merge(float &run_c, double &run_s, float c, double s) {
-    const float C = fmaxf(run_c, c);
-    run_s = scale_pow2(run_s, run_c - C) + scale_pow2(s, c - C);
-    run_c = C;
-}
 
 __global__ __launch_bounds__(kThreads, 3) void lmhead_kernel(LmheadParams P) {
     __shared__ LmStage st;
     __shared__ LmScratch sc;
+    __shared__ LmRun run;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // workgroup b runs on die b % 8: the row tiles of one vocabulary range
     // share a die, so its head tiles come from one L2
@@ -236,11 +289,16 @@ __global__ __launch_bounds__(kThreads, 3) void lmhead_kernel(LmheadParams P) {
     const long long v_end = min((long long)P.V, v_begin + P.range);
     const float NEG = -3.0e38f;
 
-    // running per-row state (threads 0..63, row = tid)
-    float rc[3] = {NEG, NEG, NEG};
-    double rs[3] = {0.0, 0.0, 0.0};
-    float rfm = -__builtin_inff();
-    int rfi = 0x7fffffff;
+    // running per-row state in LDS (threads 0..63, row = tid)
+    if (tid < kLmRows) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            run.c[k][tid] = NEG;
+            run.s[k][tid] = 0.0;
+        }
+        run.fm[tid] = -__builtin_inff();
+        run.fi[tid] = 0x7fffffff;
+    }
 
     for (long long vt0 = v_begin; vt0 < v_end; vt0 += kLmCols) {
         bool cv[2];
@@ -268,16 +326,18 @@ __global__ __launch_bounds__(kThreads, 3) void lmhead_kernel(LmheadParams P) {
                     __builtin_nontemporal_store(f32x2_t{xa[m][1][j], xb[m][1][j]}, qr + 16);
                 }
         }
-        lm_tile_stats(sc, 0, xa, cv);
-        lm_tile_stats(sc, 1, xb, cv);
+        lm_tile_stats(sc.ref0, sc.sum0, xa, cv);
+        lm_tile_stats(sc.ref1, sc.sum1, xb, cv);
 #pragma unroll
         for (int m = 0; m < kLmM; ++m)
 #pragma unroll
             for (int n = 0; n < 2; ++n)
                 xa[m][n] = xa[m][n] - xb[m][n];
+        __syncthreads();
+        lm_fold<true>(run, sc, vt0);
         f32x4_t xt[kLmM][2], unused[kLmM][2];
         lm_gemm<false>(st, P.ht, nullptr, P.Wt, row0, P.R, vt0, P.V, P.Ht, xt, unused);
-        lm_tile_stats(sc, 2, xt, cv);
+        lm_tile_stats(sc.ref0, sc.sum0, xt, cv);
 #pragma unroll
         for (int m = 0; m < kLmM; ++m)
 #pragma unroll
@@ -291,33 +351,22 @@ __global__ __launch_bounds__(kThreads, 3) void lmhead_kernel(LmheadParams P) {
                 const float fm = row16_max(fb);
                 const int fi = row16_min_int((fb == fm && (cv[0] || cv[1])) ? col : 0x7fffffff);
                 if ((lane & 15) == 0) {
-                    sc.fm[wave][lm_row(m, j)] = fm;
+                    sc.ref1[wave][lm_row(m, j)] = fm;
                     sc.fi[wave][lm_row(m, j)] = fi;
                 }
             }
         __syncthreads();
-        if (tid < kLmRows) { // waves in column order; strict > keeps the lowest index
-#pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
-#pragma unroll
-                for (int k = 0; k < 3; ++k)
-                    lm_merge(rc[k], rs[k], sc.ref[w][tid][k], (double)sc.sum[w][tid][k]);
-                if (sc.fm[w][tid] > rfm) {
-                    rfm = sc.fm[w][tid];
-                    rfi = (int)vt0 + sc.fi[w][tid];
-                }
-            }
-        }
+        lm_fold<false>(run, sc, vt0);
     }
     const long long row = row0 + tid;
     if (tid < kLmRows && row < P.R) {
         uint64_t *rec = P.rec + ((size_t)row * P.S + s) * kRecWords;
-        rec[0] = f64_bits(rs[0]);
-        rec[1] = f64_bits(rs[1]);
-        rec[2] = f64_bits(rs[2]);
-        rec[3] = pack2(rc[0], rc[1]);
-        rec[4] = pack2(rc[2], rfm);
-        rec[5] = (uint64_t)(uint32_t)rfi;
+        rec[0] = f64_bits(run.s[0][tid]);
+        rec[1] = f64_bits(run.s[1][tid]);
+        rec[2] = f64_bits(run.s[2][tid]);
+        rec[3] = pack2(run.c[0][tid], run.c[1][tid]);
+        rec[4] = pack2(run.c[2][tid], run.fm[tid]);
+        rec[5] = (uint64_t)(uint32_t)run.fi[tid];
     }
 }
 

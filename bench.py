@@ -240,9 +240,11 @@ def time_xfam(vwl, x, steps, warmup, copies=4):
 PEAK_BF16_TFLOPS = 2500.0  # dense bf16 matrix-core peak of one MI355X
 
 
-def time_lmhead(vwl, x, steps, warmup):
+def time_lmhead(vwl, x, steps, warmup, store_pairs=True):
     """asym_verify_lmhead calls on resident hidden states and heads; per-call
-    ms and the ms up to the end of the GEMM pass."""
+    ms and the ms up to the end of the last GEMM pass (the path that stores
+    the (a, b) pairs, or with store_pairs=False the one that forms a and b
+    twice)."""
     import numpy as np
     import torch
     bf = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16).cuda()
@@ -251,7 +253,7 @@ def time_lmhead(vwl, x, steps, warmup):
     out = vwl.asym_out(x.B, x.K, "cuda")
     settle_clocks()
     for _ in range(warmup):
-        vwl.asym_verify_lmhead(ha, hb, Wd, ht, Wt, d, x.beta, x.gamma, out=out)
+        vwl.asym_verify_lmhead(ha, hb, Wd, ht, Wt, d, x.beta, x.gamma, out=out, store_pairs=store_pairs)
     stream = torch.cuda.current_stream()
     start, mid, end = _events(steps), _events(steps), _events(steps)
     for e in mid:
@@ -260,7 +262,7 @@ def time_lmhead(vwl, x, steps, warmup):
     for i in range(steps):
         start[i].record(stream)
         vwl.set_phase_event(mid[i])
-        vwl.asym_verify_lmhead(ha, hb, Wd, ht, Wt, d, x.beta, x.gamma, out=out)
+        vwl.asym_verify_lmhead(ha, hb, Wd, ht, Wt, d, x.beta, x.gamma, out=out, store_pairs=store_pairs)
         end[i].record(stream)
     torch.cuda.synchronize()
     vwl.set_phase_event(None)
@@ -532,6 +534,12 @@ def secondary(args, vwl, W, x, bytes_per_call):
         "head_weight_gbs": wbytes / (ml * 1e-3) / 1e9,
         "roofline_bound_ms": bound_ms, "frac_of_roofline": bound_ms / ml,
         "flops_per_call": flops, "pair_bytes_per_call": 2.0 * 8 * Rl * xl.V}
+    # the path with no pair storage (minimal workspace): a and b formed twice
+    pn, rn = time_lmhead(vwl, xl, min(args.steps, 20), min(args.warmup, 3), store_pairs=False)
+    mn = _median(pn)
+    sec[xl.name]["no_pair_storage"] = {
+        "median_call_ms": mn, "median_gemm_passes_ms": _median(rn), "tflops": flops / (mn * 1e-3) / 1e12,
+        "executed_flops_per_call": flops + 2.0 * Rl * xl.V * 2 * xl.Hd, "frac_of_roofline": bound_ms / mn}
     for xe in (W.e2sci_batched(), W.e2sci_single()):
         pe, re_ = time_e2sci(vwl, xe, args.steps, args.warmup)
         me, mre = _median(pe), _median(re_)

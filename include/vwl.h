@@ -246,9 +246,13 @@ vwl_status asym_verify_xfam(const void *a, const void *b, int Vd, const void *t,
 /* ---------------------------------------------------------------------------
  * AsymSpec from hidden states (the step before the pass on the AsymSpec
  * pages: the LM heads turn hidden states into logits).  The heads' products
- * are formed on the matrix cores with the row statistics in their epilogue;
- * t is never written, and the drafter's logit pairs (a, b) are written once
- * to the workspace, as fp32, for the JSD pass:
+ * are formed on the matrix cores with the row statistics in their epilogue,
+ * and t is never written.  The JSD needs a and b again once their
+ * log-sum-exps are known: with a workspace of
+ * vwl_asym_lmhead_workspace_bytes the drafter's logit pairs (a, b) are
+ * written once to it, as fp32, and streamed back; with one of at least
+ * vwl_asym_lmhead_workspace_min_bytes (but less) a and b are formed again
+ * instead (the same bits), so no logit is ever written to memory:
  *   a = h_a W_d^T, b = h_b W_d^T (the drafter's head, full and compressed
  *   context), t = h_t W_t^T (the verifier's head); then everything as
  *   asym_verify (delta = a - b, the CDA gate).
@@ -261,10 +265,15 @@ vwl_status asym_verify_xfam(const void *a, const void *b, int Vd, const void *t,
  *   sum_k |h_k w_k| of its value; the draft's logits in the test are fp64
  *   dot products; statistics as asym_verify.
  * Workspace: vwl_asym_lmhead_workspace_bytes (shape only; about
- * 8 * B * (K+1) * V bytes, the stored pairs, plus the per-row records),
- * zero-filled before first use; left zero-filled where it must be.
+ * 8 * B * (K+1) * V bytes, the stored pairs, plus the per-row records and
+ * partials) for the stored pairs, at least
+ * vwl_asym_lmhead_workspace_min_bytes (the records and partials) for the
+ * path that forms a and b twice; smaller: VWL_ERR_WORKSPACE.  Zero-filled
+ * before first use; left zero-filled where it must be.  Both sizes are 0 for
+ * an invalid shape.
  * --------------------------------------------------------------------------- */
 size_t vwl_asym_lmhead_workspace_bytes(int B, int K, int V, int Hd, int Ht);
+size_t vwl_asym_lmhead_workspace_min_bytes(int B, int K, int V, int Hd, int Ht);
 
 vwl_status asym_verify_lmhead(const void *h_a, const void *h_b, const void *W_d,
                               const void *h_t, const void *W_t, const int32_t *draft,

@@ -101,6 +101,21 @@ def test_workspace_sizes(lib):
     assert lib.vwl_rapid_workspace_bytes(1, -1, 10, 0) == 0
 
 
+def test_lmhead_workspace_sizes(lib):
+    """The LM-head path's two workspace sizes: the full one holds the fp32
+    (a, b) pairs of whole 64-row and 128-token tiles beyond the minimal one
+    (records and partials); both 256-byte multiples, 0 for invalid shapes."""
+    for (B, K, V, Hd, Ht) in [(1, 0, 1, 64, 64), (3, 2, 1000, 128, 128), (64, 2, 151936, 2560, 5120)]:
+        full = lib.vwl_asym_lmhead_workspace_bytes(B, K, V, Hd, Ht)
+        small = lib.vwl_asym_lmhead_workspace_min_bytes(B, K, V, Hd, Ht)
+        assert 0 < small < full and small % 256 == 0 and full % 256 == 0
+        rows = -(-B * (K + 1) // 64) * 64
+        assert full - small >= rows * (-(-V // 128) * 128) * 8
+    for bad in [(0, 2, 10, 64, 64), (1, 2, 10, 96, 64), (1, 2, 10, 64, 32), (1, 64, 10, 64, 64)]:
+        assert lib.vwl_asym_lmhead_workspace_bytes(*bad) == 0
+        assert lib.vwl_asym_lmhead_workspace_min_bytes(*bad) == 0
+
+
 def _p(addr):
     return ctypes.c_void_p(addr)
 

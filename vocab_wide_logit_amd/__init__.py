@@ -21,7 +21,9 @@ Entry points (same names as the C ABI):
   rows on the drafter vocabulary, verifier rows on the verifier's, joined by
   a vocabulary alignment (verifier id -> paired drafter id or -1).
 * ``asym_verify_lmhead`` -- the AsymSpec pass from hidden states: the LM
-  heads' products on the matrix cores with the pass in their epilogue.
+  heads' products on the matrix cores with the row statistics in their
+  epilogue; the JSD from stored (a, b) pairs, or, with ``store_pairs=False``,
+  from a and b formed a second time (no logit written).
 * ``e2sci_verify`` -- E2-SCI adaptive JSD acceptance (E2-SCI notes, key
   design 3): per-position divergence of drafter and target against the
   window threshold, then the caller-owned credit state and next threshold.
@@ -62,7 +64,8 @@ SYMBOLS = ("vwl_status_string", "vwl_version", "vwl_workspace_reset",
            "vwl_set_plan_override", "vwl_set_xfam_override", "vwl_set_phase_event",
            "vwl_e2sci_workspace_bytes", "e2sci_verify", "vwl_e2sci_plan_info",
            "vwl_asym_xfam_workspace_bytes", "asym_verify_xfam",
-           "vwl_asym_lmhead_workspace_bytes", "asym_verify_lmhead", "asym_verify_noalloc")
+           "vwl_asym_lmhead_workspace_bytes", "vwl_asym_lmhead_workspace_min_bytes", "asym_verify_lmhead",
+           "asym_verify_noalloc")
 
 
 class E2sciParams(ctypes.Structure):
@@ -130,6 +133,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.vwl_set_xfam_override.restype = i
         lib.vwl_asym_lmhead_workspace_bytes.argtypes = [i, i, i, i, i]
         lib.vwl_asym_lmhead_workspace_bytes.restype = sz
+        lib.vwl_asym_lmhead_workspace_min_bytes.argtypes = [i, i, i, i, i]
+        lib.vwl_asym_lmhead_workspace_min_bytes.restype = sz
         lib.asym_verify_lmhead.argtypes = [P, P, P, P, P, P, i, i, i, i, i, f, f, P, P, P, P, P, P, P, P, sz, P]
         lib.asym_verify_lmhead.restype = i
         lib.vwl_asym_xfam_workspace_bytes.argtypes = [i, i, i, i, i]
@@ -484,10 +489,14 @@ def asym_verify_xfam(a: torch.Tensor, b: torch.Tensor, t: torch.Tensor, vmap: to
 
 def asym_verify_lmhead(h_a: torch.Tensor, h_b: torch.Tensor, W_d: torch.Tensor, h_t: torch.Tensor,
                        W_t: torch.Tensor, draft: torch.Tensor, beta: float, gamma: float, *,
-                       out: Optional[AsymOut] = None, workspace: Optional[torch.Tensor] = None) -> AsymOut:
+                       out: Optional[AsymOut] = None, workspace: Optional[torch.Tensor] = None,
+                       store_pairs: bool = True) -> AsymOut:
     """AsymSpec from hidden states on the current stream (bf16 tensors):
     h_a, h_b [B, K+1, Hd], h_t [B, K+1, Ht], W_d [V, Hd], W_t [V, Ht];
-    draft [B, K] int32."""
+    draft [B, K] int32.  store_pairs: the cached workspace holds the fp32
+    (a, b) pairs (8 B (K+1) V bytes) for the JSD pass; False sizes it for
+    the path that forms a and b twice instead.  A caller's workspace picks
+    the path by its size."""
     lib = load_library()
     for name, x in (("h_a", h_a), ("h_b", h_b), ("W_d", W_d), ("h_t", h_t), ("W_t", W_t)):
         _dev_tensor(x, name, torch.bfloat16)
@@ -506,8 +515,9 @@ def asym_verify_lmhead(h_a: torch.Tensor, h_b: torch.Tensor, W_d: torch.Tensor, 
         out = asym_out(B, K, h_a.device)
     stream = _stream_ptr(h_a.device)
     if workspace is None:
-        workspace = _workspace_sized(("lmhead", B, K, V, Hd, Ht),
-                                     lambda: lib.vwl_asym_lmhead_workspace_bytes(B, K, V, Hd, Ht), h_a.device, stream)
+        size = lib.vwl_asym_lmhead_workspace_bytes if store_pairs else lib.vwl_asym_lmhead_workspace_min_bytes
+        workspace = _workspace_sized(("lmhead", bool(store_pairs), B, K, V, Hd, Ht),
+                                     lambda: size(B, K, V, Hd, Ht), h_a.device, stream)
     code = lib.asym_verify_lmhead(_ptr(h_a), _ptr(h_b), _ptr(W_d), _ptr(h_t), _ptr(W_t),
                                   _ptr(draft) if K > 0 else None, B, K, V, Hd, Ht, float(beta), float(gamma),
                                   _ptr(out.D), _ptr(out.gamma_eff), _ptr(out.accept) if K > 0 else None,

@@ -7,19 +7,22 @@
 //   a = h_a W_d^T, b = h_b W_d^T   (one drafter head, two views)
 //   t = h_t W_t^T
 //
-// Launch 1, lmhead_kernel: each workgroup owns 64 rows and a range of the
+// Launch 1, lmhead_kernel<1, STORE>: each workgroup owns 64 rows and a range of the
 // vocabulary, walked in tiles of 128 tokens.  Per tile the 4 waves form a
 // [64 x 128] block of a, b (sharing each W_d tile) and then of t with bf16
 // MFMA 16x16x32 (fp32 accumulation), staged through LDS in 64-wide k
 // blocks; the epilogue folds the block into per-row online statistics of a,
 // b, t (integer references, as in the row kernel) and the fused maximum
-// t + beta*(a - b) with its lowest index, and stores the (a, b) pairs as
-// fp32 for the JSD.  One record per (row, range), in the row kernel's record
-// layout.
+// t + beta*(a - b) with its lowest index, and, with a workspace that holds
+// them, stores the (a, b) pairs as fp32 for the JSD.  One record per (row,
+// range), in the row kernel's record layout.
 // Launch 2, lmhead_combine_kernel: per row, L_a, L_b, L_t and the fused
 // token from the records, and the draft's logits as fp64 dot products.
-// Launch 3, lmhead_jsd_kernel: the JSD terms of the stored pairs against
-// L_a, L_b, one partial sum per (row, 4096-token chunk).
+// Launch 3, the JSD terms against L_a, L_b: lmhead_jsd_kernel over the stored
+// pairs, one partial sum per (row, 4096-token chunk); or, with no pair
+// storage (no logit is then ever written), lmhead_kernel<2, false>: a and b
+// formed again by the same code (the same bits), one partial per (row,
+// range).
 // Launch 4, lmhead_finalize_kernel: D, the threshold, the test and the scan.
 #include "asym_kernels.hpp"
 
@@ -193,12 +196,18 @@ struct LmScratch {
     };
 };
 // Running per-row state of the workgroup's rows across its tiles (in LDS,
-// so that no register holds it across the k loops).
+// so that no register holds it across the k loops): the statistics of the
+// first pass, or the JSD sum of the recomputing pass.
 struct LmRun {
     double s[3][kLmRows];
     float c[3][kLmRows];
     float fm[kLmRows];
     int fi[kLmRows];
+};
+// Row constants of the recomputing pass: L_a, L_b (log2 units) and their
+// difference in nats as a float pair.
+struct LmRowC {
+    float la[kLmRows], lb[kLmRows], dh[kLmRows], dlo[kLmRows];
 };
 // Merge a partial (reference c, sum s) into a running fp64 state.
 __device__ __forceinline__ void lm_merge(float &run_c, double &run_s, float c, double s) {
@@ -271,10 +280,17 @@ __device__ __forceinline__ void lm_tile_stats(float (&ref)[kWaves][kLmRows], flo
 }
 
 
+// PASS 1: the statistics of a, b, t and the fused maximum; with STORE the
+// (a, b) pairs are also written for the JSD pass.  PASS 2 (the path with no
+// pair storage): a and b formed again by the same code, so with the same
+// bits, and the JSD terms against L_a, L_b summed into one partial per (row,
+// range).
+template <int PASS, bool STORE>
 __global__ __launch_bounds__(kThreads, 3) void lmhead_kernel(LmheadParams P) {
     __shared__ LmStage st;
     __shared__ LmScratch sc;
     __shared__ LmRun run;
+    __shared__ LmRowC rowc;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // workgroup b runs on die b % 8: the row tiles of one vocabulary range
     // share a die, so its head tiles come from one L2
@@ -298,6 +314,15 @@ __global__ __launch_bounds__(kThreads, 3) void lmhead_kernel(LmheadParams P) {
         }
         run.fm[tid] = -__builtin_inff();
         run.fi[tid] = 0x7fffffff;
+        if (PASS == 2) {
+            const long long row = min(row0 + tid, P.R - 1);
+            const double La2 = P.rowstat[row * kLmStat + 0], Lb2 = P.rowstat[row * kLmStat + 1];
+            const double dl = (La2 - Lb2) * kLn2d;
+            rowc.la[tid] = (float)La2;
+            rowc.lb[tid] = (float)Lb2;
+            rowc.dh[tid] = (float)dl;
+            rowc.dlo[tid] = (float)(dl - (double)(float)dl);
+        }
     }
 
     for (long long vt0 = v_begin; vt0 < v_end; vt0 += kLmCols) {
@@ -307,13 +332,44 @@ __global__ __launch_bounds__(kThreads, 3) void lmhead_kernel(LmheadParams P) {
             cv[n] = vt0 + lm_col(n) < v_end;
         f32x4_t xa[kLmM][2], xb[kLmM][2];
         lm_gemm<true>(st, P.ha, P.hb, P.Wd, row0, P.R, vt0, P.V, P.Hd, xa, xb);
-        // the pairs for the JSD pass, streamed (read once, by the next
-        // launch but one): lg has a row for every row of the tile and a
-        // column for every column of the tile, so the stores need no guard
-        // (the pairs past R or V are never read).  The row stride is re-read
-        // opaquely per tile, so the 16 row offsets are formed here rather
-        // than held in registers across the loop.
-        {
+        if (PASS == 2) {
+            // JSD terms of the block against the row's log-sum-exps
+#pragma unroll
+            for (int m = 0; m < kLmM; ++m)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = lm_row(m, j);
+                    const float la_c = rowc.la[r], lb_c = rowc.lb[r], dh = rowc.dh[r], dlo = rowc.dlo[r];
+                    float J = 0.f;
+#pragma unroll
+                    for (int n = 0; n < 2; ++n) {
+                        if (cv[n]) {
+                            const float a = xa[m][n][j], bb = xb[m][n][j];
+                            J += jsd_term(__fmaf_rn(a, kLog2e, -la_c), __fmaf_rn(bb, kLog2e, -lb_c),
+                                          ((a - bb) - dh) - dlo);
+                        }
+                    }
+                    J = row16_sum(J);
+                    if ((lane & 15) == 0)
+                        sc.sum0[wave][r] = J;
+                }
+            __syncthreads();
+            if (tid < kLmRows) { // the waves in column order
+                double t = run.s[0][tid];
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w)
+                    t += (double)sc.sum0[w][tid];
+                run.s[0][tid] = t;
+            }
+            continue;
+        }
+        // with STORE, the pairs for the JSD pass, streamed (read once, by
+        // the next launch but one): lg has a row for every row of the tile
+        // and a column for every column of the tile, so the stores need no
+        // guard (the pairs past R or V are never read).  The row stride is
+        // re-read opaquely per tile, so the 16 row offsets are formed here
+        // rather than held in registers across the loop.
+        if (STORE) {
             long long lgs = P.lgs;
             asm volatile("" : "+s"(lgs));
             f32x2_t *q = reinterpret_cast<f32x2_t *>(P.lg) + (row0 + lm_row(0, 0)) * lgs + vt0 + lm_col(0);
@@ -359,6 +415,11 @@ __global__ __launch_bounds__(kThreads, 3) void lmhead_kernel(LmheadParams P) {
         lm_fold<false>(run, sc, vt0);
     }
     const long long row = row0 + tid;
+    if (PASS == 2) {
+        if (tid < kLmRows && row < P.R)
+            P.jpart[row * P.jc + s] = run.s[0][tid];
+        return;
+    }
     if (tid < kLmRows && row < P.R) {
         uint64_t *rec = P.rec + ((size_t)row * P.S + s) * kRecWords;
         rec[0] = f64_bits(run.s[0][tid]);
@@ -566,18 +627,22 @@ __global__ __launch_bounds__(kFinMaxThreads) void lmhead_finalize_kernel(LmheadP
 
 int lmhead_blocks_per_cu() {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, lmhead_kernel, kThreads, 0) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, lmhead_kernel<1, true>, kThreads, 0) != hipSuccess)
         return 0;
     return n;
 }
 
 hipError_t launch_lmhead(const LmheadParams &p, hipStream_t s, hipEvent_t after_rows) {
     const unsigned grid = (unsigned)(8 * (long long)p.RT * ((p.S + 7) / 8));
-    hipLaunchKernelGGL(lmhead_kernel, dim3(grid), dim3(kThreads), 0, s, p);
+    const bool store = p.lg != nullptr;
+    if (store)
+        hipLaunchKernelGGL((lmhead_kernel<1, true>), dim3(grid), dim3(kThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((lmhead_kernel<1, false>), dim3(grid), dim3(kThreads), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    if (after_rows) {
+    if (store && after_rows) {
         e = hipEventRecord(after_rows, s);
         if (e != hipSuccess)
             return e;
@@ -585,7 +650,18 @@ hipError_t launch_lmhead(const LmheadParams &p, hipStream_t s, hipEvent_t after_
     hipLaunchKernelGGL(lmhead_combine_kernel, dim3((unsigned)p.R), dim3(kThreads), 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
-    hipLaunchKernelGGL(lmhead_jsd_kernel, dim3((unsigned)(p.R * p.jc)), dim3(kThreads), 0, s, p);
+    if (store) {
+        hipLaunchKernelGGL(lmhead_jsd_kernel, dim3((unsigned)(p.R * p.jc)), dim3(kThreads), 0, s, p);
+    } else {
+        hipLaunchKernelGGL((lmhead_kernel<2, false>), dim3(grid), dim3(kThreads), 0, s, p);
+        if ((e = hipGetLastError()) != hipSuccess)
+            return e;
+        if (after_rows) {
+            e = hipEventRecord(after_rows, s);
+            if (e != hipSuccess)
+                return e;
+        }
+    }
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
     hipLaunchKernelGGL(lmhead_finalize_kernel, dim3((unsigned)p.B), dim3(fin_threads(p.K + 1)), 0, s, p);

@@ -634,12 +634,15 @@ vwl_status asym_verify_xfam(const void *a, const void *b, int Vd, const void *t,
 struct LmGeom {
     int RT, S, range, jc;
     long long lgs;
-    size_t rec, rowstat, lg, jpart, total;
+    size_t rec, rowstat, lg, jpart, total_min, total;
 };
 // Shapes and workspace layout.  The records hold one entry per (row,
 // vocabulary range) for up to one range per 128-column tile, so the size
-// does not depend on the device; lm_split picks the ranges at launch.  Every
-// launch's work-items must number below 2^32.
+// does not depend on the device; lm_split picks the ranges at launch.  The
+// JSD partials are sized for either JSD pass (one per 4096 tokens or one per
+// range), and the stored pairs come last: a workspace of total_min bytes
+// runs the path with no pair storage.  Every launch's work-items must number
+// below 2^32.
 static bool lm_geometry(int B, int K, int V, int Hd, int Ht, LmGeom &g) {
     if (!shape_ok(B, K, V) || Hd < 64 || Ht < 64 || Hd % 64 || Ht % 64)
         return false;
@@ -666,7 +669,8 @@ static bool lm_geometry(int B, int K, int V, int Hd, int Ht, LmGeom &g) {
     size_t off = 0;
     g.rec = off;      off = align256(off + (size_t)R * tiles * kRecWords * 8);
     g.rowstat = off;  off = align256(off + (size_t)R * kLmStat * 8);
-    g.jpart = off;    off = align256(off + (size_t)R * jc * 8);
+    g.jpart = off;    off = align256(off + (size_t)R * (size_t)(tiles > jc ? tiles : jc) * 8);
+    g.total_min = off;
     g.lg = off;       off = align256(off + (size_t)(RT * kLmRowTile) * (size_t)lgs * 8);
     g.total = off;
     return true;
@@ -698,6 +702,11 @@ size_t vwl_asym_lmhead_workspace_bytes(int B, int K, int V, int Hd, int Ht) {
     return lm_geometry(B, K, V, Hd, Ht, g) ? g.total : 0;
 }
 
+size_t vwl_asym_lmhead_workspace_min_bytes(int B, int K, int V, int Hd, int Ht) {
+    LmGeom g;
+    return lm_geometry(B, K, V, Hd, Ht, g) ? g.total_min : 0;
+}
+
 vwl_status asym_verify_lmhead(const void *h_a, const void *h_b, const void *W_d, const void *h_t, const void *W_t,
                               const int32_t *draft, int B, int K, int V, int Hd, int Ht, float beta, float gamma,
                               float *D, float *gamma_eff, uint8_t *accept, int32_t *fused, int32_t *accept_len,
@@ -720,10 +729,11 @@ vwl_status asym_verify_lmhead(const void *h_a, const void *h_b, const void *W_d,
         !aligned(D, 4) || !aligned(gamma_eff, 4) || !aligned(fused, 4) || !aligned(accept_len, 4) ||
         !aligned(token, 4) || (draft && !aligned(draft, 4)) || (dev_err && !aligned(dev_err, 4)))
         return VWL_ERR_ALIGN;
-    if (!workspace || workspace_bytes < g.total)
+    if (!workspace || workspace_bytes < g.total_min)
         return VWL_ERR_WORKSPACE;
     if (!aligned(workspace, 256))
         return VWL_ERR_ALIGN;
+    const bool store = workspace_bytes >= g.total; // room for the (a, b) pairs
     char *ws = static_cast<char *>(workspace);
     LmheadParams p{};
     p.ha = static_cast<const uint16_t *>(h_a);
@@ -753,10 +763,10 @@ vwl_status asym_verify_lmhead(const void *h_a, const void *h_b, const void *W_d,
     p.dev_err = dev_err;
     p.rec = reinterpret_cast<uint64_t *>(ws + g.rec);
     p.rowstat = reinterpret_cast<double *>(ws + g.rowstat);
-    p.lg = reinterpret_cast<float *>(ws + g.lg);
+    p.lg = store ? reinterpret_cast<float *>(ws + g.lg) : nullptr;
     p.lgs = g.lgs;
     p.jpart = reinterpret_cast<double *>(ws + g.jpart);
-    p.jc = g.jc;
+    p.jc = store ? g.jc : g.S; // JSD partials per row: per 4096 tokens, or per range
     return launch_lmhead(p, stream, g_phase_event.load()) == hipSuccess ? VWL_OK : VWL_ERR_HIP;
 }
 

@@ -7,8 +7,8 @@
 //   a = h_a W_d^T, b = h_b W_d^T   (one drafter head, two views)
 //   t = h_t W_t^T
 //
-// Launch 1, lmhead_kernel<1, STORE>: each workgroup owns 64 rows and a range of the
-// vocabulary, walked in tiles of 128 tokens.  Per tile the 4 waves form a
+// Launch 1, lmhead_kernel<1, STORE>: each workgroup owns 64 rows and a
+// range of the vocabulary, walked in tiles of 128 tokens.  Per tile the 4 waves form a
 // [64 x 128] block of a, b (sharing each W_d tile) and then of t with bf16
 // MFMA 16x16x32 (fp32 accumulation), staged through LDS in 64-wide k
 // blocks; the epilogue folds the block into per-row online statistics of a,
@@ -216,9 +216,8 @@ __device__ __forceinline__ void lm_merge(float &run_c, double &run_s, float c, d
     run_c = C;
 }
 
-// Fold the waves' partials into the running state: threads 0..63, one row
-// each, the waves in column order.  AB: a and b (tensors 0 and 1); else t
-// (tensor 2) and the fused maxima (a strict > keeps the lowest index).
+// Fold the waves' partials of tensor k into its running state (one thread
+// per row), the waves in column order.
 __device__ __forceinline__ void lm_fold_one(LmRun &run, int k, const float (&ref)[kWaves][kLmRows],
                                             const float (&sum)[kWaves][kLmRows]) {
     const int tid = threadIdx.x;
@@ -230,6 +229,9 @@ __device__ __forceinline__ void lm_fold_one(LmRun &run, int k, const float (&ref
     run.c[k][tid] = c;
     run.s[k][tid] = sm;
 }
+// The tile's partials into the running state: threads 0..63, one row each.
+// AB: a and b (tensors 0 and 1); else t (tensor 2) and the fused maxima (a
+// strict > keeps the lowest index).
 template <bool AB>
 __device__ __forceinline__ void lm_fold(LmRun &run, const LmScratch &sc, long long vt0) {
     const int tid = threadIdx.x;

@@ -65,10 +65,12 @@ def test_small(vwl):
 
 
 @pytest.mark.parametrize("B,K,V,Hd", [(1, 0, 1, 64), (2, 1, 127, 64), (5, 4, 129, 192), (30, 2, 3001, 64),
-                                      (23, 3, 20000, 128)])
+                                      (23, 3, 20000, 128), (43, 2, 3001, 64), (50, 2, 1000, 128),
+                                      (70, 2, 5000, 64), (129, 0, 700, 64)])
 def test_shapes(vwl, B, K, V, Hd):
-    """Row counts that are not multiples of the 64-row tile, vocabularies
-    below, at and past the 128-token tile, one token, no drafts."""
+    """Row counts that are not multiples of the row tile (64 rows up to 128,
+    192 rows past that: 129, 150, 210 rows), vocabularies below, at and past
+    the 128-token tile, one token, no drafts."""
     x = W.gen_lmhead(B, K, max(V, 2), Hd, seed=82 + V + B) if V > 1 else None
     if x is None:  # one-token vocabulary: the generator needs two tokens to plant a spike
         x = W.gen_lmhead(B, K, 2, Hd, seed=82)

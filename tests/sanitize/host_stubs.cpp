@@ -37,6 +37,6 @@ hipError_t launch_rapid(int, const Plan &, const RapidParams &, hipStream_t, hip
 hipError_t launch_lmhead(const LmheadParams &, hipStream_t, hipEvent_t) { reached("launch_lmhead"); }
 hipError_t launch_fill_zero(void *, size_t, hipStream_t) { reached("launch_fill_zero"); }
 int rapid_blocks_per_cu(int, int) { return 0; }
-int lmhead_blocks_per_cu() { return 0; }
+int lmhead_blocks_per_cu(int) { return 0; }
 
 } // namespace vwl

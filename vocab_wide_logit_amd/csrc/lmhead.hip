@@ -7,22 +7,25 @@
 //   a = h_a W_d^T, b = h_b W_d^T   (one drafter head, two views)
 //   t = h_t W_t^T
 //
-// Launch 1, lmhead_kernel<1, STORE>: each workgroup owns 64 rows and a
-// range of the vocabulary, walked in tiles of 128 tokens.  Per tile the 4 waves form a
-// [64 x 128] block of a, b (sharing each W_d tile) and then of t with bf16
-// MFMA 16x16x32 (fp32 accumulation), staged through LDS in 64-wide k
-// blocks; the epilogue folds the block into per-row online statistics of a,
-// b, t (integer references, as in the row kernel) and the fused maximum
-// t + beta*(a - b) with its lowest index, and, with a workspace that holds
-// them, stores the (a, b) pairs as fp32 for the JSD.  One record per (row,
-// range), in the row kernel's record layout.
+// Launch 1, lmhead_kernel<1, STORE, G>: each workgroup owns 64 G rows (G
+// groups of 4 waves: one group up to 128 rows, three past that) and a range
+// of the vocabulary, walked in tiles of 128 tokens.  Per tile each group's
+// 4 waves form a [64 x 128] block of a, b (all groups sharing each W_d
+// tile) and then of t with bf16 MFMA 16x16x32 (fp32 accumulation), staged
+// through LDS in 64-wide k blocks (with three groups in two buffers, the
+// next block's loads in flight during the current one); the epilogue folds
+// the block into per-row online statistics of a, b, t (integer references,
+// as in the row kernel) and the fused maximum t + beta*(a - b) with its
+// lowest index, and, with a workspace that holds them, stores the (a, b)
+// pairs as fp32 for the JSD.  One record per (row, range), in the row
+// kernel's record layout.
 // Launch 2, lmhead_combine_kernel: per row, L_a, L_b, L_t and the fused
 // token from the records, and the draft's logits as fp64 dot products.
 // Launch 3, the JSD terms against L_a, L_b: lmhead_jsd_kernel over the stored
 // pairs, one partial sum per (row, 4096-token chunk); or, with no pair
-// storage (no logit is then ever written), lmhead_kernel<2, false>: a and b
-// formed again by the same code (the same bits), one partial per (row,
-// range).
+// storage (no logit is then ever written), lmhead_kernel<2, false, 1>: a
+// and b formed again by the same arithmetic (the same bits), one partial per
+// (row, range).
 // Launch 4, lmhead_finalize_kernel: D, the threshold, the test and the scan.
 #include "asym_kernels.hpp"
 
@@ -32,17 +35,22 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kLmRows = kLmRowTile; // rows per workgroup
+constexpr int kLmRows = kLmRowTile; // rows per group of 4 waves
 constexpr int kLmM = kLmRows / 16;   // MFMA row blocks of 16
 constexpr int kLmCols = 128; // vocabulary per tile (32 per wave, 2 MFMA column blocks)
 constexpr int kLmKB = 64;    // k per LDS stage (2 MFMA k-steps of 32)
+// A workgroup is G groups of 4 waves over 64 G rows; the groups share each
+// head tile.  Waves issuing the head tile's staging loads:
+template <int G>
+constexpr int lm_w_waves() { return G == 1 ? 4 : 8; }
 
 // One stage: [rows][8 chunks of 8 bf16]; chunk c of row r sits in slot
 // c ^ (r & 7), so the 16 rows an MFMA operand read touches spread over the
 // banks.
+template <int G>
 struct LmStage {
-    uint4 a[kLmRows * 8];
-    uint4 b[kLmRows * 8];
+    uint4 a[G * kLmRows * 8];
+    uint4 b[G * kLmRows * 8];
     uint4 w[kLmCols * 8];
 };
 
@@ -55,21 +63,21 @@ __device__ __forceinline__ int lm_slot(int r, int c) { return r * 8 + (c ^ (r & 
 // The lane's byte offsets from the block's base are the same for every k
 // block of a tile, so they are formed once per tile; per block the loads
 // are a scalar base plus those offsets, with no vector arithmetic.
-template <int NR>
+template <int NR, int NW>
 struct LmLoads {
-    static constexpr int kN = NR * 8 / 64 / kWaves; // instructions per wave
-    static_assert(NR * 8 % (64 * kWaves) == 0, "every wave issues the same number of stage loads");
+    static constexpr int kN = NR * 8 / 64 / NW; // instructions per issuing wave
+    static_assert(NR * 8 % (64 * NW) == 0, "every issuing wave issues the same number of stage loads");
     uint32_t off[kN]; // lane byte offsets from the block base
     uint32_t lds[kN]; // LDS destinations (wave-uniform)
 };
 
-template <int NR>
-__device__ __forceinline__ void lm_loads(LmLoads<NR> &L, uint4 *dst, long long row0, long long max_row, int H) {
+template <int NR, int NW>
+__device__ __forceinline__ void lm_loads(LmLoads<NR, NW> &L, uint4 *dst, long long row0, long long max_row, int H) {
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) % NW; // non-issuing waves: unused
 #pragma unroll
-    for (int i = 0; i < LmLoads<NR>::kN; ++i) {
-        const int j = wave + i * kWaves;
+    for (int i = 0; i < LmLoads<NR, NW>::kN; ++i) {
+        const int j = wave + i * NW;
         const int p = j * 64 + lane;
         const int r = p >> 3, slot = p & 7;
         const int c = slot ^ (r & 7);
@@ -84,10 +92,12 @@ __device__ __forceinline__ void lm_loads(LmLoads<NR> &L, uint4 *dst, long long r
 // gives the wait states the hardware needs after M0 or the base is
 // written), so the compiler does not track them: lm_gemm waits for them
 // explicitly before its barrier.
-template <int NR>
-__device__ __forceinline__ void lm_issue(const LmLoads<NR> &L, const uint16_t *base) {
+template <int NR, int NW>
+__device__ __forceinline__ void lm_issue(const LmLoads<NR, NW> &L, const uint16_t *base) {
+    if (__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) >= NW)
+        return;
 #pragma unroll
-    for (int i = 0; i < LmLoads<NR>::kN; ++i)
+    for (int i = 0; i < LmLoads<NR, NW>::kN; ++i)
         asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(L.off[i]), "s"(base), "{m0}"(L.lds[i])
                      : "memory");
 }
@@ -120,14 +130,21 @@ __device__ __forceinline__ int row16_min_int(int x) {
     return min(x, dpp_i<kDppMirror>(x));
 }
 
-// The [64 x 128] block of one head for one or two sets of hidden states
-// (TWO: h0 and h1 share the head tile), accumulated over k in [0, H).
-template <bool TWO>
-__device__ __forceinline__ void lm_gemm(LmStage &st, const uint16_t *h0, const uint16_t *h1, const uint16_t *W,
-                                        long long row0, long long R, long long vt0, int V, int H,
+// The [64 G x 128] block of one head for one or two sets of hidden states
+// (TWO: h0 and h1 share the head tile), accumulated over k in [0, H); each
+// wave forms [64 x 32] of it (group wave / 4, columns of wave % 4).  With
+// NS = 2 staging buffers the loads of k block i + 1 are in flight while the
+// waves work on block i (barriers without a wait for global loads, and an
+// explicit wait for all but the block just issued).
+template <bool TWO, int G, int NS>
+__device__ __forceinline__ void lm_gemm(LmStage<G> (&st)[NS], const uint16_t *h0, const uint16_t *h1,
+                                        const uint16_t *W, long long row0, long long R, long long vt0, int V, int H,
                                         f32x4_t (&acc0)[kLmM][2], f32x4_t (&acc1)[kLmM][2]) {
+    using LA = LmLoads<G * kLmRows, 4 * G>;
+    using LW = LmLoads<kLmCols, lm_w_waves<G>()>;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wq = (threadIdx.x >> 6) & 3;        // the wave's 32 columns
+    const int gr = kLmRows * (threadIdx.x >> 8); // the wave's group's first row
 #pragma unroll
     for (int m = 0; m < kLmM; ++m)
 #pragma unroll
@@ -135,79 +152,134 @@ __device__ __forceinline__ void lm_gemm(LmStage &st, const uint16_t *h0, const u
             acc0[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             acc1[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
-    LmLoads<kLmRows> la;
-    LmLoads<kLmCols> lw;
-    lm_loads(la, st.a, row0, R - 1, H);
-    lm_loads(lw, st.w, vt0, V - 1, H);
-    const uint32_t lds_b = (uint32_t)(reinterpret_cast<uintptr_t>(st.b) - reinterpret_cast<uintptr_t>(st.a));
+    LA la;
+    LW lw;
+    lm_loads(la, st[0].a, row0, R - 1, H);
+    lm_loads(lw, st[0].w, vt0, V - 1, H);
+    const uint32_t lds_b = (uint32_t)(reinterpret_cast<uintptr_t>(st[0].b) - reinterpret_cast<uintptr_t>(st[0].a));
+    const uint32_t lds_s =
+        NS == 2 ? (uint32_t)(reinterpret_cast<uintptr_t>(&st[NS - 1]) - reinterpret_cast<uintptr_t>(&st[0])) : 0u;
     const uint16_t *pa = h0 + row0 * H, *pw = W + vt0 * H;
     const uint16_t *pb = TWO ? h1 + row0 * H : nullptr;
-    for (int k0 = 0; k0 < H; k0 += kLmKB) {
-        __syncthreads(); // every wave is done with the previous stage
-        lm_issue(la, pa + k0);
-        if (TWO) {
-            LmLoads<kLmRows> lb = la; // same rows and slots, the second view's LDS tile
+    auto issue = [&](int k0, int buf) {
+        LA l1 = la;
+        LW l2 = lw;
+        if (buf) {
 #pragma unroll
-            for (int i = 0; i < LmLoads<kLmRows>::kN; ++i)
-                lb.lds[i] += lds_b;
-            lm_issue(lb, pb + k0);
+            for (int i = 0; i < LA::kN; ++i)
+                l1.lds[i] += lds_s;
+#pragma unroll
+            for (int i = 0; i < LW::kN; ++i)
+                l2.lds[i] += lds_s;
         }
-        lm_issue(lw, pw + k0);
-        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+        lm_issue(l1, pa + k0);
+        if (TWO) {
+            LA l3 = l1; // same rows and slots, the second view's LDS tile
+#pragma unroll
+            for (int i = 0; i < LA::kN; ++i)
+                l3.lds[i] += lds_b;
+            lm_issue(l3, pb + k0);
+        }
+        lm_issue(l2, pw + k0);
+    };
+    auto compute = [&](const LmStage<G> &sg) {
 #pragma unroll 1
         for (int s = 0; s < kLmKB / 32; ++s) {
             const int c = 4 * s + (lane >> 4);
             bf16x8_t fw[2];
 #pragma unroll
             for (int n = 0; n < 2; ++n)
-                fw[n] = lm_frag(st.w, 32 * wave + 16 * n + (lane & 15), c);
+                fw[n] = lm_frag(sg.w, 32 * wq + 16 * n + (lane & 15), c);
 #pragma unroll
             for (int m = 0; m < kLmM; ++m) {
-                const bf16x8_t f0 = lm_frag(st.a, 16 * m + (lane & 15), c);
+                const bf16x8_t f0 = lm_frag(sg.a, gr + 16 * m + (lane & 15), c);
 #pragma unroll
                 for (int n = 0; n < 2; ++n)
                     acc0[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f0, fw[n], acc0[m][n], 0, 0, 0);
                 if (TWO) {
-                    const bf16x8_t f1 = lm_frag(st.b, 16 * m + (lane & 15), c);
+                    const bf16x8_t f1 = lm_frag(sg.b, gr + 16 * m + (lane & 15), c);
 #pragma unroll
                     for (int n = 0; n < 2; ++n)
                         acc1[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f1, fw[n], acc1[m][n], 0, 0, 0);
                 }
             }
         }
+    };
+    if constexpr (NS == 1) {
+        for (int k0 = 0; k0 < H; k0 += kLmKB) {
+            __syncthreads(); // every wave is done with the previous stage
+            issue(k0, 0);
+            __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            compute(st[0]);
+        }
+    } else {
+        // this wave's staging loads per block: h (one or two views) and, for
+        // the waves that stage it, the head tile
+        const bool w_wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) < lm_w_waves<G>();
+        const int n_blk = LA::kN * (TWO ? 2 : 1) + (w_wave ? LW::kN : 0);
+        __syncthreads(); // the buffers' previous readers are done
+        issue(0, 0);
+        int buf = 0;
+        for (int k0 = 0; k0 < H; k0 += kLmKB) {
+            const bool more = k0 + kLmKB < H;
+            if (more) {
+                issue(k0 + kLmKB, buf ^ 1);
+                // all but the block just issued (loads complete in order)
+                if (n_blk == 6)
+                    __asm__ volatile("s_waitcnt vmcnt(6)" ::: "memory");
+                else if (n_blk == 4)
+                    __asm__ volatile("s_waitcnt vmcnt(4)" ::: "memory");
+                else if (n_blk == 2)
+                    __asm__ volatile("s_waitcnt vmcnt(2)" ::: "memory");
+                else
+                    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            } else {
+                __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
+            lds_barrier(); // every wave's loads of this buffer have landed
+            compute(st[buf]);
+            lds_barrier(); // every wave is done with this buffer before its refill
+            buf ^= 1;
+        }
     }
 }
 
-// Row of accumulator slot (m, j) in the workgroup's 64 rows, and column of
+// Row of accumulator slot (m, j) in the workgroup's 64 G rows, and column of
 // block n in the tile's 128.
-__device__ __forceinline__ int lm_row(int m, int j) { return 16 * m + 4 * ((threadIdx.x & 63) >> 4) + j; }
-__device__ __forceinline__ int lm_col(int n) { return 32 * (threadIdx.x >> 6) + 16 * n + (threadIdx.x & 15); }
+__device__ __forceinline__ int lm_row(int m, int j) {
+    return kLmRows * (threadIdx.x >> 8) + 16 * m + 4 * ((threadIdx.x & 63) >> 4) + j;
+}
+__device__ __forceinline__ int lm_col(int n) { return 32 * ((threadIdx.x >> 6) & 3) + 16 * n + (threadIdx.x & 15); }
 
 // The waves' partials of a tile: a's and b's statistics, then t's and the
 // fused maxima with their columns.
+// [column quarter][row]: the 4 waves of a row's group.
+template <int G>
 struct LmScratch {
-    float ref0[kWaves][kLmRows]; // a, then t
-    float sum0[kWaves][kLmRows];
-    float ref1[kWaves][kLmRows]; // b, then the fused maxima
+    float ref0[4][G * kLmRows]; // a, then t
+    float sum0[4][G * kLmRows];
+    float ref1[4][G * kLmRows]; // b, then the fused maxima
     union {
-        float sum1[kWaves][kLmRows]; // b
-        int fi[kWaves][kLmRows];     // the fused maxima's columns
+        float sum1[4][G * kLmRows]; // b
+        int fi[4][G * kLmRows];     // the fused maxima's columns
     };
 };
 // Running per-row state of the workgroup's rows across its tiles (in LDS,
 // so that no register holds it across the k loops): the statistics of the
 // first pass, or the JSD sum of the recomputing pass.
+template <int G>
 struct LmRun {
-    double s[3][kLmRows];
-    float c[3][kLmRows];
-    float fm[kLmRows];
-    int fi[kLmRows];
+    double s[3][G * kLmRows];
+    float c[3][G * kLmRows];
+    float fm[G * kLmRows];
+    int fi[G * kLmRows];
 };
 // Row constants of the recomputing pass: L_a, L_b (log2 units) and their
 // difference in nats as a float pair.
+template <int G>
 struct LmRowC {
-    float la[kLmRows], lb[kLmRows], dh[kLmRows], dlo[kLmRows];
+    float la[G * kLmRows], lb[G * kLmRows], dh[G * kLmRows], dlo[G * kLmRows];
 };
 // Merge a partial (reference c, sum s) into a running fp64 state.
 __device__ __forceinline__ void lm_merge(float &run_c, double &run_s, float c, double s) {
@@ -218,13 +290,14 @@ __device__ __forceinline__ void lm_merge(float &run_c, double &run_s, float c, d
 
 // Fold the waves' partials of tensor k into its running state (one thread
 // per row), the waves in column order.
-__device__ __forceinline__ void lm_fold_one(LmRun &run, int k, const float (&ref)[kWaves][kLmRows],
-                                            const float (&sum)[kWaves][kLmRows]) {
+template <int G>
+__device__ __forceinline__ void lm_fold_one(LmRun<G> &run, int k, const float (&ref)[4][G * kLmRows],
+                                            const float (&sum)[4][G * kLmRows]) {
     const int tid = threadIdx.x;
     float c = run.c[k][tid];
     double sm = run.s[k][tid];
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w)
+    for (int w = 0; w < 4; ++w)
         lm_merge(c, sm, ref[w][tid], (double)sum[w][tid]);
     run.c[k][tid] = c;
     run.s[k][tid] = sm;
@@ -232,20 +305,20 @@ __device__ __forceinline__ void lm_fold_one(LmRun &run, int k, const float (&ref
 // The tile's partials into the running state: threads 0..63, one row each.
 // AB: a and b (tensors 0 and 1); else t (tensor 2) and the fused maxima (a
 // strict > keeps the lowest index).
-template <bool AB>
-__device__ __forceinline__ void lm_fold(LmRun &run, const LmScratch &sc, long long vt0) {
+template <bool AB, int G>
+__device__ __forceinline__ void lm_fold(LmRun<G> &run, const LmScratch<G> &sc, long long vt0) {
     const int tid = threadIdx.x;
-    if (tid >= kLmRows)
+    if (tid >= G * kLmRows)
         return;
     if (AB) {
-        lm_fold_one(run, 0, sc.ref0, sc.sum0);
-        lm_fold_one(run, 1, sc.ref1, sc.sum1);
+        lm_fold_one<G>(run, 0, sc.ref0, sc.sum0);
+        lm_fold_one<G>(run, 1, sc.ref1, sc.sum1);
     } else {
-        lm_fold_one(run, 2, sc.ref0, sc.sum0);
+        lm_fold_one<G>(run, 2, sc.ref0, sc.sum0);
         float fm = run.fm[tid];
         int fi = run.fi[tid];
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
+        for (int w = 0; w < 4; ++w) {
             if (sc.ref1[w][tid] > fm) {
                 fm = sc.ref1[w][tid];
                 fi = (int)vt0 + sc.fi[w][tid];
@@ -261,10 +334,11 @@ __device__ __forceinline__ void lm_fold(LmRun &run, const LmScratch &sc, long lo
 // reference and the fp32 sum of 2^(x*log2e - ref) over the wave's 32 columns
 // (identical in the 16 lanes of a DPP row; lane 0 of the row writes).
 // Invalid columns count as -inf.
-__device__ __forceinline__ void lm_tile_stats(float (&ref)[kWaves][kLmRows], float (&sum)[kWaves][kLmRows],
+template <int G>
+__device__ __forceinline__ void lm_tile_stats(float (&ref)[4][G * kLmRows], float (&sum)[4][G * kLmRows],
                                               const f32x4_t (&x)[kLmM][2], const bool (&cv)[2]) {
     const float NEG_INF = -__builtin_inff();
-    const int wave = threadIdx.x >> 6;
+    const int wave = (threadIdx.x >> 6) & 3;
 #pragma unroll
     for (int m = 0; m < kLmM; ++m)
 #pragma unroll
@@ -287,13 +361,23 @@ __device__ __forceinline__ void lm_tile_stats(float (&ref)[kWaves][kLmRows], flo
 // pair storage): a and b formed again by the same code, so with the same
 // bits, and the JSD terms against L_a, L_b summed into one partial per (row,
 // range).
-template <int PASS, bool STORE>
-__global__ __launch_bounds__(kThreads, 3) void lmhead_kernel(LmheadParams P) {
-    __shared__ LmStage st;
-    __shared__ LmScratch sc;
-    __shared__ LmRun run;
-    __shared__ LmRowC rowc;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+template <int PASS, bool STORE, int G>
+__global__ __launch_bounds__(kThreads * G, (G == 1 ? 3 : 1)) void lmhead_kernel(LmheadParams P) {
+    constexpr int kRowsWg = G * kLmRows;
+    constexpr int NS = G == 1 ? 1 : 2; // staging buffers
+    // the staging buffers first, at LDS address 0: the staging loads take
+    // their LDS address from M0
+    __shared__ struct {
+        LmStage<G> st[NS];
+        LmScratch<G> sc;
+        LmRun<G> run;
+        LmRowC<G> rowc;
+    } sh;
+    LmStage<G> (&st)[NS] = sh.st;
+    LmScratch<G> &sc = sh.sc;
+    LmRun<G> &run = sh.run;
+    LmRowC<G> &rowc = sh.rowc;
+    const int tid = threadIdx.x, lane = tid & 63, wave = (tid >> 6) & 3;
     // workgroup b runs on die b % 8: the row tiles of one vocabulary range
     // share a die, so its head tiles come from one L2
     const long long b = blockIdx.x;
@@ -302,13 +386,13 @@ __global__ __launch_bounds__(kThreads, 3) void lmhead_kernel(LmheadParams P) {
     const int s = (int)(8 * (q / P.RT) + b % 8);
     if (s >= P.S)
         return;
-    const long long row0 = (long long)rtile * kLmRows;
+    const long long row0 = (long long)rtile * kRowsWg;
     const long long v_begin = (long long)s * P.range;
     const long long v_end = min((long long)P.V, v_begin + P.range);
     const float NEG = -3.0e38f;
 
-    // running per-row state in LDS (threads 0..63, row = tid)
-    if (tid < kLmRows) {
+    // running per-row state in LDS (one thread per row, row = tid)
+    if (tid < kRowsWg) {
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
             run.c[k][tid] = NEG;
@@ -333,7 +417,7 @@ __global__ __launch_bounds__(kThreads, 3) void lmhead_kernel(LmheadParams P) {
         for (int n = 0; n < 2; ++n)
             cv[n] = vt0 + lm_col(n) < v_end;
         f32x4_t xa[kLmM][2], xb[kLmM][2];
-        lm_gemm<true>(st, P.ha, P.hb, P.Wd, row0, P.R, vt0, P.V, P.Hd, xa, xb);
+        lm_gemm<true, G, NS>(st, P.ha, P.hb, P.Wd, row0, P.R, vt0, P.V, P.Hd, xa, xb);
         if (PASS == 2) {
             // JSD terms of the block against the row's log-sum-exps
 #pragma unroll
@@ -356,10 +440,10 @@ __global__ __launch_bounds__(kThreads, 3) void lmhead_kernel(LmheadParams P) {
                         sc.sum0[wave][r] = J;
                 }
             __syncthreads();
-            if (tid < kLmRows) { // the waves in column order
+            if (tid < kRowsWg) { // the waves in column order
                 double t = run.s[0][tid];
 #pragma unroll
-                for (int w = 0; w < kWaves; ++w)
+                for (int w = 0; w < 4; ++w)
                     t += (double)sc.sum0[w][tid];
                 run.s[0][tid] = t;
             }
@@ -384,18 +468,18 @@ __global__ __launch_bounds__(kThreads, 3) void lmhead_kernel(LmheadParams P) {
                     __builtin_nontemporal_store(f32x2_t{xa[m][1][j], xb[m][1][j]}, qr + 16);
                 }
         }
-        lm_tile_stats(sc.ref0, sc.sum0, xa, cv);
-        lm_tile_stats(sc.ref1, sc.sum1, xb, cv);
+        lm_tile_stats<G>(sc.ref0, sc.sum0, xa, cv);
+        lm_tile_stats<G>(sc.ref1, sc.sum1, xb, cv);
 #pragma unroll
         for (int m = 0; m < kLmM; ++m)
 #pragma unroll
             for (int n = 0; n < 2; ++n)
                 xa[m][n] = xa[m][n] - xb[m][n];
         __syncthreads();
-        lm_fold<true>(run, sc, vt0);
+        lm_fold<true, G>(run, sc, vt0);
         f32x4_t xt[kLmM][2], unused[kLmM][2];
-        lm_gemm<false>(st, P.ht, nullptr, P.Wt, row0, P.R, vt0, P.V, P.Ht, xt, unused);
-        lm_tile_stats(sc.ref0, sc.sum0, xt, cv);
+        lm_gemm<false, G, NS>(st, P.ht, nullptr, P.Wt, row0, P.R, vt0, P.V, P.Ht, xt, unused);
+        lm_tile_stats<G>(sc.ref0, sc.sum0, xt, cv);
 #pragma unroll
         for (int m = 0; m < kLmM; ++m)
 #pragma unroll
@@ -414,15 +498,15 @@ __global__ __launch_bounds__(kThreads, 3) void lmhead_kernel(LmheadParams P) {
                 }
             }
         __syncthreads();
-        lm_fold<false>(run, sc, vt0);
+        lm_fold<false, G>(run, sc, vt0);
     }
     const long long row = row0 + tid;
     if (PASS == 2) {
-        if (tid < kLmRows && row < P.R)
+        if (tid < kRowsWg && row < P.R)
             P.jpart[row * P.jc + s] = run.s[0][tid];
         return;
     }
-    if (tid < kLmRows && row < P.R) {
+    if (tid < kRowsWg && row < P.R) {
         uint64_t *rec = P.rec + ((size_t)row * P.S + s) * kRecWords;
         rec[0] = f64_bits(run.s[0][tid]);
         rec[1] = f64_bits(run.s[1][tid]);
@@ -627,20 +711,23 @@ __global__ __launch_bounds__(kFinMaxThreads) void lmhead_finalize_kernel(LmheadP
     }
 }
 
-int lmhead_blocks_per_cu() {
+int lmhead_blocks_per_cu(int G) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, lmhead_kernel<1, true>, kThreads, 0) != hipSuccess)
-        return 0;
-    return n;
+    const hipError_t e = G == 1
+        ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, lmhead_kernel<1, true, 1>, kThreads, 0)
+        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, lmhead_kernel<1, true, 3>, kThreads * 3, 0);
+    return e == hipSuccess ? n : 0;
 }
 
-hipError_t launch_lmhead(const LmheadParams &p, hipStream_t s, hipEvent_t after_rows) {
+template <int G>
+static hipError_t launch_lmhead_g(const LmheadParams &p, hipStream_t s, hipEvent_t after_rows) {
     const unsigned grid = (unsigned)(8 * (long long)p.RT * ((p.S + 7) / 8));
+    const dim3 block(kThreads * G);
     const bool store = p.lg != nullptr;
     if (store)
-        hipLaunchKernelGGL((lmhead_kernel<1, true>), dim3(grid), dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((lmhead_kernel<1, true, G>), dim3(grid), block, 0, s, p);
     else
-        hipLaunchKernelGGL((lmhead_kernel<1, false>), dim3(grid), dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((lmhead_kernel<1, false, G>), dim3(grid), block, 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
@@ -655,7 +742,15 @@ hipError_t launch_lmhead(const LmheadParams &p, hipStream_t s, hipEvent_t after_
     if (store) {
         hipLaunchKernelGGL(lmhead_jsd_kernel, dim3((unsigned)(p.R * p.jc)), dim3(kThreads), 0, s, p);
     } else {
-        hipLaunchKernelGGL((lmhead_kernel<2, false>), dim3(grid), dim3(kThreads), 0, s, p);
+        // the recomputing pass on 64-row workgroups (its JSD epilogue is
+        // VALU work that three workgroups per CU overlap with their loads
+        // better than one 192-row workgroup does); its partials are per
+        // (row, range), as the ranges are
+        LmheadParams p1 = p;
+        p1.G = 1;
+        p1.RT = (int)((p.R + kLmRows - 1) / kLmRows);
+        const unsigned grid1 = (unsigned)(8 * (long long)p1.RT * ((p.S + 7) / 8));
+        hipLaunchKernelGGL((lmhead_kernel<2, false, 1>), dim3(grid1), dim3(kThreads), 0, s, p1);
         if ((e = hipGetLastError()) != hipSuccess)
             return e;
         if (after_rows) {
@@ -668,6 +763,10 @@ hipError_t launch_lmhead(const LmheadParams &p, hipStream_t s, hipEvent_t after_
         return e;
     hipLaunchKernelGGL(lmhead_finalize_kernel, dim3((unsigned)p.B), dim3(fin_threads(p.K + 1)), 0, s, p);
     return hipGetLastError();
+}
+
+hipError_t launch_lmhead(const LmheadParams &p, hipStream_t s, hipEvent_t after_rows) {
+    return p.G == 3 ? launch_lmhead_g<3>(p, s, after_rows) : launch_lmhead_g<1>(p, s, after_rows);
 }
 
 } // namespace vwl

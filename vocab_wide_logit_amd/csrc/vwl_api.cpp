@@ -54,7 +54,7 @@ struct DeviceInfo {
     int cus = 0;
     int asym_bpc[2][4][4][2] = {}; // [dtype][nv][delta source or kDeltaNone][gate]
     int rapid_bpc[2][4] = {};
-    int lm_bpc = 0;
+    int lm_bpc = 0, lm_bpc3 = 0; // LM-head pass workgroups per CU: 64-row, 192-row
 };
 constexpr int kMaxDevices = 64;
 DeviceInfo g_dev[kMaxDevices];
@@ -85,7 +85,8 @@ const DeviceInfo *device_info() {
                         d.asym_bpc[dt][k][ds][g] = asym_blocks_per_cu(dt, kNvChoices[k], ds, g);
                 d.rapid_bpc[dt][k] = rapid_blocks_per_cu(dt, kNvChoices[k]);
             }
-        d.lm_bpc = lmhead_blocks_per_cu();
+        d.lm_bpc = lmhead_blocks_per_cu(1);
+        d.lm_bpc3 = lmhead_blocks_per_cu(3);
         d.ready = true;
     }
     return &d;
@@ -632,7 +633,7 @@ vwl_status asym_verify_xfam(const void *a, const void *b, int Vd, const void *t,
 // LM-head pass geometry: row tiles of kLmRowTile, vocabulary ranges
 // (multiples of 128 tokens) and the JSD pass's chunks.
 struct LmGeom {
-    int RT, S, range, jc;
+    int G, RT, S, range, jc;
     long long lgs;
     size_t rec, rowstat, lg, jpart, total_min, total;
 };
@@ -647,8 +648,11 @@ static bool lm_geometry(int B, int K, int V, int Hd, int Ht, LmGeom &g) {
     if (!shape_ok(B, K, V) || Hd < 64 || Ht < 64 || Hd % 64 || Ht % 64)
         return false;
     const long long R = (long long)B * (K + 1);
-    const long long RT = (R + kLmRowTile - 1) / kLmRowTile;
-    const long long max_wgs = 0xffffffffLL / kThreads;
+    // past 128 rows a workgroup takes 192 rows (3 groups of 4 waves sharing
+    // each head tile), else 64
+    const int G = R > 2 * kLmRowTile ? 3 : 1;
+    const long long RT = (R + G * kLmRowTile - 1) / (G * kLmRowTile);
+    const long long max_wgs = 0xffffffffLL / (kThreads * G);
     if (RT > (1LL << 24))
         return false;
     const long long tiles = ((long long)V + 127) / 128;
@@ -657,10 +661,11 @@ static bool lm_geometry(int B, int K, int V, int Hd, int Ht, LmGeom &g) {
     const long long jc = ((long long)V + kLmJsdChunk - 1) / kLmJsdChunk;
     if (R * jc > max_wgs)
         return false;
-    // the stored pairs cover whole tiles: RT * 64 rows of whole 128-token tiles
+    // the stored pairs cover whole tiles: RT * 64 G rows of whole 128-token tiles
     const long long lgs = tiles * 128;
-    if ((long double)(RT * kLmRowTile) * (long double)lgs * 8.0L > 4.0e18L)
+    if ((long double)(RT * G * kLmRowTile) * (long double)lgs * 8.0L > 4.0e18L)
         return false;
+    g.G = G;
     g.RT = (int)RT;
     g.S = (int)tiles;
     g.range = 128;
@@ -671,7 +676,7 @@ static bool lm_geometry(int B, int K, int V, int Hd, int Ht, LmGeom &g) {
     g.rowstat = off;  off = align256(off + (size_t)R * kLmStat * 8);
     g.jpart = off;    off = align256(off + (size_t)R * (size_t)(tiles > jc ? tiles : jc) * 8);
     g.total_min = off;
-    g.lg = off;       off = align256(off + (size_t)(RT * kLmRowTile) * (size_t)lgs * 8);
+    g.lg = off;       off = align256(off + (size_t)(RT * G * kLmRowTile) * (size_t)lgs * 8);
     g.total = off;
     return true;
 }
@@ -724,7 +729,7 @@ vwl_status asym_verify_lmhead(const void *h_a, const void *h_b, const void *W_d,
     const DeviceInfo *dev = device_info();
     if (!dev)
         return VWL_ERR_HIP;
-    lm_split(g, V, (long long)dev->cus * dev->lm_bpc);
+    lm_split(g, V, (long long)dev->cus * (g.G == 3 ? dev->lm_bpc3 : dev->lm_bpc));
     if (!aligned(h_a, 16) || !aligned(h_b, 16) || !aligned(W_d, 16) || !aligned(h_t, 16) || !aligned(W_t, 16) ||
         !aligned(D, 4) || !aligned(gamma_eff, 4) || !aligned(fused, 4) || !aligned(accept_len, 4) ||
         !aligned(token, 4) || (draft && !aligned(draft, 4)) || (dev_err && !aligned(dev_err, 4)))
@@ -748,6 +753,7 @@ vwl_status asym_verify_lmhead(const void *h_a, const void *h_b, const void *W_d,
     p.V = V;
     p.Hd = Hd;
     p.Ht = Ht;
+    p.G = g.G;
     p.RT = g.RT;
     p.S = g.S;
     p.range = g.range;

@@ -156,7 +156,8 @@ struct LmheadParams {
     const int32_t *draft;
     long long R;
     int B, K, V, Hd, Ht;
-    int RT;    // row tiles of 64
+    int G;     // groups of 64 rows per workgroup (1 or 3)
+    int RT;    // row tiles of 64 G
     int S;     // vocabulary ranges (records per row)
     int range; // tokens per range (a multiple of 128)
     float beta, gamma;
@@ -166,7 +167,7 @@ struct LmheadParams {
     int32_t *fused, *acc_len, *token, *dev_err;
     uint64_t *rec;    // [R][S][8], the row kernel's record layout
     double *rowstat;  // [R][kLmStat] L_a, L_b, L_t (log2 units), fused token, t_d, b_d
-    float *lg;        // [RT * 64][lgs][2] the logit pairs (a, b) of the first launch
+    float *lg;        // [RT * 64 G][lgs][2] the logit pairs (a, b) of the first launch
     long long lgs;    // pairs per row of lg (V rounded up to whole 128-token tiles)
     double *jpart;    // [R][jc] the JSD pass's partial sums
     int jc;           // JSD chunks per row
@@ -179,7 +180,7 @@ constexpr int kLmStat = 6; // per-row statistics of the LM-head path
 constexpr int kLmJsdPairs = 16;
 constexpr int kLmJsdChunk = kThreads * kLmJsdPairs;
 hipError_t launch_lmhead(const LmheadParams &p, hipStream_t s, hipEvent_t after_rows);
-int lmhead_blocks_per_cu();
+int lmhead_blocks_per_cu(int G);
 
 // AsymSpec variants (values match vwl_delta_source / vwl_gate of the C ABI);
 // kDeltaNone is the two-tensor divergence pass of E2-SCI.
